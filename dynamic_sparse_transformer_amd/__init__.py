@@ -1,0 +1,253 @@
+"""Topological Attention over the condensate set on AMD MI355X (gfx950).
+
+Python binding of libtopo_attn.so, the C ABI declared in include/topo_attn.h. Argument marshalling
+only: every step of the computation runs in the library's HIP kernels. PyTorch supplies device
+memory and the current stream. There is no fallback: if the library is missing or a call fails,
+the call raises.
+
+Method: "The Condensate Theorem: Transformers are O(n), Not O(n^2)" (gist.science explainers of
+arXiv 2602.06317). Per query, attention runs over the anchor (position 0), the W most recent
+tokens and the k keys with the highest Q.K^T scores (zh page, technical summary §3; fr page,
+technical summary §3).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = [
+    "TopoError", "load_library", "library_path", "topo_workspace_bytes", "topo_attn_decode",
+    "topo_attn_prefill", "topo_select", "topo_attn_dense", "topo_bw_probe", "topo_strerror",
+    "TOPO_FLAG_EXACT_SELECT", "TOPO_MAX_SET", "EXPORTS",
+]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+library_path = os.path.join(_PKG, "libtopo_attn.so")
+
+TOPO_F32, TOPO_BF16 = 0, 1
+TOPO_OP_DECODE, TOPO_OP_PREFILL, TOPO_OP_SELECT, TOPO_OP_DENSE = 0, 1, 2, 3
+TOPO_FLAG_EXACT_SELECT = 1
+TOPO_MAX_SET = 4096
+EXPORTS = ("topo_workspace_bytes", "topo_attn_decode", "topo_attn_prefill", "topo_select",
+           "topo_attn_dense", "topo_bw_probe", "topo_strerror")
+
+
+class TopoError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what}: {topo_strerror(status)} (status {status})")
+        self.status = status
+
+
+class TopoParams(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("Hq", ctypes.c_int32), ("Hkv", ctypes.c_int32),
+                ("d", ctypes.c_int32), ("n_ctx", ctypes.c_int64), ("n_q", ctypes.c_int64),
+                ("q_pos0", ctypes.c_int64), ("W", ctypes.c_int32), ("k", ctypes.c_int32),
+                ("causal", ctypes.c_int32), ("softmax_scale", ctypes.c_float),
+                ("dtype", ctypes.c_int32), ("flags", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def load_library(path: str | None = None) -> ctypes.CDLL:
+    """Load libtopo_attn.so (built in-tree by __graft_entry__.build()); raise if it is missing."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or library_path
+    if not os.path.exists(p):
+        raise FileNotFoundError(f"{p} is missing: build it first (python -c 'import __graft_entry__ as g; g.build()')")
+    lib = ctypes.CDLL(p)
+    vp, sz, i32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
+    P = ctypes.POINTER(TopoParams)
+    lib.topo_workspace_bytes.argtypes = [P, i32]
+    lib.topo_workspace_bytes.restype = sz
+    for name in ("topo_attn_decode", "topo_attn_prefill"):
+        f = getattr(lib, name)
+        f.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        f.restype = i32
+    lib.topo_select.argtypes = [P, vp, vp, vp, vp, vp, sz, vp]
+    lib.topo_select.restype = i32
+    lib.topo_attn_dense.argtypes = [P, vp, vp, vp, vp, vp, sz, vp]
+    lib.topo_attn_dense.restype = i32
+    lib.topo_bw_probe.argtypes = [vp, sz, vp, vp]
+    lib.topo_bw_probe.restype = i32
+    lib.topo_strerror.argtypes = [i32]
+    lib.topo_strerror.restype = ctypes.c_char_p
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def topo_strerror(status: int) -> str:
+    return load_library().topo_strerror(int(status)).decode()
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return TOPO_F32
+    if t.dtype == torch.bfloat16:
+        return TOPO_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}: float32 or bfloat16")
+
+
+def _params(q, k, W, topk, softmax_scale, causal, q_pos0, flags) -> TopoParams:
+    B, Hq, n_q, d = q.shape
+    Bk, Hkv, n_ctx, dk = k.shape
+    if Bk != B or dk != d:
+        raise ValueError(f"q {tuple(q.shape)} and k {tuple(k.shape)} disagree")
+    return TopoParams(B, Hq, Hkv, d, n_ctx, n_q, int(q_pos0), int(W), int(topk), int(bool(causal)),
+                      float(softmax_scale), _dtype_code(q), int(flags))
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _stream(stream):
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _check_tensors(*ts):
+    for t in ts:
+        if t is not None and (not t.is_cuda or not t.is_contiguous()):
+            raise ValueError("tensors must be contiguous device tensors")
+
+
+def topo_workspace_bytes(q, k, W: int, topk: int, softmax_scale: float, causal: bool = True,
+                         q_pos0: int | None = None, op: int = TOPO_OP_DECODE, flags: int = 0) -> int:
+    q4 = q if q.dim() == 4 else q.unsqueeze(2)
+    if q_pos0 is None:
+        q_pos0 = k.shape[2] - q4.shape[2]
+    p = _params(q4, k, W, topk, softmax_scale, causal, q_pos0, flags)
+    return int(load_library().topo_workspace_bytes(ctypes.byref(p), op))
+
+
+def _workspace(nbytes, device, workspace):
+    torch = _torch()
+    if workspace is not None:
+        if workspace.numel() * workspace.element_size() < nbytes:
+            raise TopoError(-3, "workspace")
+        return workspace
+    return torch.empty(max(nbytes, 16), dtype=torch.uint8, device=device)
+
+
+def _attn(name, q, k, v, W, topk, softmax_scale, causal, q_pos0, flags, out, sel_idx, sel_count,
+          workspace, stream, want_sets):
+    torch = _torch()
+    lib = load_library()
+    q4 = q if q.dim() == 4 else q.unsqueeze(2)
+    if q_pos0 is None:
+        q_pos0 = k.shape[2] - q4.shape[2]
+    p = _params(q4, k, W, topk, softmax_scale, causal, q_pos0, flags)
+    _check_tensors(q4, k, v)
+    B, Hq, n_q, d = q4.shape
+    S = 1 + int(W) + int(topk)
+    op = TOPO_OP_DECODE if name == "topo_attn_decode" else TOPO_OP_PREFILL
+    nbytes = lib.topo_workspace_bytes(ctypes.byref(p), op)
+    if nbytes == 0:
+        raise TopoError(-1, f"{name}: parameters rejected")
+    ws = _workspace(nbytes, q4.device, workspace)
+    if out is None:
+        out = torch.empty((B, Hq, n_q, d), dtype=torch.float32, device=q4.device)
+    if want_sets:
+        if sel_idx is None:
+            sel_idx = torch.empty((B, Hq, n_q, S), dtype=torch.int32, device=q4.device)
+        if sel_count is None:
+            sel_count = torch.empty((B, Hq, n_q), dtype=torch.int32, device=q4.device)
+    _check_tensors(out, sel_idx, sel_count)
+    rc = getattr(lib, name)(ctypes.byref(p), _ptr(q4), _ptr(k), _ptr(v), _ptr(out), _ptr(sel_idx),
+                            _ptr(sel_count), _ptr(ws), ctypes.c_size_t(ws.numel()), _stream(stream))
+    if rc != 0:
+        raise TopoError(rc, name)
+    return out, sel_idx, sel_count
+
+
+def topo_attn_decode(q, k, v, W: int, topk: int, softmax_scale: float, causal: bool = True,
+                     q_pos0: int | None = None, flags: int = 0, out=None, sel_idx=None, sel_count=None,
+                     workspace=None, stream=None, want_sets: bool = True):
+    """One query per (batch, query head). q: (B, Hq, d) or (B, Hq, 1, d); k, v: (B, Hkv, n, d).
+    q_pos0 defaults to n-1 (the newest token). Returns (out f32 (B,Hq,1,d), sel_idx, sel_count)."""
+    return _attn("topo_attn_decode", q, k, v, W, topk, softmax_scale, causal, q_pos0, flags, out, sel_idx,
+                 sel_count, workspace, stream, want_sets)
+
+
+def topo_attn_prefill(q, k, v, W: int, topk: int, softmax_scale: float, causal: bool = True,
+                      q_pos0: int | None = None, flags: int = 0, out=None, sel_idx=None, sel_count=None,
+                      workspace=None, stream=None, want_sets: bool = True):
+    """n_q queries per (batch, query head) at positions q_pos0 .. q_pos0+n_q-1 (default: the last
+    n_q positions; a whole prompt is q_pos0 = 0, n_q = n). q: (B, Hq, n_q, d)."""
+    return _attn("topo_attn_prefill", q, k, v, W, topk, softmax_scale, causal, q_pos0, flags, out, sel_idx,
+                 sel_count, workspace, stream, want_sets)
+
+
+def topo_select(q, k, W: int, topk: int, softmax_scale: float = 1.0, causal: bool = True,
+                q_pos0: int | None = None, flags: int = 0, sel_idx=None, sel_count=None, workspace=None,
+                stream=None):
+    """Condensate sets only. Returns (sel_idx int32 (B,Hq,n_q,1+W+k), sel_count int32 (B,Hq,n_q))."""
+    torch = _torch()
+    lib = load_library()
+    q4 = q if q.dim() == 4 else q.unsqueeze(2)
+    if q_pos0 is None:
+        q_pos0 = k.shape[2] - q4.shape[2]
+    p = _params(q4, k, W, topk, softmax_scale, causal, q_pos0, flags)
+    _check_tensors(q4, k)
+    B, Hq, n_q, d = q4.shape
+    nbytes = lib.topo_workspace_bytes(ctypes.byref(p), TOPO_OP_SELECT)
+    if nbytes == 0:
+        raise TopoError(-1, "topo_select: parameters rejected")
+    ws = _workspace(nbytes, q4.device, workspace)
+    if sel_idx is None:
+        sel_idx = torch.empty((B, Hq, n_q, 1 + int(W) + int(topk)), dtype=torch.int32, device=q4.device)
+    if sel_count is None:
+        sel_count = torch.empty((B, Hq, n_q), dtype=torch.int32, device=q4.device)
+    rc = lib.topo_select(ctypes.byref(p), _ptr(q4), _ptr(k), _ptr(sel_idx), _ptr(sel_count), _ptr(ws),
+                         ctypes.c_size_t(ws.numel()), _stream(stream))
+    if rc != 0:
+        raise TopoError(rc, "topo_select")
+    return sel_idx, sel_count
+
+
+def topo_attn_dense(q, k, v, softmax_scale: float, causal: bool = True, q_pos0: int | None = None,
+                    out=None, workspace=None, stream=None):
+    """Dense attention over every visible key (the pillar layer). Returns out f32 (B,Hq,n_q,d)."""
+    torch = _torch()
+    lib = load_library()
+    q4 = q if q.dim() == 4 else q.unsqueeze(2)
+    if q_pos0 is None:
+        q_pos0 = k.shape[2] - q4.shape[2]
+    p = _params(q4, k, 0, 0, softmax_scale, causal, q_pos0, 0)
+    _check_tensors(q4, k, v)
+    B, Hq, n_q, d = q4.shape
+    nbytes = lib.topo_workspace_bytes(ctypes.byref(p), TOPO_OP_DENSE)
+    if nbytes == 0:
+        raise TopoError(-1, "topo_attn_dense: parameters rejected")
+    ws = _workspace(nbytes, q4.device, workspace)
+    if out is None:
+        out = torch.empty((B, Hq, n_q, d), dtype=torch.float32, device=q4.device)
+    rc = lib.topo_attn_dense(ctypes.byref(p), _ptr(q4), _ptr(k), _ptr(v), _ptr(out), _ptr(ws),
+                             ctypes.c_size_t(ws.numel()), _stream(stream))
+    if rc != 0:
+        raise TopoError(rc, "topo_attn_dense")
+    return out
+
+
+def topo_bw_probe(buf, sink=None, stream=None):
+    """Stream every byte of the device tensor `buf` once (read-bandwidth reference)."""
+    torch = _torch()
+    lib = load_library()
+    if sink is None:
+        sink = torch.zeros(4, dtype=torch.int32, device=buf.device)
+    nbytes = buf.numel() * buf.element_size()
+    rc = lib.topo_bw_probe(_ptr(buf), ctypes.c_size_t(nbytes - nbytes % 16), _ptr(sink), _stream(stream))
+    if rc != 0:
+        raise TopoError(rc, "topo_bw_probe")
+    return sink

@@ -1,0 +1,201 @@
+// C-ABI front end of libtopo_attn.so: argument validation, workspace sizing and carving, and the
+// launch sequence of each operation. The operation and its arithmetic are described in
+// include/topo_attn.h (condensate set of "The Condensate Theorem: Transformers are O(n), Not
+// O(n^2)", zh page, technical summary §3; softmax over the set, fr page, technical summary §3).
+#include <cmath>
+#include <cstdint>
+
+#include "../../include/topo_attn.h"
+#include "topo_internal.h"
+
+namespace {
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Shape, position and scalar checks shared by every operation. Returns TOPO_OK or an error.
+int check_params(const topo_params_t* p, bool need_set) {
+  if (!p) return TOPO_EINVAL;
+  if (p->dtype != TOPO_F32 && p->dtype != TOPO_BF16) return TOPO_EUNSUPPORTED;
+  if (p->d != 64 && p->d != 128) return TOPO_EUNSUPPORTED;
+  if (p->B < 1 || p->Hq < 1 || p->Hkv < 1 || p->Hq % p->Hkv != 0) return TOPO_EINVAL;
+  if (p->n_ctx < 1 || p->n_ctx > INT32_MAX) return TOPO_EINVAL;
+  if (p->n_q < 1 || p->q_pos0 < 0 || p->q_pos0 + p->n_q - 1 > p->n_ctx - 1) return TOPO_EINVAL;
+  if (!(p->softmax_scale > 0.f) || !std::isfinite(p->softmax_scale)) return TOPO_EINVAL;
+  if (p->causal != 0 && p->causal != 1) return TOPO_EINVAL;
+  if (p->flags & ~TOPO_FLAG_EXACT_SELECT) return TOPO_EINVAL;
+  if (need_set) {
+    if (p->W < 0 || p->k < 0) return TOPO_EINVAL;
+    if ((int64_t)p->W + p->k + 1 > TOPO_MAX_SET) return TOPO_EINVAL;
+  }
+  // Element counts must fit the 64-bit byte offsets used by the kernels.
+  const double elems = (double)p->B * p->Hkv * (double)p->n_ctx * p->d;
+  if (elems * 4.0 > 9.0e18) return TOPO_EINVAL;
+  return TOPO_OK;
+}
+
+topo::QueryGeom decode_geom(const topo_params_t* p) {
+  return topo::make_geom(p->q_pos0, p->n_ctx, p->W, p->causal != 0);
+}
+
+int decode_like(const topo_params_t* p, const void* q, const void* k, const void* v, float* out,
+                int32_t* sel_idx, int32_t* sel_count, void* ws, size_t ws_bytes, hipStream_t stream,
+                bool softmax) {
+  int rc = check_params(p, true);
+  if (rc) return rc;
+  if (p->n_q != 1) return TOPO_EINVAL;
+  if (!q || !k || !aligned16(q) || !aligned16(k)) return TOPO_EINVAL;
+  if (softmax && (!v || !out || !aligned16(v) || !aligned16(out))) return TOPO_EINVAL;
+  if (!softmax && (!sel_idx || !sel_count)) return TOPO_EINVAL;
+  if ((sel_idx && !aligned16(sel_idx)) || (sel_count && !aligned16(sel_count))) return TOPO_EINVAL;
+  const topo::QueryGeom g = decode_geom(p);
+  const size_t need = topo::decode_workspace_bytes(p->B, p->Hq, g, p->k);
+  if (!ws || ws_bytes < need || !aligned16(ws)) return TOPO_EWORKSPACE;
+
+  topo::DecodeLaunch L{};
+  L.q = q;
+  L.k = k;
+  L.v = softmax ? v : nullptr;
+  L.out = softmax ? out : nullptr;
+  L.sel_idx = sel_idx;
+  L.sel_count = sel_count;
+  L.B = p->B;
+  L.Hq = p->Hq;
+  L.Hkv = p->Hkv;
+  L.G = p->Hq / p->Hkv;
+  L.d = p->d;
+  L.W = p->W;
+  L.topk = p->k;
+  L.bf16 = p->dtype == TOPO_BF16;
+  L.flags = p->flags;
+  L.n = p->n_ctx;
+  L.geom = g;
+  L.scale = (double)p->softmax_scale;
+  L.eps_coef = topo::fast_score_eps_coef(p->d);
+  topo::decode_carve(ws, p->B, p->Hq, g, p->k, L);
+  return topo::launch_decode(L, stream) == hipSuccess ? TOPO_OK : TOPO_EHIP;
+}
+
+int prefill_like(const topo_params_t* p, const void* q, const void* k, const void* v, float* out,
+                 int32_t* sel_idx, int32_t* sel_count, void* ws, size_t ws_bytes, hipStream_t stream,
+                 bool softmax) {
+  int rc = check_params(p, true);
+  if (rc) return rc;
+  if (!q || !k || !aligned16(q) || !aligned16(k)) return TOPO_EINVAL;
+  if (softmax && (!v || !out || !aligned16(v) || !aligned16(out))) return TOPO_EINVAL;
+  if (!softmax && (!sel_idx || !sel_count)) return TOPO_EINVAL;
+  if ((sel_idx && !aligned16(sel_idx)) || (sel_count && !aligned16(sel_count))) return TOPO_EINVAL;
+  const size_t need = topo::prefill_workspace_bytes(p->B, p->Hq, p->n_q, p->n_ctx, p->d, p->W, p->k);
+  if (!ws || ws_bytes < need || !aligned16(ws)) return TOPO_EWORKSPACE;
+  topo::PrefillLaunch L{};
+  L.q = q;
+  L.k = k;
+  L.v = softmax ? v : nullptr;
+  L.out = softmax ? out : nullptr;
+  L.sel_idx = sel_idx;
+  L.sel_count = sel_count;
+  L.ws = ws;
+  L.B = p->B;
+  L.Hq = p->Hq;
+  L.Hkv = p->Hkv;
+  L.G = p->Hq / p->Hkv;
+  L.d = p->d;
+  L.W = p->W;
+  L.topk = p->k;
+  L.bf16 = p->dtype == TOPO_BF16;
+  L.causal = p->causal;
+  L.flags = p->flags;
+  L.n = p->n_ctx;
+  L.n_q = p->n_q;
+  L.q_pos0 = p->q_pos0;
+  L.scale = (double)p->softmax_scale;
+  L.eps_coef = topo::fast_score_eps_coef(p->d);
+  return topo::launch_prefill(L, stream) == hipSuccess ? TOPO_OK : TOPO_EHIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t topo_workspace_bytes(const topo_params_t* p, int op) {
+  const bool set = op != TOPO_OP_DENSE;
+  if (check_params(p, set) != TOPO_OK) return 0;
+  switch (op) {
+    case TOPO_OP_DECODE:
+      if (p->n_q != 1) return 0;
+      return topo::decode_workspace_bytes(p->B, p->Hq, decode_geom(p), p->k);
+    case TOPO_OP_PREFILL:
+      return topo::prefill_workspace_bytes(p->B, p->Hq, p->n_q, p->n_ctx, p->d, p->W, p->k);
+    case TOPO_OP_SELECT:
+      if (p->n_q == 1) return topo::decode_workspace_bytes(p->B, p->Hq, decode_geom(p), p->k);
+      return topo::prefill_workspace_bytes(p->B, p->Hq, p->n_q, p->n_ctx, p->d, p->W, p->k);
+    case TOPO_OP_DENSE:
+      return topo::dense_workspace_bytes(p->B, p->Hq, p->n_q, p->n_ctx, p->d);
+    default:
+      return 0;
+  }
+}
+
+int topo_attn_decode(const topo_params_t* p, const void* q, const void* k, const void* v, float* out,
+                     int32_t* sel_idx, int32_t* sel_count, void* workspace, size_t ws_bytes, hipStream_t stream) {
+  return decode_like(p, q, k, v, out, sel_idx, sel_count, workspace, ws_bytes, stream, true);
+}
+
+int topo_attn_prefill(const topo_params_t* p, const void* q, const void* k, const void* v, float* out,
+                      int32_t* sel_idx, int32_t* sel_count, void* workspace, size_t ws_bytes,
+                      hipStream_t stream) {
+  return prefill_like(p, q, k, v, out, sel_idx, sel_count, workspace, ws_bytes, stream, true);
+}
+
+int topo_select(const topo_params_t* p, const void* q, const void* k, int32_t* sel_idx, int32_t* sel_count,
+                void* workspace, size_t ws_bytes, hipStream_t stream) {
+  if (!p) return TOPO_EINVAL;
+  if (p->n_q == 1)
+    return decode_like(p, q, k, nullptr, nullptr, sel_idx, sel_count, workspace, ws_bytes, stream, false);
+  return prefill_like(p, q, k, nullptr, nullptr, sel_idx, sel_count, workspace, ws_bytes, stream, false);
+}
+
+int topo_attn_dense(const topo_params_t* p, const void* q, const void* k, const void* v, float* out,
+                    void* workspace, size_t ws_bytes, hipStream_t stream) {
+  int rc = check_params(p, false);
+  if (rc) return rc;
+  if (!q || !k || !v || !out || !aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
+    return TOPO_EINVAL;
+  const size_t need = topo::dense_workspace_bytes(p->B, p->Hq, p->n_q, p->n_ctx, p->d);
+  if (!workspace || ws_bytes < need || !aligned16(workspace)) return TOPO_EWORKSPACE;
+  topo::DenseLaunch L{};
+  L.q = q;
+  L.k = k;
+  L.v = v;
+  L.out = out;
+  L.ws = workspace;
+  L.B = p->B;
+  L.Hq = p->Hq;
+  L.Hkv = p->Hkv;
+  L.G = p->Hq / p->Hkv;
+  L.d = p->d;
+  L.bf16 = p->dtype == TOPO_BF16;
+  L.causal = p->causal;
+  L.n = p->n_ctx;
+  L.n_q = p->n_q;
+  L.q_pos0 = p->q_pos0;
+  L.scale = (double)p->softmax_scale;
+  return topo::launch_dense(L, stream) == hipSuccess ? TOPO_OK : TOPO_EHIP;
+}
+
+int topo_bw_probe(const void* buf, size_t bytes, uint32_t* sink, hipStream_t stream) {
+  if (!buf || !sink || !aligned16(buf) || bytes == 0 || (bytes & 15u)) return TOPO_EINVAL;
+  return topo::launch_bw_probe(buf, bytes, sink, stream) == hipSuccess ? TOPO_OK : TOPO_EHIP;
+}
+
+const char* topo_strerror(int status) {
+  switch (status) {
+    case TOPO_OK: return "ok";
+    case TOPO_EINVAL: return "invalid argument (shape, position, W/k, scale, pointer or alignment)";
+    case TOPO_EUNSUPPORTED: return "unsupported dtype or head dimension";
+    case TOPO_EWORKSPACE: return "workspace missing or smaller than topo_workspace_bytes()";
+    case TOPO_EHIP: return "HIP kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,1086 @@
+// Decode path of Topological Attention on gfx950: one query per (batch, query head).
+//
+// "The Condensate Theorem: Transformers are O(n), Not O(n^2)" (gist.science explainers of
+// arXiv 2602.06317): the condensate set of a query is the anchor (position 0), the W most recent
+// tokens and the top-k keys by Q.K^T, found again at every decoding step (zh page, technical
+// summary §3; ko page, technical summary §3 "동적 선택"); attention is the softmax over that set
+// only (fr page, technical summary §3).
+//
+// Three launches per call:
+//   decode_init    zero the per-head state.
+//   kscan          stream K once per (batch, kv head) for all G query heads of the group
+//                  (HBM bound). Fast float32 scores with a proven error bound; every wave keeps
+//                  the keys that could still be in the top-k of its run of 1024 keys, raises a
+//                  shared per-head threshold, and appends the survivors to a per-head list.
+//   decode_finish  per (batch, query head): exact k-th threshold over the survivors, float64
+//                  re-scoring of the short list, exact top-k by (score desc, position asc), set
+//                  assembly, float64 softmax and V reduction over the set.
+#include "topo_device.h"
+#include "topo_internal.h"
+
+// Tuning: blocks of the key scan that must fit on one CU (bounds its registers), and whether its
+// loads carry the non-temporal hint.
+#ifndef TOPO_KS_MIN_BLOCKS
+#define TOPO_KS_MIN_BLOCKS 2
+#endif
+#ifndef TOPO_KS_NT
+#define TOPO_KS_NT 1
+#endif
+
+namespace topo {
+
+// ---------------------------------------------------------------------------------------------
+// Error bound of the fast scores. The bf16 path sums exact products with v_dot2_f32_bf16 and the
+// float32 path with fused multiply-adds, then adds the per-lane partial sums in a tree; d terms in
+// all, and every term passes through at most d + 4 roundings of at most two units each, so
+// |s_fast - s| <= 2 (d + 4) u sum_t |q_t k_t| <= 2 (d + 4) u |q| |k| (Cauchy-Schwarz), u = 2^-24.
+// The extra 2^-20 |q| |k| covers rounding the bound itself and forming s_fast +- eps in float32.
+float fast_score_eps_coef(int d) { return (float)(2.0 * (d + 4) * 0x1p-24 + 0x1p-20); }
+
+static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+static int64_t scan_blocks(const QueryGeom& g) { return (g.scan_hi + KS_KEYS_PER_BLOCK) / KS_KEYS_PER_BLOCK; }
+static int64_t scan_slot(int32_t k) { return k + 32 < KS_WAVE_CAP ? k + 32 : KS_WAVE_CAP; }
+
+// Number of survivor-list levels: merge until the last level fits the finishing kernel's LDS.
+static int survivor_levels(int64_t nblk0, int64_t slot, int64_t (&nblk)[MAX_LEVELS]) {
+  int L = 0;
+  nblk[L++] = nblk0;
+  while (nblk[L - 1] * slot > SURV_LDS && L < MAX_LEVELS) {
+    nblk[L] = (nblk[L - 1] + MERGE_FAN - 1) / MERGE_FAN;
+    ++L;
+  }
+  return L;
+}
+
+size_t decode_workspace_bytes(int32_t B, int32_t Hq, const QueryGeom& g, int32_t k) {
+  const size_t heads = (size_t)B * Hq;
+  const int64_t slot = scan_slot(k);
+  int64_t nb[MAX_LEVELS];
+  const int L = survivor_levels(scan_blocks(g), slot, nb);
+  size_t bytes = align256(heads * sizeof(HeadState));
+  for (int l = 0; l < L; ++l)
+    bytes += 2 * align256(heads * (size_t)nb[l] * 4) + align256(heads * (size_t)nb[l] * (size_t)slot * sizeof(uint2));
+  return bytes;
+}
+
+void decode_carve(void* ws, int32_t B, int32_t Hq, const QueryGeom& g, int32_t k, DecodeLaunch& L) {
+  const size_t heads = (size_t)B * Hq;
+  L.slot = scan_slot(k);
+  L.nlevels = survivor_levels(scan_blocks(g), L.slot, L.nblk);
+  char* p = (char*)ws;
+  L.st = (HeadState*)p;
+  p += align256(heads * sizeof(HeadState));
+  for (int l = 0; l < L.nlevels; ++l) {
+    L.blk_cnt[l] = (uint32_t*)p;
+    p += align256(heads * (size_t)L.nblk[l] * 4);
+    L.blk_eps[l] = (float*)p;
+    p += align256(heads * (size_t)L.nblk[l] * 4);
+    L.surv[l] = (uint2*)p;
+    p += align256(heads * (size_t)L.nblk[l] * (size_t)L.slot * sizeof(uint2));
+  }
+}
+
+__global__ void decode_init_kernel(HeadState* st, int nheads) {
+  int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < nheads) {
+    st[i].theta = 0u;
+    st[i].overflow = 0u;
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// Cross-lane moves. partner<HALF> pairs every lane of a group of 2*HALF lanes with a lane of the
+// other half of that group (quad permutes and row mirrors are DPP modifiers, free on the add).
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+template <int HALF>
+__device__ __forceinline__ float partner(float x) {
+  if constexpr (HALF == 1) return dpp_f32<0xB1>(x);        // quad_perm [1,0,3,2]
+  else if constexpr (HALF == 2) return dpp_f32<0x4E>(x);   // quad_perm [2,3,0,1]
+  else if constexpr (HALF == 4) return dpp_f32<0x141>(x);  // row_half_mirror
+  else if constexpr (HALF == 8) return dpp_f32<0x140>(x);  // row_mirror
+  else return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x401F));  // xor 16
+}
+
+// One halving step of a reduce-scatter: the lanes of each half of a 2*HALF group keep their half
+// of the remaining keys, summed with the partner's copy.
+template <int HALF, int V, int L>
+__device__ __forceinline__ void rs_step(float (&A)[V][L], bool hi) {
+#pragma unroll
+  for (int v = 0; v < V; ++v) {
+#pragma unroll
+    for (int t = 0; t < HALF; ++t) {
+      const float x0 = A[v][t] + partner<HALF>(A[v][t]);
+      const float x1 = A[v][t + HALF] + partner<HALF>(A[v][t + HALF]);
+      A[v][t] = hi ? x1 : x0;
+    }
+  }
+}
+
+// A[v][m] holds this lane's partial sum of value v for key m of its L-lane group. Afterwards
+// A[v][0] holds the full sum of value v for key m = (lane % L).
+template <int L, int V>
+__device__ __forceinline__ void reduce_scatter(float (&A)[V][L], int s) {
+  if constexpr (L >= 32) rs_step<16, V, L>(A, (s & 16) != 0);
+  if constexpr (L >= 16) rs_step<8, V, L>(A, (s & 8) != 0);
+  rs_step<4, V, L>(A, (s & 4) != 0);
+  rs_step<2, V, L>(A, (s & 2) != 0);
+  rs_step<1, V, L>(A, (s & 1) != 0);
+}
+
+// k-th largest value among the `n` register entries of every lane (0 = empty): the largest T
+// with at least k entries >= T; 0 if fewer than k entries are non-zero.
+template <int N>
+__device__ __forceinline__ uint32_t wave_kth_largest(const uint32_t (&x)[N], int k) {
+  uint32_t T = 0;
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t cand = T | (1u << bit);
+    int c = 0;
+#pragma unroll
+    for (int i = 0; i < N; ++i) c += __popcll(__ballot(x[i] >= cand));
+    if (c >= k) T = cand;
+  }
+  return T;
+}
+
+// A threshold T such that at least k distinct entries are >= T, computed from N register entries
+// per lane (0 = empty). For k <= 64 it is the k-th largest of every lane's two largest entries,
+// which is a valid bound at a fraction of the cost of the exact k-th largest; for larger k the
+// exact k-th largest. 0 if fewer than k entries are non-zero.
+template <int N>
+__device__ __forceinline__ uint32_t wave_threshold(const uint32_t (&x)[N], int k) {
+  if (k <= 64 && N > 2) {
+    uint32_t m[2] = {0u, 0u};
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      m[1] = max(m[1], min(m[0], x[i]));
+      m[0] = max(m[0], x[i]);
+    }
+    return wave_kth_largest<2>(m, k);
+  }
+  return wave_kth_largest<N>(x, k);
+}
+
+// ---------------------------------------------------------------------------------------------
+// kscan: grid (nblk, B*Hkv, ceil(G/GT)), 256 threads = 4 waves. Wave w of block x ranks keys
+// [4096 x + 1024 w, +1024) for the GT query heads of its slice.
+//
+// A key row of RB bytes is spread over L = RB/16 lanes (one 16-byte chunk each), so every load
+// instruction is fully coalesced and each lane keeps only its chunk of the GT queries in
+// registers. Partial dot products of 64 keys are combined by a reduce-scatter over the L lanes,
+// after which every lane owns one key. Each wave keeps the keys that may be in the top-k of its
+// run, the block merges its four waves' survivors into one list per head, and a shared per-head
+// threshold lets later blocks drop keys that can no longer be selected.
+struct KscanArgs {
+  const unsigned char* k;
+  const unsigned char* q;
+  HeadState* st;
+  uint32_t* blk_cnt;
+  float* blk_eps;
+  uint2* surv;
+  int64_t n, nblk, slot;
+  int64_t p, w_lo, vis_hi, scan_hi;
+  int32_t Hq, Hkv, G, topk;
+  float eps_coef;
+};
+
+// Loads of one 64-key tile. The 64 lanes form 8 groups of 8; group r handles keys 8i + r of the
+// tile (i = 0..7) and lane s of a group holds 16-byte chunks c*8 + s (c < CPL) of each of them:
+// every load instruction reads eight 128-byte line-aligned half rows.
+template <int RB>
+__device__ __forceinline__ void kscan_load(uint4 (&buf)[8][RB / 128], const unsigned char* kb, int64_t row0,
+                                           int64_t last_row, int lane) {
+  constexpr int CPL = RB / 128;
+  const int r = lane >> 3, s = lane & 7;
+  if (row0 + 63 <= last_row) {
+    // Whole tile in range: one base pointer, constant offsets, no branches.
+    const unsigned char* base = kb + (row0 + r) * RB + s * 16;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) {
+        const unsigned char* p = base + (size_t)i * 8 * RB + c * 128;
+        buf[i][c] = TOPO_KS_NT ? ntload16(p) : *(const uint4*)p;
+      }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int64_t row = row0 + 8 * i + r;
+#pragma unroll
+      for (int c = 0; c < CPL; ++c)
+        buf[i][c] = row <= last_row ? ntload16(kb + row * RB + c * 128 + s * 16) : make_uint4(0u, 0u, 0u, 0u);
+    }
+  }
+}
+
+template <int RB, int GT, bool BF16>
+__global__ __launch_bounds__(256, TOPO_KS_MIN_BLOCKS) void kscan_kernel(KscanArgs a) {
+  constexpr int L = 8;          // lanes per key row
+  constexpr int CPL = RB / 128; // 16-byte chunks of a row per lane
+  __shared__ uint2 wbuf[KS_WAVES][GT][KS_WAVE_CAP];
+  __shared__ int wcnt[KS_WAVES][GT];
+  __shared__ float weps[KS_WAVES][GT];
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, s = lane & 7;
+  const int grp = blockIdx.y;
+  const int b = grp / a.Hkv, g = grp - b * a.Hkv;
+  const int slice0 = blockIdx.z * GT;
+  const int h0 = g * a.G + slice0;
+  const int nh = min(GT, a.G - slice0);
+
+  // This lane's chunks of every query of the slice, and |q_h| (float64 sum over the 8 lanes).
+  uint4 qv[GT][CPL];
+  float qn[GT];
+#pragma unroll
+  for (int h = 0; h < GT; ++h) {
+    double part = 0.0;
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+      qv[h][c] = h < nh ? *(const uint4*)(a.q + ((size_t)b * a.Hq + h0 + h) * RB + c * 128 + s * 16)
+                        : make_uint4(0u, 0u, 0u, 0u);
+      const uint32_t w4[4] = {qv[h][c].x, qv[h][c].y, qv[h][c].z, qv[h][c].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if constexpr (BF16) {
+          const double lo = bf16_lo(w4[e]), hi = bf16_hi(w4[e]);
+          part += lo * lo + hi * hi;
+        } else {
+          const double x = __uint_as_float(w4[e]);
+          part += x * x;
+        }
+      }
+    }
+    for (int o = 1; o < L; o <<= 1) part += __shfl_xor(part, o);
+    qn[h] = (float)sqrt(part) * (1.0f + 0x1p-20f);
+  }
+
+  const int64_t key0 = (int64_t)blockIdx.x * KS_KEYS_PER_BLOCK + (int64_t)wave * KS_KEYS_PER_WAVE;
+  const unsigned char* kb = a.k + (size_t)grp * (size_t)a.n * RB;
+  const int64_t last_row = a.scan_hi;
+  const int64_t my_off = 8 * s + (lane >> 3);  // key of this lane within a tile after the reduction
+
+  float sc[GT][KS_IT];
+  uint32_t vmask = 0;
+  float cmax2[CPL];  // largest squared norm of the chunks this lane has loaded, per chunk slot
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) cmax2[c] = 0.f;
+
+  // One tile in registers. Per head: partial dot products of this lane's chunks of the 8 keys
+  // of its group, then a reduce-scatter over the 8 lanes; the scores enter a register shift
+  // queue (sc[h][KS_IT-1] is the newest) so that every register index stays static. The next
+  // tile's loads are issued once this tile's chunks are consumed.
+  uint4 kv[8][CPL];
+  kscan_load<RB>(kv, kb, key0, last_row, lane);
+#pragma unroll 1
+  for (int it = 0; it < KS_IT; ++it) {
+#pragma unroll
+    for (int h = 0; h < GT; ++h) {
+      float P[1][8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        float acc = 0.f;
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) acc = dot_chunk<BF16>(kv[i][c], qv[h][c], acc);
+        P[0][i] = acc;
+      }
+      reduce_scatter<8, 1>(P, s);
+#pragma unroll
+      for (int i = 0; i + 1 < KS_IT; ++i) sc[h][i] = sc[h][i + 1];
+      sc[h][KS_IT - 1] = P[0][0];
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) cmax2[c] = fmaxf(cmax2[c], dot_chunk<BF16>(kv[i][c], kv[i][c], 0.f));
+    if (it + 1 < KS_IT) kscan_load<RB>(kv, kb, key0 + (int64_t)(it + 1) * KS_ROWS, last_row, lane);
+    const int64_t j = key0 + (int64_t)it * KS_ROWS + my_off;
+    const bool valid = j >= 1 && j <= a.vis_hi && (j < a.w_lo || j > a.p);
+    vmask = (vmask >> 1) | ((valid ? 1u : 0u) << (KS_IT - 1));
+  }
+
+  // Norm bound of every key of this wave: |k|^2 = sum over its chunks of |chunk|^2 <= sum over
+  // the chunk slots (c, s) of the largest |chunk|^2 seen in that slot (lanes with equal s share
+  // the slots). The float32 chunk norms carry relative error below 2^-19, covered by the factor.
+  float kbound2 = 0.f;
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) {
+    float m = cmax2[c];
+    for (int o = L; o < 64; o <<= 1) m = fmaxf(m, __shfl_xor(m, o));
+    kbound2 += m;
+  }
+  for (int o = 1; o < L; o <<= 1) kbound2 += __shfl_xor(kbound2, o);
+  const float kmax = sqrtf(kbound2) * (1.0f + 0x1p-16f);
+  const bool any_valid = __ballot(vmask != 0u) != 0ull;
+
+#pragma unroll
+  for (int h = 0; h < GT; ++h) {
+    if (h >= nh) break;
+    const float eps = a.eps_coef * qn[h] * kmax + 1e-30f;
+    int total = 0;
+    if (any_valid) {
+      const HeadState* hs = a.st + (size_t)b * a.Hq + h0 + h;
+      // A stale value is still a valid bound: the shared threshold only ever rises.
+      const uint32_t th_g = *(volatile const uint32_t*)&hs->theta;
+      // Local threshold: k distinct keys of this run have lower bounds at or above T.
+      uint32_t lb[KS_IT];
+#pragma unroll
+      for (int it = 0; it < KS_IT; ++it) lb[it] = ((vmask >> it) & 1u) ? ord_f32(sc[h][it] - eps) : 0u;
+      const uint32_t T = wave_threshold<KS_IT>(lb, a.topk);
+      const uint32_t th = max(T, th_g);
+      // Hand this run's survivors (upper bound at or above the threshold) to the block merge.
+#pragma unroll
+      for (int it = 0; it < KS_IT; ++it) {
+        const bool ok = ((vmask >> it) & 1u) && ord_f32(sc[h][it] + eps) >= th;
+        const uint64_t m = __ballot(ok);
+        if (ok) {
+          const int pos = total + lanes_below(m);
+          if (pos < KS_WAVE_CAP)
+            wbuf[wave][h][pos] = make_uint2(__float_as_uint(sc[h][it]), (uint32_t)(key0 + (int64_t)it * KS_ROWS + my_off));
+        }
+        total += __popcll(m);
+      }
+    }
+    if (lane == 0) {
+      wcnt[wave][h] = total;
+      weps[wave][h] = any_valid ? eps : 0.f;
+    }
+  }
+  __syncthreads();
+
+  // Block merge: wave h merges the four waves' survivors of query head h.
+  if (wave >= nh) return;
+  const int h = wave;
+  const size_t head = (size_t)b * a.Hq + h0 + h;
+  HeadState* hs = a.st + head;
+  const size_t bslot = head * (size_t)a.nblk + blockIdx.x;
+  static_assert(KS_WAVES == 4, "the block merge below is written for four waves");
+  const int c0 = wcnt[0][h], c1 = wcnt[1][h], c2 = wcnt[2][h], c3 = wcnt[3][h];
+  const float eps_b = fmaxf(fmaxf(weps[0][h], weps[1][h]), fmaxf(weps[2][h], weps[3][h]));
+  const bool over = c0 > KS_WAVE_CAP || c1 > KS_WAVE_CAP || c2 > KS_WAVE_CAP || c3 > KS_WAVE_CAP;
+  const int p1 = c0, p2 = c0 + c1, p3 = c0 + c1 + c2;
+  const int total = p3 + c3;
+  if (over) {
+    if (lane == 0) {
+      a.blk_cnt[bslot] = KS_OVERFLOW;
+      hs->overflow = 1u;
+    }
+    return;
+  }
+  // Entries are read from LDS on every pass (few registers stay live).
+  auto entry = [&](int idx) -> uint2 {
+    const int w = (idx >= p1) + (idx >= p2) + (idx >= p3);
+    const int i = idx - (w == 0 ? 0 : w == 1 ? p1 : w == 2 ? p2 : p3);
+    return wbuf[w][h][i];
+  };
+  auto lbkey = [&](int idx) -> uint32_t {
+    return idx < total ? ord_f32(__uint_as_float(entry(idx).x) - eps_b) : 0u;
+  };
+  constexpr int PER = KS_WAVES * KS_WAVE_CAP / 64;
+  uint32_t T = 0;
+  if (total >= a.topk) {
+    if (a.topk <= 64) {
+      uint32_t m[2] = {0u, 0u};
+      for (int r = 0; r < PER; ++r) {
+        const uint32_t x = lbkey(lane + 64 * r);
+        m[1] = max(m[1], min(m[0], x));
+        m[0] = max(m[0], x);
+      }
+      T = wave_kth_largest<2>(m, a.topk);
+    } else {
+      for (int bit = 31; bit >= 0; --bit) {
+        const uint32_t cand = T | (1u << bit);
+        int c = 0;
+        for (int r = 0; r < PER; ++r) c += __popcll(__ballot(lbkey(lane + 64 * r) >= cand));
+        if (c >= a.topk) T = cand;
+      }
+    }
+  }
+  const uint32_t th_g = *(volatile const uint32_t*)&hs->theta;
+  const uint32_t th = max(T, th_g);
+  uint2* out = a.surv + bslot * (size_t)a.slot;
+  int cnt = 0;
+  for (int r = 0; r < PER; ++r) {
+    const int idx = lane + 64 * r;
+    const uint2 e = idx < total ? entry(idx) : make_uint2(0u, 0u);
+    const bool ok = idx < total && ord_f32(__uint_as_float(e.x) + eps_b) >= th;
+    const uint64_t m = __ballot(ok);
+    if (ok) {
+      const int pos = cnt + lanes_below(m);
+      if (pos < a.slot) out[pos] = e;
+    }
+    cnt += __popcll(m);
+  }
+  if (lane == 0) {
+    if (cnt > a.slot) {
+      a.blk_cnt[bslot] = KS_OVERFLOW;
+      hs->overflow = 1u;
+    } else {
+      a.blk_cnt[bslot] = (uint32_t)cnt;
+    }
+    a.blk_eps[bslot] = eps_b;
+    if (T > th_g) atomicMax(&hs->theta, T);
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// merge_lists: one wave per (group of MERGE_FAN survivor lists, head). Keeps the entries of the
+// group that may still be in the top-k: the k-th best lower bound of the group (or the shared
+// threshold, if higher) against every entry's upper bound, with the largest error bound of the
+// group for all of them. Output has the same layout, one list per group.
+struct MergeArgs {
+  const HeadState* st;
+  HeadState* st_w;
+  const uint32_t* cnt_in;
+  const float* eps_in;
+  const uint2* surv_in;
+  uint32_t* cnt_out;
+  float* eps_out;
+  uint2* surv_out;
+  int64_t nblk_in, nblk_out, slot;
+  int32_t topk;
+};
+
+__global__ __launch_bounds__(64) void merge_lists_kernel(MergeArgs a) {
+  constexpr int PER = MERGE_FAN * KS_WAVE_CAP / 64;
+  const int lane = threadIdx.x;
+  const size_t head = blockIdx.y;
+  const int64_t g0 = (int64_t)blockIdx.x * MERGE_FAN;
+  const int nin = (int)min((int64_t)MERGE_FAN, a.nblk_in - g0);
+  const size_t in0 = head * (size_t)a.nblk_in + g0;
+  const size_t oslot = head * (size_t)a.nblk_out + blockIdx.x;
+  uint32_t c = 0;
+  float e = 0.f;
+  if (lane < nin) {
+    c = a.cnt_in[in0 + lane];
+    e = a.eps_in[in0 + lane];
+  }
+  const bool over = __ballot(c == KS_OVERFLOW) != 0ull;
+  if (over) {
+    if (lane == 0) {
+      a.cnt_out[oslot] = KS_OVERFLOW;
+      a.eps_out[oslot] = 0.f;
+      a.st_w[head].overflow = 1u;
+    }
+    return;
+  }
+  const float eps = wave_max_f32(e);
+  const int incl = wave_incl_scan_i32((int)c);
+  const int total = __shfl(incl, 63);
+  int pre[MERGE_FAN];  // start of list i in the flat order
+#pragma unroll
+  for (int i = 0; i < MERGE_FAN; ++i) pre[i] = i == 0 ? 0 : __shfl(incl, i - 1);
+  uint2 ent[PER];
+  uint32_t lbk[PER];
+#pragma unroll
+  for (int r = 0; r < PER; ++r) {
+    const int f = lane + 64 * r;
+    ent[r] = make_uint2(0u, 0u);
+    if (f < total) {
+      int w = 0;
+#pragma unroll
+      for (int i = 1; i < MERGE_FAN; ++i) w += f >= pre[i] && i < nin;
+      int base = 0;
+#pragma unroll
+      for (int i = 0; i < MERGE_FAN; ++i) base = i == w ? pre[i] : base;
+      ent[r] = a.surv_in[(in0 + w) * (size_t)a.slot + (f - base)];
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < PER; ++r) lbk[r] = lane + 64 * r < total ? ord_f32(__uint_as_float(ent[r].x) - eps) : 0u;
+  const uint32_t T = total >= a.topk ? wave_threshold<PER>(lbk, a.topk) : 0u;
+  const uint32_t th = max(T, a.st[head].theta);
+  uint2* out = a.surv_out + oslot * (size_t)a.slot;
+  int cnt = 0;
+#pragma unroll
+  for (int r = 0; r < PER; ++r) {
+    const bool ok = lane + 64 * r < total && ord_f32(__uint_as_float(ent[r].x) + eps) >= th;
+    const uint64_t m = __ballot(ok);
+    if (ok) {
+      const int pos = cnt + lanes_below(m);
+      if (pos < a.slot) out[pos] = ent[r];
+    }
+    cnt += __popcll(m);
+  }
+  if (lane == 0) {
+    if (cnt > a.slot) {
+      a.cnt_out[oslot] = KS_OVERFLOW;
+      a.st_w[head].overflow = 1u;
+    } else {
+      a.cnt_out[oslot] = (uint32_t)cnt;
+    }
+    a.eps_out[oslot] = eps;
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// decode_finish: one block of 512 threads per (batch, query head).
+//   1. Stage the head's scan survivors in LDS (every load in flight at once), as order keys of
+//      their lower and upper score bounds.
+//   2. Exact k-th largest lower bound by an 11 + 11 + 10 bit radix select in LDS; the short list
+//      is every survivor whose upper bound reaches it (it holds the whole top-k).
+//   3. Float64 canonical scores of the short list; exact ranks by (score desc, position asc).
+//   4. The set {0} u window u top-k, ascending; float64 scores of the anchor and window rows.
+//   5. Float64 softmax over the set and the weighted sum of the V rows.
+// Ties crowding the short list, overflowing scan blocks, k above the scan's limit and the
+// TOPO_FLAG_EXACT_SELECT flag all route to an exact radix select over every candidate instead.
+constexpr int FIN_THREADS = 512;
+constexpr int FIN_WAVES = FIN_THREADS / 64;
+constexpr int PRE_CAP = 2048;    // survivor lists whose counts are prefix-summed in LDS
+
+struct FinishArgs {
+  const unsigned char* q;
+  const unsigned char* k;
+  const unsigned char* v;
+  float* out;
+  int32_t* sel_idx;
+  int32_t* sel_count;
+  const HeadState* st;
+  const uint32_t* blk_cnt;
+  const float* blk_eps;
+  const uint2* surv;
+  int64_t n, nblk, slot;
+  int64_t p, w_lo, vis_hi, scan_hi, n_cand;
+  int32_t Hq, Hkv, G, W, topk, set_cap, flags;
+  double scale;
+  float eps_coef;
+};
+
+struct FinishSmem {
+  double qd[128];
+  union {
+    struct {                       // phases 1-2
+      uint32_t lbk[SURV_LDS];
+      uint32_t ubk[SURV_LDS];
+      int32_t sidx[SURV_LDS];
+      uint32_t pre[PRE_CAP + 1];
+    } s;
+    struct {                       // phases 3-5
+      int32_t tidx[MAX_SET];       // the top-k part (any order)
+      double ts[MAX_SET];
+      int32_t cidx[MAX_SET];       // the set, ascending
+      double cw[MAX_SET];          // its scores, then its softmax weights
+    } c;
+  } u;
+  uint32_t hist[2048];
+  int32_t ridx[REFINE_CAP];
+  double rs[REFINE_CAP];
+  double red[FIN_WAVES * 128];
+  double scratch[FIN_WAVES];
+  int32_t ival[8];
+};
+
+// One wave finds, scanning bins from the top, the bin where the running count reaches `need`.
+// Writes the bin (or -1) and the count strictly above it into sm->ival[0..1].
+__device__ void find_bin_from_top(FinishSmem* sm, int nbins, int64_t need) {
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    int64_t above = 0;
+    int found = -1;
+    for (int top = nbins - 1; top >= 0 && found < 0; top -= 64) {
+      const int bin = top - lane;
+      const int c = bin >= 0 ? (int)sm->hist[bin] : 0;
+      const int incl = wave_incl_scan_i32(c);  // lane 0 = highest bin of this chunk
+      const uint64_t hit = __ballot(above + incl >= need && c > 0);
+      if (hit) {
+        const int l = __builtin_ctzll(hit);
+        const int excl = __shfl(incl - c, l);
+        found = top - l;
+        above += excl;
+      } else {
+        above += __shfl(incl, 63);
+      }
+    }
+    if (lane == 0) {
+      sm->ival[0] = found;
+      sm->ival[1] = (int)above;
+    }
+  }
+  __syncthreads();
+}
+
+// Kept out of line: each call site then reuses one register allocation for the row and the query.
+template <int D, bool BF16>
+__device__ __attribute__((noinline)) double score_row(const FinishSmem* sm, const unsigned char* kb, int64_t j) {
+  constexpr int RB = D * (BF16 ? 2 : 4);
+  return canonical_score_row<BF16, D>(sm->qd, kb + (size_t)j * RB);
+}
+
+__device__ __forceinline__ bool is_candidate(const FinishArgs& a, int64_t j) {
+  return j >= 1 && j <= a.vis_hi && (j < a.w_lo || j > a.p);
+}
+
+// Exact selection over every candidate by float64 radix select on the canonical scores
+// (8 passes of 8 bits), then collection in ascending position so that equal scores resolve to
+// the lower positions. With take_all, every candidate is collected. Returns |T| (in tidx/ts).
+template <int D, bool BF16>
+__device__ int exact_select(FinishSmem* sm, const FinishArgs& a, const unsigned char* kb, bool take_all) {
+  const int tid = threadIdx.x;
+  uint64_t prefix = 0;
+  int64_t need = a.topk;  // how many of the keys equal to the final value must be taken
+  if (!take_all) {
+    for (int pass = 0; pass < 8; ++pass) {
+      const int shift = 56 - 8 * pass;
+      for (int i = tid; i < 256; i += FIN_THREADS) sm->hist[i] = 0;
+      __syncthreads();
+      for (int64_t j = 1 + tid; j <= a.scan_hi; j += FIN_THREADS) {
+        if (!is_candidate(a, j)) continue;
+        const uint64_t key = ord_f64(score_row<D, BF16>(sm, kb, j));
+        if (pass == 0 || (key >> (shift + 8)) == prefix) atomicAdd(&sm->hist[(key >> shift) & 255u], 1u);
+      }
+      __syncthreads();
+      find_bin_from_top(sm, 256, need);
+      const int digit = sm->ival[0];
+      const int above = sm->ival[1];
+      __syncthreads();
+      prefix = (prefix << 8) | (uint64_t)(digit < 0 ? 0 : digit);
+      need -= above;
+    }
+  }
+  // prefix = order key of the k-th best score: take every key above it and the `need` lowest
+  // positions among the keys equal to it.
+  if (tid == 0) {
+    sm->ival[2] = 0;
+    sm->ival[3] = 0;  // equal keys met so far
+  }
+  __syncthreads();
+  for (int64_t j0 = 1; j0 <= a.scan_hi; j0 += FIN_THREADS) {
+    const int64_t j = j0 + tid;
+    const bool is_c = j <= a.scan_hi && is_candidate(a, j);
+    double s = 0.0;
+    bool gt = false, eq = false;
+    if (is_c) {
+      s = score_row<D, BF16>(sm, kb, j);
+      if (take_all) {
+        gt = true;
+      } else {
+        const uint64_t key = ord_f64(s);
+        gt = key > prefix;
+        eq = key == prefix;
+      }
+    }
+    const uint64_t em = __ballot(eq);
+    const int w = tid >> 6;
+    __syncthreads();
+    if ((tid & 63) == 0) sm->hist[w] = __popcll(em);
+    __syncthreads();
+    int before = sm->ival[3];
+    for (int i = 0; i < w; ++i) before += sm->hist[i];
+    const int eq_rank = before + lanes_below(em);
+    if (gt || (eq && eq_rank < need)) {
+      const int slot = atomicAdd(&sm->ival[2], 1);
+      if (slot < MAX_SET) {
+        sm->u.c.tidx[slot] = (int32_t)j;
+        sm->u.c.ts[slot] = s;
+      }
+    }
+    __syncthreads();
+    if (tid == 0) {
+      int tot = 0;
+      for (int i = 0; i < FIN_WAVES; ++i) tot += sm->hist[i];
+      sm->ival[3] += tot;
+    }
+    __syncthreads();
+  }
+  const int nt = sm->ival[2];
+  __syncthreads();
+  return nt < MAX_SET ? nt : MAX_SET;
+}
+
+// Stage the survivors of head bh into LDS. Returns their number, or -1 if they do not fit.
+__device__ int stage_survivors(FinishSmem* sm, const FinishArgs& a, int bh) {
+  const int tid = threadIdx.x;
+  const int64_t nblk = a.nblk;
+  if (nblk > PRE_CAP) return -1;
+  const uint32_t* bc = a.blk_cnt + (size_t)bh * nblk;
+  const float* be = a.blk_eps + (size_t)bh * nblk;
+  const uint2* sv = a.surv + (size_t)bh * nblk * a.slot;
+  for (int i = tid; i < nblk; i += FIN_THREADS) {
+    const uint32_t c = bc[i];
+    sm->u.s.pre[i + 1] = c > (uint32_t)a.slot ? 0u : c;
+  }
+  __syncthreads();
+  if (tid < 64) {  // inclusive scan of the counts, 64 blocks at a time
+    uint32_t carry = 0;
+    for (int base = 0; base < nblk; base += 64) {
+      const int i = base + tid;
+      const uint32_t c = i < nblk ? sm->u.s.pre[i + 1] : 0u;
+      const uint32_t incl = (uint32_t)wave_incl_scan_i32((int)c) + carry;
+      if (i < nblk) sm->u.s.pre[i + 1] = incl;
+      carry = __shfl(incl, 63);
+    }
+    if (tid == 0) sm->u.s.pre[0] = 0;
+  }
+  __syncthreads();
+  const int M = (int)sm->u.s.pre[nblk];
+  if (M > SURV_LDS) return -1;
+  // Each thread copies entries f = tid, tid + 512, ... in batches of 8 independent loads.
+  constexpr int BATCH = 8;
+  for (int f0 = tid; f0 < M; f0 += FIN_THREADS * BATCH) {
+    uint2 e[BATCH];
+    float eps[BATCH];
+#pragma unroll
+    for (int u = 0; u < BATCH; ++u) {
+      const int f = f0 + u * FIN_THREADS;
+      e[u] = make_uint2(0u, 0u);
+      eps[u] = 0.f;
+      if (f < M) {
+        int lo = 0, hi = (int)nblk;  // largest bi with pre[bi] <= f
+        while (hi - lo > 1) {
+          const int mid = (lo + hi) >> 1;
+          if (sm->u.s.pre[mid] <= (uint32_t)f) lo = mid; else hi = mid;
+        }
+        e[u] = sv[(size_t)lo * a.slot + (f - sm->u.s.pre[lo])];
+        eps[u] = be[lo];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < BATCH; ++u) {
+      const int f = f0 + u * FIN_THREADS;
+      if (f < M) {
+        const float sf = __uint_as_float(e[u].x);
+        sm->u.s.lbk[f] = ord_f32(sf - eps[u]);
+        sm->u.s.ubk[f] = ord_f32(sf + eps[u]);
+        sm->u.s.sidx[f] = (int32_t)e[u].y;
+      }
+    }
+  }
+  __syncthreads();
+  return M;
+}
+
+template <int D, bool BF16>
+__global__ __launch_bounds__(FIN_THREADS) void decode_finish_kernel(FinishArgs a) {
+  constexpr int RB = D * (BF16 ? 2 : 4);
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  FinishSmem* sm = (FinishSmem*)smem_raw;
+  const int tid = threadIdx.x;
+  const int bh = blockIdx.x;
+  const int b = bh / a.Hq, h = bh - b * a.Hq, g = h / a.G;
+  const unsigned char* kb = a.k + ((size_t)b * a.Hkv + g) * (size_t)a.n * RB;
+  const unsigned char* vb = a.v + ((size_t)b * a.Hkv + g) * (size_t)a.n * RB;
+  const unsigned char* qrow = a.q + (size_t)bh * RB;
+
+  if (tid < D) sm->qd[tid] = load_elem_f64<BF16>(qrow, tid);
+  // (stage_survivors below starts with a barrier-protected phase, so qd is visible after it)
+
+  const int64_t w_lo = a.w_lo, p = a.p;
+  const int anchor = w_lo > 0 ? 1 : 0;
+  const int nwin = (int)(p - w_lo + 1);
+
+  // ---- the top-k part T; the short list R (fast path) is scored together with the anchor and
+  // window rows, so that all float64 row scores cost one memory round trip.
+  int nt = 0;
+  bool fast = false;
+  int nr = 0;
+  bool exact = false, take_all = false;
+  if (a.topk > 0 && a.n_cand > 0) {
+    const uint32_t st_theta = a.st[bh].theta, st_over = a.st[bh].overflow;
+    exact = (a.flags & 1) != 0 || st_over != 0 || a.topk > KS_MAX_K;
+    take_all = a.n_cand <= a.topk;
+    if (!take_all && !exact) {
+      const int M = stage_survivors(sm, a, bh);
+      if (M < a.topk) {
+        exact = true;  // more survivors than LDS holds (or, impossibly, fewer than k)
+      } else {
+        // A valid threshold: the k-th largest of every thread's two best lower bounds.
+        uint32_t m0 = 0u, m1 = 0u;
+        for (int f = tid; f < M; f += FIN_THREADS) {
+          const uint32_t x = sm->u.s.lbk[f];
+          m1 = max(m1, min(m0, x));
+          m0 = max(m0, x);
+        }
+        sm->hist[2 * tid] = m0;
+        sm->hist[2 * tid + 1] = m1;
+        __syncthreads();
+        if (tid < 64) {
+          uint32_t x[2 * FIN_THREADS / 64];
+#pragma unroll
+          for (int i = 0; i < 2 * FIN_THREADS / 64; ++i) x[i] = sm->hist[tid + 64 * i];
+          const uint32_t T = wave_kth_largest<2 * FIN_THREADS / 64>(x, a.topk);
+          if (tid == 0) sm->ival[5] = (int)T;
+        }
+        if (tid == 0) sm->ival[4] = 0;
+        __syncthreads();
+        const uint32_t T = (uint32_t)sm->ival[5];
+        const uint32_t theta = T > st_theta ? T : st_theta;
+        for (int f = tid; f < M; f += FIN_THREADS) {
+          if (sm->u.s.ubk[f] >= theta) {
+            const int slot = atomicAdd(&sm->ival[4], 1);
+            if (slot < REFINE_CAP) sm->ridx[slot] = sm->u.s.sidx[f];
+          }
+        }
+        __syncthreads();
+        nr = sm->ival[4];
+        if (nr > REFINE_CAP || nr < a.topk) exact = true; else fast = true;
+      }
+      __syncthreads();
+    }
+  }
+  __syncthreads();
+
+  // Row scores: [0, nr) short list (fast path), then the window, then the anchor.
+  const int nscore = (fast ? nr : 0) + nwin + anchor;
+  for (int i = tid; i < nscore; i += FIN_THREADS) {
+    int64_t j;
+    if (fast && i < nr) j = sm->ridx[i];
+    else if (i - (fast ? nr : 0) < nwin) j = w_lo + (i - (fast ? nr : 0));
+    else j = 0;
+    const double sc = score_row<D, BF16>(sm, kb, j);
+    if (fast && i < nr) sm->rs[i] = sc;
+    else if (i - (fast ? nr : 0) < nwin) sm->u.c.cw[MAX_SET - nwin - 1 + (i - (fast ? nr : 0))] = sc;  // parked
+    else sm->u.c.cw[MAX_SET - 1] = sc;
+  }
+  __syncthreads();
+  if (fast) {
+    // exact rank of each short-list entry: higher score first, then lower position
+    for (int i = tid; i < nr; i += FIN_THREADS) {
+      const double si = sm->rs[i];
+      const int32_t ji = sm->ridx[i];
+      int rank = 0;
+      for (int r = 0; r < nr; ++r) {
+        const double sr = sm->rs[r];
+        rank += (sr > si) || (sr == si && sm->ridx[r] < ji);
+      }
+      if (rank < a.topk) {
+        sm->u.c.tidx[rank] = ji;
+        sm->u.c.ts[rank] = si;
+      }
+    }
+    nt = a.topk;
+  } else if (a.topk > 0 && a.n_cand > 0) {
+    nt = exact_select<D, BF16>(sm, a, kb, take_all);
+  }
+  __syncthreads();
+
+  // ---- set assembly: C = {0} u window u T, ascending
+  const int count = anchor + nwin + nt;
+  int tlo_local = 0;
+  for (int i = tid; i < nt; i += FIN_THREADS) tlo_local += sm->u.c.tidx[i] < w_lo;
+  tlo_local = wave_sum_i32(tlo_local);
+  if ((tid & 63) == 0) sm->hist[tid >> 6] = tlo_local;
+  __syncthreads();
+  int tlo = 0;
+  for (int i = 0; i < FIN_WAVES; ++i) tlo += sm->hist[i];
+  // window and anchor scores move from their parking slots (the tail of cw, beyond every final
+  // position: count <= 1 + W + k <= MAX_SET - 1 and the parked rows are read before overwritten)
+  double wsc[(MAX_SET + FIN_THREADS - 1) / FIN_THREADS];
+  double asc = 0.0;
+  int nw_mine = 0;
+  for (int i = tid; i < nwin; i += FIN_THREADS) wsc[nw_mine++] = sm->u.c.cw[MAX_SET - nwin - 1 + i];
+  if (anchor) asc = sm->u.c.cw[MAX_SET - 1];
+  __syncthreads();
+  if (anchor && tid == 0) {
+    sm->u.c.cidx[0] = 0;
+    sm->u.c.cw[0] = asc;
+  }
+  for (int i = tid; i < nt; i += FIN_THREADS) {
+    const int32_t t = sm->u.c.tidx[i];
+    int below = 0;
+    for (int r = 0; r < nt; ++r) below += sm->u.c.tidx[r] < t;
+    const int pos = anchor + below + (t > p ? nwin : 0);
+    sm->u.c.cidx[pos] = t;
+    sm->u.c.cw[pos] = sm->u.c.ts[i];
+  }
+  nw_mine = 0;
+  for (int i = tid; i < nwin; i += FIN_THREADS) {
+    const int pos = anchor + tlo + i;
+    sm->u.c.cidx[pos] = (int32_t)(w_lo + i);
+    sm->u.c.cw[pos] = wsc[nw_mine++];
+  }
+  __syncthreads();
+
+  if (a.sel_idx) {
+    int32_t* dst = a.sel_idx + (size_t)bh * a.set_cap;
+    for (int i = tid; i < a.set_cap; i += FIN_THREADS) dst[i] = i < count ? sm->u.c.cidx[i] : -1;
+  }
+  if (a.sel_count && tid == 0) a.sel_count[bh] = count;
+  if (!a.out) return;
+
+  // ---- softmax over the set (float64) and the weighted sum of the V rows
+  double zmax = -INFINITY;
+  for (int i = tid; i < count; i += FIN_THREADS) zmax = fmax(zmax, a.scale * sm->u.c.cw[i]);
+  zmax = block_max_f64<FIN_WAVES>(zmax, sm->scratch);
+  double zsum = 0.0;
+  for (int i = tid; i < count; i += FIN_THREADS) {
+    const double w = exp(a.scale * sm->u.c.cw[i] - zmax);
+    sm->u.c.cw[i] = w;
+    zsum += w;
+  }
+  zsum = block_sum_f64<FIN_WAVES>(zsum, sm->scratch);  // (contains a barrier: weights visible)
+
+  // Thread t reads 16-byte chunk (t % CPR) of rows t / CPR, + RPP, ...; a batch of BATCH rows
+  // per thread is in flight together (one batch covers a set of up to RPP * BATCH rows).
+  constexpr int CPR = RB / 16;             // chunks per row
+  constexpr int EPC = BF16 ? 8 : 4;        // elements per chunk
+  constexpr int RPP = FIN_THREADS / CPR;   // rows per pass
+  constexpr int BATCH = 20;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int c = tid % CPR, r0 = tid / CPR;
+  double acc[EPC];
+#pragma unroll
+  for (int e = 0; e < EPC; ++e) acc[e] = 0.0;
+  for (int i0 = r0; i0 < count; i0 += RPP * BATCH) {
+    uint4 ch[BATCH];
+#pragma unroll
+    for (int u = 0; u < BATCH; ++u) {
+      const int i = i0 + u * RPP;
+      ch[u] = i < count ? *(const uint4*)(vb + (size_t)sm->u.c.cidx[i] * RB + c * 16) : make_uint4(0u, 0u, 0u, 0u);
+    }
+#pragma unroll
+    for (int u = 0; u < BATCH; ++u) {
+      const int i = i0 + u * RPP;
+      const double w = i < count ? sm->u.c.cw[i] : 0.0;
+      const uint32_t ws[4] = {ch[u].x, ch[u].y, ch[u].z, ch[u].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if constexpr (BF16) {
+          acc[2 * e] = fma(w, (double)bf16_lo(ws[e]), acc[2 * e]);
+          acc[2 * e + 1] = fma(w, (double)bf16_hi(ws[e]), acc[2 * e + 1]);
+        } else {
+          acc[e] = fma(w, (double)__uint_as_float(ws[e]), acc[e]);
+        }
+      }
+    }
+  }
+  // lanes of a wave that share a chunk: lane % CPR
+#pragma unroll
+  for (int e = 0; e < EPC; ++e)
+    for (int o = CPR; o < 64; o <<= 1) acc[e] += __shfl_xor(acc[e], o);
+  if (lane < CPR) {
+#pragma unroll
+    for (int e = 0; e < EPC; ++e) sm->red[wave * D + lane * EPC + e] = acc[e];
+  }
+  __syncthreads();
+  if (tid < D) {
+    double num = 0.0;
+    for (int w = 0; w < FIN_WAVES; ++w) num += sm->red[w * D + tid];
+    a.out[(size_t)bh * D + tid] = (float)(num / zsum);
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+template <int RB, int GT, bool BF16>
+static hipError_t launch_kscan_t(const KscanArgs& ka, dim3 grid, hipStream_t s) {
+  hipLaunchKernelGGL((kscan_kernel<RB, GT, BF16>), grid, dim3(256), 0, s, ka);
+  return hipGetLastError();
+}
+
+template <int RB, bool BF16>
+static hipError_t launch_kscan_g(const KscanArgs& ka, int GT, dim3 grid, hipStream_t s) {
+  switch (GT) {
+    case 1: return launch_kscan_t<RB, 1, BF16>(ka, grid, s);
+    case 2: return launch_kscan_t<RB, 2, BF16>(ka, grid, s);
+    default: return launch_kscan_t<RB, 4, BF16>(ka, grid, s);
+  }
+}
+
+template <int D, bool BF16>
+static hipError_t launch_finish_t(const FinishArgs& fa, int nbh, hipStream_t s) {
+  const size_t smem = sizeof(FinishSmem);
+  static bool attr_set = false;  // idempotent; setting it twice is harmless
+  if (!attr_set) {
+    (void)hipFuncSetAttribute((const void*)decode_finish_kernel<D, BF16>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+    attr_set = true;
+  }
+  hipLaunchKernelGGL((decode_finish_kernel<D, BF16>), dim3(nbh), dim3(FIN_THREADS), smem, s, fa);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode(const DecodeLaunch& L, hipStream_t stream) {
+  const int nbh = L.B * L.Hq;
+  hipLaunchKernelGGL(decode_init_kernel, dim3((nbh + 255) / 256), dim3(256), 0, stream, L.st, nbh);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+
+  const QueryGeom& g = L.geom;
+  const bool need_scan = L.topk > 0 && L.topk <= KS_MAX_K && g.n_cand > L.topk && !(L.flags & 1);
+  if (need_scan) {
+    KscanArgs ka;
+    ka.k = (const unsigned char*)L.k;
+    ka.q = (const unsigned char*)L.q;
+    ka.st = L.st;
+    ka.blk_cnt = L.blk_cnt[0];
+    ka.blk_eps = L.blk_eps[0];
+    ka.surv = L.surv[0];
+    ka.n = L.n;
+    ka.nblk = L.nblk[0];
+    ka.slot = L.slot;
+    ka.p = g.p;
+    ka.w_lo = g.w_lo;
+    ka.vis_hi = g.vis_hi;
+    ka.scan_hi = g.scan_hi;
+    ka.Hq = L.Hq;
+    ka.Hkv = L.Hkv;
+    ka.G = L.G;
+    ka.topk = L.topk;
+    ka.eps_coef = L.eps_coef;
+    const int GT = L.G >= 4 ? 4 : L.G;
+    dim3 grid((unsigned)L.nblk[0], (unsigned)(L.B * L.Hkv),
+              (unsigned)((L.G + GT - 1) / GT));
+    const int RB = L.d * (L.bf16 ? 2 : 4);
+    if (L.bf16) {
+      e = RB == 256 ? launch_kscan_g<256, true>(ka, GT, grid, stream) : launch_kscan_g<128, true>(ka, GT, grid, stream);
+    } else {
+      e = RB == 256 ? launch_kscan_g<256, false>(ka, GT, grid, stream) : launch_kscan_g<512, false>(ka, GT, grid, stream);
+    }
+    if (e != hipSuccess) return e;
+    for (int l = 0; l + 1 < L.nlevels; ++l) {
+      MergeArgs ma;
+      ma.st = L.st;
+      ma.st_w = L.st;
+      ma.cnt_in = L.blk_cnt[l];
+      ma.eps_in = L.blk_eps[l];
+      ma.surv_in = L.surv[l];
+      ma.cnt_out = L.blk_cnt[l + 1];
+      ma.eps_out = L.blk_eps[l + 1];
+      ma.surv_out = L.surv[l + 1];
+      ma.nblk_in = L.nblk[l];
+      ma.nblk_out = L.nblk[l + 1];
+      ma.slot = L.slot;
+      ma.topk = L.topk;
+      hipLaunchKernelGGL(merge_lists_kernel, dim3((unsigned)L.nblk[l + 1], (unsigned)nbh), dim3(64), 0, stream, ma);
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+  }
+
+  const int last = L.nlevels - 1;
+  FinishArgs fa;
+  fa.q = (const unsigned char*)L.q;
+  fa.k = (const unsigned char*)L.k;
+  fa.v = (const unsigned char*)L.v;
+  fa.out = L.out;
+  fa.sel_idx = L.sel_idx;
+  fa.sel_count = L.sel_count;
+  fa.st = L.st;
+  fa.blk_cnt = L.blk_cnt[last];
+  fa.blk_eps = L.blk_eps[last];
+  fa.surv = L.surv[last];
+  fa.n = L.n;
+  fa.nblk = L.nblk[last];
+  fa.slot = L.slot;
+  fa.p = g.p;
+  fa.w_lo = g.w_lo;
+  fa.vis_hi = g.vis_hi;
+  fa.scan_hi = g.scan_hi;
+  fa.n_cand = g.n_cand;
+  fa.Hq = L.Hq;
+  fa.Hkv = L.Hkv;
+  fa.G = L.G;
+  fa.W = L.W;
+  fa.topk = L.topk;
+  fa.set_cap = 1 + L.W + L.topk;
+  fa.flags = L.flags;
+  fa.scale = L.scale;
+  fa.eps_coef = L.eps_coef;
+  if (L.bf16) {
+    return L.d == 128 ? launch_finish_t<128, true>(fa, nbh, stream) : launch_finish_t<64, true>(fa, nbh, stream);
+  }
+  return L.d == 128 ? launch_finish_t<128, false>(fa, nbh, stream) : launch_finish_t<64, false>(fa, nbh, stream);
+}
+
+}  // namespace topo

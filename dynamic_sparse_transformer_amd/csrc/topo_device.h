@@ -1,0 +1,195 @@
+// Device helpers shared by the gfx950 kernels of libtopo_attn.so: bf16 unpacking, 16-byte
+// chunk dot products, order-preserving integer keys for floating point values, wave and block
+// reductions. Wavefronts are 64 lanes wide.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#define TOPO_WAVE 64
+
+namespace topo {
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+// 16-byte streaming load (global_load_dwordx4 ... nt): the data is read once, so it should not
+// displace reusable lines from the caches.
+__device__ __forceinline__ uint4 ntload16(const void* p) {
+  const u32x4_t v = __builtin_nontemporal_load((const u32x4_t*)p);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+// bf16 pair packed in a 32-bit word: element 0 in the low half.
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// acc + sum of the 8 products of two 16-byte chunks of bf16 (v_dot2_f32_bf16: two products and
+// an add per instruction, float32 accumulate).
+__device__ __forceinline__ float dot_chunk_bf16(uint4 a, uint4 b, float acc) {
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a.x), __builtin_bit_cast(bf16x2_t, b.x), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a.y), __builtin_bit_cast(bf16x2_t, b.y), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a.z), __builtin_bit_cast(bf16x2_t, b.z), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a.w), __builtin_bit_cast(bf16x2_t, b.w), acc, false);
+  return acc;
+}
+
+// acc + sum of the 4 products of two 16-byte chunks of float32 (fused multiply-adds).
+__device__ __forceinline__ float dot_chunk_f32(uint4 a, uint4 b, float acc) {
+  acc = fmaf(__uint_as_float(a.x), __uint_as_float(b.x), acc);
+  acc = fmaf(__uint_as_float(a.y), __uint_as_float(b.y), acc);
+  acc = fmaf(__uint_as_float(a.z), __uint_as_float(b.z), acc);
+  acc = fmaf(__uint_as_float(a.w), __uint_as_float(b.w), acc);
+  return acc;
+}
+
+template <bool BF16>
+__device__ __forceinline__ float dot_chunk(uint4 a, uint4 b, float acc) {
+  if constexpr (BF16) return dot_chunk_bf16(a, b, acc);
+  else return dot_chunk_f32(a, b, acc);
+}
+
+// Order-preserving maps: a < b (as numbers, -0 == +0 excluded) <=> key(a) < key(b) (unsigned).
+__device__ __forceinline__ uint32_t ord_f32(float x) {
+  uint32_t u = __float_as_uint(x);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ uint64_t ord_f64(double x) {
+  x = x + 0.0;  // -0 -> +0 so that equal scores share one key
+  uint64_t u = (uint64_t)__double_as_longlong(x);
+  return (u & 0x8000000000000000ull) ? ~u : (u | 0x8000000000000000ull);
+}
+
+// Element t of a row stored as float32 or bf16, widened to double (exact).
+template <bool BF16>
+__device__ __forceinline__ double load_elem_f64(const void* row, int t) {
+  if constexpr (BF16) {
+    uint16_t b = ((const uint16_t*)row)[t];
+    return (double)__uint_as_float((uint32_t)b << 16);
+  } else {
+    return (double)((const float*)row)[t];
+  }
+}
+
+// Canonical score: sum over t of q_t * k_t in float64, ascending t, starting from +0.0.
+// The product of two float32 (or bf16) values is exact in float64, so fma(q, k, s) rounds once,
+// exactly like s + (q*k).
+template <bool BF16, int D>
+__device__ __forceinline__ double canonical_score(const double* qd, const void* krow) {
+  double s = 0.0;
+  if constexpr (BF16) {
+    const uint4* p = (const uint4*)krow;
+#pragma unroll 2
+    for (int c = 0; c < D / 8; ++c) {
+      uint4 w = p[c];
+      uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        s = fma(qd[c * 8 + 2 * e], (double)bf16_lo(ws[e]), s);
+        s = fma(qd[c * 8 + 2 * e + 1], (double)bf16_hi(ws[e]), s);
+      }
+    }
+  } else {
+    const uint4* p = (const uint4*)krow;
+#pragma unroll 2
+    for (int c = 0; c < D / 4; ++c) {
+      uint4 w = p[c];
+      s = fma(qd[c * 4 + 0], (double)__uint_as_float(w.x), s);
+      s = fma(qd[c * 4 + 1], (double)__uint_as_float(w.y), s);
+      s = fma(qd[c * 4 + 2], (double)__uint_as_float(w.z), s);
+      s = fma(qd[c * 4 + 3], (double)__uint_as_float(w.w), s);
+    }
+  }
+  return s + 0.0;
+}
+
+// Same value as canonical_score, with every 16-byte chunk of the row requested before the first
+// multiply-add so that the row costs one memory round trip.
+template <bool BF16, int D>
+__device__ __forceinline__ double canonical_score_row(const double* qd, const void* krow) {
+  constexpr int NC = D * (BF16 ? 2 : 4) / 16;
+  const uint4* p = (const uint4*)krow;
+  uint4 w[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) w[c] = p[c];
+  double s = 0.0;
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    const uint32_t ws[4] = {w[c].x, w[c].y, w[c].z, w[c].w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if constexpr (BF16) {
+        s = fma(qd[c * 8 + 2 * e], (double)bf16_lo(ws[e]), s);
+        s = fma(qd[c * 8 + 2 * e + 1], (double)bf16_hi(ws[e]), s);
+      } else {
+        s = fma(qd[c * 4 + e], (double)__uint_as_float(ws[e]), s);
+      }
+    }
+  }
+  return s + 0.0;
+}
+
+__device__ __forceinline__ float wave_max_f32(float x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
+  return x;
+}
+__device__ __forceinline__ double wave_sum_f64(double x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
+  return x;
+}
+__device__ __forceinline__ double wave_max_f64(double x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x = fmax(x, __shfl_xor(x, o));
+  return x;
+}
+__device__ __forceinline__ int wave_sum_i32(int x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
+  return x;
+}
+// Inclusive prefix sum over the lanes of a wave.
+__device__ __forceinline__ int wave_incl_scan_i32(int x) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    int y = __shfl_up(x, o);
+    if (lane >= o) x += y;
+  }
+  return x;
+}
+
+// Number of set bits of `mask` below this lane.
+__device__ __forceinline__ int lanes_below(uint64_t mask) {
+  return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+}
+
+// Block-wide reductions through a caller-provided LDS scratch of (blockDim.x / 64) entries.
+// Every thread of the block must call them; all threads get the result.
+template <int NWAVES>
+__device__ __forceinline__ double block_max_f64(double x, double* scratch) {
+  x = wave_max_f64(x);
+  const int w = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) scratch[w] = x;
+  __syncthreads();
+  double r = scratch[0];
+#pragma unroll
+  for (int i = 1; i < NWAVES; ++i) r = fmax(r, scratch[i]);
+  return r;
+}
+template <int NWAVES>
+__device__ __forceinline__ double block_sum_f64(double x, double* scratch) {
+  x = wave_sum_f64(x);
+  const int w = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) scratch[w] = x;
+  __syncthreads();
+  double r = 0.0;
+#pragma unroll
+  for (int i = 0; i < NWAVES; ++i) r += scratch[i];
+  return r;
+}
+
+}  // namespace topo

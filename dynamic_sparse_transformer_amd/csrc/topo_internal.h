@@ -1,0 +1,122 @@
+// Internal interfaces between the C-ABI front end (topo_api.hip) and the kernel files.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+
+namespace topo {
+
+// Decode key scan geometry: a tile is 64 keys (one owned by each lane after the cross-lane
+// reduction), a wave ranks KS_IT tiles, a block of KS_WAVES waves ranks KS_KEYS_PER_BLOCK keys and
+// merges the survivors of its waves.
+constexpr int KS_ROWS = 64;
+constexpr int KS_IT = 8;
+constexpr int KS_WAVES = 4;
+constexpr int KS_KEYS_PER_WAVE = KS_ROWS * KS_IT;
+constexpr int KS_KEYS_PER_BLOCK = KS_KEYS_PER_WAVE * KS_WAVES;
+constexpr int KS_MAX_K = 224;     // largest k the scan ranks (larger k: exact selection only)
+constexpr int KS_WAVE_CAP = 256;  // survivors one wave may hand to its block merge
+constexpr int MAX_SET = 4096;     // largest 1 + W + k
+constexpr int REFINE_CAP = 1024;  // largest short list re-scored in float64 by the fast path
+constexpr uint32_t KS_OVERFLOW = 0xFFFFFFFFu;
+constexpr int MERGE_FAN = 8;      // survivor lists merged into one per merge step
+constexpr int MAX_LEVELS = 8;
+constexpr int SURV_LDS = 8192;    // survivors the finishing kernel stages in LDS
+
+// Per (batch, query head) state shared by the key scan blocks, one 128-byte line per head.
+struct alignas(128) HeadState {
+  uint32_t theta;     // order key of a proven lower bound of the k-th best candidate score
+  uint32_t overflow;  // 1 if some block had more survivors than its slot holds
+  uint32_t pad[30];
+};
+
+// Where one query sits and which keys are its candidates.
+struct QueryGeom {
+  int64_t p;        // query position
+  int64_t w_lo;     // first window position: max(0, p - W + 1)
+  int64_t vis_hi;   // last visible key: p (causal) or n - 1
+  int64_t scan_hi;  // last key the scan must look at (candidates lie in [1, scan_hi])
+  int64_t n_cand;   // number of candidates
+};
+
+inline QueryGeom make_geom(int64_t p, int64_t n, int32_t W, bool causal) {
+  QueryGeom g;
+  g.p = p;
+  g.w_lo = p - (int64_t)W + 1 > 0 ? p - (int64_t)W + 1 : 0;
+  g.vis_hi = causal ? p : n - 1;
+  int64_t wlo1 = g.w_lo > 1 ? g.w_lo : 1;
+  int64_t win_nonzero = p >= wlo1 ? p - wlo1 + 1 : 0;
+  g.n_cand = g.vis_hi - win_nonzero;
+  g.scan_hi = g.vis_hi > p ? g.vis_hi : g.w_lo - 1;
+  if (g.scan_hi < 0) g.scan_hi = 0;
+  return g;
+}
+
+struct DecodeLaunch {
+  const void* q;
+  const void* k;
+  const void* v;
+  float* out;          // may be null (select only)
+  int32_t* sel_idx;    // may be null
+  int32_t* sel_count;  // may be null
+  HeadState* st;       // [B * Hq]
+  // Survivor lists, level 0 written by the key scan and level l+1 by merging groups of
+  // MERGE_FAN level-l lists:
+  //   blk_cnt[l] [B * Hq][nblk[l]]        survivors of each list (or KS_OVERFLOW)
+  //   blk_eps[l] [B * Hq][nblk[l]]        error bound of the fast scores in that list
+  //   surv[l]    [B * Hq][nblk[l]][slot]  (float bits of the fast score, key index)
+  uint32_t* blk_cnt[MAX_LEVELS];
+  float* blk_eps[MAX_LEVELS];
+  uint2* surv[MAX_LEVELS];
+  int64_t nblk[MAX_LEVELS];
+  int nlevels;
+  int64_t slot;
+  int32_t B, Hq, Hkv, G, d, W, topk, bf16, flags;
+  int64_t n;
+  QueryGeom geom;
+  double scale;
+  float eps_coef;
+};
+
+size_t decode_workspace_bytes(int32_t B, int32_t Hq, const QueryGeom& g, int32_t k);
+// Carve the workspace into the HeadState array and the survivor lists.
+void decode_carve(void* ws, int32_t B, int32_t Hq, const QueryGeom& g, int32_t k, DecodeLaunch& L);
+hipError_t launch_decode(const DecodeLaunch& L, hipStream_t stream);
+
+// Float32 error-bound coefficient of the fast scores: |s_fast - s| <= coef * |q|_2 * |k|_2.
+float fast_score_eps_coef(int d);
+
+// Dense attention (pillar layer).
+struct DenseLaunch {
+  const void* q;
+  const void* k;
+  const void* v;
+  float* out;
+  void* ws;
+  int32_t B, Hq, Hkv, G, d, bf16, causal;
+  int64_t n, n_q, q_pos0;
+  double scale;
+};
+size_t dense_workspace_bytes(int32_t B, int32_t Hq, int64_t n_q, int64_t n, int32_t d);
+hipError_t launch_dense(const DenseLaunch& L, hipStream_t stream);
+
+// Many-query (prefill) path.
+struct PrefillLaunch {
+  const void* q;
+  const void* k;
+  const void* v;
+  float* out;
+  int32_t* sel_idx;
+  int32_t* sel_count;
+  void* ws;
+  int32_t B, Hq, Hkv, G, d, W, topk, bf16, causal, flags;
+  int64_t n, n_q, q_pos0;
+  double scale;
+  float eps_coef;
+};
+size_t prefill_workspace_bytes(int32_t B, int32_t Hq, int64_t n_q, int64_t n, int32_t d, int32_t W, int32_t k);
+hipError_t launch_prefill(const PrefillLaunch& L, hipStream_t stream);
+
+hipError_t launch_bw_probe(const void* buf, size_t bytes, uint32_t* sink, hipStream_t stream);
+
+}  // namespace topo

@@ -1,0 +1,139 @@
+/*
+ * topo_attn.h — C ABI of the MI355X (gfx950) Topological Attention library, libtopo_attn.so.
+ *
+ * The operation. "The Condensate Theorem: Transformers are O(n), Not O(n^2)" (gist.science
+ * explainers of arXiv 2602.06317) defines, for every query position i, a condensate set C_i made
+ * of three parts: the anchor at position 0 (the attention sink), a local window of the W most
+ * recent tokens, and the k positions with the highest Q.K^T scores, found again at every step
+ * (zh page, technical summary §3 "研究方法"; fr page, technical summary §2; ko page, technical
+ * summary §3 "동적 선택"). Topological Attention computes the softmax only over the positions in
+ * C_i and sums their V rows with those weights (fr page, technical summary §3). The method swaps
+ * only the attention operation of a frozen model (plug-and-play, zh technical summary §3), so
+ * this interface takes the same tensors as an attention call: Q, the K and V caches, W, k and
+ * the causal mask; it returns the output and the index set it used.
+ *
+ * Arithmetic (where the pages are silent, this library fixes one reading):
+ *   score    s_j = sum_t q_t * k_{j,t}, the exact products summed in float64 in ascending t.
+ *            The library ranks with fast float32 scores and re-scores the short list of possible
+ *            members this way, so the index set is the one this definition gives.
+ *   window   positions max(0, p-W+1) .. p (the query's own position p included).
+ *   top-k    over the candidates: visible positions outside the anchor and the window. Higher
+ *            score first, on equal scores the lower position first. If there are at most k
+ *            candidates, all of them are taken.
+ *   softmax  float64 on z_j = softmax_scale * s_j; the output is rounded once to float32.
+ *   GQA      query head h reads kv head h / (Hq / Hkv) and selects its own set.
+ *   visible  causal: positions 0..p; otherwise 0..n_ctx-1 (the window still ends at p).
+ *
+ * Layouts (row-major, contiguous, element strides implied by the shapes):
+ *   q        [B, Hq, n_q, d]        dtype of the call (float32 or bfloat16)
+ *   k, v     [B, Hkv, n_ctx, d]     same dtype
+ *   out      [B, Hq, n_q, d]        float32
+ *   sel_idx  [B, Hq, n_q, 1+W+k]    int32, the set in ascending order, padded with -1
+ *   sel_count[B, Hq, n_q]           int32, |C_i| = number of valid entries of sel_idx
+ * Query i of a call sits at position q_pos0 + i.
+ *
+ * Ownership and execution. Every pointer argument is a device pointer owned by the caller
+ * (q, k, v, out, sel_idx, sel_count, workspace), 16-byte aligned. The library never allocates or
+ * frees device memory, keeps no mutable global state, and is safe to call from several host
+ * threads on different streams with different workspaces. Calls are asynchronous on `stream`:
+ * a return of TOPO_OK means every kernel was launched; faults surface at the caller's next
+ * synchronisation. Arguments are validated before anything is launched, so on an error return
+ * nothing has been written. The workspace must hold topo_workspace_bytes() bytes for the same
+ * parameters and operation; its contents on entry do not matter and are scratch afterwards.
+ * Two calls that run concurrently must not share a workspace.
+ */
+#ifndef TOPO_ATTN_H
+#define TOPO_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes (negative on error). */
+#define TOPO_OK            0
+#define TOPO_EINVAL       -1   /* bad shape, position, W, k, scale, pointer or alignment      */
+#define TOPO_EUNSUPPORTED -2   /* dtype or head dimension this build has no kernels for       */
+#define TOPO_EWORKSPACE   -3   /* workspace NULL or smaller than topo_workspace_bytes()       */
+#define TOPO_EHIP         -4   /* a kernel launch failed (hipGetLastError after the launch)   */
+
+/* Element type of q, k and v. The output is always float32. */
+#define TOPO_F32  0
+#define TOPO_BF16 1
+
+/* Operations, for topo_workspace_bytes(). */
+#define TOPO_OP_DECODE  0
+#define TOPO_OP_PREFILL 1
+#define TOPO_OP_SELECT  2
+#define TOPO_OP_DENSE   3
+
+/* Largest condensate set (1 + W + k) a call may ask for. */
+#define TOPO_MAX_SET 4096
+
+/* Flag bits of topo_params_t.flags. */
+#define TOPO_FLAG_EXACT_SELECT 1  /* skip the float32 pre-ranking and select every query by the
+                                     exact float64 radix path (slow; for checking)             */
+
+typedef struct {
+    int32_t B;              /* batch                                                     >= 1 */
+    int32_t Hq;             /* query heads                                               >= 1 */
+    int32_t Hkv;            /* kv heads; Hq % Hkv == 0                                   >= 1 */
+    int32_t d;              /* head dimension: 64 or 128                                      */
+    int64_t n_ctx;          /* keys per (batch, kv head), 1 .. 2^31-1                         */
+    int64_t n_q;            /* queries per (batch, head): decode 1; prefill 1 .. n_ctx        */
+    int64_t q_pos0;         /* position of query 0; q_pos0 + n_q - 1 <= n_ctx - 1             */
+    int32_t W;              /* window length                                             >= 0 */
+    int32_t k;              /* top-k size                                                >= 0 */
+    int32_t causal;         /* 1: query at p sees keys 0..p; 0: it sees all n_ctx keys        */
+    float   softmax_scale;  /* > 0 and finite (1/sqrt(d), or a temperature over sqrt(d))      */
+    int32_t dtype;          /* TOPO_F32 or TOPO_BF16                                          */
+    int32_t flags;          /* TOPO_FLAG_* bits, 0 normally                                   */
+} topo_params_t;
+
+/* Workspace bytes that the operation needs for these parameters (0 if they are invalid). */
+size_t topo_workspace_bytes(const topo_params_t* p, int op);
+
+/* Topological attention of one query per (batch, query head): n_q == 1, the query at position
+ * q_pos0 (the newest token of a decode step is q_pos0 = n_ctx - 1). Writes out, and sel_idx /
+ * sel_count unless they are NULL. Condensate set and softmax as above (zh technical summary §3;
+ * fr technical summary §3). */
+int topo_attn_decode(const topo_params_t* p, const void* q, const void* k, const void* v,
+                     float* out, int32_t* sel_idx, int32_t* sel_count,
+                     void* workspace, size_t ws_bytes, hipStream_t stream);
+
+/* Topological attention of n_q consecutive queries per (batch, query head), query i at position
+ * q_pos0 + i (a whole causal prompt is q_pos0 = 0, n_q = n_ctx). Same outputs as decode, one row
+ * per query (zh technical summary §3). */
+int topo_attn_prefill(const topo_params_t* p, const void* q, const void* k, const void* v,
+                      float* out, int32_t* sel_idx, int32_t* sel_count,
+                      void* workspace, size_t ws_bytes, hipStream_t stream);
+
+/* The condensate sets only (the selection of decode or prefill, chosen by n_q == 1 or not),
+ * without the softmax and V reduction. sel_idx and sel_count must not be NULL. */
+int topo_select(const topo_params_t* p, const void* q, const void* k,
+                int32_t* sel_idx, int32_t* sel_count,
+                void* workspace, size_t ws_bytes, hipStream_t stream);
+
+/* Dense softmax attention over every visible key (W and k are ignored): the full-attention
+ * layers the zh page keeps in a few "pillar" layers (technical summary §3) and the comparator of
+ * the exactness claim (technical summary §2). float32 scores and accumulation for bfloat16
+ * inputs, float64 for float32 inputs. Any n_q; writes out. */
+int topo_attn_dense(const topo_params_t* p, const void* q, const void* k, const void* v,
+                    float* out, void* workspace, size_t ws_bytes, hipStream_t stream);
+
+/* Measurement helper, not part of the method: streams `bytes` (a multiple of 16) from `buf`
+ * once with the same load path as the decode key scan and reduces them into `sink`
+ * (one uint32, device memory), so the achievable read bandwidth can be timed next to it. */
+int topo_bw_probe(const void* buf, size_t bytes, uint32_t* sink, hipStream_t stream);
+
+/* Static description of a status code. */
+const char* topo_strerror(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TOPO_ATTN_H */

@@ -1,0 +1,68 @@
+"""Shared helpers of the GPU parity tests: device upload and the comparison bar."""
+from __future__ import annotations
+
+import numpy as np
+
+# Tolerances: float32 inputs |gpu - oracle| <= 1e-6 + 2e-6 |oracle|; bf16 inputs relative 1e-2.
+F32_ATOL, F32_RTOL = 1e-6, 2e-6
+BF16_RTOL = 1e-2
+
+
+def torch_cuda():
+    import pytest
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.fail("a GPU test ran without a GPU")
+    return torch
+
+
+def to_device(arr: np.ndarray, dtype: str):
+    """numpy storage array (float32 or uint16 bf16 bits) -> contiguous device tensor."""
+    torch = torch_cuda()
+    if dtype == "bf16":
+        t = torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).view(torch.bfloat16)
+    else:
+        t = torch.from_numpy(np.ascontiguousarray(arr, dtype=np.float32))
+    return t.cuda()
+
+
+def assert_out_close(gpu: np.ndarray, ref: np.ndarray, dtype: str, what: str = ""):
+    gpu = np.asarray(gpu, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert np.all(np.isfinite(gpu)), f"{what}: non-finite output"
+    if dtype == "bf16":
+        bad = np.abs(gpu - ref) > BF16_RTOL * np.abs(ref) + 1e-6
+    else:
+        bad = np.abs(gpu - ref) > F32_ATOL + F32_RTOL * np.abs(ref)
+    if bad.any():
+        i = np.argwhere(bad)[0]
+        raise AssertionError(f"{what}: {bad.sum()} outputs off, first at {tuple(i)}: gpu {gpu[tuple(i)]!r} "
+                             f"oracle {ref[tuple(i)]!r}")
+
+
+def assert_sets_equal(sel_gpu: np.ndarray, cnt_gpu: np.ndarray, sel_ref: np.ndarray, cnt_ref: np.ndarray,
+                      what: str = ""):
+    if not np.array_equal(cnt_gpu, cnt_ref):
+        i = np.argwhere(cnt_gpu != cnt_ref)[0]
+        raise AssertionError(f"{what}: count differs at {tuple(i)}: gpu {cnt_gpu[tuple(i)]} oracle {cnt_ref[tuple(i)]}")
+    if not np.array_equal(sel_gpu, sel_ref):
+        i = np.argwhere(sel_gpu != sel_ref)[0]
+        raise AssertionError(f"{what}: set differs at {tuple(i)}: gpu {sel_gpu[tuple(i)[:-1]]} "
+                             f"oracle {sel_ref[tuple(i)[:-1]]}")
+
+
+def check_set_structure(sel: np.ndarray, cnt: np.ndarray, p: int, W: int, k: int, n_cand: int):
+    """Invariants every returned set must satisfy (any size): count, anchor, window, order, padding."""
+    S = sel.shape[-1]
+    want = min(p + 1, 1 + W + k) if n_cand >= 0 else None
+    flat_sel = sel.reshape(-1, S)
+    flat_cnt = cnt.reshape(-1)
+    assert np.all(flat_cnt == want), (np.unique(flat_cnt), want)
+    c = flat_cnt[0]
+    assert np.all(flat_sel[:, c:] == -1)
+    body = flat_sel[:, :c]
+    assert np.all(np.diff(body, axis=1) > 0)
+    assert np.all(body[:, 0] == 0)
+    w_lo = max(0, p - W + 1)
+    assert np.all(body[:, c - (p - w_lo + 1):] == np.arange(w_lo, p + 1))
+    assert np.all(body <= p)

@@ -1,0 +1,95 @@
+"""The C-ABI library without a GPU: it loads, exports every entry point that include/topo_attn.h
+declares, agrees with the binding on the parameter struct layout, and rejects bad arguments on the
+host before anything is launched (no compute calls here)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import dynamic_sparse_transformer_amd as topo
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "topo_attn.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(topo_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    lib = topo.load_library()
+    names = declared_functions()
+    assert set(names) == set(topo.EXPORTS)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_params_layout_matches_header(tmp_path):
+    src = tmp_path / "layout.c"
+    src.write_text("""
+#include <stdio.h>
+#include <stddef.h>
+#include "topo_attn.h"
+int main(void) {
+  printf("%zu %zu %zu %zu %zu %zu %zu %zu\\n", sizeof(topo_params_t), offsetof(topo_params_t, n_ctx),
+         offsetof(topo_params_t, q_pos0), offsetof(topo_params_t, W), offsetof(topo_params_t, softmax_scale),
+         offsetof(topo_params_t, dtype), offsetof(topo_params_t, flags), offsetof(topo_params_t, causal));
+  return 0;
+}
+""")
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(ROOT, "include"), "-I", "/opt/rocm/include",
+                    str(src), "-o", str(exe)], check=True)
+    got = [int(x) for x in subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split()]
+    P = topo.TopoParams
+    want = [ctypes.sizeof(P), P.n_ctx.offset, P.q_pos0.offset, P.W.offset, P.softmax_scale.offset, P.dtype.offset,
+            P.flags.offset, P.causal.offset]
+    assert got == want
+
+
+def _p(**kw):
+    base = dict(B=1, Hq=32, Hkv=8, d=128, n_ctx=1 << 20, n_q=1, q_pos0=(1 << 20) - 1, W=512, k=64, causal=1,
+                softmax_scale=1.25, dtype=1, flags=0)
+    base.update(kw)
+    return topo.TopoParams(**base)
+
+
+@pytest.mark.parametrize("bad,code", [
+    (dict(d=96), -2), (dict(dtype=7), -2), (dict(Hq=30), -1), (dict(n_ctx=0), -1), (dict(q_pos0=1 << 20), -1),
+    (dict(W=-1), -1), (dict(k=4000, W=100), -1), (dict(softmax_scale=0.0), -1),
+    (dict(softmax_scale=float("inf")), -1), (dict(causal=2), -1), (dict(flags=8), -1), (dict(n_q=2), -1),
+])
+def test_decode_rejects_bad_arguments_on_host(bad, code):
+    lib = topo.load_library()
+    p = _p(**bad)
+    rc = lib.topo_attn_decode(ctypes.byref(p), None, None, None, None, None, None, None, 0, None)
+    assert rc == code
+    assert topo.topo_strerror(rc)
+
+
+def test_decode_rejects_null_and_misaligned_pointers_and_small_workspace():
+    lib = topo.load_library()
+    p = _p()
+    a = ctypes.c_void_p(1 << 40)  # never dereferenced: validation fails first
+    mis = ctypes.c_void_p((1 << 40) + 8)
+    assert lib.topo_attn_decode(ctypes.byref(p), a, None, a, a, None, None, a, 1 << 30, None) == -1
+    assert lib.topo_attn_decode(ctypes.byref(p), mis, a, a, a, None, None, a, 1 << 30, None) == -1
+    need = lib.topo_workspace_bytes(ctypes.byref(p), 0)
+    assert need > 0
+    assert lib.topo_attn_decode(ctypes.byref(p), a, a, a, a, None, None, a, need - 1, None) == -3
+    assert lib.topo_select(ctypes.byref(p), a, a, None, None, a, need, None) == -1
+
+
+def test_workspace_sizes():
+    lib = topo.load_library()
+    p = _p()
+    dec = lib.topo_workspace_bytes(ctypes.byref(p), 0)
+    assert 0 < dec < 64 << 20            # survivor lists of the 1M decode stay modest
+    assert lib.topo_workspace_bytes(ctypes.byref(p), 3) > 0
+    assert lib.topo_workspace_bytes(ctypes.byref(p), 9) == 0
+    assert lib.topo_workspace_bytes(ctypes.byref(_p(d=96)), 0) == 0
+    assert lib.topo_bw_probe(None, 16, None, None) == -1
