@@ -1,0 +1,224 @@
+#!/usr/bin/env python3
+"""Benchmark of Topological Attention decode on one MI355X.
+
+Metric: decode queries/s counted in head-tokens (one (batch, query head, query) = one query) and
+the HBM bandwidth of the key scan, the step that streams K once per decode step. The method
+recomputes the dynamic top-k of Q.K^T over every key at every step ("The Condensate Theorem:
+Transformers are O(n), Not O(n^2)", ko page, technical summary §3), so the scan of K is the
+bandwidth-bound core of the hot path.
+
+Workload (default): the 1M-token GQA decode: batch 1, 32 query heads sharing 8 kv heads, d=128,
+n = 2^20 bf16 keys, W=512, k=64, seeded synthetic inputs with a heavy anchor key and planted
+high-score keys (workloads/synth.py). A step is one topo_attn_decode call over all 32 heads,
+inputs resident in HBM. The 128K-context batch-4 decode is reported alongside.
+
+One JSON line on stdout; progress on stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X published HBM3E bandwidth
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for name in ("topo_decode.hip", "topo_device.h", "topo_internal.h"):
+        with open(os.path.join(ROOT, "dynamic_sparse_transformer_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per key-scan launch from the committed counter summary, if it was taken on the
+    current kernel source (else None)."""
+    path = os.path.join(ROOT, "profiles", "kscan_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    entry = rec.get(workload)
+    if not entry or rec.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return entry.get("hbm_bytes_per_launch")
+
+
+def run_decode_bench(cfg: int, steps: int, warmup: int):
+    import torch
+
+    import dynamic_sparse_transformer_amd as topo
+    from workloads import make_workload
+
+    t0 = time.time()
+    w = make_workload(cfg)
+    s = w.spec
+    log(f"[bench] {s.name}: generated in {time.time() - t0:.1f}s")
+
+    def dev(arr):
+        import numpy as np
+        if s.dtype == "bf16":
+            return torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(arr).cuda()
+
+    q, k, v = dev(w.q), dev(w.k), dev(w.v)
+    scale = float(s.softmax_scale)
+    ws = torch.empty(topo.topo_workspace_bytes(q, k, s.W, s.k, scale), dtype=torch.uint8, device="cuda")
+    out = torch.empty((s.B, s.Hq, 1, s.d), dtype=torch.float32, device="cuda")
+    sel = torch.empty((s.B, s.Hq, 1, 1 + s.W + s.k), dtype=torch.int32, device="cuda")
+    cnt = torch.empty((s.B, s.Hq, 1), dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step():
+        topo.topo_attn_decode(q, k, v, s.W, s.k, scale, out=out, sel_idx=sel, sel_count=cnt, workspace=ws)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # Timed region: K steps, synchronised on both sides (wall clock), plus HIP events that the
+    # library records around every key-scan launch on this stream.
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for a, b in evs:  # create the underlying HIP events
+        a.record(stream)
+        b.record(stream)
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for a, b in evs:
+        topo.topo_attn_decode_timed(q, k, v, s.W, s.k, scale, a, b, out=out, sel_idx=sel, sel_count=cnt,
+                                    workspace=ws)
+    torch.cuda.synchronize()
+    t_end = time.perf_counter()
+    ms_per_step = (t_end - t_start) * 1e3 / steps
+    scan_ms = sum(a.elapsed_time(b) for a, b in evs) / steps
+
+    n_cand = s.n_ctx - 1 - s.W                     # keys the scan must rank per (batch, kv head)
+    row_bytes = s.d * (2 if s.dtype == "bf16" else 4)
+    alg_bytes = s.B * s.Hkv * n_cand * row_bytes   # each candidate key row read once per step
+    queries = s.B * s.Hq
+    res = {
+        "spec": s, "workload": w, "ms_per_step": ms_per_step, "scan_ms": scan_ms, "alg_bytes": alg_bytes,
+        "queries": queries, "out": out.cpu().numpy()[:, :, 0], "sel": sel.cpu().numpy()[:, :, 0],
+        "cnt": cnt.cpu().numpy()[:, :, 0],
+    }
+    del q, k, v, ws
+    torch.cuda.empty_cache()
+    return res
+
+
+def cpu_baseline(res, heads: int):
+    """The CPU oracle, as it stands, on a bounded sample of the same workload: the first `heads`
+    query heads of batch 0. Also checks the GPU sets of those heads against it."""
+    import numpy as np
+
+    import oracle
+
+    w, s = res["workload"], res["spec"]
+    sample = [(0, h) for h in range(min(heads, s.Hq))]
+    q, k, v = w.f32("q"), w.f32("k"), w.f32("v")
+    t0 = time.perf_counter()
+    ro, rs, rc = oracle.topo_attn_decode(q, k, v, s.W, s.k, float(s.softmax_scale), heads=sample)
+    dt = time.perf_counter() - t0
+    idx = tuple(np.array(sample).T)
+    sets_equal = bool(np.array_equal(res["sel"][idx], rs[idx]) and np.array_equal(res["cnt"][idx], rc[idx]))
+    err = float(np.max(np.abs(res["out"][idx].astype(np.float64) - ro[idx])))
+    rel = float(np.max(np.abs(res["out"][idx].astype(np.float64) - ro[idx]) / (np.abs(ro[idx]) + 1e-30)))
+    return {
+        "value": len(sample) / dt, "unit": "queries/s", "cores": 1, "kind": "oracle",
+        "sample": f"{len(sample)} of {s.B * s.Hq} query heads of {s.name} (batch 0), {dt:.1f} s, "
+                  "numpy float64, one thread",
+    }, {"heads_checked": len(sample), "sets_bit_exact": sets_equal, "max_abs_err": err, "max_rel_err": rel}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=5, help="workload config (default 5: 1M-token GQA decode)")
+    ap.add_argument("--also", type=int, nargs="*", default=[4], help="extra decode configs reported alongside")
+    ap.add_argument("--cpu-heads", type=int, default=32, help="query heads in the CPU-oracle sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate", action="store_true",
+                    help="also run kernels of known traffic (for scaling hardware byte counters): a 2 GiB "
+                         "read-only probe and a 256 MiB device copy")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path (sharding over "
+              "(batch, kv head) is described in the design notes, not implemented).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    import dynamic_sparse_transformer_amd as topo
+    topo.load_library()  # fail loudly if the HIP library is missing
+
+    main_res = run_decode_bench(args.config, args.steps, args.warmup)
+    s = main_res["spec"]
+    also = []
+    for c in args.also or []:
+        if c == args.config:
+            continue
+        r = run_decode_bench(c, args.steps, args.warmup)
+        also.append({
+            "workload": r["spec"].name, "value": r["queries"] / (r["ms_per_step"] / 1e3), "unit": "queries/s",
+            "ms_per_step": r["ms_per_step"], "kscan_us": r["scan_ms"] * 1e3,
+            "kscan_gbs": r["alg_bytes"] / (r["scan_ms"] / 1e3) / 1e9,
+            "kscan_frac": r["alg_bytes"] / (r["scan_ms"] / 1e3) / 1e9 / HBM_PEAK_GBS,
+        })
+
+    if args.calibrate:
+        # Known traffic: the probe reads every byte of a 2 GiB buffer once; the copy reads and
+        # writes 256 MiB. Counter readings of these kernels give the bytes-per-count factors.
+        buf = torch.empty(1 << 31, dtype=torch.uint8, device="cuda").fill_(1)
+        sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+        src = torch.empty(1 << 28, dtype=torch.uint8, device="cuda").fill_(2)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            topo.topo_bw_probe(buf, sink)
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del buf, src, dst
+
+    achieved = main_res["alg_bytes"] / (main_res["scan_ms"] / 1e3) / 1e9
+    traffic = measured_traffic(s.name)
+    roofline = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                "kernel": "kscan_kernel<256,4,bf16>", "kernel_us": main_res["scan_ms"] * 1e3,
+                "alg_bytes_per_launch": main_res["alg_bytes"]}
+
+    cpu, parity = (None, None)
+    if not args.no_cpu_baseline:
+        log(f"[bench] CPU oracle on {args.cpu_heads} heads")
+        cpu, parity = cpu_baseline(main_res, args.cpu_heads)
+
+    value = main_res["queries"] / (main_res["ms_per_step"] / 1e3)
+    line = {
+        "metric": "decode queries/s (head-tokens) at n=1M; K-scan HBM GB/s vs peak",
+        "value": value, "unit": "queries/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": main_res["ms_per_step"], "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": s.name, "batch": s.B, "q_heads": s.Hq, "kv_heads": s.Hkv, "head_dim": s.d,
+                   "context": s.n_ctx, "window": s.W, "topk": s.k, "set_size": 1 + s.W + s.k,
+                   "precision": "bf16 inputs, float64 set re-score and softmax, float32 output"},
+        "roofline": roofline, "cpu_baseline": cpu, "parity_sample": parity, "also": also,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

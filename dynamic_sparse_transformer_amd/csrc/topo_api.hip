@@ -39,7 +39,7 @@ topo::QueryGeom decode_geom(const topo_params_t* p) {
 
 int decode_like(const topo_params_t* p, const void* q, const void* k, const void* v, float* out,
                 int32_t* sel_idx, int32_t* sel_count, void* ws, size_t ws_bytes, hipStream_t stream,
-                bool softmax) {
+                bool softmax, hipEvent_t ev_begin = nullptr, hipEvent_t ev_end = nullptr) {
   int rc = check_params(p, true);
   if (rc) return rc;
   if (p->n_q != 1) return TOPO_EINVAL;
@@ -71,6 +71,8 @@ int decode_like(const topo_params_t* p, const void* q, const void* k, const void
   L.geom = g;
   L.scale = (double)p->softmax_scale;
   L.eps_coef = topo::fast_score_eps_coef(p->d);
+  L.ev_scan_begin = ev_begin;
+  L.ev_scan_end = ev_end;
   topo::decode_carve(ws, p->B, p->Hq, g, p->k, L);
   return topo::launch_decode(L, stream) == hipSuccess ? TOPO_OK : TOPO_EHIP;
 }
@@ -138,6 +140,13 @@ size_t topo_workspace_bytes(const topo_params_t* p, int op) {
 int topo_attn_decode(const topo_params_t* p, const void* q, const void* k, const void* v, float* out,
                      int32_t* sel_idx, int32_t* sel_count, void* workspace, size_t ws_bytes, hipStream_t stream) {
   return decode_like(p, q, k, v, out, sel_idx, sel_count, workspace, ws_bytes, stream, true);
+}
+
+int topo_attn_decode_timed(const topo_params_t* p, const void* q, const void* k, const void* v, float* out,
+                           int32_t* sel_idx, int32_t* sel_count, void* workspace, size_t ws_bytes,
+                           hipStream_t stream, hipEvent_t scan_begin, hipEvent_t scan_end) {
+  if (!scan_begin || !scan_end) return TOPO_EINVAL;
+  return decode_like(p, q, k, v, out, sel_idx, sel_count, workspace, ws_bytes, stream, true, scan_begin, scan_end);
 }
 
 int topo_attn_prefill(const topo_params_t* p, const void* q, const void* k, const void* v, float* out,

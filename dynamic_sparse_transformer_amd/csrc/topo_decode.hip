@@ -997,6 +997,10 @@ hipError_t launch_decode(const DecodeLaunch& L, hipStream_t stream) {
   if (e != hipSuccess) return e;
 
   const QueryGeom& g = L.geom;
+  if (L.ev_scan_begin) {
+    e = hipEventRecord(L.ev_scan_begin, stream);
+    if (e != hipSuccess) return e;
+  }
   const bool need_scan = L.topk > 0 && L.topk <= KS_MAX_K && g.n_cand > L.topk && !(L.flags & 1);
   if (need_scan) {
     KscanArgs ka;
@@ -1028,6 +1032,10 @@ hipError_t launch_decode(const DecodeLaunch& L, hipStream_t stream) {
       e = RB == 256 ? launch_kscan_g<256, false>(ka, GT, grid, stream) : launch_kscan_g<512, false>(ka, GT, grid, stream);
     }
     if (e != hipSuccess) return e;
+    if (L.ev_scan_end) {
+      e = hipEventRecord(L.ev_scan_end, stream);
+      if (e != hipSuccess) return e;
+    }
     for (int l = 0; l + 1 < L.nlevels; ++l) {
       MergeArgs ma;
       ma.st = L.st;
@@ -1048,6 +1056,10 @@ hipError_t launch_decode(const DecodeLaunch& L, hipStream_t stream) {
     }
   }
 
+  if (!need_scan && L.ev_scan_end) {
+    e = hipEventRecord(L.ev_scan_end, stream);
+    if (e != hipSuccess) return e;
+  }
   const int last = L.nlevels - 1;
   FinishArgs fa;
   fa.q = (const unsigned char*)L.q;

@@ -76,6 +76,8 @@ struct DecodeLaunch {
   QueryGeom geom;
   double scale;
   float eps_coef;
+  hipEvent_t ev_scan_begin;  // optional: recorded around the key-scan launch
+  hipEvent_t ev_scan_end;
 };
 
 size_t decode_workspace_bytes(int32_t B, int32_t Hq, const QueryGeom& g, int32_t k);

@@ -104,6 +104,16 @@ int topo_attn_decode(const topo_params_t* p, const void* q, const void* k, const
                      float* out, int32_t* sel_idx, int32_t* sel_count,
                      void* workspace, size_t ws_bytes, hipStream_t stream);
 
+/* Measurement variant of topo_attn_decode: identical results, and additionally records the
+ * caller's events scan_begin / scan_end on `stream` immediately before and after the key-scan
+ * kernel (the step that streams K from HBM), so its duration can be read with
+ * hipEventElapsedTime. The events must be valid hipEvent_t handles created by the caller; if no
+ * scan is needed (k = 0, or at most k candidates) both are recorded back to back. */
+int topo_attn_decode_timed(const topo_params_t* p, const void* q, const void* k, const void* v,
+                           float* out, int32_t* sel_idx, int32_t* sel_count,
+                           void* workspace, size_t ws_bytes, hipStream_t stream,
+                           hipEvent_t scan_begin, hipEvent_t scan_end);
+
 /* Topological attention of n_q consecutive queries per (batch, query head), query i at position
  * q_pos0 + i (a whole causal prompt is q_pos0 = 0, n_q = n_ctx). Same outputs as decode, one row
  * per query (zh technical summary §3). */

@@ -489,3 +489,40 @@ def test_planted_softmax_mistakes_are_caught(mutant):
         except AssertionError:
             caught += 1
     assert caught >= 1
+
+
+# ----------------------------------------------------------------------------- certificate helpers
+
+def test_omitted_mass_matches_textbook_softmax_weights():
+    """rho equals the summed textbook softmax probabilities (numpy matrix route) of the visible
+    positions left out of the set."""
+    rng = np.random.default_rng(13)
+    q, K, _ = rand_case(rng, 900, 32)
+    p, W, k, scale = 850, 40, 20, 0.4
+    s = oracle.canonical_scores(q, K)
+    C, _ = oracle.condensate_set(s, p, W, k)
+    logits = scale * (K[:p + 1].astype(np.float64) @ q.astype(np.float64))
+    prob = np.exp(logits - logits.max())
+    prob /= prob.sum()
+    out = np.setdiff1d(np.arange(p + 1), C)
+    assert abs(oracle.omitted_mass(s, C, p, scale) - prob[out].sum()) < 1e-12
+
+
+def test_ulp_distance_counts_representable_floats():
+    x = np.float32(1.5)
+    assert oracle.ulp_distance_f32(x, x) == 0
+    assert oracle.ulp_distance_f32(x, np.nextafter(x, np.float32(2))) == 1
+    y = np.nextafter(np.nextafter(x, np.float32(0)), np.float32(0))
+    assert oracle.ulp_distance_f32(x, y) == 2
+    assert oracle.ulp_distance_f32(np.float32(0.0), np.float32(-0.0)) == 0
+    tiny = np.nextafter(np.float32(0), np.float32(1))
+    assert oracle.ulp_distance_f32(tiny, -tiny) == 2
+
+
+def test_certificate_bound_is_sound():
+    """Where a component is certified, moving the exact output by the bound keeps the float32
+    roundings within one ulp (checked against the actual dense result)."""
+    s_ = spec(1, beta=16.0)
+    q, K, V, _ = gen_group(s_, 0, 0, 0)
+    rho, cert, ulps = exactness_check(q[0, 0], K, V, s_.n_ctx - 1, s_.W, s_.k, float(s_.softmax_scale))
+    assert cert.any() and np.all(ulps[cert] <= 1)
