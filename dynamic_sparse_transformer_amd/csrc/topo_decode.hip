@@ -131,39 +131,6 @@ __device__ __forceinline__ void reduce_scatter(float (&A)[V][L], int s) {
   rs_step<1, V, L>(A, (s & 1) != 0);
 }
 
-// k-th largest value among the `n` register entries of every lane (0 = empty): the largest T
-// with at least k entries >= T; 0 if fewer than k entries are non-zero.
-template <int N>
-__device__ __forceinline__ uint32_t wave_kth_largest(const uint32_t (&x)[N], int k) {
-  uint32_t T = 0;
-  for (int bit = 31; bit >= 0; --bit) {
-    const uint32_t cand = T | (1u << bit);
-    int c = 0;
-#pragma unroll
-    for (int i = 0; i < N; ++i) c += __popcll(__ballot(x[i] >= cand));
-    if (c >= k) T = cand;
-  }
-  return T;
-}
-
-// A threshold T such that at least k distinct entries are >= T, computed from N register entries
-// per lane (0 = empty). For k <= 64 it is the k-th largest of every lane's two largest entries,
-// which is a valid bound at a fraction of the cost of the exact k-th largest; for larger k the
-// exact k-th largest. 0 if fewer than k entries are non-zero.
-template <int N>
-__device__ __forceinline__ uint32_t wave_threshold(const uint32_t (&x)[N], int k) {
-  if (k <= 64 && N > 2) {
-    uint32_t m[2] = {0u, 0u};
-#pragma unroll
-    for (int i = 0; i < N; ++i) {
-      m[1] = max(m[1], min(m[0], x[i]));
-      m[0] = max(m[0], x[i]);
-    }
-    return wave_kth_largest<2>(m, k);
-  }
-  return wave_kth_largest<N>(x, k);
-}
-
 // ---------------------------------------------------------------------------------------------
 // kscan: grid (nblk, B*Hkv, ceil(G/GT)), 256 threads = 4 waves. Wave w of block x ranks keys
 // [4096 x + 1024 w, +1024) for the GT query heads of its slice.

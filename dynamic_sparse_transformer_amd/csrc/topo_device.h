@@ -165,6 +165,39 @@ __device__ __forceinline__ int lanes_below(uint64_t mask) {
   return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
 }
 
+// k-th largest value among the `n` register entries of every lane (0 = empty): the largest T
+// with at least k entries >= T; 0 if fewer than k entries are non-zero.
+template <int N>
+__device__ __forceinline__ uint32_t wave_kth_largest(const uint32_t (&x)[N], int k) {
+  uint32_t T = 0;
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t cand = T | (1u << bit);
+    int c = 0;
+#pragma unroll
+    for (int i = 0; i < N; ++i) c += __popcll(__ballot(x[i] >= cand));
+    if (c >= k) T = cand;
+  }
+  return T;
+}
+
+// A threshold T such that at least k distinct entries are >= T, computed from N register entries
+// per lane (0 = empty). For k <= 64 it is the k-th largest of every lane's two largest entries,
+// which is a valid bound at a fraction of the cost of the exact k-th largest; for larger k the
+// exact k-th largest. 0 if fewer than k entries are non-zero.
+template <int N>
+__device__ __forceinline__ uint32_t wave_threshold(const uint32_t (&x)[N], int k) {
+  if (k <= 64 && N > 2) {
+    uint32_t m[2] = {0u, 0u};
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      m[1] = max(m[1], min(m[0], x[i]));
+      m[0] = max(m[0], x[i]);
+    }
+    return wave_kth_largest<2>(m, k);
+  }
+  return wave_kth_largest<N>(x, k);
+}
+
 // Block-wide reductions through a caller-provided LDS scratch of (blockDim.x / 64) entries.
 // Every thread of the block must call them; all threads get the result.
 template <int NWAVES>
