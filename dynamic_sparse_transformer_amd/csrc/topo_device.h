@@ -54,6 +54,10 @@ __device__ __forceinline__ uint32_t ord_f32(float x) {
   uint32_t u = __float_as_uint(x);
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
+// Inverse of ord_f32 (for keys of non-NaN floats).
+__device__ __forceinline__ float unord_f32(uint32_t o) {
+  return __uint_as_float((o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o);
+}
 __device__ __forceinline__ uint64_t ord_f64(double x) {
   x = x + 0.0;  // -0 -> +0 so that equal scores share one key
   uint64_t u = (uint64_t)__double_as_longlong(x);

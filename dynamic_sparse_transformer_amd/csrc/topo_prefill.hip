@@ -21,10 +21,9 @@
 
 namespace topo {
 
-constexpr int PF_ROWS = 64;          // query rows per scan block
+constexpr int PF_ROWS = 128;         // query rows per scan block (8 waves: 4 row groups x 2 key halves)
 constexpr int PF_KEYS = 64;          // keys per scan step
 constexpr int PF_MAX_K = 96;         // largest k the MFMA scan ranks
-constexpr int PF_LIST = PF_MAX_K + 96;  // per-row LDS list (room for one step after a prune)
 constexpr uint32_t PF_OVERFLOW = 0xFFFFFFFFu;
 
 // Error bound of the MFMA float32 scores: products of bf16 values are exact in float32; allowing
@@ -33,19 +32,20 @@ constexpr uint32_t PF_OVERFLOW = 0xFFFFFFFFu;
 constexpr float PF_EPS_COEF = 0x1p-14f;
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
-static int64_t pf_slot(int32_t k) { return (int64_t)k + 32; }
+// Per-row list of possible top-k keys: k entries plus room for one more step after a prune.
+static int64_t pf_list(int32_t k) { return (int64_t)k + 96; }
 
 struct PfWs {
   float* qn;        // [B*Hq*n_q]
   uint32_t* knmax;  // [B*Hkv] float bits
-  uint32_t* cnt;    // [B*Hq*n_q]
-  uint2* surv;      // [B*Hq*n_q][slot]
+  uint32_t* cnt;    // [B*Hq*n_q]: entries of the row's list (or PF_OVERFLOW)
+  uint2* surv;      // [B*Hq*n_q][list]: (float bits of the fast score, key position)
 };
 
 size_t prefill_workspace_bytes(int32_t B, int32_t Hq, int64_t n_q, int64_t, int32_t, int32_t, int32_t k) {
   const size_t rows = (size_t)B * Hq * (size_t)n_q;
   return align256(rows * 4) + align256((size_t)B * Hq * 4) + align256(rows * 4) +
-         rows * (size_t)pf_slot(k) * sizeof(uint2);
+         rows * (size_t)pf_list(k) * sizeof(uint2);
 }
 
 static PfWs pf_carve(void* ws, int32_t B, int32_t Hq, int64_t n_q) {
@@ -63,29 +63,50 @@ static PfWs pf_carve(void* ws, int32_t B, int32_t Hq, int64_t n_q) {
 }
 
 // ---------------------------------------------------------------------------------------------
-// pf_norms: one wave per row of Q (rows < nq_rows) or of K (the rest): |row|_2 in float64, rounded
-// up to float32. K norms reduce to the max per kv head.
+// |q| of every query row: one wave per row (coalesced), float64 sum, rounded up to float32.
 template <int D, bool BF16>
-__global__ __launch_bounds__(256) void pf_norms_kernel(const unsigned char* q, const unsigned char* k, float* qn,
-                                                       uint32_t* knmax, int64_t nq_rows, int64_t nk_rows, int64_t n) {
+__global__ __launch_bounds__(256) void pf_qnorm_kernel(const unsigned char* q, float* qn, int64_t rows) {
   constexpr int RB = D * (BF16 ? 2 : 4);
   const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
-  if (row >= nq_rows + nk_rows) return;
-  const bool isq = row < nq_rows;
-  const unsigned char* base = isq ? q + (size_t)row * RB : k + (size_t)(row - nq_rows) * RB;
+  if (row >= rows) return;
   double s2 = 0.0;
-  constexpr int EPL = D / 64;  // elements per lane
+  constexpr int EPL = D / 64;
 #pragma unroll
   for (int e = 0; e < EPL; ++e) {
-    const double x = load_elem_f64<BF16>(base, lane * EPL + e);
+    const double x = load_elem_f64<BF16>(q + (size_t)row * RB, lane * EPL + e);
     s2 += x * x;
   }
   s2 = wave_sum_f64(s2);
-  if (lane == 0) {
-    const float nrm = (float)sqrt(s2) * (1.0f + 0x1p-20f);
-    if (isq) qn[row] = nrm;
-    else atomicMax(&knmax[(row - nq_rows) / n], __float_as_uint(nrm));
+  if (lane == 0) qn[row] = (float)sqrt(s2) * (1.0f + 0x1p-20f);
+}
+
+// Largest |k| of every kv head: grid (ceil(n/PF_KMAX_ROWS), B*Hkv); one atomicMax per block.
+constexpr int PF_KMAX_ROWS = 128;
+template <int D, bool BF16>
+__global__ __launch_bounds__(256) void pf_kmax_kernel(const unsigned char* k, uint32_t* knmax, int64_t n) {
+  constexpr int RB = D * (BF16 ? 2 : 4);
+  __shared__ float wm[4];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const unsigned char* kb = k + (size_t)blockIdx.y * (size_t)n * RB;
+  float mx = 0.f;
+  const int64_t r0 = (int64_t)blockIdx.x * PF_KMAX_ROWS;
+  for (int64_t row = r0 + wave; row < r0 + PF_KMAX_ROWS && row < n; row += 4) {
+    double s2 = 0.0;
+    constexpr int EPL = D / 64;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+      const double x = load_elem_f64<BF16>(kb + (size_t)row * RB, lane * EPL + e);
+      s2 += x * x;
+    }
+    s2 = wave_sum_f64(s2);
+    mx = fmaxf(mx, (float)sqrt(s2) * (1.0f + 0x1p-20f));
+  }
+  if (lane == 0) wm[wave] = mx;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const float m = fmaxf(fmaxf(wm[0], wm[1]), fmaxf(wm[2], wm[3]));
+    atomicMax(&knmax[blockIdx.y], __float_as_uint(m));
   }
 }
 
@@ -118,36 +139,89 @@ __device__ __forceinline__ bool pf_is_cand(int64_t j, int64_t p, int64_t n, int3
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
-// pf_scan: grid (ceil(n_q / 64), B*Hq), 256 threads. Wave w computes the 32x32 quadrant
-// (rows 32*(w/2).., keys 32*(w%2)..) of each 64x64 score tile with v_mfma_f32_32x32x16_bf16:
-// lane l supplies row / key (l % 32) and elements 8*(l/32) .. +8 of each 16-deep slice, and holds
-// output (row 8*(r/4) + 4*(l/32) + r%4, key l % 32) in register r.
+// Reads of a row list in global memory that other waves of the block may have written this step:
+// device-scope loads, so they are served past this CU's vector cache.
+__device__ __forceinline__ uint2 list_load(const uint2* p) {
+  const uint64_t x = __hip_atomic_load((const uint64_t*)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return make_uint2((uint32_t)x, (uint32_t)(x >> 32));
+}
+
+// Prune one row's list (one wave): keep the entries whose upper bound reaches the k-th best lower
+// bound of the list (or the row's current threshold, if higher). Returns the new count; the new
+// threshold goes to *th.
+template <int PER>
+__device__ int prune_row(uint2* lst, int c, float eps, int k, uint32_t* th) {
+  const int lane = threadIdx.x & 63;
+  uint2 e[PER];
+  uint32_t lb[PER];
+#pragma unroll
+  for (int t = 0; t < PER; ++t) {
+    const int idx = lane + 64 * t;
+    e[t] = idx < c ? list_load(lst + idx) : make_uint2(0u, 0u);
+    lb[t] = idx < c ? ord_f32(__uint_as_float(e[t].x) - eps) : 0u;
+  }
+  const uint32_t T = c > k ? wave_kth_largest<PER>(lb, k) : 0u;
+  const uint32_t t_new = max(T, *th);
+  int nc = 0;
+#pragma unroll
+  for (int t = 0; t < PER; ++t) {
+    const int idx = lane + 64 * t;
+    const bool keep = idx < c && ord_f32(__uint_as_float(e[t].x) + eps) >= t_new;
+    const uint64_t mk = __ballot(keep);
+    if (keep) lst[nc + lanes_below(mk)] = e[t];
+    nc += __popcll(mk);
+  }
+  *th = t_new;
+  return nc;
+}
+
+// pf_scan: one block of 512 threads per (b, h, 128 consecutive query rows). Each step stages 64
+// key rows in LDS (padded rows, double-buffered, coalesced loads). Wave w computes the 32x32
+// quadrant (rows 32*(w/2).., keys 32*(w%2)..) with v_mfma_f32_32x32x16_bf16: lane l supplies row /
+// key (l % 32) and elements 8*(l/32) .. +8 of each 16-deep slice, and holds output
+// (row 8*(r/4) + 4*(l/32) + r%4, key l % 32) in register r.
+// Phase 1 keeps, per lane and row, the two largest fast scores it has seen. Those 128 values per
+// row belong to distinct candidate keys, so their k-th largest x_k gives the bound T = x_k - eps
+// below the row's k-th largest exact score. Phase 2 scores the keys again and appends those whose
+// upper bound reaches T, i.e. fast score >= x_k - 2 eps, to the row's list in global memory.
+constexpr int PF_TOPS_BYTES = PF_ROWS * 128 * 4;
+
 template <int D>
-__global__ __launch_bounds__(256) void pf_scan_kernel(PfArgs a) {
+__global__ __launch_bounds__(512) void pf_scan_kernel(PfArgs a) {
   constexpr int RB = D * 2;
   constexpr int STEPS = D / 16;
-  __shared__ uint2 list[PF_ROWS][PF_LIST];
+  constexpr int NCH = RB / 16;            // 16-byte chunks per key row
+  constexpr int STRIDE = RB + 16;         // padded LDS row
+  constexpr int RPP = 512 / NCH;          // key rows staged per load pass
+  constexpr int PASSES = PF_KEYS / RPP;
+  constexpr int LMAX = PF_MAX_K + 96;
+  constexpr int TILE_BYTES = PF_KEYS * STRIDE;
+  static_assert(2 * TILE_BYTES <= PF_TOPS_BYTES, "LDS layout");
+  // the two key tiles during the scans; the per-lane top-2 values between them
+  __shared__ __align__(16) unsigned char lds[PF_TOPS_BYTES];
   __shared__ int lcnt[PF_ROWS];
-  __shared__ uint32_t lth[PF_ROWS];   // per-row threshold (order key of a lower bound)
-  __shared__ float leps[PF_ROWS];
+  __shared__ float lthf[PF_ROWS];
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int bh = blockIdx.y;
+  // Job of this block: consecutive block indices go to different XCDs (round robin), so the jobs
+  // are dealt out in eight contiguous ranges, one per XCD, which keeps the blocks of one head on
+  // one XCD's L2. Within a head the row blocks run from the last (most keys under a causal mask)
+  // to the first, so the long jobs start first.
+  const int64_t nrb = (a.n_q + PF_ROWS - 1) / PF_ROWS;
+  const int64_t njobs = nrb * a.Hq * (a.rows / (a.n_q * a.Hq));
+  int64_t job = blockIdx.x;
+  if (njobs % 8 == 0) job = (job & 7) * (njobs >> 3) + (job >> 3);
+  const int bh = (int)(job / nrb);
   const int b = bh / a.Hq, h = bh - b * a.Hq, g = h / a.G;
-  const int64_t i0 = (int64_t)blockIdx.x * PF_ROWS;
+  const int64_t i0 = (nrb - 1 - (job - (int64_t)bh * nrb)) * PF_ROWS;
   const unsigned char* kb = a.k + ((size_t)b * a.Hkv + g) * (size_t)a.n * RB;
   const float knmax = __uint_as_float(a.w.knmax[(size_t)b * a.Hkv + g]);
+  const int64_t LIST = a.slot;
 
-  if (tid < PF_ROWS) {
-    lcnt[tid] = 0;
-    lth[tid] = 0u;
-    const int64_t i = i0 + tid;
-    leps[tid] = i < a.n_q ? PF_EPS_COEF * a.w.qn[(size_t)bh * a.n_q + i] * knmax + 1e-30f : 0.f;
-  }
+  if (tid < PF_ROWS) lcnt[tid] = 0;
 
   const int rq = wave >> 1, kq = wave & 1;
   const int m = lane & 31, half = lane >> 5;
-  // A operand: this lane's query row, all K-slices.
   bf16x8_t qa[STEPS];
   {
     const int64_t i = i0 + rq * 32 + m;
@@ -158,106 +232,176 @@ __global__ __launch_bounds__(256) void pf_scan_kernel(PfArgs a) {
       qa[st] = __builtin_bit_cast(bf16x8_t, w);
     }
   }
-  // Row positions held by this lane (register r): block row rq*32 + 8*(r/4) + 4*half + r%4.
-  int64_t pos[16];
-#pragma unroll
-  for (int r = 0; r < 16; ++r) pos[r] = a.q_pos0 + i0 + rq * 32 + 8 * (r / 4) + 4 * half + (r % 4);
+  const int row_base = rq * 32 + 4 * half;  // block row of register r: row_base + 8*(r/4) + r%4
 
-  // Keys to scan: up to the last candidate of the block's last row.
   const int64_t i_last = min(i0 + PF_ROWS, a.n_q) - 1;
-  const int64_t p_last = a.q_pos0 + i_last;
+  const int64_t p_first = a.q_pos0 + i0, p_last = a.q_pos0 + i_last;
   const int64_t key_hi = a.causal ? p_last - a.W : a.n - 1;
+  const int64_t ntiles = key_hi >= 0 ? key_hi / PF_KEYS + 1 : 0;
+  const bool full_rows = i0 + PF_ROWS <= a.n_q;
+
+  // Each thread stages chunk (tid % NCH) of key rows kt0 + ps*RPP + tid/NCH.
+  const int srow = tid / NCH, schunk = tid % NCH;
+  uint4 pre0 = make_uint4(0u, 0u, 0u, 0u), pre1 = pre0, pre2 = pre0, pre3 = pre0;
+  static_assert(PASSES >= 1 && PASSES <= 4, "staging passes");
+#define PF_FETCH(KT0)                                                                              \
+  {                                                                                                \
+    const int64_t key0 = (KT0) + srow;                                                             \
+    const unsigned char* src = kb + (size_t)schunk * 16;                                           \
+    pre0 = *(const uint4*)(src + (size_t)(key0 < a.n ? key0 : a.n - 1) * RB);                      \
+    if (PASSES > 1) pre1 = *(const uint4*)(src + (size_t)(key0 + RPP < a.n ? key0 + RPP : a.n - 1) * RB);          \
+    if (PASSES > 2) pre2 = *(const uint4*)(src + (size_t)(key0 + 2 * RPP < a.n ? key0 + 2 * RPP : a.n - 1) * RB);  \
+    if (PASSES > 3) pre3 = *(const uint4*)(src + (size_t)(key0 + 3 * RPP < a.n ? key0 + 3 * RPP : a.n - 1) * RB);  \
+  }
+#define PF_STASH(BUF)                                                                              \
+  {                                                                                                \
+    unsigned char* dst = &lds[(BUF) * TILE_BYTES + srow * STRIDE + schunk * 16];                   \
+    *(uint4*)dst = pre0;                                                                           \
+    if (PASSES > 1) *(uint4*)(dst + RPP * STRIDE) = pre1;                                          \
+    if (PASSES > 2) *(uint4*)(dst + 2 * RPP * STRIDE) = pre2;                                      \
+    if (PASSES > 3) *(uint4*)(dst + 3 * RPP * STRIDE) = pre3;                                      \
+  }
+// Scores of step t into acc (every wave), with the next tile staged meanwhile.
+#define PF_TILE(t)                                                                                 \
+  if ((t) + 1 < ntiles) PF_FETCH(((t) + 1) * PF_KEYS);                                             \
+  acc = f32x16_t{};                                                                                \
+  {                                                                                                \
+    const unsigned char* krow = &lds[((t) & 1) * TILE_BYTES + (kq * 32 + m) * STRIDE + half * 16]; \
+    _Pragma("unroll") for (int st = 0; st < STEPS; ++st) {                                         \
+      const uint4 w = *(const uint4*)(krow + st * 32);                                             \
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[st], __builtin_bit_cast(bf16x8_t, w), acc, 0, 0, 0); \
+    }                                                                                              \
+  }
+#define PF_NEXT(t)                                                                                 \
+  if ((t) + 1 < ntiles) PF_STASH(((t) + 1) & 1);                                                   \
   __syncthreads();
 
-  for (int64_t kt0 = 0; kt0 <= key_hi; kt0 += PF_KEYS) {
-    const int64_t j = kt0 + kq * 32 + m;  // key of this lane's B operand and output column
-    f32x16_t acc = {};
-    {
-      const unsigned char* krow = kb + (size_t)(j < a.n ? j : a.n - 1) * RB;
+  // Candidate test of register r on a boundary step, in 32-bit arithmetic: with
+  // dr = (position of the register's row) - j, key j is a candidate of the row iff 1 <= j < n, the
+  // row exists, and dr >= W (j before the window) or, without the causal mask, dr < 0 (j after p).
+  const int rows_valid = (int)min((int64_t)PF_ROWS, a.n_q - i0);
+#define PF_CAND(r, dl, jok)                                                                        \
+  ((jok) && row_base + 8 * ((r) / 4) + ((r) % 4) < rows_valid &&                                   \
+   ((dl) + 8 * ((r) / 4) + ((r) % 4) >= a.W || (!a.causal && (dl) + 8 * ((r) / 4) + ((r) % 4) < 0)))
+#define PF_GEOM(t)                                                                                 \
+  const int64_t kt0 = (t) * PF_KEYS;                                                               \
+  const int64_t j = kt0 + kq * 32 + m;                                                             \
+  const bool interior = full_rows && kt0 >= 1 &&                                                   \
+      (kt0 + PF_KEYS - 1 <= p_first - a.W || (!a.causal && kt0 > p_last && kt0 + PF_KEYS <= a.n)); \
+  const int64_t dl64 = p_first + row_base - j;                                                     \
+  const int dl = (int)(dl64 > (1 << 30) ? (1 << 30) : (dl64 < -(1 << 30) ? -(1 << 30) : dl64));     \
+  const bool jok = j >= 1 && j < a.n;
+
+  f32x16_t acc;
+  // ---- phase 1: per lane and row, the two largest fast scores of candidate keys
+  float m1[16], m2[16];
 #pragma unroll
-      for (int st = 0; st < STEPS; ++st) {
-        const uint4 w = *(const uint4*)(krow + st * 32 + half * 16);
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[st], __builtin_bit_cast(bf16x8_t, w), acc, 0, 0, 0);
+  for (int r = 0; r < 16; ++r) m1[r] = m2[r] = -INFINITY;
+  if (ntiles > 0) {
+    PF_FETCH(0);
+    PF_STASH(0);
+  }
+  __syncthreads();
+  for (int64_t t = 0; t < ntiles; ++t) {
+    PF_TILE(t)
+    PF_GEOM(t)
+    if (interior) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        m2[r] = fmaxf(m2[r], fminf(m1[r], acc[r]));
+        m1[r] = fmaxf(m1[r], acc[r]);
+      }
+    } else {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float x = PF_CAND(r, dl, jok) ? acc[r] : -INFINITY;
+        m2[r] = fmaxf(m2[r], fminf(m1[r], x));
+        m1[r] = fmaxf(m1[r], x);
       }
     }
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int row = rq * 32 + 8 * (r / 4) + 4 * half + (r % 4);
-      const bool ok = i0 + row < a.n_q && pf_is_cand(j, pos[r], a.n, a.W, a.causal) &&
-                      ord_f32(acc[r] + leps[row]) >= lth[row];
-      if (ok) {
-        const int slot = atomicAdd(&lcnt[row], 1);
-        if (slot < PF_LIST) list[row][slot] = make_uint2(__float_as_uint(acc[r]), (uint32_t)j);
-      }
-    }
-    __syncthreads();
-    // Prune the lists that may not hold another step: wave w takes rows w, w+4, ...
-    for (int row = wave; row < PF_ROWS; row += 4) {
-      const int c = lcnt[row];
-      if (c <= PF_LIST - PF_KEYS) continue;
-      const float eps = leps[row];
-      constexpr int PER = PF_LIST / 64;
-      uint2 e[PER];
-      uint32_t lb[PER];
-#pragma unroll
-      for (int t = 0; t < PER; ++t) {
-        const int idx = lane + 64 * t;
-        e[t] = idx < c ? list[row][idx] : make_uint2(0u, 0u);
-        lb[t] = idx < c ? ord_f32(__uint_as_float(e[t].x) - eps) : 0u;
-      }
-      const uint32_t T = wave_kth_largest<PER>(lb, a.topk);
-      const uint32_t th = max(T, lth[row]);
-      int nc = 0;
-#pragma unroll
-      for (int t = 0; t < PER; ++t) {
-        const int idx = lane + 64 * t;
-        const bool keep = idx < c && ord_f32(__uint_as_float(e[t].x) + eps) >= th;
-        const uint64_t mk = __ballot(keep);
-        if (keep) list[row][nc + lanes_below(mk)] = e[t];
-        nc += __popcll(mk);
-      }
-      if (lane == 0) {
-        lcnt[row] = c > PF_LIST ? (int)PF_LIST + 1 : nc;  // more than the list held: overflow
-        lth[row] = th;
-      }
-    }
-    __syncthreads();
+    PF_NEXT(t)
   }
 
-  // Final prune and hand-over: wave w writes rows w, w+4, ...
-  for (int row = wave; row < PF_ROWS; row += 4) {
+  // ---- thresholds: row R's 128 values sit at tops[R][64 * kq + 2 * m + {0, 1}]
+  float* tops = (float*)lds;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int row = row_base + 8 * (r / 4) + (r % 4);
+    *(float2*)&tops[row * 128 + 64 * kq + 2 * m] = make_float2(m1[r], m2[r]);
+  }
+  __syncthreads();
+  for (int row = wave; row < PF_ROWS; row += 8) {
+    const float2 v = *(const float2*)&tops[row * 128 + 2 * lane];
+    const uint32_t key[2] = {ord_f32(v.x), ord_f32(v.y)};
+    const uint32_t xk = wave_kth_largest<2>(key, a.topk);
+    if (lane == 0) {
+      const int64_t i = i0 + row;
+      const float eps = i < a.n_q ? PF_EPS_COEF * a.w.qn[(size_t)bh * a.n_q + i] * knmax + 1e-30f : 0.f;
+      // fewer than k finite values (or none): every candidate stays
+      const float x = xk == 0u ? -INFINITY : unord_f32(xk);
+      lthf[row] = x - 2.0f * eps;
+    }
+  }
+  __syncthreads();
+  float thf[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) thf[r] = lthf[row_base + 8 * (r / 4) + (r % 4)];
+
+  // ---- phase 2: append every candidate key whose upper bound reaches the row's bound
+  if (ntiles > 0) {
+    PF_FETCH(0);
+    PF_STASH(0);
+  }
+  __syncthreads();
+  for (int64_t t = 0; t < ntiles; ++t) {
+    PF_TILE(t)
+    PF_GEOM(t)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      bool ok = acc[r] >= thf[r];
+      const int row = row_base + 8 * (r / 4) + (r % 4);
+      if (!interior) ok = ok && PF_CAND(r, dl, jok);
+      const uint64_t mk = __ballot(ok);
+      if (mk) {
+        // lanes 0-31 hold block row `row` of half 0, lanes 32-63 the row 4 below it
+        const uint32_t mine = half ? (uint32_t)(mk >> 32) : (uint32_t)mk;
+        int base = 0;
+        if ((lane & 31) == 0 && mine) base = atomicAdd(&lcnt[row], __popc(mine));
+        base = __shfl(base, lane & 32);
+        if (ok) {
+          const int slot = base + __popc(mine & ((1u << (lane & 31)) - 1u));
+          if (slot < LIST)
+            a.w.surv[((size_t)bh * a.n_q + i0 + row) * (size_t)LIST + slot] = make_uint2(__float_as_uint(acc[r]), (uint32_t)j);
+        }
+      }
+    }
+    PF_NEXT(t)
+  }
+  // The list entries written above must have left their waves before other waves read them.
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  __syncthreads();
+
+  // Final prune to the top-k band and hand-over of the counts: wave w takes rows w, w+8, ...
+  for (int row = wave; row < PF_ROWS; row += 8) {
     const int64_t i = i0 + row;
     if (i >= a.n_q) continue;
     const size_t grow = (size_t)bh * a.n_q + i;
     const int c = lcnt[row];
-    if (c > PF_LIST) {
+    if (c > LIST) {
       if (lane == 0) a.w.cnt[grow] = PF_OVERFLOW;
       continue;
     }
-    const float eps = leps[row];
-    constexpr int PER = PF_LIST / 64;
-    uint2 e[PER];
-    uint32_t lb[PER];
-#pragma unroll
-    for (int t = 0; t < PER; ++t) {
-      const int idx = lane + 64 * t;
-      e[t] = idx < c ? list[row][idx] : make_uint2(0u, 0u);
-      lb[t] = idx < c ? ord_f32(__uint_as_float(e[t].x) - eps) : 0u;
-    }
-    const uint32_t T = c > a.topk ? wave_kth_largest<PER>(lb, a.topk) : 0u;
-    const uint32_t th = max(T, lth[row]);
-    uint2* out = a.w.surv + grow * (size_t)a.slot;
-    int nc = 0;
-#pragma unroll
-    for (int t = 0; t < PER; ++t) {
-      const int idx = lane + 64 * t;
-      const bool keep = idx < c && ord_f32(__uint_as_float(e[t].x) + eps) >= th;
-      const uint64_t mk = __ballot(keep);
-      if (keep && nc + lanes_below(mk) < a.slot) out[nc + lanes_below(mk)] = e[t];
-      nc += __popcll(mk);
-    }
-    if (lane == 0) a.w.cnt[grow] = nc > a.slot ? PF_OVERFLOW : (uint32_t)nc;
+    const float eps = PF_EPS_COEF * a.w.qn[grow] * knmax + 1e-30f;
+    uint32_t thr = 0u;
+    const int nc = prune_row<(LMAX + 63) / 64>(a.w.surv + grow * (size_t)LIST, c, eps, a.topk, &thr);
+    if (lane == 0) a.w.cnt[grow] = (uint32_t)nc;
   }
+#undef PF_FETCH
+#undef PF_STASH
+#undef PF_TILE
+#undef PF_NEXT
+#undef PF_CAND
+#undef PF_GEOM
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -266,23 +410,23 @@ __global__ __launch_bounds__(256) void pf_scan_kernel(PfArgs a) {
 constexpr int PF_FIN_SET = 4096;   // largest 1 + W + k served by the per-row finish
 struct PfRowSmem {
   double* qd;      // [128]
-  int32_t* ridx;   // [slot]
-  double* rs;      // [slot]
-  int32_t* tidx;   // [k]
+  double* rs;      // [slot + set_cap]: float64 scores of the row's list, window and anchor keys
   double* ts;      // [k]
-  int32_t* cidx;   // [set_cap]
   double* cw;      // [set_cap]
+  int32_t* ridx;   // [slot]
+  int32_t* tidx;   // [k]
+  int32_t* cidx;   // [set_cap]
   uint32_t* hist;  // [256]
   static __host__ __device__ size_t bytes(int64_t slot, int k, int set_cap) {
     const size_t kk = (size_t)(k > 0 ? k : 1);
-    return 128 * 8 + (size_t)slot * 12 + kk * 12 + (size_t)set_cap * 12 + 256 * 4 + 64;
+    return 128 * 8 + ((size_t)slot + set_cap) * 8 + kk * 12 + (size_t)set_cap * 12 + (size_t)slot * 4 + 256 * 4 + 64;
   }
   __device__ void carve(unsigned char* p, int64_t slot, int k, int set_cap) {
     const size_t kk = (size_t)(k > 0 ? k : 1);
     qd = (double*)p;
     p += 128 * 8;
     rs = (double*)p;
-    p += (size_t)slot * 8;
+    p += ((size_t)slot + set_cap) * 8;
     ts = (double*)p;
     p += kk * 8;
     cw = (double*)p;
@@ -376,6 +520,10 @@ __device__ int pf_exact_row(PfRowSmem* sm, const PfArgs& a, const unsigned char*
   return nt;
 }
 
+// pf_finish: one wave per query row (consecutive rows of one head share a block, so their
+// window rows are served from the caches). Steps: float64 scores of the row's list, window and
+// anchor keys in one pass (each lane one key, the whole row requested at once); exact rank of the
+// list; the set in ascending order; float64 softmax over it and the weighted V rows.
 template <int D, bool BF16>
 __global__ __launch_bounds__(256) void pf_finish_kernel(PfArgs a) {
   constexpr int RB = D * (BF16 ? 2 : 4);
@@ -394,51 +542,64 @@ __global__ __launch_bounds__(256) void pf_finish_kernel(PfArgs a) {
   const int64_t p = a.q_pos0 + i;
   const unsigned char* qrow = a.q + grow * RB;
   for (int t = lane; t < D; t += 64) sm->qd[t] = load_elem_f64<BF16>(qrow, t);
-  __builtin_amdgcn_wave_barrier();
 
-  // ---- the top-k part
-  int nt = 0;
-  if (a.topk > 0) {
-    const uint32_t c = a.exact_all ? PF_OVERFLOW : a.w.cnt[grow];
-    bool exact = c == PF_OVERFLOW;
-    if (!exact) {
-      const uint2* sv = a.w.surv + grow * (size_t)a.slot;
-      for (uint32_t t = lane; t < c; t += 64) {
-        const int32_t j = (int32_t)sv[t].y;
-        sm->ridx[t] = j;
-        sm->rs[t] = pf_score<D, BF16>(sm->qd, kb, j);
-      }
-      __builtin_amdgcn_wave_barrier();
-      // exact rank among the list: higher score first, then lower position. The list holds
-      // every key of the row's top-k (or all of its candidates when it has at most k).
-      for (uint32_t t = lane; t < c; t += 64) {
-        const double si = sm->rs[t];
-        const int32_t ji = sm->ridx[t];
-        int rank = 0;
-        for (uint32_t r = 0; r < c; ++r) rank += (sm->rs[r] > si) || (sm->rs[r] == si && sm->ridx[r] < ji);
-        if (rank < a.topk) {
-          sm->tidx[rank] = ji;
-          sm->ts[rank] = si;
-        }
-      }
-      nt = (int)min(c, (uint32_t)a.topk);
-      __builtin_amdgcn_wave_barrier();
-    } else {
-      nt = pf_exact_row<D, BF16>(sm, a, kb, p);
-    }
-  }
-
-  // ---- set: {0} u window u T, ascending
   const int64_t w_lo = p - a.W + 1 > 0 ? p - a.W + 1 : 0;
   const int anchor = w_lo > 0 ? 1 : 0;
   const int nwin = (int)(p - w_lo + 1);
+
+  // ---- the row's list of possible top-k keys (fast path) or the exact path
+  int c = 0;
+  bool exact = false;
+  if (a.topk > 0) {
+    const uint32_t cr = a.exact_all ? PF_OVERFLOW : a.w.cnt[grow];
+    exact = cr == PF_OVERFLOW;
+    if (!exact) {
+      c = (int)cr;
+      const uint2* sv = a.w.surv + grow * (size_t)a.slot;
+      for (int t = lane; t < c; t += 64) sm->ridx[t] = (int32_t)sv[t].y;
+    }
+  }
+  __builtin_amdgcn_wave_barrier();
+
+  // ---- float64 scores: items [0, c) the list, [c, c + nwin) the window, then the anchor
+  const int nitems = c + nwin + anchor;
+  for (int t = lane; t < nitems; t += 64) {
+    const int64_t j = t < c ? (int64_t)sm->ridx[t] : (t < c + nwin ? w_lo + (t - c) : 0);
+    sm->rs[t] = canonical_score_row<BF16, D>(sm->qd, kb + (size_t)j * RB);
+  }
+  __builtin_amdgcn_wave_barrier();
+
+  int nt = 0;
+  if (exact) {
+    nt = pf_exact_row<D, BF16>(sm, a, kb, p);
+  } else if (c > 0) {
+    // exact rank among the list: higher score first, then lower position. The list holds every
+    // key of the row's top-k (or all of its candidates when it has at most k).
+    for (int t = lane; t < c; t += 64) {
+      const double si = sm->rs[t];
+      const int32_t ji = sm->ridx[t];
+      int rank = 0;
+      for (int r = 0; r < c; ++r) {
+        const double sr = sm->rs[r];
+        rank += (sr > si) || (sr == si && sm->ridx[r] < ji);
+      }
+      if (rank < a.topk) {
+        sm->tidx[rank] = ji;
+        sm->ts[rank] = si;
+      }
+    }
+    nt = min(c, a.topk);
+    __builtin_amdgcn_wave_barrier();
+  }
+
+  // ---- set: {0} u window u T, ascending
   const int count = anchor + nwin + nt;
   int tlo = 0;
   for (int t = lane; t < nt; t += 64) tlo += sm->tidx[t] < w_lo;
   tlo = wave_sum_i32(tlo);
   if (anchor && lane == 0) {
     sm->cidx[0] = 0;
-    sm->cw[0] = pf_score<D, BF16>(sm->qd, kb, 0);
+    sm->cw[0] = sm->rs[c + nwin];
   }
   for (int t = lane; t < nt; t += 64) {
     const int32_t j = sm->tidx[t];
@@ -451,7 +612,7 @@ __global__ __launch_bounds__(256) void pf_finish_kernel(PfArgs a) {
   for (int t = lane; t < nwin; t += 64) {
     const int pos = anchor + tlo + t;
     sm->cidx[pos] = (int32_t)(w_lo + t);
-    sm->cw[pos] = pf_score<D, BF16>(sm->qd, kb, w_lo + t);
+    sm->cw[pos] = sm->rs[c + t];
   }
   __builtin_amdgcn_wave_barrier();
   if (a.sel_idx) {
@@ -461,7 +622,7 @@ __global__ __launch_bounds__(256) void pf_finish_kernel(PfArgs a) {
   if (a.sel_count && lane == 0) a.sel_count[grow] = count;
   if (!a.out) return;
 
-  // ---- float64 softmax over the set and the weighted V rows (lane: D/64 columns)
+  // ---- float64 softmax over the set
   double zmax = -INFINITY;
   for (int t = lane; t < count; t += 64) zmax = fmax(zmax, a.scale * sm->cw[t]);
   zmax = wave_max_f64(zmax);
@@ -473,30 +634,49 @@ __global__ __launch_bounds__(256) void pf_finish_kernel(PfArgs a) {
   }
   zsum = wave_sum_f64(zsum);
   __builtin_amdgcn_wave_barrier();
-  constexpr int CPL = D / 64;
-  constexpr int BATCH = 16;
-  double acc[CPL];
+
+  // ---- weighted V rows: a row is LPR lanes x 16 bytes, so one load instruction covers RPI rows;
+  // lane group gq = lane / LPR takes the set entries t = gq (mod RPI), then the groups are summed.
+  constexpr int LPR = RB / 16, RPI = 64 / LPR, EPC = BF16 ? 8 : 4, U = 8;
+  const int gq = lane / LPR, cc = lane % LPR;
+  double acc[EPC];
 #pragma unroll
-  for (int e = 0; e < CPL; ++e) acc[e] = 0.0;
-  for (int t0 = 0; t0 < count; t0 += BATCH) {
-    double x[BATCH][CPL];
+  for (int e = 0; e < EPC; ++e) acc[e] = 0.0;
+  for (int t0 = 0; t0 < count; t0 += U * RPI) {
+    uint4 x[U];
 #pragma unroll
-    for (int u = 0; u < BATCH; ++u) {
-      const int t = t0 + u;
-#pragma unroll
-      for (int e = 0; e < CPL; ++e)
-        x[u][e] = t < count ? load_elem_f64<BF16>(vb + (size_t)sm->cidx[t] * RB, lane * CPL + e) : 0.0;
+    for (int u = 0; u < U; ++u) {
+      const int t = t0 + u * RPI + gq;
+      x[u] = t < count ? *(const uint4*)(vb + (size_t)sm->cidx[t] * RB + cc * 16) : make_uint4(0u, 0u, 0u, 0u);
     }
 #pragma unroll
-    for (int u = 0; u < BATCH; ++u) {
-      const int t = t0 + u;
+    for (int u = 0; u < U; ++u) {
+      const int t = t0 + u * RPI + gq;
       const double w = t < count ? sm->cw[t] : 0.0;
+      const uint32_t xs[4] = {x[u].x, x[u].y, x[u].z, x[u].w};
 #pragma unroll
-      for (int e = 0; e < CPL; ++e) acc[e] = fma(w, x[u][e], acc[e]);
+      for (int e = 0; e < 4; ++e) {
+        if constexpr (BF16) {
+          acc[2 * e] = fma(w, (double)bf16_lo(xs[e]), acc[2 * e]);
+          acc[2 * e + 1] = fma(w, (double)bf16_hi(xs[e]), acc[2 * e + 1]);
+        } else {
+          acc[e] = fma(w, (double)__uint_as_float(xs[e]), acc[e]);
+        }
+      }
     }
   }
 #pragma unroll
-  for (int e = 0; e < CPL; ++e) a.out[grow * D + lane * CPL + e] = (float)(acc[e] / zsum);
+  for (int o = LPR; o < 64; o <<= 1)
+#pragma unroll
+    for (int e = 0; e < EPC; ++e) acc[e] += __shfl_xor(acc[e], o);
+  if (gq == 0) {
+    float r[EPC];
+#pragma unroll
+    for (int e = 0; e < EPC; ++e) r[e] = (float)(acc[e] / zsum);
+    float4* dst = (float4*)(a.out + grow * D + cc * EPC);
+#pragma unroll
+    for (int e = 0; e < EPC / 4; ++e) dst[e] = make_float4(r[4 * e], r[4 * e + 1], r[4 * e + 2], r[4 * e + 3]);
+  }
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -506,17 +686,16 @@ static hipError_t launch_pf_t(const PrefillLaunch& L, const PfArgs& pa, hipStrea
   // norms and zeroed kv-head maxima
   hipLaunchKernelGGL(pf_zero_kernel, dim3((unsigned)((L.B * L.Hkv + 255) / 256)), dim3(256), 0, s, pa.w.knmax,
                      (int64_t)L.B * L.Hkv);
-  const int64_t nk_rows = (int64_t)L.B * L.Hkv * L.n;
-  const int64_t tot = (int64_t)rows + nk_rows;
-  hipLaunchKernelGGL((pf_norms_kernel<D, BF16>), dim3((unsigned)((tot + 3) / 4)), dim3(256), 0, s,
-                     (const unsigned char*)L.q, (const unsigned char*)L.k, pa.w.qn, pa.w.knmax, (int64_t)rows, nk_rows,
-                     L.n);
+  hipLaunchKernelGGL((pf_qnorm_kernel<D, BF16>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s,
+                     (const unsigned char*)L.q, pa.w.qn, (int64_t)rows);
+  hipLaunchKernelGGL((pf_kmax_kernel<D, BF16>), dim3((unsigned)((L.n + PF_KMAX_ROWS - 1) / PF_KMAX_ROWS), (unsigned)(L.B * L.Hkv)),
+                     dim3(256), 0, s, (const unsigned char*)L.k, pa.w.knmax, L.n);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (!pa.exact_all) {
+  if (!pa.exact_all && L.topk > 0) {
     if constexpr (BF16) {
-      hipLaunchKernelGGL((pf_scan_kernel<D>), dim3((unsigned)((L.n_q + PF_ROWS - 1) / PF_ROWS), (unsigned)(L.B * L.Hq)),
-                         dim3(256), 0, s, pa);
+      hipLaunchKernelGGL((pf_scan_kernel<D>), dim3((unsigned)((L.n_q + PF_ROWS - 1) / PF_ROWS * L.B * L.Hq)),
+                         dim3(512), 0, s, pa);
       e = hipGetLastError();
       if (e != hipSuccess) return e;
     }
@@ -542,7 +721,7 @@ hipError_t launch_prefill(const PrefillLaunch& L, hipStream_t stream) {
   pa.n = L.n;
   pa.n_q = L.n_q;
   pa.q_pos0 = L.q_pos0;
-  pa.slot = pf_slot(L.topk);
+  pa.slot = pf_list(L.topk);
   pa.Hq = L.Hq;
   pa.Hkv = L.Hkv;
   pa.G = L.G;
