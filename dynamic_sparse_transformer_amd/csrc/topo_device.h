@@ -138,6 +138,11 @@ __device__ __forceinline__ float wave_max_f32(float x) {
   for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
   return x;
 }
+__device__ __forceinline__ float wave_sum_f32(float x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
+  return x;
+}
 __device__ __forceinline__ double wave_sum_f64(double x) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);

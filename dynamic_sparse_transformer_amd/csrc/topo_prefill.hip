@@ -520,20 +520,19 @@ __device__ int pf_exact_row(PfRowSmem* sm, const PfArgs& a, const unsigned char*
   return nt;
 }
 
-// pf_finish: one wave per query row (consecutive rows of one head share a block, so their
-// window rows are served from the caches). Steps: float64 scores of the row's list, window and
-// anchor keys in one pass (each lane one key, the whole row requested at once); exact rank of the
-// list; the set in ascending order; float64 softmax over it and the weighted V rows.
+// One query row of the finish, by one wave. Steps: float64 canonical scores of the row's list and
+// of the anchor (each lane one key, the whole row requested at once) and the exact rank of the
+// list; scores of the window keys; the set in ascending order; softmax over it and the weighted V
+// rows. Arithmetic: the ranking always uses the float64 canonical scores. With bf16 inputs the
+// window logits (16-byte chunks per lane, summed across lanes), the softmax and the V sum are
+// float32 (products of bf16 values are exact in float32; sums round once per add); with float32
+// inputs all of it is float64.
 template <int D, bool BF16>
-__global__ __launch_bounds__(256) void pf_finish_kernel(PfArgs a) {
+__device__ void pf_row(const PfArgs& a, PfRowSmem* sm, size_t grow) {
   constexpr int RB = D * (BF16 ? 2 : 4);
-  extern __shared__ __align__(16) unsigned char smem_raw[];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  PfRowSmem smv;
-  smv.carve(smem_raw + wave * a.wave_smem, a.slot, a.topk, a.set_cap);
-  PfRowSmem* sm = &smv;
-  const size_t grow = (size_t)blockIdx.x * 4 + wave;  // (b*Hq + h) * n_q + i
-  if (grow >= (size_t)a.rows) return;
+  // a key row is LPR lanes x 16 bytes, so one load instruction covers RPI rows
+  constexpr int LPR = RB / 16, RPI = 64 / LPR, EPC = BF16 ? 8 : 4;
+  const int lane = threadIdx.x & 63;
   const size_t bh = grow / (size_t)a.n_q;
   const int64_t i = (int64_t)(grow - bh * (size_t)a.n_q);
   const int b = (int)(bh / a.Hq), h = (int)(bh - (size_t)b * a.Hq), g = h / a.G;
@@ -541,6 +540,7 @@ __global__ __launch_bounds__(256) void pf_finish_kernel(PfArgs a) {
   const unsigned char* vb = a.v ? a.v + ((size_t)b * a.Hkv + g) * (size_t)a.n * RB : nullptr;
   const int64_t p = a.q_pos0 + i;
   const unsigned char* qrow = a.q + grow * RB;
+  const int gq = lane / LPR, cc = lane % LPR;
   for (int t = lane; t < D; t += 64) sm->qd[t] = load_elem_f64<BF16>(qrow, t);
 
   const int64_t w_lo = p - a.W + 1 > 0 ? p - a.W + 1 : 0;
@@ -561,20 +561,42 @@ __global__ __launch_bounds__(256) void pf_finish_kernel(PfArgs a) {
   }
   __builtin_amdgcn_wave_barrier();
 
-  // ---- float64 scores: items [0, c) the list, [c, c + nwin) the window, then the anchor
-  const int nitems = c + nwin + anchor;
-  for (int t = lane; t < nitems; t += 64) {
-    const int64_t j = t < c ? (int64_t)sm->ridx[t] : (t < c + nwin ? w_lo + (t - c) : 0);
+  // ---- scores: items [0, c) the list, c the anchor (if any), then the window
+  const int wbase = c + anchor;
+  const int nitems = wbase + nwin;
+  const int ncanon = BF16 ? wbase : nitems;
+  for (int t = lane; t < ncanon; t += 64) {
+    const int64_t j = t < c ? (int64_t)sm->ridx[t] : (t < wbase ? 0 : w_lo + (t - wbase));
     sm->rs[t] = canonical_score_row<BF16, D>(sm->qd, kb + (size_t)j * RB);
+  }
+  if constexpr (BF16) {
+    const uint4 qv = *(const uint4*)(qrow + cc * 16);
+    constexpr int U = 4;
+    for (int t0 = 0; t0 < nwin; t0 += U * RPI) {
+      uint4 x[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int t = t0 + u * RPI + gq;
+        x[u] = t < nwin ? *(const uint4*)(kb + (size_t)(w_lo + t) * RB + cc * 16) : make_uint4(0u, 0u, 0u, 0u);
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        float part = dot_chunk_bf16(qv, x[u], 0.0f);
+#pragma unroll
+        for (int o = 1; o < LPR; o <<= 1) part += __shfl_xor(part, o);
+        const int t = t0 + u * RPI + gq;
+        if (cc == 0 && t < nwin) sm->rs[wbase + t] = (double)part;
+      }
+    }
   }
   __builtin_amdgcn_wave_barrier();
 
   int nt = 0;
   if (exact) {
     nt = pf_exact_row<D, BF16>(sm, a, kb, p);
-  } else if (c > 0) {
+  } else if (c > a.topk) {
     // exact rank among the list: higher score first, then lower position. The list holds every
-    // key of the row's top-k (or all of its candidates when it has at most k).
+    // key of the row's top-k.
     for (int t = lane; t < c; t += 64) {
       const double si = sm->rs[t];
       const int32_t ji = sm->ridx[t];
@@ -588,7 +610,15 @@ __global__ __launch_bounds__(256) void pf_finish_kernel(PfArgs a) {
         sm->ts[rank] = si;
       }
     }
-    nt = min(c, a.topk);
+    nt = a.topk;
+    __builtin_amdgcn_wave_barrier();
+  } else if (c > 0) {
+    // at most k candidates: all of them
+    for (int t = lane; t < c; t += 64) {
+      sm->tidx[t] = sm->ridx[t];
+      sm->ts[t] = sm->rs[t];
+    }
+    nt = c;
     __builtin_amdgcn_wave_barrier();
   }
 
@@ -599,7 +629,7 @@ __global__ __launch_bounds__(256) void pf_finish_kernel(PfArgs a) {
   tlo = wave_sum_i32(tlo);
   if (anchor && lane == 0) {
     sm->cidx[0] = 0;
-    sm->cw[0] = sm->rs[c + nwin];
+    sm->cw[0] = sm->rs[c];
   }
   for (int t = lane; t < nt; t += 64) {
     const int32_t j = sm->tidx[t];
@@ -612,7 +642,7 @@ __global__ __launch_bounds__(256) void pf_finish_kernel(PfArgs a) {
   for (int t = lane; t < nwin; t += 64) {
     const int pos = anchor + tlo + t;
     sm->cidx[pos] = (int32_t)(w_lo + t);
-    sm->cw[pos] = sm->rs[c + t];
+    sm->cw[pos] = sm->rs[wbase + t];
   }
   __builtin_amdgcn_wave_barrier();
   if (a.sel_idx) {
@@ -622,61 +652,112 @@ __global__ __launch_bounds__(256) void pf_finish_kernel(PfArgs a) {
   if (a.sel_count && lane == 0) a.sel_count[grow] = count;
   if (!a.out) return;
 
-  // ---- float64 softmax over the set
-  double zmax = -INFINITY;
-  for (int t = lane; t < count; t += 64) zmax = fmax(zmax, a.scale * sm->cw[t]);
-  zmax = wave_max_f64(zmax);
-  double zsum = 0.0;
-  for (int t = lane; t < count; t += 64) {
-    const double w = exp(a.scale * sm->cw[t] - zmax);
-    sm->cw[t] = w;
-    zsum += w;
-  }
-  zsum = wave_sum_f64(zsum);
-  __builtin_amdgcn_wave_barrier();
-
-  // ---- weighted V rows: a row is LPR lanes x 16 bytes, so one load instruction covers RPI rows;
-  // lane group gq = lane / LPR takes the set entries t = gq (mod RPI), then the groups are summed.
-  constexpr int LPR = RB / 16, RPI = 64 / LPR, EPC = BF16 ? 8 : 4, U = 8;
-  const int gq = lane / LPR, cc = lane % LPR;
-  double acc[EPC];
-#pragma unroll
-  for (int e = 0; e < EPC; ++e) acc[e] = 0.0;
-  for (int t0 = 0; t0 < count; t0 += U * RPI) {
-    uint4 x[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int t = t0 + u * RPI + gq;
-      x[u] = t < count ? *(const uint4*)(vb + (size_t)sm->cidx[t] * RB + cc * 16) : make_uint4(0u, 0u, 0u, 0u);
+  // ---- softmax over the set and the weighted V rows: lane group gq takes the entries
+  // t = gq (mod RPI), each lane a 16-byte chunk of the row; then the groups are summed.
+  constexpr int U = 8;
+  if constexpr (BF16) {
+    const float sc = (float)a.scale;
+    float zmax = -INFINITY;
+    for (int t = lane; t < count; t += 64) zmax = fmaxf(zmax, sc * (float)sm->cw[t]);
+    zmax = wave_max_f32(zmax);
+    float zsum = 0.f;
+    for (int t = lane; t < count; t += 64) {
+      const float w = __expf(sc * (float)sm->cw[t] - zmax);
+      sm->cw[t] = (double)w;
+      zsum += w;
     }
+    zsum = wave_sum_f32(zsum);
+    __builtin_amdgcn_wave_barrier();
+    float acc[EPC];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int t = t0 + u * RPI + gq;
-      const double w = t < count ? sm->cw[t] : 0.0;
-      const uint32_t xs[4] = {x[u].x, x[u].y, x[u].z, x[u].w};
+    for (int e = 0; e < EPC; ++e) acc[e] = 0.f;
+    auto accumulate = [&](const uint4 (&x)[U], const float (&w)[U]) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        if constexpr (BF16) {
-          acc[2 * e] = fma(w, (double)bf16_lo(xs[e]), acc[2 * e]);
-          acc[2 * e + 1] = fma(w, (double)bf16_hi(xs[e]), acc[2 * e + 1]);
-        } else {
-          acc[e] = fma(w, (double)__uint_as_float(xs[e]), acc[e]);
+      for (int u = 0; u < U; ++u) {
+        const uint32_t xs[4] = {x[u].x, x[u].y, x[u].z, x[u].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          acc[2 * e] = fmaf(w[u], bf16_lo(xs[e]), acc[2 * e]);
+          acc[2 * e + 1] = fmaf(w[u], bf16_hi(xs[e]), acc[2 * e + 1]);
         }
       }
+    };
+    for (int t0 = 0; t0 < count; t0 += U * RPI) {
+      uint4 x[U];
+      float w[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int t = t0 + u * RPI + gq;
+        const bool ok = t < count;
+        x[u] = ok ? *(const uint4*)(vb + (size_t)sm->cidx[t] * RB + cc * 16) : make_uint4(0u, 0u, 0u, 0u);
+        w[u] = ok ? (float)sm->cw[t] : 0.f;
+      }
+      accumulate(x, w);
+    }
+#pragma unroll
+    for (int o = LPR; o < 64; o <<= 1)
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) acc[e] += __shfl_xor(acc[e], o);
+    if (gq == 0) {
+      const float inv = 1.0f / zsum;
+      float4* dst = (float4*)(a.out + grow * D + cc * EPC);
+#pragma unroll
+      for (int e = 0; e < EPC / 4; ++e)
+        dst[e] = make_float4(acc[4 * e] * inv, acc[4 * e + 1] * inv, acc[4 * e + 2] * inv, acc[4 * e + 3] * inv);
+    }
+  } else {
+    double zmax = -INFINITY;
+    for (int t = lane; t < count; t += 64) zmax = fmax(zmax, a.scale * sm->cw[t]);
+    zmax = wave_max_f64(zmax);
+    double zsum = 0.0;
+    for (int t = lane; t < count; t += 64) {
+      const double w = exp(a.scale * sm->cw[t] - zmax);
+      sm->cw[t] = w;
+      zsum += w;
+    }
+    zsum = wave_sum_f64(zsum);
+    __builtin_amdgcn_wave_barrier();
+    double acc[EPC];
+#pragma unroll
+    for (int e = 0; e < EPC; ++e) acc[e] = 0.0;
+    for (int t0 = 0; t0 < count; t0 += U * RPI) {
+      uint4 x[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int t = t0 + u * RPI + gq;
+        x[u] = t < count ? *(const uint4*)(vb + (size_t)sm->cidx[t] * RB + cc * 16) : make_uint4(0u, 0u, 0u, 0u);
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int t = t0 + u * RPI + gq;
+        const double w = t < count ? sm->cw[t] : 0.0;
+        acc[0] = fma(w, (double)__uint_as_float(x[u].x), acc[0]);
+        acc[1] = fma(w, (double)__uint_as_float(x[u].y), acc[1]);
+        acc[2] = fma(w, (double)__uint_as_float(x[u].z), acc[2]);
+        acc[3] = fma(w, (double)__uint_as_float(x[u].w), acc[3]);
+      }
+    }
+#pragma unroll
+    for (int o = LPR; o < 64; o <<= 1)
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) acc[e] += __shfl_xor(acc[e], o);
+    if (gq == 0) {
+      float4* dst = (float4*)(a.out + grow * D + cc * EPC);
+      dst[0] = make_float4((float)(acc[0] / zsum), (float)(acc[1] / zsum), (float)(acc[2] / zsum), (float)(acc[3] / zsum));
     }
   }
-#pragma unroll
-  for (int o = LPR; o < 64; o <<= 1)
-#pragma unroll
-    for (int e = 0; e < EPC; ++e) acc[e] += __shfl_xor(acc[e], o);
-  if (gq == 0) {
-    float r[EPC];
-#pragma unroll
-    for (int e = 0; e < EPC; ++e) r[e] = (float)(acc[e] / zsum);
-    float4* dst = (float4*)(a.out + grow * D + cc * EPC);
-#pragma unroll
-    for (int e = 0; e < EPC / 4; ++e) dst[e] = make_float4(r[4 * e], r[4 * e + 1], r[4 * e + 2], r[4 * e + 3]);
-  }
+}
+
+// pf_finish: one wave per query row, 4 rows per block (consecutive rows of one head).
+template <int D, bool BF16>
+__global__ __launch_bounds__(256) void pf_finish_kernel(PfArgs a) {
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  const int wave = threadIdx.x >> 6;
+  PfRowSmem smv;
+  smv.carve(smem_raw + wave * a.wave_smem, a.slot, a.topk, a.set_cap);
+  const size_t grow = (size_t)blockIdx.x * 4 + wave;  // (b*Hq + h) * n_q + i
+  if (grow >= (size_t)a.rows) return;
+  pf_row<D, BF16>(a, &smv, grow);
 }
 
 // ---------------------------------------------------------------------------------------------
