@@ -139,52 +139,49 @@ __device__ __forceinline__ bool pf_is_cand(int64_t j, int64_t p, int64_t n, int3
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
-// Reads of a row list in global memory that other waves of the block may have written this step:
-// device-scope loads, so they are served past this CU's vector cache.
-__device__ __forceinline__ uint2 list_load(const uint2* p) {
-  const uint64_t x = __hip_atomic_load((const uint64_t*)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  return make_uint2((uint32_t)x, (uint32_t)(x >> 32));
-}
-
-// Prune one row's list (one wave): keep the entries whose upper bound reaches the k-th best lower
-// bound of the list (or the row's current threshold, if higher). Returns the new count; the new
-// threshold goes to *th.
+// Final cut of one row's list (one wave): keep the entries whose upper bound reaches the k-th
+// best lower bound of the list; they go to dst in list order. The list is src[0, c0) followed by
+// src[cap - c1, cap). Returns the number kept.
 template <int PER>
-__device__ int prune_row(uint2* lst, int c, float eps, int k, uint32_t* th) {
+__device__ int prune_row(const uint2* src, int c0, int c1, int cap, uint2* dst, float eps, int k) {
   const int lane = threadIdx.x & 63;
+  const int c = c0 + c1;
   uint2 e[PER];
   uint32_t lb[PER];
 #pragma unroll
   for (int t = 0; t < PER; ++t) {
     const int idx = lane + 64 * t;
-    e[t] = idx < c ? list_load(lst + idx) : make_uint2(0u, 0u);
+    e[t] = idx < c ? src[idx < c0 ? idx : cap - c1 + (idx - c0)] : make_uint2(0u, 0u);
     lb[t] = idx < c ? ord_f32(__uint_as_float(e[t].x) - eps) : 0u;
   }
   const uint32_t T = c > k ? wave_kth_largest<PER>(lb, k) : 0u;
-  const uint32_t t_new = max(T, *th);
   int nc = 0;
 #pragma unroll
   for (int t = 0; t < PER; ++t) {
     const int idx = lane + 64 * t;
-    const bool keep = idx < c && ord_f32(__uint_as_float(e[t].x) + eps) >= t_new;
+    const bool keep = idx < c && ord_f32(__uint_as_float(e[t].x) + eps) >= T;
     const uint64_t mk = __ballot(keep);
-    if (keep) lst[nc + lanes_below(mk)] = e[t];
+    if (keep) dst[nc + lanes_below(mk)] = e[t];
     nc += __popcll(mk);
   }
-  *th = t_new;
   return nc;
 }
 
-// pf_scan: one block of 512 threads per (b, h, 128 consecutive query rows). Each step stages 64
-// key rows in LDS (padded rows, double-buffered, coalesced loads). Wave w computes the 32x32
-// quadrant (rows 32*(w/2).., keys 32*(w%2)..) with v_mfma_f32_32x32x16_bf16: lane l supplies row /
-// key (l % 32) and elements 8*(l/32) .. +8 of each 16-deep slice, and holds output
+// pf_scan: one block of 512 threads per (b, h, 128 consecutive query rows). Each step scores 64
+// keys held in LDS (padded rows, two buffers) while the loads of the key tile two steps ahead are
+// in flight and the tile one step ahead is written to the other buffer. Wave w computes the
+// 32x32 quadrant (rows 32*(w/2).., keys 32*(w%2)..) with v_mfma_f32_32x32x16_bf16: lane l
+// supplies row / key (l % 32) and elements 8*(l/32) .. +8 of each 16-deep slice, and holds output
 // (row 8*(r/4) + 4*(l/32) + r%4, key l % 32) in register r.
 // Phase 1 keeps, per lane and row, the two largest fast scores it has seen. Those 128 values per
 // row belong to distinct candidate keys, so their k-th largest x_k gives the bound T = x_k - eps
 // below the row's k-th largest exact score. Phase 2 scores the keys again and appends those whose
-// upper bound reaches T, i.e. fast score >= x_k - 2 eps, to the row's list in global memory.
+// upper bound reaches T (fast score >= x_k - 2 eps) to the row's list in LDS; the lists are cut to
+// the top-k band and copied out at the end.
 constexpr int PF_TOPS_BYTES = PF_ROWS * 128 * 4;
+constexpr int PF_LIST_BYTES = 126976;  // LDS for the row lists (and the top-2 values before them)
+constexpr int PF_LCAP_MAX = PF_LIST_BYTES / (PF_ROWS * 8);
+static_assert(PF_LIST_BYTES >= PF_TOPS_BYTES, "LDS layout");
 
 template <int D>
 __global__ __launch_bounds__(512) void pf_scan_kernel(PfArgs a) {
@@ -194,12 +191,11 @@ __global__ __launch_bounds__(512) void pf_scan_kernel(PfArgs a) {
   constexpr int STRIDE = RB + 16;         // padded LDS row
   constexpr int RPP = 512 / NCH;          // key rows staged per load pass
   constexpr int PASSES = PF_KEYS / RPP;
-  constexpr int LMAX = PF_MAX_K + 96;
   constexpr int TILE_BYTES = PF_KEYS * STRIDE;
-  static_assert(2 * TILE_BYTES <= PF_TOPS_BYTES, "LDS layout");
-  // the two key tiles during the scans; the per-lane top-2 values between them
-  __shared__ __align__(16) unsigned char lds[PF_TOPS_BYTES];
-  __shared__ int lcnt[PF_ROWS];
+  static_assert(PASSES >= 1 && PASSES <= 2, "staging passes");
+  __shared__ __align__(16) unsigned char ktiles[2 * TILE_BYTES];
+  __shared__ __align__(16) unsigned char lists[PF_LIST_BYTES];
+  __shared__ int lcnt[2][PF_ROWS];  // entries appended by the waves of key half 0 / 1
   __shared__ float lthf[PF_ROWS];
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -216,9 +212,8 @@ __global__ __launch_bounds__(512) void pf_scan_kernel(PfArgs a) {
   const int64_t i0 = (nrb - 1 - (job - (int64_t)bh * nrb)) * PF_ROWS;
   const unsigned char* kb = a.k + ((size_t)b * a.Hkv + g) * (size_t)a.n * RB;
   const float knmax = __uint_as_float(a.w.knmax[(size_t)b * a.Hkv + g]);
-  const int64_t LIST = a.slot;
-
-  if (tid < PF_ROWS) lcnt[tid] = 0;
+  const int LCAP = (int)a.slot;
+  uint2* llist = (uint2*)lists;
 
   const int rq = wave >> 1, kq = wave & 1;
   const int m = lane & 31, half = lane >> 5;
@@ -240,40 +235,46 @@ __global__ __launch_bounds__(512) void pf_scan_kernel(PfArgs a) {
   const int64_t ntiles = key_hi >= 0 ? key_hi / PF_KEYS + 1 : 0;
   const bool full_rows = i0 + PF_ROWS <= a.n_q;
 
-  // Each thread stages chunk (tid % NCH) of key rows kt0 + ps*RPP + tid/NCH.
+  // Each thread stages chunk (tid % NCH) of key rows kt0 + ps*RPP + tid/NCH. Tile u is loaded
+  // into register set (u & 1) two steps before it is used.
   const int srow = tid / NCH, schunk = tid % NCH;
-  uint4 pre0 = make_uint4(0u, 0u, 0u, 0u), pre1 = pre0, pre2 = pre0, pre3 = pre0;
-  static_assert(PASSES >= 1 && PASSES <= 4, "staging passes");
-#define PF_FETCH(KT0)                                                                              \
+  uint4 r00 = make_uint4(0u, 0u, 0u, 0u), r01 = r00, r10 = r00, r11 = r00;
+#define PF_LOAD(DST0, DST1, U)                                                                     \
   {                                                                                                \
-    const int64_t key0 = (KT0) + srow;                                                             \
+    const int64_t key0 = (U) * PF_KEYS + srow;                                                     \
     const unsigned char* src = kb + (size_t)schunk * 16;                                           \
-    pre0 = *(const uint4*)(src + (size_t)(key0 < a.n ? key0 : a.n - 1) * RB);                      \
-    if (PASSES > 1) pre1 = *(const uint4*)(src + (size_t)(key0 + RPP < a.n ? key0 + RPP : a.n - 1) * RB);          \
-    if (PASSES > 2) pre2 = *(const uint4*)(src + (size_t)(key0 + 2 * RPP < a.n ? key0 + 2 * RPP : a.n - 1) * RB);  \
-    if (PASSES > 3) pre3 = *(const uint4*)(src + (size_t)(key0 + 3 * RPP < a.n ? key0 + 3 * RPP : a.n - 1) * RB);  \
+    DST0 = *(const uint4*)(src + (size_t)(key0 < a.n ? key0 : a.n - 1) * RB);                      \
+    if (PASSES > 1) DST1 = *(const uint4*)(src + (size_t)(key0 + RPP < a.n ? key0 + RPP : a.n - 1) * RB); \
   }
-#define PF_STASH(BUF)                                                                              \
+#define PF_STORE(SRC0, SRC1, U)                                                                    \
   {                                                                                                \
-    unsigned char* dst = &lds[(BUF) * TILE_BYTES + srow * STRIDE + schunk * 16];                   \
-    *(uint4*)dst = pre0;                                                                           \
-    if (PASSES > 1) *(uint4*)(dst + RPP * STRIDE) = pre1;                                          \
-    if (PASSES > 2) *(uint4*)(dst + 2 * RPP * STRIDE) = pre2;                                      \
-    if (PASSES > 3) *(uint4*)(dst + 3 * RPP * STRIDE) = pre3;                                      \
+    unsigned char* dst = &ktiles[((U) & 1) * TILE_BYTES + srow * STRIDE + schunk * 16];            \
+    *(uint4*)dst = SRC0;                                                                           \
+    if (PASSES > 1) *(uint4*)(dst + RPP * STRIDE) = SRC1;                                          \
   }
-// Scores of step t into acc (every wave), with the next tile staged meanwhile.
-#define PF_TILE(t)                                                                                 \
-  if ((t) + 1 < ntiles) PF_FETCH(((t) + 1) * PF_KEYS);                                             \
+// Prologue of a scan: tile 0 to LDS, tile 1 in flight. The loads are unconditional (tiles past
+// the end read clamped, in-bounds rows and are never used), so every path has the same loads in
+// flight and waits only for the older register set.
+#define PF_PROLOGUE()                                                                              \
+  PF_LOAD(r00, r01, 0)                                                                             \
+  PF_STORE(r00, r01, 0)                                                                            \
+  PF_LOAD(r10, r11, 1)                                                                             \
+  __syncthreads();
+// Scores of step t into acc, then tile t+2 requested into register set (t & 1), whose tile t went
+// to LDS a step ago.
+#define PF_TILE(t, SET0, SET1)                                                                     \
   acc = f32x16_t{};                                                                                \
   {                                                                                                \
-    const unsigned char* krow = &lds[((t) & 1) * TILE_BYTES + (kq * 32 + m) * STRIDE + half * 16]; \
+    const unsigned char* krow = &ktiles[((t) & 1) * TILE_BYTES + (kq * 32 + m) * STRIDE + half * 16]; \
     _Pragma("unroll") for (int st = 0; st < STEPS; ++st) {                                         \
       const uint4 w = *(const uint4*)(krow + st * 32);                                             \
       acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[st], __builtin_bit_cast(bf16x8_t, w), acc, 0, 0, 0); \
     }                                                                                              \
-  }
-#define PF_NEXT(t)                                                                                 \
-  if ((t) + 1 < ntiles) PF_STASH(((t) + 1) & 1);                                                   \
+  }                                                                                                \
+  PF_LOAD(SET0, SET1, (t) + 2)
+// End of step t: tile t+1 (register set ((t+1) & 1)) to the other LDS buffer.
+#define PF_NEXT(t, NSET0, NSET1)                                                                   \
+  if ((t) + 1 < ntiles) PF_STORE(NSET0, NSET1, (t) + 1)                                            \
   __syncthreads();
 
   // Candidate test of register r on a boundary step, in 32-bit arithmetic: with
@@ -297,33 +298,36 @@ __global__ __launch_bounds__(512) void pf_scan_kernel(PfArgs a) {
   float m1[16], m2[16];
 #pragma unroll
   for (int r = 0; r < 16; ++r) m1[r] = m2[r] = -INFINITY;
-  if (ntiles > 0) {
-    PF_FETCH(0);
-    PF_STASH(0);
+#define PF_P1_BODY(t)                                                                              \
+  {                                                                                                \
+    PF_GEOM(t)                                                                                     \
+    if (interior) {                                                                                \
+      _Pragma("unroll") for (int r = 0; r < 16; ++r) {                                             \
+        m2[r] = fmaxf(m2[r], fminf(m1[r], acc[r]));                                                \
+        m1[r] = fmaxf(m1[r], acc[r]);                                                              \
+      }                                                                                            \
+    } else {                                                                                       \
+      _Pragma("unroll") for (int r = 0; r < 16; ++r) {                                             \
+        const float x = PF_CAND(r, dl, jok) ? acc[r] : -INFINITY;                                  \
+        m2[r] = fmaxf(m2[r], fminf(m1[r], x));                                                     \
+        m1[r] = fmaxf(m1[r], x);                                                                   \
+      }                                                                                            \
+    }                                                                                              \
   }
-  __syncthreads();
-  for (int64_t t = 0; t < ntiles; ++t) {
-    PF_TILE(t)
-    PF_GEOM(t)
-    if (interior) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        m2[r] = fmaxf(m2[r], fminf(m1[r], acc[r]));
-        m1[r] = fmaxf(m1[r], acc[r]);
-      }
-    } else {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float x = PF_CAND(r, dl, jok) ? acc[r] : -INFINITY;
-        m2[r] = fmaxf(m2[r], fminf(m1[r], x));
-        m1[r] = fmaxf(m1[r], x);
-      }
+  PF_PROLOGUE()
+  for (int64_t t = 0; t < ntiles; t += 2) {
+    PF_TILE(t, r00, r01)
+    PF_P1_BODY(t)
+    PF_NEXT(t, r10, r11)
+    if (t + 1 < ntiles) {
+      PF_TILE(t + 1, r10, r11)
+      PF_P1_BODY(t + 1)
+      PF_NEXT(t + 1, r00, r01)
     }
-    PF_NEXT(t)
   }
 
   // ---- thresholds: row R's 128 values sit at tops[R][64 * kq + 2 * m + {0, 1}]
-  float* tops = (float*)lds;
+  float* tops = (float*)lists;
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     const int row = row_base + 8 * (r / 4) + (r % 4);
@@ -347,61 +351,74 @@ __global__ __launch_bounds__(512) void pf_scan_kernel(PfArgs a) {
 #pragma unroll
   for (int r = 0; r < 16; ++r) thf[r] = lthf[row_base + 8 * (r / 4) + (r % 4)];
 
-  // ---- phase 2: append every candidate key whose upper bound reaches the row's bound
-  if (ntiles > 0) {
-    PF_FETCH(0);
-    PF_STASH(0);
-  }
-  __syncthreads();
-  for (int64_t t = 0; t < ntiles; ++t) {
-    PF_TILE(t)
-    PF_GEOM(t)
+  // ---- phase 2: append every candidate key whose upper bound reaches the row's bound. A row's
+  // list has LCAP slots; the wave of key half 0 fills them from the front, the wave of half 1 from
+  // the back, each counting its own entries in registers (uniform per half-wave). Writes stay in
+  // the row's slots; if the two ends cross, the row is marked for the exact path.
+  int ncnt[16];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      bool ok = acc[r] >= thf[r];
-      const int row = row_base + 8 * (r / 4) + (r % 4);
-      if (!interior) ok = ok && PF_CAND(r, dl, jok);
-      const uint64_t mk = __ballot(ok);
-      if (mk) {
-        // lanes 0-31 hold block row `row` of half 0, lanes 32-63 the row 4 below it
-        const uint32_t mine = half ? (uint32_t)(mk >> 32) : (uint32_t)mk;
-        int base = 0;
-        if ((lane & 31) == 0 && mine) base = atomicAdd(&lcnt[row], __popc(mine));
-        base = __shfl(base, lane & 32);
-        if (ok) {
-          const int slot = base + __popc(mine & ((1u << (lane & 31)) - 1u));
-          if (slot < LIST)
-            a.w.surv[((size_t)bh * a.n_q + i0 + row) * (size_t)LIST + slot] = make_uint2(__float_as_uint(acc[r]), (uint32_t)j);
-        }
-      }
-    }
-    PF_NEXT(t)
+  for (int r = 0; r < 16; ++r) ncnt[r] = 0;
+#define PF_P2_BODY(t)                                                                              \
+  {                                                                                                \
+    PF_GEOM(t)                                                                                     \
+    _Pragma("unroll") for (int r = 0; r < 16; ++r) {                                               \
+      bool ok = acc[r] >= thf[r];                                                                  \
+      if (!interior) ok = ok && PF_CAND(r, dl, jok);                                               \
+      const uint64_t mk = __ballot(ok);                                                            \
+      if (mk) {                                                                                    \
+        /* lanes 0-31 hold block row `row` of half 0, lanes 32-63 the row 4 below it */           \
+        const uint32_t mine = half ? (uint32_t)(mk >> 32) : (uint32_t)mk;                          \
+        if (ok) {                                                                                  \
+          const int row = row_base + 8 * (r / 4) + (r % 4);                                        \
+          const int s = ncnt[r] + __popc(mine & ((1u << m) - 1u));                                 \
+          if (s < LCAP) llist[row * LCAP + (kq ? LCAP - 1 - s : s)] = make_uint2(__float_as_uint(acc[r]), (uint32_t)j); \
+        }                                                                                          \
+        ncnt[r] += __popc(mine);                                                                   \
+      }                                                                                            \
+    }                                                                                              \
   }
-  // The list entries written above must have left their waves before other waves read them.
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-  __syncthreads();
+  PF_PROLOGUE()
+  for (int64_t t = 0; t < ntiles; t += 2) {
+    PF_TILE(t, r00, r01)
+    PF_P2_BODY(t)
+    PF_NEXT(t, r10, r11)
+    if (t + 1 < ntiles) {
+      PF_TILE(t + 1, r10, r11)
+      PF_P2_BODY(t + 1)
+      PF_NEXT(t + 1, r00, r01)
+    }
+  }
 
-  // Final prune to the top-k band and hand-over of the counts: wave w takes rows w, w+8, ...
+  // per-row counts of both halves, then the final cut to the top-k band, out to global memory with
+  // the counts: wave w takes rows w, w+8, ...
+  if (m == 0) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) lcnt[kq][row_base + 8 * (r / 4) + (r % 4)] = ncnt[r];
+  }
+  __syncthreads();
   for (int row = wave; row < PF_ROWS; row += 8) {
     const int64_t i = i0 + row;
     if (i >= a.n_q) continue;
     const size_t grow = (size_t)bh * a.n_q + i;
-    const int c = lcnt[row];
-    if (c > LIST) {
+    const int c0 = lcnt[0][row], c1 = lcnt[1][row];
+    if (c0 + c1 > LCAP) {
       if (lane == 0) a.w.cnt[grow] = PF_OVERFLOW;
       continue;
     }
     const float eps = PF_EPS_COEF * a.w.qn[grow] * knmax + 1e-30f;
-    uint32_t thr = 0u;
-    const int nc = prune_row<(LMAX + 63) / 64>(a.w.surv + grow * (size_t)LIST, c, eps, a.topk, &thr);
+    const int nc = prune_row<(PF_LCAP_MAX + 63) / 64>(llist + row * LCAP, c0, c1, LCAP, a.w.surv + grow * (size_t)LCAP,
+                                                       eps, a.topk);
     if (lane == 0) a.w.cnt[grow] = (uint32_t)nc;
   }
-#undef PF_FETCH
-#undef PF_STASH
+#undef PF_LOAD
+#undef PF_STORE
+#undef PF_PROLOGUE
 #undef PF_TILE
 #undef PF_NEXT
 #undef PF_CAND
 #undef PF_GEOM
+#undef PF_P1_BODY
+#undef PF_P2_BODY
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -802,7 +819,7 @@ hipError_t launch_prefill(const PrefillLaunch& L, hipStream_t stream) {
   pa.n = L.n;
   pa.n_q = L.n_q;
   pa.q_pos0 = L.q_pos0;
-  pa.slot = pf_list(L.topk);
+  pa.slot = (int64_t)L.topk + 48 < PF_LCAP_MAX ? (int64_t)L.topk + 48 : PF_LCAP_MAX;
   pa.Hq = L.Hq;
   pa.Hkv = L.Hkv;
   pa.G = L.G;
@@ -811,6 +828,7 @@ hipError_t launch_prefill(const PrefillLaunch& L, hipStream_t stream) {
   pa.causal = L.causal;
   pa.set_cap = 1 + L.W + L.topk;
   pa.exact_all = (!L.bf16 || L.topk > PF_MAX_K || (L.flags & 1)) ? 1 : 0;
+  static_assert(PF_MAX_K + 16 <= PF_LCAP_MAX, "list room above k");
   pa.scale = L.scale;
   pa.rows = (int64_t)L.B * L.Hq * L.n_q;
   pa.wave_smem = (PfRowSmem::bytes(pa.slot, L.topk, pa.set_cap) + 255) & ~(size_t)255;
