@@ -10,7 +10,8 @@ bandwidth-bound core of the hot path.
 Workload (default): the 1M-token GQA decode: batch 1, 32 query heads sharing 8 kv heads, d=128,
 n = 2^20 bf16 keys, W=512, k=64, seeded synthetic inputs with a heavy anchor key and planted
 high-score keys (workloads/synth.py). A step is one topo_attn_decode call over all 32 heads,
-inputs resident in HBM. The 128K-context batch-4 decode is reported alongside.
+inputs resident in HBM. The 128K-context batch-4 decode and the causal 8K-token prefill (matrix-core
+key scan, reported against the bf16 MFMA peak) are reported alongside.
 
 One JSON line on stdout; progress on stderr.
 """
@@ -27,30 +28,39 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X published HBM3E bandwidth
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X published dense bf16 matrix peak
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def kernel_source_hash() -> str:
+# Sources that define each measured kernel; a stored counter reading applies only while they are
+# unchanged.
+KERNEL_SOURCES = {
+    "kscan": ("topo_decode.hip", "topo_device.h", "topo_internal.h"),
+    "pf_scan": ("topo_prefill.hip", "topo_device.h", "topo_internal.h"),
+}
+
+
+def kernel_source_hash(kernel: str) -> str:
     h = hashlib.sha256()
-    for name in ("topo_decode.hip", "topo_device.h", "topo_internal.h"):
+    for name in KERNEL_SOURCES[kernel]:
         with open(os.path.join(ROOT, "dynamic_sparse_transformer_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload: str):
-    """HBM bytes per key-scan launch from the committed counter summary, if it was taken on the
-    current kernel source (else None)."""
-    path = os.path.join(ROOT, "profiles", "kscan_traffic.json")
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch of `kernel` on `workload` from the committed counter summary
+    (profiles/hbm_traffic.json), if it was taken on the current kernel source (else None)."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
-        rec = json.load(f)
+        rec = json.load(f).get(kernel, {})
     entry = rec.get(workload)
-    if not entry or rec.get("kernel_source_hash") != kernel_source_hash():
+    if not entry or rec.get("kernel_source_hash") != kernel_source_hash(kernel):
         return None
     return entry.get("hbm_bytes_per_launch")
 
@@ -117,6 +127,75 @@ def run_decode_bench(cfg: int, steps: int, warmup: int):
     return res
 
 
+def run_prefill_bench(cfg: int, steps: int, warmup: int):
+    """Whole-prompt causal prefill (every position of the prompt is a query) with the key-scan
+    kernel timed by HIP events on the library's stream; a few rows are checked against the oracle."""
+    import numpy as np
+    import torch
+
+    import dynamic_sparse_transformer_amd as topo
+    from workloads import make_workload
+
+    w = make_workload(cfg)
+    s = w.spec
+
+    def dev(arr):
+        if s.dtype == "bf16":
+            return torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(arr).cuda()
+
+    q, k, v = dev(w.q), dev(w.k), dev(w.v)
+    scale = float(s.softmax_scale)
+    n_q = s.n_ctx
+    ws = torch.empty(topo.topo_workspace_bytes(q, k, s.W, s.k, scale, q_pos0=0, op=topo.TOPO_OP_PREFILL),
+                     dtype=torch.uint8, device="cuda")
+    out = torch.empty((s.B, s.Hq, n_q, s.d), dtype=torch.float32, device="cuda")
+    sel = torch.empty((s.B, s.Hq, n_q, 1 + s.W + s.k), dtype=torch.int32, device="cuda")
+    cnt = torch.empty((s.B, s.Hq, n_q), dtype=torch.int32, device="cuda")
+    for _ in range(warmup):
+        topo.topo_attn_prefill(q, k, v, s.W, s.k, scale, q_pos0=0, out=out, sel_idx=sel, sel_count=cnt, workspace=ws)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for a, b in evs:
+        a.record(stream)
+        b.record(stream)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for a, b in evs:
+        topo.topo_attn_prefill_timed(q, k, v, s.W, s.k, scale, a, b, q_pos0=0, out=out, sel_idx=sel, sel_count=cnt,
+                                     workspace=ws)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    scan_ms = sum(a.elapsed_time(b) for a, b in evs) / steps
+    # algorithmic work of the scan: one q.k product per (row, candidate key); causal candidates of
+    # position p are [1, p - W], so a head has sum_p max(0, p - W) of them
+    n, W = s.n_ctx, s.W
+    cand = (n - 1 - W) * (n - W) // 2 if n > W else 0
+    flops = 2.0 * s.d * s.B * s.Hq * cand
+    # parity sample: rows spread over the prompt, every head, against the float64 oracle
+    import oracle
+    rows = [(h, i) for h in range(s.Hq) for i in (0, W, W + s.k + 1, n // 3, n // 2, n - 1)]
+    res = oracle.topo_attn_rows(w.f32("q")[0], w.f32("k")[0], w.f32("v")[0], rows, W, s.k, float(np.float32(scale)),
+                                True, 0)
+    o_gpu, s_gpu, c_gpu = out.cpu().numpy(), sel.cpu().numpy(), cnt.cpu().numpy()
+    sets_ok, rel = True, 0.0
+    for (h, i), (o, C) in res.items():
+        sets_ok &= bool(c_gpu[0, h, i] == C.size and np.array_equal(s_gpu[0, h, i, :C.size], C))
+        rel = max(rel, float(np.max(np.abs(o_gpu[0, h, i] - o)) / (np.max(np.abs(o)) + 1e-30)))
+    del q, k, v, ws, out, sel, cnt
+    torch.cuda.empty_cache()
+    tflops = flops / (scan_ms / 1e3) / 1e12
+    return {
+        "workload": s.name, "value": s.B * s.Hq * n_q / (ms / 1e3), "unit": "query rows/s", "ms_per_step": ms,
+        "roofline": {"bound": "mfma", "achieved": tflops, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": tflops / MFMA_BF16_PEAK_TFLOPS, "traffic": measured_traffic("pf_scan", s.name),
+                     "kernel": "pf_scan_kernel<128>",
+                     "kernel_us": scan_ms * 1e3, "alg_flops_per_launch": flops},
+        "parity_sample": {"rows_checked": len(res), "sets_bit_exact": sets_ok, "max_rel_err": rel},
+    }
+
+
 def cpu_baseline(res, heads: int):
     """The CPU oracle, as it stands, on a bounded sample of the same workload: the first `heads`
     query heads of batch 0. Also checks the GPU sets of those heads against it."""
@@ -150,6 +229,8 @@ def main():
     ap.add_argument("--also", type=int, nargs="*", default=[4], help="extra decode configs reported alongside")
     ap.add_argument("--cpu-heads", type=int, default=32, help="query heads in the CPU-oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--prefill", type=int, default=3,
+                    help="prefill config reported alongside (default 3: causal 8K prompt, 8 heads); 0 = none")
     ap.add_argument("--calibrate", action="store_true",
                     help="also run kernels of known traffic (for scaling hardware byte counters): a 2 GiB "
                          "read-only probe and a 256 MiB device copy")
@@ -181,6 +262,10 @@ def main():
             "kscan_frac": r["alg_bytes"] / (r["scan_ms"] / 1e3) / 1e9 / HBM_PEAK_GBS,
         })
 
+    if args.prefill:
+        log(f"[bench] prefill config {args.prefill}")
+        also.append(run_prefill_bench(args.prefill, max(3, args.steps // 5), min(args.warmup, 2)))
+
     if args.calibrate:
         # Known traffic: the probe reads every byte of a 2 GiB buffer once; the copy reads and
         # writes 256 MiB. Counter readings of these kernels give the bytes-per-count factors.
@@ -195,7 +280,7 @@ def main():
         del buf, src, dst
 
     achieved = main_res["alg_bytes"] / (main_res["scan_ms"] / 1e3) / 1e9
-    traffic = measured_traffic(s.name)
+    traffic = measured_traffic("kscan", s.name)
     roofline = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                 "kernel": "kscan_kernel<256,4,bf16>", "kernel_us": main_res["scan_ms"] * 1e3,

@@ -19,6 +19,7 @@ __all__ = [
     "TopoError", "load_library", "library_path", "topo_workspace_bytes", "topo_attn_decode",
     "topo_attn_prefill", "topo_select", "topo_attn_dense", "topo_bw_probe", "topo_strerror",
     "topo_attn_decode_timed",
+    "topo_attn_prefill_timed",
     "TOPO_FLAG_EXACT_SELECT", "TOPO_MAX_SET", "EXPORTS",
 ]
 
@@ -30,6 +31,7 @@ TOPO_OP_DECODE, TOPO_OP_PREFILL, TOPO_OP_SELECT, TOPO_OP_DENSE = 0, 1, 2, 3
 TOPO_FLAG_EXACT_SELECT = 1
 TOPO_MAX_SET = 4096
 EXPORTS = ("topo_workspace_bytes", "topo_attn_decode", "topo_attn_decode_timed", "topo_attn_prefill",
+           "topo_attn_prefill_timed",
            "topo_select", "topo_attn_dense", "topo_bw_probe", "topo_strerror")
 
 
@@ -69,6 +71,8 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
         f.restype = i32
     lib.topo_attn_decode_timed.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, sz, vp, vp, vp]
     lib.topo_attn_decode_timed.restype = i32
+    lib.topo_attn_prefill_timed.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, sz, vp, vp, vp]
+    lib.topo_attn_prefill_timed.restype = i32
     lib.topo_select.argtypes = [P, vp, vp, vp, vp, vp, sz, vp]
     lib.topo_select.restype = i32
     lib.topo_attn_dense.argtypes = [P, vp, vp, vp, vp, vp, sz, vp]
@@ -183,12 +187,8 @@ def topo_attn_decode(q, k, v, W: int, topk: int, softmax_scale: float, causal: b
                  sel_count, workspace, stream, want_sets)
 
 
-def topo_attn_decode_timed(q, k, v, W: int, topk: int, softmax_scale: float, scan_begin, scan_end,
-                           causal: bool = True, q_pos0: int | None = None, flags: int = 0, out=None,
-                           sel_idx=None, sel_count=None, workspace=None, stream=None):
-    """topo_attn_decode that also records the torch.cuda.Event pair scan_begin / scan_end around the
-    key-scan kernel on the call's stream (both events must have been recorded once, so that their
-    HIP handles exist). Read the scan time with scan_begin.elapsed_time(scan_end)."""
+def _attn_timed(name, op, q, k, v, W, topk, softmax_scale, scan_begin, scan_end, causal, q_pos0, flags, out,
+                sel_idx, sel_count, workspace, stream):
     torch = _torch()
     lib = load_library()
     q4 = q if q.dim() == 4 else q.unsqueeze(2)
@@ -197,18 +197,36 @@ def topo_attn_decode_timed(q, k, v, W: int, topk: int, softmax_scale: float, sca
     p = _params(q4, k, W, topk, softmax_scale, causal, q_pos0, flags)
     _check_tensors(q4, k, v)
     B, Hq, n_q, d = q4.shape
-    nbytes = lib.topo_workspace_bytes(ctypes.byref(p), TOPO_OP_DECODE)
+    nbytes = lib.topo_workspace_bytes(ctypes.byref(p), op)
     if nbytes == 0:
-        raise TopoError(-1, "topo_attn_decode_timed: parameters rejected")
+        raise TopoError(-1, f"{name}: parameters rejected")
     ws = _workspace(nbytes, q4.device, workspace)
     if out is None:
         out = torch.empty((B, Hq, n_q, d), dtype=torch.float32, device=q4.device)
-    rc = lib.topo_attn_decode_timed(ctypes.byref(p), _ptr(q4), _ptr(k), _ptr(v), _ptr(out), _ptr(sel_idx),
-                                    _ptr(sel_count), _ptr(ws), ctypes.c_size_t(ws.numel()), _stream(stream),
-                                    ctypes.c_void_p(scan_begin.cuda_event), ctypes.c_void_p(scan_end.cuda_event))
+    rc = getattr(lib, name)(ctypes.byref(p), _ptr(q4), _ptr(k), _ptr(v), _ptr(out), _ptr(sel_idx),
+                            _ptr(sel_count), _ptr(ws), ctypes.c_size_t(ws.numel()), _stream(stream),
+                            ctypes.c_void_p(scan_begin.cuda_event), ctypes.c_void_p(scan_end.cuda_event))
     if rc != 0:
-        raise TopoError(rc, "topo_attn_decode_timed")
+        raise TopoError(rc, name)
     return out, sel_idx, sel_count
+
+
+def topo_attn_decode_timed(q, k, v, W: int, topk: int, softmax_scale: float, scan_begin, scan_end,
+                           causal: bool = True, q_pos0: int | None = None, flags: int = 0, out=None,
+                           sel_idx=None, sel_count=None, workspace=None, stream=None):
+    """topo_attn_decode that also records the torch.cuda.Event pair scan_begin / scan_end around the
+    key-scan kernel on the call's stream (both events must have been recorded once, so that their
+    HIP handles exist). Read the scan time with scan_begin.elapsed_time(scan_end)."""
+    return _attn_timed("topo_attn_decode_timed", TOPO_OP_DECODE, q, k, v, W, topk, softmax_scale, scan_begin,
+                       scan_end, causal, q_pos0, flags, out, sel_idx, sel_count, workspace, stream)
+
+
+def topo_attn_prefill_timed(q, k, v, W: int, topk: int, softmax_scale: float, scan_begin, scan_end,
+                            causal: bool = True, q_pos0: int | None = None, flags: int = 0, out=None,
+                            sel_idx=None, sel_count=None, workspace=None, stream=None):
+    """topo_attn_prefill that also records scan_begin / scan_end around the matrix-core key scan."""
+    return _attn_timed("topo_attn_prefill_timed", TOPO_OP_PREFILL, q, k, v, W, topk, softmax_scale, scan_begin,
+                       scan_end, causal, q_pos0, flags, out, sel_idx, sel_count, workspace, stream)
 
 
 def topo_attn_prefill(q, k, v, W: int, topk: int, softmax_scale: float, causal: bool = True,

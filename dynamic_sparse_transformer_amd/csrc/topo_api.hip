@@ -79,7 +79,7 @@ int decode_like(const topo_params_t* p, const void* q, const void* k, const void
 
 int prefill_like(const topo_params_t* p, const void* q, const void* k, const void* v, float* out,
                  int32_t* sel_idx, int32_t* sel_count, void* ws, size_t ws_bytes, hipStream_t stream,
-                 bool softmax) {
+                 bool softmax, hipEvent_t ev_begin = nullptr, hipEvent_t ev_end = nullptr) {
   int rc = check_params(p, true);
   if (rc) return rc;
   if (!q || !k || !aligned16(q) || !aligned16(k)) return TOPO_EINVAL;
@@ -111,6 +111,8 @@ int prefill_like(const topo_params_t* p, const void* q, const void* k, const voi
   L.q_pos0 = p->q_pos0;
   L.scale = (double)p->softmax_scale;
   L.eps_coef = topo::fast_score_eps_coef(p->d);
+  L.ev_scan_begin = ev_begin;
+  L.ev_scan_end = ev_end;
   return topo::launch_prefill(L, stream) == hipSuccess ? TOPO_OK : TOPO_EHIP;
 }
 
@@ -153,6 +155,13 @@ int topo_attn_prefill(const topo_params_t* p, const void* q, const void* k, cons
                       int32_t* sel_idx, int32_t* sel_count, void* workspace, size_t ws_bytes,
                       hipStream_t stream) {
   return prefill_like(p, q, k, v, out, sel_idx, sel_count, workspace, ws_bytes, stream, true);
+}
+
+int topo_attn_prefill_timed(const topo_params_t* p, const void* q, const void* k, const void* v, float* out,
+                            int32_t* sel_idx, int32_t* sel_count, void* workspace, size_t ws_bytes,
+                            hipStream_t stream, hipEvent_t scan_begin, hipEvent_t scan_end) {
+  if (!scan_begin || !scan_end) return TOPO_EINVAL;
+  return prefill_like(p, q, k, v, out, sel_idx, sel_count, workspace, ws_bytes, stream, true, scan_begin, scan_end);
 }
 
 int topo_select(const topo_params_t* p, const void* q, const void* k, int32_t* sel_idx, int32_t* sel_count,

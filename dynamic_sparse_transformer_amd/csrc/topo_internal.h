@@ -115,6 +115,8 @@ struct PrefillLaunch {
   int64_t n, n_q, q_pos0;
   double scale;
   float eps_coef;
+  hipEvent_t ev_scan_begin;  // optional: recorded around the key-scan launch
+  hipEvent_t ev_scan_end;
 };
 size_t prefill_workspace_bytes(int32_t B, int32_t Hq, int64_t n_q, int64_t n, int32_t d, int32_t W, int32_t k);
 hipError_t launch_prefill(const PrefillLaunch& L, hipStream_t stream);

@@ -790,6 +790,7 @@ static hipError_t launch_pf_t(const PrefillLaunch& L, const PfArgs& pa, hipStrea
                      dim3(256), 0, s, (const unsigned char*)L.k, pa.w.knmax, L.n);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if (L.ev_scan_begin) (void)hipEventRecord(L.ev_scan_begin, s);
   if (!pa.exact_all && L.topk > 0) {
     if constexpr (BF16) {
       hipLaunchKernelGGL((pf_scan_kernel<D>), dim3((unsigned)((L.n_q + PF_ROWS - 1) / PF_ROWS * L.B * L.Hq)),
@@ -798,6 +799,7 @@ static hipError_t launch_pf_t(const PrefillLaunch& L, const PfArgs& pa, hipStrea
       if (e != hipSuccess) return e;
     }
   }
+  if (L.ev_scan_end) (void)hipEventRecord(L.ev_scan_end, s);
   const size_t smem = 4 * pa.wave_smem;
   if (smem > 48 * 1024)
     (void)hipFuncSetAttribute((const void*)pf_finish_kernel<D, BF16>, hipFuncAttributeMaxDynamicSharedMemorySize,

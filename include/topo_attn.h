@@ -121,6 +121,16 @@ int topo_attn_prefill(const topo_params_t* p, const void* q, const void* k, cons
                       float* out, int32_t* sel_idx, int32_t* sel_count,
                       void* workspace, size_t ws_bytes, hipStream_t stream);
 
+/* Measurement variant of topo_attn_prefill: identical results, and additionally records the
+ * caller's events scan_begin / scan_end on `stream` immediately before and after the key-scan
+ * kernel (the matrix-core pass that scores every candidate key of every query row). The events
+ * must be valid hipEvent_t handles created by the caller; when no scan runs (k = 0, float32
+ * inputs, k above the scan's limit, or TOPO_FLAG_EXACT_SELECT) both are recorded back to back. */
+int topo_attn_prefill_timed(const topo_params_t* p, const void* q, const void* k, const void* v,
+                            float* out, int32_t* sel_idx, int32_t* sel_count,
+                            void* workspace, size_t ws_bytes, hipStream_t stream,
+                            hipEvent_t scan_begin, hipEvent_t scan_end);
+
 /* The condensate sets only (the selection of decode or prefill, chosen by n_q == 1 or not),
  * without the softmax and V reduction. sel_idx and sel_count must not be NULL. */
 int topo_select(const topo_params_t* p, const void* q, const void* k,
