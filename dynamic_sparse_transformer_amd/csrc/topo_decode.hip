@@ -39,7 +39,24 @@ float fast_score_eps_coef(int d) { return (float)(2.0 * (d + 4) * 0x1p-24 + 0x1p
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-static int64_t scan_blocks(const QueryGeom& g) { return (g.scan_hi + KS_KEYS_PER_BLOCK) / KS_KEYS_PER_BLOCK; }
+static int64_t scan_blocks(const QueryGeom& g, int runs) {
+  const int64_t span = (int64_t)KS_KEYS_PER_RUN * runs;
+  return (g.scan_hi + span) / span;
+}
+
+// Runs per key-scan block: the largest count that still leaves at least two blocks per compute
+// unit (fewer, longer blocks amortise each block's start and survivor merge; too few blocks
+// would leave compute units idle).
+static int scan_runs(const QueryGeom& g, int64_t groups) {
+  int dev = 0, cus = 256;
+  if (hipGetDevice(&dev) == hipSuccess) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0) cus = v;
+  }
+  for (int r = KS_MAX_RUNS; r > 1; r >>= 1)
+    if (scan_blocks(g, r) * groups >= 2 * (int64_t)cus) return r;
+  return 1;
+}
 static int64_t scan_slot(int32_t k) { return k + 32 < KS_WAVE_CAP ? k + 32 : KS_WAVE_CAP; }
 
 // Number of survivor-list levels: merge until the last level fits the finishing kernel's LDS.
@@ -57,7 +74,8 @@ size_t decode_workspace_bytes(int32_t B, int32_t Hq, const QueryGeom& g, int32_t
   const size_t heads = (size_t)B * Hq;
   const int64_t slot = scan_slot(k);
   int64_t nb[MAX_LEVELS];
-  const int L = survivor_levels(scan_blocks(g), slot, nb);
+  // sized for one run per block: the most blocks, so any run count chosen at launch fits
+  const int L = survivor_levels(scan_blocks(g, 1), slot, nb);
   size_t bytes = align256(heads * sizeof(HeadState));
   for (int l = 0; l < L; ++l)
     bytes += 2 * align256(heads * (size_t)nb[l] * 4) + align256(heads * (size_t)nb[l] * (size_t)slot * sizeof(uint2));
@@ -67,7 +85,9 @@ size_t decode_workspace_bytes(int32_t B, int32_t Hq, const QueryGeom& g, int32_t
 void decode_carve(void* ws, int32_t B, int32_t Hq, const QueryGeom& g, int32_t k, DecodeLaunch& L) {
   const size_t heads = (size_t)B * Hq;
   L.slot = scan_slot(k);
-  L.nlevels = survivor_levels(scan_blocks(g), L.slot, L.nblk);
+  const int GT = L.G >= 4 ? 4 : L.G;
+  L.runs = scan_runs(g, (int64_t)L.B * L.Hkv * ((L.G + GT - 1) / GT));
+  L.nlevels = survivor_levels(scan_blocks(g, L.runs), L.slot, L.nblk);
   char* p = (char*)ws;
   L.st = (HeadState*)p;
   p += align256(heads * sizeof(HeadState));
@@ -132,8 +152,9 @@ __device__ __forceinline__ void reduce_scatter(float (&A)[V][L], int s) {
 }
 
 // ---------------------------------------------------------------------------------------------
-// kscan: grid (nblk, B*Hkv, ceil(G/GT)), 256 threads = 4 waves. Wave w of block x ranks keys
-// [4096 x + 1024 w, +1024) for the GT query heads of its slice.
+// kscan: grid (nblk, B*Hkv, ceil(G/GT)), 256 threads = 4 waves. Block x ranks keys
+// [2048 runs x, +2048 runs) for the GT query heads of its slice, in `runs` runs of 4 x 512 keys
+// (wave w takes the w-th 512 keys of each run).
 //
 // A key row of RB bytes is spread over L = RB/16 lanes (one 16-byte chunk each), so every load
 // instruction is fully coalesced and each lane keeps only its chunk of the GT queries in
@@ -150,7 +171,7 @@ struct KscanArgs {
   uint2* surv;
   int64_t n, nblk, slot;
   int64_t p, w_lo, vis_hi, scan_hi;
-  int32_t Hq, Hkv, G, topk;
+  int32_t Hq, Hkv, G, topk, runs;
   float eps_coef;
 };
 
@@ -162,24 +183,12 @@ __device__ __forceinline__ void kscan_load(uint4 (&buf)[8][RB / 128], const unsi
                                            int64_t last_row, int lane) {
   constexpr int CPL = RB / 128;
   const int r = lane >> 3, s = lane & 7;
-  if (row0 + 63 <= last_row) {
-    // Whole tile in range: one base pointer, constant offsets, no branches.
-    const unsigned char* base = kb + (row0 + r) * RB + s * 16;
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+  for (int i = 0; i < 8; ++i) {
+    const int64_t row = row0 + 8 * i + r;
+    const unsigned char* p = kb + (row <= last_row ? row : last_row) * RB + s * 16;
 #pragma unroll
-      for (int c = 0; c < CPL; ++c) {
-        const unsigned char* p = base + (size_t)i * 8 * RB + c * 128;
-        buf[i][c] = TOPO_KS_NT ? ntload16(p) : *(const uint4*)p;
-      }
-  } else {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int64_t row = row0 + 8 * i + r;
-#pragma unroll
-      for (int c = 0; c < CPL; ++c)
-        buf[i][c] = row <= last_row ? ntload16(kb + row * RB + c * 128 + s * 16) : make_uint4(0u, 0u, 0u, 0u);
-    }
+    for (int c = 0; c < CPL; ++c) buf[i][c] = TOPO_KS_NT ? ntload16(p + c * 128) : *(const uint4*)(p + c * 128);
   }
 }
 
@@ -224,7 +233,12 @@ __global__ __launch_bounds__(256, TOPO_KS_MIN_BLOCKS) void kscan_kernel(KscanArg
     qn[h] = (float)sqrt(part) * (1.0f + 0x1p-20f);
   }
 
-  const int64_t key0 = (int64_t)blockIdx.x * KS_KEYS_PER_BLOCK + (int64_t)wave * KS_KEYS_PER_WAVE;
+  // The block ranks a.runs runs of KS_WAVES x KS_KEYS_PER_WAVE keys; in run r, wave w takes the
+  // KS_KEYS_PER_WAVE keys starting at run_key0(r).
+  const int64_t blk_key0 = (int64_t)blockIdx.x * KS_KEYS_PER_RUN * a.runs;
+  auto run_key0 = [&](int r) -> int64_t {
+    return blk_key0 + (int64_t)(r * KS_WAVES + wave) * KS_KEYS_PER_WAVE;
+  };
   const unsigned char* kb = a.k + (size_t)grp * (size_t)a.n * RB;
   const int64_t last_row = a.scan_hi;
   const int64_t my_off = 8 * s + (lane >> 3);  // key of this lane within a tile after the reduction
@@ -235,84 +249,148 @@ __global__ __launch_bounds__(256, TOPO_KS_MIN_BLOCKS) void kscan_kernel(KscanArg
 #pragma unroll
   for (int c = 0; c < CPL; ++c) cmax2[c] = 0.f;
 
-  // One tile in registers. Per head: partial dot products of this lane's chunks of the 8 keys
-  // of its group, then a reduce-scatter over the 8 lanes; the scores enter a register shift
-  // queue (sc[h][KS_IT-1] is the newest) so that every register index stays static. The next
-  // tile's loads are issued once this tile's chunks are consumed.
+  // One tile in registers. Per key group i (8 keys, one per lane group): partial dot products of
+  // this lane's chunks with every query of the slice, then the chunk norms; right after that the
+  // registers of group i are reloaded with group i of the next tile (of this run or the next),
+  // so loads stream out during the whole scan. The loads are unconditional (rows past the end of
+  // the scan are clamped to its last row and never selected), which keeps the wait counts exact.
+  // Then per head a reduce-scatter over the 8 lanes, and the scores enter a register shift queue
+  // (sc[h][KS_IT-1] is the newest) so that every register index stays static.
   uint4 kv[8][CPL];
-  kscan_load<RB>(kv, kb, key0, last_row, lane);
-#pragma unroll 1
-  for (int it = 0; it < KS_IT; ++it) {
+  kscan_load<RB>(kv, kb, run_key0(0), last_row, lane);
+  const int kr = lane >> 3;
+  auto tile = [&](int64_t row0, int64_t nrow0, bool more) {
+    const bool nfull = nrow0 + 63 <= last_row;
+    const unsigned char* nbase = kb + (nrow0 + kr) * RB + s * 16;
+    float P[GT][8];
 #pragma unroll
-    for (int h = 0; h < GT; ++h) {
-      float P[1][8];
+    for (int i = 0; i < 8; ++i) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
+      for (int h = 0; h < GT; ++h) {
         float acc = 0.f;
 #pragma unroll
         for (int c = 0; c < CPL; ++c) acc = dot_chunk<BF16>(kv[i][c], qv[h][c], acc);
-        P[0][i] = acc;
+        P[h][i] = acc;
       }
-      reduce_scatter<8, 1>(P, s);
-#pragma unroll
-      for (int i = 0; i + 1 < KS_IT; ++i) sc[h][i] = sc[h][i + 1];
-      sc[h][KS_IT - 1] = P[0][0];
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
 #pragma unroll
       for (int c = 0; c < CPL; ++c) cmax2[c] = fmaxf(cmax2[c], dot_chunk<BF16>(kv[i][c], kv[i][c], 0.f));
-    if (it + 1 < KS_IT) kscan_load<RB>(kv, kb, key0 + (int64_t)(it + 1) * KS_ROWS, last_row, lane);
-    const int64_t j = key0 + (int64_t)it * KS_ROWS + my_off;
+      if (more) {
+        const int64_t row = nrow0 + 8 * i + kr;
+        const unsigned char* p = nfull ? nbase + (size_t)i * 8 * RB : kb + (row <= last_row ? row : last_row) * RB + s * 16;
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) kv[i][c] = TOPO_KS_NT ? ntload16(p + c * 128) : *(const uint4*)(p + c * 128);
+      }
+    }
+#pragma unroll
+    for (int h = 0; h < GT; ++h) {
+      float Q1[1][8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) Q1[0][i] = P[h][i];
+      reduce_scatter<8, 1>(Q1, s);
+#pragma unroll
+      for (int i = 0; i + 1 < KS_IT; ++i) sc[h][i] = sc[h][i + 1];
+      sc[h][KS_IT - 1] = Q1[0][0];
+    }
+    const int64_t j = row0 + my_off;
     const bool valid = j >= 1 && j <= a.vis_hi && (j < a.w_lo || j > a.p);
     vmask = (vmask >> 1) | ((valid ? 1u : 0u) << (KS_IT - 1));
-  }
+  };
 
-  // Norm bound of every key of this wave: |k|^2 = sum over its chunks of |chunk|^2 <= sum over
-  // the chunk slots (c, s) of the largest |chunk|^2 seen in that slot (lanes with equal s share
-  // the slots). The float32 chunk norms carry relative error below 2^-19, covered by the factor.
-  float kbound2 = 0.f;
-#pragma unroll
-  for (int c = 0; c < CPL; ++c) {
-    float m = cmax2[c];
-    for (int o = L; o < 64; o <<= 1) m = fmaxf(m, __shfl_xor(m, o));
-    kbound2 += m;
-  }
-  for (int o = 1; o < L; o <<= 1) kbound2 += __shfl_xor(kbound2, o);
-  const float kmax = sqrtf(kbound2) * (1.0f + 0x1p-16f);
-  const bool any_valid = __ballot(vmask != 0u) != 0ull;
-
+  int wtotal[GT];       // survivors of each head handed to the block merge so far
+  uint32_t trun[GT];    // each head's best threshold of this wave's runs so far
 #pragma unroll
   for (int h = 0; h < GT; ++h) {
-    if (h >= nh) break;
-    const float eps = a.eps_coef * qn[h] * kmax + 1e-30f;
-    int total = 0;
-    if (any_valid) {
+    wtotal[h] = 0;
+    trun[h] = 0u;
+  }
+  bool seen_valid = false;
+  float kmax = 0.f;
+#pragma unroll 1
+  for (int r = 0; r < a.runs; ++r) {
+    const int64_t key0 = run_key0(r);
+#pragma unroll 1
+    for (int it = 0; it + 1 < KS_IT; ++it) tile(key0 + (int64_t)it * KS_ROWS, key0 + (int64_t)(it + 1) * KS_ROWS, true);
+    tile(key0 + (int64_t)(KS_IT - 1) * KS_ROWS, run_key0(r + 1), r + 1 < a.runs);
+
+    // Norm bound of every key seen so far: |k|^2 = sum over its chunks of |chunk|^2 <= sum over
+    // the chunk slots (c, s) of the largest |chunk|^2 seen in that slot (lanes with equal s
+    // share the slots). The float32 chunk norms carry relative error below 2^-19, covered by the
+    // factor.
+    float kbound2 = 0.f;
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+      float m = cmax2[c];
+      for (int o = L; o < 64; o <<= 1) m = fmaxf(m, __shfl_xor(m, o));
+      kbound2 += m;
+    }
+    for (int o = 1; o < L; o <<= 1) kbound2 += __shfl_xor(kbound2, o);
+    kmax = sqrtf(kbound2) * (1.0f + 0x1p-16f);
+    const bool any_valid = __ballot(vmask != 0u) != 0ull;
+    if (!any_valid) continue;
+    seen_valid = true;
+
+#pragma unroll
+    for (int h = 0; h < GT; ++h) {
+      if (h >= nh) break;
+      // eps grows with the norm bound, so the last run's value covers every earlier entry
+      const float eps = a.eps_coef * qn[h] * kmax + 1e-30f;
       const HeadState* hs = a.st + (size_t)b * a.Hq + h0 + h;
       // A stale value is still a valid bound: the shared threshold only ever rises.
       const uint32_t th_g = *(volatile const uint32_t*)&hs->theta;
-      // Local threshold: k distinct keys of this run have lower bounds at or above T.
+      // Local threshold: k distinct keys of this run have lower bounds at or above T; earlier
+      // runs' thresholds stay valid.
       uint32_t lb[KS_IT];
 #pragma unroll
       for (int it = 0; it < KS_IT; ++it) lb[it] = ((vmask >> it) & 1u) ? ord_f32(sc[h][it] - eps) : 0u;
-      const uint32_t T = wave_threshold<KS_IT>(lb, a.topk);
-      const uint32_t th = max(T, th_g);
+      trun[h] = max(trun[h], wave_threshold<KS_IT>(lb, a.topk));
+      const uint32_t th = max(trun[h], th_g);
       // Hand this run's survivors (upper bound at or above the threshold) to the block merge.
 #pragma unroll
       for (int it = 0; it < KS_IT; ++it) {
         const bool ok = ((vmask >> it) & 1u) && ord_f32(sc[h][it] + eps) >= th;
         const uint64_t m = __ballot(ok);
         if (ok) {
-          const int pos = total + lanes_below(m);
+          const int pos = wtotal[h] + lanes_below(m);
           if (pos < KS_WAVE_CAP)
             wbuf[wave][h][pos] = make_uint2(__float_as_uint(sc[h][it]), (uint32_t)(key0 + (int64_t)it * KS_ROWS + my_off));
         }
-        total += __popcll(m);
+        wtotal[h] += __popcll(m);
+      }
+      // Before the next run, cut a long list to the k-th best lower bound among its entries (a
+      // valid threshold: k distinct keys reach it), in place: every lane reads its entries first.
+      if (r + 1 < a.runs && wtotal[h] > KS_WAVE_CAP / 2 && wtotal[h] <= KS_WAVE_CAP) {
+        constexpr int PER = KS_WAVE_CAP / 64;
+        uint2 e[PER];
+        uint32_t lbk[PER];
+        const int c = wtotal[h];
+#pragma unroll
+        for (int t = 0; t < PER; ++t) {
+          const int idx = lane + 64 * t;
+          e[t] = idx < c ? wbuf[wave][h][idx] : make_uint2(0u, 0u);
+          lbk[t] = idx < c ? ord_f32(__uint_as_float(e[t].x) - eps) : 0u;
+        }
+        trun[h] = max(trun[h], wave_kth_largest<PER>(lbk, a.topk));
+        const uint32_t thc = max(trun[h], th_g);
+        __builtin_amdgcn_wave_barrier();
+        int nc = 0;
+#pragma unroll
+        for (int t = 0; t < PER; ++t) {
+          const int idx = lane + 64 * t;
+          const bool keep = idx < c && ord_f32(__uint_as_float(e[t].x) + eps) >= thc;
+          const uint64_t m = __ballot(keep);
+          if (keep) wbuf[wave][h][nc + lanes_below(m)] = e[t];
+          nc += __popcll(m);
+        }
+        wtotal[h] = nc;
+        __builtin_amdgcn_wave_barrier();
       }
     }
-    if (lane == 0) {
-      wcnt[wave][h] = total;
-      weps[wave][h] = any_valid ? eps : 0.f;
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int h = 0; h < GT; ++h) {
+      wcnt[wave][h] = wtotal[h];
+      weps[wave][h] = seen_valid ? a.eps_coef * qn[h] * kmax + 1e-30f : 0.f;
     }
   }
   __syncthreads();
@@ -988,6 +1066,7 @@ hipError_t launch_decode(const DecodeLaunch& L, hipStream_t stream) {
     ka.Hkv = L.Hkv;
     ka.G = L.G;
     ka.topk = L.topk;
+    ka.runs = L.runs;
     ka.eps_coef = L.eps_coef;
     const int GT = L.G >= 4 ? 4 : L.G;
     dim3 grid((unsigned)L.nblk[0], (unsigned)(L.B * L.Hkv),

@@ -7,13 +7,15 @@
 namespace topo {
 
 // Decode key scan geometry: a tile is 64 keys (one owned by each lane after the cross-lane
-// reduction), a wave ranks KS_IT tiles, a block of KS_WAVES waves ranks KS_KEYS_PER_BLOCK keys and
-// merges the survivors of its waves.
+// reduction), a wave ranks KS_IT tiles per run, a block of KS_WAVES waves ranks `runs` runs of
+// KS_KEYS_PER_RUN keys (chosen per call so that the grid still fills the chip) and merges the
+// survivors of its waves.
 constexpr int KS_ROWS = 64;
 constexpr int KS_IT = 8;
 constexpr int KS_WAVES = 4;
 constexpr int KS_KEYS_PER_WAVE = KS_ROWS * KS_IT;
-constexpr int KS_KEYS_PER_BLOCK = KS_KEYS_PER_WAVE * KS_WAVES;
+constexpr int KS_KEYS_PER_RUN = KS_KEYS_PER_WAVE * KS_WAVES;  // a block ranks 1..KS_MAX_RUNS runs
+constexpr int KS_MAX_RUNS = 16;
 constexpr int KS_MAX_K = 224;     // largest k the scan ranks (larger k: exact selection only)
 constexpr int KS_WAVE_CAP = 256;  // survivors one wave may hand to its block merge
 constexpr int MAX_SET = 4096;     // largest 1 + W + k
@@ -71,6 +73,7 @@ struct DecodeLaunch {
   int64_t nblk[MAX_LEVELS];
   int nlevels;
   int64_t slot;
+  int32_t runs;  // runs of KS_KEYS_PER_RUN keys per key-scan block
   int32_t B, Hq, Hkv, G, d, W, topk, bf16, flags;
   int64_t n;
   QueryGeom geom;

@@ -212,6 +212,16 @@ def _full_config(cfg, sample_heads):
     assert np.mean(hits) > 0.99
 
 
+@pytest.mark.parametrize("ties", [False, True])
+def test_multi_run_scan_blocks(ties):
+    """32 (batch, kv head) groups over 64K keys: enough blocks that each key-scan block ranks more
+    than one run of keys (and, with many equal scores, cuts its list between runs)."""
+    torch_cuda()
+    vals, store = random_case(900 + int(ties), 4, 32, 8, 65536, 128, "bf16", ties=ties)
+    heads = [(0, 0), (1, 7), (2, 16), (3, 31), (3, 2)]
+    compare_case(vals, store, "bf16", 64, 64, 0.088, heads=heads, what=f"multi-run ties={ties}")
+
+
 def test_config4_full_size():
     _full_config(4, [(0, 0), (1, 5), (2, 18), (3, 31)])
 
