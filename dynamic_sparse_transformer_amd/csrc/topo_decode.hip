@@ -830,21 +830,18 @@ __global__ __launch_bounds__(FIN_THREADS) void decode_finish_kernel(FinishArgs a
       if (M < a.topk) {
         exact = true;  // more survivors than LDS holds (or, impossibly, fewer than k)
       } else {
-        // A valid threshold: the k-th largest of every thread's two best lower bounds.
-        uint32_t m0 = 0u, m1 = 0u;
-        for (int f = tid; f < M; f += FIN_THREADS) {
-          const uint32_t x = sm->u.s.lbk[f];
-          m1 = max(m1, min(m0, x));
-          m0 = max(m0, x);
-        }
-        sm->hist[2 * tid] = m0;
-        sm->hist[2 * tid + 1] = m1;
+        // A valid threshold: the k-th largest of every thread's best lower bound (distinct keys;
+        // 0 if fewer than k threads hold one). With k <= 224 and 512 threads it stays close to the
+        // k-th largest of all survivors, and it needs a quarter of the search of a top-2 bound.
+        uint32_t m0 = 0u;
+        for (int f = tid; f < M; f += FIN_THREADS) m0 = max(m0, sm->u.s.lbk[f]);
+        sm->hist[tid] = m0;
         __syncthreads();
         if (tid < 64) {
-          uint32_t x[2 * FIN_THREADS / 64];
+          uint32_t x[FIN_THREADS / 64];
 #pragma unroll
-          for (int i = 0; i < 2 * FIN_THREADS / 64; ++i) x[i] = sm->hist[tid + 64 * i];
-          const uint32_t T = wave_kth_largest<2 * FIN_THREADS / 64>(x, a.topk);
+          for (int i = 0; i < FIN_THREADS / 64; ++i) x[i] = sm->hist[tid + 64 * i];
+          const uint32_t T = wave_kth_largest<FIN_THREADS / 64>(x, a.topk);
           if (tid == 0) sm->ival[5] = (int)T;
         }
         if (tid == 0) sm->ival[4] = 0;
@@ -880,18 +877,31 @@ __global__ __launch_bounds__(FIN_THREADS) void decode_finish_kernel(FinishArgs a
   }
   __syncthreads();
   if (fast) {
-    // exact rank of each short-list entry: higher score first, then lower position
-    for (int i = tid; i < nr; i += FIN_THREADS) {
+    // exact rank of each short-list entry (higher score first, then lower position): the
+    // comparisons of entry i are split into `parts` slices over all threads, summed in LDS
+    int* rank = (int*)sm->hist;
+    for (int i = tid; i < nr; i += FIN_THREADS) rank[i] = 0;
+    __syncthreads();
+    const int parts = nr < FIN_THREADS ? FIN_THREADS / nr : 1;
+    const int chunk = (nr + parts - 1) / parts;
+    for (int idx = tid; idx < nr * parts; idx += FIN_THREADS) {
+      const int i = idx % nr, part = idx / nr;
       const double si = sm->rs[i];
       const int32_t ji = sm->ridx[i];
-      int rank = 0;
-      for (int r = 0; r < nr; ++r) {
+      const int r1 = min(nr, (part + 1) * chunk);
+      int cnt = 0;
+      for (int r = part * chunk; r < r1; ++r) {
         const double sr = sm->rs[r];
-        rank += (sr > si) || (sr == si && sm->ridx[r] < ji);
+        cnt += (sr > si) || (sr == si && sm->ridx[r] < ji);
       }
-      if (rank < a.topk) {
-        sm->u.c.tidx[rank] = ji;
-        sm->u.c.ts[rank] = si;
+      if (cnt) atomicAdd(&rank[i], cnt);
+    }
+    __syncthreads();
+    for (int i = tid; i < nr; i += FIN_THREADS) {
+      const int rk = rank[i];
+      if (rk < a.topk) {
+        sm->u.c.tidx[rk] = sm->ridx[i];
+        sm->u.c.ts[rk] = sm->rs[i];
       }
     }
     nt = a.topk;
