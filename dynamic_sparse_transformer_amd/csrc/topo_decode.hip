@@ -308,6 +308,14 @@ __global__ __launch_bounds__(256, TOPO_KS_MIN_BLOCKS) void kscan_kernel(KscanArg
 #pragma unroll 1
   for (int r = 0; r < a.runs; ++r) {
     const int64_t key0 = run_key0(r);
+    // The shared thresholds are read now, so the load overlaps the run (a stale value is still a
+    // valid bound: the shared threshold only ever rises). Unconditional loads keep the wait
+    // counts of the tile stream exact.
+    uint32_t thp[GT];
+#pragma unroll
+    for (int h = 0; h < GT; ++h)
+      thp[h] = __hip_atomic_load(&a.st[(size_t)b * a.Hq + h0 + (h < nh ? h : nh - 1)].theta, __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_AGENT);
 #pragma unroll 1
     for (int it = 0; it + 1 < KS_IT; ++it) tile(key0 + (int64_t)it * KS_ROWS, key0 + (int64_t)(it + 1) * KS_ROWS, true);
     tile(key0 + (int64_t)(KS_IT - 1) * KS_ROWS, run_key0(r + 1), r + 1 < a.runs);
@@ -329,20 +337,69 @@ __global__ __launch_bounds__(256, TOPO_KS_MIN_BLOCKS) void kscan_kernel(KscanArg
     if (!any_valid) continue;
     seen_valid = true;
 
+    // Local thresholds: k distinct keys of this run have lower bounds at or above T (earlier
+    // runs' thresholds stay valid). For k <= 64 all heads share one bitwise search over the
+    // k-th largest of each lane's two best lower bounds; larger k take the exact k-th largest.
+    float eps_r[GT];
+#pragma unroll
+    for (int h = 0; h < GT; ++h) eps_r[h] = a.eps_coef * qn[h] * kmax + 1e-30f;
+    if (a.topk <= 64) {
+      uint32_t m0[GT], m1[GT], T[GT];
+#pragma unroll
+      for (int h = 0; h < GT; ++h) {
+        float x0 = -INFINITY, x1 = -INFINITY;
+#pragma unroll
+        for (int it = 0; it < KS_IT; ++it) {
+          const float x = ((vmask >> it) & 1u) ? sc[h][it] : -INFINITY;
+          x1 = fmaxf(x1, fminf(x0, x));
+          x0 = fmaxf(x0, x);
+        }
+        // lower bounds are monotone in the score, so these are the two best lower bounds
+        m0[h] = x0 == -INFINITY ? 0u : ord_f32(x0 - eps_r[h]);
+        m1[h] = x1 == -INFINITY ? 0u : ord_f32(x1 - eps_r[h]);
+        T[h] = 0u;
+      }
+      // The search only matters where it can beat the best known bound: fewer than k values
+      // above it means this run's threshold is lower (the common case after the first run).
+      bool any_search = false;
+      bool search[GT];
+#pragma unroll
+      for (int h = 0; h < GT; ++h) {
+        const uint32_t cur = max(trun[h], thp[h]);
+        search[h] = h < nh && cur < 0xFFFFFFFFu &&
+                    __popcll(__ballot(m0[h] > cur)) + __popcll(__ballot(m1[h] > cur)) >= a.topk;
+        any_search |= search[h];
+      }
+      if (any_search) {
+        for (int bit = 31; bit >= 0; --bit) {
+#pragma unroll
+          for (int h = 0; h < GT; ++h) {
+            const uint32_t cand = T[h] | (1u << bit);
+            const int c = __popcll(__ballot(m0[h] >= cand)) + __popcll(__ballot(m1[h] >= cand));
+            if (c >= a.topk) T[h] = cand;
+          }
+        }
+#pragma unroll
+        for (int h = 0; h < GT; ++h)
+          if (search[h]) trun[h] = max(trun[h], T[h]);
+      }
+    } else {
+#pragma unroll
+      for (int h = 0; h < GT; ++h) {
+        if (h >= nh) break;
+        uint32_t lb[KS_IT];
+#pragma unroll
+        for (int it = 0; it < KS_IT; ++it) lb[it] = ((vmask >> it) & 1u) ? ord_f32(sc[h][it] - eps_r[h]) : 0u;
+        trun[h] = max(trun[h], wave_kth_largest<KS_IT>(lb, a.topk));
+      }
+    }
+
 #pragma unroll
     for (int h = 0; h < GT; ++h) {
       if (h >= nh) break;
       // eps grows with the norm bound, so the last run's value covers every earlier entry
-      const float eps = a.eps_coef * qn[h] * kmax + 1e-30f;
-      const HeadState* hs = a.st + (size_t)b * a.Hq + h0 + h;
-      // A stale value is still a valid bound: the shared threshold only ever rises.
-      const uint32_t th_g = *(volatile const uint32_t*)&hs->theta;
-      // Local threshold: k distinct keys of this run have lower bounds at or above T; earlier
-      // runs' thresholds stay valid.
-      uint32_t lb[KS_IT];
-#pragma unroll
-      for (int it = 0; it < KS_IT; ++it) lb[it] = ((vmask >> it) & 1u) ? ord_f32(sc[h][it] - eps) : 0u;
-      trun[h] = max(trun[h], wave_threshold<KS_IT>(lb, a.topk));
+      const float eps = eps_r[h];
+      const uint32_t th_g = thp[h];
       const uint32_t th = max(trun[h], th_g);
       // Hand this run's survivors (upper bound at or above the threshold) to the block merge.
 #pragma unroll
