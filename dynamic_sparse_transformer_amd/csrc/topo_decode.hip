@@ -630,7 +630,6 @@ __global__ __launch_bounds__(64) void merge_lists_kernel(MergeArgs a) {
 // TOPO_FLAG_EXACT_SELECT flag all route to an exact radix select over every candidate instead.
 constexpr int FIN_THREADS = 512;
 constexpr int FIN_WAVES = FIN_THREADS / 64;
-constexpr int PRE_CAP = 2048;    // survivor lists whose counts are prefix-summed in LDS
 
 struct FinishArgs {
   const unsigned char* q;
@@ -657,7 +656,6 @@ struct FinishSmem {
       uint32_t lbk[SURV_LDS];
       uint32_t ubk[SURV_LDS];
       int32_t sidx[SURV_LDS];
-      uint32_t pre[PRE_CAP + 1];
     } s;
     struct {                       // phases 3-5
       int32_t tidx[MAX_SET];       // the top-k part (any order)
@@ -791,66 +789,69 @@ __device__ int exact_select(FinishSmem* sm, const FinishArgs& a, const unsigned 
   return nt < MAX_SET ? nt : MAX_SET;
 }
 
-// Stage the survivors of head bh into LDS. Returns their number, or -1 if they do not fit.
-__device__ int stage_survivors(FinishSmem* sm, const FinishArgs& a, int bh) {
-  const int tid = threadIdx.x;
+// Copies into LDS every survivor whose upper bound reaches `theta` (a proven bound of the head's
+// k-th best score: no other entry can be selected), with its bounds as order keys. List l is
+// read by `tpl` threads; each issues all of its loads of a batch before using any, and the
+// count of the list is only applied afterwards, so a batch costs one memory round trip. Kept
+// entries are appended in any order (one LDS atomic per wave and batch). Returns the number of
+// entries, or -1 if they do not fit.
+__device__ int stage_survivors(FinishSmem* sm, const FinishArgs& a, int bh, uint32_t theta) {
+  constexpr int BATCH = 12;
+  const int tid = threadIdx.x, lane = tid & 63;
   const int64_t nblk = a.nblk;
-  if (nblk > PRE_CAP) return -1;
+  const int slot = (int)a.slot;
   const uint32_t* bc = a.blk_cnt + (size_t)bh * nblk;
   const float* be = a.blk_eps + (size_t)bh * nblk;
-  const uint2* sv = a.surv + (size_t)bh * nblk * a.slot;
-  for (int i = tid; i < nblk; i += FIN_THREADS) {
-    const uint32_t c = bc[i];
-    sm->u.s.pre[i + 1] = c > (uint32_t)a.slot ? 0u : c;
-  }
+  const uint2* sv = a.surv + (size_t)bh * nblk * slot;
+  int tpl = 1;
+  while (tpl < 64 && (int64_t)tpl * 2 * nblk <= FIN_THREADS) tpl *= 2;
+  const int lpp = FIN_THREADS / tpl;  // lists per pass
+  if (tid == 0) sm->ival[6] = 0;
   __syncthreads();
-  if (tid < 64) {  // inclusive scan of the counts, 64 blocks at a time
-    uint32_t carry = 0;
-    for (int base = 0; base < nblk; base += 64) {
-      const int i = base + tid;
-      const uint32_t c = i < nblk ? sm->u.s.pre[i + 1] : 0u;
-      const uint32_t incl = (uint32_t)wave_incl_scan_i32((int)c) + carry;
-      if (i < nblk) sm->u.s.pre[i + 1] = incl;
-      carry = __shfl(incl, 63);
-    }
-    if (tid == 0) sm->u.s.pre[0] = 0;
-  }
-  __syncthreads();
-  const int M = (int)sm->u.s.pre[nblk];
-  if (M > SURV_LDS) return -1;
-  // Each thread copies entries f = tid, tid + 512, ... in batches of 8 independent loads.
-  constexpr int BATCH = 8;
-  for (int f0 = tid; f0 < M; f0 += FIN_THREADS * BATCH) {
-    uint2 e[BATCH];
-    float eps[BATCH];
+  for (int64_t l0 = 0; l0 < nblk; l0 += lpp) {
+    const int64_t l = l0 + tid / tpl;
+    const int sub = tid % tpl;
+    const bool lv = l < nblk;
+    uint32_t c = lv ? bc[l] : 0u;
+    const float eps = lv ? be[l] : 0.f;
+    if (c > (uint32_t)slot) c = 0u;  // overflowed list: the head is on the exact path anyway
+    for (int jb = 0; jb < slot; jb += tpl * BATCH) {  // same trip count in every lane
+      const int j0 = jb + sub;
+      uint2 e[BATCH];
 #pragma unroll
-    for (int u = 0; u < BATCH; ++u) {
-      const int f = f0 + u * FIN_THREADS;
-      e[u] = make_uint2(0u, 0u);
-      eps[u] = 0.f;
-      if (f < M) {
-        int lo = 0, hi = (int)nblk;  // largest bi with pre[bi] <= f
-        while (hi - lo > 1) {
-          const int mid = (lo + hi) >> 1;
-          if (sm->u.s.pre[mid] <= (uint32_t)f) lo = mid; else hi = mid;
+      for (int u = 0; u < BATCH; ++u) {
+        const int j = j0 + u * tpl;
+        e[u] = lv && j < slot ? sv[(size_t)l * slot + j] : make_uint2(0u, 0u);
+      }
+      uint32_t keep = 0u;
+#pragma unroll
+      for (int u = 0; u < BATCH; ++u) {
+        const int j = j0 + u * tpl;
+        const bool k = j < (int)c && ord_f32(__uint_as_float(e[u].x) + eps) >= theta;
+        keep |= (k ? 1u : 0u) << u;
+      }
+      const int n = __popc(keep);
+      const int incl = wave_incl_scan_i32(n);
+      int base = 0;
+      if (lane == 63 && incl > 0) base = atomicAdd(&sm->ival[6], incl);
+      base = __shfl(base, 63) + incl - n;
+#pragma unroll
+      for (int u = 0; u < BATCH; ++u) {
+        if ((keep >> u) & 1u) {
+          if (base < SURV_LDS) {
+            const float sf = __uint_as_float(e[u].x);
+            sm->u.s.lbk[base] = ord_f32(sf - eps);
+            sm->u.s.ubk[base] = ord_f32(sf + eps);
+            sm->u.s.sidx[base] = (int32_t)e[u].y;
+          }
+          ++base;
         }
-        e[u] = sv[(size_t)lo * a.slot + (f - sm->u.s.pre[lo])];
-        eps[u] = be[lo];
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < BATCH; ++u) {
-      const int f = f0 + u * FIN_THREADS;
-      if (f < M) {
-        const float sf = __uint_as_float(e[u].x);
-        sm->u.s.lbk[f] = ord_f32(sf - eps[u]);
-        sm->u.s.ubk[f] = ord_f32(sf + eps[u]);
-        sm->u.s.sidx[f] = (int32_t)e[u].y;
       }
     }
   }
   __syncthreads();
-  return M;
+  const int M = sm->ival[6];
+  return M > SURV_LDS ? -1 : M;
 }
 
 template <int D, bool BF16>
@@ -883,22 +884,42 @@ __global__ __launch_bounds__(FIN_THREADS) void decode_finish_kernel(FinishArgs a
     exact = (a.flags & 1) != 0 || st_over != 0 || a.topk > KS_MAX_K;
     take_all = a.n_cand <= a.topk;
     if (!take_all && !exact) {
-      const int M = stage_survivors(sm, a, bh);
+      const int M = stage_survivors(sm, a, bh, st_theta);
       if (M < a.topk) {
         exact = true;  // more survivors than LDS holds (or, impossibly, fewer than k)
       } else {
         // A valid threshold: the k-th largest of every thread's best lower bound (distinct keys;
         // 0 if fewer than k threads hold one). With k <= 224 and 512 threads it stays close to the
         // k-th largest of all survivors, and it needs a quarter of the search of a top-2 bound.
+        // Only values at or above the shared bound st_theta matter; between it and the largest
+        // value all keys share their leading bits, so the bitwise search starts below them.
         uint32_t m0 = 0u;
         for (int f = tid; f < M; f += FIN_THREADS) m0 = max(m0, sm->u.s.lbk[f]);
         sm->hist[tid] = m0;
         __syncthreads();
         if (tid < 64) {
           uint32_t x[FIN_THREADS / 64];
+          uint32_t hi = 0u;
+          int above = 0;
 #pragma unroll
-          for (int i = 0; i < FIN_THREADS / 64; ++i) x[i] = sm->hist[tid + 64 * i];
-          const uint32_t T = wave_kth_largest<FIN_THREADS / 64>(x, a.topk);
+          for (int i = 0; i < FIN_THREADS / 64; ++i) {
+            x[i] = sm->hist[tid + 64 * i];
+            hi = max(hi, x[i]);
+            above += __popcll(__ballot(x[i] >= st_theta));
+          }
+          for (int o = 32; o > 0; o >>= 1) hi = max(hi, (uint32_t)__shfl_xor((int)hi, o));
+          uint32_t T = 0u;
+          if (above >= a.topk && hi > st_theta) {
+            const int top = 31 - __builtin_clz(st_theta ^ hi);  // highest bit where they differ
+            T = top == 31 ? 0u : (hi & ~((2u << top) - 1u));
+            for (int bit = top; bit >= 0; --bit) {
+              const uint32_t cand = T | (1u << bit);
+              int c = 0;
+#pragma unroll
+              for (int i = 0; i < FIN_THREADS / 64; ++i) c += __popcll(__ballot(x[i] >= cand));
+              if (c >= a.topk) T = cand;
+            }
+          }
           if (tid == 0) sm->ival[5] = (int)T;
         }
         if (tid == 0) sm->ival[4] = 0;
@@ -920,17 +941,53 @@ __global__ __launch_bounds__(FIN_THREADS) void decode_finish_kernel(FinishArgs a
   }
   __syncthreads();
 
-  // Row scores: [0, nr) short list (fast path), then the window, then the anchor.
-  const int nscore = (fast ? nr : 0) + nwin + anchor;
-  for (int i = tid; i < nscore; i += FIN_THREADS) {
-    int64_t j;
-    if (fast && i < nr) j = sm->ridx[i];
-    else if (i - (fast ? nr : 0) < nwin) j = w_lo + (i - (fast ? nr : 0));
-    else j = 0;
-    const double sc = score_row<D, BF16>(sm, kb, j);
-    if (fast && i < nr) sm->rs[i] = sc;
-    else if (i - (fast ? nr : 0) < nwin) sm->u.c.cw[MAX_SET - nwin - 1 + (i - (fast ? nr : 0))] = sc;  // parked
-    else sm->u.c.cw[MAX_SET - 1] = sc;
+  // Row scores. Waves 0-1: the short list (fast path) and the anchor in the canonical float64
+  // order (they decide the set), one row per thread. Waves 2-7 at the same time: the window rows,
+  // whose scores only enter the softmax, with LPR lanes per row (a 16-byte chunk each, float64
+  // partial sums added across the lanes). Window scores are parked at the tail of cw, the anchor
+  // score in its last entry.
+  {
+    const int nc = (fast ? nr : 0) + anchor;
+    if (tid < 128) {
+      for (int i = tid; i < nc; i += 128) {
+        const int64_t j = (fast && i < nr) ? (int64_t)sm->ridx[i] : 0;
+        const double sc = score_row<D, BF16>(sm, kb, j);
+        if (fast && i < nr) sm->rs[i] = sc;
+        else sm->u.c.cw[MAX_SET - 1] = sc;
+      }
+    } else {
+      constexpr int LPR = RB / 16, EPC = BF16 ? 8 : 4, RPP = (FIN_THREADS - 128) / LPR, WB = 12;
+      const int t = tid - 128, rsub = t / LPR, cc = t % LPR;
+      double qv[EPC];
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) qv[e] = sm->qd[cc * EPC + e];
+      for (int r0 = 0; r0 < nwin; r0 += RPP * WB) {  // same trip count in every lane
+        uint4 x[WB];
+#pragma unroll
+        for (int u = 0; u < WB; ++u) {
+          const int row = r0 + u * RPP + rsub;
+          x[u] = row < nwin ? *(const uint4*)(kb + (size_t)(w_lo + row) * RB + cc * 16) : make_uint4(0u, 0u, 0u, 0u);
+        }
+#pragma unroll
+        for (int u = 0; u < WB; ++u) {
+          const uint32_t w4[4] = {x[u].x, x[u].y, x[u].z, x[u].w};
+          double part = 0.0;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            if constexpr (BF16) {
+              part = fma(qv[2 * e], (double)bf16_lo(w4[e]), part);
+              part = fma(qv[2 * e + 1], (double)bf16_hi(w4[e]), part);
+            } else {
+              part = fma(qv[e], (double)__uint_as_float(w4[e]), part);
+            }
+          }
+#pragma unroll
+          for (int o = 1; o < LPR; o <<= 1) part += __shfl_xor(part, o);
+          const int row = r0 + u * RPP + rsub;
+          if (cc == 0 && row < nwin) sm->u.c.cw[MAX_SET - nwin - 1 + row] = part;
+        }
+      }
+    }
   }
   __syncthreads();
   if (fast) {
