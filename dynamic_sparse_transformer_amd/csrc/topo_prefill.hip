@@ -356,25 +356,43 @@ __global__ __launch_bounds__(512) void pf_scan_kernel(PfArgs a) {
   // the back, each counting its own entries in registers (uniform per half-wave). Writes stay in
   // the row's slots; if the two ends cross, the row is marked for the exact path.
   int ncnt[16];
+  // Slot sl of register r's row at this wave's end of the list is list index (sl ^ lsgn) +
+  // lbase[r]: sl from the front (lsgn = 0), LCAP - 1 - sl from the back (lsgn = -1).
+  int lbase[16];
+  const int lsgn = kq ? -1 : 0;
 #pragma unroll
-  for (int r = 0; r < 16; ++r) ncnt[r] = 0;
+  for (int r = 0; r < 16; ++r) {
+    ncnt[r] = 0;
+    lbase[r] = (row_base + 8 * (r / 4) + (r % 4)) * LCAP + (kq ? LCAP : 0);
+  }
+// Append the lanes of register r whose test `ok` holds: lanes 0-31 hold block row `row` of half
+// 0, lanes 32-63 the row 4 below it; each half counts its own entries (ncnt, uniform per half).
+// A lane's place is the number of passing lanes below it in its half (mbcnt over the ballot,
+// with the other half's bits left out). Slots past the end are clamped onto the last one: that
+// only happens when the two ends of the list cross, which the final count check detects, and
+// the row then takes the exact path. The scores are first copied out of the MFMA result vector,
+// so that no branch keeps the whole vector live.
+#define PF_APPEND(r, OK)                                                                           \
+  {                                                                                                \
+    const bool ok = (OK);                                                                          \
+    const uint64_t mk = __ballot(ok);                                                              \
+    const uint32_t lo_ = (uint32_t)mk, hi_ = (uint32_t)(mk >> 32);                                 \
+    if (ok) {                                                                                      \
+      const int pre = (int)__builtin_amdgcn_mbcnt_hi(hi_, __builtin_amdgcn_mbcnt_lo(half ? 0u : lo_, 0u)); \
+      const int sl = min(ncnt[r] + pre, LCAP - 1);                                                 \
+      llist[(sl ^ lsgn) + lbase[r]] = make_uint2(__float_as_uint(x16[r]), (uint32_t)j);             \
+    }                                                                                              \
+    ncnt[r] += half ? __popc(hi_) : __popc(lo_);                                                   \
+  }
 #define PF_P2_BODY(t)                                                                              \
   {                                                                                                \
     PF_GEOM(t)                                                                                     \
-    _Pragma("unroll") for (int r = 0; r < 16; ++r) {                                               \
-      bool ok = acc[r] >= thf[r];                                                                  \
-      if (!interior) ok = ok && PF_CAND(r, dl, jok);                                               \
-      const uint64_t mk = __ballot(ok);                                                            \
-      if (mk) {                                                                                    \
-        /* lanes 0-31 hold block row `row` of half 0, lanes 32-63 the row 4 below it */           \
-        const uint32_t mine = half ? (uint32_t)(mk >> 32) : (uint32_t)mk;                          \
-        if (ok) {                                                                                  \
-          const int row = row_base + 8 * (r / 4) + (r % 4);                                        \
-          const int s = ncnt[r] + __popc(mine & ((1u << m) - 1u));                                 \
-          if (s < LCAP) llist[row * LCAP + (kq ? LCAP - 1 - s : s)] = make_uint2(__float_as_uint(acc[r]), (uint32_t)j); \
-        }                                                                                          \
-        ncnt[r] += __popc(mine);                                                                   \
-      }                                                                                            \
+    float x16[16];                                                                                 \
+    _Pragma("unroll") for (int r = 0; r < 16; ++r) x16[r] = acc[r];                                \
+    if (interior) {                                                                                \
+      _Pragma("unroll") for (int r = 0; r < 16; ++r) PF_APPEND(r, x16[r] >= thf[r])                \
+    } else {                                                                                       \
+      _Pragma("unroll") for (int r = 0; r < 16; ++r) PF_APPEND(r, x16[r] >= thf[r] && PF_CAND(r, dl, jok)) \
     }                                                                                              \
   }
   PF_PROLOGUE()
@@ -419,6 +437,7 @@ __global__ __launch_bounds__(512) void pf_scan_kernel(PfArgs a) {
 #undef PF_GEOM
 #undef PF_P1_BODY
 #undef PF_P2_BODY
+#undef PF_APPEND
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -573,7 +592,9 @@ __device__ void pf_row(const PfArgs& a, PfRowSmem* sm, size_t grow) {
     if (!exact) {
       c = (int)cr;
       const uint2* sv = a.w.surv + grow * (size_t)a.slot;
-      for (int t = lane; t < c; t += 64) sm->ridx[t] = (int32_t)sv[t].y;
+      // positions come from the scan and are always keys of the cache; clamping only guards
+      // the reads below
+      for (int t = lane; t < c; t += 64) sm->ridx[t] = (int32_t)min((uint32_t)sv[t].y, (uint32_t)(a.n - 1));
     }
   }
   __builtin_amdgcn_wave_barrier();
