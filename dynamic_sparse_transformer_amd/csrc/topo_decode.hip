@@ -110,20 +110,6 @@ __global__ void decode_init_kernel(HeadState* st, int nheads) {
 }
 
 // ---------------------------------------------------------------------------------------------
-// Cross-lane moves. partner<HALF> pairs every lane of a group of 2*HALF lanes with a lane of the
-// other half of that group (quad permutes and row mirrors are DPP modifiers, free on the add).
-template <int CTRL>
-__device__ __forceinline__ float dpp_f32(float x) {
-  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, false));
-}
-template <int HALF>
-__device__ __forceinline__ float partner(float x) {
-  if constexpr (HALF == 1) return dpp_f32<0xB1>(x);        // quad_perm [1,0,3,2]
-  else if constexpr (HALF == 2) return dpp_f32<0x4E>(x);   // quad_perm [2,3,0,1]
-  else if constexpr (HALF == 4) return dpp_f32<0x141>(x);  // row_half_mirror
-  else if constexpr (HALF == 8) return dpp_f32<0x140>(x);  // row_mirror
-  else return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x401F));  // xor 16
-}
 
 // One halving step of a reduce-scatter: the lanes of each half of a 2*HALF group keep their half
 // of the remaining keys, summed with the partner's copy.

@@ -207,6 +207,35 @@ __device__ __forceinline__ uint32_t wave_threshold(const uint32_t (&x)[N], int k
   return wave_kth_largest<N>(x, k);
 }
 
+// Cross-lane moves. partner<HALF> pairs every lane of a group of 2*HALF lanes with a lane of the
+// other half of that group (quad permutes and row mirrors are DPP modifiers, free on the add).
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+template <int HALF>
+__device__ __forceinline__ float partner(float x) {
+  if constexpr (HALF == 1) return dpp_f32<0xB1>(x);        // quad_perm [1,0,3,2]
+  else if constexpr (HALF == 2) return dpp_f32<0x4E>(x);   // quad_perm [2,3,0,1]
+  else if constexpr (HALF == 4) return dpp_f32<0x141>(x);  // row_half_mirror
+  else if constexpr (HALF == 8) return dpp_f32<0x140>(x);  // row_mirror
+  else return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x401F));  // xor 16
+}
+
+// Sum over aligned groups of G lanes (G = 2..32); every lane of a group gets the group's sum.
+template <int G>
+__device__ __forceinline__ float group_sum_f32(float x) {
+#pragma unroll
+  for (int hf = 1; hf < G; hf <<= 1) {
+    if (hf == 1) x += partner<1>(x);
+    else if (hf == 2) x += partner<2>(x);
+    else if (hf == 4) x += partner<4>(x);
+    else if (hf == 8) x += partner<8>(x);
+    else x += partner<16>(x);
+  }
+  return x;
+}
+
 // Block-wide reductions through a caller-provided LDS scratch of (blockDim.x / 64) entries.
 // Every thread of the block must call them; all threads get the result.
 template <int NWAVES>

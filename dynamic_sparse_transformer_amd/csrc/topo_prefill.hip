@@ -126,6 +126,7 @@ struct PfArgs {
   PfWs w;
   int64_t n, n_q, q_pos0, slot, rows;
   int32_t Hq, Hkv, G, W, topk, causal, set_cap, exact_all;
+  float eps32;  // float32 dot-product error bound coefficient: |s32 - s| <= eps32 |q| |k|
   double scale;
   size_t wave_smem;  // bytes of LDS per wave in pf_finish
 };
@@ -602,62 +603,127 @@ __device__ void pf_row(const PfArgs& a, PfRowSmem* sm, size_t grow) {
   // ---- scores: items [0, c) the list, c the anchor (if any), then the window
   const int wbase = c + anchor;
   const int nitems = wbase + nwin;
-  const int ncanon = BF16 ? wbase : nitems;
-  for (int t = lane; t < ncanon; t += 64) {
-    const int64_t j = t < c ? (int64_t)sm->ridx[t] : (t < wbase ? 0 : w_lo + (t - wbase));
-    sm->rs[t] = canonical_score_row<BF16, D>(sm->qd, kb + (size_t)j * RB);
-  }
-  if constexpr (BF16) {
-    const uint4 qv = *(const uint4*)(qrow + cc * 16);
-    constexpr int U = 4;
-    for (int t0 = 0; t0 < nwin; t0 += U * RPI) {
-      uint4 x[U];
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int t = t0 + u * RPI + gq;
-        x[u] = t < nwin ? *(const uint4*)(kb + (size_t)(w_lo + t) * RB + cc * 16) : make_uint4(0u, 0u, 0u, 0u);
-      }
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        float part = dot_chunk_bf16(qv, x[u], 0.0f);
-#pragma unroll
-        for (int o = 1; o < LPR; o <<= 1) part += __shfl_xor(part, o);
-        const int t = t0 + u * RPI + gq;
-        if (cc == 0 && t < nwin) sm->rs[wbase + t] = (double)part;
-      }
-    }
-  }
-  __builtin_amdgcn_wave_barrier();
-
   int nt = 0;
-  if (exact) {
-    nt = pf_exact_row<D, BF16>(sm, a, kb, p);
-  } else if (c > a.topk) {
-    // exact rank among the list: higher score first, then lower position. The list holds every
-    // key of the row's top-k.
-    for (int t = lane; t < c; t += 64) {
-      const double si = sm->rs[t];
-      const int32_t ji = sm->ridx[t];
-      int rank = 0;
-      for (int r = 0; r < c; ++r) {
-        const double sr = sm->rs[r];
-        rank += (sr > si) || (sr == si && sm->ridx[r] < ji);
-      }
-      if (rank < a.topk) {
-        sm->tidx[rank] = ji;
-        sm->ts[rank] = si;
+  if constexpr (BF16) {
+    // float32 scores of every item: LPR lanes per key, a 16-byte chunk each (v_dot2_f32_bf16),
+    // summed across the lanes with DPP adds. |s32 - s| <= eps32 for every item (s the exact score).
+    {
+      const uint4 qv = *(const uint4*)(qrow + cc * 16);
+      constexpr int U = 8;
+      for (int t0 = 0; t0 < nitems; t0 += U * RPI) {
+        uint4 x[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int t = t0 + u * RPI + gq;
+          const int64_t j = t < c ? (int64_t)sm->ridx[t] : (t < wbase ? 0 : w_lo + (t - wbase));
+          x[u] = t < nitems ? *(const uint4*)(kb + (size_t)j * RB + cc * 16) : make_uint4(0u, 0u, 0u, 0u);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const float part = group_sum_f32<LPR>(dot_chunk_bf16(qv, x[u], 0.0f));
+          const int t = t0 + u * RPI + gq;
+          if (cc == 0 && t < nitems) sm->rs[t] = (double)part;
+        }
       }
     }
-    nt = a.topk;
     __builtin_amdgcn_wave_barrier();
-  } else if (c > 0) {
-    // at most k candidates: all of them
-    for (int t = lane; t < c; t += 64) {
-      sm->tidx[t] = sm->ridx[t];
-      sm->ts[t] = sm->rs[t];
+    const float eps32 =
+        a.eps32 * a.w.qn[grow] * __uint_as_float(a.w.knmax[(size_t)b * a.Hkv + g]) * (1.0f + 0x1p-10f) + 1e-30f;
+    if (exact) {
+      nt = pf_exact_row<D, BF16>(sm, a, kb, p);
+    } else if (c > a.topk) {
+      // x_k = k-th largest float32 score of the list; A = entries with s32 >= x_k - 2 eps32. Every
+      // entry outside A scores below all k entries with s32 >= x_k, so the top-k lies in A, and
+      // if |A| = k it is A. Otherwise (entries within the error band of the boundary, or ties)
+      // the entries of A are ranked by their float64 canonical scores, then by position.
+      const float s0 = lane < c ? (float)sm->rs[lane] : 0.f;
+      const float s1 = lane + 64 < c ? (float)sm->rs[lane + 64] : 0.f;
+      const uint32_t key[2] = {lane < c ? ord_f32(s0) : 0u, lane + 64 < c ? ord_f32(s1) : 0u};
+      const float xk = unord_f32(wave_kth_largest<2>(key, a.topk));
+      const float thr = (xk - 2.0f * eps32) - fabsf(xk) * 0x1p-20f;
+      const bool in0 = lane < c && s0 >= thr, in1 = lane + 64 < c && s1 >= thr;
+      const uint64_t m0 = __ballot(in0), m1 = __ballot(in1);
+      const int na = __popcll(m0) + __popcll(m1);
+      if (na == a.topk) {
+        if (in0) {
+          const int pos = lanes_below(m0);
+          sm->tidx[pos] = sm->ridx[lane];
+          sm->ts[pos] = (double)s0;
+        }
+        if (in1) {
+          const int pos = __popcll(m0) + lanes_below(m1);
+          sm->tidx[pos] = sm->ridx[lane + 64];
+          sm->ts[pos] = (double)s1;
+        }
+        nt = a.topk;
+        __builtin_amdgcn_wave_barrier();
+      } else {
+        // compact A (positions to ridx[0, na), canonical scores to rs[0, na)) and rank it
+        int32_t j0 = in0 ? sm->ridx[lane] : 0, j1 = in1 ? sm->ridx[lane + 64] : 0;
+        __builtin_amdgcn_wave_barrier();
+        if (in0) sm->ridx[lanes_below(m0)] = j0;
+        if (in1) sm->ridx[__popcll(m0) + lanes_below(m1)] = j1;
+        __builtin_amdgcn_wave_barrier();
+        for (int t = lane; t < na; t += 64)
+          sm->rs[t] = canonical_score_row<BF16, D>(sm->qd, kb + (size_t)sm->ridx[t] * RB);
+        __builtin_amdgcn_wave_barrier();
+        for (int t = lane; t < na; t += 64) {
+          const double si = sm->rs[t];
+          const int32_t ji = sm->ridx[t];
+          int rank = 0;
+          for (int r = 0; r < na; ++r) {
+            const double sr = sm->rs[r];
+            rank += (sr > si) || (sr == si && sm->ridx[r] < ji);
+          }
+          if (rank < a.topk) {
+            sm->tidx[rank] = ji;
+            sm->ts[rank] = si;
+          }
+        }
+        nt = a.topk;
+        __builtin_amdgcn_wave_barrier();
+      }
+    } else if (c > 0) {
+      for (int t = lane; t < c; t += 64) {
+        sm->tidx[t] = sm->ridx[t];
+        sm->ts[t] = sm->rs[t];
+      }
+      nt = c;
+      __builtin_amdgcn_wave_barrier();
     }
-    nt = c;
+  } else {
+    // float32 inputs: float64 canonical scores throughout
+    for (int t = lane; t < nitems; t += 64) {
+      const int64_t j = t < c ? (int64_t)sm->ridx[t] : (t < wbase ? 0 : w_lo + (t - wbase));
+      sm->rs[t] = canonical_score_row<BF16, D>(sm->qd, kb + (size_t)j * RB);
+    }
     __builtin_amdgcn_wave_barrier();
+    if (exact) {
+      nt = pf_exact_row<D, BF16>(sm, a, kb, p);
+    } else if (c > a.topk) {
+      for (int t = lane; t < c; t += 64) {
+        const double si = sm->rs[t];
+        const int32_t ji = sm->ridx[t];
+        int rank = 0;
+        for (int r = 0; r < c; ++r) {
+          const double sr = sm->rs[r];
+          rank += (sr > si) || (sr == si && sm->ridx[r] < ji);
+        }
+        if (rank < a.topk) {
+          sm->tidx[rank] = ji;
+          sm->ts[rank] = si;
+        }
+      }
+      nt = a.topk;
+      __builtin_amdgcn_wave_barrier();
+    } else if (c > 0) {
+      for (int t = lane; t < c; t += 64) {
+        sm->tidx[t] = sm->ridx[t];
+        sm->ts[t] = sm->rs[t];
+      }
+      nt = c;
+      __builtin_amdgcn_wave_barrier();
+    }
   }
 
   // ---- set: {0} u window u T, ascending
@@ -853,6 +919,7 @@ hipError_t launch_prefill(const PrefillLaunch& L, hipStream_t stream) {
   pa.exact_all = (!L.bf16 || L.topk > PF_MAX_K || (L.flags & 1)) ? 1 : 0;
   static_assert(PF_MAX_K + 16 <= PF_LCAP_MAX, "list room above k");
   pa.scale = L.scale;
+  pa.eps32 = L.eps_coef;
   pa.rows = (int64_t)L.B * L.Hq * L.n_q;
   pa.wave_smem = (PfRowSmem::bytes(pa.slot, L.topk, pa.set_cap) + 255) & ~(size_t)255;
   if (4 * pa.wave_smem > 160 * 1024) return hipErrorNotSupported;
