@@ -18,21 +18,22 @@ import os
 __all__ = [
     "TopoError", "load_library", "library_path", "topo_workspace_bytes", "topo_attn_decode",
     "topo_attn_prefill", "topo_select", "topo_attn_dense", "topo_bw_probe", "topo_strerror",
-    "topo_attn_decode_timed",
-    "topo_attn_prefill_timed",
-    "TOPO_FLAG_EXACT_SELECT", "TOPO_MAX_SET", "EXPORTS",
+    "topo_attn_decode_timed", "topo_attn_prefill_timed", "topo_attn_decode_certified",
+    "TOPO_FLAG_EXACT_SELECT", "TOPO_FLAG_DENSE_FALLBACK", "TOPO_CERT_RHO", "TOPO_MAX_SET", "EXPORTS",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 library_path = os.path.join(_PKG, "libtopo_attn.so")
 
 TOPO_F32, TOPO_BF16 = 0, 1
-TOPO_OP_DECODE, TOPO_OP_PREFILL, TOPO_OP_SELECT, TOPO_OP_DENSE = 0, 1, 2, 3
+TOPO_OP_DECODE, TOPO_OP_PREFILL, TOPO_OP_SELECT, TOPO_OP_DENSE, TOPO_OP_DECODE_CERTIFIED = 0, 1, 2, 3, 4
 TOPO_FLAG_EXACT_SELECT = 1
+TOPO_FLAG_DENSE_FALLBACK = 2
+TOPO_CERT_RHO = 2.0 ** -24
 TOPO_MAX_SET = 4096
-EXPORTS = ("topo_workspace_bytes", "topo_attn_decode", "topo_attn_decode_timed", "topo_attn_prefill",
-           "topo_attn_prefill_timed",
-           "topo_select", "topo_attn_dense", "topo_bw_probe", "topo_strerror")
+EXPORTS = ("topo_workspace_bytes", "topo_attn_decode", "topo_attn_decode_timed", "topo_attn_decode_certified",
+           "topo_attn_prefill", "topo_attn_prefill_timed", "topo_select", "topo_attn_dense", "topo_bw_probe",
+           "topo_strerror")
 
 
 class TopoError(RuntimeError):
@@ -73,6 +74,8 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.topo_attn_decode_timed.restype = i32
     lib.topo_attn_prefill_timed.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, sz, vp, vp, vp]
     lib.topo_attn_prefill_timed.restype = i32
+    lib.topo_attn_decode_certified.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.topo_attn_decode_certified.restype = i32
     lib.topo_select.argtypes = [P, vp, vp, vp, vp, vp, sz, vp]
     lib.topo_select.restype = i32
     lib.topo_attn_dense.argtypes = [P, vp, vp, vp, vp, vp, sz, vp]
@@ -227,6 +230,42 @@ def topo_attn_prefill_timed(q, k, v, W: int, topk: int, softmax_scale: float, sc
     """topo_attn_prefill that also records scan_begin / scan_end around the matrix-core key scan."""
     return _attn_timed("topo_attn_prefill_timed", TOPO_OP_PREFILL, q, k, v, W, topk, softmax_scale, scan_begin,
                        scan_end, causal, q_pos0, flags, out, sel_idx, sel_count, workspace, stream)
+
+
+def topo_attn_decode_certified(q, k, v, W: int, topk: int, softmax_scale: float, dense_fallback: bool = False,
+                               causal: bool = True, q_pos0: int | None = None, flags: int = 0, out=None,
+                               sel_idx=None, sel_count=None, rho=None, workspace=None, stream=None):
+    """topo_attn_decode plus the exactness certificate: rho (B, Hq) float32, an upper bound on the
+    softmax mass left out of each query's set. With dense_fallback, queries with
+    rho >= TOPO_CERT_RHO get dense attention in out. Returns (out, sel_idx, sel_count, rho)."""
+    torch = _torch()
+    lib = load_library()
+    q4 = q if q.dim() == 4 else q.unsqueeze(2)
+    if q_pos0 is None:
+        q_pos0 = k.shape[2] - q4.shape[2]
+    if dense_fallback:
+        flags |= TOPO_FLAG_DENSE_FALLBACK
+    p = _params(q4, k, W, topk, softmax_scale, causal, q_pos0, flags)
+    _check_tensors(q4, k, v)
+    B, Hq, n_q, d = q4.shape
+    nbytes = lib.topo_workspace_bytes(ctypes.byref(p), TOPO_OP_DECODE_CERTIFIED)
+    if nbytes == 0:
+        raise TopoError(-1, "topo_attn_decode_certified: parameters rejected")
+    ws = _workspace(nbytes, q4.device, workspace)
+    if out is None:
+        out = torch.empty((B, Hq, n_q, d), dtype=torch.float32, device=q4.device)
+    if sel_idx is None:
+        sel_idx = torch.empty((B, Hq, n_q, 1 + int(W) + int(topk)), dtype=torch.int32, device=q4.device)
+    if sel_count is None:
+        sel_count = torch.empty((B, Hq, n_q), dtype=torch.int32, device=q4.device)
+    if rho is None:
+        rho = torch.empty((B, Hq), dtype=torch.float32, device=q4.device)
+    rc = lib.topo_attn_decode_certified(ctypes.byref(p), _ptr(q4), _ptr(k), _ptr(v), _ptr(out), _ptr(sel_idx),
+                                        _ptr(sel_count), _ptr(rho), _ptr(ws), ctypes.c_size_t(ws.numel()),
+                                        _stream(stream))
+    if rc != 0:
+        raise TopoError(rc, "topo_attn_decode_certified")
+    return out, sel_idx, sel_count, rho
 
 
 def topo_attn_prefill(q, k, v, W: int, topk: int, softmax_scale: float, causal: bool = True,

@@ -22,7 +22,7 @@ int check_params(const topo_params_t* p, bool need_set) {
   if (p->n_q < 1 || p->q_pos0 < 0 || p->q_pos0 + p->n_q - 1 > p->n_ctx - 1) return TOPO_EINVAL;
   if (!(p->softmax_scale > 0.f) || !std::isfinite(p->softmax_scale)) return TOPO_EINVAL;
   if (p->causal != 0 && p->causal != 1) return TOPO_EINVAL;
-  if (p->flags & ~TOPO_FLAG_EXACT_SELECT) return TOPO_EINVAL;
+  if (p->flags & ~(TOPO_FLAG_EXACT_SELECT | TOPO_FLAG_DENSE_FALLBACK)) return TOPO_EINVAL;
   if (need_set) {
     if (p->W < 0 || p->k < 0) return TOPO_EINVAL;
     if ((int64_t)p->W + p->k + 1 > TOPO_MAX_SET) return TOPO_EINVAL;
@@ -37,21 +37,34 @@ topo::QueryGeom decode_geom(const topo_params_t* p) {
   return topo::make_geom(p->q_pos0, p->n_ctx, p->W, p->causal != 0);
 }
 
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Workspace of the certified decode: the decode's, then (with the dense fallback) the dense
+// attention's partials.
+size_t certified_workspace_bytes(const topo_params_t* p) {
+  size_t b = align256(topo::decode_workspace_bytes(p->B, p->Hq, decode_geom(p), p->k));
+  if (p->flags & TOPO_FLAG_DENSE_FALLBACK) b += topo::dense_workspace_bytes(p->B, p->Hq, 1, p->n_ctx, p->d);
+  return b;
+}
+
 int decode_like(const topo_params_t* p, const void* q, const void* k, const void* v, float* out,
                 int32_t* sel_idx, int32_t* sel_count, void* ws, size_t ws_bytes, hipStream_t stream,
-                bool softmax, hipEvent_t ev_begin = nullptr, hipEvent_t ev_end = nullptr) {
+                bool softmax, hipEvent_t ev_begin = nullptr, hipEvent_t ev_end = nullptr, float* rho = nullptr) {
   int rc = check_params(p, true);
   if (rc) return rc;
   if (p->n_q != 1) return TOPO_EINVAL;
+  if (!rho && (p->flags & TOPO_FLAG_DENSE_FALLBACK)) return TOPO_EINVAL;
+  if (rho && !aligned16(rho)) return TOPO_EINVAL;
   if (!q || !k || !aligned16(q) || !aligned16(k)) return TOPO_EINVAL;
   if (softmax && (!v || !out || !aligned16(v) || !aligned16(out))) return TOPO_EINVAL;
   if (!softmax && (!sel_idx || !sel_count)) return TOPO_EINVAL;
   if ((sel_idx && !aligned16(sel_idx)) || (sel_count && !aligned16(sel_count))) return TOPO_EINVAL;
   const topo::QueryGeom g = decode_geom(p);
-  const size_t need = topo::decode_workspace_bytes(p->B, p->Hq, g, p->k);
+  const size_t need = rho ? certified_workspace_bytes(p) : topo::decode_workspace_bytes(p->B, p->Hq, g, p->k);
   if (!ws || ws_bytes < need || !aligned16(ws)) return TOPO_EWORKSPACE;
 
   topo::DecodeLaunch L{};
+  L.rho = rho;
   L.q = q;
   L.k = k;
   L.v = softmax ? v : nullptr;
@@ -74,7 +87,31 @@ int decode_like(const topo_params_t* p, const void* q, const void* k, const void
   L.ev_scan_begin = ev_begin;
   L.ev_scan_end = ev_end;
   topo::decode_carve(ws, p->B, p->Hq, g, p->k, L);
-  return topo::launch_decode(L, stream) == hipSuccess ? TOPO_OK : TOPO_EHIP;
+  if (topo::launch_decode(L, stream) != hipSuccess) return TOPO_EHIP;
+  if (rho && (p->flags & TOPO_FLAG_DENSE_FALLBACK)) {
+    // dense attention for the queries the certificate does not cover (the others skip)
+    topo::DenseLaunch D{};
+    D.q = q;
+    D.k = k;
+    D.v = v;
+    D.out = out;
+    D.ws = (char*)ws + align256(topo::decode_workspace_bytes(p->B, p->Hq, g, p->k));
+    D.B = p->B;
+    D.Hq = p->Hq;
+    D.Hkv = p->Hkv;
+    D.G = p->Hq / p->Hkv;
+    D.d = p->d;
+    D.bf16 = p->dtype == TOPO_BF16;
+    D.causal = p->causal;
+    D.n = p->n_ctx;
+    D.n_q = 1;
+    D.q_pos0 = p->q_pos0;
+    D.scale = (double)p->softmax_scale;
+    D.gate = rho;
+    D.gate_min = TOPO_CERT_RHO;
+    if (topo::launch_dense(D, stream) != hipSuccess) return TOPO_EHIP;
+  }
+  return TOPO_OK;
 }
 
 int prefill_like(const topo_params_t* p, const void* q, const void* k, const void* v, float* out,
@@ -82,6 +119,7 @@ int prefill_like(const topo_params_t* p, const void* q, const void* k, const voi
                  bool softmax, hipEvent_t ev_begin = nullptr, hipEvent_t ev_end = nullptr) {
   int rc = check_params(p, true);
   if (rc) return rc;
+  if (p->flags & TOPO_FLAG_DENSE_FALLBACK) return TOPO_EINVAL;
   if (!q || !k || !aligned16(q) || !aligned16(k)) return TOPO_EINVAL;
   if (softmax && (!v || !out || !aligned16(v) || !aligned16(out))) return TOPO_EINVAL;
   if (!softmax && (!sel_idx || !sel_count)) return TOPO_EINVAL;
@@ -134,6 +172,9 @@ size_t topo_workspace_bytes(const topo_params_t* p, int op) {
       return topo::prefill_workspace_bytes(p->B, p->Hq, p->n_q, p->n_ctx, p->d, p->W, p->k);
     case TOPO_OP_DENSE:
       return topo::dense_workspace_bytes(p->B, p->Hq, p->n_q, p->n_ctx, p->d);
+    case TOPO_OP_DECODE_CERTIFIED:
+      if (p->n_q != 1) return 0;
+      return certified_workspace_bytes(p);
     default:
       return 0;
   }
@@ -149,6 +190,13 @@ int topo_attn_decode_timed(const topo_params_t* p, const void* q, const void* k,
                            hipStream_t stream, hipEvent_t scan_begin, hipEvent_t scan_end) {
   if (!scan_begin || !scan_end) return TOPO_EINVAL;
   return decode_like(p, q, k, v, out, sel_idx, sel_count, workspace, ws_bytes, stream, true, scan_begin, scan_end);
+}
+
+int topo_attn_decode_certified(const topo_params_t* p, const void* q, const void* k, const void* v, float* out,
+                               int32_t* sel_idx, int32_t* sel_count, float* rho, void* workspace, size_t ws_bytes,
+                               hipStream_t stream) {
+  if (!rho) return TOPO_EINVAL;
+  return decode_like(p, q, k, v, out, sel_idx, sel_count, workspace, ws_bytes, stream, true, nullptr, nullptr, rho);
 }
 
 int topo_attn_prefill(const topo_params_t* p, const void* q, const void* k, const void* v, float* out,
@@ -176,6 +224,7 @@ int topo_attn_dense(const topo_params_t* p, const void* q, const void* k, const 
                     void* workspace, size_t ws_bytes, hipStream_t stream) {
   int rc = check_params(p, false);
   if (rc) return rc;
+  if (p->flags & TOPO_FLAG_DENSE_FALLBACK) return TOPO_EINVAL;
   if (!q || !k || !v || !out || !aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
     return TOPO_EINVAL;
   const size_t need = topo::dense_workspace_bytes(p->B, p->Hq, p->n_q, p->n_ctx, p->d);

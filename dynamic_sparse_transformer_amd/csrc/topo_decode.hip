@@ -624,6 +624,7 @@ struct FinishArgs {
   float* out;
   int32_t* sel_idx;
   int32_t* sel_count;
+  float* rho;
   const HeadState* st;
   const uint32_t* blk_cnt;
   const float* blk_eps;
@@ -1065,6 +1066,22 @@ __global__ __launch_bounds__(FIN_THREADS) void decode_finish_kernel(FinishArgs a
     zsum += w;
   }
   zsum = block_sum_f64<FIN_WAVES>(zsum, sm->scratch);  // (contains a barrier: weights visible)
+  if (a.rho) {
+    // Exactness certificate: every candidate left out scores at most s_k, the lowest score of
+    // the top-k part, so the left-out mass relative to the dense total is at most
+    // n_omit * exp(scale * s_k - zmax) / zsum (rounded up to float32).
+    double smin = INFINITY;
+    for (int i = tid; i < nt; i += FIN_THREADS) smin = fmin(smin, sm->u.c.ts[i]);
+    smin = -block_max_f64<FIN_WAVES>(-smin, sm->scratch);
+    if (tid == 0) {
+      const int64_t n_omit = a.n_cand - nt;
+      double r = 0.0;
+      if (n_omit > 0) r = nt == 0 ? INFINITY : (double)n_omit * exp(a.scale * smin - zmax) / zsum;
+      float rf = (float)r;
+      if ((double)rf < r) rf = nextafterf(rf, INFINITY);
+      a.rho[bh] = rf;
+    }
+  }
 
   // Thread t reads 16-byte chunk (t % CPR) of rows t / CPR, + RPP, ...; a batch of BATCH rows
   // per thread is in flight together (one batch covers a set of up to RPP * BATCH rows).
@@ -1224,6 +1241,7 @@ hipError_t launch_decode(const DecodeLaunch& L, hipStream_t stream) {
   fa.out = L.out;
   fa.sel_idx = L.sel_idx;
   fa.sel_count = L.sel_count;
+  fa.rho = L.rho;
   fa.st = L.st;
   fa.blk_cnt = L.blk_cnt[last];
   fa.blk_eps = L.blk_eps[last];

@@ -34,6 +34,8 @@ struct DenseArgs {
   int64_t n, n_q, q_pos0, chunks;
   int32_t Hq, Hkv, G, causal, nslices;
   double scale;
+  const float* gate;  // may be null; else rows with gate[row] < gate_min are skipped
+  float gate_min;
 };
 
 template <bool BF16>
@@ -74,6 +76,11 @@ __global__ __launch_bounds__(256) void dense_partial_kernel(DenseArgs a) {
   const int nh = min(GT, a.G - slice * GT);
   const int64_t p = a.q_pos0 + qi;
   const int64_t vis_hi = a.causal ? p : a.n - 1;
+  if (a.gate) {  // skip the block if none of its query rows is gated in
+    bool any = false;
+    for (int h = 0; h < nh; ++h) any |= a.gate[((size_t)b * a.Hq + h0 + h) * a.n_q + qi] >= a.gate_min;
+    if (!any) return;
+  }
 
   for (int i = tid; i < GT * NCH; i += 256) {
     const int h = i / NCH, c = i % NCH;
@@ -245,8 +252,10 @@ __global__ __launch_bounds__(256) void dense_partial_kernel(DenseArgs a) {
 // One wave per (batch, query head, query): merge the chunk partials.
 template <int D>
 __global__ __launch_bounds__(64) void dense_combine_kernel(const void* partv, float* out, int64_t chunks,
-                                                           int64_t n_q, int64_t q_pos0, int64_t n, int causal) {
+                                                           int64_t n_q, int64_t q_pos0, int64_t n, int causal,
+                                                           const float* gate, float gate_min) {
   const size_t row = blockIdx.x;  // (b*Hq + h)*n_q + qi
+  if (gate && !(gate[row] >= gate_min)) return;
   const int64_t qi = (int64_t)(row % (size_t)n_q);
   const int64_t p = q_pos0 + qi;
   const int64_t vis_hi = causal ? p : n - 1;
@@ -299,6 +308,8 @@ hipError_t launch_dense(const DenseLaunch& L, hipStream_t stream) {
   da.G = L.G;
   da.causal = L.causal;
   da.scale = L.scale;
+  da.gate = L.gate;
+  da.gate_min = L.gate_min;
   // float64 accumulation (float32 inputs) needs more registers and LDS per head: fewer heads per block.
   int GT = L.G >= 4 ? 4 : L.G;
   if (!L.bf16) GT = L.d == 128 ? 1 : (L.G >= 2 ? 2 : 1);
@@ -316,10 +327,10 @@ hipError_t launch_dense(const DenseLaunch& L, hipStream_t stream) {
   const unsigned rows = (unsigned)((size_t)L.B * L.Hq * L.n_q);
   if (L.d == 128) {
     hipLaunchKernelGGL(dense_combine_kernel<128>, dim3(rows), dim3(64), 0, stream, L.ws, L.out, da.chunks, L.n_q,
-                       L.q_pos0, L.n, L.causal);
+                       L.q_pos0, L.n, L.causal, L.gate, L.gate_min);
   } else {
     hipLaunchKernelGGL(dense_combine_kernel<64>, dim3(rows), dim3(64), 0, stream, L.ws, L.out, da.chunks, L.n_q,
-                       L.q_pos0, L.n, L.causal);
+                       L.q_pos0, L.n, L.causal, L.gate, L.gate_min);
   }
   return hipGetLastError();
 }

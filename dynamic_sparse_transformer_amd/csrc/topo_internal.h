@@ -61,6 +61,7 @@ struct DecodeLaunch {
   float* out;          // may be null (select only)
   int32_t* sel_idx;    // may be null
   int32_t* sel_count;  // may be null
+  float* rho;          // may be null: the exactness certificate per query
   HeadState* st;       // [B * Hq]
   // Survivor lists, level 0 written by the key scan and level l+1 by merging groups of
   // MERGE_FAN level-l lists:
@@ -101,6 +102,8 @@ struct DenseLaunch {
   int32_t B, Hq, Hkv, G, d, bf16, causal;
   int64_t n, n_q, q_pos0;
   double scale;
+  const float* gate;  // may be null; else only rows with gate[row] >= gate_min are computed
+  float gate_min;
 };
 size_t dense_workspace_bytes(int32_t B, int32_t Hq, int64_t n_q, int64_t n, int32_t d);
 hipError_t launch_dense(const DenseLaunch& L, hipStream_t stream);

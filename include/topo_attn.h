@@ -69,6 +69,8 @@ extern "C" {
 #define TOPO_OP_PREFILL 1
 #define TOPO_OP_SELECT  2
 #define TOPO_OP_DENSE   3
+#define TOPO_OP_DECODE_CERTIFIED 4  /* topo_attn_decode_certified (includes the dense fallback's
+                                       scratch when TOPO_FLAG_DENSE_FALLBACK is set)            */
 
 /* Largest condensate set (1 + W + k) a call may ask for. */
 #define TOPO_MAX_SET 4096
@@ -76,6 +78,13 @@ extern "C" {
 /* Flag bits of topo_params_t.flags. */
 #define TOPO_FLAG_EXACT_SELECT 1  /* skip the float32 pre-ranking and select every query by the
                                      exact float64 radix path (slow; for checking)             */
+#define TOPO_FLAG_DENSE_FALLBACK 2  /* topo_attn_decode_certified only: queries whose bound rho is
+                                       not below TOPO_CERT_RHO get dense attention in out      */
+
+/* A query is certified when its bound on the left-out softmax mass is below the float32
+ * rounding unit 2^-24: the set then carries the dense softmax to float32 precision, the
+ * exactness claim of the pages (zh technical summary §2; hi technical summary §2). */
+#define TOPO_CERT_RHO 0x1p-24f
 
 typedef struct {
     int32_t B;              /* batch                                                     >= 1 */
@@ -113,6 +122,20 @@ int topo_attn_decode_timed(const topo_params_t* p, const void* q, const void* k,
                            float* out, int32_t* sel_idx, int32_t* sel_count,
                            void* workspace, size_t ws_bytes, hipStream_t stream,
                            hipEvent_t scan_begin, hipEvent_t scan_end);
+
+/* topo_attn_decode plus an exactness certificate per query. rho[B*Hq] (device, float32, written
+ * for every query) receives an upper bound on the softmax mass of the visible keys left out of
+ * the set, relative to the dense total: every left-out candidate scores at most s_k, the lowest
+ * score of the top-k part, so rho = (number of left-out candidates) * exp(scale*s_k - zmax) / Z,
+ * with zmax and Z the float64 softmax maximum and sum over the set (rounded up to float32; 0 if
+ * no candidate is left out; +inf if candidates are left out and k = 0). With
+ * TOPO_FLAG_DENSE_FALLBACK in p->flags, every query with rho >= TOPO_CERT_RHO gets the dense
+ * attention output (as topo_attn_dense) in out instead; sel_idx / sel_count still describe the
+ * condensate set. Workspace: topo_workspace_bytes(p, TOPO_OP_DECODE_CERTIFIED). Errors as
+ * topo_attn_decode, and TOPO_EINVAL if rho is NULL or not 16-byte aligned. */
+int topo_attn_decode_certified(const topo_params_t* p, const void* q, const void* k, const void* v,
+                               float* out, int32_t* sel_idx, int32_t* sel_count, float* rho,
+                               void* workspace, size_t ws_bytes, hipStream_t stream);
 
 /* Topological attention of n_q consecutive queries per (batch, query head), query i at position
  * q_pos0 + i (a whole causal prompt is q_pos0 = 0, n_q = n_ctx). Same outputs as decode, one row

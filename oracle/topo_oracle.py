@@ -39,8 +39,13 @@ import numpy as np
 __all__ = [
     "canonical_scores", "condensate_set", "softmax_weighted_v", "attend", "dense_attend",
     "omitted_mass", "certified_components", "ulp_distance_f32", "topo_attn_decode",
-    "topo_attn_rows", "dense_decode", "KEY_BLOCK",
+    "topo_attn_rows", "dense_decode", "certificate_bound", "CERT_RHO", "KEY_BLOCK",
 ]
+
+# A query is certified when its bound on the omitted softmax mass is below the float32 rounding
+# unit: the set then carries the dense softmax to float32 precision (the exactness claim of zh T§2
+# and hi T§2, excluded weights below float32 precision).
+CERT_RHO = 2.0 ** -24
 
 # Keys are processed in slices of this many rows only to bound memory; every key's score is an
 # independent sum, so the slice size does not change any result.
@@ -153,6 +158,34 @@ def omitted_mass(s: np.ndarray, C: np.ndarray, p: int, scale: float, causal: boo
     inside = np.zeros(vis_hi + 1, dtype=bool)
     inside[C] = True
     return float(w[~inside].sum() / w.sum())
+
+
+def certificate_bound(s: np.ndarray, p: int, W: int, k: int, scale: float, causal: bool = True) -> float:
+    """An upper bound on omitted_mass from what is known once the set is chosen.
+
+    Every candidate left out of the set scores at most s_k, the lowest score of the top-k part,
+    so the omitted mass relative to the dense total is at most
+        rho_hat = (number of omitted candidates) * exp(scale * s_k - zmax) / Z_C,
+    with zmax and Z_C the softmax maximum and sum over the set (as in softmax_weighted_v). It is 0
+    when no candidate is left out, and +inf when candidates are left out with k = 0 (no top-k part
+    to bound them). Reading: the pages state the claim (zh T§2, hi T§2) but give no test; this is
+    the plainest bound the selected scores support.
+    """
+    C, T = condensate_set(s, p, W, k, causal)
+    vis_hi = p if causal else s.shape[0] - 1
+    w_lo = max(0, p - W + 1)
+    pos = np.arange(vis_hi + 1)
+    n_cand = int(((pos != 0) & ~((pos >= w_lo) & (pos <= p))).sum())
+    n_omit = n_cand - T.size
+    if n_omit <= 0:
+        return 0.0
+    if T.size == 0:
+        return float("inf")
+    z = np.float64(scale) * np.asarray(s[C], dtype=np.float64)
+    zmax = z.max()
+    Z = np.cumsum(np.exp(z - zmax))[-1]
+    s_k = float(np.min(s[T]))
+    return float(n_omit * np.exp(np.float64(scale) * s_k - zmax) / Z)
 
 
 def certified_components(o_set: np.ndarray, rho: float, vmax_out: np.ndarray) -> np.ndarray:

@@ -93,3 +93,25 @@ def test_workspace_sizes():
     assert lib.topo_workspace_bytes(ctypes.byref(p), 9) == 0
     assert lib.topo_workspace_bytes(ctypes.byref(_p(d=96)), 0) == 0
     assert lib.topo_bw_probe(None, 16, None, None) == -1
+
+
+def test_certified_decode_rejects_bad_arguments_on_host():
+    lib = topo.load_library()
+    a = ctypes.c_void_p(1 << 40)  # never dereferenced: validation fails first
+    mis = ctypes.c_void_p((1 << 40) + 8)
+    p = _p()
+    need = lib.topo_workspace_bytes(ctypes.byref(p), 4)
+    assert need >= lib.topo_workspace_bytes(ctypes.byref(p), 0) > 0
+    # rho missing or misaligned, workspace too small
+    assert lib.topo_attn_decode_certified(ctypes.byref(p), a, a, a, a, None, None, None, a, need, None) == -1
+    assert lib.topo_attn_decode_certified(ctypes.byref(p), a, a, a, a, None, None, mis, a, need, None) == -1
+    assert lib.topo_attn_decode_certified(ctypes.byref(p), a, a, a, a, None, None, a, a, need - 1, None) == -3
+    # the dense fallback needs the dense scratch too, and is only accepted by the certified call
+    pf = _p(flags=2)
+    need_f = lib.topo_workspace_bytes(ctypes.byref(pf), 4)
+    assert need_f > need
+    assert lib.topo_attn_decode_certified(ctypes.byref(pf), a, a, a, a, None, None, a, a, need, None) == -3
+    assert lib.topo_attn_decode(ctypes.byref(pf), a, a, a, a, None, None, a, 1 << 40, None) == -1
+    assert lib.topo_attn_prefill(ctypes.byref(pf), a, a, a, a, None, None, a, 1 << 40, None) == -1
+    assert lib.topo_attn_dense(ctypes.byref(pf), a, a, a, a, a, 1 << 40, None) == -1
+    assert lib.topo_workspace_bytes(ctypes.byref(_p(n_q=2)), 4) == 0

@@ -526,3 +526,59 @@ def test_certificate_bound_is_sound():
     q, K, V, _ = gen_group(s_, 0, 0, 0)
     rho, cert, ulps = exactness_check(q[0, 0], K, V, s_.n_ctx - 1, s_.W, s_.k, float(s_.softmax_scale))
     assert cert.any() and np.all(ulps[cert] <= 1)
+
+
+# ----------------------------------------------------------------------------- certificate bound
+
+def test_certificate_bound_hand_example():
+    """n = 6, p = 5, W = 2, k = 1, scale 1, scores by position [0, 1, 3, 2, 0, 0]: the set is
+    {0, 2, 4, 5} (anchor, the best candidate 2, window 4-5) and candidates 1 and 3 are left out.
+    s_k = 3, zmax = 3, Z_C = 1 + 3 e^-3 = 1.14936120510359..., so the bound is 2 e^0 / Z_C =
+    1.74009701312..."""
+    s = np.array([0.0, 1.0, 3.0, 2.0, 0.0, 0.0])
+    assert oracle.certificate_bound(s, 5, 2, 1, 1.0) == pytest.approx(1.7400970131228157, rel=1e-15)
+    # and it bounds the true omitted mass (e^-2 + e^-1) / (Z_C + e^-2 + e^-1)
+    C, _ = oracle.condensate_set(s, 5, 2, 1)
+    assert oracle.omitted_mass(s, C, 5, 1.0) < oracle.certificate_bound(s, 5, 2, 1, 1.0)
+
+
+def test_certificate_bound_closed_form_when_omitted_tie_the_kth():
+    """If every omitted candidate scores exactly s_k, the bound is n_omit e^(z_k - m) / Z_C and the
+    true omitted mass is n_omit e^(z_k - m) / (Z_C + n_omit e^(z_k - m)), so rho = b / (1 + b)."""
+    rng = np.random.default_rng(31)
+    n, p, W, k, scale = 400, 399, 16, 8, 0.7
+    s = rng.standard_normal(n)
+    cand = np.arange(1, p - W + 1)
+    top = rng.choice(cand, size=k, replace=False)
+    s[cand] = -1.0                       # every candidate ties at -1 ...
+    s[top] = 2.0 + rng.random(k)         # ... except k clearly higher ones
+    s[top[np.argmin(s[top])]] = -1.0     # the k-th is tied with the omitted ones
+    C, T = oracle.condensate_set(s, p, W, k)
+    assert s[T].min() == -1.0
+    b = oracle.certificate_bound(s, p, W, k, scale)
+    rho = oracle.omitted_mass(s, C, p, scale)
+    assert rho == pytest.approx(b / (1.0 + b), rel=1e-12)
+
+
+def test_certificate_bound_dominates_omitted_mass():
+    """Soundness on random scores, several shapes, causal and not: the bound is never below the
+    true omitted mass; it is 0 with nothing left out and +inf when k = 0 leaves candidates out."""
+    rng = np.random.default_rng(32)
+    for trial in range(60):
+        n = int(rng.integers(2, 300))
+        p = int(rng.integers(0, n))
+        W, k = int(rng.integers(0, 40)), int(rng.integers(0, 40))
+        causal = bool(rng.integers(0, 2))
+        scale = float(rng.uniform(0.05, 3.0))
+        s = rng.standard_normal(n) * float(rng.uniform(0.1, 4.0))
+        C, T = oracle.condensate_set(s, p, W, k, causal)
+        b = oracle.certificate_bound(s, p, W, k, scale, causal)
+        rho = oracle.omitted_mass(s, C, p, scale, causal)
+        vis = p + 1 if causal else n
+        n_cand = vis - C.size + T.size  # visible positions outside anchor and window
+        if n_cand <= k:
+            assert b == 0.0 and rho == 0.0
+        elif k == 0:
+            assert b == float("inf")
+        else:
+            assert b >= rho * (1 - 1e-12)
