@@ -113,13 +113,33 @@ def run_decode_bench(cfg: int, steps: int, warmup: int):
     ms_per_step = (t_end - t_start) * 1e3 / steps
     scan_ms = sum(a.elapsed_time(b) for a, b in evs) / steps
 
+    # The exactness certificate on the same inputs (untimed for the main line): how many query
+    # heads it certifies, the largest bound, and the cost of the certified call per step.
+    rho = torch.empty((s.B, s.Hq), dtype=torch.float32, device="cuda")
+    wsc = torch.empty(topo.topo_workspace_bytes(q, k, s.W, s.k, scale, op=topo.TOPO_OP_DECODE_CERTIFIED),
+                      dtype=torch.uint8, device="cuda")
+    topo.topo_attn_decode_certified(q, k, v, s.W, s.k, scale, out=out, sel_idx=sel, sel_count=cnt, rho=rho,
+                                    workspace=wsc)
+    torch.cuda.synchronize()
+    tc0 = time.perf_counter()
+    for _ in range(10):
+        topo.topo_attn_decode_certified(q, k, v, s.W, s.k, scale, out=out, sel_idx=sel, sel_count=cnt, rho=rho,
+                                        workspace=wsc)
+    torch.cuda.synchronize()
+    rho_np = rho.cpu().numpy()
+    certificate = {"certified_heads": int((rho_np < topo.TOPO_CERT_RHO).sum()), "heads": int(rho_np.size),
+                   "max_rho": float(rho_np.max()), "threshold": topo.TOPO_CERT_RHO,
+                   "ms_per_step": (time.perf_counter() - tc0) * 1e3 / 10}
+    del wsc
+
     n_cand = s.n_ctx - 1 - s.W                     # keys the scan must rank per (batch, kv head)
     row_bytes = s.d * (2 if s.dtype == "bf16" else 4)
     alg_bytes = s.B * s.Hkv * n_cand * row_bytes   # each candidate key row read once per step
     queries = s.B * s.Hq
     res = {
         "spec": s, "workload": w, "ms_per_step": ms_per_step, "scan_ms": scan_ms, "alg_bytes": alg_bytes,
-        "queries": queries, "out": out.cpu().numpy()[:, :, 0], "sel": sel.cpu().numpy()[:, :, 0],
+        "queries": queries, "certificate": certificate,
+        "out": out.cpu().numpy()[:, :, 0], "sel": sel.cpu().numpy()[:, :, 0],
         "cnt": cnt.cpu().numpy()[:, :, 0],
     }
     del q, k, v, ws
@@ -260,6 +280,7 @@ def main():
             "ms_per_step": r["ms_per_step"], "kscan_us": r["scan_ms"] * 1e3,
             "kscan_gbs": r["alg_bytes"] / (r["scan_ms"] / 1e3) / 1e9,
             "kscan_frac": r["alg_bytes"] / (r["scan_ms"] / 1e3) / 1e9 / HBM_PEAK_GBS,
+            "certificate": r["certificate"],
         })
 
     if args.prefill:
@@ -300,7 +321,8 @@ def main():
         "config": {"workload": s.name, "batch": s.B, "q_heads": s.Hq, "kv_heads": s.Hkv, "head_dim": s.d,
                    "context": s.n_ctx, "window": s.W, "topk": s.k, "set_size": 1 + s.W + s.k,
                    "precision": "bf16 inputs, float64 set re-score and softmax, float32 output"},
-        "roofline": roofline, "cpu_baseline": cpu, "parity_sample": parity, "also": also,
+        "roofline": roofline, "cpu_baseline": cpu, "parity_sample": parity,
+        "certificate": main_res["certificate"], "also": also,
     }
     print(json.dumps(line), flush=True)
 
