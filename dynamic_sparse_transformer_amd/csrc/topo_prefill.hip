@@ -304,13 +304,14 @@ __global__ __launch_bounds__(512) void pf_scan_kernel(PfArgs a) {
     PF_GEOM(t)                                                                                     \
     if (interior) {                                                                                \
       _Pragma("unroll") for (int r = 0; r < 16; ++r) {                                             \
-        m2[r] = fmaxf(m2[r], fminf(m1[r], acc[r]));                                                \
+        /* with m1 >= m2, the new second best is the median of m1, m2 and the score */           \
+        m2[r] = __builtin_amdgcn_fmed3f(m1[r], m2[r], acc[r]);                                     \
         m1[r] = fmaxf(m1[r], acc[r]);                                                              \
       }                                                                                            \
     } else {                                                                                       \
       _Pragma("unroll") for (int r = 0; r < 16; ++r) {                                             \
         const float x = PF_CAND(r, dl, jok) ? acc[r] : -INFINITY;                                  \
-        m2[r] = fmaxf(m2[r], fminf(m1[r], x));                                                     \
+        m2[r] = __builtin_amdgcn_fmed3f(m1[r], m2[r], x);                                          \
         m1[r] = fmaxf(m1[r], x);                                                                   \
       }                                                                                            \
     }                                                                                              \
