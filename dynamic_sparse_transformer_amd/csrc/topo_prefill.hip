@@ -9,13 +9,14 @@
 //
 // Launches:
 //   pf_norms   |q| of every query row and the largest |k| of every kv head (error bounds).
-//   pf_scan    bf16 MFMA tiles: 64 query rows x 64 keys per step (4 waves, 32x32x16 MFMA each),
-//              float32 scores; per row, an LDS list of the keys that may still be in its top-k,
-//              pruned against the row's own k-th best lower bound whenever it fills up.
-//   pf_finish  one wave per query row: float64 re-score of the row's list, exact top-k by
-//              (score desc, position asc), the set, float64 softmax and V reduction. Rows whose list
-//              overflowed (ties), float32 inputs and k above the scan's limit take an exact
-//              float64 radix selection over all of the row's candidates instead.
+//   pf_scan    bf16 MFMA tiles, 128 query rows x 64 keys per step (8 waves, one 32x32x16 tile
+//              each), float32 scores, two passes over the keys: the first bounds each row's k-th
+//              best score from below, the second lists every key that may still reach it.
+//   pf_finish  one wave per query row: float32 re-score of the row's list with its error band,
+//              float64 canonical scores where the band leaves the top-k open, the set, softmax
+//              and V reduction. Rows whose list overflowed (ties), float32 inputs and k above the
+//              scan's limit take an exact float64 radix selection over all of the row's
+//              candidates instead.
 #include "topo_device.h"
 #include "topo_internal.h"
 
@@ -32,20 +33,23 @@ constexpr uint32_t PF_OVERFLOW = 0xFFFFFFFFu;
 constexpr float PF_EPS_COEF = 0x1p-14f;
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
-// Per-row list of possible top-k keys: k entries plus room for one more step after a prune.
-static int64_t pf_list(int32_t k) { return (int64_t)k + 96; }
+// LDS of the scan for the per-row lists of possible top-k keys (and the top-2 values before
+// them): 128 floats per row, so a list holds at most 128 key positions; k + 48 slots are used.
+constexpr int PF_LIST_BYTES = PF_ROWS * 128 * 4;
+constexpr int PF_LCAP_MAX = PF_LIST_BYTES / (PF_ROWS * 4);
+static int64_t pf_slot(int32_t k) { return k + 48 < PF_LCAP_MAX ? k + 48 : PF_LCAP_MAX; }
 
 struct PfWs {
   float* qn;        // [B*Hq*n_q]
   uint32_t* knmax;  // [B*Hkv] float bits
   uint32_t* cnt;    // [B*Hq*n_q]: entries of the row's list (or PF_OVERFLOW)
-  uint2* surv;      // [B*Hq*n_q][list]: (float bits of the fast score, key position)
+  uint32_t* surv;   // [B*Hq*n_q][list]: key positions of the row's list
 };
 
 size_t prefill_workspace_bytes(int32_t B, int32_t Hq, int64_t n_q, int64_t, int32_t, int32_t, int32_t k) {
   const size_t rows = (size_t)B * Hq * (size_t)n_q;
   return align256(rows * 4) + align256((size_t)B * Hq * 4) + align256(rows * 4) +
-         rows * (size_t)pf_list(k) * sizeof(uint2);
+         rows * (size_t)pf_slot(k) * sizeof(uint32_t);
 }
 
 static PfWs pf_carve(void* ws, int32_t B, int32_t Hq, int64_t n_q) {
@@ -58,7 +62,7 @@ static PfWs pf_carve(void* ws, int32_t B, int32_t Hq, int64_t n_q) {
   p += align256((size_t)B * Hq * 4);
   w.cnt = (uint32_t*)p;
   p += align256(rows * 4);
-  w.surv = (uint2*)p;
+  w.surv = (uint32_t*)p;
   return w;
 }
 
@@ -127,6 +131,7 @@ struct PfArgs {
   int64_t n, n_q, q_pos0, slot, rows;
   int32_t Hq, Hkv, G, W, topk, causal, set_cap, exact_all;
   float eps32;  // float32 dot-product error bound coefficient: |s32 - s| <= eps32 |q| |k|
+  float pinf;   // +inf (a run-time operand of the scan's medians)
   double scale;
   size_t wave_smem;  // bytes of LDS per wave in pf_finish
 };
@@ -140,34 +145,6 @@ __device__ __forceinline__ bool pf_is_cand(int64_t j, int64_t p, int64_t n, int3
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
-// Final cut of one row's list (one wave): keep the entries whose upper bound reaches the k-th
-// best lower bound of the list; they go to dst in list order. The list is src[0, c0) followed by
-// src[cap - c1, cap). Returns the number kept.
-template <int PER>
-__device__ int prune_row(const uint2* src, int c0, int c1, int cap, uint2* dst, float eps, int k) {
-  const int lane = threadIdx.x & 63;
-  const int c = c0 + c1;
-  uint2 e[PER];
-  uint32_t lb[PER];
-#pragma unroll
-  for (int t = 0; t < PER; ++t) {
-    const int idx = lane + 64 * t;
-    e[t] = idx < c ? src[idx < c0 ? idx : cap - c1 + (idx - c0)] : make_uint2(0u, 0u);
-    lb[t] = idx < c ? ord_f32(__uint_as_float(e[t].x) - eps) : 0u;
-  }
-  const uint32_t T = c > k ? wave_kth_largest<PER>(lb, k) : 0u;
-  int nc = 0;
-#pragma unroll
-  for (int t = 0; t < PER; ++t) {
-    const int idx = lane + 64 * t;
-    const bool keep = idx < c && ord_f32(__uint_as_float(e[t].x) + eps) >= T;
-    const uint64_t mk = __ballot(keep);
-    if (keep) dst[nc + lanes_below(mk)] = e[t];
-    nc += __popcll(mk);
-  }
-  return nc;
-}
-
 // pf_scan: one block of 512 threads per (b, h, 128 consecutive query rows). Each step scores 64
 // keys held in LDS (padded rows, two buffers) while the loads of the key tile two steps ahead are
 // in flight and the tile one step ahead is written to the other buffer. Wave w computes the
@@ -176,13 +153,9 @@ __device__ int prune_row(const uint2* src, int c0, int c1, int cap, uint2* dst, 
 // (row 8*(r/4) + 4*(l/32) + r%4, key l % 32) in register r.
 // Phase 1 keeps, per lane and row, the two largest fast scores it has seen. Those 128 values per
 // row belong to distinct candidate keys, so their k-th largest x_k gives the bound T = x_k - eps
-// below the row's k-th largest exact score. Phase 2 scores the keys again and appends those whose
-// upper bound reaches T (fast score >= x_k - 2 eps) to the row's list in LDS; the lists are cut to
-// the top-k band and copied out at the end.
-constexpr int PF_TOPS_BYTES = PF_ROWS * 128 * 4;
-constexpr int PF_LIST_BYTES = 126976;  // LDS for the row lists (and the top-2 values before them)
-constexpr int PF_LCAP_MAX = PF_LIST_BYTES / (PF_ROWS * 8);
-static_assert(PF_LIST_BYTES >= PF_TOPS_BYTES, "LDS layout");
+// below the row's k-th largest exact score. Phase 2 scores the keys again and appends the
+// position of every key whose upper bound reaches T (fast score >= x_k - 2 eps) to the row's list
+// in LDS; the lists are copied out at the end, and the finish ranks them.
 
 template <int D>
 __global__ __launch_bounds__(512) void pf_scan_kernel(PfArgs a) {
@@ -196,7 +169,7 @@ __global__ __launch_bounds__(512) void pf_scan_kernel(PfArgs a) {
   static_assert(PASSES >= 1 && PASSES <= 2, "staging passes");
   __shared__ __align__(16) unsigned char ktiles[2 * TILE_BYTES];
   __shared__ __align__(16) unsigned char lists[PF_LIST_BYTES];
-  __shared__ int lcnt[2][PF_ROWS];  // entries appended by the waves of key half 0 / 1
+  __shared__ uint32_t lcnt[PF_ROWS];  // keys appended to each row's list
   __shared__ float lthf[PF_ROWS];
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -213,8 +186,9 @@ __global__ __launch_bounds__(512) void pf_scan_kernel(PfArgs a) {
   const int64_t i0 = (nrb - 1 - (job - (int64_t)bh * nrb)) * PF_ROWS;
   const unsigned char* kb = a.k + ((size_t)b * a.Hkv + g) * (size_t)a.n * RB;
   const float knmax = __uint_as_float(a.w.knmax[(size_t)b * a.Hkv + g]);
-  const int LCAP = (int)a.slot;
-  uint2* llist = (uint2*)lists;
+  const uint32_t LCAP = (uint32_t)a.slot;
+  uint32_t* lkeys = (uint32_t*)lists;
+  const int n = (int)a.n;  // the host runs this scan only when n * RB < 2^31
 
   const int rq = wave >> 1, kq = wave & 1;
   const int m = lane & 31, half = lane >> 5;
@@ -233,19 +207,30 @@ __global__ __launch_bounds__(512) void pf_scan_kernel(PfArgs a) {
   const int64_t i_last = min(i0 + PF_ROWS, a.n_q) - 1;
   const int64_t p_first = a.q_pos0 + i0, p_last = a.q_pos0 + i_last;
   const int64_t key_hi = a.causal ? p_last - a.W : a.n - 1;
-  const int64_t ntiles = key_hi >= 0 ? key_hi / PF_KEYS + 1 : 0;
+  const int ntiles = key_hi >= 0 ? (int)(key_hi / PF_KEYS) + 1 : 0;
+  // Interior tiles (every key a candidate of every row of the block): 1 <= t <= t_a (all keys
+  // before every row's window) or, without the causal mask, t_b <= t <= t_c (all keys after
+  // every row's position, inside the cache). Other tiles mask each register by its own test.
   const bool full_rows = i0 + PF_ROWS <= a.n_q;
+  const int64_t ea = p_first - a.W - (PF_KEYS - 1);
+  const int t_a = full_rows && ea >= 0 ? (int)(ea / PF_KEYS) : -1;
+  const int t_b = (int)(p_last / PF_KEYS) + 1, t_c = full_rows && !a.causal ? n / PF_KEYS - 1 : -1;
+#define PF_INTERIOR(t) ((t) >= 1 && ((t) <= t_a || ((t) >= t_b && (t) <= t_c)))
 
-  // Each thread stages chunk (tid % NCH) of key rows kt0 + ps*RPP + tid/NCH. Tile u is loaded
-  // into register set (u & 1) two steps before it is used.
+  // Staging of key tiles: thread tid copies 16-byte chunk (tid % NCH) of key rows
+  // u * PF_KEYS + tid / NCH (+ RPP). Raw buffer loads whose range ends at the cache's last key:
+  // rows past the end read as zero, so every load is issued unconditionally and no address is
+  // clamped. Register set (u & 1) holds tile u from its load until its store two steps later.
   const int srow = tid / NCH, schunk = tid % NCH;
+  const int voff0 = srow * RB + schunk * 16, voff1 = voff0 + RPP * RB;
   uint4 r00 = make_uint4(0u, 0u, 0u, 0u), r01 = r00, r10 = r00, r11 = r00;
 #define PF_LOAD(DST0, DST1, U)                                                                     \
   {                                                                                                \
-    const int64_t key0 = (U) * PF_KEYS + srow;                                                     \
-    const unsigned char* src = kb + (size_t)schunk * 16;                                           \
-    DST0 = *(const uint4*)(src + (size_t)(key0 < a.n ? key0 : a.n - 1) * RB);                      \
-    if (PASSES > 1) DST1 = *(const uint4*)(src + (size_t)(key0 + RPP < a.n ? key0 + RPP : a.n - 1) * RB); \
+    const int kt_ = min((U) * PF_KEYS, n);                                                         \
+    const __amdgpu_buffer_rsrc_t rs_ =                                                             \
+        __builtin_amdgcn_make_buffer_rsrc((void*)(kb + (size_t)kt_ * RB), (short)0, (n - kt_) * RB, 0x00020000); \
+    DST0 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs_, voff0, 0, 0));    \
+    if (PASSES > 1) DST1 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs_, voff1, 0, 0)); \
   }
 #define PF_STORE(SRC0, SRC1, U)                                                                    \
   {                                                                                                \
@@ -253,78 +238,81 @@ __global__ __launch_bounds__(512) void pf_scan_kernel(PfArgs a) {
     *(uint4*)dst = SRC0;                                                                           \
     if (PASSES > 1) *(uint4*)(dst + RPP * STRIDE) = SRC1;                                          \
   }
-// Prologue of a scan: tile 0 to LDS, tile 1 in flight. The loads are unconditional (tiles past
-// the end read clamped, in-bounds rows and are never used), so every path has the same loads in
-// flight and waits only for the older register set.
-#define PF_PROLOGUE()                                                                              \
+// Prologue of a pass over the tiles: tiles 0 and 1 to LDS, tiles 2 and 3 in flight, scores of
+// tile 0 into ACC.
+#define PF_PROLOGUE(ACC)                                                                           \
   PF_LOAD(r00, r01, 0)                                                                             \
-  PF_STORE(r00, r01, 0)                                                                            \
   PF_LOAD(r10, r11, 1)                                                                             \
-  __syncthreads();
-// Scores of step t into acc, then tile t+2 requested into register set (t & 1), whose tile t went
-// to LDS a step ago.
-#define PF_TILE(t, SET0, SET1)                                                                     \
-  acc = f32x16_t{};                                                                                \
+  PF_STORE(r00, r01, 0)                                                                            \
+  PF_STORE(r10, r11, 1)                                                                            \
+  PF_LOAD(r00, r01, 2)                                                                             \
+  PF_LOAD(r10, r11, 3)                                                                             \
+  __syncthreads();                                                                                 \
+  PF_MMA(ACC, 0)
+// Scores of the tile in LDS buffer BUF into ACC: v_mfma_f32_32x32x16_bf16 over the D / 16 slices.
+#define PF_MMA(ACC, BUF)                                                                           \
   {                                                                                                \
-    const unsigned char* krow = &ktiles[((t) & 1) * TILE_BYTES + (kq * 32 + m) * STRIDE + half * 16]; \
-    _Pragma("unroll") for (int st = 0; st < STEPS; ++st) {                                         \
-      const uint4 w = *(const uint4*)(krow + st * 32);                                             \
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[st], __builtin_bit_cast(bf16x8_t, w), acc, 0, 0, 0); \
-    }                                                                                              \
-  }                                                                                                \
-  PF_LOAD(SET0, SET1, (t) + 2)
-// End of step t: tile t+1 (register set ((t+1) & 1)) to the other LDS buffer.
-#define PF_NEXT(t, NSET0, NSET1)                                                                   \
-  if ((t) + 1 < ntiles) PF_STORE(NSET0, NSET1, (t) + 1)                                            \
-  __syncthreads();
-
-  // Candidate test of register r on a boundary step, in 32-bit arithmetic: with
-  // dr = (position of the register's row) - j, key j is a candidate of the row iff 1 <= j < n, the
-  // row exists, and dr >= W (j before the window) or, without the causal mask, dr < 0 (j after p).
+    const unsigned char* krow = &ktiles[(BUF) * TILE_BYTES + (kq * 32 + m) * STRIDE + half * 16]; \
+    uint4 kf[STEPS];                                                                               \
+    _Pragma("unroll") for (int st = 0; st < STEPS; ++st) kf[st] = *(const uint4*)(krow + st * 32); \
+    ACC = f32x16_t{};                                                                              \
+    _Pragma("unroll") for (int st = 0; st < STEPS; ++st)                                           \
+      ACC = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[st], __builtin_bit_cast(bf16x8_t, kf[st]), ACC, 0, 0, 0); \
+  }
+// On a boundary tile, scores of keys that are not candidates of the register's row become -inf.
+// With dr = (position of the register's row) - j, key j is a candidate of the row iff
+// 1 <= j < n, the row exists, and dr >= W (j before the window) or, without the causal mask,
+// dr < 0 (j after p).
   const int rows_valid = (int)min((int64_t)PF_ROWS, a.n_q - i0);
-#define PF_CAND(r, dl, jok)                                                                        \
-  ((jok) && row_base + 8 * ((r) / 4) + ((r) % 4) < rows_valid &&                                   \
-   ((dl) + 8 * ((r) / 4) + ((r) % 4) >= a.W || (!a.causal && (dl) + 8 * ((r) / 4) + ((r) % 4) < 0)))
-#define PF_GEOM(t)                                                                                 \
-  const int64_t kt0 = (t) * PF_KEYS;                                                               \
-  const int64_t j = kt0 + kq * 32 + m;                                                             \
-  const bool interior = full_rows && kt0 >= 1 &&                                                   \
-      (kt0 + PF_KEYS - 1 <= p_first - a.W || (!a.causal && kt0 > p_last && kt0 + PF_KEYS <= a.n)); \
-  const int64_t dl64 = p_first + row_base - j;                                                     \
-  const int dl = (int)(dl64 > (1 << 30) ? (1 << 30) : (dl64 < -(1 << 30) ? -(1 << 30) : dl64));     \
-  const bool jok = j >= 1 && j < a.n;
+#define PF_MASK(ACC, t)                                                                            \
+  if (!PF_INTERIOR(t)) {                                                                           \
+    const int64_t j_ = (int64_t)(t) * PF_KEYS + kq * 32 + m;                                       \
+    const int64_t dl64 = p_first + row_base - j_;                                                  \
+    const int dl = (int)(dl64 > (1 << 30) ? (1 << 30) : (dl64 < -(1 << 30) ? -(1 << 30) : dl64));  \
+    const bool jok = j_ >= 1 && j_ < a.n;                                                          \
+    _Pragma("unroll") for (int r = 0; r < 16; ++r) {                                               \
+      const int o = 8 * (r / 4) + (r % 4);                                                         \
+      const bool cand = jok && row_base + o < rows_valid && (dl + o >= a.W || (!a.causal && dl + o < 0)); \
+      ACC[r] = cand ? ACC[r] : -INFINITY;                                                          \
+    }                                                                                              \
+  }
+// One step t of a pass: the scores of tile t are in ACC_CUR (issued a step earlier); the matrix
+// cores score tile t+1 into ACC_NEXT while the vector units run EPI on tile t; then tile t+2 goes
+// from its registers to the LDS buffer that tile t used and tile t+4 is requested. The scheduling
+// barriers interleave the eight matrix instructions with the vector work.
+#define PF_STEP(EPI, t, ACC_CUR, ACC_NEXT, SET0, SET1)                                             \
+  PF_MASK(ACC_CUR, t)                                                                              \
+  PF_MMA(ACC_NEXT, ((t) + 1) & 1)                                                                  \
+  EPI(ACC_CUR, t)                                                                                  \
+  PF_STORE(SET0, SET1, (t) + 2)                                                                    \
+  PF_LOAD(SET0, SET1, (t) + 4)                                                                     \
+  __syncthreads();
+#define PF_INTERLEAVE()                                                                            \
+  __builtin_amdgcn_sched_group_barrier(0x100, STEPS, 0);                                           \
+  _Pragma("unroll") for (int st = 0; st < STEPS; ++st) {                                           \
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                             \
+    __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);                                             \
+  }
 
-  f32x16_t acc;
-  // ---- phase 1: per lane and row, the two largest fast scores of candidate keys
+  f32x16_t accA, accB;
+  // ---- phase 1: per lane and row, the two largest fast scores of candidate keys. With m1 >= m2,
+  // the new second best is the median of m1, m2 and the score, and the new best is the median of
+  // m1, the score and +inf (a run-time operand, so that no NaN-quieting is added around a max).
+  const float pinf = a.pinf;
   float m1[16], m2[16];
 #pragma unroll
   for (int r = 0; r < 16; ++r) m1[r] = m2[r] = -INFINITY;
-#define PF_P1_BODY(t)                                                                              \
-  {                                                                                                \
-    PF_GEOM(t)                                                                                     \
-    if (interior) {                                                                                \
-      _Pragma("unroll") for (int r = 0; r < 16; ++r) {                                             \
-        /* with m1 >= m2, the new second best is the median of m1, m2 and the score */           \
-        m2[r] = __builtin_amdgcn_fmed3f(m1[r], m2[r], acc[r]);                                     \
-        m1[r] = fmaxf(m1[r], acc[r]);                                                              \
-      }                                                                                            \
-    } else {                                                                                       \
-      _Pragma("unroll") for (int r = 0; r < 16; ++r) {                                             \
-        const float x = PF_CAND(r, dl, jok) ? acc[r] : -INFINITY;                                  \
-        m2[r] = __builtin_amdgcn_fmed3f(m1[r], m2[r], x);                                          \
-        m1[r] = fmaxf(m1[r], x);                                                                   \
-      }                                                                                            \
-    }                                                                                              \
-  }
-  PF_PROLOGUE()
-  for (int64_t t = 0; t < ntiles; t += 2) {
-    PF_TILE(t, r00, r01)
-    PF_P1_BODY(t)
-    PF_NEXT(t, r10, r11)
-    if (t + 1 < ntiles) {
-      PF_TILE(t + 1, r10, r11)
-      PF_P1_BODY(t + 1)
-      PF_NEXT(t + 1, r00, r01)
+#define PF_EPI1(ACC, t)                                                                            \
+  _Pragma("unroll") for (int r = 0; r < 16; ++r) {                                                 \
+    m2[r] = __builtin_amdgcn_fmed3f(m1[r], m2[r], ACC[r]);                                         \
+    m1[r] = __builtin_amdgcn_fmed3f(m1[r], ACC[r], pinf);                                          \
+  }                                                                                                \
+  PF_INTERLEAVE()
+  if (ntiles > 0) {
+    PF_PROLOGUE(accA)
+    for (int t = 0; t < ntiles; t += 2) {
+      PF_STEP(PF_EPI1, t, accA, accB, r00, r01)
+      PF_STEP(PF_EPI1, t + 1, accB, accA, r10, r11)
     }
   }
 
@@ -343,103 +331,72 @@ __global__ __launch_bounds__(512) void pf_scan_kernel(PfArgs a) {
     if (lane == 0) {
       const int64_t i = i0 + row;
       const float eps = i < a.n_q ? PF_EPS_COEF * a.w.qn[(size_t)bh * a.n_q + i] * knmax + 1e-30f : 0.f;
-      // fewer than k finite values (or none): every candidate stays
+      // fewer than k finite values (or none): every candidate stays. The bound is kept finite
+      // (at least the lowest float), so that the -inf of a masked score never passes it.
       const float x = xk == 0u ? -INFINITY : unord_f32(xk);
-      lthf[row] = x - 2.0f * eps;
+      lthf[row] = fmaxf(x - 2.0f * eps, -0x1.fffffep+127f);
     }
   }
+  if (tid < PF_ROWS) lcnt[tid] = 0u;
   __syncthreads();
   float thf[16];
 #pragma unroll
   for (int r = 0; r < 16; ++r) thf[r] = lthf[row_base + 8 * (r / 4) + (r % 4)];
 
-  // ---- phase 2: append every candidate key whose upper bound reaches the row's bound. A row's
-  // list has LCAP slots; the wave of key half 0 fills them from the front, the wave of half 1 from
-  // the back, each counting its own entries in registers (uniform per half-wave). Writes stay in
-  // the row's slots; if the two ends cross, the row is marked for the exact path.
-  int ncnt[16];
-  // Slot sl of register r's row at this wave's end of the list is list index (sl ^ lsgn) +
-  // lbase[r]: sl from the front (lsgn = 0), LCAP - 1 - sl from the back (lsgn = -1).
-  int lbase[16];
-  const int lsgn = kq ? -1 : 0;
-#pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    ncnt[r] = 0;
-    lbase[r] = (row_base + 8 * (r / 4) + (r % 4)) * LCAP + (kq ? LCAP : 0);
-  }
-// Append the lanes of register r whose test `ok` holds: lanes 0-31 hold block row `row` of half
-// 0, lanes 32-63 the row 4 below it; each half counts its own entries (ncnt, uniform per half).
-// A lane's place is the number of passing lanes below it in its half (mbcnt over the ballot,
-// with the other half's bits left out). Slots past the end are clamped onto the last one: that
-// only happens when the two ends of the list cross, which the final count check detects, and
-// the row then takes the exact path. The scores are first copied out of the MFMA result vector,
-// so that no branch keeps the whole vector live.
-#define PF_APPEND(r, OK)                                                                           \
+  // ---- phase 2: every candidate key whose upper bound reaches the row's bound goes to the row's
+  // list. A lane first gathers the test results of its 16 registers into bit r of `bits`: the
+  // test x >= T is the sign of x - T (T finite, x finite or -inf), shifted in by v_alignbit. Then
+  // it takes its set bits one at a time: a slot from the row's LDS counter, the key position into
+  // the slot. The lanes of a wave pass through that loop together as often as the busiest lane
+  // needs (a step has about one passing register per four lanes). Slots past the end are clamped
+  // onto the last one; a row whose count ends above LCAP takes the exact path.
+#define PF_EPI2(ACC, t)                                                                            \
   {                                                                                                \
-    const bool ok = (OK);                                                                          \
-    const uint64_t mk = __ballot(ok);                                                              \
-    const uint32_t lo_ = (uint32_t)mk, hi_ = (uint32_t)(mk >> 32);                                 \
-    if (ok) {                                                                                      \
-      const int pre = (int)__builtin_amdgcn_mbcnt_hi(hi_, __builtin_amdgcn_mbcnt_lo(half ? 0u : lo_, 0u)); \
-      const int sl = min(ncnt[r] + pre, LCAP - 1);                                                 \
-      llist[(sl ^ lsgn) + lbase[r]] = make_uint2(__float_as_uint(x16[r]), (uint32_t)j);             \
-    }                                                                                              \
-    ncnt[r] += half ? __popc(hi_) : __popc(lo_);                                                   \
-  }
-#define PF_P2_BODY(t)                                                                              \
-  {                                                                                                \
-    PF_GEOM(t)                                                                                     \
-    float x16[16];                                                                                 \
-    _Pragma("unroll") for (int r = 0; r < 16; ++r) x16[r] = acc[r];                                \
-    if (interior) {                                                                                \
-      _Pragma("unroll") for (int r = 0; r < 16; ++r) PF_APPEND(r, x16[r] >= thf[r])                \
-    } else {                                                                                       \
-      _Pragma("unroll") for (int r = 0; r < 16; ++r) PF_APPEND(r, x16[r] >= thf[r] && PF_CAND(r, dl, jok)) \
+    uint32_t fail = 0u;                                                                            \
+    _Pragma("unroll") for (int r = 15; r >= 0; --r)                                                \
+      fail = __builtin_amdgcn_alignbit(fail, __float_as_uint(ACC[r] - thf[r]), 31);                \
+    PF_INTERLEAVE()                                                                                \
+    uint32_t bits = ~fail & 0xFFFFu;                                                               \
+    const uint32_t jj = (uint32_t)((t) * PF_KEYS + kq * 32 + m);                                   \
+    while (bits) {                                                                                 \
+      const int r = __builtin_ctz(bits);                                                           \
+      bits &= bits - 1u;                                                                           \
+      const int row = row_base + r + (r & 12); /* row_base + 8 * (r / 4) + r % 4 */               \
+      const uint32_t sl = min(atomicAdd(&lcnt[row], 1u), LCAP - 1u);                               \
+      lkeys[__umul24((uint32_t)row, LCAP) + sl] = jj;                                              \
     }                                                                                              \
   }
-  PF_PROLOGUE()
-  for (int64_t t = 0; t < ntiles; t += 2) {
-    PF_TILE(t, r00, r01)
-    PF_P2_BODY(t)
-    PF_NEXT(t, r10, r11)
-    if (t + 1 < ntiles) {
-      PF_TILE(t + 1, r10, r11)
-      PF_P2_BODY(t + 1)
-      PF_NEXT(t + 1, r00, r01)
+  if (ntiles > 0) {
+    PF_PROLOGUE(accA)
+    for (int t = 0; t < ntiles; t += 2) {
+      PF_STEP(PF_EPI2, t, accA, accB, r00, r01)
+      PF_STEP(PF_EPI2, t + 1, accB, accA, r10, r11)
     }
   }
 
-  // per-row counts of both halves, then the final cut to the top-k band, out to global memory with
-  // the counts: wave w takes rows w, w+8, ...
-  if (m == 0) {
-#pragma unroll
-    for (int r = 0; r < 16; ++r) lcnt[kq][row_base + 8 * (r / 4) + (r % 4)] = ncnt[r];
-  }
-  __syncthreads();
+  // the lists and their counts to global memory: wave w takes rows w, w+8, ...
   for (int row = wave; row < PF_ROWS; row += 8) {
     const int64_t i = i0 + row;
     if (i >= a.n_q) continue;
     const size_t grow = (size_t)bh * a.n_q + i;
-    const int c0 = lcnt[0][row], c1 = lcnt[1][row];
-    if (c0 + c1 > LCAP) {
+    const uint32_t c = lcnt[row];
+    if (c > LCAP) {
       if (lane == 0) a.w.cnt[grow] = PF_OVERFLOW;
       continue;
     }
-    const float eps = PF_EPS_COEF * a.w.qn[grow] * knmax + 1e-30f;
-    const int nc = prune_row<(PF_LCAP_MAX + 63) / 64>(llist + row * LCAP, c0, c1, LCAP, a.w.surv + grow * (size_t)LCAP,
-                                                       eps, a.topk);
-    if (lane == 0) a.w.cnt[grow] = (uint32_t)nc;
+    for (uint32_t t = lane; t < c; t += 64) a.w.surv[grow * LCAP + t] = lkeys[row * LCAP + t];
+    if (lane == 0) a.w.cnt[grow] = c;
   }
+#undef PF_INTERIOR
 #undef PF_LOAD
 #undef PF_STORE
 #undef PF_PROLOGUE
-#undef PF_TILE
-#undef PF_NEXT
-#undef PF_CAND
-#undef PF_GEOM
-#undef PF_P1_BODY
-#undef PF_P2_BODY
-#undef PF_APPEND
+#undef PF_MMA
+#undef PF_MASK
+#undef PF_STEP
+#undef PF_INTERLEAVE
+#undef PF_EPI1
+#undef PF_EPI2
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -593,10 +550,10 @@ __device__ void pf_row(const PfArgs& a, PfRowSmem* sm, size_t grow) {
     exact = cr == PF_OVERFLOW;
     if (!exact) {
       c = (int)cr;
-      const uint2* sv = a.w.surv + grow * (size_t)a.slot;
+      const uint32_t* sv = a.w.surv + grow * (size_t)a.slot;
       // positions come from the scan and are always keys of the cache; clamping only guards
       // the reads below
-      for (int t = lane; t < c; t += 64) sm->ridx[t] = (int32_t)min((uint32_t)sv[t].y, (uint32_t)(a.n - 1));
+      for (int t = lane; t < c; t += 64) sm->ridx[t] = (int32_t)min(sv[t], (uint32_t)(a.n - 1));
     }
   }
   __builtin_amdgcn_wave_barrier();
@@ -909,7 +866,7 @@ hipError_t launch_prefill(const PrefillLaunch& L, hipStream_t stream) {
   pa.n = L.n;
   pa.n_q = L.n_q;
   pa.q_pos0 = L.q_pos0;
-  pa.slot = (int64_t)L.topk + 48 < PF_LCAP_MAX ? (int64_t)L.topk + 48 : PF_LCAP_MAX;
+  pa.slot = pf_slot(L.topk);
   pa.Hq = L.Hq;
   pa.Hkv = L.Hkv;
   pa.G = L.G;
@@ -917,10 +874,12 @@ hipError_t launch_prefill(const PrefillLaunch& L, hipStream_t stream) {
   pa.topk = L.topk;
   pa.causal = L.causal;
   pa.set_cap = 1 + L.W + L.topk;
-  pa.exact_all = (!L.bf16 || L.topk > PF_MAX_K || (L.flags & 1)) ? 1 : 0;
+  // the scan addresses a kv head's keys with 32-bit buffer offsets
+  pa.exact_all = (!L.bf16 || L.topk > PF_MAX_K || (L.flags & 1) || L.n * 2 * L.d >= ((int64_t)1 << 31)) ? 1 : 0;
   static_assert(PF_MAX_K + 16 <= PF_LCAP_MAX, "list room above k");
   pa.scale = L.scale;
   pa.eps32 = L.eps_coef;
+  pa.pinf = INFINITY;
   pa.rows = (int64_t)L.B * L.Hq * L.n_q;
   pa.wave_smem = (PfRowSmem::bytes(pa.slot, L.topk, pa.set_cap) + 255) & ~(size_t)255;
   if (4 * pa.wave_smem > 160 * 1024) return hipErrorNotSupported;
