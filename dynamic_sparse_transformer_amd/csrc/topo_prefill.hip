@@ -44,15 +44,17 @@ struct PfWs {
   uint32_t* knmax;  // [B*Hkv] float bits
   uint32_t* cnt;    // [B*Hq*n_q]: entries of the row's list (or PF_OVERFLOW)
   uint32_t* surv;   // [B*Hq*n_q][list]: key positions of the row's list
+  float* win_o;     // [B*Hq*n_q][d]: sum over the row's window of exp(z - m_w) v (bf16 inputs)
+  float2* win_mz;   // [B*Hq*n_q]: (m_w, sum over the window of exp(z - m_w))
 };
 
-size_t prefill_workspace_bytes(int32_t B, int32_t Hq, int64_t n_q, int64_t, int32_t, int32_t, int32_t k) {
+size_t prefill_workspace_bytes(int32_t B, int32_t Hq, int64_t n_q, int64_t, int32_t d, int32_t, int32_t k) {
   const size_t rows = (size_t)B * Hq * (size_t)n_q;
   return align256(rows * 4) + align256((size_t)B * Hq * 4) + align256(rows * 4) +
-         rows * (size_t)pf_slot(k) * sizeof(uint32_t);
+         align256(rows * (size_t)pf_slot(k) * sizeof(uint32_t)) + align256(rows * (size_t)d * 4) + rows * 8;
 }
 
-static PfWs pf_carve(void* ws, int32_t B, int32_t Hq, int64_t n_q) {
+static PfWs pf_carve(void* ws, int32_t B, int32_t Hq, int64_t n_q, int32_t d, int32_t k) {
   const size_t rows = (size_t)B * Hq * (size_t)n_q;
   PfWs w;
   char* p = (char*)ws;
@@ -63,6 +65,10 @@ static PfWs pf_carve(void* ws, int32_t B, int32_t Hq, int64_t n_q) {
   w.cnt = (uint32_t*)p;
   p += align256(rows * 4);
   w.surv = (uint32_t*)p;
+  p += align256(rows * (size_t)pf_slot(k) * sizeof(uint32_t));
+  w.win_o = (float*)p;
+  p += align256(rows * (size_t)d * 4);
+  w.win_mz = (float2*)p;
   return w;
 }
 
@@ -130,6 +136,7 @@ struct PfArgs {
   PfWs w;
   int64_t n, n_q, q_pos0, slot, rows;
   int32_t Hq, Hkv, G, W, topk, causal, set_cap, exact_all;
+  int32_t win;  // 1: the window kernel has left (m_w, Z_w, O_w) of every row in the workspace
   float eps32;  // float32 dot-product error bound coefficient: |s32 - s| <= eps32 |q| |k|
   float pinf;   // +inf (a run-time operand of the scan's medians)
   double scale;
@@ -400,24 +407,162 @@ __global__ __launch_bounds__(512) void pf_scan_kernel(PfArgs a) {
 }
 
 // ---------------------------------------------------------------------------------------------
+// pf_window: the window's share of the softmax of every query row (bf16 inputs), on the matrix
+// cores. One block per (b, h, 32 consecutive query rows), one wave per 32 output dimensions.
+// The window keys of the block, [max(0, p_first - W + 1), p_last], go in tiles of 32 keys,
+// staged in LDS (K and V, two buffers; tile u+1 is loaded while tile u is used). Per tile:
+// S' = K_tile . Q^T with v_mfma_f32_32x32x16_bf16 (A = key rows, B = query rows), so lane l
+// holds query row l % 32 and, in register r, key 8*(r/4) + 4*(l/32) + r%4 of the tile; keys
+// outside the row's window [p - W + 1, p] are masked. The row's running maximum m, sum Z and
+// output O are updated online: factor exp(m_old - m_new) on Z and O, weights w = exp(z - m_new),
+// and O += w V with v_mfma_f32_32x32x2_f32: register r's weight is the A operand of query row
+// l % 32 and key (r, l / 32), the B operand is that key's V element at the wave's dimension
+// 32 * wave + l % 32 (the bf16 value widened to float32, exactly). The output tile's rows are
+// 8*(r/4) + 4*(l/32) + r%4, so their factors are read back from LDS. Every product is a float32
+// product of the float32 weight and the exact V value, as in the per-row path.
+template <int D>
+__global__ __launch_bounds__(256) void pf_window_kernel(PfArgs a) {
+  constexpr int RB = D * 2, STEPS = D / 16, NW = D / 32, NT = NW * 64;
+  constexpr int STR = RB + 16;         // padded LDS row (K and V)
+  constexpr int CPR = RB / 16;         // 16-byte chunks per key row
+  static_assert(2 * NT == 32 * CPR, "tile staging: two 16-byte chunks of K and of V per thread");
+  __shared__ __align__(16) unsigned char kt[2][32 * STR];
+  __shared__ __align__(16) unsigned char vt[2][32 * STR];
+  __shared__ __align__(16) float alpha[NW][32];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int m = lane & 31, half = lane >> 5;
+  const int64_t nrb = (a.n_q + 31) / 32;
+  const int bh = (int)(blockIdx.x / nrb);
+  const int64_t i0 = ((int64_t)blockIdx.x - (int64_t)bh * nrb) * 32;
+  const int b = bh / a.Hq, h = bh - b * a.Hq, g = h / a.G;
+  const unsigned char* kb = a.k + ((size_t)b * a.Hkv + g) * (size_t)a.n * RB;
+  const unsigned char* vb = a.v + ((size_t)b * a.Hkv + g) * (size_t)a.n * RB;
+
+  bf16x8_t qf[STEPS];
+  {
+    const int64_t iq = min(i0 + m, a.n_q - 1);
+    const unsigned char* qrow = a.q + ((size_t)bh * a.n_q + iq) * RB;
+#pragma unroll
+    for (int st = 0; st < STEPS; ++st) qf[st] = __builtin_bit_cast(bf16x8_t, *(const uint4*)(qrow + st * 32 + half * 16));
+  }
+  const int64_t key_lo = a.q_pos0 + i0 - a.W + 1 > 0 ? a.q_pos0 + i0 - a.W + 1 : 0;
+  const int64_t p_last = a.q_pos0 + min(i0 + 31, a.n_q - 1);
+  const int ntk = (int)((p_last - key_lo) / 32) + 1;
+  // the lane's row relative to key_lo (rows past n_q get -1: no key passes)
+  const int prel = i0 + m < a.n_q ? (int)(a.q_pos0 + i0 + m - key_lo) : -1;
+  const float sc = (float)a.scale;
+  const int dim = 32 * wave + m;
+
+  // thread tid stages chunks tid and tid + NT of the tile: key row c / CPR, chunk c % CPR
+  const int c0 = tid, c1 = tid + NT;
+  uint4 kr0, kr1, vr0, vr1;
+#define PW_LOAD(u)                                                                                 \
+  {                                                                                                \
+    const int64_t j0 = min(key_lo + 32 * (u) + c0 / CPR, a.n - 1);                                 \
+    const int64_t j1 = min(key_lo + 32 * (u) + c1 / CPR, a.n - 1);                                 \
+    kr0 = *(const uint4*)(kb + (size_t)j0 * RB + (c0 % CPR) * 16);                                 \
+    vr0 = *(const uint4*)(vb + (size_t)j0 * RB + (c0 % CPR) * 16);                                 \
+    kr1 = *(const uint4*)(kb + (size_t)j1 * RB + (c1 % CPR) * 16);                                 \
+    vr1 = *(const uint4*)(vb + (size_t)j1 * RB + (c1 % CPR) * 16);                                 \
+  }
+#define PW_STORE(buf)                                                                              \
+  {                                                                                                \
+    *(uint4*)&kt[buf][(c0 / CPR) * STR + (c0 % CPR) * 16] = kr0;                                   \
+    *(uint4*)&vt[buf][(c0 / CPR) * STR + (c0 % CPR) * 16] = vr0;                                   \
+    *(uint4*)&kt[buf][(c1 / CPR) * STR + (c1 % CPR) * 16] = kr1;                                   \
+    *(uint4*)&vt[buf][(c1 / CPR) * STR + (c1 % CPR) * 16] = vr1;                                   \
+  }
+  PW_LOAD(0)
+  PW_STORE(0)
+  __syncthreads();
+
+  float mrun = -INFINITY, zs = 0.f;
+  f32x16_t o = f32x16_t{};
+  for (int u = 0; u < ntk; ++u) {
+    const int buf = u & 1;
+    if (u + 1 < ntk) PW_LOAD(u + 1)
+    f32x16_t S = f32x16_t{};
+    {
+      const unsigned char* krow = &kt[buf][m * STR + half * 16];
+      uint4 kf[STEPS];
+#pragma unroll
+      for (int st = 0; st < STEPS; ++st) kf[st] = *(const uint4*)(krow + st * 32);
+#pragma unroll
+      for (int st = 0; st < STEPS; ++st)
+        S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, kf[st]), qf[st], S, 0, 0, 0);
+    }
+    // key (r, half) of this tile is offset 32 u + 4 half + o_r from key_lo; it is in the row's
+    // window iff prel - W < offset <= prel
+    const int d = prel - 32 * u - 4 * half;
+    float tm = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int o_r = 8 * (r / 4) + (r % 4);
+      S[r] = (o_r <= d && o_r > d - a.W) ? sc * S[r] : -INFINITY;
+      tm = fmaxf(tm, S[r]);
+    }
+    tm = fmaxf(tm, __shfl_xor(tm, 32));
+    const float mnew = fmaxf(mrun, tm);
+    const float al = mnew == -INFINITY ? 1.f : __expf(mrun - mnew);
+    mrun = mnew;
+    zs *= al;
+    if (half == 0) alpha[wave][m] = al;
+    __builtin_amdgcn_wave_barrier();
+    const float4* a4 = (const float4*)&alpha[wave][4 * half];
+    float fr[16];
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const float4 x = a4[2 * q4];  // rows 8 q4 + 4 half + 0..3
+      fr[4 * q4] = x.x;
+      fr[4 * q4 + 1] = x.y;
+      fr[4 * q4 + 2] = x.z;
+      fr[4 * q4 + 3] = x.w;
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) o[r] *= fr[r];
+    const unsigned char* vcol = &vt[buf][(4 * half) * STR + dim * 2];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float w = S[r] == -INFINITY ? 0.f : __expf(S[r] - mnew);
+      zs += w;
+      const float v = __uint_as_float((uint32_t)*(const uint16_t*)(vcol + (8 * (r / 4) + (r % 4)) * STR) << 16);
+      o = __builtin_amdgcn_mfma_f32_32x32x2f32(w, v, o, 0, 0, 0);
+    }
+    if (u + 1 < ntk) PW_STORE(buf ^ 1)
+    __syncthreads();
+  }
+  zs += __shfl_xor(zs, 32);
+#undef PW_LOAD
+#undef PW_STORE
+
+  // O_w: register r holds query row 8*(r/4) + 4*half + r%4, dimension `dim`
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int64_t i = i0 + 8 * (r / 4) + 4 * half + (r % 4);
+    if (i < a.n_q) a.w.win_o[((size_t)bh * a.n_q + i) * D + dim] = o[r];
+  }
+  if (wave == 0 && half == 0 && i0 + m < a.n_q) a.w.win_mz[(size_t)bh * a.n_q + i0 + m] = make_float2(mrun, zs);
+}
+
+// ---------------------------------------------------------------------------------------------
 // pf_finish: one wave per query row (4 rows per 256-thread block), each wave with its own LDS
 // region laid out by PfRowSmem::carve for the call's k and 1 + W + k.
 constexpr int PF_FIN_SET = 4096;   // largest 1 + W + k served by the per-row finish
 struct PfRowSmem {
   double* qd;      // [128]
   double* rs;      // [slot + set_cap]: float64 scores of the row's list, window and anchor keys
-  double* ts;      // [k]
+  double* ts;      // [k + 1]
   double* cw;      // [set_cap]
   int32_t* ridx;   // [slot]
-  int32_t* tidx;   // [k]
+  int32_t* tidx;   // [k + 1]
   int32_t* cidx;   // [set_cap]
   uint32_t* hist;  // [256]
   static __host__ __device__ size_t bytes(int64_t slot, int k, int set_cap) {
-    const size_t kk = (size_t)(k > 0 ? k : 1);
+    const size_t kk = (size_t)k + 1;
     return 128 * 8 + ((size_t)slot + set_cap) * 8 + kk * 12 + (size_t)set_cap * 12 + (size_t)slot * 4 + 256 * 4 + 64;
   }
   __device__ void carve(unsigned char* p, int64_t slot, int k, int set_cap) {
-    const size_t kk = (size_t)(k > 0 ? k : 1);
+    const size_t kk = (size_t)k + 1;
     qd = (double*)p;
     p += 128 * 8;
     rs = (double*)p;
@@ -558,9 +703,10 @@ __device__ void pf_row(const PfArgs& a, PfRowSmem* sm, size_t grow) {
   }
   __builtin_amdgcn_wave_barrier();
 
-  // ---- scores: items [0, c) the list, c the anchor (if any), then the window
+  // ---- scores: items [0, c) the list, c the anchor (if any), then (float32 inputs) the window;
+  // with bf16 inputs the window's share of the softmax comes from pf_window
   const int wbase = c + anchor;
-  const int nitems = wbase + nwin;
+  const int nitems = BF16 ? wbase : wbase + nwin;
   int nt = 0;
   if constexpr (BF16) {
     // float32 scores of every item: LPR lanes per key, a 16-byte chunk each (v_dot2_f32_bf16),
@@ -704,7 +850,7 @@ __device__ void pf_row(const PfArgs& a, PfRowSmem* sm, size_t grow) {
   for (int t = lane; t < nwin; t += 64) {
     const int pos = anchor + tlo + t;
     sm->cidx[pos] = (int32_t)(w_lo + t);
-    sm->cw[pos] = sm->rs[wbase + t];
+    if constexpr (!BF16) sm->cw[pos] = sm->rs[wbase + t];
   }
   __builtin_amdgcn_wave_barrier();
   if (a.sel_idx) {
@@ -718,17 +864,29 @@ __device__ void pf_row(const PfArgs& a, PfRowSmem* sm, size_t grow) {
   // t = gq (mod RPI), each lane a 16-byte chunk of the row; then the groups are summed.
   constexpr int U = 8;
   if constexpr (BF16) {
+    // The window's part (m_w, Z_w, O_w) comes from pf_window; here the anchor and the top-k
+    // (tidx / ts [0, nt), the anchor appended at nt), then the merge of the two parts:
+    // out = (f O_w + sum_e w_e v_e) / (f Z_w + sum_e w_e), w_e = exp(z_e - zmax),
+    // f = exp(m_w - zmax), zmax the largest logit of the set.
     const float sc = (float)a.scale;
-    float zmax = -INFINITY;
-    for (int t = lane; t < count; t += 64) zmax = fmaxf(zmax, sc * (float)sm->cw[t]);
+    const int ne = nt + anchor;
+    if (anchor && lane == 0) {
+      sm->tidx[nt] = 0;
+      sm->ts[nt] = sm->rs[c];
+    }
+    __builtin_amdgcn_wave_barrier();
+    const float2 mz = a.win ? a.w.win_mz[grow] : make_float2(-INFINITY, 0.f);
+    float zmax = mz.x;
+    for (int t = lane; t < ne; t += 64) zmax = fmaxf(zmax, sc * (float)sm->ts[t]);
     zmax = wave_max_f32(zmax);
     float zsum = 0.f;
-    for (int t = lane; t < count; t += 64) {
-      const float w = __expf(sc * (float)sm->cw[t] - zmax);
-      sm->cw[t] = (double)w;
+    for (int t = lane; t < ne; t += 64) {
+      const float w = __expf(sc * (float)sm->ts[t] - zmax);
+      sm->ts[t] = (double)w;
       zsum += w;
     }
-    zsum = wave_sum_f32(zsum);
+    const float fw = a.win ? __expf(mz.x - zmax) : 0.f;
+    zsum = wave_sum_f32(zsum) + fw * mz.y;
     __builtin_amdgcn_wave_barrier();
     float acc[EPC];
 #pragma unroll
@@ -744,15 +902,15 @@ __device__ void pf_row(const PfArgs& a, PfRowSmem* sm, size_t grow) {
         }
       }
     };
-    for (int t0 = 0; t0 < count; t0 += U * RPI) {
+    for (int t0 = 0; t0 < ne; t0 += U * RPI) {
       uint4 x[U];
       float w[U];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int t = t0 + u * RPI + gq;
-        const bool ok = t < count;
-        x[u] = ok ? *(const uint4*)(vb + (size_t)sm->cidx[t] * RB + cc * 16) : make_uint4(0u, 0u, 0u, 0u);
-        w[u] = ok ? (float)sm->cw[t] : 0.f;
+        const bool ok = t < ne;
+        x[u] = ok ? *(const uint4*)(vb + (size_t)sm->tidx[t] * RB + cc * 16) : make_uint4(0u, 0u, 0u, 0u);
+        w[u] = ok ? (float)sm->ts[t] : 0.f;
       }
       accumulate(x, w);
     }
@@ -761,6 +919,17 @@ __device__ void pf_row(const PfArgs& a, PfRowSmem* sm, size_t grow) {
 #pragma unroll
       for (int e = 0; e < EPC; ++e) acc[e] += __shfl_xor(acc[e], o);
     if (gq == 0) {
+      if (a.win) {
+        const float4* wo = (const float4*)(a.w.win_o + grow * D + cc * EPC);
+#pragma unroll
+        for (int e = 0; e < EPC / 4; ++e) {
+          const float4 o4 = wo[e];
+          acc[4 * e] = fmaf(fw, o4.x, acc[4 * e]);
+          acc[4 * e + 1] = fmaf(fw, o4.y, acc[4 * e + 1]);
+          acc[4 * e + 2] = fmaf(fw, o4.z, acc[4 * e + 2]);
+          acc[4 * e + 3] = fmaf(fw, o4.w, acc[4 * e + 3]);
+        }
+      }
       const float inv = 1.0f / zsum;
       float4* dst = (float4*)(a.out + grow * D + cc * EPC);
 #pragma unroll
@@ -845,6 +1014,14 @@ static hipError_t launch_pf_t(const PrefillLaunch& L, const PfArgs& pa, hipStrea
     }
   }
   if (L.ev_scan_end) (void)hipEventRecord(L.ev_scan_end, s);
+  if constexpr (BF16) {
+    if (pa.win) {
+      hipLaunchKernelGGL((pf_window_kernel<D>), dim3((unsigned)((L.n_q + 31) / 32 * L.B * L.Hq)), dim3(D / 32 * 64), 0, s,
+                         pa);
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+  }
   const size_t smem = 4 * pa.wave_smem;
   if (smem > 48 * 1024)
     (void)hipFuncSetAttribute((const void*)pf_finish_kernel<D, BF16>, hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -862,7 +1039,7 @@ hipError_t launch_prefill(const PrefillLaunch& L, hipStream_t stream) {
   pa.out = L.out;
   pa.sel_idx = L.sel_idx;
   pa.sel_count = L.sel_count;
-  pa.w = pf_carve(L.ws, L.B, L.Hq, L.n_q);
+  pa.w = pf_carve(L.ws, L.B, L.Hq, L.n_q, L.d, L.topk);
   pa.n = L.n;
   pa.n_q = L.n_q;
   pa.q_pos0 = L.q_pos0;
@@ -874,6 +1051,7 @@ hipError_t launch_prefill(const PrefillLaunch& L, hipStream_t stream) {
   pa.topk = L.topk;
   pa.causal = L.causal;
   pa.set_cap = 1 + L.W + L.topk;
+  pa.win = (L.bf16 && L.W > 0 && L.out) ? 1 : 0;
   // the scan addresses a kv head's keys with 32-bit buffer offsets
   pa.exact_all = (!L.bf16 || L.topk > PF_MAX_K || (L.flags & 1) || L.n * 2 * L.d >= ((int64_t)1 << 31)) ? 1 : 0;
   static_assert(PF_MAX_K + 16 <= PF_LCAP_MAX, "list room above k");
