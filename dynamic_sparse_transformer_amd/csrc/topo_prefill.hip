@@ -120,6 +120,13 @@ __global__ __launch_bounds__(256) void pf_kmax_kernel(const unsigned char* k, ui
   }
 }
 
+// Job of block `blk` among `njobs`: consecutive block indices go to different XCDs (round robin),
+// so the jobs are dealt out in eight contiguous ranges, one per XCD, and the rows of one head
+// share one XCD's L2.
+__device__ __forceinline__ int64_t xcd_job(int64_t blk, int64_t njobs) {
+  return njobs % 8 == 0 ? (blk & 7) * (njobs >> 3) + (blk >> 3) : blk;
+}
+
 __global__ void pf_zero_kernel(uint32_t* x, int64_t n) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) x[i] = 0u;
@@ -180,14 +187,10 @@ __global__ __launch_bounds__(512) void pf_scan_kernel(PfArgs a) {
   __shared__ float lthf[PF_ROWS];
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  // Job of this block: consecutive block indices go to different XCDs (round robin), so the jobs
-  // are dealt out in eight contiguous ranges, one per XCD, which keeps the blocks of one head on
-  // one XCD's L2. Within a head the row blocks run from the last (most keys under a causal mask)
-  // to the first, so the long jobs start first.
+  // Job of this block (the blocks of one head on one XCD). Within a head the row blocks run from
+  // the last (most keys under a causal mask) to the first, so the long jobs start first.
   const int64_t nrb = (a.n_q + PF_ROWS - 1) / PF_ROWS;
-  const int64_t njobs = nrb * a.Hq * (a.rows / (a.n_q * a.Hq));
-  int64_t job = blockIdx.x;
-  if (njobs % 8 == 0) job = (job & 7) * (njobs >> 3) + (job >> 3);
+  const int64_t job = xcd_job(blockIdx.x, nrb * a.Hq * (a.rows / (a.n_q * a.Hq)));
   const int bh = (int)(job / nrb);
   const int b = bh / a.Hq, h = bh - b * a.Hq, g = h / a.G;
   const int64_t i0 = (nrb - 1 - (job - (int64_t)bh * nrb)) * PF_ROWS;
@@ -432,8 +435,9 @@ __global__ __launch_bounds__(256) void pf_window_kernel(PfArgs a) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int m = lane & 31, half = lane >> 5;
   const int64_t nrb = (a.n_q + 31) / 32;
-  const int bh = (int)(blockIdx.x / nrb);
-  const int64_t i0 = ((int64_t)blockIdx.x - (int64_t)bh * nrb) * 32;
+  const int64_t job = xcd_job(blockIdx.x, nrb * a.Hq * (a.rows / (a.n_q * a.Hq)));
+  const int bh = (int)(job / nrb);
+  const int64_t i0 = (job - (int64_t)bh * nrb) * 32;
   const int b = bh / a.Hq, h = bh - b * a.Hq, g = h / a.G;
   const unsigned char* kb = a.k + ((size_t)b * a.Hkv + g) * (size_t)a.n * RB;
   const unsigned char* vb = a.v + ((size_t)b * a.Hkv + g) * (size_t)a.n * RB;
@@ -553,13 +557,13 @@ struct PfRowSmem {
   double* rs;      // [slot + set_cap]: float64 scores of the row's list, window and anchor keys
   double* ts;      // [k + 1]
   double* cw;      // [set_cap]
-  int32_t* ridx;   // [slot]
+  int32_t* ridx;   // [slot + 1]: the list, then the anchor
   int32_t* tidx;   // [k + 1]
   int32_t* cidx;   // [set_cap]
   uint32_t* hist;  // [256]
   static __host__ __device__ size_t bytes(int64_t slot, int k, int set_cap) {
     const size_t kk = (size_t)k + 1;
-    return 128 * 8 + ((size_t)slot + set_cap) * 8 + kk * 12 + (size_t)set_cap * 12 + (size_t)slot * 4 + 256 * 4 + 64;
+    return 128 * 8 + ((size_t)slot + set_cap) * 8 + kk * 12 + (size_t)set_cap * 12 + ((size_t)slot + 1) * 4 + 256 * 4 + 64;
   }
   __device__ void carve(unsigned char* p, int64_t slot, int k, int set_cap) {
     const size_t kk = (size_t)k + 1;
@@ -572,7 +576,7 @@ struct PfRowSmem {
     cw = (double*)p;
     p += (size_t)set_cap * 8;
     ridx = (int32_t*)p;
-    p += (size_t)slot * 4;
+    p += ((size_t)slot + 1) * 4;
     tidx = (int32_t*)p;
     p += kk * 4;
     cidx = (int32_t*)p;
@@ -660,13 +664,12 @@ __device__ int pf_exact_row(PfRowSmem* sm, const PfArgs& a, const unsigned char*
   return nt;
 }
 
-// One query row of the finish, by one wave. Steps: float64 canonical scores of the row's list and
-// of the anchor (each lane one key, the whole row requested at once) and the exact rank of the
-// list; scores of the window keys; the set in ascending order; softmax over it and the weighted V
-// rows. Arithmetic: the ranking always uses the float64 canonical scores. With bf16 inputs the
-// window logits (16-byte chunks per lane, summed across lanes), the softmax and the V sum are
-// float32 (products of bf16 values are exact in float32; sums round once per add); with float32
-// inputs all of it is float64.
+// One query row of the finish, by one wave. bf16 inputs: float32 scores of the row's list and of
+// the anchor (16-byte chunks per lane, summed across lanes), the top-k from them with the error
+// band (float64 canonical scores only for entries inside the band), the set in ascending order,
+// then softmax and V sum over the anchor and the top-k in float32, merged with the window's share
+// from pf_window. float32 inputs: float64 canonical scores of the list, anchor and window, exact
+// rank of the list, float64 softmax and V sum over the whole set.
 template <int D, bool BF16>
 __device__ void pf_row(const PfArgs& a, PfRowSmem* sm, size_t grow) {
   constexpr int RB = D * (BF16 ? 2 : 4);
@@ -681,6 +684,9 @@ __device__ void pf_row(const PfArgs& a, PfRowSmem* sm, size_t grow) {
   const int64_t p = a.q_pos0 + i;
   const unsigned char* qrow = a.q + grow * RB;
   const int gq = lane / LPR, cc = lane % LPR;
+  // error-bound inputs, requested early: |q| of the row and the largest |k| of the kv head
+  const float qn_row = a.w.qn[grow];
+  const float kn_max = __uint_as_float(a.w.knmax[(size_t)b * a.Hkv + g]);
   for (int t = lane; t < D; t += 64) sm->qd[t] = load_elem_f64<BF16>(qrow, t);
 
   const int64_t w_lo = p - a.W + 1 > 0 ? p - a.W + 1 : 0;
@@ -711,16 +717,19 @@ __device__ void pf_row(const PfArgs& a, PfRowSmem* sm, size_t grow) {
   if constexpr (BF16) {
     // float32 scores of every item: LPR lanes per key, a 16-byte chunk each (v_dot2_f32_bf16),
     // summed across the lanes with DPP adds. |s32 - s| <= eps32 for every item (s the exact score).
+    // The anchor's position goes after the list, so every item is read through ridx; the loads of
+    // the last group are clamped onto the last item.
     {
+      if (anchor && lane == 0) sm->ridx[c] = 0;
+      __builtin_amdgcn_wave_barrier();
       const uint4 qv = *(const uint4*)(qrow + cc * 16);
       constexpr int U = 8;
       for (int t0 = 0; t0 < nitems; t0 += U * RPI) {
         uint4 x[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-          const int t = t0 + u * RPI + gq;
-          const int64_t j = t < c ? (int64_t)sm->ridx[t] : (t < wbase ? 0 : w_lo + (t - wbase));
-          x[u] = t < nitems ? *(const uint4*)(kb + (size_t)j * RB + cc * 16) : make_uint4(0u, 0u, 0u, 0u);
+          const int t = min(t0 + u * RPI + gq, nitems - 1);
+          x[u] = *(const uint4*)(kb + (size_t)sm->ridx[t] * RB + cc * 16);
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
@@ -731,15 +740,16 @@ __device__ void pf_row(const PfArgs& a, PfRowSmem* sm, size_t grow) {
       }
     }
     __builtin_amdgcn_wave_barrier();
-    const float eps32 =
-        a.eps32 * a.w.qn[grow] * __uint_as_float(a.w.knmax[(size_t)b * a.Hkv + g]) * (1.0f + 0x1p-10f) + 1e-30f;
+    const float eps32 = a.eps32 * qn_row * kn_max * (1.0f + 0x1p-10f) + 1e-30f;
     if (exact) {
       nt = pf_exact_row<D, BF16>(sm, a, kb, p);
     } else if (c > a.topk) {
       // x_k = k-th largest float32 score of the list; A = entries with s32 >= x_k - 2 eps32. Every
       // entry outside A scores below all k entries with s32 >= x_k, so the top-k lies in A, and
-      // if |A| = k it is A. Otherwise (entries within the error band of the boundary, or ties)
-      // the entries of A are ranked by their float64 canonical scores, then by position.
+      // if |A| = k it is A. Otherwise an entry with s32 > x_k + 2 eps32 is surely in the top-k
+      // (only entries with s32 > x_k, at most k - 1 of them, can score above it), and the rest of
+      // A, the band around x_k, is ranked by float64 canonical scores, then by position; its best
+      // k - (sure entries) complete the top-k.
       const float s0 = lane < c ? (float)sm->rs[lane] : 0.f;
       const float s1 = lane + 64 < c ? (float)sm->rs[lane + 64] : 0.f;
       const uint32_t key[2] = {lane < c ? ord_f32(s0) : 0u, lane + 64 < c ? ord_f32(s1) : 0u};
@@ -762,26 +772,42 @@ __device__ void pf_row(const PfArgs& a, PfRowSmem* sm, size_t grow) {
         nt = a.topk;
         __builtin_amdgcn_wave_barrier();
       } else {
-        // compact A (positions to ridx[0, na), canonical scores to rs[0, na)) and rank it
-        int32_t j0 = in0 ? sm->ridx[lane] : 0, j1 = in1 ? sm->ridx[lane + 64] : 0;
+        const float hi = (xk + 2.0f * eps32) + fabsf(xk) * 0x1p-20f;
+        const bool su0 = in0 && s0 > hi, su1 = in1 && s1 > hi;
+        const bool bd0 = in0 && !su0, bd1 = in1 && !su1;
+        const uint64_t ms0 = __ballot(su0), ms1 = __ballot(su1), mb0 = __ballot(bd0), mb1 = __ballot(bd1);
+        const int ns = __popcll(ms0) + __popcll(ms1), nb = __popcll(mb0) + __popcll(mb1);
+        // sure entries to tidx / ts [0, ns); the band's positions to ridx [0, nb)
+        const int32_t j0 = in0 ? sm->ridx[lane] : 0, j1 = in1 ? sm->ridx[lane + 64] : 0;
         __builtin_amdgcn_wave_barrier();
-        if (in0) sm->ridx[lanes_below(m0)] = j0;
-        if (in1) sm->ridx[__popcll(m0) + lanes_below(m1)] = j1;
+        if (su0) {
+          const int pos = lanes_below(ms0);
+          sm->tidx[pos] = j0;
+          sm->ts[pos] = (double)s0;
+        }
+        if (su1) {
+          const int pos = __popcll(ms0) + lanes_below(ms1);
+          sm->tidx[pos] = j1;
+          sm->ts[pos] = (double)s1;
+        }
+        if (bd0) sm->ridx[lanes_below(mb0)] = j0;
+        if (bd1) sm->ridx[__popcll(mb0) + lanes_below(mb1)] = j1;
         __builtin_amdgcn_wave_barrier();
-        for (int t = lane; t < na; t += 64)
+        for (int t = lane; t < nb; t += 64)
           sm->rs[t] = canonical_score_row<BF16, D>(sm->qd, kb + (size_t)sm->ridx[t] * RB);
         __builtin_amdgcn_wave_barrier();
-        for (int t = lane; t < na; t += 64) {
+        const int need = a.topk - ns;
+        for (int t = lane; t < nb; t += 64) {
           const double si = sm->rs[t];
           const int32_t ji = sm->ridx[t];
           int rank = 0;
-          for (int r = 0; r < na; ++r) {
+          for (int r = 0; r < nb; ++r) {
             const double sr = sm->rs[r];
             rank += (sr > si) || (sr == si && sm->ridx[r] < ji);
           }
-          if (rank < a.topk) {
-            sm->tidx[rank] = ji;
-            sm->ts[rank] = si;
+          if (rank < need) {
+            sm->tidx[ns + rank] = ji;
+            sm->ts[ns + rank] = si;
           }
         }
         nt = a.topk;
@@ -986,7 +1012,7 @@ __global__ __launch_bounds__(256) void pf_finish_kernel(PfArgs a) {
   const int wave = threadIdx.x >> 6;
   PfRowSmem smv;
   smv.carve(smem_raw + wave * a.wave_smem, a.slot, a.topk, a.set_cap);
-  const size_t grow = (size_t)blockIdx.x * 4 + wave;  // (b*Hq + h) * n_q + i
+  const size_t grow = (size_t)xcd_job(blockIdx.x, gridDim.x) * 4 + wave;  // (b*Hq + h) * n_q + i
   if (grow >= (size_t)a.rows) return;
   pf_row<D, BF16>(a, &smv, grow);
 }
