@@ -664,6 +664,30 @@ __device__ int pf_exact_row(PfRowSmem* sm, const PfArgs& a, const unsigned char*
   return nt;
 }
 
+// Ascending bitonic sort of the 64 E values of a wave (value i = x[i / 64] of lane i % 64).
+template <int E>
+__device__ __forceinline__ void wave_sort_asc_u32(uint32_t (&x)[E]) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int size = 2; size <= 64 * E; size <<= 1) {
+#pragma unroll
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      if (stride == 64) {  // E == 2: values lane and lane + 64, one ascending block
+        const uint32_t lo = min(x[0], x[1]), hi = max(x[0], x[1]);
+        x[0] = lo;
+        x[1] = hi;
+      } else {
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          const int i = lane + 64 * e;
+          const uint32_t y = (uint32_t)__shfl_xor((int)x[e], stride);
+          x[e] = (((i & size) == 0) == ((i & stride) == 0)) ? min(x[e], y) : max(x[e], y);
+        }
+      }
+    }
+  }
+}
+
 // One query row of the finish, by one wave. bf16 inputs: float32 scores of the row's list and of
 // the anchor (16-byte chunks per lane, summed across lanes), the top-k from them with the error
 // band (float64 canonical scores only for entries inside the band), the set in ascending order,
@@ -723,7 +747,7 @@ __device__ void pf_row(const PfArgs& a, PfRowSmem* sm, size_t grow) {
       if (anchor && lane == 0) sm->ridx[c] = 0;
       __builtin_amdgcn_wave_barrier();
       const uint4 qv = *(const uint4*)(qrow + cc * 16);
-      constexpr int U = 8;
+      constexpr int U = 4;
       for (int t0 = 0; t0 < nitems; t0 += U * RPI) {
         uint4 x[U];
 #pragma unroll
@@ -863,15 +887,31 @@ __device__ void pf_row(const PfArgs& a, PfRowSmem* sm, size_t grow) {
   tlo = wave_sum_i32(tlo);
   if (anchor && lane == 0) {
     sm->cidx[0] = 0;
-    sm->cw[0] = sm->rs[c];
+    if constexpr (!BF16) sm->cw[0] = sm->rs[c];
   }
-  for (int t = lane; t < nt; t += 64) {
-    const int32_t j = sm->tidx[t];
-    int below = 0;
-    for (int r = 0; r < nt; ++r) below += sm->tidx[r] < j;
-    const int pos = anchor + below + (j > p ? nwin : 0);
-    sm->cidx[pos] = j;
-    sm->cw[pos] = sm->ts[t];
+  if (BF16 && nt <= 128) {
+    // the top-k positions sorted (distinct keys; empty slots sort last): the t-th smallest goes
+    // to slot anchor + t, after the window if it lies past p
+    if (nt <= 64) {
+      uint32_t x[1] = {lane < nt ? (uint32_t)sm->tidx[lane] : 0xFFFFFFFFu};
+      wave_sort_asc_u32<1>(x);
+      if (lane < nt) sm->cidx[anchor + lane + ((int64_t)x[0] > p ? nwin : 0)] = (int32_t)x[0];
+    } else {
+      uint32_t x[2] = {(uint32_t)sm->tidx[lane], lane + 64 < nt ? (uint32_t)sm->tidx[lane + 64] : 0xFFFFFFFFu};
+      wave_sort_asc_u32<2>(x);
+      sm->cidx[anchor + lane + ((int64_t)x[0] > p ? nwin : 0)] = (int32_t)x[0];
+      if (lane + 64 < nt) sm->cidx[anchor + lane + 64 + ((int64_t)x[1] > p ? nwin : 0)] = (int32_t)x[1];
+    }
+  } else {
+    // rank of each top-k position among the others
+    for (int t = lane; t < nt; t += 64) {
+      const int32_t j = sm->tidx[t];
+      int below = 0;
+      for (int r = 0; r < nt; ++r) below += sm->tidx[r] < j;
+      const int pos = anchor + below + (j > p ? nwin : 0);
+      sm->cidx[pos] = j;
+      if constexpr (!BF16) sm->cw[pos] = sm->ts[t];
+    }
   }
   for (int t = lane; t < nwin; t += 64) {
     const int pos = anchor + tlo + t;
@@ -888,7 +928,7 @@ __device__ void pf_row(const PfArgs& a, PfRowSmem* sm, size_t grow) {
 
   // ---- softmax over the set and the weighted V rows: lane group gq takes the entries
   // t = gq (mod RPI), each lane a 16-byte chunk of the row; then the groups are summed.
-  constexpr int U = 8;
+  constexpr int U = 4;
   if constexpr (BF16) {
     // The window's part (m_w, Z_w, O_w) comes from pf_window; here the anchor and the top-k
     // (tidx / ts [0, nt), the anchor appended at nt), then the merge of the two parts:
