@@ -12,11 +12,12 @@
 //   pf_scan    bf16 MFMA tiles, 128 query rows x 64 keys per step (8 waves, one 32x32x16 tile
 //              each), float32 scores, two passes over the keys: the first bounds each row's k-th
 //              best score from below, the second lists every key that may still reach it.
-//   pf_finish  one wave per query row: float32 re-score of the row's list with its error band,
+//   pf_window  matrix-core softmax share of every row's window (max, sum, weighted V).
+//   pf_finish  one wave per query row: top-k from the list's scores with their error band,
 //              float64 canonical scores where the band leaves the top-k open, the set, softmax
-//              and V reduction. Rows whose list overflowed (ties), float32 inputs and k above the
-//              scan's limit take an exact float64 radix selection over all of the row's
-//              candidates instead.
+//              and V reduction over anchor and top-k, merged with the window's share. Rows
+//              whose list overflowed (ties), float32 inputs and k above the scan's limit take
+//              an exact float64 radix selection over all of the row's candidates instead.
 #include "topo_device.h"
 #include "topo_internal.h"
 
@@ -33,17 +34,18 @@ constexpr uint32_t PF_OVERFLOW = 0xFFFFFFFFu;
 constexpr float PF_EPS_COEF = 0x1p-14f;
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
-// LDS of the scan for the per-row lists of possible top-k keys (and the top-2 values before
-// them): 128 floats per row, so a list holds at most 128 key positions; k + 48 slots are used.
+// LDS of the scan for the top-2 values of each row's lanes (phase 1), then for the waves' score
+// stages (phase 2). A row's list of possible top-k keys holds k + 48 entries, at most 128 (the
+// finish ranks two per lane).
 constexpr int PF_LIST_BYTES = PF_ROWS * 128 * 4;
-constexpr int PF_LCAP_MAX = PF_LIST_BYTES / (PF_ROWS * 4);
+constexpr int PF_LCAP_MAX = 128;
 static int64_t pf_slot(int32_t k) { return k + 48 < PF_LCAP_MAX ? k + 48 : PF_LCAP_MAX; }
 
 struct PfWs {
   float* qn;        // [B*Hq*n_q]
   uint32_t* knmax;  // [B*Hkv] float bits
   uint32_t* cnt;    // [B*Hq*n_q]: entries of the row's list (or PF_OVERFLOW)
-  uint32_t* surv;   // [B*Hq*n_q][list]: key positions of the row's list
+  uint2* surv;      // [B*Hq*n_q][list]: (float bits of the matrix-core score, key position)
   float* win_o;     // [B*Hq*n_q][d]: sum over the row's window of exp(z - m_w) v (bf16 inputs)
   float2* win_mz;   // [B*Hq*n_q]: (m_w, sum over the window of exp(z - m_w))
 };
@@ -51,7 +53,7 @@ struct PfWs {
 size_t prefill_workspace_bytes(int32_t B, int32_t Hq, int64_t n_q, int64_t, int32_t d, int32_t, int32_t k) {
   const size_t rows = (size_t)B * Hq * (size_t)n_q;
   return align256(rows * 4) + align256((size_t)B * Hq * 4) + align256(rows * 4) +
-         align256(rows * (size_t)pf_slot(k) * sizeof(uint32_t)) + align256(rows * (size_t)d * 4) + rows * 8;
+         align256(rows * (size_t)pf_slot(k) * sizeof(uint2)) + align256(rows * (size_t)d * 4) + rows * 8;
 }
 
 static PfWs pf_carve(void* ws, int32_t B, int32_t Hq, int64_t n_q, int32_t d, int32_t k) {
@@ -64,8 +66,8 @@ static PfWs pf_carve(void* ws, int32_t B, int32_t Hq, int64_t n_q, int32_t d, in
   p += align256((size_t)B * Hq * 4);
   w.cnt = (uint32_t*)p;
   p += align256(rows * 4);
-  w.surv = (uint32_t*)p;
-  p += align256(rows * (size_t)pf_slot(k) * sizeof(uint32_t));
+  w.surv = (uint2*)p;
+  p += align256(rows * (size_t)pf_slot(k) * sizeof(uint2));
   w.win_o = (float*)p;
   p += align256(rows * (size_t)d * 4);
   w.win_mz = (float2*)p;
@@ -144,7 +146,6 @@ struct PfArgs {
   int64_t n, n_q, q_pos0, slot, rows;
   int32_t Hq, Hkv, G, W, topk, causal, set_cap, exact_all;
   int32_t win;  // 1: the window kernel has left (m_w, Z_w, O_w) of every row in the workspace
-  float eps32;  // float32 dot-product error bound coefficient: |s32 - s| <= eps32 |q| |k|
   float pinf;   // +inf (a run-time operand of the scan's medians)
   double scale;
   size_t wave_smem;  // bytes of LDS per wave in pf_finish
@@ -197,7 +198,10 @@ __global__ __launch_bounds__(512) void pf_scan_kernel(PfArgs a) {
   const unsigned char* kb = a.k + ((size_t)b * a.Hkv + g) * (size_t)a.n * RB;
   const float knmax = __uint_as_float(a.w.knmax[(size_t)b * a.Hkv + g]);
   const uint32_t LCAP = (uint32_t)a.slot;
-  uint32_t* lkeys = (uint32_t*)lists;
+  // phase 2 stages each wave's 16 scores per lane here (where the top-2 values were): chunk q
+  // (registers 4q..4q+3) of lane l at float4 index q * 64 + l of the wave's 4 KB
+  float4* sst = (float4*)lists + wave * 256;
+  const size_t grow0 = (size_t)bh * a.n_q + i0;  // global row of block row 0
   const int n = (int)a.n;  // the host runs this scan only when n * RB < 2^31
 
   const int rq = wave >> 1, kq = wave & 1;
@@ -354,12 +358,13 @@ __global__ __launch_bounds__(512) void pf_scan_kernel(PfArgs a) {
   for (int r = 0; r < 16; ++r) thf[r] = lthf[row_base + 8 * (r / 4) + (r % 4)];
 
   // ---- phase 2: every candidate key whose upper bound reaches the row's bound goes to the row's
-  // list. A lane first gathers the test results of its 16 registers into bit r of `bits`: the
-  // test x >= T is the sign of x - T (T finite, x finite or -inf), shifted in by v_alignbit. Then
-  // it takes its set bits one at a time: a slot from the row's LDS counter, the key position into
-  // the slot. The lanes of a wave pass through that loop together as often as the busiest lane
-  // needs (a step has about one passing register per four lanes). Slots past the end are clamped
-  // onto the last one; a row whose count ends above LCAP takes the exact path.
+  // list in global memory, with its score. A lane first gathers the test results of its 16
+  // registers into bit r of `bits`: the test x >= T is the sign of x - T (T finite, x finite or
+  // -inf), shifted in by v_alignbit; its 16 scores go to the wave's LDS stage. Then it takes its
+  // set bits one at a time: a slot from the row's LDS counter, (score read back from the stage,
+  // key position) into the slot. The lanes of a wave pass through that loop together as often as
+  // the busiest lane needs (a step has about one passing register per four lanes). Slots past the
+  // end are clamped onto the last one; a row whose count ends above LCAP takes the exact path.
 #define PF_EPI2(ACC, t)                                                                            \
   {                                                                                                \
     uint32_t fail = 0u;                                                                            \
@@ -367,13 +372,16 @@ __global__ __launch_bounds__(512) void pf_scan_kernel(PfArgs a) {
       fail = __builtin_amdgcn_alignbit(fail, __float_as_uint(ACC[r] - thf[r]), 31);                \
     PF_INTERLEAVE()                                                                                \
     uint32_t bits = ~fail & 0xFFFFu;                                                               \
+    _Pragma("unroll") for (int q4 = 0; q4 < 4; ++q4)                                               \
+      sst[q4 * 64 + lane] = make_float4(ACC[4 * q4], ACC[4 * q4 + 1], ACC[4 * q4 + 2], ACC[4 * q4 + 3]); \
     const uint32_t jj = (uint32_t)((t) * PF_KEYS + kq * 32 + m);                                   \
     while (bits) {                                                                                 \
       const int r = __builtin_ctz(bits);                                                           \
       bits &= bits - 1u;                                                                           \
       const int row = row_base + r + (r & 12); /* row_base + 8 * (r / 4) + r % 4 */               \
       const uint32_t sl = min(atomicAdd(&lcnt[row], 1u), LCAP - 1u);                               \
-      lkeys[__umul24((uint32_t)row, LCAP) + sl] = jj;                                              \
+      const float x = ((const float*)sst)[((r >> 2) * 64 + lane) * 4 + (r & 3)];                   \
+      a.w.surv[(grow0 + row) * LCAP + sl] = make_uint2(__float_as_uint(x), jj);                    \
     }                                                                                              \
   }
   if (ntiles > 0) {
@@ -384,18 +392,10 @@ __global__ __launch_bounds__(512) void pf_scan_kernel(PfArgs a) {
     }
   }
 
-  // the lists and their counts to global memory: wave w takes rows w, w+8, ...
-  for (int row = wave; row < PF_ROWS; row += 8) {
-    const int64_t i = i0 + row;
-    if (i >= a.n_q) continue;
-    const size_t grow = (size_t)bh * a.n_q + i;
-    const uint32_t c = lcnt[row];
-    if (c > LCAP) {
-      if (lane == 0) a.w.cnt[grow] = PF_OVERFLOW;
-      continue;
-    }
-    for (uint32_t t = lane; t < c; t += 64) a.w.surv[grow * LCAP + t] = lkeys[row * LCAP + t];
-    if (lane == 0) a.w.cnt[grow] = c;
+  // the counts of the lists (or the overflow mark)
+  if (tid < PF_ROWS && i0 + tid < a.n_q) {
+    const uint32_t c = lcnt[tid];
+    a.w.cnt[grow0 + tid] = c > LCAP ? PF_OVERFLOW : c;
   }
 #undef PF_INTERIOR
 #undef PF_LOAD
@@ -688,11 +688,10 @@ __device__ __forceinline__ void wave_sort_asc_u32(uint32_t (&x)[E]) {
   }
 }
 
-// One query row of the finish, by one wave. bf16 inputs: float32 scores of the row's list and of
-// the anchor (16-byte chunks per lane, summed across lanes), the top-k from them with the error
-// band (float64 canonical scores only for entries inside the band), the set in ascending order,
-// then softmax and V sum over the anchor and the top-k in float32, merged with the window's share
-// from pf_window. float32 inputs: float64 canonical scores of the list, anchor and window, exact
+// One query row of the finish, by one wave. bf16 inputs: the top-k from the scan's matrix-core
+// scores of the row's list with their error band (float64 canonical scores only for entries
+// inside the band), the set in ascending order, then softmax and V sum over the anchor and the
+// top-k in float32, merged with the window's share from pf_window. float32 inputs: float64 canonical scores of the list, anchor and window, exact
 // rank of the list, float64 softmax and V sum over the whole set.
 template <int D, bool BF16>
 __device__ void pf_row(const PfArgs& a, PfRowSmem* sm, size_t grow) {
@@ -725,10 +724,14 @@ __device__ void pf_row(const PfArgs& a, PfRowSmem* sm, size_t grow) {
     exact = cr == PF_OVERFLOW;
     if (!exact) {
       c = (int)cr;
-      const uint32_t* sv = a.w.surv + grow * (size_t)a.slot;
+      const uint2* sv = a.w.surv + grow * (size_t)a.slot;
       // positions come from the scan and are always keys of the cache; clamping only guards
-      // the reads below
-      for (int t = lane; t < c; t += 64) sm->ridx[t] = (int32_t)min(sv[t], (uint32_t)(a.n - 1));
+      // the reads below. With bf16 inputs the scan's matrix-core scores come along.
+      for (int t = lane; t < c; t += 64) {
+        const uint2 e = sv[t];
+        sm->ridx[t] = (int32_t)min(e.y, (uint32_t)(a.n - 1));
+        if constexpr (BF16) sm->rs[t] = (double)__uint_as_float(e.x);
+      }
     }
   }
   __builtin_amdgcn_wave_barrier();
@@ -739,46 +742,31 @@ __device__ void pf_row(const PfArgs& a, PfRowSmem* sm, size_t grow) {
   const int nitems = BF16 ? wbase : wbase + nwin;
   int nt = 0;
   if constexpr (BF16) {
-    // float32 scores of every item: LPR lanes per key, a 16-byte chunk each (v_dot2_f32_bf16),
-    // summed across the lanes with DPP adds. |s32 - s| <= eps32 for every item (s the exact score).
-    // The anchor's position goes after the list, so every item is read through ridx; the loads of
-    // the last group are clamped onto the last item.
-    {
-      if (anchor && lane == 0) sm->ridx[c] = 0;
-      __builtin_amdgcn_wave_barrier();
+    // The list's scores are the scan's matrix-core float32 scores, |s_mc - s| <= eps (s the
+    // exact score). The anchor gets a float32 score here (LPR lanes, a 16-byte chunk each,
+    // v_dot2_f32_bf16, summed across the lanes with DPP adds); it only enters the softmax.
+    if (anchor) {
       const uint4 qv = *(const uint4*)(qrow + cc * 16);
-      constexpr int U = 4;
-      for (int t0 = 0; t0 < nitems; t0 += U * RPI) {
-        uint4 x[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-          const int t = min(t0 + u * RPI + gq, nitems - 1);
-          x[u] = *(const uint4*)(kb + (size_t)sm->ridx[t] * RB + cc * 16);
-        }
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-          const float part = group_sum_f32<LPR>(dot_chunk_bf16(qv, x[u], 0.0f));
-          const int t = t0 + u * RPI + gq;
-          if (cc == 0 && t < nitems) sm->rs[t] = (double)part;
-        }
-      }
+      const uint4 x = *(const uint4*)(kb + cc * 16);
+      const float part = group_sum_f32<LPR>(dot_chunk_bf16(qv, x, 0.0f));
+      if (lane == 0) sm->rs[c] = (double)part;
     }
     __builtin_amdgcn_wave_barrier();
-    const float eps32 = a.eps32 * qn_row * kn_max * (1.0f + 0x1p-10f) + 1e-30f;
+    const float eps = PF_EPS_COEF * qn_row * kn_max + 1e-30f;
     if (exact) {
       nt = pf_exact_row<D, BF16>(sm, a, kb, p);
     } else if (c > a.topk) {
-      // x_k = k-th largest float32 score of the list; A = entries with s32 >= x_k - 2 eps32. Every
-      // entry outside A scores below all k entries with s32 >= x_k, so the top-k lies in A, and
-      // if |A| = k it is A. Otherwise an entry with s32 > x_k + 2 eps32 is surely in the top-k
-      // (only entries with s32 > x_k, at most k - 1 of them, can score above it), and the rest of
+      // x_k = k-th largest score of the list; A = entries with s_mc >= x_k - 2 eps. Every
+      // entry outside A scores below all k entries with s_mc >= x_k, so the top-k lies in A, and
+      // if |A| = k it is A. Otherwise an entry with s_mc > x_k + 2 eps is surely in the top-k
+      // (only entries with s_mc > x_k, at most k - 1 of them, can score above it), and the rest of
       // A, the band around x_k, is ranked by float64 canonical scores, then by position; its best
       // k - (sure entries) complete the top-k.
       const float s0 = lane < c ? (float)sm->rs[lane] : 0.f;
       const float s1 = lane + 64 < c ? (float)sm->rs[lane + 64] : 0.f;
       const uint32_t key[2] = {lane < c ? ord_f32(s0) : 0u, lane + 64 < c ? ord_f32(s1) : 0u};
       const float xk = unord_f32(wave_kth_largest<2>(key, a.topk));
-      const float thr = (xk - 2.0f * eps32) - fabsf(xk) * 0x1p-20f;
+      const float thr = (xk - 2.0f * eps) - fabsf(xk) * 0x1p-20f;
       const bool in0 = lane < c && s0 >= thr, in1 = lane + 64 < c && s1 >= thr;
       const uint64_t m0 = __ballot(in0), m1 = __ballot(in1);
       const int na = __popcll(m0) + __popcll(m1);
@@ -796,7 +784,7 @@ __device__ void pf_row(const PfArgs& a, PfRowSmem* sm, size_t grow) {
         nt = a.topk;
         __builtin_amdgcn_wave_barrier();
       } else {
-        const float hi = (xk + 2.0f * eps32) + fabsf(xk) * 0x1p-20f;
+        const float hi = (xk + 2.0f * eps) + fabsf(xk) * 0x1p-20f;
         const bool su0 = in0 && s0 > hi, su1 = in1 && s1 > hi;
         const bool bd0 = in0 && !su0, bd1 = in1 && !su1;
         const uint64_t ms0 = __ballot(su0), ms1 = __ballot(su1), mb0 = __ballot(bd0), mb1 = __ballot(bd1);
@@ -1122,7 +1110,6 @@ hipError_t launch_prefill(const PrefillLaunch& L, hipStream_t stream) {
   pa.exact_all = (!L.bf16 || L.topk > PF_MAX_K || (L.flags & 1) || L.n * 2 * L.d >= ((int64_t)1 << 31)) ? 1 : 0;
   static_assert(PF_MAX_K + 16 <= PF_LCAP_MAX, "list room above k");
   pa.scale = L.scale;
-  pa.eps32 = L.eps_coef;
   pa.pinf = INFINITY;
   pa.rows = (int64_t)L.B * L.Hq * L.n_q;
   pa.wave_smem = (PfRowSmem::bytes(pa.slot, L.topk, pa.set_cap) + 255) & ~(size_t)255;
