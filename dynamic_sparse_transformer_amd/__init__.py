@@ -19,6 +19,7 @@ __all__ = [
     "TopoError", "load_library", "library_path", "topo_workspace_bytes", "topo_attn_decode",
     "topo_attn_prefill", "topo_select", "topo_attn_dense", "topo_bw_probe", "topo_strerror",
     "topo_attn_decode_timed", "topo_attn_prefill_timed", "topo_attn_decode_certified",
+    "topo_attn_decode_ragged", "topo_kv_append",
     "TOPO_FLAG_EXACT_SELECT", "TOPO_FLAG_DENSE_FALLBACK", "TOPO_CERT_RHO", "TOPO_MAX_SET", "EXPORTS",
 ]
 
@@ -27,13 +28,14 @@ library_path = os.path.join(_PKG, "libtopo_attn.so")
 
 TOPO_F32, TOPO_BF16 = 0, 1
 TOPO_OP_DECODE, TOPO_OP_PREFILL, TOPO_OP_SELECT, TOPO_OP_DENSE, TOPO_OP_DECODE_CERTIFIED = 0, 1, 2, 3, 4
+TOPO_OP_DECODE_RAGGED = 5
 TOPO_FLAG_EXACT_SELECT = 1
 TOPO_FLAG_DENSE_FALLBACK = 2
 TOPO_CERT_RHO = 2.0 ** -24
 TOPO_MAX_SET = 4096
 EXPORTS = ("topo_workspace_bytes", "topo_attn_decode", "topo_attn_decode_timed", "topo_attn_decode_certified",
-           "topo_attn_prefill", "topo_attn_prefill_timed", "topo_select", "topo_attn_dense", "topo_bw_probe",
-           "topo_strerror")
+           "topo_attn_decode_ragged", "topo_kv_append", "topo_attn_prefill", "topo_attn_prefill_timed",
+           "topo_select", "topo_attn_dense", "topo_bw_probe", "topo_strerror")
 
 
 class TopoError(RuntimeError):
@@ -76,6 +78,10 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.topo_attn_prefill_timed.restype = i32
     lib.topo_attn_decode_certified.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.topo_attn_decode_certified.restype = i32
+    lib.topo_attn_decode_ragged.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.topo_attn_decode_ragged.restype = i32
+    lib.topo_kv_append.argtypes = [P, vp, vp, vp, vp, vp, vp]
+    lib.topo_kv_append.restype = i32
     lib.topo_select.argtypes = [P, vp, vp, vp, vp, vp, sz, vp]
     lib.topo_select.restype = i32
     lib.topo_attn_dense.argtypes = [P, vp, vp, vp, vp, vp, sz, vp]
@@ -230,6 +236,63 @@ def topo_attn_prefill_timed(q, k, v, W: int, topk: int, softmax_scale: float, sc
     """topo_attn_prefill that also records scan_begin / scan_end around the matrix-core key scan."""
     return _attn_timed("topo_attn_prefill_timed", TOPO_OP_PREFILL, q, k, v, W, topk, softmax_scale, scan_begin,
                        scan_end, causal, q_pos0, flags, out, sel_idx, sel_count, workspace, stream)
+
+
+def _check_pos(pos, B):
+    torch = _torch()
+    if pos.dtype != torch.int64 or pos.dim() != 1 or pos.shape[0] != B:
+        raise ValueError(f"pos must be an int64 device tensor of shape ({B},)")
+    _check_tensors(pos)
+
+
+def topo_attn_decode_ragged(q, k, v, pos, W: int, topk: int, softmax_scale: float, flags: int = 0, out=None,
+                            sel_idx=None, sel_count=None, workspace=None, stream=None):
+    """Decode of sequences of different lengths: the query of batch element b sits at position
+    pos[b] (int64 device tensor (B,)) of its own cache and sees keys 0..pos[b]. q: (B, Hq, d) or
+    (B, Hq, 1, d); k, v: (B, Hkv, n_ctx, d). Returns (out f32 (B,Hq,1,d), sel_idx, sel_count)."""
+    torch = _torch()
+    lib = load_library()
+    q4 = q if q.dim() == 4 else q.unsqueeze(2)
+    p = _params(q4, k, W, topk, softmax_scale, True, k.shape[2] - 1, flags)
+    _check_tensors(q4, k, v)
+    B, Hq, n_q, d = q4.shape
+    _check_pos(pos, B)
+    nbytes = lib.topo_workspace_bytes(ctypes.byref(p), TOPO_OP_DECODE_RAGGED)
+    if nbytes == 0:
+        raise TopoError(-1, "topo_attn_decode_ragged: parameters rejected")
+    ws = _workspace(nbytes, q4.device, workspace)
+    if out is None:
+        out = torch.empty((B, Hq, n_q, d), dtype=torch.float32, device=q4.device)
+    if sel_idx is None:
+        sel_idx = torch.empty((B, Hq, n_q, 1 + int(W) + int(topk)), dtype=torch.int32, device=q4.device)
+    if sel_count is None:
+        sel_count = torch.empty((B, Hq, n_q), dtype=torch.int32, device=q4.device)
+    _check_tensors(out, sel_idx, sel_count)
+    rc = lib.topo_attn_decode_ragged(ctypes.byref(p), _ptr(pos), _ptr(q4), _ptr(k), _ptr(v), _ptr(out),
+                                     _ptr(sel_idx), _ptr(sel_count), _ptr(ws), ctypes.c_size_t(ws.numel()),
+                                     _stream(stream))
+    if rc != 0:
+        raise TopoError(rc, "topo_attn_decode_ragged")
+    return out, sel_idx, sel_count
+
+
+def topo_kv_append(k_cache, v_cache, k_new, v_new, pos, stream=None):
+    """Write one token's key and value rows per (batch, kv head) into the caches at row pos[b].
+    k_cache, v_cache: (B, Hkv, n_ctx, d); k_new, v_new: (B, Hkv, d) (or (B, Hkv, 1, d)), same
+    dtype; pos: int64 device tensor (B,)."""
+    lib = load_library()
+    B, Hkv, n_ctx, d = k_cache.shape
+    k3 = k_new.reshape(B, Hkv, d)
+    v3 = v_new.reshape(B, Hkv, d)
+    if v_cache.shape != k_cache.shape or k3.dtype != k_cache.dtype or v3.dtype != k_cache.dtype:
+        raise ValueError("caches and new rows disagree in shape or dtype")
+    _check_tensors(k_cache, v_cache, k3, v3)
+    _check_pos(pos, B)
+    p = TopoParams(B, Hkv, Hkv, d, n_ctx, 1, n_ctx - 1, 0, 0, 1, 1.0, _dtype_code(k_cache), 0)
+    rc = lib.topo_kv_append(ctypes.byref(p), _ptr(pos), _ptr(k3), _ptr(v3), _ptr(k_cache), _ptr(v_cache),
+                            _stream(stream))
+    if rc != 0:
+        raise TopoError(rc, "topo_kv_append")
 
 
 def topo_attn_decode_certified(q, k, v, W: int, topk: int, softmax_scale: float, dense_fallback: bool = False,

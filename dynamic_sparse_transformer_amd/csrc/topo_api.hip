@@ -37,6 +37,12 @@ topo::QueryGeom decode_geom(const topo_params_t* p) {
   return topo::make_geom(p->q_pos0, p->n_ctx, p->W, p->causal != 0);
 }
 
+// Sizes of a call with per-sequence positions: those of a query at the cache's last row, the
+// longest scan any position can need.
+topo::QueryGeom ragged_sizes_geom(const topo_params_t* p) { return topo::make_geom(p->n_ctx - 1, p->n_ctx, p->W, true); }
+
+bool aligned8(const void* p) { return ((uintptr_t)p & 7u) == 0; }
+
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // Workspace of the certified decode: the decode's, then (with the dense fallback) the dense
@@ -49,17 +55,19 @@ size_t certified_workspace_bytes(const topo_params_t* p) {
 
 int decode_like(const topo_params_t* p, const void* q, const void* k, const void* v, float* out,
                 int32_t* sel_idx, int32_t* sel_count, void* ws, size_t ws_bytes, hipStream_t stream,
-                bool softmax, hipEvent_t ev_begin = nullptr, hipEvent_t ev_end = nullptr, float* rho = nullptr) {
+                bool softmax, hipEvent_t ev_begin = nullptr, hipEvent_t ev_end = nullptr, float* rho = nullptr,
+                const int64_t* pos = nullptr) {
   int rc = check_params(p, true);
   if (rc) return rc;
   if (p->n_q != 1) return TOPO_EINVAL;
+  if (pos && (p->causal != 1 || rho || !aligned8(pos))) return TOPO_EINVAL;
   if (!rho && (p->flags & TOPO_FLAG_DENSE_FALLBACK)) return TOPO_EINVAL;
   if (rho && !aligned16(rho)) return TOPO_EINVAL;
   if (!q || !k || !aligned16(q) || !aligned16(k)) return TOPO_EINVAL;
   if (softmax && (!v || !out || !aligned16(v) || !aligned16(out))) return TOPO_EINVAL;
   if (!softmax && (!sel_idx || !sel_count)) return TOPO_EINVAL;
   if ((sel_idx && !aligned16(sel_idx)) || (sel_count && !aligned16(sel_count))) return TOPO_EINVAL;
-  const topo::QueryGeom g = decode_geom(p);
+  const topo::QueryGeom g = pos ? ragged_sizes_geom(p) : decode_geom(p);
   const size_t need = rho ? certified_workspace_bytes(p) : topo::decode_workspace_bytes(p->B, p->Hq, g, p->k);
   if (!ws || ws_bytes < need || !aligned16(ws)) return TOPO_EWORKSPACE;
 
@@ -82,6 +90,7 @@ int decode_like(const topo_params_t* p, const void* q, const void* k, const void
   L.flags = p->flags;
   L.n = p->n_ctx;
   L.geom = g;
+  L.pos = pos;
   L.scale = (double)p->softmax_scale;
   L.eps_coef = topo::fast_score_eps_coef(p->d);
   L.ev_scan_begin = ev_begin;
@@ -175,6 +184,9 @@ size_t topo_workspace_bytes(const topo_params_t* p, int op) {
     case TOPO_OP_DECODE_CERTIFIED:
       if (p->n_q != 1) return 0;
       return certified_workspace_bytes(p);
+    case TOPO_OP_DECODE_RAGGED:
+      if (p->n_q != 1 || p->causal != 1) return 0;
+      return topo::decode_workspace_bytes(p->B, p->Hq, ragged_sizes_geom(p), p->k);
     default:
       return 0;
   }
@@ -197,6 +209,29 @@ int topo_attn_decode_certified(const topo_params_t* p, const void* q, const void
                                hipStream_t stream) {
   if (!rho) return TOPO_EINVAL;
   return decode_like(p, q, k, v, out, sel_idx, sel_count, workspace, ws_bytes, stream, true, nullptr, nullptr, rho);
+}
+
+int topo_attn_decode_ragged(const topo_params_t* p, const int64_t* pos, const void* q, const void* k, const void* v,
+                            float* out, int32_t* sel_idx, int32_t* sel_count, void* workspace, size_t ws_bytes,
+                            hipStream_t stream) {
+  if (!pos) return TOPO_EINVAL;
+  return decode_like(p, q, k, v, out, sel_idx, sel_count, workspace, ws_bytes, stream, true, nullptr, nullptr, nullptr,
+                     pos);
+}
+
+int topo_kv_append(const topo_params_t* p, const int64_t* pos, const void* k_new, const void* v_new, void* k_cache,
+                   void* v_cache, hipStream_t stream) {
+  int rc = check_params(p, false);
+  if (rc) return rc;
+  if (!pos || !aligned8(pos)) return TOPO_EINVAL;
+  if (!k_new || !v_new || !k_cache || !v_cache || !aligned16(k_new) || !aligned16(v_new) || !aligned16(k_cache) ||
+      !aligned16(v_cache))
+    return TOPO_EINVAL;
+  const int32_t row_bytes = p->d * (p->dtype == TOPO_BF16 ? 2 : 4);
+  return topo::launch_kv_append(k_new, v_new, k_cache, v_cache, pos, p->B, p->Hkv, p->n_ctx, row_bytes, stream) ==
+                 hipSuccess
+             ? TOPO_OK
+             : TOPO_EHIP;
 }
 
 int topo_attn_prefill(const topo_params_t* p, const void* q, const void* k, const void* v, float* out,

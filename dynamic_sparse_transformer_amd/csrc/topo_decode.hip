@@ -157,9 +157,16 @@ struct KscanArgs {
   uint2* surv;
   int64_t n, nblk, slot;
   int64_t p, w_lo, vis_hi, scan_hi;
-  int32_t Hq, Hkv, G, topk, runs;
+  const int64_t* pos;  // may be null: causal query position of each batch element
+  int32_t Hq, Hkv, G, W, topk, runs;
   float eps_coef;
 };
+
+// Geometry of batch element b's query from its position pos[b] (clamped into the cache; causal).
+__device__ __forceinline__ QueryGeom ragged_geom(const int64_t* pos, int b, int64_t n, int32_t W) {
+  const int64_t p = pos[b];
+  return make_geom(p < 0 ? 0 : (p > n - 1 ? n - 1 : p), n, W, true);
+}
 
 // Loads of one 64-key tile. The 64 lanes form 8 groups of 8; group r handles keys 8i + r of the
 // tile (i = 0..7) and lane s of a group holds 16-byte chunks c*8 + s (c < CPL) of each of them:
@@ -178,7 +185,7 @@ __device__ __forceinline__ void kscan_load(uint4 (&buf)[8][RB / 128], const unsi
   }
 }
 
-template <int RB, int GT, bool BF16>
+template <int RB, int GT, bool BF16, bool RAGGED>
 __global__ __launch_bounds__(256, TOPO_KS_MIN_BLOCKS) void kscan_kernel(KscanArgs a) {
   constexpr int L = 8;          // lanes per key row
   constexpr int CPL = RB / 128; // 16-byte chunks of a row per lane
@@ -192,6 +199,24 @@ __global__ __launch_bounds__(256, TOPO_KS_MIN_BLOCKS) void kscan_kernel(KscanArg
   const int slice0 = blockIdx.z * GT;
   const int h0 = g * a.G + slice0;
   const int nh = min(GT, a.G - slice0);
+  // the query's geometry: the call's, or (RAGGED) that of this sequence's position
+  int64_t q_p = a.p, q_wlo = a.w_lo, q_vis = a.vis_hi, q_scan = a.scan_hi;
+  if constexpr (RAGGED) {
+    // the grid covers the longest scan; blocks past this sequence's candidates leave empty lists
+    const QueryGeom gq = ragged_geom(a.pos, b, a.n, a.W);
+    q_p = gq.p;
+    q_wlo = gq.w_lo;
+    q_vis = gq.vis_hi;
+    q_scan = gq.scan_hi;
+    if ((int64_t)blockIdx.x * KS_KEYS_PER_RUN * a.runs > q_scan) {
+      if (tid < nh) {
+        const size_t bslot = ((size_t)b * a.Hq + h0 + tid) * (size_t)a.nblk + blockIdx.x;
+        a.blk_cnt[bslot] = 0u;
+        a.blk_eps[bslot] = 0.f;
+      }
+      return;
+    }
+  }
 
   // This lane's chunks of every query of the slice, and |q_h| (float64 sum over the 8 lanes).
   uint4 qv[GT][CPL];
@@ -226,7 +251,7 @@ __global__ __launch_bounds__(256, TOPO_KS_MIN_BLOCKS) void kscan_kernel(KscanArg
     return blk_key0 + (int64_t)(r * KS_WAVES + wave) * KS_KEYS_PER_WAVE;
   };
   const unsigned char* kb = a.k + (size_t)grp * (size_t)a.n * RB;
-  const int64_t last_row = a.scan_hi;
+  const int64_t last_row = q_scan;
   const int64_t my_off = 8 * s + (lane >> 3);  // key of this lane within a tile after the reduction
 
   float sc[GT][KS_IT];
@@ -278,7 +303,7 @@ __global__ __launch_bounds__(256, TOPO_KS_MIN_BLOCKS) void kscan_kernel(KscanArg
       sc[h][KS_IT - 1] = Q1[0][0];
     }
     const int64_t j = row0 + my_off;
-    const bool valid = j >= 1 && j <= a.vis_hi && (j < a.w_lo || j > a.p);
+    const bool valid = j >= 1 && j <= q_vis && (j < q_wlo || j > q_p);
     vmask = (vmask >> 1) | ((valid ? 1u : 0u) << (KS_IT - 1));
   };
 
@@ -631,6 +656,7 @@ struct FinishArgs {
   const uint2* surv;
   int64_t n, nblk, slot;
   int64_t p, w_lo, vis_hi, scan_hi, n_cand;
+  const int64_t* pos;  // may be null: causal query position of each batch element
   int32_t Hq, Hkv, G, W, topk, set_cap, flags;
   double scale;
   float eps_coef;
@@ -842,13 +868,22 @@ __device__ int stage_survivors(FinishSmem* sm, const FinishArgs& a, int bh, uint
 }
 
 template <int D, bool BF16>
-__global__ __launch_bounds__(FIN_THREADS) void decode_finish_kernel(FinishArgs a) {
+__global__ __launch_bounds__(FIN_THREADS) void decode_finish_kernel(FinishArgs args) {
   constexpr int RB = D * (BF16 ? 2 : 4);
   extern __shared__ __align__(16) unsigned char smem_raw[];
   FinishSmem* sm = (FinishSmem*)smem_raw;
   const int tid = threadIdx.x;
   const int bh = blockIdx.x;
+  FinishArgs a = args;
   const int b = bh / a.Hq, h = bh - b * a.Hq, g = h / a.G;
+  if (a.pos) {
+    const QueryGeom gq = ragged_geom(a.pos, b, a.n, a.W);
+    a.p = gq.p;
+    a.w_lo = gq.w_lo;
+    a.vis_hi = gq.vis_hi;
+    a.scan_hi = gq.scan_hi;
+    a.n_cand = gq.n_cand;
+  }
   const unsigned char* kb = a.k + ((size_t)b * a.Hkv + g) * (size_t)a.n * RB;
   const unsigned char* vb = a.v + ((size_t)b * a.Hkv + g) * (size_t)a.n * RB;
   const unsigned char* qrow = a.q + (size_t)bh * RB;
@@ -1136,7 +1171,10 @@ __global__ __launch_bounds__(FIN_THREADS) void decode_finish_kernel(FinishArgs a
 // ---------------------------------------------------------------------------------------------
 template <int RB, int GT, bool BF16>
 static hipError_t launch_kscan_t(const KscanArgs& ka, dim3 grid, hipStream_t s) {
-  hipLaunchKernelGGL((kscan_kernel<RB, GT, BF16>), grid, dim3(256), 0, s, ka);
+  if (ka.pos)
+    hipLaunchKernelGGL((kscan_kernel<RB, GT, BF16, true>), grid, dim3(256), 0, s, ka);
+  else
+    hipLaunchKernelGGL((kscan_kernel<RB, GT, BF16, false>), grid, dim3(256), 0, s, ka);
   return hipGetLastError();
 }
 
@@ -1189,6 +1227,8 @@ hipError_t launch_decode(const DecodeLaunch& L, hipStream_t stream) {
     ka.w_lo = g.w_lo;
     ka.vis_hi = g.vis_hi;
     ka.scan_hi = g.scan_hi;
+    ka.pos = L.pos;
+    ka.W = L.W;
     ka.Hq = L.Hq;
     ka.Hkv = L.Hkv;
     ka.G = L.G;
@@ -1254,6 +1294,7 @@ hipError_t launch_decode(const DecodeLaunch& L, hipStream_t stream) {
   fa.vis_hi = g.vis_hi;
   fa.scan_hi = g.scan_hi;
   fa.n_cand = g.n_cand;
+  fa.pos = L.pos;
   fa.Hq = L.Hq;
   fa.Hkv = L.Hkv;
   fa.G = L.G;
@@ -1267,6 +1308,31 @@ hipError_t launch_decode(const DecodeLaunch& L, hipStream_t stream) {
     return L.d == 128 ? launch_finish_t<128, true>(fa, nbh, stream) : launch_finish_t<64, true>(fa, nbh, stream);
   }
   return L.d == 128 ? launch_finish_t<128, false>(fa, nbh, stream) : launch_finish_t<64, false>(fa, nbh, stream);
+}
+
+// ---------------------------------------------------------------------------------------------
+// KV append: block (b, g) copies the new key and value rows of batch element b, kv head g
+// (row_bytes each, in 16-byte chunks) to row pos[b] of the caches; a position outside
+// [0, n - 1] writes nothing.
+__global__ __launch_bounds__(64) void kv_append_kernel(const uint4* k_new, const uint4* v_new, unsigned char* k_cache,
+                                                       unsigned char* v_cache, const int64_t* pos, int32_t Hkv,
+                                                       int64_t n, int32_t row_bytes) {
+  const int grp = blockIdx.x, b = grp / Hkv;
+  const int64_t p = pos[b];
+  if (p < 0 || p >= n) return;
+  const int nch = row_bytes / 16;
+  const size_t dst = ((size_t)grp * (size_t)n + (size_t)p) * (size_t)row_bytes;
+  for (int c = threadIdx.x; c < nch; c += 64) {
+    *(uint4*)(k_cache + dst + (size_t)c * 16) = k_new[(size_t)grp * nch + c];
+    *(uint4*)(v_cache + dst + (size_t)c * 16) = v_new[(size_t)grp * nch + c];
+  }
+}
+
+hipError_t launch_kv_append(const void* k_new, const void* v_new, void* k_cache, void* v_cache, const int64_t* pos,
+                            int32_t B, int32_t Hkv, int64_t n, int32_t row_bytes, hipStream_t stream) {
+  hipLaunchKernelGGL(kv_append_kernel, dim3((unsigned)(B * Hkv)), dim3(64), 0, stream, (const uint4*)k_new,
+                     (const uint4*)v_new, (unsigned char*)k_cache, (unsigned char*)v_cache, pos, Hkv, n, row_bytes);
+  return hipGetLastError();
 }
 
 }  // namespace topo

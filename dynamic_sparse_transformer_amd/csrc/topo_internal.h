@@ -41,7 +41,7 @@ struct QueryGeom {
   int64_t n_cand;   // number of candidates
 };
 
-inline QueryGeom make_geom(int64_t p, int64_t n, int32_t W, bool causal) {
+__host__ __device__ inline QueryGeom make_geom(int64_t p, int64_t n, int32_t W, bool causal) {
   QueryGeom g;
   g.p = p;
   g.w_lo = p - (int64_t)W + 1 > 0 ? p - (int64_t)W + 1 : 0;
@@ -77,7 +77,8 @@ struct DecodeLaunch {
   int32_t runs;  // runs of KS_KEYS_PER_RUN keys per key-scan block
   int32_t B, Hq, Hkv, G, d, W, topk, bf16, flags;
   int64_t n;
-  QueryGeom geom;
+  QueryGeom geom;     // the query's geometry; with pos, the geometry of position n - 1 (sizes)
+  const int64_t* pos;  // may be null: per batch element b, the causal query position pos[b]
   double scale;
   float eps_coef;
   hipEvent_t ev_scan_begin;  // optional: recorded around the key-scan launch
@@ -88,6 +89,9 @@ size_t decode_workspace_bytes(int32_t B, int32_t Hq, const QueryGeom& g, int32_t
 // Carve the workspace into the HeadState array and the survivor lists.
 void decode_carve(void* ws, int32_t B, int32_t Hq, const QueryGeom& g, int32_t k, DecodeLaunch& L);
 hipError_t launch_decode(const DecodeLaunch& L, hipStream_t stream);
+// New key and value rows of one token per (batch, kv head) into the caches at row pos[b].
+hipError_t launch_kv_append(const void* k_new, const void* v_new, void* k_cache, void* v_cache, const int64_t* pos,
+                            int32_t B, int32_t Hkv, int64_t n, int32_t row_bytes, hipStream_t stream);
 
 // Float32 error-bound coefficient of the fast scores: |s_fast - s| <= coef * |q|_2 * |k|_2.
 float fast_score_eps_coef(int d);

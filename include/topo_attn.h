@@ -71,6 +71,7 @@ extern "C" {
 #define TOPO_OP_DENSE   3
 #define TOPO_OP_DECODE_CERTIFIED 4  /* topo_attn_decode_certified (includes the dense fallback's
                                        scratch when TOPO_FLAG_DENSE_FALLBACK is set)            */
+#define TOPO_OP_DECODE_RAGGED 5     /* topo_attn_decode_ragged (sized for the longest position) */
 
 /* Largest condensate set (1 + W + k) a call may ask for. */
 #define TOPO_MAX_SET 4096
@@ -136,6 +137,31 @@ int topo_attn_decode_timed(const topo_params_t* p, const void* q, const void* k,
 int topo_attn_decode_certified(const topo_params_t* p, const void* q, const void* k, const void* v,
                                float* out, int32_t* sel_idx, int32_t* sel_count, float* rho,
                                void* workspace, size_t ws_bytes, hipStream_t stream);
+
+/* Decode of a batch whose sequences have different lengths, the per-token step of a generation
+ * loop (the pages re-select the set at every generated token: zh technical summary §3). pos is a
+ * device array of B int64 positions, 8-byte aligned: the query of batch element b sits at
+ * position pos[b] of its own cache and sees keys 0 .. pos[b] (the call is causal; p->causal must
+ * be 1). The caches keep their [B, Hkv, n_ctx, d] layout; rows past a sequence's position are not
+ * read by its query. p->q_pos0 is not used for the positions (it is still validated). Each query's
+ * set and output are those of topo_attn_decode with q_pos0 = pos[b] on that sequence. A position
+ * outside [0, n_ctx - 1] is clamped into it (a caller error; no memory outside the caches is
+ * read). Because the positions live in device memory, a captured HIP graph of this call serves
+ * every step of a loop that advances them on the device. Workspace:
+ * topo_workspace_bytes(p, TOPO_OP_DECODE_RAGGED). Errors as topo_attn_decode, and TOPO_EINVAL if
+ * pos is NULL or misaligned or p->causal != 1. */
+int topo_attn_decode_ragged(const topo_params_t* p, const int64_t* pos, const void* q, const void* k, const void* v,
+                            float* out, int32_t* sel_idx, int32_t* sel_count,
+                            void* workspace, size_t ws_bytes, hipStream_t stream);
+
+/* KV-cache append, the step before a decode: for every (b, kv head g), the new key and value rows
+ * k_new[b, g, :] and v_new[b, g, :] (layout [B, Hkv, d], the call's dtype) are copied to row
+ * pos[b] of k_cache and v_cache ([B, Hkv, n_ctx, d]). pos as in topo_attn_decode_ragged (device,
+ * B int64); a position outside [0, n_ctx - 1] writes nothing for that batch element. Uses B, Hkv,
+ * d, n_ctx and dtype of p; no workspace. Asynchronous on stream; TOPO_EINVAL on a NULL or
+ * misaligned pointer. */
+int topo_kv_append(const topo_params_t* p, const int64_t* pos, const void* k_new, const void* v_new,
+                   void* k_cache, void* v_cache, hipStream_t stream);
 
 /* Topological attention of n_q consecutive queries per (batch, query head), query i at position
  * q_pos0 + i (a whole causal prompt is q_pos0 = 0, n_q = n_ctx). Same outputs as decode, one row

@@ -115,3 +115,27 @@ def test_certified_decode_rejects_bad_arguments_on_host():
     assert lib.topo_attn_prefill(ctypes.byref(pf), a, a, a, a, None, None, a, 1 << 40, None) == -1
     assert lib.topo_attn_dense(ctypes.byref(pf), a, a, a, a, a, 1 << 40, None) == -1
     assert lib.topo_workspace_bytes(ctypes.byref(_p(n_q=2)), 4) == 0
+
+
+def test_ragged_decode_and_kv_append_reject_bad_arguments_on_host():
+    lib = topo.load_library()
+    a = ctypes.c_void_p(1 << 40)  # never dereferenced: validation fails first
+    mis8 = ctypes.c_void_p((1 << 40) + 4)
+    p = _p()
+    need = lib.topo_workspace_bytes(ctypes.byref(p), 5)
+    # sized for a query at the cache's last row, whatever q_pos0 says
+    assert need == lib.topo_workspace_bytes(ctypes.byref(_p(q_pos0=1000)), 5) == lib.topo_workspace_bytes(
+        ctypes.byref(p), 0) > 0
+    assert lib.topo_workspace_bytes(ctypes.byref(_p(causal=0)), 5) == 0
+    assert lib.topo_workspace_bytes(ctypes.byref(_p(n_q=2)), 5) == 0
+    # positions missing or misaligned, non-causal call, small workspace
+    assert lib.topo_attn_decode_ragged(ctypes.byref(p), None, a, a, a, a, None, None, a, need, None) == -1
+    assert lib.topo_attn_decode_ragged(ctypes.byref(p), mis8, a, a, a, a, None, None, a, need, None) == -1
+    assert lib.topo_attn_decode_ragged(ctypes.byref(_p(causal=0)), a, a, a, a, a, None, None, a, need, None) == -1
+    assert lib.topo_attn_decode_ragged(ctypes.byref(p), a, a, a, a, a, None, None, a, need - 1, None) == -3
+    # append: every pointer required and aligned; shape checks as the other calls
+    assert lib.topo_kv_append(ctypes.byref(p), None, a, a, a, a, None) == -1
+    assert lib.topo_kv_append(ctypes.byref(p), mis8, a, a, a, a, None) == -1
+    assert lib.topo_kv_append(ctypes.byref(p), a, None, a, a, a, None) == -1
+    assert lib.topo_kv_append(ctypes.byref(p), a, a, a, ctypes.c_void_p((1 << 40) + 8), a, None) == -1
+    assert lib.topo_kv_append(ctypes.byref(_p(d=96)), a, a, a, a, a, None) == -2
