@@ -237,6 +237,44 @@ def run_prefill_bench(cfg: int, steps: int, warmup: int):
     }
 
 
+def run_layers_bench(n_layers: int, steps: int, warmup: int):
+    """A decode step through a stack of attention layers (topo_attn_decode_layers): the GQA decode
+    shape (batch 4, 32 query heads over 8 kv heads, d=128, bf16) at a 32K-token context, one KV
+    cache per layer, the pillar / layer-adaptive plan of pillar_schedule (dense layers about one
+    in sixteen; W from 512 to 128 and k from 64 to 32 with depth). Seeded N(0,1) inputs generated
+    on the device. Reports sequence-tokens per second of the whole stack."""
+    import torch
+
+    import dynamic_sparse_transformer_amd as topo
+
+    B, Hq, Hkv, d, n = 4, 32, 8, 128, 32768
+    plan = topo.pillar_schedule(n_layers, 512, 64, 128, 32)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(6001)
+    layers = []
+    for _ in range(n_layers):
+        q = torch.randn((B, Hq, 1, d), generator=gen, device="cuda").to(torch.bfloat16)
+        k = torch.randn((B, Hkv, n, d), generator=gen, device="cuda").to(torch.bfloat16)
+        v = torch.randn((B, Hkv, n, d), generator=gen, device="cuda").to(torch.bfloat16)
+        layers.append((q, k, v))
+    scale = 1.0 / d ** 0.5
+    for _ in range(warmup):
+        topo.topo_attn_decode_layers(layers, plan, scale)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        topo.topo_attn_decode_layers(layers, plan, scale)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    del layers
+    torch.cuda.empty_cache()
+    return {"workload": f"gqa-decode-32k-{n_layers}-layer-stack", "value": B / (ms / 1e3),
+            "unit": "sequence-tokens/s", "ms_per_step": ms, "layers": n_layers,
+            "pillar_layers": [i for i, (p, _, _) in enumerate(plan) if p],
+            "config": {"batch": B, "q_heads": Hq, "kv_heads": Hkv, "head_dim": d, "context": n,
+                       "W_first": 512, "k_first": 64, "W_last": 128, "k_last": 32}}
+
+
 def cpu_baseline(res, heads: int):
     """The CPU oracle, as it stands, on a bounded sample of the same workload: the first `heads`
     query heads of batch 0. Also checks the GPU sets of those heads against it."""
@@ -272,6 +310,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--prefill", type=int, default=3,
                     help="prefill config reported alongside (default 3: causal 8K prompt, 8 heads); 0 = none")
+    ap.add_argument("--layers", type=int, default=32,
+                    help="layers of the stacked decode step reported alongside (0: skip)")
     ap.add_argument("--calibrate", action="store_true",
                     help="also run kernels of known traffic (for scaling hardware byte counters): a 2 GiB "
                          "read-only probe and a 256 MiB device copy")
@@ -309,6 +349,10 @@ def main():
     if args.prefill:
         log(f"[bench] prefill config {args.prefill}")
         also.append(run_prefill_bench(args.prefill, max(3, args.steps // 5), min(args.warmup, 2)))
+
+    if args.layers:
+        log(f"[bench] {args.layers}-layer stack")
+        also.append(run_layers_bench(args.layers, max(3, args.steps // 5), min(args.warmup, 2)))
 
     if args.calibrate:
         # Known traffic: the probe reads every byte of a 2 GiB buffer once; the copy reads and

@@ -19,7 +19,7 @@ __all__ = [
     "TopoError", "load_library", "library_path", "topo_workspace_bytes", "topo_attn_decode",
     "topo_attn_prefill", "topo_select", "topo_attn_dense", "topo_bw_probe", "topo_strerror",
     "topo_attn_decode_timed", "topo_attn_prefill_timed", "topo_attn_decode_certified",
-    "topo_attn_decode_ragged", "topo_kv_append",
+    "topo_attn_decode_ragged", "topo_kv_append", "topo_attn_decode_layers", "pillar_schedule",
     "TOPO_FLAG_EXACT_SELECT", "TOPO_FLAG_DENSE_FALLBACK", "TOPO_CERT_RHO", "TOPO_MAX_SET", "EXPORTS",
 ]
 
@@ -34,8 +34,15 @@ TOPO_FLAG_DENSE_FALLBACK = 2
 TOPO_CERT_RHO = 2.0 ** -24
 TOPO_MAX_SET = 4096
 EXPORTS = ("topo_workspace_bytes", "topo_attn_decode", "topo_attn_decode_timed", "topo_attn_decode_certified",
-           "topo_attn_decode_ragged", "topo_kv_append", "topo_attn_prefill", "topo_attn_prefill_timed",
-           "topo_select", "topo_attn_dense", "topo_bw_probe", "topo_strerror")
+           "topo_attn_decode_ragged", "topo_kv_append", "topo_attn_decode_layers", "topo_layers_workspace_bytes",
+           "topo_attn_prefill", "topo_attn_prefill_timed", "topo_select", "topo_attn_dense", "topo_bw_probe",
+           "topo_strerror")
+
+
+class TopoLayer(ctypes.Structure):
+    _fields_ = [("q", ctypes.c_void_p), ("k_cache", ctypes.c_void_p), ("v_cache", ctypes.c_void_p),
+                ("out", ctypes.c_void_p), ("sel_idx", ctypes.c_void_p), ("sel_count", ctypes.c_void_p),
+                ("W", ctypes.c_int32), ("k", ctypes.c_int32), ("pillar", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
 class TopoError(RuntimeError):
@@ -82,6 +89,11 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.topo_attn_decode_ragged.restype = i32
     lib.topo_kv_append.argtypes = [P, vp, vp, vp, vp, vp, vp]
     lib.topo_kv_append.restype = i32
+    LP = ctypes.POINTER(TopoLayer)
+    lib.topo_layers_workspace_bytes.argtypes = [P, LP, i32]
+    lib.topo_layers_workspace_bytes.restype = sz
+    lib.topo_attn_decode_layers.argtypes = [P, LP, i32, vp, sz, vp]
+    lib.topo_attn_decode_layers.restype = i32
     lib.topo_select.argtypes = [P, vp, vp, vp, vp, vp, sz, vp]
     lib.topo_select.restype = i32
     lib.topo_attn_dense.argtypes = [P, vp, vp, vp, vp, vp, sz, vp]
@@ -293,6 +305,73 @@ def topo_kv_append(k_cache, v_cache, k_new, v_new, pos, stream=None):
                             _stream(stream))
     if rc != 0:
         raise TopoError(rc, "topo_kv_append")
+
+
+def pillar_schedule(n_layers: int, W_first: int, k_first: int, W_last: int | None = None, k_last: int | None = None):
+    """Per-layer plan of a decode step through n_layers attention layers: a list of
+    (pillar, W, k). About one layer in sixteen is a pillar (dense) layer: max(1, round(L / 16))
+    of them, evenly spaced from layer 0. The other layers take (W, k) interpolated linearly from
+    (W_first, k_first) at layer 0 to (W_last, k_last) at the last layer, rounded: wider windows
+    early, leaner sets late (zh page, technical summary §3)."""
+    if n_layers < 1:
+        raise ValueError("n_layers >= 1")
+    W_last = W_first if W_last is None else W_last
+    k_last = k_first if k_last is None else k_last
+    n_pillar = max(1, int(round(n_layers / 16)))
+    pillars = {i * n_layers // n_pillar for i in range(n_pillar)}
+    plan = []
+    for layer in range(n_layers):
+        t = layer / (n_layers - 1) if n_layers > 1 else 0.0
+        W = int(round(W_first + (W_last - W_first) * t))
+        kk = int(round(k_first + (k_last - k_first) * t))
+        plan.append((layer in pillars, W, kk))
+    return plan
+
+
+def topo_attn_decode_layers(layers, plan, softmax_scale: float, q_pos0: int | None = None, flags: int = 0,
+                            want_sets: bool = True, workspace=None, stream=None):
+    """A decode step through a stack of attention layers, launched by one library call.
+    layers: sequence of (q, k, v) per layer, q (B, Hq, d) or (B, Hq, 1, d), k and v (B, Hkv, n, d),
+    all layers of one shape and dtype. plan: per layer (pillar, W, k), e.g. from pillar_schedule.
+    Returns a list of (out f32 (B,Hq,1,d), sel_idx or None, sel_count or None) per layer (no sets
+    for pillar layers)."""
+    torch = _torch()
+    lib = load_library()
+    if len(layers) != len(plan) or not layers:
+        raise ValueError("one plan entry per layer")
+    q0 = layers[0][0]
+    q04 = q0 if q0.dim() == 4 else q0.unsqueeze(2)
+    k0 = layers[0][1]
+    if q_pos0 is None:
+        q_pos0 = k0.shape[2] - 1
+    p = _params(q04, k0, 0, 0, softmax_scale, True, q_pos0, flags)
+    B, Hq, _, d = q04.shape
+    arr = (TopoLayer * len(layers))()
+    results, keep = [], []
+    for i, ((q, k, v), (pillar, W, kk)) in enumerate(zip(layers, plan)):
+        q4 = q if q.dim() == 4 else q.unsqueeze(2)
+        if q4.shape != q04.shape or k.shape != k0.shape or v.shape != k0.shape or q4.dtype != q04.dtype:
+            raise ValueError(f"layer {i}: shapes or dtype differ from layer 0")
+        _check_tensors(q4, k, v)
+        out = torch.empty((B, Hq, 1, d), dtype=torch.float32, device=q4.device)
+        sel = cnt = None
+        if want_sets and not pillar:
+            sel = torch.empty((B, Hq, 1, 1 + int(W) + int(kk)), dtype=torch.int32, device=q4.device)
+            cnt = torch.empty((B, Hq, 1), dtype=torch.int32, device=q4.device)
+        arr[i] = TopoLayer(q4.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                           sel.data_ptr() if sel is not None else None, cnt.data_ptr() if cnt is not None else None,
+                           int(W), int(kk), int(bool(pillar)), 0)
+        keep.append(q4)
+        results.append((out, sel, cnt))
+    nbytes = lib.topo_layers_workspace_bytes(ctypes.byref(p), arr, len(layers))
+    if nbytes == 0:
+        raise TopoError(-1, "topo_attn_decode_layers: parameters rejected")
+    ws = _workspace(nbytes, q04.device, workspace)
+    rc = lib.topo_attn_decode_layers(ctypes.byref(p), arr, len(layers), _ptr(ws), ctypes.c_size_t(ws.numel()),
+                                     _stream(stream))
+    if rc != 0:
+        raise TopoError(rc, "topo_attn_decode_layers")
+    return results
 
 
 def topo_attn_decode_certified(q, k, v, W: int, topk: int, softmax_scale: float, dense_fallback: bool = False,

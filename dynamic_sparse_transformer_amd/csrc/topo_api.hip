@@ -284,6 +284,55 @@ int topo_attn_dense(const topo_params_t* p, const void* q, const void* k, const 
   return topo::launch_dense(L, stream) == hipSuccess ? TOPO_OK : TOPO_EHIP;
 }
 
+size_t topo_layers_workspace_bytes(const topo_params_t* p, const topo_layer_t* layers, int32_t n_layers) {
+  if (!p || !layers || n_layers < 1) return 0;
+  size_t need = 16;
+  for (int32_t i = 0; i < n_layers; ++i) {
+    topo_params_t pl = *p;
+    pl.W = layers[i].W;
+    pl.k = layers[i].k;
+    const size_t b = layers[i].pillar ? topo_workspace_bytes(&pl, TOPO_OP_DENSE) : topo_workspace_bytes(&pl, TOPO_OP_DECODE);
+    if (b == 0 || layers[i].reserved != 0 || (layers[i].pillar != 0 && layers[i].pillar != 1)) return 0;
+    if (b > need) need = b;
+  }
+  return need;
+}
+
+int topo_attn_decode_layers(const topo_params_t* p, const topo_layer_t* layers, int32_t n_layers, void* workspace,
+                            size_t ws_bytes, hipStream_t stream) {
+  if (!p || !layers || n_layers < 1) return TOPO_EINVAL;
+  int rc = check_params(p, false);
+  if (rc) return rc;
+  if (p->n_q != 1 || (p->flags & TOPO_FLAG_DENSE_FALLBACK)) return TOPO_EINVAL;
+  // every layer checked before the first launch
+  for (int32_t i = 0; i < n_layers; ++i) {
+    const topo_layer_t& L = layers[i];
+    if (L.reserved != 0 || (L.pillar != 0 && L.pillar != 1)) return TOPO_EINVAL;
+    topo_params_t pl = *p;
+    pl.W = L.W;
+    pl.k = L.k;
+    if (!L.pillar && (rc = check_params(&pl, true)) != TOPO_OK) return rc;
+    if (!L.q || !L.k_cache || !L.v_cache || !L.out || !aligned16(L.q) || !aligned16(L.k_cache) ||
+        !aligned16(L.v_cache) || !aligned16(L.out))
+      return TOPO_EINVAL;
+    if ((L.sel_idx && !aligned16(L.sel_idx)) || (L.sel_count && !aligned16(L.sel_count))) return TOPO_EINVAL;
+  }
+  const size_t need = topo_layers_workspace_bytes(p, layers, n_layers);
+  if (need == 0) return TOPO_EINVAL;
+  if (!workspace || ws_bytes < need || !aligned16(workspace)) return TOPO_EWORKSPACE;
+  for (int32_t i = 0; i < n_layers; ++i) {
+    const topo_layer_t& L = layers[i];
+    topo_params_t pl = *p;
+    pl.W = L.W;
+    pl.k = L.k;
+    rc = L.pillar ? topo_attn_dense(&pl, L.q, L.k_cache, L.v_cache, L.out, workspace, ws_bytes, stream)
+                  : topo_attn_decode(&pl, L.q, L.k_cache, L.v_cache, L.out, L.sel_idx, L.sel_count, workspace,
+                                     ws_bytes, stream);
+    if (rc != TOPO_OK) return rc;
+  }
+  return TOPO_OK;
+}
+
 int topo_bw_probe(const void* buf, size_t bytes, uint32_t* sink, hipStream_t stream) {
   if (!buf || !sink || !aligned16(buf) || bytes == 0 || (bytes & 15u)) return TOPO_EINVAL;
   return topo::launch_bw_probe(buf, bytes, sink, stream) == hipSuccess ? TOPO_OK : TOPO_EHIP;

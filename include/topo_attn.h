@@ -193,6 +193,35 @@ int topo_select(const topo_params_t* p, const void* q, const void* k,
 int topo_attn_dense(const topo_params_t* p, const void* q, const void* k, const void* v,
                     float* out, void* workspace, size_t ws_bytes, hipStream_t stream);
 
+/* One attention layer of a decode step through a model's stack of layers. The pages keep a few
+ * layers fully dense, the "pillar" layers (about one layer in sixteen), and size the condensate
+ * set per layer: wider windows in early layers, leaner sets in later ones (zh technical summary
+ * §3). Pointers are device pointers; the struct itself lives in host memory. */
+typedef struct {
+    const void* q;        /* [B, Hq, d] the layer's queries (dtype of the call)                  */
+    const void* k_cache;  /* [B, Hkv, n_ctx, d] the layer's key cache                            */
+    const void* v_cache;  /* [B, Hkv, n_ctx, d] the layer's value cache                          */
+    float*      out;      /* [B, Hq, d] float32                                                  */
+    int32_t*    sel_idx;  /* [B, Hq, 1 + W + k] or NULL; not written for a pillar layer          */
+    int32_t*    sel_count;/* [B, Hq] or NULL; not written for a pillar layer                     */
+    int32_t     W;        /* the layer's window (>= 0; unused by a pillar layer)                 */
+    int32_t     k;        /* the layer's top-k (>= 0; unused by a pillar layer)                  */
+    int32_t     pillar;   /* 1: dense attention over every visible key (topo_attn_dense); 0: the
+                             condensate set (topo_attn_decode)                                   */
+    int32_t     reserved; /* 0                                                                   */
+} topo_layer_t;
+
+/* Workspace bytes for topo_attn_decode_layers: the largest any of the layers needs (the layers
+ * run one after the other on the stream and share it). 0 if a layer's parameters are invalid. */
+size_t topo_layers_workspace_bytes(const topo_params_t* p, const topo_layer_t* layers, int32_t n_layers);
+
+/* A decode step through n_layers attention layers (n_layers >= 1): layer i runs topo_attn_decode
+ * with p's shapes, position, scale, dtype and flags and the layer's W and k, or topo_attn_dense
+ * when it is a pillar layer, in order on `stream`. Every layer is validated before anything is
+ * launched (errors as those calls; TOPO_EINVAL if layers is NULL, n_layers < 1 or reserved != 0). */
+int topo_attn_decode_layers(const topo_params_t* p, const topo_layer_t* layers, int32_t n_layers,
+                            void* workspace, size_t ws_bytes, hipStream_t stream);
+
 /* Measurement helper, not part of the method: streams `bytes` (a multiple of 16) from `buf`
  * once with the same load path as the decode key scan and reduces them into `sink`
  * (one uint32, device memory), so the achievable read bandwidth can be timed next to it. */
