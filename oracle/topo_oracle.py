@@ -30,6 +30,10 @@ Readings where the pages leave the arithmetic open (each is a choice, not someth
     w_j = exp(z_j - max z). Z = sum of w_j and N = sum of w_j * v_j, both summed in ascending j;
     the output is N / Z rounded once to float32.
   * GQA: query head h reads kv head floor(h / G), G = Hq / Hkv, and selects its own set.
+  * GQA, shared selection (a variant; the pages name GQA without detail): one set per (batch,
+    kv head) for all G query heads of the group. A key's group score is the largest score any of
+    the group's heads gives it; the top-k ranks group scores as above; each head then takes the
+    softmax of its own scores over the shared set.
   * Non-causal: every key 0..n-1 is visible; the window is still the W positions ending at p.
 """
 from __future__ import annotations
@@ -40,6 +44,7 @@ __all__ = [
     "canonical_scores", "condensate_set", "softmax_weighted_v", "attend", "dense_attend",
     "omitted_mass", "certified_components", "ulp_distance_f32", "topo_attn_decode",
     "topo_attn_rows", "dense_decode", "certificate_bound", "CERT_RHO", "KEY_BLOCK",
+    "group_scores", "topo_attn_decode_group",
 ]
 
 # A query is certified when its bound on the omitted softmax mass is below the float32 rounding
@@ -240,6 +245,45 @@ def topo_attn_decode(q, K, V, W: int, k: int, scale: float, causal: bool = True,
         out[b, h] = o
         sel[b, h, :C.size] = C
         cnt[b, h] = C.size
+    return out, sel, cnt
+
+
+def group_scores(s_heads: np.ndarray) -> np.ndarray:
+    """Group score of every key for a shared selection: the largest of the group's per-head
+    scores (s_heads: (G, n) float64)."""
+    return np.max(np.asarray(s_heads, dtype=np.float64), axis=0)
+
+
+def topo_attn_decode_group(q, K, V, W: int, k: int, scale: float, causal: bool = True, q_pos=None,
+                           groups=None):
+    """Topological attention with one condensate set per (batch, kv head), shared by the group's
+    query heads: the set of the group scores (largest per-head score of each key), then each
+    head's softmax of its own scores over it (the GQA shared-selection reading above).
+
+    q: (B, Hq, d) or (B, Hq, 1, d); K, V: (B, Hkv, n, d). groups: optional list of (b, g).
+    Returns (out float32 (B, Hq, d), sel_idx int32 (B, Hq, 1+W+k), sel_count int32 (B, Hq)); the
+    heads of a group share sel_idx and sel_count.
+    """
+    q = np.asarray(q)
+    if q.ndim == 4:
+        q = q[:, :, 0, :]
+    B, Hq, d = q.shape
+    _, Hkv, n, _ = K.shape
+    G = Hq // Hkv
+    p = n - 1 if q_pos is None else int(q_pos)
+    out = np.full((B, Hq, d), np.nan, dtype=np.float32)
+    sel = np.full((B, Hq, 1 + W + k), -1, dtype=np.int32)
+    cnt = np.full((B, Hq), -1, dtype=np.int32)
+    todo = groups if groups is not None else [(b, g) for b in range(B) for g in range(Hkv)]
+    for b, g in todo:
+        heads = range(g * G, (g + 1) * G)
+        s_heads = np.stack([canonical_scores(q[b, h], K[b, g]) for h in heads])
+        C, _ = condensate_set(group_scores(s_heads), p, W, k, causal)
+        for i, h in enumerate(heads):
+            o, _, _ = softmax_weighted_v(s_heads[i][C], np.asarray(V[b, g])[C], scale)
+            out[b, h] = o.astype(np.float32)
+            sel[b, h, :C.size] = C
+            cnt[b, h] = C.size
     return out, sel, cnt
 
 

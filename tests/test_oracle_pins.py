@@ -582,3 +582,66 @@ def test_certificate_bound_dominates_omitted_mass():
             assert b == float("inf")
         else:
             assert b >= rho * (1 - 1e-12)
+
+
+# ----------------------------------------------------------------------------- GQA shared selection
+
+def test_group_selection_hand_example():
+    """Two query heads on one kv head, d = 2, exact integer scores worked by hand. Head 0 scores
+    keys 1..4 as (3, 0, 1, 2), head 1 as (0, 2, 1, 2): the group scores are (3, 2, 1, 2); with W = 1
+    (window {5}) and k = 2 the shared top-k is {1, 2} (key 2 ties key 4 and is lower), so the set
+    is {0, 1, 2, 5}; on their own the heads would pick {1, 4} and {2, 4}."""
+    q = np.array([[[1.0, 0.0], [0.0, 1.0]]], np.float32)           # (B=1, Hq=2, d=2)
+    K = np.array([[[0, 0], [3, 0], [0, 2], [1, 1], [2, 2], [0.5, 0.5]]], np.float32)[:, None]
+    V = np.arange(12, dtype=np.float32).reshape(1, 1, 6, 2) / 7.0
+    scale = 0.5
+    out, sel, cnt = oracle.topo_attn_decode_group(q, K, V, 1, 2, scale)
+    assert cnt.tolist() == [[4, 4]]
+    assert sel[0, 0, :4].tolist() == sel[0, 1, :4].tolist() == [0, 1, 2, 5]
+    _, own, _ = oracle.topo_attn_decode(q, K, V, 1, 2, scale)
+    assert own[0, 0, :4].tolist() == [0, 1, 4, 5] and own[0, 1, :4].tolist() == [0, 2, 4, 5]
+    # textbook softmax over the shared set, per head, with each head's own scores
+    C = [0, 1, 2, 5]
+    for h, sh in enumerate(([0, 3, 0, 0.5], [0, 0, 2, 0.5])):
+        z = scale * np.array(sh)
+        w = np.exp(z - z.max())
+        want = (w / w.sum()) @ V[0, 0, C].astype(np.float64)
+        assert np.allclose(out[0, h], want, rtol=1e-6, atol=1e-7)
+
+
+def test_group_selection_reduces_to_per_head_selection():
+    rng = np.random.default_rng(41)
+    # one query head per kv head: the shared set is the head's own set
+    q = rng.standard_normal((2, 3, 16), dtype=np.float32)
+    K = rng.standard_normal((2, 3, 200, 16), dtype=np.float32)
+    V = rng.standard_normal((2, 3, 200, 16), dtype=np.float32)
+    a = oracle.topo_attn_decode_group(q, K, V, 8, 12, 0.25, q_pos=150)
+    b = oracle.topo_attn_decode(q, K, V, 8, 12, 0.25, q_pos=150)
+    assert all(np.array_equal(x, y) for x, y in zip(a, b))
+    # the same query for every head of a group: the same set as each head's own
+    q4 = np.repeat(rng.standard_normal((1, 2, 1, 16), dtype=np.float32), 4, axis=1)  # Hq = 8, Hkv = 2
+    K2 = rng.standard_normal((1, 2, 300, 16), dtype=np.float32)
+    V2 = rng.standard_normal((1, 2, 300, 16), dtype=np.float32)
+    qq = np.concatenate([np.repeat(q4[:, 0:1], 4, axis=1), np.repeat(q4[:, 4:5], 4, axis=1)], axis=1)
+    a = oracle.topo_attn_decode_group(qq, K2, V2, 16, 20, 0.25)
+    b = oracle.topo_attn_decode(qq, K2, V2, 16, 20, 0.25)
+    assert all(np.array_equal(x, y) for x, y in zip(a, b))
+
+
+def test_group_selection_rank_count_on_integer_scores():
+    """Small-integer vectors make every score exact: the shared top-k must be the brute-force
+    rank-count top-k of the element-wise maximum of the heads' scores."""
+    rng = np.random.default_rng(42)
+    for trial in range(40):
+        G, n, d = int(rng.integers(1, 5)), int(rng.integers(2, 80)), 4
+        q = rng.integers(-2, 3, size=(1, G, d)).astype(np.float32)
+        K = rng.integers(-2, 3, size=(1, 1, n, d)).astype(np.float32)
+        V = rng.standard_normal((1, 1, n, d)).astype(np.float32)
+        p = int(rng.integers(0, n))
+        W, k = int(rng.integers(0, 10)), int(rng.integers(0, 12))
+        _, sel, cnt = oracle.topo_attn_decode_group(q, K, V, W, k, 1.0, q_pos=p)
+        s = np.max(K[0, 0].astype(np.int64) @ q[0].astype(np.int64).T, axis=1).astype(np.float64)
+        cand = candidates(n, p, W, True)
+        want = np.union1d(np.union1d([0], np.arange(max(0, p - W + 1), p + 1)), rank_count_topk(s, cand, k))
+        for h in range(G):
+            assert cnt[0, h] == want.size and np.array_equal(sel[0, h, :want.size], want), (trial, h)
