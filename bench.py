@@ -153,13 +153,31 @@ def run_decode_bench(cfg: int, steps: int, warmup: int):
                    "ms_per_step": (time.perf_counter() - tc0) * 1e3 / 10}
     del wsc
 
+    # The GQA shared selection on the same inputs (one set per kv head, TOPO_FLAG_GROUP_SELECT):
+    # cost per step, on separate outputs.
+    group = None
+    if s.Hq // s.Hkv <= 4:
+        og, sg, cg = torch.empty_like(out), torch.empty_like(sel), torch.empty_like(cnt)
+        gstep = lambda: topo.topo_attn_decode(q, k, v, s.W, s.k, scale, flags=topo.TOPO_FLAG_GROUP_SELECT, out=og,
+                                              sel_idx=sg, sel_count=cg, workspace=ws)
+        gstep()
+        torch.cuda.synchronize()
+        tq0 = time.perf_counter()
+        for _ in range(10):
+            gstep()
+        torch.cuda.synchronize()
+        gms = (time.perf_counter() - tq0) * 1e3 / 10
+        group = {"ms_per_step": gms, "value": s.B * s.Hq / (gms / 1e3),
+                 "note": "one condensate set per kv head, shared by its query heads"}
+        del og, sg, cg
+
     n_cand = s.n_ctx - 1 - s.W                     # keys the scan must rank per (batch, kv head)
     row_bytes = s.d * (2 if s.dtype == "bf16" else 4)
     alg_bytes = s.B * s.Hkv * n_cand * row_bytes   # each candidate key row read once per step
     queries = s.B * s.Hq
     res = {
         "spec": s, "workload": w, "ms_per_step": ms_per_step, "scan_ms": scan_ms, "alg_bytes": alg_bytes,
-        "queries": queries, "certificate": certificate, "graph_ms_per_step": graph_ms,
+        "queries": queries, "certificate": certificate, "graph_ms_per_step": graph_ms, "group_select": group,
         "out": out.cpu().numpy()[:, :, 0], "sel": sel.cpu().numpy()[:, :, 0],
         "cnt": cnt.cpu().numpy()[:, :, 0],
     }
@@ -344,6 +362,7 @@ def main():
             "certificate": r["certificate"],
             "graph_replay": {"ms_per_step": r["graph_ms_per_step"],
                              "value": r["queries"] / (r["graph_ms_per_step"] / 1e3)},
+            "group_select": r["group_select"],
         })
 
     if args.prefill:
@@ -393,6 +412,7 @@ def main():
         "graph_replay": {"ms_per_step": main_res["graph_ms_per_step"],
                          "value": main_res["queries"] / (main_res["graph_ms_per_step"] / 1e3),
                          "note": "the same step captured once into a HIP graph and replayed"},
+        "group_select": main_res["group_select"],
         "also": also,
     }
     print(json.dumps(line), flush=True)

@@ -20,7 +20,7 @@ __all__ = [
     "topo_attn_prefill", "topo_select", "topo_attn_dense", "topo_bw_probe", "topo_strerror",
     "topo_attn_decode_timed", "topo_attn_prefill_timed", "topo_attn_decode_certified",
     "topo_attn_decode_ragged", "topo_kv_append", "topo_attn_decode_layers", "pillar_schedule",
-    "TOPO_FLAG_EXACT_SELECT", "TOPO_FLAG_DENSE_FALLBACK", "TOPO_CERT_RHO", "TOPO_MAX_SET", "EXPORTS",
+    "TOPO_FLAG_EXACT_SELECT", "TOPO_FLAG_DENSE_FALLBACK", "TOPO_FLAG_GROUP_SELECT", "TOPO_CERT_RHO", "TOPO_MAX_SET", "EXPORTS",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -31,6 +31,7 @@ TOPO_OP_DECODE, TOPO_OP_PREFILL, TOPO_OP_SELECT, TOPO_OP_DENSE, TOPO_OP_DECODE_C
 TOPO_OP_DECODE_RAGGED = 5
 TOPO_FLAG_EXACT_SELECT = 1
 TOPO_FLAG_DENSE_FALLBACK = 2
+TOPO_FLAG_GROUP_SELECT = 4
 TOPO_CERT_RHO = 2.0 ** -24
 TOPO_MAX_SET = 4096
 EXPORTS = ("topo_workspace_bytes", "topo_attn_decode", "topo_attn_decode_timed", "topo_attn_decode_certified",

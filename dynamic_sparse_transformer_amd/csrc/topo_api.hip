@@ -8,6 +8,9 @@
 #include "../../include/topo_attn.h"
 #include "topo_internal.h"
 
+static_assert(TOPO_FLAG_EXACT_SELECT == topo::FLAG_EXACT_SELECT && TOPO_FLAG_GROUP_SELECT == topo::FLAG_GROUP_SELECT,
+              "flag values shared with the kernels");
+
 namespace {
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
@@ -22,7 +25,7 @@ int check_params(const topo_params_t* p, bool need_set) {
   if (p->n_q < 1 || p->q_pos0 < 0 || p->q_pos0 + p->n_q - 1 > p->n_ctx - 1) return TOPO_EINVAL;
   if (!(p->softmax_scale > 0.f) || !std::isfinite(p->softmax_scale)) return TOPO_EINVAL;
   if (p->causal != 0 && p->causal != 1) return TOPO_EINVAL;
-  if (p->flags & ~(TOPO_FLAG_EXACT_SELECT | TOPO_FLAG_DENSE_FALLBACK)) return TOPO_EINVAL;
+  if (p->flags & ~(TOPO_FLAG_EXACT_SELECT | TOPO_FLAG_DENSE_FALLBACK | TOPO_FLAG_GROUP_SELECT)) return TOPO_EINVAL;
   if (need_set) {
     if (p->W < 0 || p->k < 0) return TOPO_EINVAL;
     if ((int64_t)p->W + p->k + 1 > TOPO_MAX_SET) return TOPO_EINVAL;
@@ -61,6 +64,10 @@ int decode_like(const topo_params_t* p, const void* q, const void* k, const void
   if (rc) return rc;
   if (p->n_q != 1) return TOPO_EINVAL;
   if (pos && (p->causal != 1 || rho || !aligned8(pos))) return TOPO_EINVAL;
+  if (p->flags & TOPO_FLAG_GROUP_SELECT) {
+    if (rho) return TOPO_EINVAL;                        // no certificate for a shared selection
+    if (p->Hq / p->Hkv > 4) return TOPO_EUNSUPPORTED;   // one key-scan slice per group
+  }
   if (!rho && (p->flags & TOPO_FLAG_DENSE_FALLBACK)) return TOPO_EINVAL;
   if (rho && !aligned16(rho)) return TOPO_EINVAL;
   if (!q || !k || !aligned16(q) || !aligned16(k)) return TOPO_EINVAL;
@@ -128,7 +135,7 @@ int prefill_like(const topo_params_t* p, const void* q, const void* k, const voi
                  bool softmax, hipEvent_t ev_begin = nullptr, hipEvent_t ev_end = nullptr) {
   int rc = check_params(p, true);
   if (rc) return rc;
-  if (p->flags & TOPO_FLAG_DENSE_FALLBACK) return TOPO_EINVAL;
+  if (p->flags & (TOPO_FLAG_DENSE_FALLBACK | TOPO_FLAG_GROUP_SELECT)) return TOPO_EINVAL;
   if (!q || !k || !aligned16(q) || !aligned16(k)) return TOPO_EINVAL;
   if (softmax && (!v || !out || !aligned16(v) || !aligned16(out))) return TOPO_EINVAL;
   if (!softmax && (!sel_idx || !sel_count)) return TOPO_EINVAL;
@@ -259,7 +266,7 @@ int topo_attn_dense(const topo_params_t* p, const void* q, const void* k, const 
                     void* workspace, size_t ws_bytes, hipStream_t stream) {
   int rc = check_params(p, false);
   if (rc) return rc;
-  if (p->flags & TOPO_FLAG_DENSE_FALLBACK) return TOPO_EINVAL;
+  if (p->flags & (TOPO_FLAG_DENSE_FALLBACK | TOPO_FLAG_GROUP_SELECT)) return TOPO_EINVAL;
   if (!q || !k || !v || !out || !aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
     return TOPO_EINVAL;
   const size_t need = topo::dense_workspace_bytes(p->B, p->Hq, p->n_q, p->n_ctx, p->d);

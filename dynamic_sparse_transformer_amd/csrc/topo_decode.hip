@@ -159,6 +159,7 @@ struct KscanArgs {
   int64_t p, w_lo, vis_hi, scan_hi;
   const int64_t* pos;  // may be null: causal query position of each batch element
   int32_t Hq, Hkv, G, W, topk, runs;
+  int32_t group;       // 1: one selection per kv head (group score = largest of the heads' scores)
   float eps_coef;
 };
 
@@ -185,7 +186,9 @@ __device__ __forceinline__ void kscan_load(uint4 (&buf)[8][RB / 128], const unsi
   }
 }
 
-template <int RB, int GT, bool BF16, bool RAGGED>
+// RAGGED: per-sequence positions; GROUP: one shared selection per kv head (template switches, so
+// the plain scan carries none of their registers).
+template <int RB, int GT, bool BF16, bool RAGGED, bool GROUP>
 __global__ __launch_bounds__(256, TOPO_KS_MIN_BLOCKS) void kscan_kernel(KscanArgs a) {
   constexpr int L = 8;          // lanes per key row
   constexpr int CPL = RB / 128; // 16-byte chunks of a row per lane
@@ -242,6 +245,14 @@ __global__ __launch_bounds__(256, TOPO_KS_MIN_BLOCKS) void kscan_kernel(KscanArg
     }
     for (int o = 1; o < L; o <<= 1) part += __shfl_xor(part, o);
     qn[h] = (float)sqrt(part) * (1.0f + 0x1p-20f);
+  }
+  // Shared selection: the group score max_h s_h of a key is ranked as the scores of one head
+  // (slot 0); |max_h s^_h - max_h s_h| <= max_h eps_h, so head 0 takes the largest |q_h|.
+  const int nsel = GROUP ? 1 : nh;
+  if constexpr (GROUP) {
+#pragma unroll
+    for (int h = 1; h < GT; ++h)
+      if (h < nh) qn[0] = fmaxf(qn[0], qn[h]);
   }
 
   // The block ranks a.runs runs of KS_WAVES x KS_KEYS_PER_WAVE keys; in run r, wave w takes the
@@ -330,6 +341,13 @@ __global__ __launch_bounds__(256, TOPO_KS_MIN_BLOCKS) void kscan_kernel(KscanArg
 #pragma unroll 1
     for (int it = 0; it + 1 < KS_IT; ++it) tile(key0 + (int64_t)it * KS_ROWS, key0 + (int64_t)(it + 1) * KS_ROWS, true);
     tile(key0 + (int64_t)(KS_IT - 1) * KS_ROWS, run_key0(r + 1), r + 1 < a.runs);
+    if constexpr (GROUP) {
+#pragma unroll
+      for (int it = 0; it < KS_IT; ++it)
+#pragma unroll
+        for (int h = 1; h < GT; ++h)
+          if (h < nh) sc[0][it] = fmaxf(sc[0][it], sc[h][it]);
+    }
 
     // Norm bound of every key seen so far: |k|^2 = sum over its chunks of |chunk|^2 <= sum over
     // the chunk slots (c, s) of the largest |chunk|^2 seen in that slot (lanes with equal s
@@ -377,7 +395,7 @@ __global__ __launch_bounds__(256, TOPO_KS_MIN_BLOCKS) void kscan_kernel(KscanArg
 #pragma unroll
       for (int h = 0; h < GT; ++h) {
         const uint32_t cur = max(trun[h], thp[h]);
-        search[h] = h < nh && cur < 0xFFFFFFFFu &&
+        search[h] = h < nsel && cur < 0xFFFFFFFFu &&
                     __popcll(__ballot(m0[h] > cur)) + __popcll(__ballot(m1[h] > cur)) >= a.topk;
         any_search |= search[h];
       }
@@ -397,7 +415,7 @@ __global__ __launch_bounds__(256, TOPO_KS_MIN_BLOCKS) void kscan_kernel(KscanArg
     } else {
 #pragma unroll
       for (int h = 0; h < GT; ++h) {
-        if (h >= nh) break;
+        if (h >= nsel) break;
         uint32_t lb[KS_IT];
 #pragma unroll
         for (int it = 0; it < KS_IT; ++it) lb[it] = ((vmask >> it) & 1u) ? ord_f32(sc[h][it] - eps_r[h]) : 0u;
@@ -407,7 +425,7 @@ __global__ __launch_bounds__(256, TOPO_KS_MIN_BLOCKS) void kscan_kernel(KscanArg
 
 #pragma unroll
     for (int h = 0; h < GT; ++h) {
-      if (h >= nh) break;
+      if (h >= nsel) break;
       // eps grows with the norm bound, so the last run's value covers every earlier entry
       const float eps = eps_r[h];
       const uint32_t th_g = thp[h];
@@ -463,8 +481,16 @@ __global__ __launch_bounds__(256, TOPO_KS_MIN_BLOCKS) void kscan_kernel(KscanArg
   }
   __syncthreads();
 
-  // Block merge: wave h merges the four waves' survivors of query head h.
-  if (wave >= nh) return;
+  // Block merge: wave h merges the four waves' survivors of query head h (shared selection: wave
+  // 0 the group's, and the other heads of the slice get empty lists).
+  if (wave >= nsel) {
+    if (wave < nh && lane == 0) {
+      const size_t bslot = ((size_t)b * a.Hq + h0 + wave) * (size_t)a.nblk + blockIdx.x;
+      a.blk_cnt[bslot] = 0u;
+      a.blk_eps[bslot] = 0.f;
+    }
+    return;
+  }
   const int h = wave;
   const size_t head = (size_t)b * a.Hq + h0 + h;
   HeadState* hs = a.st + head;
@@ -664,6 +690,7 @@ struct FinishArgs {
 
 struct FinishSmem {
   double qd[128];
+  double qg[4][128];  // shared selection: the float64 queries of the group's heads
   union {
     struct {                       // phases 1-2
       uint32_t lbk[SURV_LDS];
@@ -680,6 +707,7 @@ struct FinishSmem {
   uint32_t hist[2048];
   int32_t ridx[REFINE_CAP];
   double rs[REFINE_CAP];
+  double rg[REFINE_CAP];  // shared selection: group scores of the short list
   double red[FIN_WAVES * 128];
   double scratch[FIN_WAVES];
   int32_t ival[8];
@@ -721,6 +749,21 @@ __device__ __attribute__((noinline)) double score_row(const FinishSmem* sm, cons
   return canonical_score_row<BF16, D>(sm->qd, kb + (size_t)j * RB);
 }
 
+// Canonical score of key j for the float64 query qd (LDS).
+template <int D, bool BF16>
+__device__ __attribute__((noinline)) double score_row_q(const double* qd, const unsigned char* kb, int64_t j) {
+  constexpr int RB = D * (BF16 ? 2 : 4);
+  return canonical_score_row<BF16, D>(qd, kb + (size_t)j * RB);
+}
+
+// Group score of key j for a shared selection: the largest of the G heads' canonical scores.
+template <int D, bool BF16>
+__device__ double group_score_row(const FinishSmem* sm, const unsigned char* kb, int64_t j, int G) {
+  double m = score_row_q<D, BF16>(sm->qg[0], kb, j);
+  for (int i = 1; i < G; ++i) m = fmax(m, score_row_q<D, BF16>(sm->qg[i], kb, j));
+  return m;
+}
+
 __device__ __forceinline__ bool is_candidate(const FinishArgs& a, int64_t j) {
   return j >= 1 && j <= a.vis_hi && (j < a.w_lo || j > a.p);
 }
@@ -740,7 +783,8 @@ __device__ int exact_select(FinishSmem* sm, const FinishArgs& a, const unsigned 
       __syncthreads();
       for (int64_t j = 1 + tid; j <= a.scan_hi; j += FIN_THREADS) {
         if (!is_candidate(a, j)) continue;
-        const uint64_t key = ord_f64(score_row<D, BF16>(sm, kb, j));
+        const uint64_t key =
+            ord_f64((a.flags & FLAG_GROUP_SELECT) ? group_score_row<D, BF16>(sm, kb, j, a.G) : score_row<D, BF16>(sm, kb, j));
         if (pass == 0 || (key >> (shift + 8)) == prefix) atomicAdd(&sm->hist[(key >> shift) & 255u], 1u);
       }
       __syncthreads();
@@ -765,7 +809,7 @@ __device__ int exact_select(FinishSmem* sm, const FinishArgs& a, const unsigned 
     double s = 0.0;
     bool gt = false, eq = false;
     if (is_c) {
-      s = score_row<D, BF16>(sm, kb, j);
+      s = (a.flags & FLAG_GROUP_SELECT) ? group_score_row<D, BF16>(sm, kb, j, a.G) : score_row<D, BF16>(sm, kb, j);
       if (take_all) {
         gt = true;
       } else {
@@ -889,7 +933,15 @@ __global__ __launch_bounds__(FIN_THREADS) void decode_finish_kernel(FinishArgs a
   const unsigned char* qrow = a.q + (size_t)bh * RB;
 
   if (tid < D) sm->qd[tid] = load_elem_f64<BF16>(qrow, tid);
-  // (stage_survivors below starts with a barrier-protected phase, so qd is visible after it)
+  // Shared selection: the group's first head holds the survivor lists and the shared state of
+  // the whole group, and every head of the group ranks by the same group scores.
+  const bool group = (a.flags & FLAG_GROUP_SELECT) != 0;
+  const int sh = group ? b * a.Hq + g * a.G : bh;  // head whose lists and state this block reads
+  if (group) {
+    for (int t = tid; t < a.G * D; t += FIN_THREADS)
+      sm->qg[t / D][t % D] = load_elem_f64<BF16>(a.q + (size_t)(b * a.Hq + g * a.G + t / D) * RB, t % D);
+  }
+  // (stage_survivors below starts with a barrier-protected phase, so qd and qg are visible after it)
 
   const int64_t w_lo = a.w_lo, p = a.p;
   const int anchor = w_lo > 0 ? 1 : 0;
@@ -902,11 +954,11 @@ __global__ __launch_bounds__(FIN_THREADS) void decode_finish_kernel(FinishArgs a
   int nr = 0;
   bool exact = false, take_all = false;
   if (a.topk > 0 && a.n_cand > 0) {
-    const uint32_t st_theta = a.st[bh].theta, st_over = a.st[bh].overflow;
+    const uint32_t st_theta = a.st[sh].theta, st_over = a.st[sh].overflow;
     exact = (a.flags & 1) != 0 || st_over != 0 || a.topk > KS_MAX_K;
     take_all = a.n_cand <= a.topk;
     if (!take_all && !exact) {
-      const int M = stage_survivors(sm, a, bh, st_theta);
+      const int M = stage_survivors(sm, a, sh, st_theta);
       if (M < a.topk) {
         exact = true;  // more survivors than LDS holds (or, impossibly, fewer than k)
       } else {
@@ -974,8 +1026,12 @@ __global__ __launch_bounds__(FIN_THREADS) void decode_finish_kernel(FinishArgs a
       for (int i = tid; i < nc; i += 128) {
         const int64_t j = (fast && i < nr) ? (int64_t)sm->ridx[i] : 0;
         const double sc = score_row<D, BF16>(sm, kb, j);
-        if (fast && i < nr) sm->rs[i] = sc;
-        else sm->u.c.cw[MAX_SET - 1] = sc;
+        if (fast && i < nr) {
+          sm->rs[i] = sc;
+          if (group) sm->rg[i] = group_score_row<D, BF16>(sm, kb, j, a.G);
+        } else {
+          sm->u.c.cw[MAX_SET - 1] = sc;
+        }
       }
     } else {
       constexpr int LPR = RB / 16, EPC = BF16 ? 8 : 4, RPP = (FIN_THREADS - 128) / LPR, WB = 12;
@@ -1013,8 +1069,10 @@ __global__ __launch_bounds__(FIN_THREADS) void decode_finish_kernel(FinishArgs a
   }
   __syncthreads();
   if (fast) {
-    // exact rank of each short-list entry (higher score first, then lower position): the
-    // comparisons of entry i are split into `parts` slices over all threads, summed in LDS
+    // exact rank of each short-list entry (higher score first, then lower position; group scores
+    // for a shared selection): the comparisons of entry i are split into `parts` slices over all
+    // threads, summed in LDS
+    const double* rk_s = group ? sm->rg : sm->rs;
     int* rank = (int*)sm->hist;
     for (int i = tid; i < nr; i += FIN_THREADS) rank[i] = 0;
     __syncthreads();
@@ -1022,12 +1080,12 @@ __global__ __launch_bounds__(FIN_THREADS) void decode_finish_kernel(FinishArgs a
     const int chunk = (nr + parts - 1) / parts;
     for (int idx = tid; idx < nr * parts; idx += FIN_THREADS) {
       const int i = idx % nr, part = idx / nr;
-      const double si = sm->rs[i];
+      const double si = rk_s[i];
       const int32_t ji = sm->ridx[i];
       const int r1 = min(nr, (part + 1) * chunk);
       int cnt = 0;
       for (int r = part * chunk; r < r1; ++r) {
-        const double sr = sm->rs[r];
+        const double sr = rk_s[r];
         cnt += (sr > si) || (sr == si && sm->ridx[r] < ji);
       }
       if (cnt) atomicAdd(&rank[i], cnt);
@@ -1043,6 +1101,11 @@ __global__ __launch_bounds__(FIN_THREADS) void decode_finish_kernel(FinishArgs a
     nt = a.topk;
   } else if (a.topk > 0 && a.n_cand > 0) {
     nt = exact_select<D, BF16>(sm, a, kb, take_all);
+    if (group) {
+      // the selection ranked group scores; the softmax takes this head's own scores
+      for (int t = tid; t < nt; t += FIN_THREADS) sm->u.c.ts[t] = score_row<D, BF16>(sm, kb, sm->u.c.tidx[t]);
+      __syncthreads();
+    }
   }
   __syncthreads();
 
@@ -1171,10 +1234,17 @@ __global__ __launch_bounds__(FIN_THREADS) void decode_finish_kernel(FinishArgs a
 // ---------------------------------------------------------------------------------------------
 template <int RB, int GT, bool BF16>
 static hipError_t launch_kscan_t(const KscanArgs& ka, dim3 grid, hipStream_t s) {
-  if (ka.pos)
-    hipLaunchKernelGGL((kscan_kernel<RB, GT, BF16, true>), grid, dim3(256), 0, s, ka);
-  else
-    hipLaunchKernelGGL((kscan_kernel<RB, GT, BF16, false>), grid, dim3(256), 0, s, ka);
+  if (ka.group) {
+    if (ka.pos)
+      hipLaunchKernelGGL((kscan_kernel<RB, GT, BF16, true, true>), grid, dim3(256), 0, s, ka);
+    else
+      hipLaunchKernelGGL((kscan_kernel<RB, GT, BF16, false, true>), grid, dim3(256), 0, s, ka);
+  } else {
+    if (ka.pos)
+      hipLaunchKernelGGL((kscan_kernel<RB, GT, BF16, true, false>), grid, dim3(256), 0, s, ka);
+    else
+      hipLaunchKernelGGL((kscan_kernel<RB, GT, BF16, false, false>), grid, dim3(256), 0, s, ka);
+  }
   return hipGetLastError();
 }
 
@@ -1229,6 +1299,7 @@ hipError_t launch_decode(const DecodeLaunch& L, hipStream_t stream) {
     ka.scan_hi = g.scan_hi;
     ka.pos = L.pos;
     ka.W = L.W;
+    ka.group = (L.flags & FLAG_GROUP_SELECT) ? 1 : 0;
     ka.Hq = L.Hq;
     ka.Hkv = L.Hkv;
     ka.G = L.G;

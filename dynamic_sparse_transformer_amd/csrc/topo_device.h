@@ -109,13 +109,11 @@ __device__ __forceinline__ double canonical_score(const double* qd, const void* 
 
 // Same value as canonical_score, with every 16-byte chunk of the row requested before the first
 // multiply-add so that the row costs one memory round trip.
+// The canonical float64 score of a key row already in registers (w: its 16-byte chunks), in the
+// order of canonical_score_row.
 template <bool BF16, int D>
-__device__ __forceinline__ double canonical_score_row(const double* qd, const void* krow) {
+__device__ __forceinline__ double canonical_score_words(const double* qd, const uint4* w) {
   constexpr int NC = D * (BF16 ? 2 : 4) / 16;
-  const uint4* p = (const uint4*)krow;
-  uint4 w[NC];
-#pragma unroll
-  for (int c = 0; c < NC; ++c) w[c] = p[c];
   double s = 0.0;
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
@@ -131,6 +129,16 @@ __device__ __forceinline__ double canonical_score_row(const double* qd, const vo
     }
   }
   return s + 0.0;
+}
+
+template <bool BF16, int D>
+__device__ __forceinline__ double canonical_score_row(const double* qd, const void* krow) {
+  constexpr int NC = D * (BF16 ? 2 : 4) / 16;
+  const uint4* p = (const uint4*)krow;
+  uint4 w[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) w[c] = p[c];
+  return canonical_score_words<BF16, D>(qd, w);
 }
 
 __device__ __forceinline__ float wave_max_f32(float x) {

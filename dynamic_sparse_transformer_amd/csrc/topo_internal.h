@@ -25,6 +25,10 @@ constexpr int MERGE_FAN = 8;      // survivor lists merged into one per merge st
 constexpr int MAX_LEVELS = 8;
 constexpr int SURV_LDS = 8192;    // survivors the finishing kernel stages in LDS
 
+// Flag bits of the call (the values of TOPO_FLAG_EXACT_SELECT and TOPO_FLAG_GROUP_SELECT).
+constexpr int32_t FLAG_EXACT_SELECT = 1;
+constexpr int32_t FLAG_GROUP_SELECT = 4;
+
 // Per (batch, query head) state shared by the key scan blocks, one 128-byte line per head.
 struct alignas(128) HeadState {
   uint32_t theta;     // order key of a proven lower bound of the k-th best candidate score

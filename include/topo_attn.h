@@ -82,6 +82,18 @@ extern "C" {
 #define TOPO_FLAG_DENSE_FALLBACK 2  /* topo_attn_decode_certified only: queries whose bound rho is
                                        not below TOPO_CERT_RHO get dense attention in out      */
 
+#define TOPO_FLAG_GROUP_SELECT 4  /* decode calls (topo_attn_decode, _timed, _ragged, topo_select
+                                     with n_q == 1): one condensate set per (batch, kv head),
+                                     shared by the G = Hq / Hkv query heads of the group (G <= 4;
+                                     TOPO_EUNSUPPORTED otherwise). A key's group score is the
+                                     largest of the group's per-head scores; the top-k ranks group
+                                     scores (higher first, lower position on ties); each head then
+                                     takes the softmax of its own scores over the shared set, and
+                                     sel_idx / sel_count repeat the set for every head of the
+                                     group. The pages name GQA without fixing how it selects; this
+                                     is the shared-selection variant. Not accepted by the prefill,
+                                     dense and certified calls (TOPO_EINVAL).                   */
+
 /* A query is certified when its bound on the left-out softmax mass is below the float32
  * rounding unit 2^-24: the set then carries the dense softmax to float32 precision, the
  * exactness claim of the pages (zh technical summary §2; hi technical summary §2). */

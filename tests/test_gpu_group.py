@@ -1,0 +1,122 @@
+"""GPU parity of the GQA shared selection (TOPO_FLAG_GROUP_SELECT: one condensate set per kv head,
+ranked by the largest of the group's per-head scores, each head's own softmax over it) with the
+CPU oracle's topo_attn_decode_group. The pages name GQA without fixing how it selects ("The
+Condensate Theorem: Transformers are O(n), Not O(n^2)"); the set and softmax are those of the zh
+page's technical summary §3 and the fr page's §3. Sets bit-exact; outputs within 1e-6 + 2e-6 |ref|
+(float32 inputs) or a relative 1e-2 (bf16 inputs)."""
+import sys
+
+import numpy as np
+import pytest
+
+import dynamic_sparse_transformer_amd as topo
+import oracle
+from tests._util import assert_out_close, assert_sets_equal, to_device, torch_cuda
+from workloads import bf16_bits_to_f32, f32_to_bf16_bits, make_workload
+
+pytestmark = pytest.mark.gpu
+GROUP = topo.TOPO_FLAG_GROUP_SELECT
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def make_case(seed, B, Hq, Hkv, n, d, dtype, ties=False):
+    rng = np.random.default_rng(seed)
+    if ties:
+        q = rng.integers(-2, 3, size=(B, Hq, 1, d)).astype(np.float32)
+        k = rng.integers(-1, 2, size=(B, Hkv, n, d)).astype(np.float32)
+    else:
+        q = rng.standard_normal((B, Hq, 1, d), dtype=np.float32)
+        k = rng.standard_normal((B, Hkv, n, d), dtype=np.float32)
+    v = rng.standard_normal((B, Hkv, n, d), dtype=np.float32)
+    if dtype == "bf16":
+        st = tuple(f32_to_bf16_bits(x) for x in (q, k, v))
+        return tuple(bf16_bits_to_f32(x) for x in st), st
+    return (q, k, v), (q, k, v)
+
+
+def compare(vals, out, sel, cnt, W, K, scale, dtype, what, q_pos=None, groups=None):
+    q, k, v = vals
+    o_ref, s_ref, c_ref = oracle.topo_attn_decode_group(q, k, v, W, K, scale, True, q_pos=q_pos, groups=groups)
+    G = q.shape[1] // k.shape[1]
+    todo = groups if groups is not None else [(b, g) for b in range(q.shape[0]) for g in range(k.shape[1])]
+    for b, g in todo:
+        for h in range(g * G, (g + 1) * G):
+            assert_sets_equal(sel[b, h], cnt[b, h], s_ref[b, h], c_ref[b, h], f"{what} b{b} h{h}")
+            assert_out_close(out[b, h], o_ref[b, h], dtype, f"{what} b{b} h{h}")
+
+
+CASES = [
+    # (seed, B, Hq, Hkv, n, d, dtype, W, k, ties)
+    (1, 2, 8, 2, 6000, 128, "bf16", 64, 32, False),
+    (2, 1, 4, 2, 3000, 64, "f32", 16, 48, False),
+    (3, 1, 6, 2, 4097, 128, "bf16", 100, 64, False),   # G = 3
+    (4, 2, 3, 3, 2000, 128, "bf16", 32, 16, False),    # G = 1: the per-head selection
+    (5, 1, 8, 2, 5000, 64, "bf16", 32, 64, True),      # ties everywhere
+    (6, 1, 4, 1, 3000, 128, "bf16", 64, 300, False),   # k above the fast path: exact selection
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[f"n{c[4]}-d{c[5]}-{c[6]}-G{c[2] // c[3]}-W{c[7]}-k{c[8]}"
+                                            f"{'-ties' if c[9] else ''}" for c in CASES])
+def test_group_decode_matches_oracle(case):
+    torch = torch_cuda()
+    seed, B, Hq, Hkv, n, d, dtype, W, K, ties = case
+    say("case", case)
+    vals, store = make_case(300 + seed, B, Hq, Hkv, n, d, dtype, ties)
+    dq, dk, dv = (to_device(x, dtype) for x in store)
+    scale = 1.0 / np.sqrt(d)
+    out, sel, cnt = topo.topo_attn_decode(dq, dk, dv, W, K, scale, flags=GROUP)
+    ex = topo.topo_attn_decode(dq, dk, dv, W, K, scale, flags=GROUP | topo.TOPO_FLAG_EXACT_SELECT)
+    torch.cuda.synchronize()
+    out, sel, cnt = out.cpu().numpy()[:, :, 0], sel.cpu().numpy()[:, :, 0], cnt.cpu().numpy()[:, :, 0]
+    compare(vals, out, sel, cnt, W, K, scale, dtype, "group")
+    assert np.array_equal(ex[1].cpu().numpy()[:, :, 0], sel) and np.array_equal(ex[2].cpu().numpy()[:, :, 0], cnt)
+
+
+def test_group_ragged_positions():
+    torch = torch_cuda()
+    vals, store = make_case(310, 3, 8, 2, 4000, 128, "bf16")
+    dq, dk, dv = (to_device(x, "bf16") for x in store)
+    pos = [3999, 1500, 90]
+    dpos = torch.tensor(pos, dtype=torch.int64, device="cuda")
+    scale = 1.0 / np.sqrt(128)
+    out, sel, cnt = topo.topo_attn_decode_ragged(dq, dk, dv, dpos, 32, 32, scale, flags=GROUP)
+    torch.cuda.synchronize()
+    out, sel, cnt = out.cpu().numpy()[:, :, 0], sel.cpu().numpy()[:, :, 0], cnt.cpu().numpy()[:, :, 0]
+    q, k, v = vals
+    for b, p in enumerate(pos):
+        compare((q[b:b + 1], k[b:b + 1], v[b:b + 1]), out[b:b + 1], sel[b:b + 1], cnt[b:b + 1], 32, 32, scale,
+                "bf16", f"ragged b{b}", q_pos=p)
+
+
+def test_group_at_the_128k_gqa_workload():
+    """The batch-4 GQA workload at full size (G = 4) with a shared selection: sampled groups
+    against the oracle."""
+    torch = torch_cuda()
+    w = make_workload(4)
+    s = w.spec
+    dq, dk, dv = (to_device(getattr(w, x), s.dtype) for x in ("q", "k", "v"))
+    say("128K group decode on GPU")
+    out, sel, cnt = topo.topo_attn_decode(dq, dk, dv, s.W, s.k, float(s.softmax_scale), flags=GROUP)
+    torch.cuda.synchronize()
+    groups = [(0, 0), (1, 3), (2, 5), (3, 7)]
+    say("oracle on groups", groups)
+    compare((w.f32("q"), w.f32("k"), w.f32("v")), out.cpu().numpy()[:, :, 0], sel.cpu().numpy()[:, :, 0],
+            cnt.cpu().numpy()[:, :, 0], s.W, s.k, float(s.softmax_scale), s.dtype, "128K group", groups=groups)
+
+
+def test_group_rejects_wide_groups_and_other_calls():
+    torch = torch_cuda()
+    _, store = make_case(320, 1, 8, 1, 500, 64, "bf16")  # G = 8
+    dq, dk, dv = (to_device(x, "bf16") for x in store)
+    with pytest.raises(topo.TopoError) as e:
+        topo.topo_attn_decode(dq, dk, dv, 16, 16, 0.125, flags=GROUP)
+    assert e.value.status == -2
+    with pytest.raises(topo.TopoError) as e:
+        topo.topo_attn_prefill(dq.expand(1, 8, 500, 64).contiguous(), dk, dv, 16, 16, 0.125, q_pos0=0, flags=GROUP)
+    assert e.value.status == -1
+    torch.cuda.synchronize()
