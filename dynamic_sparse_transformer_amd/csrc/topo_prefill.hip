@@ -75,50 +75,52 @@ static PfWs pf_carve(void* ws, int32_t B, int32_t Hq, int64_t n_q, int32_t d, in
 }
 
 // ---------------------------------------------------------------------------------------------
-// |q| of every query row: one wave per row (coalesced), float64 sum, rounded up to float32.
-template <int D, bool BF16>
-__global__ __launch_bounds__(256) void pf_qnorm_kernel(const unsigned char* q, float* qn, int64_t rows) {
-  constexpr int RB = D * (BF16 ? 2 : 4);
-  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  if (row >= rows) return;
-  double s2 = 0.0;
-  constexpr int EPL = D / 64;
-#pragma unroll
-  for (int e = 0; e < EPL; ++e) {
-    const double x = load_elem_f64<BF16>(q + (size_t)row * RB, lane * EPL + e);
-    s2 += x * x;
-  }
-  s2 = wave_sum_f64(s2);
-  if (lane == 0) qn[row] = (float)sqrt(s2) * (1.0f + 0x1p-20f);
-}
-
-// Largest |k| of every kv head: grid (ceil(n/PF_KMAX_ROWS), B*Hkv); one atomicMax per block.
-constexpr int PF_KMAX_ROWS = 128;
-template <int D, bool BF16>
-__global__ __launch_bounds__(256) void pf_kmax_kernel(const unsigned char* k, uint32_t* knmax, int64_t n) {
-  constexpr int RB = D * (BF16 ? 2 : 4);
+// Norms of bf16 rows for the error bounds of the matrix-core scores: |q| of every query row and
+// the largest |k| of every kv head. A row is LPR lanes x 16 bytes (coalesced, RPW rows per load
+// instruction). The squares of bf16 values are exact in float32; their float32 sum (8 terms per
+// lane, then a tree over the LPR lanes) and sqrtf carry a relative error far below the factor
+// (1 + 2^-15) that rounds the norm up. Grid (blocks over the rows of a head, heads); with
+// `norm` every row's norm is written, with `head_max` one atomicMax per block into its head
+// (U rows per lane, large for this use: the atomics of all blocks meet on one cache line). Block
+// (0, 0) also clears the `nzero` words at `zero` (the head maxima of the launch that follows).
+template <int D, int U>
+__global__ __launch_bounds__(256) void pf_norm_kernel(const unsigned char* x, int64_t rows_per_head, float* norm,
+                                                      uint32_t* head_max, uint32_t* zero, int nzero) {
+  constexpr int RB = D * 2, LPR = RB / 16, RPW = 64 / LPR;
   __shared__ float wm[4];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const unsigned char* kb = k + (size_t)blockIdx.y * (size_t)n * RB;
-  float mx = 0.f;
-  const int64_t r0 = (int64_t)blockIdx.x * PF_KMAX_ROWS;
-  for (int64_t row = r0 + wave; row < r0 + PF_KMAX_ROWS && row < n; row += 4) {
-    double s2 = 0.0;
-    constexpr int EPL = D / 64;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, gq = lane / LPR, cc = lane % LPR;
+  const unsigned char* base = x + (size_t)blockIdx.y * (size_t)rows_per_head * RB;
+  const int64_t r0 = (int64_t)blockIdx.x * (4 * U * RPW) + (int64_t)wave * U * RPW + gq;
+  uint4 v[U];
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) {
-      const double x = load_elem_f64<BF16>(kb + (size_t)row * RB, lane * EPL + e);
-      s2 += x * x;
-    }
-    s2 = wave_sum_f64(s2);
-    mx = fmaxf(mx, (float)sqrt(s2) * (1.0f + 0x1p-20f));
+  for (int u = 0; u < U; ++u) {
+    const int64_t row = r0 + u * RPW;
+    v[u] = row < rows_per_head ? *(const uint4*)(base + (size_t)row * RB + cc * 16) : make_uint4(0u, 0u, 0u, 0u);
   }
-  if (lane == 0) wm[wave] = mx;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const float m = fmaxf(fmaxf(wm[0], wm[1]), fmaxf(wm[2], wm[3]));
-    atomicMax(&knmax[blockIdx.y], __float_as_uint(m));
+  if (zero && blockIdx.x == 0 && blockIdx.y == 0)
+    for (int t = threadIdx.x; t < nzero; t += 256) zero[t] = 0u;
+  float mx = 0.f;
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const uint32_t w4[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+    float s2 = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float lo = bf16_lo(w4[e]), hi = bf16_hi(w4[e]);
+      s2 = fmaf(lo, lo, s2);
+      s2 = fmaf(hi, hi, s2);
+    }
+    s2 = group_sum_f32<LPR>(s2);
+    const float nrm = sqrtf(s2) * (1.0f + 0x1p-15f);
+    const int64_t row = r0 + u * RPW;
+    if (norm && cc == 0 && row < rows_per_head) norm[(size_t)blockIdx.y * rows_per_head + row] = nrm;
+    mx = fmaxf(mx, nrm);
+  }
+  if (head_max) {
+    for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+    if (lane == 0) wm[wave] = mx;
+    __syncthreads();
+    if (threadIdx.x == 0) atomicMax(&head_max[blockIdx.y], __float_as_uint(fmaxf(fmaxf(wm[0], wm[1]), fmaxf(wm[2], wm[3]))));
   }
 }
 
@@ -127,11 +129,6 @@ __global__ __launch_bounds__(256) void pf_kmax_kernel(const unsigned char* k, ui
 // share one XCD's L2.
 __device__ __forceinline__ int64_t xcd_job(int64_t blk, int64_t njobs) {
   return njobs % 8 == 0 ? (blk & 7) * (njobs >> 3) + (blk >> 3) : blk;
-}
-
-__global__ void pf_zero_kernel(uint32_t* x, int64_t n) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) x[i] = 0u;
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -1049,15 +1046,20 @@ __global__ __launch_bounds__(256) void pf_finish_kernel(PfArgs a) {
 template <int D, bool BF16>
 static hipError_t launch_pf_t(const PrefillLaunch& L, const PfArgs& pa, hipStream_t s) {
   const size_t rows = (size_t)L.B * L.Hq * (size_t)L.n_q;
-  // norms and zeroed kv-head maxima
-  hipLaunchKernelGGL(pf_zero_kernel, dim3((unsigned)((L.B * L.Hkv + 255) / 256)), dim3(256), 0, s, pa.w.knmax,
-                     (int64_t)L.B * L.Hkv);
-  hipLaunchKernelGGL((pf_qnorm_kernel<D, BF16>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s,
-                     (const unsigned char*)L.q, pa.w.qn, (int64_t)rows);
-  hipLaunchKernelGGL((pf_kmax_kernel<D, BF16>), dim3((unsigned)((L.n + PF_KMAX_ROWS - 1) / PF_KMAX_ROWS), (unsigned)(L.B * L.Hkv)),
-                     dim3(256), 0, s, (const unsigned char*)L.k, pa.w.knmax, L.n);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  hipError_t e = hipSuccess;
+  if constexpr (BF16) {
+    if (!pa.exact_all && L.topk > 0) {
+      // norms for the error bounds of the matrix-core scores (only the fast selection uses them)
+      constexpr int RPW = 64 / (D * 2 / 16), QU = 4, KU = 16;  // rows per wave load; loads per lane
+      hipLaunchKernelGGL((pf_norm_kernel<D, QU>), dim3((unsigned)((rows + 4 * QU * RPW - 1) / (4 * QU * RPW)), 1), dim3(256),
+                         0, s, (const unsigned char*)L.q, (int64_t)rows, pa.w.qn, (uint32_t*)nullptr, pa.w.knmax,
+                         L.B * L.Hkv);
+      hipLaunchKernelGGL((pf_norm_kernel<D, KU>), dim3((unsigned)((L.n + 4 * KU * RPW - 1) / (4 * KU * RPW)), (unsigned)(L.B * L.Hkv)),
+                         dim3(256), 0, s, (const unsigned char*)L.k, L.n, (float*)nullptr, pa.w.knmax, (uint32_t*)nullptr, 0);
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+  }
   if (L.ev_scan_begin) (void)hipEventRecord(L.ev_scan_begin, s);
   if (!pa.exact_all && L.topk > 0) {
     if constexpr (BF16) {
