@@ -124,6 +124,22 @@ __global__ __launch_bounds__(256) void pf_norm_kernel(const unsigned char* x, in
   }
 }
 
+// Sum, maximum or minimum over each row of 16 lanes, in every lane of the row (DPP: quad swaps,
+// half-row and row mirrors).
+template <int CTRL, typename T>
+__device__ __forceinline__ T pf_dpp(T y) {
+  return __builtin_bit_cast(T, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, y), CTRL, 0xF, 0xF, false));
+}
+template <int OP, typename T>
+__device__ __forceinline__ T pf_row16(T x) {
+  const auto f = [](T p, T q) { return OP == 0 ? p + q : OP == 1 ? (p > q ? p : q) : (p < q ? p : q); };
+  x = f(x, pf_dpp<0xB1>(x));
+  x = f(x, pf_dpp<0x4E>(x));
+  x = f(x, pf_dpp<0x141>(x));
+  x = f(x, pf_dpp<0x140>(x));
+  return x;
+}
+
 // Job of block `blk` among `njobs`: consecutive block indices go to different XCDs (round robin),
 // so the jobs are dealt out in eight contiguous ranges, one per XCD, and the rows of one head
 // share one XCD's L2.
@@ -288,22 +304,31 @@ __global__ __launch_bounds__(512) void pf_scan_kernel(PfArgs a) {
     }                                                                                              \
   }
 // One step t of a pass: the scores of tile t are in ACC_CUR (issued a step earlier); the matrix
-// cores score tile t+1 into ACC_NEXT while the vector units run EPI on tile t; then tile t+2 goes
-// from its registers to the LDS buffer that tile t used and tile t+4 is requested. The scheduling
-// barriers interleave the eight matrix instructions with the vector work.
-#define PF_STEP(EPI, t, ACC_CUR, ACC_NEXT, SET0, SET1)                                             \
+// cores score tile t+1 into ACC_NEXT while the vector units run the per-score work on tile t: PART
+// for each register of ACC_CUR, 16 / STEPS of them after each matrix instruction, then POST. Tile
+// t+2 then goes from its registers to the LDS buffer that tile t used and tile t+4 is requested.
+// Scheduling fences keep that order: left to itself the compiler puts the vector work before the
+// matrix instructions, and as the waves of a block meet at every barrier, the two waves of a
+// SIMD would then take turns on the matrix core instead of overlapping.
+#define PF_STEP(PART, POST, t, ACC_CUR, ACC_NEXT, SET0, SET1)                                      \
   PF_MASK(ACC_CUR, t)                                                                              \
-  PF_MMA(ACC_NEXT, ((t) + 1) & 1)                                                                  \
-  EPI(ACC_CUR, t)                                                                                  \
+  {                                                                                                \
+    const unsigned char* krow = &ktiles[(((t) + 1) & 1) * TILE_BYTES + (kq * 32 + m) * STRIDE + half * 16]; \
+    uint4 kf[STEPS];                                                                               \
+    _Pragma("unroll") for (int st = 0; st < STEPS; ++st) kf[st] = *(const uint4*)(krow + st * 32); \
+    __builtin_amdgcn_sched_barrier(0);                                                             \
+    ACC_NEXT = f32x16_t{};                                                                         \
+    _Pragma("unroll") for (int st = 0; st < STEPS; ++st) {                                         \
+      ACC_NEXT = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[st], __builtin_bit_cast(bf16x8_t, kf[st]), ACC_NEXT, 0, 0, 0); \
+      __builtin_amdgcn_sched_barrier(0);                                                           \
+      _Pragma("unroll") for (int e = 0; e < 16 / STEPS; ++e) PART(ACC_CUR, st * (16 / STEPS) + e)  \
+      __builtin_amdgcn_sched_barrier(0);                                                           \
+    }                                                                                              \
+  }                                                                                                \
+  POST(ACC_CUR, t)                                                                                 \
   PF_STORE(SET0, SET1, (t) + 2)                                                                    \
   PF_LOAD(SET0, SET1, (t) + 4)                                                                     \
   __syncthreads();
-#define PF_INTERLEAVE()                                                                            \
-  __builtin_amdgcn_sched_group_barrier(0x100, STEPS, 0);                                           \
-  _Pragma("unroll") for (int st = 0; st < STEPS; ++st) {                                           \
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                             \
-    __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);                                             \
-  }
 
   f32x16_t accA, accB;
   // ---- phase 1: per lane and row, the two largest fast scores of candidate keys. With m1 >= m2,
@@ -313,39 +338,103 @@ __global__ __launch_bounds__(512) void pf_scan_kernel(PfArgs a) {
   float m1[16], m2[16];
 #pragma unroll
   for (int r = 0; r < 16; ++r) m1[r] = m2[r] = -INFINITY;
-#define PF_EPI1(ACC, t)                                                                            \
-  _Pragma("unroll") for (int r = 0; r < 16; ++r) {                                                 \
+// (The empty asm statements pin each result to its place between the matrix instructions;
+// without them the compiler sinks the work of a step past the next step's boundary-tile branch.)
+#define PF_PART1(ACC, r)                                                                           \
+  {                                                                                                \
     m2[r] = __builtin_amdgcn_fmed3f(m1[r], m2[r], ACC[r]);                                         \
     m1[r] = __builtin_amdgcn_fmed3f(m1[r], ACC[r], pinf);                                          \
-  }                                                                                                \
-  PF_INTERLEAVE()
+    asm volatile("" : "+v"(m1[r]), "+v"(m2[r]));                                                   \
+  }
+#define PF_POST1(ACC, t)
   if (ntiles > 0) {
     PF_PROLOGUE(accA)
     for (int t = 0; t < ntiles; t += 2) {
-      PF_STEP(PF_EPI1, t, accA, accB, r00, r01)
-      PF_STEP(PF_EPI1, t + 1, accB, accA, r10, r11)
+      PF_STEP(PF_PART1, PF_POST1, t, accA, accB, r00, r01)
+      PF_STEP(PF_PART1, PF_POST1, t + 1, accB, accA, r10, r11)
     }
   }
 
-  // ---- thresholds: row R's 128 values sit at tops[R][64 * kq + 2 * m + {0, 1}]
+  // ---- thresholds: row R's 128 values sit at tops[R][64 * kq + 2 * m + {0, 1}] (even entries:
+  // the lanes' best values, 64 distinct keys; odd entries: their second best). Each row needs a
+  // lower bound T of the k-th largest of its 128 values such that few values lie between: the
+  // largest T = lo + c (hi - lo) / 1024, c = 0..1023, that at least k values reach (a bitwise
+  // search over c, monotone in c), where hi is the largest value and lo a known lower bound of the
+  // k-th largest: for k <= 64 and 64 finite best values the smallest of them, else the smallest
+  // finite value (if fewer than k values are finite every candidate stays). The bound is at most
+  // (hi - lo) / 1024 below the k-th largest, and it is never above it. A wave takes 16 rows in
+  // four groups of four; the 16 lanes of a row hold 8 values each, counted lane by lane and
+  // summed over the row with DPP moves.
   float* tops = (float*)lists;
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     const int row = row_base + 8 * (r / 4) + (r % 4);
     *(float2*)&tops[row * 128 + 64 * kq + 2 * m] = make_float2(m1[r], m2[r]);
   }
+  const int sub = lane & 15;
+  float qn_g[4];
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    const int64_t i = i0 + wave * 16 + 4 * g + (lane >> 4);
+    qn_g[g] = i < a.n_q ? a.w.qn[(size_t)bh * a.n_q + i] : 0.f;
+  }
   __syncthreads();
-  for (int row = wave; row < PF_ROWS; row += 8) {
-    const float2 v = *(const float2*)&tops[row * 128 + 2 * lane];
-    const uint32_t key[2] = {ord_f32(v.x), ord_f32(v.y)};
-    const uint32_t xk = wave_kth_largest<2>(key, a.topk);
-    if (lane == 0) {
-      const int64_t i = i0 + row;
-      const float eps = i < a.n_q ? PF_EPS_COEF * a.w.qn[(size_t)bh * a.n_q + i] * knmax + 1e-30f : 0.f;
-      // fewer than k finite values (or none): every candidate stays. The bound is kept finite
-      // (at least the lowest float), so that the -inf of a masked score never passes it.
-      const float x = xk == 0u ? -INFINITY : unord_f32(xk);
-      lthf[row] = fmaxf(x - 2.0f * eps, -0x1.fffffep+127f);
+  {
+    float v[4][8], lo[4], step[4];
+    int c[4];
+    bool ok[4];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const float* src = &tops[(wave * 16 + 4 * g + (lane >> 4)) * 128 + 8 * sub];
+      const float4 x0 = *(const float4*)src, x1 = *(const float4*)(src + 4);
+      v[g][0] = x0.x; v[g][1] = x0.y; v[g][2] = x0.z; v[g][3] = x0.w;
+      v[g][4] = x1.x; v[g][5] = x1.y; v[g][6] = x1.z; v[g][7] = x1.w;
+      float hi = -INFINITY, lo_best = INFINITY, lo_fin = INFINITY;
+      int nfin = 0, nbest = 0;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const bool fin = v[g][j] > -INFINITY;
+        hi = fmaxf(hi, v[g][j]);
+        nfin += fin;
+        lo_fin = fin ? fminf(lo_fin, v[g][j]) : lo_fin;
+        if ((j & 1) == 0) {
+          nbest += fin;
+          lo_best = fminf(lo_best, v[g][j]);
+        }
+      }
+      hi = pf_row16<1>(hi);
+      nfin = pf_row16<0>(nfin);
+      nbest = pf_row16<0>(nbest);
+      lo_fin = pf_row16<2>(lo_fin);
+      lo_best = pf_row16<2>(lo_best);
+      ok[g] = nfin >= a.topk;
+      lo[g] = a.topk <= 64 && nbest == 64 ? lo_best : lo_fin;
+      step[g] = ok[g] ? (hi - lo[g]) * (1.0f / 1024.0f) : 0.f;
+      lo[g] = ok[g] ? lo[g] : 0.f;
+      c[g] = 0;
+    }
+#pragma unroll
+    for (int bit = 9; bit >= 0; --bit) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int cc = c[g] | (1 << bit);
+        const float cand = fmaf((float)cc, step[g], lo[g]);
+        int n = 0;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) n += v[g][j] >= cand;
+        n = pf_row16<0>(n);
+        c[g] = n >= a.topk ? cc : c[g];
+      }
+    }
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int row = wave * 16 + 4 * g + (lane >> 4);
+      if (sub == 0) {
+        const float eps = i0 + row < a.n_q ? PF_EPS_COEF * qn_g[g] * knmax + 1e-30f : 0.f;
+        const float x = ok[g] ? fmaf((float)c[g], step[g], lo[g]) : -INFINITY;
+        // kept finite (at least the lowest float), so that the -inf of a masked score never passes
+        lthf[row] = fmaxf(x - 2.0f * eps, -0x1.fffffep+127f);
+      }
     }
   }
   if (tid < PF_ROWS) lcnt[tid] = 0u;
@@ -356,18 +445,20 @@ __global__ __launch_bounds__(512) void pf_scan_kernel(PfArgs a) {
 
   // ---- phase 2: every candidate key whose upper bound reaches the row's bound goes to the row's
   // list in global memory, with its score. A lane first gathers the test results of its 16
-  // registers into bit r of `bits`: the test x >= T is the sign of x - T (T finite, x finite or
-  // -inf), shifted in by v_alignbit; its 16 scores go to the wave's LDS stage. Then it takes its
-  // set bits one at a time: a slot from the row's LDS counter, (score read back from the stage,
-  // key position) into the slot. The lanes of a wave pass through that loop together as often as
-  // the busiest lane needs (a step has about one passing register per four lanes). Slots past the
-  // end are clamped onto the last one; a row whose count ends above LCAP takes the exact path.
-#define PF_EPI2(ACC, t)                                                                            \
+  // registers into bit r of `fail`'s complement: the test x >= T is the sign of x - T (T finite,
+  // x finite or -inf), shifted in by v_alignbit from register 15 down to 0; its 16 scores go to
+  // the wave's LDS stage. Then the lane takes its set bits one at a time: a slot from the row's LDS counter, (score read back from the stage, key
+  // position) into the slot. The lanes of a wave pass through that loop together as often as the
+  // busiest lane needs (a step has about one passing register per four lanes). Slots past the end
+  // are clamped onto the last one; a row whose count ends above LCAP takes the exact path.
+  uint32_t fail = 0u;
+#define PF_PART2(ACC, i)                                                                           \
   {                                                                                                \
-    uint32_t fail = 0u;                                                                            \
-    _Pragma("unroll") for (int r = 15; r >= 0; --r)                                                \
-      fail = __builtin_amdgcn_alignbit(fail, __float_as_uint(ACC[r] - thf[r]), 31);                \
-    PF_INTERLEAVE()                                                                                \
+    fail = __builtin_amdgcn_alignbit((i) == 0 ? 0u : fail, __float_as_uint(ACC[15 - (i)] - thf[15 - (i)]), 31); \
+    asm volatile("" : "+v"(fail));                                                                 \
+  }
+#define PF_POST2(ACC, t)                                                                           \
+  {                                                                                                \
     uint32_t bits = ~fail & 0xFFFFu;                                                               \
     _Pragma("unroll") for (int q4 = 0; q4 < 4; ++q4)                                               \
       sst[q4 * 64 + lane] = make_float4(ACC[4 * q4], ACC[4 * q4 + 1], ACC[4 * q4 + 2], ACC[4 * q4 + 3]); \
@@ -384,8 +475,8 @@ __global__ __launch_bounds__(512) void pf_scan_kernel(PfArgs a) {
   if (ntiles > 0) {
     PF_PROLOGUE(accA)
     for (int t = 0; t < ntiles; t += 2) {
-      PF_STEP(PF_EPI2, t, accA, accB, r00, r01)
-      PF_STEP(PF_EPI2, t + 1, accB, accA, r10, r11)
+      PF_STEP(PF_PART2, PF_POST2, t, accA, accB, r00, r01)
+      PF_STEP(PF_PART2, PF_POST2, t + 1, accB, accA, r10, r11)
     }
   }
 
@@ -401,9 +492,10 @@ __global__ __launch_bounds__(512) void pf_scan_kernel(PfArgs a) {
 #undef PF_MMA
 #undef PF_MASK
 #undef PF_STEP
-#undef PF_INTERLEAVE
-#undef PF_EPI1
-#undef PF_EPI2
+#undef PF_PART1
+#undef PF_POST1
+#undef PF_PART2
+#undef PF_POST2
 }
 
 // ---------------------------------------------------------------------------------------------
