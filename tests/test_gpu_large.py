@@ -53,6 +53,37 @@ def test_decode_merged_survivor_lists(ties):
     assert_out_close(out, ro, "bf16", f"merged ties={ties}")
 
 
+def test_group_and_ragged_with_merged_lists():
+    """The merge path under the shared selection (one set per kv head, G = 4) and under
+    per-sequence positions (two sequences of one kv head each, at different lengths)."""
+    torch = torch_cuda()
+    B, Hq, Hkv, n, d, W, K = 2, 4, 1, 700_001, 128, 64, 32
+    vals, store = random_case(1750, B, Hq, Hkv, n, d, "bf16")
+    dq, dk, dv = (to_device(x, "bf16") for x in store)
+    scale = 1.0 / np.sqrt(d)
+    say("group selection over merged lists")
+    out, sel, cnt = topo.topo_attn_decode(dq, dk, dv, W, K, scale, flags=topo.TOPO_FLAG_GROUP_SELECT)
+    torch.cuda.synchronize()
+    out, sel, cnt = out.cpu().numpy()[:, :, 0], sel.cpu().numpy()[:, :, 0], cnt.cpu().numpy()[:, :, 0]
+    ro, rs, rc = oracle.topo_attn_decode_group(*vals, W, K, float(np.float32(scale)))
+    assert_sets_equal(sel, cnt, rs, rc, "group merged")
+    assert_out_close(out, ro, "bf16", "group merged")
+    pos = [n - 1, 400_000]
+    say("ragged positions over merged lists", pos)
+    dpos = torch.tensor(pos, dtype=torch.int64, device="cuda")
+    out, sel, cnt = topo.topo_attn_decode_ragged(dq, dk, dv, dpos, W, K, scale)
+    torch.cuda.synchronize()
+    out, sel, cnt = out.cpu().numpy()[:, :, 0], sel.cpu().numpy()[:, :, 0], cnt.cpu().numpy()[:, :, 0]
+    del dq, dk, dv
+    torch.cuda.empty_cache()
+    q, k, v = vals
+    for b, p in enumerate(pos):
+        ro, rs, rc = oracle.topo_attn_decode(q[b:b + 1], k[b:b + 1, :, :p + 1], v[b:b + 1, :, :p + 1], W, K,
+                                             float(np.float32(scale)))
+        assert_sets_equal(sel[b:b + 1], cnt[b:b + 1], rs, rc, f"ragged merged b{b}")
+        assert_out_close(out[b:b + 1], ro, "bf16", f"ragged merged b{b}")
+
+
 def _device_cache(torch, n, d, seed, std):
     """(1, 1, n, d) bf16 cache of N(0, std^2) values, generated on the device in slices."""
     gen = torch.Generator(device="cuda")
