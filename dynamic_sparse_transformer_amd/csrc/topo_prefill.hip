@@ -809,17 +809,29 @@ __device__ void pf_row(const PfArgs& a, PfRowSmem* sm, size_t grow) {
   int c = 0;
   bool exact = false;
   if (a.topk > 0) {
-    const uint32_t cr = a.exact_all ? PF_OVERFLOW : a.w.cnt[grow];
+    // The count and the row's whole slot area (at most 128 entries, two per lane) are read
+    // together, so that the list costs one memory round trip; slots at or past the count hold
+    // stale entries and are ignored.
+    uint32_t cr = PF_OVERFLOW;
+    uint2 e0 = make_uint2(0u, 0u), e1 = e0;
+    if (!a.exact_all) {
+      const uint2* sv = a.w.surv + grow * (size_t)a.slot;
+      cr = a.w.cnt[grow];
+      if (lane < a.slot) e0 = sv[lane];
+      if (lane + 64 < a.slot) e1 = sv[lane + 64];
+    }
     exact = cr == PF_OVERFLOW;
     if (!exact) {
       c = (int)cr;
-      const uint2* sv = a.w.surv + grow * (size_t)a.slot;
       // positions come from the scan and are always keys of the cache; clamping only guards
       // the reads below. With bf16 inputs the scan's matrix-core scores come along.
-      for (int t = lane; t < c; t += 64) {
-        const uint2 e = sv[t];
-        sm->ridx[t] = (int32_t)min(e.y, (uint32_t)(a.n - 1));
-        if constexpr (BF16) sm->rs[t] = (double)__uint_as_float(e.x);
+      if (lane < c) {
+        sm->ridx[lane] = (int32_t)min(e0.y, (uint32_t)(a.n - 1));
+        if constexpr (BF16) sm->rs[lane] = (double)__uint_as_float(e0.x);
+      }
+      if (lane + 64 < c) {
+        sm->ridx[lane + 64] = (int32_t)min(e1.y, (uint32_t)(a.n - 1));
+        if constexpr (BF16) sm->rs[lane + 64] = (double)__uint_as_float(e1.x);
       }
     }
   }
@@ -1005,7 +1017,7 @@ __device__ void pf_row(const PfArgs& a, PfRowSmem* sm, size_t grow) {
 
   // ---- softmax over the set and the weighted V rows: lane group gq takes the entries
   // t = gq (mod RPI), each lane a 16-byte chunk of the row; then the groups are summed.
-  constexpr int U = 4;
+  constexpr int U = BF16 ? 17 : 4;  // V rows per lane group in flight together (bf16: the whole set for k <= 67)
   if constexpr (BF16) {
     // The window's part (m_w, Z_w, O_w) comes from pf_window; here the anchor and the top-k
     // (tidx / ts [0, nt), the anchor appended at nt), then the merge of the two parts:
@@ -1018,7 +1030,15 @@ __device__ void pf_row(const PfArgs& a, PfRowSmem* sm, size_t grow) {
       sm->ts[nt] = sm->rs[c];
     }
     __builtin_amdgcn_wave_barrier();
+    // the window's part and the first batch of V rows are requested before the weights are
+    // computed, so that their memory latency overlaps the softmax
     const float2 mz = a.win ? a.w.win_mz[grow] : make_float2(-INFINITY, 0.f);
+    uint4 x[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int t = u * RPI + gq;
+      x[u] = t < ne ? *(const uint4*)(vb + (size_t)sm->tidx[t] * RB + cc * 16) : make_uint4(0u, 0u, 0u, 0u);
+    }
     float zmax = mz.x;
     for (int t = lane; t < ne; t += 64) zmax = fmaxf(zmax, sc * (float)sm->ts[t]);
     zmax = wave_max_f32(zmax);
@@ -1046,14 +1066,18 @@ __device__ void pf_row(const PfArgs& a, PfRowSmem* sm, size_t grow) {
       }
     };
     for (int t0 = 0; t0 < ne; t0 += U * RPI) {
-      uint4 x[U];
+      if (t0 > 0) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int t = t0 + u * RPI + gq;
+          x[u] = t < ne ? *(const uint4*)(vb + (size_t)sm->tidx[t] * RB + cc * 16) : make_uint4(0u, 0u, 0u, 0u);
+        }
+      }
       float w[U];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int t = t0 + u * RPI + gq;
-        const bool ok = t < ne;
-        x[u] = ok ? *(const uint4*)(vb + (size_t)sm->tidx[t] * RB + cc * 16) : make_uint4(0u, 0u, 0u, 0u);
-        w[u] = ok ? (float)sm->ts[t] : 0.f;
+        w[u] = t < ne ? (float)sm->ts[t] : 0.f;
       }
       accumulate(x, w);
     }
