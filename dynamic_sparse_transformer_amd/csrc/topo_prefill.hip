@@ -799,7 +799,21 @@ __device__ void pf_row(const PfArgs& a, PfRowSmem* sm, size_t grow) {
   // error-bound inputs, requested early: |q| of the row and the largest |k| of the kv head
   const float qn_row = a.w.qn[grow];
   const float kn_max = __uint_as_float(a.w.knmax[(size_t)b * a.Hkv + g]);
-  for (int t = lane; t < D; t += 64) sm->qd[t] = load_elem_f64<BF16>(qrow, t);
+  // the float64 query (canonical scores) is filled where a path needs it: float32 inputs and
+  // the exact path always, the bf16 fast path only for a band to re-score
+  auto fill_qd = [&]() {
+    for (int t = lane; t < D; t += 64) sm->qd[t] = load_elem_f64<BF16>(qrow, t);
+    __builtin_amdgcn_wave_barrier();
+  };
+  // bf16: the anchor's key chunk and the row's query chunk for its float32 score, requested with
+  // the list so that both cost one memory round trip
+  uint4 k0v = make_uint4(0u, 0u, 0u, 0u), q0v = k0v;
+  if constexpr (BF16) {
+    k0v = *(const uint4*)(kb + cc * 16);
+    q0v = *(const uint4*)(qrow + cc * 16);
+  } else {
+    fill_qd();
+  }
 
   const int64_t w_lo = p - a.W + 1 > 0 ? p - a.W + 1 : 0;
   const int anchor = w_lo > 0 ? 1 : 0;
@@ -847,14 +861,13 @@ __device__ void pf_row(const PfArgs& a, PfRowSmem* sm, size_t grow) {
     // exact score). The anchor gets a float32 score here (LPR lanes, a 16-byte chunk each,
     // v_dot2_f32_bf16, summed across the lanes with DPP adds); it only enters the softmax.
     if (anchor) {
-      const uint4 qv = *(const uint4*)(qrow + cc * 16);
-      const uint4 x = *(const uint4*)(kb + cc * 16);
-      const float part = group_sum_f32<LPR>(dot_chunk_bf16(qv, x, 0.0f));
+      const float part = group_sum_f32<LPR>(dot_chunk_bf16(q0v, k0v, 0.0f));
       if (lane == 0) sm->rs[c] = (double)part;
     }
     __builtin_amdgcn_wave_barrier();
     const float eps = PF_EPS_COEF * qn_row * kn_max + 1e-30f;
     if (exact) {
+      fill_qd();
       nt = pf_exact_row<D, BF16>(sm, a, kb, p);
     } else if (c > a.topk) {
       // x_k = k-th largest score of the list; A = entries with s_mc >= x_k - 2 eps. Every
@@ -906,6 +919,7 @@ __device__ void pf_row(const PfArgs& a, PfRowSmem* sm, size_t grow) {
         if (bd0) sm->ridx[lanes_below(mb0)] = j0;
         if (bd1) sm->ridx[__popcll(mb0) + lanes_below(mb1)] = j1;
         __builtin_amdgcn_wave_barrier();
+        if (nb > 0) fill_qd();
         for (int t = lane; t < nb; t += 64)
           sm->rs[t] = canonical_score_row<BF16, D>(sm->qd, kb + (size_t)sm->ridx[t] * RB);
         __builtin_amdgcn_wave_barrier();
