@@ -1044,8 +1044,9 @@ __device__ void pf_row(const PfArgs& a, PfRowSmem* sm, size_t grow) {
       sm->ts[nt] = sm->rs[c];
     }
     __builtin_amdgcn_wave_barrier();
-    // the window's part and the first batch of V rows are requested before the weights are
-    // computed, so that their memory latency overlaps the softmax
+    // the window's part (maximum and sum, then its partial output) and the first batch of V rows
+    // are requested before the weights are computed, so that their memory latency overlaps the
+    // softmax
     const float2 mz = a.win ? a.w.win_mz[grow] : make_float2(-INFINITY, 0.f);
     uint4 x[U];
 #pragma unroll
@@ -1053,6 +1054,10 @@ __device__ void pf_row(const PfArgs& a, PfRowSmem* sm, size_t grow) {
       const int t = u * RPI + gq;
       x[u] = t < ne ? *(const uint4*)(vb + (size_t)sm->tidx[t] * RB + cc * 16) : make_uint4(0u, 0u, 0u, 0u);
     }
+    float4 wo[EPC / 4];
+#pragma unroll
+    for (int e = 0; e < EPC / 4; ++e)
+      wo[e] = a.win && gq == 0 ? ((const float4*)(a.w.win_o + grow * D + cc * EPC))[e] : make_float4(0.f, 0.f, 0.f, 0.f);
     float zmax = mz.x;
     for (int t = lane; t < ne; t += 64) zmax = fmaxf(zmax, sc * (float)sm->ts[t]);
     zmax = wave_max_f32(zmax);
@@ -1101,7 +1106,6 @@ __device__ void pf_row(const PfArgs& a, PfRowSmem* sm, size_t grow) {
       for (int e = 0; e < EPC; ++e) acc[e] += __shfl_xor(acc[e], o);
     if (gq == 0) {
       if (a.win) {
-        const float4* wo = (const float4*)(a.w.win_o + grow * D + cc * EPC);
 #pragma unroll
         for (int e = 0; e < EPC / 4; ++e) {
           const float4 o4 = wo[e];
