@@ -613,13 +613,46 @@ __global__ __launch_bounds__(256) void pf_window_kernel(PfArgs a) {
     }
 #pragma unroll
     for (int r = 0; r < 16; ++r) o[r] *= fr[r];
+    // P.V on the bf16 matrix cores: each float32 weight is split into three bf16 parts
+    // w = w1 + w2 + w3 (w1 = w with its low 16 bits cleared, w2 the same of w - w1, w3 = the
+    // rest, at most 8 significant bits; exact for w >= 2^-110, below which w3 may lose bits
+    // worth less than 2^-133, nothing next to the largest weight, 1), every product of a part
+    // and a bf16 V element is exact in float32, and the three products are accumulated in
+    // float32 (smallest part first). The 16
+    // keys of matrix instruction s are the keys of registers 8s .. 8s+7 (lane half h: keys
+    // 8(r/4) + 4h + r%4), in the same order in the weight (A) and V (B) operands.
     const unsigned char* vcol = &vt[buf][(4 * half) * STR + dim * 2];
+    float w[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const float w = S[r] == -INFINITY ? 0.f : __expf(S[r] - mnew);
-      zs += w;
-      const float v = __uint_as_float((uint32_t)*(const uint16_t*)(vcol + (8 * (r / 4) + (r % 4)) * STR) << 16);
-      o = __builtin_amdgcn_mfma_f32_32x32x2f32(w, v, o, 0, 0, 0);
+      w[r] = S[r] == -INFINITY ? 0.f : __expf(S[r] - mnew);
+      zs += w[r];
+    }
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+      uint32_t p1[4], p2[4], p3[4], vb4[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        uint32_t h1[2], h2[2], h3[2], vv[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const int r = 8 * s2 + 2 * j + e;
+          const float x = w[r];
+          h1[e] = __float_as_uint(x) & 0xFFFF0000u;
+          const float r1 = x - __uint_as_float(h1[e]);
+          h2[e] = __float_as_uint(r1) & 0xFFFF0000u;
+          h3[e] = __float_as_uint(r1 - __uint_as_float(h2[e]));
+          vv[e] = *(const uint16_t*)(vcol + (8 * (r / 4) + (r % 4)) * STR);
+        }
+        p1[j] = (h1[0] >> 16) | h1[1];
+        p2[j] = (h2[0] >> 16) | h2[1];
+        p3[j] = (h3[0] >> 16) | (h3[1] & 0xFFFF0000u);
+        vb4[j] = vv[0] | (vv[1] << 16);
+      }
+      const bf16x8_t vb = __builtin_bit_cast(bf16x8_t, make_uint4(vb4[0], vb4[1], vb4[2], vb4[3]));
+      o = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, make_uint4(p3[0], p3[1], p3[2], p3[3])), vb, o, 0, 0, 0);
+      o = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, make_uint4(p2[0], p2[1], p2[2], p2[3])), vb, o, 0, 0, 0);
+      o = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, make_uint4(p1[0], p1[1], p1[2], p1[3])), vb, o, 0, 0, 0);
     }
     if (u + 1 < ntk) PW_STORE(buf ^ 1)
     __syncthreads();
