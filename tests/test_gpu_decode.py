@@ -12,7 +12,7 @@ import pytest
 
 import dynamic_sparse_transformer_amd as topo
 import oracle
-from tests._util import (assert_out_close, assert_sets_equal, check_set_structure, to_device, torch_cuda)
+from tests._util import (assert_out_arith, assert_out_close, assert_sets_equal, check_set_structure, to_device, torch_cuda)
 from workloads import f32_to_bf16_bits, make_workload, spec
 
 pytestmark = pytest.mark.gpu
@@ -60,9 +60,13 @@ def compare_case(vals, store, dtype, W, K, scale, causal=True, q_pos=None, flags
         idx = tuple(np.array(heads).T)
         assert_sets_equal(sel[idx], cnt[idx], rs[idx], rc[idx], what)
         assert_out_close(out[idx], ro[idx], dtype, what)
+        if dtype == "bf16":
+            assert_out_arith(out[idx], ro[idx], what)
     else:
         assert_sets_equal(sel, cnt, rs, rc, what)
         assert_out_close(out, ro, dtype, what)
+        if dtype == "bf16":
+            assert_out_arith(out, ro, what)
     return out, sel, cnt
 
 
@@ -206,6 +210,8 @@ def _full_config(cfg, sample_heads):
     idx = tuple(np.array(sample_heads).T)
     assert_sets_equal(sel[idx], cnt[idx], rs[idx], rc[idx], s.name)
     assert_out_close(out[idx], ro[idx], s.dtype, s.name)
+    if s.dtype == "bf16":
+        assert_out_arith(out[idx], ro[idx], s.name)
     # planted keys are retrieved (synthetic needle retrieval)
     hits = [np.isin(w.planted[(b, h)], sel[b, h]).mean() for (b, h) in w.planted]
     say(f"config {cfg}: planted recall {np.mean(hits):.4f}")

@@ -11,7 +11,7 @@ import pytest
 
 import dynamic_sparse_transformer_amd as topo
 import oracle
-from tests._util import assert_out_close, assert_sets_equal, to_device, torch_cuda
+from tests._util import assert_out_arith, assert_out_close, assert_sets_equal, to_device, torch_cuda
 from workloads import bf16_bits_to_f32, f32_to_bf16_bits, make_workload
 
 pytestmark = pytest.mark.gpu
@@ -47,6 +47,8 @@ def compare(vals, out, sel, cnt, W, K, scale, dtype, what, q_pos=None, groups=No
         for h in range(g * G, (g + 1) * G):
             assert_sets_equal(sel[b, h], cnt[b, h], s_ref[b, h], c_ref[b, h], f"{what} b{b} h{h}")
             assert_out_close(out[b, h], o_ref[b, h], dtype, f"{what} b{b} h{h}")
+            if dtype == "bf16":
+                assert_out_arith(out[b, h], o_ref[b, h], f"{what} b{b} h{h}")
 
 
 CASES = [

@@ -20,7 +20,7 @@ import pytest
 
 import dynamic_sparse_transformer_amd as topo
 import oracle
-from tests._util import assert_out_close, assert_sets_equal, to_device, torch_cuda
+from tests._util import assert_out_arith, assert_out_close, assert_sets_equal, to_device, torch_cuda
 from tests.test_gpu_decode import random_case
 from workloads import bf16_bits_to_f32, f32_to_bf16_bits
 
@@ -51,6 +51,7 @@ def test_decode_merged_survivor_lists(ties):
     ro, rs, rc = oracle.topo_attn_decode(*vals, W, K, float(np.float32(scale)))
     assert_sets_equal(sel, cnt, rs, rc, f"merged ties={ties}")
     assert_out_close(out, ro, "bf16", f"merged ties={ties}")
+    assert_out_arith(out, ro, f"merged ties={ties}")
 
 
 def test_group_and_ragged_with_merged_lists():
@@ -179,6 +180,7 @@ def test_decode_beyond_4gib_offsets():
         assert cnt[0, h, 0] == len(C) and np.array_equal(sel[0, h, 0, :len(C)], C), f"set of head {h}"
         assert rc[0, 0] == len(C)
         assert_out_close(out[0, h, 0], ro[0, 0], "bf16", f"4GiB head {h}")
+        assert_out_arith(out[0, h, 0], ro[0, 0], f"4GiB head {h}")
     del kc, vc, dq
     torch.cuda.empty_cache()
 
@@ -219,5 +221,6 @@ def test_prefill_at_the_scan_byte_limit(side):
                                              float(np.float32(scale)))
         assert cnt[0, 0, i] == len(C) and np.array_equal(sel[0, 0, i, :len(C)], C), f"set of row {i}"
         assert_out_close(out[0, 0, i], ro[0, 0], "bf16", f"prefill {side} row {i}")
+        assert_out_arith(out[0, 0, i], ro[0, 0], f"prefill {side} row {i}")
     del kc, vc, dq
     torch.cuda.empty_cache()

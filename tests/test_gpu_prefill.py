@@ -12,7 +12,7 @@ import pytest
 
 import dynamic_sparse_transformer_amd as topo
 import oracle
-from tests._util import assert_out_close, assert_sets_equal, to_device, torch_cuda
+from tests._util import assert_out_arith, assert_out_close, assert_sets_equal, to_device, torch_cuda
 from workloads import bf16_bits_to_f32, f32_to_bf16_bits, make_workload
 
 pytestmark = pytest.mark.gpu
@@ -40,6 +40,8 @@ def compare_rows(vals, out, sel, cnt, rows, W, K, scale, causal, q_pos0, dtype, 
             ref_sel[:C.size] = C
             assert_sets_equal(sel[b, h, i], np.int32(cnt[b, h, i]), ref_sel, np.int32(C.size), f"{what} b{b} h{h} i{i}")
             assert_out_close(out[b, h, i], o, dtype, f"{what} b{b} h{h} i{i}")
+            if dtype == "bf16":
+                assert_out_arith(out[b, h, i], o, f"{what} b{b} h{h} i{i}")
 
 
 def random_prefill(seed, B, Hq, Hkv, n, n_q, d, dtype, ties=False):

@@ -12,7 +12,7 @@ import pytest
 
 import dynamic_sparse_transformer_amd as topo
 import oracle
-from tests._util import assert_out_close, assert_sets_equal, to_device, torch_cuda
+from tests._util import assert_out_arith, assert_out_close, assert_sets_equal, to_device, torch_cuda
 from workloads import bf16_bits_to_f32, f32_to_bf16_bits
 
 pytestmark = pytest.mark.gpu
@@ -41,6 +41,8 @@ def check_against_oracle(vals, pos, out, sel, cnt, W, K, scale, dtype, what):
         for h in range(q.shape[1]):
             assert_sets_equal(sel[b, h], cnt[b, h], s_ref[0, h], c_ref[0, h], f"{what} b{b} p{p} h{h}")
             assert_out_close(out[b, h], o_ref[0, h], dtype, f"{what} b{b} p{p} h{h}")
+            if dtype == "bf16":
+                assert_out_arith(out[b, h], o_ref[0, h], f"{what} b{b} p{p} h{h}")
 
 
 # (seed, B, Hq, Hkv, n, d, dtype, positions, W, k): positions cover the full cache, a mid-length
