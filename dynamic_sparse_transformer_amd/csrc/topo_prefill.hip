@@ -500,77 +500,89 @@ __global__ __launch_bounds__(512) void pf_scan_kernel(PfArgs a) {
 
 // ---------------------------------------------------------------------------------------------
 // pf_window: the window's share of the softmax of every query row (bf16 inputs), on the matrix
-// cores. One block per (b, h, 32 consecutive query rows), one wave per 32 output dimensions.
-// The window keys of the block, [max(0, p_first - W + 1), p_last], go in tiles of 32 keys,
-// staged in LDS (K and V, two buffers; tile u+1 is loaded while tile u is used). Per tile:
-// S' = K_tile . Q^T with v_mfma_f32_32x32x16_bf16 (A = key rows, B = query rows), so lane l
-// holds query row l % 32 and, in register r, key 8*(r/4) + 4*(l/32) + r%4 of the tile; keys
-// outside the row's window [p - W + 1, p] are masked. The row's running maximum m, sum Z and
-// output O are updated online: factor exp(m_old - m_new) on Z and O, weights w = exp(z - m_new),
-// and O += w V with v_mfma_f32_32x32x2_f32: register r's weight is the A operand of query row
-// l % 32 and key (r, l / 32), the B operand is that key's V element at the wave's dimension
-// 32 * wave + l % 32 (the bf16 value widened to float32, exactly). The output tile's rows are
-// 8*(r/4) + 4*(l/32) + r%4, so their factors are read back from LDS. Every product is a float32
-// product of the float32 weight and the exact V value, as in the per-row path.
+// cores. One block per (b, h, 64 consecutive query rows), four waves: wave w takes the 32 rows of
+// row tile w / 2 and half w % 2 of the output dimensions. The window keys of the block,
+// [max(0, p_first - W + 1), p_last], go in tiles of 32 keys, staged in LDS (K and V, two buffers;
+// tile u+1 is loaded while tile u is used). Per tile: S' = K_tile . Q^T with
+// v_mfma_f32_32x32x16_bf16 (A = key rows, B = query rows), so lane l holds query row l % 32 of
+// the wave's row tile and, in register r, key 8*(r/4) + 4*(l/32) + r%4 of the tile; keys outside
+// the row's window [p - W + 1, p] are masked. (The two waves of a row tile compute the same
+// scores; each needs them in its registers.) The row's running maximum m, sum Z and output O
+// are updated online: factor exp(m_old - m_new) on Z and O, weights w = exp(z - m_new). O += w V
+// on the bf16 matrix cores: each float32 weight is split into three bf16 parts w = w1 + w2 + w3
+// (w1 = w with its low 16 bits cleared, w2 the same of w - w1, w3 = the rest, at most 8
+// significant bits; exact for w >= 2^-110, below which w3 may lose bits worth less than 2^-133,
+// nothing next to the largest weight, 1), every product of a part and a bf16 V element is exact
+// in float32, and the three products are accumulated in float32 (smallest part first). The 16
+// keys of matrix instruction s are the keys of registers 8s .. 8s+7 (lane half h: keys
+// 8(r/4) + 4h + r%4), in the same order in the weight (A) and V (B) operands. The output tiles'
+// rows are 8*(r/4) + 4*(l/32) + r%4, so their factors are read back from LDS.
 template <int D>
 __global__ __launch_bounds__(256) void pf_window_kernel(PfArgs a) {
-  constexpr int RB = D * 2, STEPS = D / 16, NW = D / 32, NT = NW * 64;
+  constexpr int RB = D * 2, STEPS = D / 16, NW = D / 32, NWD = NW / 2;  // dim tiles per wave
   constexpr int STR = RB + 16;         // padded LDS row (K and V)
   constexpr int CPR = RB / 16;         // 16-byte chunks per key row
-  static_assert(2 * NT == 32 * CPR, "tile staging: two 16-byte chunks of K and of V per thread");
+  constexpr int CPT = 32 * CPR / 256;  // chunks of K (and of V) per thread and tile
+  static_assert(NWD >= 1 && CPT >= 1, "window tiles");
   __shared__ __align__(16) unsigned char kt[2][32 * STR];
   __shared__ __align__(16) unsigned char vt[2][32 * STR];
-  __shared__ __align__(16) float alpha[NW][32];
+  __shared__ __align__(16) float alpha[4][32];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int m = lane & 31, half = lane >> 5;
-  const int64_t nrb = (a.n_q + 31) / 32;
+  const int m = lane & 31, half = lane >> 5, rt = wave >> 1, dh = wave & 1;
+  const int64_t nrb = (a.n_q + 63) / 64;
   const int64_t job = xcd_job(blockIdx.x, nrb * a.Hq * (a.rows / (a.n_q * a.Hq)));
   const int bh = (int)(job / nrb);
-  const int64_t i0 = (job - (int64_t)bh * nrb) * 32;
+  const int64_t i0 = (job - (int64_t)bh * nrb) * 64;
   const int b = bh / a.Hq, h = bh - b * a.Hq, g = h / a.G;
   const unsigned char* kb = a.k + ((size_t)b * a.Hkv + g) * (size_t)a.n * RB;
   const unsigned char* vb = a.v + ((size_t)b * a.Hkv + g) * (size_t)a.n * RB;
 
+  const int64_t iw = i0 + 32 * rt + m;  // the lane's query row
   bf16x8_t qf[STEPS];
   {
-    const int64_t iq = min(i0 + m, a.n_q - 1);
+    const int64_t iq = min(iw, a.n_q - 1);
     const unsigned char* qrow = a.q + ((size_t)bh * a.n_q + iq) * RB;
 #pragma unroll
     for (int st = 0; st < STEPS; ++st) qf[st] = __builtin_bit_cast(bf16x8_t, *(const uint4*)(qrow + st * 32 + half * 16));
   }
   const int64_t key_lo = a.q_pos0 + i0 - a.W + 1 > 0 ? a.q_pos0 + i0 - a.W + 1 : 0;
-  const int64_t p_last = a.q_pos0 + min(i0 + 31, a.n_q - 1);
+  const int64_t p_last = a.q_pos0 + min(i0 + 63, a.n_q - 1);
   const int ntk = (int)((p_last - key_lo) / 32) + 1;
   // the lane's row relative to key_lo (rows past n_q get -1: no key passes)
-  const int prel = i0 + m < a.n_q ? (int)(a.q_pos0 + i0 + m - key_lo) : -1;
+  const int prel = iw < a.n_q ? (int)(a.q_pos0 + iw - key_lo) : -1;
   const float sc = (float)a.scale;
-  const int dim = 32 * wave + m;
 
-  // thread tid stages chunks tid and tid + NT of the tile: key row c / CPR, chunk c % CPR
-  const int c0 = tid, c1 = tid + NT;
-  uint4 kr0, kr1, vr0, vr1;
+  // thread tid stages chunks tid and (CPT = 2) tid + 256 of the tile: key row c / CPR, chunk
+  // c % CPR (scalar registers: a staging array would go to scratch memory)
+  static_assert(CPT <= 2, "window staging");
+  const int c0 = tid, c1 = tid + 256;
+  uint4 kr0, kr1 = make_uint4(0u, 0u, 0u, 0u), vr0, vr1 = kr1;
 #define PW_LOAD(u)                                                                                 \
   {                                                                                                \
     const int64_t j0 = min(key_lo + 32 * (u) + c0 / CPR, a.n - 1);                                 \
-    const int64_t j1 = min(key_lo + 32 * (u) + c1 / CPR, a.n - 1);                                 \
     kr0 = *(const uint4*)(kb + (size_t)j0 * RB + (c0 % CPR) * 16);                                 \
     vr0 = *(const uint4*)(vb + (size_t)j0 * RB + (c0 % CPR) * 16);                                 \
-    kr1 = *(const uint4*)(kb + (size_t)j1 * RB + (c1 % CPR) * 16);                                 \
-    vr1 = *(const uint4*)(vb + (size_t)j1 * RB + (c1 % CPR) * 16);                                 \
+    if (CPT > 1) {                                                                                 \
+      const int64_t j1 = min(key_lo + 32 * (u) + c1 / CPR, a.n - 1);                               \
+      kr1 = *(const uint4*)(kb + (size_t)j1 * RB + (c1 % CPR) * 16);                               \
+      vr1 = *(const uint4*)(vb + (size_t)j1 * RB + (c1 % CPR) * 16);                               \
+    }                                                                                              \
   }
 #define PW_STORE(buf)                                                                              \
   {                                                                                                \
     *(uint4*)&kt[buf][(c0 / CPR) * STR + (c0 % CPR) * 16] = kr0;                                   \
     *(uint4*)&vt[buf][(c0 / CPR) * STR + (c0 % CPR) * 16] = vr0;                                   \
-    *(uint4*)&kt[buf][(c1 / CPR) * STR + (c1 % CPR) * 16] = kr1;                                   \
-    *(uint4*)&vt[buf][(c1 / CPR) * STR + (c1 % CPR) * 16] = vr1;                                   \
+    if (CPT > 1) {                                                                                 \
+      *(uint4*)&kt[buf][(c1 / CPR) * STR + (c1 % CPR) * 16] = kr1;                                 \
+      *(uint4*)&vt[buf][(c1 / CPR) * STR + (c1 % CPR) * 16] = vr1;                                 \
+    }                                                                                              \
   }
   PW_LOAD(0)
   PW_STORE(0)
   __syncthreads();
 
   float mrun = -INFINITY, zs = 0.f;
-  f32x16_t o = f32x16_t{};
+  f32x16_t o0 = f32x16_t{}, o1 = f32x16_t{};  // output tiles t = 0, 1 (o1 unused when NWD = 1)
   for (int u = 0; u < ntk; ++u) {
     const int buf = u & 1;
     if (u + 1 < ntk) PW_LOAD(u + 1)
@@ -612,16 +624,10 @@ __global__ __launch_bounds__(256) void pf_window_kernel(PfArgs a) {
       fr[4 * q4 + 3] = x.w;
     }
 #pragma unroll
-    for (int r = 0; r < 16; ++r) o[r] *= fr[r];
-    // P.V on the bf16 matrix cores: each float32 weight is split into three bf16 parts
-    // w = w1 + w2 + w3 (w1 = w with its low 16 bits cleared, w2 the same of w - w1, w3 = the
-    // rest, at most 8 significant bits; exact for w >= 2^-110, below which w3 may lose bits
-    // worth less than 2^-133, nothing next to the largest weight, 1), every product of a part
-    // and a bf16 V element is exact in float32, and the three products are accumulated in
-    // float32 (smallest part first). The 16
-    // keys of matrix instruction s are the keys of registers 8s .. 8s+7 (lane half h: keys
-    // 8(r/4) + 4h + r%4), in the same order in the weight (A) and V (B) operands.
-    const unsigned char* vcol = &vt[buf][(4 * half) * STR + dim * 2];
+    for (int r = 0; r < 16; ++r) {
+      o0[r] *= fr[r];
+      if (NWD > 1) o1[r] *= fr[r];
+    }
     float w[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
@@ -630,29 +636,43 @@ __global__ __launch_bounds__(256) void pf_window_kernel(PfArgs a) {
     }
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2) {
-      uint32_t p1[4], p2[4], p3[4], vb4[4];
+      uint32_t p1[4], p2[4], p3[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        uint32_t h1[2], h2[2], h3[2], vv[2];
+        uint32_t h1[2], h2[2], h3[2];
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
-          const int r = 8 * s2 + 2 * j + e;
-          const float x = w[r];
+          const float x = w[8 * s2 + 2 * j + e];
           h1[e] = __float_as_uint(x) & 0xFFFF0000u;
           const float r1 = x - __uint_as_float(h1[e]);
           h2[e] = __float_as_uint(r1) & 0xFFFF0000u;
           h3[e] = __float_as_uint(r1 - __uint_as_float(h2[e]));
-          vv[e] = *(const uint16_t*)(vcol + (8 * (r / 4) + (r % 4)) * STR);
         }
         p1[j] = (h1[0] >> 16) | h1[1];
         p2[j] = (h2[0] >> 16) | h2[1];
         p3[j] = (h3[0] >> 16) | (h3[1] & 0xFFFF0000u);
-        vb4[j] = vv[0] | (vv[1] << 16);
       }
-      const bf16x8_t vb = __builtin_bit_cast(bf16x8_t, make_uint4(vb4[0], vb4[1], vb4[2], vb4[3]));
-      o = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, make_uint4(p3[0], p3[1], p3[2], p3[3])), vb, o, 0, 0, 0);
-      o = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, make_uint4(p2[0], p2[1], p2[2], p2[3])), vb, o, 0, 0, 0);
-      o = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, make_uint4(p1[0], p1[1], p1[2], p1[3])), vb, o, 0, 0, 0);
+      const bf16x8_t a1 = __builtin_bit_cast(bf16x8_t, make_uint4(p1[0], p1[1], p1[2], p1[3]));
+      const bf16x8_t a2 = __builtin_bit_cast(bf16x8_t, make_uint4(p2[0], p2[1], p2[2], p2[3]));
+      const bf16x8_t a3 = __builtin_bit_cast(bf16x8_t, make_uint4(p3[0], p3[1], p3[2], p3[3]));
+#pragma unroll
+      for (int t = 0; t < NWD; ++t) {
+        const unsigned char* vcol = &vt[buf][(4 * half) * STR + (32 * (dh * NWD + t) + m) * 2];
+        uint32_t vb4[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int r0 = 8 * s2 + 2 * j;
+          const uint32_t v0 = *(const uint16_t*)(vcol + (8 * (r0 / 4) + (r0 % 4)) * STR);
+          const uint32_t v1 = *(const uint16_t*)(vcol + (8 * ((r0 + 1) / 4) + ((r0 + 1) % 4)) * STR);
+          vb4[j] = v0 | (v1 << 16);
+        }
+        const bf16x8_t vbf = __builtin_bit_cast(bf16x8_t, make_uint4(vb4[0], vb4[1], vb4[2], vb4[3]));
+        f32x16_t ot = t == 0 ? o0 : o1;
+        ot = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a3, vbf, ot, 0, 0, 0);
+        ot = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a2, vbf, ot, 0, 0, 0);
+        ot = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, vbf, ot, 0, 0, 0);
+        if (t == 0) o0 = ot; else o1 = ot;
+      }
     }
     if (u + 1 < ntk) PW_STORE(buf ^ 1)
     __syncthreads();
@@ -661,13 +681,19 @@ __global__ __launch_bounds__(256) void pf_window_kernel(PfArgs a) {
 #undef PW_LOAD
 #undef PW_STORE
 
-  // O_w: register r holds query row 8*(r/4) + 4*half + r%4, dimension `dim`
+  // O_w: register r of tile t holds query row 32 rt + 8*(r/4) + 4*half + r%4 of the block and
+  // dimension 32 (dh NWD + t) + m
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int64_t i = i0 + 8 * (r / 4) + 4 * half + (r % 4);
-    if (i < a.n_q) a.w.win_o[((size_t)bh * a.n_q + i) * D + dim] = o[r];
+  for (int t = 0; t < NWD; ++t) {
+    const int dim = 32 * (dh * NWD + t) + m;
+    const f32x16_t ot = t == 0 ? o0 : o1;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int64_t i = i0 + 32 * rt + 8 * (r / 4) + 4 * half + (r % 4);
+      if (i < a.n_q) a.w.win_o[((size_t)bh * a.n_q + i) * D + dim] = ot[r];
+    }
   }
-  if (wave == 0 && half == 0 && i0 + m < a.n_q) a.w.win_mz[(size_t)bh * a.n_q + i0 + m] = make_float2(mrun, zs);
+  if (dh == 0 && half == 0 && iw < a.n_q) a.w.win_mz[(size_t)bh * a.n_q + iw] = make_float2(mrun, zs);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -1239,7 +1265,7 @@ static hipError_t launch_pf_t(const PrefillLaunch& L, const PfArgs& pa, hipStrea
   if (L.ev_scan_end) (void)hipEventRecord(L.ev_scan_end, s);
   if constexpr (BF16) {
     if (pa.win) {
-      hipLaunchKernelGGL((pf_window_kernel<D>), dim3((unsigned)((L.n_q + 31) / 32 * L.B * L.Hq)), dim3(D / 32 * 64), 0, s,
+      hipLaunchKernelGGL((pf_window_kernel<D>), dim3((unsigned)((L.n_q + 63) / 64 * L.B * L.Hq)), dim3(256), 0, s,
                          pa);
       e = hipGetLastError();
       if (e != hipSuccess) return e;
