@@ -518,7 +518,7 @@ __global__ __launch_bounds__(512) void pf_scan_kernel(PfArgs a) {
 // 8(r/4) + 4h + r%4), in the same order in the weight (A) and V (B) operands. The output tiles'
 // rows are 8*(r/4) + 4*(l/32) + r%4, so their factors are read back from LDS.
 template <int D>
-__global__ __launch_bounds__(256) void pf_window_kernel(PfArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void pf_window_kernel(PfArgs a) {
   constexpr int RB = D * 2, STEPS = D / 16, NW = D / 32, NWD = NW / 2;  // dim tiles per wave
   constexpr int STR = RB + 16;         // padded LDS row (K and V)
   constexpr int CPR = RB / 16;         // 16-byte chunks per key row
