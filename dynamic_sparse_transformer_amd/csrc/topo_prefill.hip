@@ -291,15 +291,19 @@ __global__ __launch_bounds__(512) void pf_scan_kernel(PfArgs a) {
 // 1 <= j < n, the row exists, and dr >= W (j before the window) or, without the causal mask,
 // dr < 0 (j after p).
   const int rows_valid = (int)min((int64_t)PF_ROWS, a.n_q - i0);
+// (Positions fit in 32 bits here: the scan runs only when n * RB < 2^31. The tests combine with
+// & and |, so that the 16 selects need no branches.)
+  const int p_first32 = (int)p_first, rv_ = rows_valid - row_base;
+  const bool ncausal_ = !a.causal;
 #define PF_MASK(ACC, t)                                                                            \
   if (!PF_INTERIOR(t)) {                                                                           \
-    const int64_t j_ = (int64_t)(t) * PF_KEYS + kq * 32 + m;                                       \
-    const int64_t dl64 = p_first + row_base - j_;                                                  \
-    const int dl = (int)(dl64 > (1 << 30) ? (1 << 30) : (dl64 < -(1 << 30) ? -(1 << 30) : dl64));  \
-    const bool jok = j_ >= 1 && j_ < a.n;                                                          \
+    const int j_ = (t) * PF_KEYS + kq * 32 + m;                                                    \
+    const int dl = p_first32 + row_base - j_;                                                      \
+    const bool jok = (j_ >= 1) & (j_ < n);                                                         \
+    const int wl = a.W - dl;                                                                       \
     _Pragma("unroll") for (int r = 0; r < 16; ++r) {                                               \
       const int o = 8 * (r / 4) + (r % 4);                                                         \
-      const bool cand = jok && row_base + o < rows_valid && (dl + o >= a.W || (!a.causal && dl + o < 0)); \
+      const bool cand = jok & (o < rv_) & ((o >= wl) | (ncausal_ & (o < -dl)));                    \
       ACC[r] = cand ? ACC[r] : -INFINITY;                                                          \
     }                                                                                              \
   }
