@@ -21,6 +21,10 @@
  *            score first, on equal scores the lower position first. If there are at most k
  *            candidates, all of them are taken.
  *   softmax  float64 on z_j = softmax_scale * s_j; the output is rounded once to float32.
+ *            Exception: the prefill with bfloat16 inputs computes the logits, the softmax and
+ *            the V sum in float32 (products of bfloat16 values exact; the set is still the one
+ *            the score definition above gives), agreeing with the float64 definition to a few
+ *            float32 roundings of the output's scale.
  *   GQA      query head h reads kv head h / (Hq / Hkv) and selects its own set.
  *   visible  causal: positions 0..p; otherwise 0..n_ctx-1 (the window still ends at p).
  *
