@@ -51,7 +51,7 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 // Workspace of the certified decode: the decode's, then (with the dense fallback) the dense
 // attention's partials.
 size_t certified_workspace_bytes(const topo_params_t* p) {
-  size_t b = align256(topo::decode_workspace_bytes(p->B, p->Hq, decode_geom(p), p->k));
+  size_t b = align256(topo::decode_workspace_bytes(p->B, p->Hq, decode_geom(p), p->k, p->d, p->dtype == TOPO_BF16));
   if (p->flags & TOPO_FLAG_DENSE_FALLBACK) b += topo::dense_workspace_bytes(p->B, p->Hq, 1, p->n_ctx, p->d);
   return b;
 }
@@ -75,7 +75,7 @@ int decode_like(const topo_params_t* p, const void* q, const void* k, const void
   if (!softmax && (!sel_idx || !sel_count)) return TOPO_EINVAL;
   if ((sel_idx && !aligned16(sel_idx)) || (sel_count && !aligned16(sel_count))) return TOPO_EINVAL;
   const topo::QueryGeom g = pos ? ragged_sizes_geom(p) : decode_geom(p);
-  const size_t need = rho ? certified_workspace_bytes(p) : topo::decode_workspace_bytes(p->B, p->Hq, g, p->k);
+  const size_t need = rho ? certified_workspace_bytes(p) : topo::decode_workspace_bytes(p->B, p->Hq, g, p->k, p->d, p->dtype == TOPO_BF16);
   if (!ws || ws_bytes < need || !aligned16(ws)) return TOPO_EWORKSPACE;
 
   topo::DecodeLaunch L{};
@@ -111,7 +111,7 @@ int decode_like(const topo_params_t* p, const void* q, const void* k, const void
     D.k = k;
     D.v = v;
     D.out = out;
-    D.ws = (char*)ws + align256(topo::decode_workspace_bytes(p->B, p->Hq, g, p->k));
+    D.ws = (char*)ws + align256(topo::decode_workspace_bytes(p->B, p->Hq, g, p->k, p->d, p->dtype == TOPO_BF16));
     D.B = p->B;
     D.Hq = p->Hq;
     D.Hkv = p->Hkv;
@@ -180,11 +180,11 @@ size_t topo_workspace_bytes(const topo_params_t* p, int op) {
   switch (op) {
     case TOPO_OP_DECODE:
       if (p->n_q != 1) return 0;
-      return topo::decode_workspace_bytes(p->B, p->Hq, decode_geom(p), p->k);
+      return topo::decode_workspace_bytes(p->B, p->Hq, decode_geom(p), p->k, p->d, p->dtype == TOPO_BF16);
     case TOPO_OP_PREFILL:
       return topo::prefill_workspace_bytes(p->B, p->Hq, p->n_q, p->n_ctx, p->d, p->W, p->k);
     case TOPO_OP_SELECT:
-      if (p->n_q == 1) return topo::decode_workspace_bytes(p->B, p->Hq, decode_geom(p), p->k);
+      if (p->n_q == 1) return topo::decode_workspace_bytes(p->B, p->Hq, decode_geom(p), p->k, p->d, p->dtype == TOPO_BF16);
       return topo::prefill_workspace_bytes(p->B, p->Hq, p->n_q, p->n_ctx, p->d, p->W, p->k);
     case TOPO_OP_DENSE:
       return topo::dense_workspace_bytes(p->B, p->Hq, p->n_q, p->n_ctx, p->d);
@@ -193,7 +193,7 @@ size_t topo_workspace_bytes(const topo_params_t* p, int op) {
       return certified_workspace_bytes(p);
     case TOPO_OP_DECODE_RAGGED:
       if (p->n_q != 1 || p->causal != 1) return 0;
-      return topo::decode_workspace_bytes(p->B, p->Hq, ragged_sizes_geom(p), p->k);
+      return topo::decode_workspace_bytes(p->B, p->Hq, ragged_sizes_geom(p), p->k, p->d, p->dtype == TOPO_BF16);
     default:
       return 0;
   }

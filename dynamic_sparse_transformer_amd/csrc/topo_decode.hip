@@ -7,14 +7,17 @@
 // only (fr page, technical summary §3).
 //
 // Three launches per call:
-//   decode_init    zero the per-head state.
+//   decode_window  the window's share of the softmax per (batch, query head), in parts of a few
+//                  dozen rows (float64), and the clearing of the per-head scan state
+//                  (decode_init clears it alone when no softmax is asked for).
 //   kscan          stream K once per (batch, kv head) for all G query heads of the group
 //                  (HBM bound). Fast float32 scores with a proven error bound; every wave keeps
-//                  the keys that could still be in the top-k of its run of 1024 keys, raises a
+//                  the keys that could still be in the top-k of its run of 512 keys, raises a
 //                  shared per-head threshold, and appends the survivors to a per-head list.
 //   decode_finish  per (batch, query head): exact k-th threshold over the survivors, float64
 //                  re-scoring of the short list, exact top-k by (score desc, position asc), set
-//                  assembly, float64 softmax and V reduction over the set.
+//                  assembly, float64 softmax and V reduction over the anchor and the top-k,
+//                  combined with decode_window's records.
 #include "topo_device.h"
 #include "topo_internal.h"
 
@@ -70,13 +73,22 @@ static int survivor_levels(int64_t nblk0, int64_t slot, int64_t (&nblk)[MAX_LEVE
   return L;
 }
 
-size_t decode_workspace_bytes(int32_t B, int32_t Hq, const QueryGeom& g, int32_t k) {
+// Window rows per decode_window block: four rows per group of RB / 16 lanes of its 256 threads.
+static int window_rows(int32_t d, int32_t bf16) { return 4 * (256 / (d * (bf16 ? 2 : 4) / 16)); }
+// decode_window blocks (records) per (batch, query head): enough for the longest window.
+static int64_t window_parts(const QueryGeom& g, int32_t d, int32_t bf16) {
+  const int64_t nwin = g.p - g.w_lo + 1, wr = window_rows(d, bf16);
+  return nwin > 0 ? (nwin + wr - 1) / wr : 0;
+}
+
+size_t decode_workspace_bytes(int32_t B, int32_t Hq, const QueryGeom& g, int32_t k, int32_t d, int32_t bf16) {
   const size_t heads = (size_t)B * Hq;
   const int64_t slot = scan_slot(k);
   int64_t nb[MAX_LEVELS];
   // sized for one run per block: the most blocks, so any run count chosen at launch fits
   const int L = survivor_levels(scan_blocks(g, 1), slot, nb);
   size_t bytes = align256(heads * sizeof(HeadState));
+  bytes += align256(heads * (size_t)window_parts(g, d, bf16) * (size_t)(d + 2) * sizeof(double));
   for (int l = 0; l < L; ++l)
     bytes += 2 * align256(heads * (size_t)nb[l] * 4) + align256(heads * (size_t)nb[l] * (size_t)slot * sizeof(uint2));
   return bytes;
@@ -85,12 +97,15 @@ size_t decode_workspace_bytes(int32_t B, int32_t Hq, const QueryGeom& g, int32_t
 void decode_carve(void* ws, int32_t B, int32_t Hq, const QueryGeom& g, int32_t k, DecodeLaunch& L) {
   const size_t heads = (size_t)B * Hq;
   L.slot = scan_slot(k);
+  L.wstride = window_parts(g, L.d, L.bf16);
   const int GT = L.G >= 4 ? 4 : L.G;
   L.runs = scan_runs(g, (int64_t)L.B * L.Hkv * ((L.G + GT - 1) / GT));
   L.nlevels = survivor_levels(scan_blocks(g, L.runs), L.slot, L.nblk);
   char* p = (char*)ws;
   L.st = (HeadState*)p;
   p += align256(heads * sizeof(HeadState));
+  L.wrec = (double*)p;
+  p += align256(heads * (size_t)L.wstride * (size_t)(L.d + 2) * sizeof(double));
   for (int l = 0; l < L.nlevels; ++l) {
     L.blk_cnt[l] = (uint32_t*)p;
     p += align256(heads * (size_t)L.nblk[l] * 4);
@@ -101,11 +116,148 @@ void decode_carve(void* ws, int32_t B, int32_t Hq, const QueryGeom& g, int32_t k
   }
 }
 
+// Geometry of batch element b's query from its position pos[b] (clamped into the cache; causal).
+__device__ __forceinline__ QueryGeom ragged_geom(const int64_t* pos, int b, int64_t n, int32_t W) {
+  const int64_t p = pos[b];
+  return make_geom(p < 0 ? 0 : (p > n - 1 ? n - 1 : p), n, W, true);
+}
+
 __global__ void decode_init_kernel(HeadState* st, int nheads) {
   int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i < nheads) {
     st[i].theta = 0u;
     st[i].overflow = 0u;
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// decode_window: the window's share of the softmax, before the key scan (it needs only the query
+// and the cache). Block (j, bh) takes window rows [j * WR, (j + 1) * WR) of query head bh (the
+// window is the W positions up to p; fr page, technical summary §3, the softmax over the set) and
+// writes one record: O_j = sum_r exp(z_r - m_j) v_r (d values), m_j = max_r z_r and
+// Z_j = sum_r exp(z_r - m_j), with z_r = scale * q.k_r in float64 (an empty part writes m_j = -inf,
+// Z_j = 0, O_j = 0). The finishing kernel combines the records with the rest of the set. Block
+// (0, 0) also clears the per-head scan state, the job of decode_init when this kernel runs.
+// 256 threads: groups of LPR = RB / 16 lanes hold one row each (a 16-byte chunk per lane), four
+// rows per group; the K and V chunks of all of them are requested at once.
+struct WindowArgs {
+  const unsigned char* q;
+  const unsigned char* k;
+  const unsigned char* v;
+  HeadState* st;
+  double* rec;       // [B * Hq][rstride][D + 2]
+  const int64_t* pos;  // may be null: causal query position of each batch element
+  int64_t n, p, w_lo, rstride;
+  int32_t Hq, Hkv, G, W, nheads;
+  double scale;
+};
+
+template <int D, bool BF16>
+__global__ __launch_bounds__(256) void decode_window_kernel(WindowArgs a) {
+  constexpr int RB = D * (BF16 ? 2 : 4), LPR = RB / 16, RPP = 256 / LPR, U = 4, EPC = BF16 ? 8 : 4;
+  constexpr int WR = U * RPP;
+  __shared__ double red[4][D];
+  __shared__ double scr[4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (blockIdx.x == 0 && blockIdx.y == 0) {
+    for (int i = tid; i < a.nheads; i += 256) {
+      a.st[i].theta = 0u;
+      a.st[i].overflow = 0u;
+    }
+  }
+  const int bh = blockIdx.y, part = blockIdx.x;
+  const int b = bh / a.Hq, h = bh - b * a.Hq, g = h / a.G;
+  int64_t p = a.p, w_lo = a.w_lo;
+  if (a.pos) {
+    const QueryGeom gq = ragged_geom(a.pos, b, a.n, a.W);
+    p = gq.p;
+    w_lo = gq.w_lo;
+  }
+  const int nwin = (int)(p - w_lo + 1);
+  const unsigned char* kb = a.k + ((size_t)b * a.Hkv + g) * (size_t)a.n * RB;
+  const unsigned char* vb = a.v + ((size_t)b * a.Hkv + g) * (size_t)a.n * RB;
+  const int rsub = tid / LPR, cc = tid % LPR;
+  // every load first: the query chunk, then the K and V chunks of the four rows (row indexes
+  // clamped into the cache; rows past the window are ignored below)
+  const uint4 qc = *(const uint4*)(a.q + (size_t)bh * RB + cc * 16);
+  uint4 kx[U], vx[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    int64_t j = w_lo + part * WR + u * RPP + rsub;
+    j = j > a.n - 1 ? a.n - 1 : j;
+    kx[u] = *(const uint4*)(kb + (size_t)j * RB + cc * 16);
+    vx[u] = *(const uint4*)(vb + (size_t)j * RB + cc * 16);
+  }
+  double qd[EPC];
+  {
+    const uint32_t w4[4] = {qc.x, qc.y, qc.z, qc.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if constexpr (BF16) {
+        qd[2 * e] = bf16_lo(w4[e]);
+        qd[2 * e + 1] = bf16_hi(w4[e]);
+      } else {
+        qd[e] = __uint_as_float(w4[e]);
+      }
+    }
+  }
+  // logits: float64 partial dot of the lane's chunk, summed over the LPR lanes of the row
+  double z[U];
+  double zm = -INFINITY;
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const uint32_t w4[4] = {kx[u].x, kx[u].y, kx[u].z, kx[u].w};
+    double part_s = 0.0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if constexpr (BF16) {
+        part_s = fma(qd[2 * e], (double)bf16_lo(w4[e]), part_s);
+        part_s = fma(qd[2 * e + 1], (double)bf16_hi(w4[e]), part_s);
+      } else {
+        part_s = fma(qd[e], (double)__uint_as_float(w4[e]), part_s);
+      }
+    }
+#pragma unroll
+    for (int o = 1; o < LPR; o <<= 1) part_s += __shfl_xor(part_s, o);
+    const bool valid = part * WR + u * RPP + rsub < nwin;
+    z[u] = valid ? a.scale * part_s : -INFINITY;
+    zm = fmax(zm, z[u]);
+  }
+  const double m = block_max_f64<4>(zm, scr);
+  double wsum = 0.0;
+  double acc[EPC];
+#pragma unroll
+  for (int e = 0; e < EPC; ++e) acc[e] = 0.0;
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const double w = z[u] > -INFINITY ? exp(z[u] - m) : 0.0;
+    if (cc == 0) wsum += w;
+    const uint32_t w4[4] = {vx[u].x, vx[u].y, vx[u].z, vx[u].w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if constexpr (BF16) {
+        acc[2 * e] = fma(w, (double)bf16_lo(w4[e]), acc[2 * e]);
+        acc[2 * e + 1] = fma(w, (double)bf16_hi(w4[e]), acc[2 * e + 1]);
+      } else {
+        acc[e] = fma(w, (double)__uint_as_float(w4[e]), acc[e]);
+      }
+    }
+  }
+  const double zs = block_sum_f64<4>(wsum, scr);
+  // the rows of a wave that share chunk cc: lanes cc + LPR * i
+#pragma unroll
+  for (int e = 0; e < EPC; ++e)
+    for (int o = LPR; o < 64; o <<= 1) acc[e] += __shfl_xor(acc[e], o);
+  if (lane < LPR) {
+#pragma unroll
+    for (int e = 0; e < EPC; ++e) red[wave][cc * EPC + e] = acc[e];
+  }
+  __syncthreads();
+  double* rec = a.rec + ((size_t)bh * a.rstride + part) * (D + 2);
+  if (tid < D) rec[tid] = red[0][tid] + red[1][tid] + red[2][tid] + red[3][tid];
+  if (tid == 0) {
+    rec[D] = m;
+    rec[D + 1] = zs;
   }
 }
 
@@ -163,11 +315,6 @@ struct KscanArgs {
   float eps_coef;
 };
 
-// Geometry of batch element b's query from its position pos[b] (clamped into the cache; causal).
-__device__ __forceinline__ QueryGeom ragged_geom(const int64_t* pos, int b, int64_t n, int32_t W) {
-  const int64_t p = pos[b];
-  return make_geom(p < 0 ? 0 : (p > n - 1 ? n - 1 : p), n, W, true);
-}
 
 // Loads of one 64-key tile. The 64 lanes form 8 groups of 8; group r handles keys 8i + r of the
 // tile (i = 0..7) and lane s of a group holds 16-byte chunks c*8 + s (c < CPL) of each of them:
@@ -660,9 +807,11 @@ __global__ __launch_bounds__(64) void merge_lists_kernel(MergeArgs a) {
 //      their lower and upper score bounds.
 //   2. Exact k-th largest lower bound by an 11 + 11 + 10 bit radix select in LDS; the short list
 //      is every survivor whose upper bound reaches it (it holds the whole top-k).
-//   3. Float64 canonical scores of the short list; exact ranks by (score desc, position asc).
-//   4. The set {0} u window u top-k, ascending; float64 scores of the anchor and window rows.
-//   5. Float64 softmax over the set and the weighted sum of the V rows.
+//   3. Float64 canonical scores of the short list and the anchor; exact ranks by (score desc,
+//      position asc).
+//   4. The set {0} u window u top-k, ascending.
+//   5. Float64 softmax and weighted V rows over the anchor and the top-k, merged with the
+//      window's share from decode_window's records.
 // Ties crowding the short list, overflowing scan blocks, k above the scan's limit and the
 // TOPO_FLAG_EXACT_SELECT flag all route to an exact radix select over every candidate instead.
 constexpr int FIN_THREADS = 512;
@@ -683,6 +832,9 @@ struct FinishArgs {
   int64_t n, nblk, slot;
   int64_t p, w_lo, vis_hi, scan_hi, n_cand;
   const int64_t* pos;  // may be null: causal query position of each batch element
+  const double* wrec;  // the window kernel's records: [B * Hq][wstride][D + 2] (partial output, m, Z)
+  int64_t wstride;
+  int32_t wparts;      // records per head written by the window kernel (0: none)
   int32_t Hq, Hkv, G, W, topk, set_cap, flags;
   double scale;
   float eps_coef;
@@ -710,6 +862,8 @@ struct FinishSmem {
   double rg[REFINE_CAP];  // shared selection: group scores of the short list
   double red[FIN_WAVES * 128];
   double scratch[FIN_WAVES];
+  double2 wmz[8];  // (maximum logit, sum) of the first window records
+  double ascore;   // float64 score of the anchor
   int32_t ival[8];
 };
 
@@ -852,7 +1006,12 @@ __device__ int exact_select(FinishSmem* sm, const FinishArgs& a, const unsigned 
 // count of the list is only applied afterwards, so a batch costs one memory round trip. Kept
 // entries are appended in any order (one LDS atomic per wave and batch). Returns the number of
 // entries, or -1 if they do not fit.
-__device__ int stage_survivors(FinishSmem* sm, const FinishArgs& a, int bh, uint32_t theta) {
+// Also requests the shared state of the head (its threshold and overflow flag, returned in
+// theta_out / over_out) and the caller's query element qraw (element min(tid, qn - 1) of qrow, qb
+// bytes each, raw bits) after the first batch of list loads, so that the lists, the state and the
+// query share one memory round trip. sm->ival[6] must be 0 on entry.
+__device__ int stage_survivors(FinishSmem* sm, const FinishArgs& a, int bh, uint32_t& theta_out, uint32_t& over_out,
+                               const unsigned char* qrow, int qb, int qn, uint32_t& qraw) {
   constexpr int BATCH = 12;
   const int tid = threadIdx.x, lane = tid & 63;
   const int64_t nblk = a.nblk;
@@ -863,50 +1022,82 @@ __device__ int stage_survivors(FinishSmem* sm, const FinishArgs& a, int bh, uint
   int tpl = 1;
   while (tpl < 64 && (int64_t)tpl * 2 * nblk <= FIN_THREADS) tpl *= 2;
   const int lpp = FIN_THREADS / tpl;  // lists per pass
-  if (tid == 0) sm->ival[6] = 0;
-  __syncthreads();
-  for (int64_t l0 = 0; l0 < nblk; l0 += lpp) {
+  const int sub = tid % tpl;
+  uint32_t theta = 0u, over = 0u;
+  // the shared state and the query element, after the first batch (see above)
+  auto request_rest = [&]() {
+    theta = a.st[bh].theta;
+    over = a.st[bh].overflow;
+    const int qi = tid < qn ? tid : qn - 1;
+    qraw = qb == 2 ? (uint32_t)((const uint16_t*)qrow)[qi] : ((const uint32_t*)qrow)[qi];
+  };
+  // loads of batch (l0, jb): count, error bound and BATCH entries of list l0 + tid / tpl. The
+  // addresses are clamped into the arrays and every load is issued (no branches, so no load
+  // waits for another); entries past the list's count, or of a list past the last, are ignored.
+  auto load_batch = [&](int64_t l0, int jb, uint2 (&e)[BATCH], uint32_t& c, float& eps) {
     const int64_t l = l0 + tid / tpl;
-    const int sub = tid % tpl;
-    const bool lv = l < nblk;
-    uint32_t c = lv ? bc[l] : 0u;
-    const float eps = lv ? be[l] : 0.f;
+    const int64_t lc = l < nblk ? l : nblk - 1;
+    c = bc[lc];
+    eps = be[lc];
+    if (l >= nblk) c = 0u;
+    const int j0 = jb + sub;
+#pragma unroll
+    for (int u = 0; u < BATCH; ++u) {
+      const int j = j0 + u * tpl;
+      e[u] = sv[(size_t)lc * slot + (j < slot ? j : slot - 1)];
+    }
+  };
+  // keep the entries whose upper bound reaches theta: append them to the LDS arrays
+  auto filter_batch = [&](int jb, const uint2 (&e)[BATCH], uint32_t c, float eps) {
     if (c > (uint32_t)slot) c = 0u;  // overflowed list: the head is on the exact path anyway
-    for (int jb = 0; jb < slot; jb += tpl * BATCH) {  // same trip count in every lane
-      const int j0 = jb + sub;
-      uint2 e[BATCH];
+    const int j0 = jb + sub;
+    uint32_t keep = 0u;
 #pragma unroll
-      for (int u = 0; u < BATCH; ++u) {
-        const int j = j0 + u * tpl;
-        e[u] = lv && j < slot ? sv[(size_t)l * slot + j] : make_uint2(0u, 0u);
-      }
-      uint32_t keep = 0u;
+    for (int u = 0; u < BATCH; ++u) {
+      const int j = j0 + u * tpl;
+      const bool k = j < (int)c && ord_f32(__uint_as_float(e[u].x) + eps) >= theta;
+      keep |= (k ? 1u : 0u) << u;
+    }
+    const int n = __popc(keep);
+    const int incl = wave_incl_scan_i32(n);
+    int base = 0;
+    if (lane == 63 && incl > 0) base = atomicAdd(&sm->ival[6], incl);
+    base = __shfl(base, 63) + incl - n;
 #pragma unroll
-      for (int u = 0; u < BATCH; ++u) {
-        const int j = j0 + u * tpl;
-        const bool k = j < (int)c && ord_f32(__uint_as_float(e[u].x) + eps) >= theta;
-        keep |= (k ? 1u : 0u) << u;
-      }
-      const int n = __popc(keep);
-      const int incl = wave_incl_scan_i32(n);
-      int base = 0;
-      if (lane == 63 && incl > 0) base = atomicAdd(&sm->ival[6], incl);
-      base = __shfl(base, 63) + incl - n;
-#pragma unroll
-      for (int u = 0; u < BATCH; ++u) {
-        if ((keep >> u) & 1u) {
-          if (base < SURV_LDS) {
-            const float sf = __uint_as_float(e[u].x);
-            sm->u.s.lbk[base] = ord_f32(sf - eps);
-            sm->u.s.ubk[base] = ord_f32(sf + eps);
-            sm->u.s.sidx[base] = (int32_t)e[u].y;
-          }
-          ++base;
+    for (int u = 0; u < BATCH; ++u) {
+      if ((keep >> u) & 1u) {
+        if (base < SURV_LDS) {
+          const float sf = __uint_as_float(e[u].x);
+          sm->u.s.lbk[base] = ord_f32(sf - eps);
+          sm->u.s.ubk[base] = ord_f32(sf + eps);
+          sm->u.s.sidx[base] = (int32_t)e[u].y;
         }
+        ++base;
+      }
+    }
+  };
+  uint2 e[BATCH];
+  uint32_t c;
+  float eps;
+  if (nblk <= lpp && slot <= tpl * BATCH) {
+    // the usual case: every list in one batch
+    load_batch(0, 0, e, c, eps);
+    request_rest();
+    __syncthreads();  // the cleared counter
+    filter_batch(0, e, c, eps);
+  } else {
+    request_rest();
+    __syncthreads();
+    for (int64_t l0 = 0; l0 < nblk; l0 += lpp) {
+      for (int jb = 0; jb < slot; jb += tpl * BATCH) {  // same trip count in every lane
+        load_batch(l0, jb, e, c, eps);
+        filter_batch(jb, e, c, eps);
       }
     }
   }
   __syncthreads();
+  theta_out = theta;
+  over_out = over;
   const int M = sm->ival[6];
   return M > SURV_LDS ? -1 : M;
 }
@@ -932,7 +1123,27 @@ __global__ __launch_bounds__(FIN_THREADS) void decode_finish_kernel(FinishArgs a
   const unsigned char* vb = a.v + ((size_t)b * a.Hkv + g) * (size_t)a.n * RB;
   const unsigned char* qrow = a.q + (size_t)bh * RB;
 
-  if (tid < D) sm->qd[tid] = load_elem_f64<BF16>(qrow, tid);
+  // The thread's query element (raw bits) is requested with the staging's loads when the staging
+  // runs, else just before it is needed; it reaches LDS after the selection.
+  uint32_t qraw = 0u;
+  bool q_requested = false;
+  if (tid == 0) sm->ival[6] = 0;  // survivor counter of the staging
+  // The window's share of the softmax comes from decode_window as a[bh].wparts records (partial
+  // output, maximum logit m_j, sum Z_j); the first WPF are requested now (partial outputs by the
+  // threads t < D, one element each; (m_j, Z_j) by threads D + j) and combined after the
+  // selection. Addresses are clamped so that every load is issued without a branch.
+  constexpr int WPF = 8;
+  const bool use_win = a.out != nullptr && a.wparts > 0;
+  const double* wr = a.wrec + (size_t)bh * a.wstride * (D + 2);
+  double ow[WPF];
+  double2 wmz_pf = make_double2(-INFINITY, 0.0);
+  if (use_win) {
+    const int tc = tid < D ? tid : D - 1;
+#pragma unroll
+    for (int j = 0; j < WPF; ++j) ow[j] = wr[(size_t)(j < a.wparts ? j : a.wparts - 1) * (D + 2) + tc];
+    const int jm = tid - D < 0 ? 0 : (tid - D < a.wparts ? tid - D : a.wparts - 1);
+    wmz_pf = *(const double2*)(wr + (size_t)jm * (D + 2) + D);
+  }
   // Shared selection: the group's first head holds the survivor lists and the shared state of
   // the whole group, and every head of the group ranks by the same group scores.
   const bool group = (a.flags & FLAG_GROUP_SELECT) != 0;
@@ -941,26 +1152,29 @@ __global__ __launch_bounds__(FIN_THREADS) void decode_finish_kernel(FinishArgs a
     for (int t = tid; t < a.G * D; t += FIN_THREADS)
       sm->qg[t / D][t % D] = load_elem_f64<BF16>(a.q + (size_t)(b * a.Hq + g * a.G + t / D) * RB, t % D);
   }
-  // (stage_survivors below starts with a barrier-protected phase, so qd and qg are visible after it)
+  // (every path below passes a barrier before qg is used)
 
   const int64_t w_lo = a.w_lo, p = a.p;
   const int anchor = w_lo > 0 ? 1 : 0;
   const int nwin = (int)(p - w_lo + 1);
 
-  // ---- the top-k part T; the short list R (fast path) is scored together with the anchor and
-  // window rows, so that all float64 row scores cost one memory round trip.
+  // ---- the top-k part T; the short list R (fast path) is scored together with the anchor, so
+  // that all float64 row scores cost one memory round trip.
   int nt = 0;
   bool fast = false;
   int nr = 0;
   bool exact = false, take_all = false;
   if (a.topk > 0 && a.n_cand > 0) {
-    const uint32_t st_theta = a.st[sh].theta, st_over = a.st[sh].overflow;
-    exact = (a.flags & 1) != 0 || st_over != 0 || a.topk > KS_MAX_K;
+    exact = (a.flags & 1) != 0 || a.topk > KS_MAX_K;
     take_all = a.n_cand <= a.topk;
     if (!take_all && !exact) {
-      const int M = stage_survivors(sm, a, sh, st_theta);
-      if (M < a.topk) {
-        exact = true;  // more survivors than LDS holds (or, impossibly, fewer than k)
+      uint32_t st_theta = 0u, st_over = 0u;
+      const int M = stage_survivors(sm, a, sh, st_theta, st_over, qrow, BF16 ? 2 : 4, D, qraw);
+      q_requested = true;
+      if (st_over != 0 || M < a.topk) {
+        // a scan block overflowed its slot, more survivors than LDS holds, or (impossibly) fewer
+        // than k: the exact path
+        exact = true;
       } else {
         // A valid threshold: the k-th largest of every thread's best lower bound (distinct keys;
         // 0 if fewer than k threads hold one). With k <= 224 and 512 threads it stays close to the
@@ -1013,57 +1227,24 @@ __global__ __launch_bounds__(FIN_THREADS) void decode_finish_kernel(FinishArgs a
       __syncthreads();
     }
   }
+  if (!q_requested && tid < D) qraw = BF16 ? (uint32_t)((const uint16_t*)qrow)[tid] : ((const uint32_t*)qrow)[tid];
+  asm volatile("" : "+v"(qraw));  // the conversion stays here, after the staging
+  if (tid < D) sm->qd[tid] = (double)__uint_as_float(BF16 ? qraw << 16 : qraw);
+  if (use_win && tid >= D && tid - D < WPF && tid - D < a.wparts) sm->wmz[tid - D] = wmz_pf;
   __syncthreads();
 
-  // Row scores. Waves 0-1: the short list (fast path) and the anchor in the canonical float64
-  // order (they decide the set), one row per thread. Waves 2-7 at the same time: the window rows,
-  // whose scores only enter the softmax, with LPR lanes per row (a 16-byte chunk each, float64
-  // partial sums added across the lanes). Window scores are parked at the tail of cw, the anchor
-  // score in its last entry.
+  // Row scores: the short list (fast path) and the anchor in the canonical float64 order, one row
+  // per thread (the window rows are decode_window's).
   {
     const int nc = (fast ? nr : 0) + anchor;
-    if (tid < 128) {
-      for (int i = tid; i < nc; i += 128) {
-        const int64_t j = (fast && i < nr) ? (int64_t)sm->ridx[i] : 0;
-        const double sc = score_row<D, BF16>(sm, kb, j);
-        if (fast && i < nr) {
-          sm->rs[i] = sc;
-          if (group) sm->rg[i] = group_score_row<D, BF16>(sm, kb, j, a.G);
-        } else {
-          sm->u.c.cw[MAX_SET - 1] = sc;
-        }
-      }
-    } else {
-      constexpr int LPR = RB / 16, EPC = BF16 ? 8 : 4, RPP = (FIN_THREADS - 128) / LPR, WB = 12;
-      const int t = tid - 128, rsub = t / LPR, cc = t % LPR;
-      double qv[EPC];
-#pragma unroll
-      for (int e = 0; e < EPC; ++e) qv[e] = sm->qd[cc * EPC + e];
-      for (int r0 = 0; r0 < nwin; r0 += RPP * WB) {  // same trip count in every lane
-        uint4 x[WB];
-#pragma unroll
-        for (int u = 0; u < WB; ++u) {
-          const int row = r0 + u * RPP + rsub;
-          x[u] = row < nwin ? *(const uint4*)(kb + (size_t)(w_lo + row) * RB + cc * 16) : make_uint4(0u, 0u, 0u, 0u);
-        }
-#pragma unroll
-        for (int u = 0; u < WB; ++u) {
-          const uint32_t w4[4] = {x[u].x, x[u].y, x[u].z, x[u].w};
-          double part = 0.0;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            if constexpr (BF16) {
-              part = fma(qv[2 * e], (double)bf16_lo(w4[e]), part);
-              part = fma(qv[2 * e + 1], (double)bf16_hi(w4[e]), part);
-            } else {
-              part = fma(qv[e], (double)__uint_as_float(w4[e]), part);
-            }
-          }
-#pragma unroll
-          for (int o = 1; o < LPR; o <<= 1) part += __shfl_xor(part, o);
-          const int row = r0 + u * RPP + rsub;
-          if (cc == 0 && row < nwin) sm->u.c.cw[MAX_SET - nwin - 1 + row] = part;
-        }
+    for (int i = tid; i < nc; i += FIN_THREADS) {
+      const int64_t j = (fast && i < nr) ? (int64_t)sm->ridx[i] : 0;
+      const double sc = score_row<D, BF16>(sm, kb, j);
+      if (fast && i < nr) {
+        sm->rs[i] = sc;
+        if (group) sm->rg[i] = group_score_row<D, BF16>(sm, kb, j, a.G);
+      } else {
+        sm->ascore = sc;
       }
     }
   }
@@ -1118,32 +1299,14 @@ __global__ __launch_bounds__(FIN_THREADS) void decode_finish_kernel(FinishArgs a
   __syncthreads();
   int tlo = 0;
   for (int i = 0; i < FIN_WAVES; ++i) tlo += sm->hist[i];
-  // window and anchor scores move from their parking slots (the tail of cw, beyond every final
-  // position: count <= 1 + W + k <= MAX_SET - 1 and the parked rows are read before overwritten)
-  double wsc[(MAX_SET + FIN_THREADS - 1) / FIN_THREADS];
-  double asc = 0.0;
-  int nw_mine = 0;
-  for (int i = tid; i < nwin; i += FIN_THREADS) wsc[nw_mine++] = sm->u.c.cw[MAX_SET - nwin - 1 + i];
-  if (anchor) asc = sm->u.c.cw[MAX_SET - 1];
-  __syncthreads();
-  if (anchor && tid == 0) {
-    sm->u.c.cidx[0] = 0;
-    sm->u.c.cw[0] = asc;
-  }
+  if (anchor && tid == 0) sm->u.c.cidx[0] = 0;
   for (int i = tid; i < nt; i += FIN_THREADS) {
     const int32_t t = sm->u.c.tidx[i];
     int below = 0;
     for (int r = 0; r < nt; ++r) below += sm->u.c.tidx[r] < t;
-    const int pos = anchor + below + (t > p ? nwin : 0);
-    sm->u.c.cidx[pos] = t;
-    sm->u.c.cw[pos] = sm->u.c.ts[i];
+    sm->u.c.cidx[anchor + below + (t > p ? nwin : 0)] = t;
   }
-  nw_mine = 0;
-  for (int i = tid; i < nwin; i += FIN_THREADS) {
-    const int pos = anchor + tlo + i;
-    sm->u.c.cidx[pos] = (int32_t)(w_lo + i);
-    sm->u.c.cw[pos] = wsc[nw_mine++];
-  }
+  for (int i = tid; i < nwin; i += FIN_THREADS) sm->u.c.cidx[anchor + tlo + i] = (int32_t)(w_lo + i);
   __syncthreads();
 
   if (a.sel_idx) {
@@ -1153,17 +1316,54 @@ __global__ __launch_bounds__(FIN_THREADS) void decode_finish_kernel(FinishArgs a
   if (a.sel_count && tid == 0) a.sel_count[bh] = count;
   if (!a.out) return;
 
-  // ---- softmax over the set (float64) and the weighted sum of the V rows
-  double zmax = -INFINITY;
-  for (int i = tid; i < count; i += FIN_THREADS) zmax = fmax(zmax, a.scale * sm->u.c.cw[i]);
+  // ---- softmax over the set (float64) and the weighted sum of the V rows. Here the anchor and
+  // the top-k part (ts / tidx [0, nt), the anchor appended at nt); the window's share is the
+  // combination of decode_window's records: with M_w the largest of their m_j,
+  // Z_w = sum_j Z_j exp(m_j - M_w) and O_w = sum_j O_j exp(m_j - M_w); then with zmax the largest
+  // logit of the set, out = (sum_e w_e v_e + f O_w) / (sum_e w_e + f Z_w), w_e = exp(z_e - zmax),
+  // f = exp(M_w - zmax).
+  const int ne = nt + anchor;
+  if (anchor && tid == 0) {
+    sm->u.c.tidx[nt] = 0;
+    sm->u.c.ts[nt] = sm->ascore;
+  }
+  double Mw = -INFINITY, Zw = 0.0, Ow = 0.0;
+  if (use_win) {
+#pragma unroll
+    for (int j = 0; j < WPF; ++j)
+      if (j < a.wparts) Mw = fmax(Mw, sm->wmz[j].x);
+    for (int j = WPF; j < a.wparts; ++j) Mw = fmax(Mw, wr[(size_t)j * (D + 2) + D]);
+    if (Mw > -INFINITY) {
+#pragma unroll
+      for (int j = 0; j < WPF; ++j) {
+        if (j < a.wparts && sm->wmz[j].x > -INFINITY) {
+          const double f = exp(sm->wmz[j].x - Mw);
+          Zw += f * sm->wmz[j].y;
+          Ow += f * ow[j];
+        }
+      }
+      for (int j = WPF; j < a.wparts; ++j) {
+        const double2 mz = *(const double2*)(wr + (size_t)j * (D + 2) + D);
+        if (mz.x > -INFINITY) {
+          const double f = exp(mz.x - Mw);
+          Zw += f * mz.y;
+          if (tid < D) Ow += f * wr[(size_t)j * (D + 2) + tid];
+        }
+      }
+    }
+  }
+  __syncthreads();
+  double zmax = Mw;
+  for (int i = tid; i < ne; i += FIN_THREADS) zmax = fmax(zmax, a.scale * sm->u.c.ts[i]);
   zmax = block_max_f64<FIN_WAVES>(zmax, sm->scratch);
   double zsum = 0.0;
-  for (int i = tid; i < count; i += FIN_THREADS) {
-    const double w = exp(a.scale * sm->u.c.cw[i] - zmax);
+  for (int i = tid; i < ne; i += FIN_THREADS) {
+    const double w = exp(a.scale * sm->u.c.ts[i] - zmax);
     sm->u.c.cw[i] = w;
     zsum += w;
   }
-  zsum = block_sum_f64<FIN_WAVES>(zsum, sm->scratch);  // (contains a barrier: weights visible)
+  const double fw = Mw > -INFINITY ? exp(Mw - zmax) : 0.0;
+  zsum = block_sum_f64<FIN_WAVES>(zsum, sm->scratch) + fw * Zw;  // (contains a barrier: weights visible)
   if (a.rho) {
     // Exactness certificate: every candidate left out scores at most s_k, the lowest score of
     // the top-k part, so the left-out mass relative to the dense total is at most
@@ -1181,28 +1381,28 @@ __global__ __launch_bounds__(FIN_THREADS) void decode_finish_kernel(FinishArgs a
     }
   }
 
-  // Thread t reads 16-byte chunk (t % CPR) of rows t / CPR, + RPP, ...; a batch of BATCH rows
-  // per thread is in flight together (one batch covers a set of up to RPP * BATCH rows).
+  // Thread t reads 16-byte chunk (t % CPR) of entries t / CPR, + RPP, ...; a batch of BATCH rows
+  // per thread is in flight together (one batch covers up to RPP * BATCH entries).
   constexpr int CPR = RB / 16;             // chunks per row
   constexpr int EPC = BF16 ? 8 : 4;        // elements per chunk
   constexpr int RPP = FIN_THREADS / CPR;   // rows per pass
-  constexpr int BATCH = 20;
+  constexpr int BATCH = 8;
   const int wave = tid >> 6, lane = tid & 63;
   const int c = tid % CPR, r0 = tid / CPR;
   double acc[EPC];
 #pragma unroll
   for (int e = 0; e < EPC; ++e) acc[e] = 0.0;
-  for (int i0 = r0; i0 < count; i0 += RPP * BATCH) {
+  for (int i0 = r0; i0 < ne; i0 += RPP * BATCH) {
     uint4 ch[BATCH];
 #pragma unroll
     for (int u = 0; u < BATCH; ++u) {
       const int i = i0 + u * RPP;
-      ch[u] = i < count ? *(const uint4*)(vb + (size_t)sm->u.c.cidx[i] * RB + c * 16) : make_uint4(0u, 0u, 0u, 0u);
+      ch[u] = i < ne ? *(const uint4*)(vb + (size_t)sm->u.c.tidx[i] * RB + c * 16) : make_uint4(0u, 0u, 0u, 0u);
     }
 #pragma unroll
     for (int u = 0; u < BATCH; ++u) {
       const int i = i0 + u * RPP;
-      const double w = i < count ? sm->u.c.cw[i] : 0.0;
+      const double w = i < ne ? sm->u.c.cw[i] : 0.0;
       const uint32_t ws[4] = {ch[u].x, ch[u].y, ch[u].z, ch[u].w};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -1225,7 +1425,7 @@ __global__ __launch_bounds__(FIN_THREADS) void decode_finish_kernel(FinishArgs a
   }
   __syncthreads();
   if (tid < D) {
-    double num = 0.0;
+    double num = fw * Ow;
     for (int w = 0; w < FIN_WAVES; ++w) num += sm->red[w * D + tid];
     a.out[(size_t)bh * D + tid] = (float)(num / zsum);
   }
@@ -1272,11 +1472,41 @@ static hipError_t launch_finish_t(const FinishArgs& fa, int nbh, hipStream_t s) 
 
 hipError_t launch_decode(const DecodeLaunch& L, hipStream_t stream) {
   const int nbh = L.B * L.Hq;
-  hipLaunchKernelGGL(decode_init_kernel, dim3((nbh + 255) / 256), dim3(256), 0, stream, L.st, nbh);
+  const QueryGeom& g = L.geom;
+  // the window's share of the softmax (with the clearing of the scan state), or the clearing alone
+  const int64_t wparts = L.out ? window_parts(g, L.d, L.bf16) : 0;
+  if (wparts > 0) {
+    WindowArgs wa;
+    wa.q = (const unsigned char*)L.q;
+    wa.k = (const unsigned char*)L.k;
+    wa.v = (const unsigned char*)L.v;
+    wa.st = L.st;
+    wa.rec = L.wrec;
+    wa.pos = L.pos;
+    wa.n = L.n;
+    wa.p = g.p;
+    wa.w_lo = g.w_lo;
+    wa.rstride = L.wstride;
+    wa.Hq = L.Hq;
+    wa.Hkv = L.Hkv;
+    wa.G = L.G;
+    wa.W = L.W;
+    wa.nheads = nbh;
+    wa.scale = L.scale;
+    const dim3 grid((unsigned)wparts, (unsigned)nbh);
+    if (L.bf16) {
+      if (L.d == 128) hipLaunchKernelGGL((decode_window_kernel<128, true>), grid, dim3(256), 0, stream, wa);
+      else hipLaunchKernelGGL((decode_window_kernel<64, true>), grid, dim3(256), 0, stream, wa);
+    } else {
+      if (L.d == 128) hipLaunchKernelGGL((decode_window_kernel<128, false>), grid, dim3(256), 0, stream, wa);
+      else hipLaunchKernelGGL((decode_window_kernel<64, false>), grid, dim3(256), 0, stream, wa);
+    }
+  } else {
+    hipLaunchKernelGGL(decode_init_kernel, dim3((nbh + 255) / 256), dim3(256), 0, stream, L.st, nbh);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
 
-  const QueryGeom& g = L.geom;
   if (L.ev_scan_begin) {
     e = hipEventRecord(L.ev_scan_begin, stream);
     if (e != hipSuccess) return e;
@@ -1366,6 +1596,9 @@ hipError_t launch_decode(const DecodeLaunch& L, hipStream_t stream) {
   fa.scan_hi = g.scan_hi;
   fa.n_cand = g.n_cand;
   fa.pos = L.pos;
+  fa.wrec = L.wrec;
+  fa.wstride = L.wstride;
+  fa.wparts = (int32_t)wparts;
   fa.Hq = L.Hq;
   fa.Hkv = L.Hkv;
   fa.G = L.G;

@@ -67,6 +67,8 @@ struct DecodeLaunch {
   int32_t* sel_count;  // may be null
   float* rho;          // may be null: the exactness certificate per query
   HeadState* st;       // [B * Hq]
+  double* wrec;        // [B * Hq][wstride][d + 2]: the window kernel's records
+  int64_t wstride;
   // Survivor lists, level 0 written by the key scan and level l+1 by merging groups of
   // MERGE_FAN level-l lists:
   //   blk_cnt[l] [B * Hq][nblk[l]]        survivors of each list (or KS_OVERFLOW)
@@ -89,8 +91,9 @@ struct DecodeLaunch {
   hipEvent_t ev_scan_end;
 };
 
-size_t decode_workspace_bytes(int32_t B, int32_t Hq, const QueryGeom& g, int32_t k);
-// Carve the workspace into the HeadState array and the survivor lists.
+size_t decode_workspace_bytes(int32_t B, int32_t Hq, const QueryGeom& g, int32_t k, int32_t d, int32_t bf16);
+// Carve the workspace into the HeadState array, the window records and the survivor lists
+// (L.d and L.bf16 must be set).
 void decode_carve(void* ws, int32_t B, int32_t Hq, const QueryGeom& g, int32_t k, DecodeLaunch& L);
 hipError_t launch_decode(const DecodeLaunch& L, hipStream_t stream);
 // New key and value rows of one token per (batch, kv head) into the caches at row pos[b].
