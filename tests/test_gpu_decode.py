@@ -105,6 +105,7 @@ CASES = [
     (20000, 128, "bf16", 1, 4, 1, 512, 64, True, None),
     (33000, 64, "f32", 1, 2, 2, 0, 0, True, None),       # k = 0, W = 0: the anchor alone
     (3000, 128, "bf16", 1, 4, 2, 1000, 0, True, None),   # k = 0: sink + window
+    (6000, 128, "f32", 1, 2, 1, 700, 16, True, None),     # window in 22 parts of 32 rows
     (70000, 128, "bf16", 1, 4, 1, 64, 1000, True, None),  # large k
 ]
 

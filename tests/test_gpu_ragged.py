@@ -51,6 +51,8 @@ CASES = [
     (11, 4, 4, 2, 3000, 128, "bf16", [2999, 1234, 40, 10], 32, 16),
     (12, 4, 4, 1, 2100, 64, "f32", [150, 2099, 1, 777], 64, 32),
     (13, 2, 8, 8, 5000, 128, "bf16", [4999, 2500], 128, 64),
+    # a window wider than most sequences: parts of the window past a short sequence stay empty
+    (14, 3, 4, 2, 3000, 128, "f32", [2999, 300, 5], 700, 16),
 ]
 
 
