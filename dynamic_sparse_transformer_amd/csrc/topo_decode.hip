@@ -149,6 +149,7 @@ struct WindowArgs {
   const int64_t* pos;  // may be null: causal query position of each batch element
   int64_t n, p, w_lo, rstride;
   int32_t Hq, Hkv, G, W, nheads;
+  int32_t rstride_parts;  // blocks (parts) per head in this launch
   double scale;
 };
 
@@ -159,14 +160,20 @@ __global__ __launch_bounds__(256) void decode_window_kernel(WindowArgs a) {
   __shared__ double red[4][D];
   __shared__ double scr[4];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  if (blockIdx.x == 0 && blockIdx.y == 0) {
+  if (blockIdx.x == 0) {
     for (int i = tid; i < a.nheads; i += 256) {
       a.st[i].theta = 0u;
       a.st[i].overflow = 0u;
     }
   }
-  const int bh = blockIdx.y, part = blockIdx.x;
-  const int b = bh / a.Hq, h = bh - b * a.Hq, g = h / a.G;
+  // Job order: (batch, kv head, part, query head of the group), dealt to the XCDs in contiguous
+  // ranges, so that the G blocks reading the same K and V rows share one XCD's L2.
+  const int64_t job = xcd_job(blockIdx.x, gridDim.x);
+  const int hh = (int)(job % a.G);
+  const int64_t gp = job / a.G;
+  const int part = (int)(gp % a.rstride_parts), bg = (int)(gp / a.rstride_parts);
+  const int b = bg / a.Hkv, g = bg - b * a.Hkv, h = g * a.G + hh;
+  const int bh = b * a.Hq + h;
   int64_t p = a.p, w_lo = a.w_lo;
   if (a.pos) {
     const QueryGeom gq = ragged_geom(a.pos, b, a.n, a.W);
@@ -1492,8 +1499,9 @@ hipError_t launch_decode(const DecodeLaunch& L, hipStream_t stream) {
     wa.G = L.G;
     wa.W = L.W;
     wa.nheads = nbh;
+    wa.rstride_parts = (int32_t)wparts;
     wa.scale = L.scale;
-    const dim3 grid((unsigned)wparts, (unsigned)nbh);
+    const dim3 grid((unsigned)(wparts * nbh));
     if (L.bf16) {
       if (L.d == 128) hipLaunchKernelGGL((decode_window_kernel<128, true>), grid, dim3(256), 0, stream, wa);
       else hipLaunchKernelGGL((decode_window_kernel<64, true>), grid, dim3(256), 0, stream, wa);

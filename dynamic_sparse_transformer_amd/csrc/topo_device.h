@@ -244,6 +244,13 @@ __device__ __forceinline__ float group_sum_f32(float x) {
   return x;
 }
 
+// Job of block `blk` among `njobs`: consecutive block indices go to different XCDs (round robin),
+// so the jobs are dealt out in eight contiguous ranges, one per XCD, and neighbouring jobs (the
+// rows of one head, the heads of one kv group) share one XCD's L2.
+__device__ __forceinline__ int64_t xcd_job(int64_t blk, int64_t njobs) {
+  return njobs % 8 == 0 ? (blk & 7) * (njobs >> 3) + (blk >> 3) : blk;
+}
+
 // Block-wide reductions through a caller-provided LDS scratch of (blockDim.x / 64) entries.
 // Every thread of the block must call them; all threads get the result.
 template <int NWAVES>

@@ -140,13 +140,6 @@ __device__ __forceinline__ T pf_row16(T x) {
   return x;
 }
 
-// Job of block `blk` among `njobs`: consecutive block indices go to different XCDs (round robin),
-// so the jobs are dealt out in eight contiguous ranges, one per XCD, and the rows of one head
-// share one XCD's L2.
-__device__ __forceinline__ int64_t xcd_job(int64_t blk, int64_t njobs) {
-  return njobs % 8 == 0 ? (blk & 7) * (njobs >> 3) + (blk >> 3) : blk;
-}
-
 // ---------------------------------------------------------------------------------------------
 struct PfArgs {
   const unsigned char* q;
