@@ -132,12 +132,12 @@ __global__ void decode_init_kernel(HeadState* st, int nheads) {
 
 // ---------------------------------------------------------------------------------------------
 // decode_window: the window's share of the softmax, before the key scan (it needs only the query
-// and the cache). Block (j, bh) takes window rows [j * WR, (j + 1) * WR) of query head bh (the
-// window is the W positions up to p; fr page, technical summary §3, the softmax over the set) and
-// writes one record: O_j = sum_r exp(z_r - m_j) v_r (d values), m_j = max_r z_r and
-// Z_j = sum_r exp(z_r - m_j), with z_r = scale * q.k_r in float64 (an empty part writes m_j = -inf,
-// Z_j = 0, O_j = 0). The finishing kernel combines the records with the rest of the set. Block
-// (0, 0) also clears the per-head scan state, the job of decode_init when this kernel runs.
+// and the cache). One block per (query head bh, part j) takes window rows [j * WR, (j + 1) * WR)
+// of the head (the window is the W positions up to p; fr page, technical summary §3, the softmax
+// over the set) and writes one record: O_j = sum_r exp(z_r - m_j) v_r (d values), m_j = max_r z_r
+// and Z_j = sum_r exp(z_r - m_j), with z_r = scale * q.k_r in float64 (an empty part writes
+// m_j = -inf, Z_j = 0, O_j = 0). The finishing kernel combines the records with the rest of the
+// set. Block 0 also clears the per-head scan state, the job of decode_init when this kernel runs.
 // 256 threads: groups of LPR = RB / 16 lanes hold one row each (a 16-byte chunk per lane), four
 // rows per group; the K and V chunks of all of them are requested at once.
 struct WindowArgs {
