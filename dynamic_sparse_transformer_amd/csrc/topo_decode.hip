@@ -1183,11 +1183,14 @@ __global__ __launch_bounds__(FIN_THREADS) void decode_finish_kernel(FinishArgs a
         // than k: the exact path
         exact = true;
       } else {
-        // A valid threshold: the k-th largest of every thread's best lower bound (distinct keys;
-        // 0 if fewer than k threads hold one). With k <= 224 and 512 threads it stays close to the
-        // k-th largest of all survivors, and it needs a quarter of the search of a top-2 bound.
-        // Only values at or above the shared bound st_theta matter; between it and the largest
-        // value all keys share their leading bits, so the bitwise search starts below them.
+        // A valid threshold: at least k of the threads' best lower bounds (distinct keys) reach
+        // it. Only values at or above the shared bound st_theta matter. For k <= 64 the search
+        // runs between lo, the smallest of the 64 lanes' largest values (64 distinct keys reach
+        // it), and hi, the largest value: the largest T = lo + c (hi - lo) / 1024 that k values
+        // reach, counted per lane and summed with DPP moves, one bit of c per step. T lies less
+        // than (hi - lo) / 1024 below the k-th largest value (a few more keys for the short
+        // list). For larger k, or a range under 1024, the exact k-th largest by a bitwise search
+        // that starts below the leading bits the range shares.
         uint32_t m0 = 0u;
         for (int f = tid; f < M; f += FIN_THREADS) m0 = max(m0, sm->u.s.lbk[f]);
         sm->hist[tid] = m0;
@@ -1202,17 +1205,49 @@ __global__ __launch_bounds__(FIN_THREADS) void decode_finish_kernel(FinishArgs a
             hi = max(hi, x[i]);
             above += __popcll(__ballot(x[i] >= st_theta));
           }
-          for (int o = 32; o > 0; o >>= 1) hi = max(hi, (uint32_t)__shfl_xor((int)hi, o));
+          uint32_t lmax = x[0];
+#pragma unroll
+          for (int i = 1; i < FIN_THREADS / 64; ++i) lmax = max(lmax, x[i]);
+          uint32_t lmin = lmax;
+          for (int o = 32; o > 0; o >>= 1) {
+            hi = max(hi, (uint32_t)__shfl_xor((int)hi, o));
+            lmin = min(lmin, (uint32_t)__shfl_xor((int)lmin, o));
+          }
           uint32_t T = 0u;
           if (above >= a.topk && hi > st_theta) {
-            const int top = 31 - __builtin_clz(st_theta ^ hi);  // highest bit where they differ
-            T = top == 31 ? 0u : (hi & ~((2u << top) - 1u));
-            for (int bit = top; bit >= 0; --bit) {
-              const uint32_t cand = T | (1u << bit);
-              int c = 0;
+            const uint32_t lo = a.topk <= 64 && lmin > st_theta ? lmin : st_theta;
+            if (lo == hi) {
+              T = hi;  // the 64 lane maxima all equal hi: at least 64 >= k values reach it
+            } else if (a.topk <= 64 && hi - lo >= 1024u) {
+              const uint32_t step = (hi - lo) >> 10;
+              uint32_t c = 0u;
+              for (int bit = 9; bit >= 0; --bit) {
+                const uint32_t cc = c | (1u << bit);
+                const uint32_t cand = lo + cc * step;
+                int n = 0;
 #pragma unroll
-              for (int i = 0; i < FIN_THREADS / 64; ++i) c += __popcll(__ballot(x[i] >= cand));
-              if (c >= a.topk) T = cand;
+                for (int i = 0; i < FIN_THREADS / 64; ++i) n += x[i] >= cand ? 1 : 0;
+                // sum over the 16 lanes of each row (quad permutes, row half mirror, row
+                // mirror), then over the four rows
+                n += __builtin_amdgcn_mov_dpp(n, 0xB1, 0xF, 0xF, false);
+                n += __builtin_amdgcn_mov_dpp(n, 0x4E, 0xF, 0xF, false);
+                n += __builtin_amdgcn_mov_dpp(n, 0x141, 0xF, 0xF, false);
+                n += __builtin_amdgcn_mov_dpp(n, 0x140, 0xF, 0xF, false);
+                const int tot = __builtin_amdgcn_readlane(n, 0) + __builtin_amdgcn_readlane(n, 16) +
+                                __builtin_amdgcn_readlane(n, 32) + __builtin_amdgcn_readlane(n, 48);
+                if (tot >= a.topk) c = cc;
+              }
+              T = lo + c * step;
+            } else {
+              const int top = 31 - __builtin_clz(lo ^ hi);  // highest bit where they differ
+              T = top == 31 ? 0u : (hi & ~((2u << top) - 1u));
+              for (int bit = top; bit >= 0; --bit) {
+                const uint32_t cand = T | (1u << bit);
+                int c = 0;
+#pragma unroll
+                for (int i = 0; i < FIN_THREADS / 64; ++i) c += __popcll(__ballot(x[i] >= cand));
+                if (c >= a.topk) T = cand;
+              }
             }
           }
           if (tid == 0) sm->ival[5] = (int)T;
