@@ -1376,10 +1376,14 @@ __global__ __launch_bounds__(FIN_THREADS) void decode_finish_kernel(FinishArgs a
       if (j < a.wparts) Mw = fmax(Mw, sm->wmz[j].x);
     for (int j = WPF; j < a.wparts; ++j) Mw = fmax(Mw, wr[(size_t)j * (D + 2) + D]);
     if (Mw > -INFINITY) {
+      // one exponential per record: lane j of every wave takes record j < WPF, then shuffles
+      const int lw = tid & 63;
+      const double mj = sm->wmz[lw < WPF ? lw : 0].x;
+      const double fl = lw < WPF && lw < a.wparts && mj > -INFINITY ? exp(mj - Mw) : 0.0;
 #pragma unroll
       for (int j = 0; j < WPF; ++j) {
-        if (j < a.wparts && sm->wmz[j].x > -INFINITY) {
-          const double f = exp(sm->wmz[j].x - Mw);
+        const double f = __shfl(fl, j);
+        if (j < a.wparts) {
           Zw += f * sm->wmz[j].y;
           Ow += f * ow[j];
         }
