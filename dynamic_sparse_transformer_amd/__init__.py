@@ -20,7 +20,10 @@ __all__ = [
     "topo_attn_prefill", "topo_select", "topo_attn_dense", "topo_bw_probe", "topo_strerror",
     "topo_attn_decode_timed", "topo_attn_prefill_timed", "topo_attn_decode_certified",
     "topo_attn_decode_ragged", "topo_kv_append", "topo_attn_decode_layers", "pillar_schedule",
+    "topo_check_finite", "topo_workspace_view", "WorkspaceView",
     "TOPO_FLAG_EXACT_SELECT", "TOPO_FLAG_DENSE_FALLBACK", "TOPO_FLAG_GROUP_SELECT", "TOPO_CERT_RHO", "TOPO_MAX_SET", "EXPORTS",
+    "TOPO_PATH_NONE", "TOPO_PATH_ALL", "TOPO_PATH_FAST", "TOPO_PATH_BAND", "TOPO_PATH_EXACT_ASKED",
+    "TOPO_PATH_EXACT_OVERFLOW", "TOPO_PATH_EXACT_CROWDED", "PATH_NAMES",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -34,16 +37,27 @@ TOPO_FLAG_DENSE_FALLBACK = 2
 TOPO_FLAG_GROUP_SELECT = 4
 TOPO_CERT_RHO = 2.0 ** -24
 TOPO_MAX_SET = 4096
+TOPO_PATH_NONE, TOPO_PATH_ALL, TOPO_PATH_FAST, TOPO_PATH_BAND = 0, 1, 2, 3
+TOPO_PATH_EXACT_ASKED, TOPO_PATH_EXACT_OVERFLOW, TOPO_PATH_EXACT_CROWDED = 4, 5, 6
+PATH_NAMES = {0: "none", 1: "all", 2: "fast", 3: "band", 4: "exact_asked", 5: "exact_overflow", 6: "exact_crowded"}
 EXPORTS = ("topo_workspace_bytes", "topo_attn_decode", "topo_attn_decode_timed", "topo_attn_decode_certified",
            "topo_attn_decode_ragged", "topo_kv_append", "topo_attn_decode_layers", "topo_layers_workspace_bytes",
-           "topo_attn_prefill", "topo_attn_prefill_timed", "topo_select", "topo_attn_dense", "topo_bw_probe",
-           "topo_strerror")
+           "topo_pillar_plan", "topo_attn_prefill", "topo_attn_prefill_timed", "topo_select", "topo_attn_dense",
+           "topo_check_finite", "topo_workspace_view", "topo_bw_probe", "topo_strerror")
 
 
 class TopoLayer(ctypes.Structure):
     _fields_ = [("q", ctypes.c_void_p), ("k_cache", ctypes.c_void_p), ("v_cache", ctypes.c_void_p),
                 ("out", ctypes.c_void_p), ("sel_idx", ctypes.c_void_p), ("sel_count", ctypes.c_void_p),
                 ("W", ctypes.c_int32), ("k", ctypes.c_int32), ("pillar", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+
+class WorkspaceView(ctypes.Structure):
+    """topo_ws_view_t: where a call leaves its candidate lists and selection paths in the workspace."""
+    _fields_ = [("queries", ctypes.c_int64), ("lists", ctypes.c_int64), ("slots", ctypes.c_int64),
+                ("count_offset", ctypes.c_size_t), ("entry_offset", ctypes.c_size_t),
+                ("eps_offset", ctypes.c_size_t), ("path_offset", ctypes.c_size_t),
+                ("path_stride", ctypes.c_size_t), ("eps_coef", ctypes.c_float), ("reserved", ctypes.c_int32)]
 
 
 class TopoError(RuntimeError):
@@ -99,6 +113,12 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.topo_select.restype = i32
     lib.topo_attn_dense.argtypes = [P, vp, vp, vp, vp, vp, sz, vp]
     lib.topo_attn_dense.restype = i32
+    lib.topo_pillar_plan.argtypes = [i32, i32, i32, i32, i32, LP]
+    lib.topo_pillar_plan.restype = i32
+    lib.topo_check_finite.argtypes = [vp, sz, i32, vp, vp]
+    lib.topo_check_finite.restype = i32
+    lib.topo_workspace_view.argtypes = [P, i32, ctypes.POINTER(WorkspaceView)]
+    lib.topo_workspace_view.restype = i32
     lib.topo_bw_probe.argtypes = [vp, sz, vp, vp]
     lib.topo_bw_probe.restype = i32
     lib.topo_strerror.argtypes = [i32]
@@ -309,24 +329,49 @@ def topo_kv_append(k_cache, v_cache, k_new, v_new, pos, stream=None):
 
 
 def pillar_schedule(n_layers: int, W_first: int, k_first: int, W_last: int | None = None, k_last: int | None = None):
-    """Per-layer plan of a decode step through n_layers attention layers: a list of
-    (pillar, W, k). About one layer in sixteen is a pillar (dense) layer: max(1, round(L / 16))
-    of them, evenly spaced from layer 0. The other layers take (W, k) interpolated linearly from
-    (W_first, k_first) at layer 0 to (W_last, k_last) at the last layer, rounded: wider windows
-    early, leaner sets late (zh page, technical summary §3)."""
-    if n_layers < 1:
-        raise ValueError("n_layers >= 1")
+    """Per-layer plan of a decode step through n_layers attention layers, from the library's
+    topo_pillar_plan: a list of (pillar, W, k). About one layer in sixteen is a pillar (dense)
+    layer: max(1, round(L / 16)) of them, evenly spaced from layer 0. Every layer takes (W, k)
+    interpolated linearly from (W_first, k_first) at layer 0 to (W_last, k_last) at the last
+    layer, rounded: wider windows early, leaner sets late (zh page, technical summary §3)."""
     W_last = W_first if W_last is None else W_last
     k_last = k_first if k_last is None else k_last
-    n_pillar = max(1, int(round(n_layers / 16)))
-    pillars = {i * n_layers // n_pillar for i in range(n_pillar)}
-    plan = []
-    for layer in range(n_layers):
-        t = layer / (n_layers - 1) if n_layers > 1 else 0.0
-        W = int(round(W_first + (W_last - W_first) * t))
-        kk = int(round(k_first + (k_last - k_first) * t))
-        plan.append((layer in pillars, W, kk))
-    return plan
+    if n_layers < 1:
+        raise ValueError("n_layers >= 1")
+    arr = (TopoLayer * n_layers)()
+    rc = load_library().topo_pillar_plan(int(n_layers), int(W_first), int(k_first), int(W_last), int(k_last), arr)
+    if rc != 0:
+        raise TopoError(rc, "topo_pillar_plan")
+    return [(bool(arr[i].pillar), int(arr[i].W), int(arr[i].k)) for i in range(n_layers)]
+
+
+def topo_check_finite(buf, flag=None, stream=None):
+    """Set flag[0] (an int32 device tensor, not cleared here) to 1 if the float32 or bfloat16
+    device tensor `buf` holds a NaN or an infinity. Returns flag (read it after synchronising)."""
+    torch = _torch()
+    if flag is None:
+        flag = torch.zeros(1, dtype=torch.int32, device=buf.device)
+    _check_tensors(buf, flag)
+    rc = load_library().topo_check_finite(_ptr(buf), ctypes.c_size_t(buf.numel()), _dtype_code(buf), _ptr(flag),
+                                          _stream(stream))
+    if rc != 0:
+        raise TopoError(rc, "topo_check_finite")
+    return flag
+
+
+def topo_workspace_view(q, k, W: int, topk: int, softmax_scale: float = 1.0, causal: bool = True,
+                        q_pos0: int | None = None, op: int = TOPO_OP_DECODE, flags: int = 0) -> WorkspaceView:
+    """Where a call with these arguments leaves the key scan's candidate lists and each query's
+    selection path (TOPO_PATH_*) in its workspace (topo_workspace_view)."""
+    q4 = q if q.dim() == 4 else q.unsqueeze(2)
+    if q_pos0 is None:
+        q_pos0 = k.shape[2] - q4.shape[2]
+    p = _params(q4, k, W, topk, softmax_scale, causal, q_pos0, flags)
+    v = WorkspaceView()
+    rc = load_library().topo_workspace_view(ctypes.byref(p), int(op), ctypes.byref(v))
+    if rc != 0:
+        raise TopoError(rc, "topo_workspace_view")
+    return v
 
 
 def topo_attn_decode_layers(layers, plan, softmax_scale: float, q_pos0: int | None = None, flags: int = 0,

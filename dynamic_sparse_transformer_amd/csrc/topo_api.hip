@@ -3,6 +3,7 @@
 // include/topo_attn.h (condensate set of "The Condensate Theorem: Transformers are O(n), Not
 // O(n^2)", zh page, technical summary §3; softmax over the set, fr page, technical summary §3).
 #include <cmath>
+#include <cstddef>
 #include <cstdint>
 
 #include "../../include/topo_attn.h"
@@ -10,6 +11,11 @@
 
 static_assert(TOPO_FLAG_EXACT_SELECT == topo::FLAG_EXACT_SELECT && TOPO_FLAG_GROUP_SELECT == topo::FLAG_GROUP_SELECT,
               "flag values shared with the kernels");
+static_assert(TOPO_PATH_NONE == topo::PATH_NONE && TOPO_PATH_ALL == topo::PATH_ALL && TOPO_PATH_FAST == topo::PATH_FAST &&
+                  TOPO_PATH_BAND == topo::PATH_BAND && TOPO_PATH_EXACT_ASKED == topo::PATH_EXACT_ASKED &&
+                  TOPO_PATH_EXACT_OVERFLOW == topo::PATH_EXACT_OVERFLOW &&
+                  TOPO_PATH_EXACT_CROWDED == topo::PATH_EXACT_CROWDED,
+              "path codes shared with the kernels");
 
 namespace {
 
@@ -54,6 +60,11 @@ size_t certified_workspace_bytes(const topo_params_t* p) {
   size_t b = align256(topo::decode_workspace_bytes(p->B, p->Hq, decode_geom(p), p->k, p->d, p->dtype == TOPO_BF16));
   if (p->flags & TOPO_FLAG_DENSE_FALLBACK) b += topo::dense_workspace_bytes(p->B, p->Hq, 1, p->n_ctx, p->d);
   return b;
+}
+
+size_t prefill_ws(const topo_params_t* p) {
+  if (!topo::prefill_fits(p->W, p->k)) return 0;
+  return topo::prefill_workspace_bytes(p->B, p->Hq, p->Hkv, p->n_q, p->n_ctx, p->d, p->W, p->k);
 }
 
 int decode_like(const topo_params_t* p, const void* q, const void* k, const void* v, float* out,
@@ -140,7 +151,8 @@ int prefill_like(const topo_params_t* p, const void* q, const void* k, const voi
   if (softmax && (!v || !out || !aligned16(v) || !aligned16(out))) return TOPO_EINVAL;
   if (!softmax && (!sel_idx || !sel_count)) return TOPO_EINVAL;
   if ((sel_idx && !aligned16(sel_idx)) || (sel_count && !aligned16(sel_count))) return TOPO_EINVAL;
-  const size_t need = topo::prefill_workspace_bytes(p->B, p->Hq, p->n_q, p->n_ctx, p->d, p->W, p->k);
+  if (!topo::prefill_fits(p->W, p->k)) return TOPO_EUNSUPPORTED;
+  const size_t need = prefill_ws(p);
   if (!ws || ws_bytes < need || !aligned16(ws)) return TOPO_EWORKSPACE;
   topo::PrefillLaunch L{};
   L.q = q;
@@ -182,10 +194,10 @@ size_t topo_workspace_bytes(const topo_params_t* p, int op) {
       if (p->n_q != 1) return 0;
       return topo::decode_workspace_bytes(p->B, p->Hq, decode_geom(p), p->k, p->d, p->dtype == TOPO_BF16);
     case TOPO_OP_PREFILL:
-      return topo::prefill_workspace_bytes(p->B, p->Hq, p->n_q, p->n_ctx, p->d, p->W, p->k);
+      return prefill_ws(p);
     case TOPO_OP_SELECT:
       if (p->n_q == 1) return topo::decode_workspace_bytes(p->B, p->Hq, decode_geom(p), p->k, p->d, p->dtype == TOPO_BF16);
-      return topo::prefill_workspace_bytes(p->B, p->Hq, p->n_q, p->n_ctx, p->d, p->W, p->k);
+      return prefill_ws(p);
     case TOPO_OP_DENSE:
       return topo::dense_workspace_bytes(p->B, p->Hq, p->n_q, p->n_ctx, p->d);
     case TOPO_OP_DECODE_CERTIFIED:
@@ -298,6 +310,7 @@ size_t topo_layers_workspace_bytes(const topo_params_t* p, const topo_layer_t* l
     topo_params_t pl = *p;
     pl.W = layers[i].W;
     pl.k = layers[i].k;
+    if (layers[i].pillar) pl.flags &= ~TOPO_FLAG_GROUP_SELECT;
     const size_t b = layers[i].pillar ? topo_workspace_bytes(&pl, TOPO_OP_DENSE) : topo_workspace_bytes(&pl, TOPO_OP_DECODE);
     if (b == 0 || layers[i].reserved != 0 || (layers[i].pillar != 0 && layers[i].pillar != 1)) return 0;
     if (b > need) need = b;
@@ -311,6 +324,9 @@ int topo_attn_decode_layers(const topo_params_t* p, const topo_layer_t* layers, 
   int rc = check_params(p, false);
   if (rc) return rc;
   if (p->n_q != 1 || (p->flags & TOPO_FLAG_DENSE_FALLBACK)) return TOPO_EINVAL;
+  // the shared selection serves groups of up to four query heads (checked here, before any layer
+  // runs, as decode_like would check it at the first condensate-set layer)
+  if ((p->flags & TOPO_FLAG_GROUP_SELECT) && p->Hq / p->Hkv > 4) return TOPO_EUNSUPPORTED;
   // every layer checked before the first launch
   for (int32_t i = 0; i < n_layers; ++i) {
     const topo_layer_t& L = layers[i];
@@ -332,11 +348,76 @@ int topo_attn_decode_layers(const topo_params_t* p, const topo_layer_t* layers, 
     topo_params_t pl = *p;
     pl.W = L.W;
     pl.k = L.k;
+    if (L.pillar) pl.flags &= ~TOPO_FLAG_GROUP_SELECT;  // a dense layer has no selection to share
     rc = L.pillar ? topo_attn_dense(&pl, L.q, L.k_cache, L.v_cache, L.out, workspace, ws_bytes, stream)
                   : topo_attn_decode(&pl, L.q, L.k_cache, L.v_cache, L.out, L.sel_idx, L.sel_count, workspace,
                                      ws_bytes, stream);
     if (rc != TOPO_OK) return rc;
   }
+  return TOPO_OK;
+}
+
+int topo_pillar_plan(int32_t n_layers, int32_t W_first, int32_t k_first, int32_t W_last, int32_t k_last,
+                     topo_layer_t* layers) {
+  if (!layers || n_layers < 1 || W_first < 0 || k_first < 0 || W_last < 0 || k_last < 0) return TOPO_EINVAL;
+  // rint rounds halves to even (the default rounding mode)
+  int32_t n_pillar = (int32_t)std::rint((double)n_layers / 16.0);
+  if (n_pillar < 1) n_pillar = 1;
+  for (int32_t i = 0; i < n_layers; ++i) layers[i].pillar = 0;
+  for (int32_t i = 0; i < n_pillar; ++i) layers[(int64_t)i * n_layers / n_pillar].pillar = 1;
+  for (int32_t i = 0; i < n_layers; ++i) {
+    const double t = n_layers > 1 ? (double)i / (double)(n_layers - 1) : 0.0;
+    layers[i].W = (int32_t)std::rint((double)W_first + (double)(W_last - W_first) * t);
+    layers[i].k = (int32_t)std::rint((double)k_first + (double)(k_last - k_first) * t);
+  }
+  return TOPO_OK;
+}
+
+int topo_check_finite(const void* buf, size_t count, int32_t dtype, uint32_t* flag, hipStream_t stream) {
+  if (dtype != TOPO_F32 && dtype != TOPO_BF16) return TOPO_EUNSUPPORTED;
+  if (!flag || ((uintptr_t)flag & 3u) || (count > 0 && (!buf || !aligned16(buf)))) return TOPO_EINVAL;
+  if (count == 0) return TOPO_OK;
+  return topo::launch_check_finite(buf, count, dtype == TOPO_BF16, flag, stream) == hipSuccess ? TOPO_OK : TOPO_EHIP;
+}
+
+int topo_workspace_view(const topo_params_t* p, int op, topo_ws_view_t* view) {
+  if (!view) return TOPO_EINVAL;
+  int rc = check_params(p, true);
+  if (rc) return rc;
+  topo_ws_view_t v{};
+  if (op == TOPO_OP_PREFILL || (op == TOPO_OP_SELECT && p->n_q != 1)) {
+    if (!topo::prefill_fits(p->W, p->k)) return TOPO_EUNSUPPORTED;
+    const topo::PrefillView pv = topo::prefill_view(p->B, p->Hq, p->Hkv, p->n_q, p->n_ctx, p->d, p->k);
+    v.queries = (int64_t)p->B * p->Hq * p->n_q;
+    v.lists = 1;
+    v.slots = pv.slot;
+    v.count_offset = pv.count;
+    v.entry_offset = pv.entry;
+    v.eps_offset = 0;
+    v.path_offset = pv.path;
+    v.path_stride = sizeof(int32_t);
+    v.eps_coef = topo::prefill_eps_coef();
+  } else if (op == TOPO_OP_DECODE || op == TOPO_OP_SELECT || op == TOPO_OP_DECODE_CERTIFIED ||
+             op == TOPO_OP_DECODE_RAGGED) {
+    if (p->n_q != 1) return TOPO_EINVAL;
+    if (op == TOPO_OP_DECODE_RAGGED && p->causal != 1) return TOPO_EINVAL;
+    const topo::QueryGeom g = op == TOPO_OP_DECODE_RAGGED ? ragged_sizes_geom(p) : decode_geom(p);
+    const topo::DecodeView dv =
+        topo::decode_view(p->B, p->Hq, p->Hkv, g, p->k, p->d, p->dtype == TOPO_BF16);
+    const bool scan = p->k > 0 && p->k <= topo::KS_MAX_K && g.n_cand > p->k && !(p->flags & TOPO_FLAG_EXACT_SELECT);
+    v.queries = (int64_t)p->B * p->Hq;
+    v.lists = scan ? dv.lists : 0;
+    v.slots = dv.slot;
+    v.count_offset = dv.count;
+    v.entry_offset = dv.entry;
+    v.eps_offset = dv.eps;
+    v.path_offset = dv.state + offsetof(topo::HeadState, path);
+    v.path_stride = sizeof(topo::HeadState);
+    v.eps_coef = topo::fast_score_eps_coef(p->d);
+  } else {
+    return TOPO_EINVAL;
+  }
+  *view = v;
   return TOPO_OK;
 }
 

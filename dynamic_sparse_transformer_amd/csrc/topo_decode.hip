@@ -90,7 +90,8 @@ size_t decode_workspace_bytes(int32_t B, int32_t Hq, const QueryGeom& g, int32_t
   size_t bytes = align256(heads * sizeof(HeadState));
   bytes += align256(heads * (size_t)window_parts(g, d, bf16) * (size_t)(d + 2) * sizeof(double));
   for (int l = 0; l < L; ++l)
-    bytes += 2 * align256(heads * (size_t)nb[l] * 4) + align256(heads * (size_t)nb[l] * (size_t)slot * sizeof(uint2));
+    bytes += align256(heads * (size_t)nb[l] * 4) + align256(heads * (size_t)nb[l] * (size_t)slot * sizeof(uint2)) +
+             align256(heads * (size_t)nb[l] * (size_t)slot * sizeof(float));
   return bytes;
 }
 
@@ -109,11 +110,30 @@ void decode_carve(void* ws, int32_t B, int32_t Hq, const QueryGeom& g, int32_t k
   for (int l = 0; l < L.nlevels; ++l) {
     L.blk_cnt[l] = (uint32_t*)p;
     p += align256(heads * (size_t)L.nblk[l] * 4);
-    L.blk_eps[l] = (float*)p;
-    p += align256(heads * (size_t)L.nblk[l] * 4);
     L.surv[l] = (uint2*)p;
     p += align256(heads * (size_t)L.nblk[l] * (size_t)L.slot * sizeof(uint2));
+    L.surv_eps[l] = (float*)p;
+    p += align256(heads * (size_t)L.nblk[l] * (size_t)L.slot * sizeof(float));
   }
+}
+
+DecodeView decode_view(int32_t B, int32_t Hq, int32_t Hkv, const QueryGeom& g, int32_t k, int32_t d, int32_t bf16) {
+  DecodeLaunch L{};
+  L.B = B;
+  L.Hq = Hq;
+  L.Hkv = Hkv;
+  L.G = Hq / Hkv;
+  L.d = d;
+  L.bf16 = bf16;
+  decode_carve(nullptr, B, Hq, g, k, L);
+  DecodeView v;
+  v.state = (size_t)(uintptr_t)L.st;
+  v.count = (size_t)(uintptr_t)L.blk_cnt[0];
+  v.entry = (size_t)(uintptr_t)L.surv[0];
+  v.eps = (size_t)(uintptr_t)L.surv_eps[0];
+  v.lists = L.nblk[0];
+  v.slot = L.slot;
+  return v;
 }
 
 // Geometry of batch element b's query from its position pos[b] (clamped into the cache; causal).
@@ -312,8 +332,8 @@ struct KscanArgs {
   const unsigned char* q;
   HeadState* st;
   uint32_t* blk_cnt;
-  float* blk_eps;
   uint2* surv;
+  float* surv_eps;
   int64_t n, nblk, slot;
   int64_t p, w_lo, vis_hi, scan_hi;
   const int64_t* pos;  // may be null: causal query position of each batch element
@@ -347,8 +367,8 @@ __global__ __launch_bounds__(256, TOPO_KS_MIN_BLOCKS) void kscan_kernel(KscanArg
   constexpr int L = 8;          // lanes per key row
   constexpr int CPL = RB / 128; // 16-byte chunks of a row per lane
   __shared__ uint2 wbuf[KS_WAVES][GT][KS_WAVE_CAP];
+  __shared__ float wbe[KS_WAVES][GT][KS_WAVE_CAP];  // each entry's error bound
   __shared__ int wcnt[KS_WAVES][GT];
-  __shared__ float weps[KS_WAVES][GT];
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, s = lane & 7;
   const int grp = blockIdx.y;
@@ -366,11 +386,7 @@ __global__ __launch_bounds__(256, TOPO_KS_MIN_BLOCKS) void kscan_kernel(KscanArg
     q_vis = gq.vis_hi;
     q_scan = gq.scan_hi;
     if ((int64_t)blockIdx.x * KS_KEYS_PER_RUN * a.runs > q_scan) {
-      if (tid < nh) {
-        const size_t bslot = ((size_t)b * a.Hq + h0 + tid) * (size_t)a.nblk + blockIdx.x;
-        a.blk_cnt[bslot] = 0u;
-        a.blk_eps[bslot] = 0.f;
-      }
+      if (tid < nh) a.blk_cnt[((size_t)b * a.Hq + h0 + tid) * (size_t)a.nblk + blockIdx.x] = 0u;
       return;
     }
   }
@@ -400,6 +416,7 @@ __global__ __launch_bounds__(256, TOPO_KS_MIN_BLOCKS) void kscan_kernel(KscanArg
     for (int o = 1; o < L; o <<= 1) part += __shfl_xor(part, o);
     qn[h] = (float)sqrt(part) * (1.0f + 0x1p-20f);
   }
+  // With cq[h] = eps_coef |q_h|, a key of norm |k| has the error bound cq[h] |k| (its own).
   // Shared selection: the group score max_h s_h of a key is ranked as the scores of one head
   // (slot 0); |max_h s^_h - max_h s_h| <= max_h eps_h, so head 0 takes the largest |q_h|.
   const int nsel = GROUP ? 1 : nh;
@@ -408,6 +425,9 @@ __global__ __launch_bounds__(256, TOPO_KS_MIN_BLOCKS) void kscan_kernel(KscanArg
     for (int h = 1; h < GT; ++h)
       if (h < nh) qn[0] = fmaxf(qn[0], qn[h]);
   }
+  float cq[GT];
+#pragma unroll
+  for (int h = 0; h < GT; ++h) cq[h] = a.eps_coef * qn[h];
 
   // The block ranks a.runs runs of KS_WAVES x KS_KEYS_PER_WAVE keys; in run r, wave w takes the
   // KS_KEYS_PER_WAVE keys starting at run_key0(r).
@@ -420,18 +440,19 @@ __global__ __launch_bounds__(256, TOPO_KS_MIN_BLOCKS) void kscan_kernel(KscanArg
   const int64_t my_off = 8 * s + (lane >> 3);  // key of this lane within a tile after the reduction
 
   float sc[GT][KS_IT];
+  float kn[KS_IT];  // norm of the lane's key of each tile of the run (rounded up)
   uint32_t vmask = 0;
-  float cmax2[CPL];  // largest squared norm of the chunks this lane has loaded, per chunk slot
-#pragma unroll
-  for (int c = 0; c < CPL; ++c) cmax2[c] = 0.f;
 
   // One tile in registers. Per key group i (8 keys, one per lane group): partial dot products of
-  // this lane's chunks with every query of the slice, then the chunk norms; right after that the
-  // registers of group i are reloaded with group i of the next tile (of this run or the next),
-  // so loads stream out during the whole scan. The loads are unconditional (rows past the end of
-  // the scan are clamped to its last row and never selected), which keeps the wait counts exact.
-  // Then per head a reduce-scatter over the 8 lanes, and the scores enter a register shift queue
-  // (sc[h][KS_IT-1] is the newest) so that every register index stays static.
+  // this lane's chunks with every query of the slice and the partial squared norm of the key;
+  // right after that the registers of group i are reloaded with group i of the next tile (of
+  // this run or the next), so loads stream out during the whole scan. The loads are
+  // unconditional (rows past the end of the scan are clamped to its last row and never
+  // selected), which keeps the wait counts exact. Then per head, and for the squared norms, a
+  // reduce-scatter over the 8 lanes, and the scores and norms enter register shift queues
+  // (sc[h][KS_IT-1] is the newest) so that every register index stays static. The squares of
+  // bf16 values are exact in float32 and the float32 sum of the d squares carries a relative
+  // error below 2^-19 (float32 data: below 2^-18), covered by the factor that rounds the norm up.
   uint4 kv[8][CPL];
   kscan_load<RB>(kv, kb, run_key0(0), last_row, lane);
   const int kr = lane >> 3;
@@ -439,6 +460,7 @@ __global__ __launch_bounds__(256, TOPO_KS_MIN_BLOCKS) void kscan_kernel(KscanArg
     const bool nfull = nrow0 + 63 <= last_row;
     const unsigned char* nbase = kb + (nrow0 + kr) * RB + s * 16;
     float P[GT][8];
+    float N2[1][8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
 #pragma unroll
@@ -448,8 +470,10 @@ __global__ __launch_bounds__(256, TOPO_KS_MIN_BLOCKS) void kscan_kernel(KscanArg
         for (int c = 0; c < CPL; ++c) acc = dot_chunk<BF16>(kv[i][c], qv[h][c], acc);
         P[h][i] = acc;
       }
+      float n2 = 0.f;
 #pragma unroll
-      for (int c = 0; c < CPL; ++c) cmax2[c] = fmaxf(cmax2[c], dot_chunk<BF16>(kv[i][c], kv[i][c], 0.f));
+      for (int c = 0; c < CPL; ++c) n2 = dot_chunk<BF16>(kv[i][c], kv[i][c], n2);
+      N2[0][i] = n2;
       if (more) {
         const int64_t row = nrow0 + 8 * i + kr;
         const unsigned char* p = nfull ? nbase + (size_t)i * 8 * RB : kb + (row <= last_row ? row : last_row) * RB + s * 16;
@@ -467,6 +491,10 @@ __global__ __launch_bounds__(256, TOPO_KS_MIN_BLOCKS) void kscan_kernel(KscanArg
       for (int i = 0; i + 1 < KS_IT; ++i) sc[h][i] = sc[h][i + 1];
       sc[h][KS_IT - 1] = Q1[0][0];
     }
+    reduce_scatter<8, 1>(N2, s);
+#pragma unroll
+    for (int i = 0; i + 1 < KS_IT; ++i) kn[i] = kn[i + 1];
+    kn[KS_IT - 1] = sqrtf(N2[0][0]) * (1.0f + 0x1p-16f);
     const int64_t j = row0 + my_off;
     const bool valid = j >= 1 && j <= q_vis && (j < q_wlo || j > q_p);
     vmask = (vmask >> 1) | ((valid ? 1u : 0u) << (KS_IT - 1));
@@ -479,8 +507,6 @@ __global__ __launch_bounds__(256, TOPO_KS_MIN_BLOCKS) void kscan_kernel(KscanArg
     wtotal[h] = 0;
     trun[h] = 0u;
   }
-  bool seen_valid = false;
-  float kmax = 0.f;
 #pragma unroll 1
   for (int r = 0; r < a.runs; ++r) {
     const int64_t key0 = run_key0(r);
@@ -502,30 +528,13 @@ __global__ __launch_bounds__(256, TOPO_KS_MIN_BLOCKS) void kscan_kernel(KscanArg
         for (int h = 1; h < GT; ++h)
           if (h < nh) sc[0][it] = fmaxf(sc[0][it], sc[h][it]);
     }
-
-    // Norm bound of every key seen so far: |k|^2 = sum over its chunks of |chunk|^2 <= sum over
-    // the chunk slots (c, s) of the largest |chunk|^2 seen in that slot (lanes with equal s
-    // share the slots). The float32 chunk norms carry relative error below 2^-19, covered by the
-    // factor.
-    float kbound2 = 0.f;
-#pragma unroll
-    for (int c = 0; c < CPL; ++c) {
-      float m = cmax2[c];
-      for (int o = L; o < 64; o <<= 1) m = fmaxf(m, __shfl_xor(m, o));
-      kbound2 += m;
-    }
-    for (int o = 1; o < L; o <<= 1) kbound2 += __shfl_xor(kbound2, o);
-    kmax = sqrtf(kbound2) * (1.0f + 0x1p-16f);
     const bool any_valid = __ballot(vmask != 0u) != 0ull;
     if (!any_valid) continue;
-    seen_valid = true;
 
-    // Local thresholds: k distinct keys of this run have lower bounds at or above T (earlier
-    // runs' thresholds stay valid). For k <= 64 all heads share one bitwise search over the
-    // k-th largest of each lane's two best lower bounds; larger k take the exact k-th largest.
-    float eps_r[GT];
-#pragma unroll
-    for (int h = 0; h < GT; ++h) eps_r[h] = a.eps_coef * qn[h] * kmax + 1e-30f;
+    // Local thresholds: k distinct keys of this run have lower bounds (score minus the key's own
+    // error bound) at or above T (earlier runs' thresholds stay valid). For k <= 64 all heads
+    // share one bitwise search over the k-th largest of each lane's two best lower bounds;
+    // larger k take the exact k-th largest.
     if (a.topk <= 64) {
       uint32_t m0[GT], m1[GT], T[GT];
 #pragma unroll
@@ -533,13 +542,12 @@ __global__ __launch_bounds__(256, TOPO_KS_MIN_BLOCKS) void kscan_kernel(KscanArg
         float x0 = -INFINITY, x1 = -INFINITY;
 #pragma unroll
         for (int it = 0; it < KS_IT; ++it) {
-          const float x = ((vmask >> it) & 1u) ? sc[h][it] : -INFINITY;
+          const float x = ((vmask >> it) & 1u) ? sc[h][it] - cq[h] * kn[it] : -INFINITY;
           x1 = fmaxf(x1, fminf(x0, x));
           x0 = fmaxf(x0, x);
         }
-        // lower bounds are monotone in the score, so these are the two best lower bounds
-        m0[h] = x0 == -INFINITY ? 0u : ord_f32(x0 - eps_r[h]);
-        m1[h] = x1 == -INFINITY ? 0u : ord_f32(x1 - eps_r[h]);
+        m0[h] = x0 == -INFINITY ? 0u : ord_f32(x0);
+        m1[h] = x1 == -INFINITY ? 0u : ord_f32(x1);
         T[h] = 0u;
       }
       // The search only matters where it can beat the best known bound: fewer than k values
@@ -572,7 +580,7 @@ __global__ __launch_bounds__(256, TOPO_KS_MIN_BLOCKS) void kscan_kernel(KscanArg
         if (h >= nsel) break;
         uint32_t lb[KS_IT];
 #pragma unroll
-        for (int it = 0; it < KS_IT; ++it) lb[it] = ((vmask >> it) & 1u) ? ord_f32(sc[h][it] - eps_r[h]) : 0u;
+        for (int it = 0; it < KS_IT; ++it) lb[it] = ((vmask >> it) & 1u) ? ord_f32(sc[h][it] - cq[h] * kn[it]) : 0u;
         trun[h] = max(trun[h], wave_kth_largest<KS_IT>(lb, a.topk));
       }
     }
@@ -580,19 +588,21 @@ __global__ __launch_bounds__(256, TOPO_KS_MIN_BLOCKS) void kscan_kernel(KscanArg
 #pragma unroll
     for (int h = 0; h < GT; ++h) {
       if (h >= nsel) break;
-      // eps grows with the norm bound, so the last run's value covers every earlier entry
-      const float eps = eps_r[h];
       const uint32_t th_g = thp[h];
       const uint32_t th = max(trun[h], th_g);
-      // Hand this run's survivors (upper bound at or above the threshold) to the block merge.
+      // Hand this run's survivors (upper bound at or above the threshold) to the block merge,
+      // each with its own error bound.
 #pragma unroll
       for (int it = 0; it < KS_IT; ++it) {
-        const bool ok = ((vmask >> it) & 1u) && ord_f32(sc[h][it] + eps) >= th;
+        const float e = cq[h] * kn[it];
+        const bool ok = ((vmask >> it) & 1u) && ord_f32(sc[h][it] + e) >= th;
         const uint64_t m = __ballot(ok);
         if (ok) {
           const int pos = wtotal[h] + lanes_below(m);
-          if (pos < KS_WAVE_CAP)
+          if (pos < KS_WAVE_CAP) {
             wbuf[wave][h][pos] = make_uint2(__float_as_uint(sc[h][it]), (uint32_t)(key0 + (int64_t)it * KS_ROWS + my_off));
+            wbe[wave][h][pos] = e;
+          }
         }
         wtotal[h] += __popcll(m);
       }
@@ -601,13 +611,15 @@ __global__ __launch_bounds__(256, TOPO_KS_MIN_BLOCKS) void kscan_kernel(KscanArg
       if (r + 1 < a.runs && wtotal[h] > KS_WAVE_CAP / 2 && wtotal[h] <= KS_WAVE_CAP) {
         constexpr int PER = KS_WAVE_CAP / 64;
         uint2 e[PER];
+        float ee[PER];
         uint32_t lbk[PER];
         const int c = wtotal[h];
 #pragma unroll
         for (int t = 0; t < PER; ++t) {
           const int idx = lane + 64 * t;
           e[t] = idx < c ? wbuf[wave][h][idx] : make_uint2(0u, 0u);
-          lbk[t] = idx < c ? ord_f32(__uint_as_float(e[t].x) - eps) : 0u;
+          ee[t] = idx < c ? wbe[wave][h][idx] : 0.f;
+          lbk[t] = idx < c ? ord_f32(__uint_as_float(e[t].x) - ee[t]) : 0u;
         }
         trun[h] = max(trun[h], wave_kth_largest<PER>(lbk, a.topk));
         const uint32_t thc = max(trun[h], th_g);
@@ -616,9 +628,12 @@ __global__ __launch_bounds__(256, TOPO_KS_MIN_BLOCKS) void kscan_kernel(KscanArg
 #pragma unroll
         for (int t = 0; t < PER; ++t) {
           const int idx = lane + 64 * t;
-          const bool keep = idx < c && ord_f32(__uint_as_float(e[t].x) + eps) >= thc;
+          const bool keep = idx < c && ord_f32(__uint_as_float(e[t].x) + ee[t]) >= thc;
           const uint64_t m = __ballot(keep);
-          if (keep) wbuf[wave][h][nc + lanes_below(m)] = e[t];
+          if (keep) {
+            wbuf[wave][h][nc + lanes_below(m)] = e[t];
+            wbe[wave][h][nc + lanes_below(m)] = ee[t];
+          }
           nc += __popcll(m);
         }
         wtotal[h] = nc;
@@ -628,21 +643,14 @@ __global__ __launch_bounds__(256, TOPO_KS_MIN_BLOCKS) void kscan_kernel(KscanArg
   }
   if (lane == 0) {
 #pragma unroll
-    for (int h = 0; h < GT; ++h) {
-      wcnt[wave][h] = wtotal[h];
-      weps[wave][h] = seen_valid ? a.eps_coef * qn[h] * kmax + 1e-30f : 0.f;
-    }
+    for (int h = 0; h < GT; ++h) wcnt[wave][h] = wtotal[h];
   }
   __syncthreads();
 
   // Block merge: wave h merges the four waves' survivors of query head h (shared selection: wave
   // 0 the group's, and the other heads of the slice get empty lists).
   if (wave >= nsel) {
-    if (wave < nh && lane == 0) {
-      const size_t bslot = ((size_t)b * a.Hq + h0 + wave) * (size_t)a.nblk + blockIdx.x;
-      a.blk_cnt[bslot] = 0u;
-      a.blk_eps[bslot] = 0.f;
-    }
+    if (wave < nh && lane == 0) a.blk_cnt[((size_t)b * a.Hq + h0 + wave) * (size_t)a.nblk + blockIdx.x] = 0u;
     return;
   }
   const int h = wave;
@@ -651,7 +659,6 @@ __global__ __launch_bounds__(256, TOPO_KS_MIN_BLOCKS) void kscan_kernel(KscanArg
   const size_t bslot = head * (size_t)a.nblk + blockIdx.x;
   static_assert(KS_WAVES == 4, "the block merge below is written for four waves");
   const int c0 = wcnt[0][h], c1 = wcnt[1][h], c2 = wcnt[2][h], c3 = wcnt[3][h];
-  const float eps_b = fmaxf(fmaxf(weps[0][h], weps[1][h]), fmaxf(weps[2][h], weps[3][h]));
   const bool over = c0 > KS_WAVE_CAP || c1 > KS_WAVE_CAP || c2 > KS_WAVE_CAP || c3 > KS_WAVE_CAP;
   const int p1 = c0, p2 = c0 + c1, p3 = c0 + c1 + c2;
   const int total = p3 + c3;
@@ -663,13 +670,16 @@ __global__ __launch_bounds__(256, TOPO_KS_MIN_BLOCKS) void kscan_kernel(KscanArg
     return;
   }
   // Entries are read from LDS on every pass (few registers stay live).
-  auto entry = [&](int idx) -> uint2 {
+  auto wsel = [&](int idx, int& i) -> int {
     const int w = (idx >= p1) + (idx >= p2) + (idx >= p3);
-    const int i = idx - (w == 0 ? 0 : w == 1 ? p1 : w == 2 ? p2 : p3);
-    return wbuf[w][h][i];
+    i = idx - (w == 0 ? 0 : w == 1 ? p1 : w == 2 ? p2 : p3);
+    return w;
   };
   auto lbkey = [&](int idx) -> uint32_t {
-    return idx < total ? ord_f32(__uint_as_float(entry(idx).x) - eps_b) : 0u;
+    if (idx >= total) return 0u;
+    int i;
+    const int w = wsel(idx, i);
+    return ord_f32(__uint_as_float(wbuf[w][h][i].x) - wbe[w][h][i]);
   };
   constexpr int PER = KS_WAVES * KS_WAVE_CAP / 64;
   uint32_t T = 0;
@@ -694,15 +704,26 @@ __global__ __launch_bounds__(256, TOPO_KS_MIN_BLOCKS) void kscan_kernel(KscanArg
   const uint32_t th_g = *(volatile const uint32_t*)&hs->theta;
   const uint32_t th = max(T, th_g);
   uint2* out = a.surv + bslot * (size_t)a.slot;
+  float* oeps = a.surv_eps + bslot * (size_t)a.slot;
   int cnt = 0;
   for (int r = 0; r < PER; ++r) {
     const int idx = lane + 64 * r;
-    const uint2 e = idx < total ? entry(idx) : make_uint2(0u, 0u);
-    const bool ok = idx < total && ord_f32(__uint_as_float(e.x) + eps_b) >= th;
+    uint2 e = make_uint2(0u, 0u);
+    float ee = 0.f;
+    if (idx < total) {
+      int i;
+      const int w = wsel(idx, i);
+      e = wbuf[w][h][i];
+      ee = wbe[w][h][i];
+    }
+    const bool ok = idx < total && ord_f32(__uint_as_float(e.x) + ee) >= th;
     const uint64_t m = __ballot(ok);
     if (ok) {
       const int pos = cnt + lanes_below(m);
-      if (pos < a.slot) out[pos] = e;
+      if (pos < a.slot) {
+        out[pos] = e;
+        oeps[pos] = ee;
+      }
     }
     cnt += __popcll(m);
   }
@@ -713,7 +734,6 @@ __global__ __launch_bounds__(256, TOPO_KS_MIN_BLOCKS) void kscan_kernel(KscanArg
     } else {
       a.blk_cnt[bslot] = (uint32_t)cnt;
     }
-    a.blk_eps[bslot] = eps_b;
     if (T > th_g) atomicMax(&hs->theta, T);
   }
 }
@@ -721,17 +741,17 @@ __global__ __launch_bounds__(256, TOPO_KS_MIN_BLOCKS) void kscan_kernel(KscanArg
 // ---------------------------------------------------------------------------------------------
 // merge_lists: one wave per (group of MERGE_FAN survivor lists, head). Keeps the entries of the
 // group that may still be in the top-k: the k-th best lower bound of the group (or the shared
-// threshold, if higher) against every entry's upper bound, with the largest error bound of the
-// group for all of them. Output has the same layout, one list per group.
+// threshold, if higher) against every entry's upper bound, each entry with its own error bound.
+// Output has the same layout, one list per group.
 struct MergeArgs {
   const HeadState* st;
   HeadState* st_w;
   const uint32_t* cnt_in;
-  const float* eps_in;
   const uint2* surv_in;
+  const float* eps_in;
   uint32_t* cnt_out;
-  float* eps_out;
   uint2* surv_out;
+  float* eps_out;
   int64_t nblk_in, nblk_out, slot;
   int32_t topk;
 };
@@ -745,32 +765,28 @@ __global__ __launch_bounds__(64) void merge_lists_kernel(MergeArgs a) {
   const size_t in0 = head * (size_t)a.nblk_in + g0;
   const size_t oslot = head * (size_t)a.nblk_out + blockIdx.x;
   uint32_t c = 0;
-  float e = 0.f;
-  if (lane < nin) {
-    c = a.cnt_in[in0 + lane];
-    e = a.eps_in[in0 + lane];
-  }
+  if (lane < nin) c = a.cnt_in[in0 + lane];
   const bool over = __ballot(c == KS_OVERFLOW) != 0ull;
   if (over) {
     if (lane == 0) {
       a.cnt_out[oslot] = KS_OVERFLOW;
-      a.eps_out[oslot] = 0.f;
       a.st_w[head].overflow = 1u;
     }
     return;
   }
-  const float eps = wave_max_f32(e);
   const int incl = wave_incl_scan_i32((int)c);
   const int total = __shfl(incl, 63);
   int pre[MERGE_FAN];  // start of list i in the flat order
 #pragma unroll
   for (int i = 0; i < MERGE_FAN; ++i) pre[i] = i == 0 ? 0 : __shfl(incl, i - 1);
   uint2 ent[PER];
+  float ee[PER];
   uint32_t lbk[PER];
 #pragma unroll
   for (int r = 0; r < PER; ++r) {
     const int f = lane + 64 * r;
     ent[r] = make_uint2(0u, 0u);
+    ee[r] = 0.f;
     if (f < total) {
       int w = 0;
 #pragma unroll
@@ -778,22 +794,28 @@ __global__ __launch_bounds__(64) void merge_lists_kernel(MergeArgs a) {
       int base = 0;
 #pragma unroll
       for (int i = 0; i < MERGE_FAN; ++i) base = i == w ? pre[i] : base;
-      ent[r] = a.surv_in[(in0 + w) * (size_t)a.slot + (f - base)];
+      const size_t at = (in0 + w) * (size_t)a.slot + (f - base);
+      ent[r] = a.surv_in[at];
+      ee[r] = a.eps_in[at];
     }
   }
 #pragma unroll
-  for (int r = 0; r < PER; ++r) lbk[r] = lane + 64 * r < total ? ord_f32(__uint_as_float(ent[r].x) - eps) : 0u;
+  for (int r = 0; r < PER; ++r) lbk[r] = lane + 64 * r < total ? ord_f32(__uint_as_float(ent[r].x) - ee[r]) : 0u;
   const uint32_t T = total >= a.topk ? wave_threshold<PER>(lbk, a.topk) : 0u;
   const uint32_t th = max(T, a.st[head].theta);
   uint2* out = a.surv_out + oslot * (size_t)a.slot;
+  float* oeps = a.eps_out + oslot * (size_t)a.slot;
   int cnt = 0;
 #pragma unroll
   for (int r = 0; r < PER; ++r) {
-    const bool ok = lane + 64 * r < total && ord_f32(__uint_as_float(ent[r].x) + eps) >= th;
+    const bool ok = lane + 64 * r < total && ord_f32(__uint_as_float(ent[r].x) + ee[r]) >= th;
     const uint64_t m = __ballot(ok);
     if (ok) {
       const int pos = cnt + lanes_below(m);
-      if (pos < a.slot) out[pos] = ent[r];
+      if (pos < a.slot) {
+        out[pos] = ent[r];
+        oeps[pos] = ee[r];
+      }
     }
     cnt += __popcll(m);
   }
@@ -804,16 +826,19 @@ __global__ __launch_bounds__(64) void merge_lists_kernel(MergeArgs a) {
     } else {
       a.cnt_out[oslot] = (uint32_t)cnt;
     }
-    a.eps_out[oslot] = eps;
   }
 }
 
 // ---------------------------------------------------------------------------------------------
 // decode_finish: one block of 512 threads per (batch, query head).
 //   1. Stage the head's scan survivors in LDS (every load in flight at once), as order keys of
-//      their lower and upper score bounds.
-//   2. Exact k-th largest lower bound by an 11 + 11 + 10 bit radix select in LDS; the short list
-//      is every survivor whose upper bound reaches it (it holds the whole top-k).
+//      their lower and upper score bounds (each entry with its own key's error bound).
+//   2. A threshold T that at least k of the survivors' lower bounds reach (distinct keys, so no
+//      key whose upper bound is below T can be in the top-k): for k <= 64 a ten-step search for
+//      the largest T = lo + c (hi - lo) / 1024 between the smallest of the 64 lane maxima and the
+//      largest value, which lies at most (hi - lo) / 1024 below the k-th largest lower bound; for
+//      larger k, or a narrower range, the exact k-th largest by a bitwise search. The short list
+//      is every survivor whose upper bound reaches T (it holds the whole top-k).
 //   3. Float64 canonical scores of the short list and the anchor; exact ranks by (score desc,
 //      position asc).
 //   4. The set {0} u window u top-k, ascending.
@@ -832,10 +857,10 @@ struct FinishArgs {
   int32_t* sel_idx;
   int32_t* sel_count;
   float* rho;
-  const HeadState* st;
+  HeadState* st;
   const uint32_t* blk_cnt;
-  const float* blk_eps;
   const uint2* surv;
+  const float* surv_eps;
   int64_t n, nblk, slot;
   int64_t p, w_lo, vis_hi, scan_hi, n_cand;
   const int64_t* pos;  // may be null: causal query position of each batch element
@@ -1024,8 +1049,8 @@ __device__ int stage_survivors(FinishSmem* sm, const FinishArgs& a, int bh, uint
   const int64_t nblk = a.nblk;
   const int slot = (int)a.slot;
   const uint32_t* bc = a.blk_cnt + (size_t)bh * nblk;
-  const float* be = a.blk_eps + (size_t)bh * nblk;
   const uint2* sv = a.surv + (size_t)bh * nblk * slot;
+  const float* se = a.surv_eps + (size_t)bh * nblk * slot;
   int tpl = 1;
   while (tpl < 64 && (int64_t)tpl * 2 * nblk <= FIN_THREADS) tpl *= 2;
   const int lpp = FIN_THREADS / tpl;  // lists per pass
@@ -1038,31 +1063,33 @@ __device__ int stage_survivors(FinishSmem* sm, const FinishArgs& a, int bh, uint
     const int qi = tid < qn ? tid : qn - 1;
     qraw = qb == 2 ? (uint32_t)((const uint16_t*)qrow)[qi] : ((const uint32_t*)qrow)[qi];
   };
-  // loads of batch (l0, jb): count, error bound and BATCH entries of list l0 + tid / tpl. The
-  // addresses are clamped into the arrays and every load is issued (no branches, so no load
-  // waits for another); entries past the list's count, or of a list past the last, are ignored.
-  auto load_batch = [&](int64_t l0, int jb, uint2 (&e)[BATCH], uint32_t& c, float& eps) {
+  // loads of batch (l0, jb): count and BATCH entries (with their error bounds) of list
+  // l0 + tid / tpl. The addresses are clamped into the arrays and every load is issued (no
+  // branches, so no load waits for another); entries past the list's count, or of a list past
+  // the last, are ignored.
+  auto load_batch = [&](int64_t l0, int jb, uint2 (&e)[BATCH], float (&ee)[BATCH], uint32_t& c) {
     const int64_t l = l0 + tid / tpl;
     const int64_t lc = l < nblk ? l : nblk - 1;
     c = bc[lc];
-    eps = be[lc];
     if (l >= nblk) c = 0u;
     const int j0 = jb + sub;
 #pragma unroll
     for (int u = 0; u < BATCH; ++u) {
       const int j = j0 + u * tpl;
-      e[u] = sv[(size_t)lc * slot + (j < slot ? j : slot - 1)];
+      const size_t at = (size_t)lc * slot + (j < slot ? j : slot - 1);
+      e[u] = sv[at];
+      ee[u] = se[at];
     }
   };
   // keep the entries whose upper bound reaches theta: append them to the LDS arrays
-  auto filter_batch = [&](int jb, const uint2 (&e)[BATCH], uint32_t c, float eps) {
+  auto filter_batch = [&](int jb, const uint2 (&e)[BATCH], const float (&ee)[BATCH], uint32_t c) {
     if (c > (uint32_t)slot) c = 0u;  // overflowed list: the head is on the exact path anyway
     const int j0 = jb + sub;
     uint32_t keep = 0u;
 #pragma unroll
     for (int u = 0; u < BATCH; ++u) {
       const int j = j0 + u * tpl;
-      const bool k = j < (int)c && ord_f32(__uint_as_float(e[u].x) + eps) >= theta;
+      const bool k = j < (int)c && ord_f32(__uint_as_float(e[u].x) + ee[u]) >= theta;
       keep |= (k ? 1u : 0u) << u;
     }
     const int n = __popc(keep);
@@ -1075,8 +1102,8 @@ __device__ int stage_survivors(FinishSmem* sm, const FinishArgs& a, int bh, uint
       if ((keep >> u) & 1u) {
         if (base < SURV_LDS) {
           const float sf = __uint_as_float(e[u].x);
-          sm->u.s.lbk[base] = ord_f32(sf - eps);
-          sm->u.s.ubk[base] = ord_f32(sf + eps);
+          sm->u.s.lbk[base] = ord_f32(sf - ee[u]);
+          sm->u.s.ubk[base] = ord_f32(sf + ee[u]);
           sm->u.s.sidx[base] = (int32_t)e[u].y;
         }
         ++base;
@@ -1084,21 +1111,21 @@ __device__ int stage_survivors(FinishSmem* sm, const FinishArgs& a, int bh, uint
     }
   };
   uint2 e[BATCH];
+  float ee[BATCH];
   uint32_t c;
-  float eps;
   if (nblk <= lpp && slot <= tpl * BATCH) {
     // the usual case: every list in one batch
-    load_batch(0, 0, e, c, eps);
+    load_batch(0, 0, e, ee, c);
     request_rest();
     __syncthreads();  // the cleared counter
-    filter_batch(0, e, c, eps);
+    filter_batch(0, e, ee, c);
   } else {
     request_rest();
     __syncthreads();
     for (int64_t l0 = 0; l0 < nblk; l0 += lpp) {
       for (int jb = 0; jb < slot; jb += tpl * BATCH) {  // same trip count in every lane
-        load_batch(l0, jb, e, c, eps);
-        filter_batch(jb, e, c, eps);
+        load_batch(l0, jb, e, ee, c);
+        filter_batch(jb, e, ee, c);
       }
     }
   }
@@ -1171,9 +1198,11 @@ __global__ __launch_bounds__(FIN_THREADS) void decode_finish_kernel(FinishArgs a
   bool fast = false;
   int nr = 0;
   bool exact = false, take_all = false;
+  int32_t path = PATH_NONE;
   if (a.topk > 0 && a.n_cand > 0) {
     exact = (a.flags & 1) != 0 || a.topk > KS_MAX_K;
     take_all = a.n_cand <= a.topk;
+    path = take_all ? PATH_ALL : exact ? PATH_EXACT_ASKED : PATH_FAST;
     if (!take_all && !exact) {
       uint32_t st_theta = 0u, st_over = 0u;
       const int M = stage_survivors(sm, a, sh, st_theta, st_over, qrow, BF16 ? 2 : 4, D, qraw);
@@ -1182,6 +1211,7 @@ __global__ __launch_bounds__(FIN_THREADS) void decode_finish_kernel(FinishArgs a
         // a scan block overflowed its slot, more survivors than LDS holds, or (impossibly) fewer
         // than k: the exact path
         exact = true;
+        path = st_over != 0 ? PATH_EXACT_OVERFLOW : PATH_EXACT_CROWDED;
       } else {
         // A valid threshold: at least k of the threads' best lower bounds (distinct keys) reach
         // it. Only values at or above the shared bound st_theta matter. For k <= 64 the search
@@ -1264,11 +1294,17 @@ __global__ __launch_bounds__(FIN_THREADS) void decode_finish_kernel(FinishArgs a
         }
         __syncthreads();
         nr = sm->ival[4];
-        if (nr > REFINE_CAP || nr < a.topk) exact = true; else fast = true;
+        if (nr > REFINE_CAP || nr < a.topk) {
+          exact = true;
+          path = PATH_EXACT_CROWDED;
+        } else {
+          fast = true;
+        }
       }
       __syncthreads();
     }
   }
+  if (tid == 0) a.st[bh].path = path;
   if (!q_requested && tid < D) qraw = BF16 ? (uint32_t)((const uint16_t*)qrow)[tid] : ((const uint32_t*)qrow)[tid];
   asm volatile("" : "+v"(qraw));  // the conversion stays here, after the staging
   if (tid < D) sm->qd[tid] = (double)__uint_as_float(BF16 ? qraw << 16 : qraw);
@@ -1303,13 +1339,13 @@ __global__ __launch_bounds__(FIN_THREADS) void decode_finish_kernel(FinishArgs a
     const int chunk = (nr + parts - 1) / parts;
     for (int idx = tid; idx < nr * parts; idx += FIN_THREADS) {
       const int i = idx % nr, part = idx / nr;
-      const double si = rk_s[i];
+      const uint64_t ki = ord_f64(rk_s[i]);
       const int32_t ji = sm->ridx[i];
       const int r1 = min(nr, (part + 1) * chunk);
       int cnt = 0;
       for (int r = part * chunk; r < r1; ++r) {
-        const double sr = rk_s[r];
-        cnt += (sr > si) || (sr == si && sm->ridx[r] < ji);
+        const uint64_t kr = ord_f64(rk_s[r]);
+        cnt += (kr > ki) || (kr == ki && sm->ridx[r] < ji);
       }
       if (cnt) atomicAdd(&rank[i], cnt);
     }
@@ -1565,8 +1601,8 @@ hipError_t launch_decode(const DecodeLaunch& L, hipStream_t stream) {
     ka.q = (const unsigned char*)L.q;
     ka.st = L.st;
     ka.blk_cnt = L.blk_cnt[0];
-    ka.blk_eps = L.blk_eps[0];
     ka.surv = L.surv[0];
+    ka.surv_eps = L.surv_eps[0];
     ka.n = L.n;
     ka.nblk = L.nblk[0];
     ka.slot = L.slot;
@@ -1602,11 +1638,11 @@ hipError_t launch_decode(const DecodeLaunch& L, hipStream_t stream) {
       ma.st = L.st;
       ma.st_w = L.st;
       ma.cnt_in = L.blk_cnt[l];
-      ma.eps_in = L.blk_eps[l];
       ma.surv_in = L.surv[l];
+      ma.eps_in = L.surv_eps[l];
       ma.cnt_out = L.blk_cnt[l + 1];
-      ma.eps_out = L.blk_eps[l + 1];
       ma.surv_out = L.surv[l + 1];
+      ma.eps_out = L.surv_eps[l + 1];
       ma.nblk_in = L.nblk[l];
       ma.nblk_out = L.nblk[l + 1];
       ma.slot = L.slot;
@@ -1632,8 +1668,8 @@ hipError_t launch_decode(const DecodeLaunch& L, hipStream_t stream) {
   fa.rho = L.rho;
   fa.st = L.st;
   fa.blk_cnt = L.blk_cnt[last];
-  fa.blk_eps = L.blk_eps[last];
   fa.surv = L.surv[last];
+  fa.surv_eps = L.surv_eps[last];
   fa.n = L.n;
   fa.nblk = L.nblk[last];
   fa.slot = L.slot;

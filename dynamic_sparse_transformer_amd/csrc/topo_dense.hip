@@ -364,4 +364,44 @@ hipError_t launch_bw_probe(const void* buf, size_t bytes, uint32_t* sink, hipStr
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------------------------
+// Finite-input check: every thread tests 16-byte chunks (grid-stride) for an all-ones exponent
+// field (NaN or infinity), plus the elements of a ragged tail; one atomicOr per wave that found one.
+__global__ __launch_bounds__(256) void check_finite_kernel(const unsigned char* buf, size_t count, int bf16,
+                                                           uint32_t* flag) {
+  const size_t esize = bf16 ? 2 : 4;
+  const size_t nchunk = count * esize / 16;
+  bool bad = false;
+  for (size_t c = (size_t)blockIdx.x * 256 + threadIdx.x; c < nchunk; c += (size_t)gridDim.x * 256) {
+    const uint4 w = *(const uint4*)(buf + c * 16);
+    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if (bf16) {
+        bad |= (ws[e] & 0x7F80u) == 0x7F80u;
+        bad |= (ws[e] & 0x7F800000u) == 0x7F800000u;
+      } else {
+        bad |= (ws[e] & 0x7F800000u) == 0x7F800000u;
+      }
+    }
+  }
+  // elements past the last whole chunk
+  const size_t done = nchunk * 16 / esize;
+  for (size_t i = done + (size_t)blockIdx.x * 256 + threadIdx.x; i < count; i += (size_t)gridDim.x * 256) {
+    if (bf16) bad |= (((const uint16_t*)buf)[i] & 0x7F80u) == 0x7F80u;
+    else bad |= (((const uint32_t*)buf)[i] & 0x7F800000u) == 0x7F800000u;
+  }
+  if (__ballot(bad) != 0ull && (threadIdx.x & 63) == 0) atomicOr(flag, 1u);
+}
+
+hipError_t launch_check_finite(const void* buf, size_t count, int bf16, uint32_t* flag, hipStream_t stream) {
+  const size_t nchunk = count * (bf16 ? 2 : 4) / 16;
+  size_t blocks = (nchunk + 255) / 256;
+  if (blocks < 1) blocks = 1;
+  if (blocks > 4096) blocks = 4096;
+  hipLaunchKernelGGL(check_finite_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, (const unsigned char*)buf, count,
+                     bf16, flag);
+  return hipGetLastError();
+}
+
 }  // namespace topo

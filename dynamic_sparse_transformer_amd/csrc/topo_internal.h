@@ -33,8 +33,20 @@ constexpr int32_t FLAG_GROUP_SELECT = 4;
 struct alignas(128) HeadState {
   uint32_t theta;     // order key of a proven lower bound of the k-th best candidate score
   uint32_t overflow;  // 1 if some block had more survivors than its slot holds
-  uint32_t pad[30];
+  int32_t path;       // how the finish chose the top-k part (PATH_* below)
+  uint32_t pad[29];
 };
+
+// Selection path of a query, left in the workspace for diagnostics (the values of TOPO_PATH_*).
+constexpr int32_t PATH_NONE = 0;            // no top-k part: k = 0 or no candidate
+constexpr int32_t PATH_ALL = 1;             // at most k candidates: all taken
+constexpr int32_t PATH_FAST = 2;            // from the scan's lists (decode: short list re-scored in float64;
+                                            // prefill: the fast scores' bounds decided every member)
+constexpr int32_t PATH_BAND = 3;            // prefill: as PATH_FAST, the entries inside the band re-scored in float64
+constexpr int32_t PATH_EXACT_ASKED = 4;     // exact radix selection: flag, float32 prefill inputs, or a size
+                                            // above the scan's limits
+constexpr int32_t PATH_EXACT_OVERFLOW = 5;  // exact radix selection: a scan list overflowed (ties)
+constexpr int32_t PATH_EXACT_CROWDED = 6;   // exact radix selection: the short list was crowded (ties)
 
 // Where one query sits and which keys are its candidates.
 struct QueryGeom {
@@ -71,12 +83,12 @@ struct DecodeLaunch {
   int64_t wstride;
   // Survivor lists, level 0 written by the key scan and level l+1 by merging groups of
   // MERGE_FAN level-l lists:
-  //   blk_cnt[l] [B * Hq][nblk[l]]        survivors of each list (or KS_OVERFLOW)
-  //   blk_eps[l] [B * Hq][nblk[l]]        error bound of the fast scores in that list
-  //   surv[l]    [B * Hq][nblk[l]][slot]  (float bits of the fast score, key index)
+  //   blk_cnt[l]  [B * Hq][nblk[l]]        survivors of each list (or KS_OVERFLOW)
+  //   surv[l]     [B * Hq][nblk[l]][slot]  (float bits of the fast score, key index)
+  //   surv_eps[l] [B * Hq][nblk[l]][slot]  error bound of that entry's fast score (its own key's)
   uint32_t* blk_cnt[MAX_LEVELS];
-  float* blk_eps[MAX_LEVELS];
   uint2* surv[MAX_LEVELS];
+  float* surv_eps[MAX_LEVELS];
   int64_t nblk[MAX_LEVELS];
   int nlevels;
   int64_t slot;
@@ -92,6 +104,13 @@ struct DecodeLaunch {
 };
 
 size_t decode_workspace_bytes(int32_t B, int32_t Hq, const QueryGeom& g, int32_t k, int32_t d, int32_t bf16);
+// Byte offsets, within a decode workspace, of the HeadState array and of the key scan's own
+// (level 0) survivor lists, with their shape, as decode_carve lays them out.
+struct DecodeView {
+  size_t state, count, entry, eps;
+  int64_t lists, slot;
+};
+DecodeView decode_view(int32_t B, int32_t Hq, int32_t Hkv, const QueryGeom& g, int32_t k, int32_t d, int32_t bf16);
 // Carve the workspace into the HeadState array, the window records and the survivor lists
 // (L.d and L.bf16 must be set).
 void decode_carve(void* ws, int32_t B, int32_t Hq, const QueryGeom& g, int32_t k, DecodeLaunch& L);
@@ -135,9 +154,21 @@ struct PrefillLaunch {
   hipEvent_t ev_scan_begin;  // optional: recorded around the key-scan launch
   hipEvent_t ev_scan_end;
 };
-size_t prefill_workspace_bytes(int32_t B, int32_t Hq, int64_t n_q, int64_t n, int32_t d, int32_t W, int32_t k);
+size_t prefill_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int64_t n_q, int64_t n, int32_t d, int32_t W, int32_t k);
+// Whether the per-row finish's LDS holds a set of 1 + W + k (false: the prefill is unsupported).
+bool prefill_fits(int32_t W, int32_t k);
+// Byte offsets, within a prefill workspace, of the scan's per-row lists and the rows' paths.
+struct PrefillView {
+  size_t count, entry, path;
+  int64_t slot;
+};
+PrefillView prefill_view(int32_t B, int32_t Hq, int32_t Hkv, int64_t n_q, int64_t n, int32_t d, int32_t k);
+// Error-bound coefficient of the matrix-core scores: |s_fast - s| <= coef * |q|_2 * |k|_2.
+float prefill_eps_coef();
 hipError_t launch_prefill(const PrefillLaunch& L, hipStream_t stream);
 
 hipError_t launch_bw_probe(const void* buf, size_t bytes, uint32_t* sink, hipStream_t stream);
+// Sets bit 0 of *flag if any of the count elements (float32, or bf16 when bf16) is NaN or infinite.
+hipError_t launch_check_finite(const void* buf, size_t count, int bf16, uint32_t* flag, hipStream_t stream);
 
 }  // namespace topo

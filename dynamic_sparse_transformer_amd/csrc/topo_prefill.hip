@@ -8,7 +8,7 @@
 // contraction, so the scan runs on the matrix cores.
 //
 // Launches:
-//   pf_norms   |q| of every query row and the largest |k| of every kv head (error bounds).
+//   pf_norms   |q| of every query row and |k| of every key (each score's own error bound).
 //   pf_scan    bf16 MFMA tiles, 128 query rows x 64 keys per step (8 waves, one 32x32x16 tile
 //              each), float32 scores, two passes over the keys: the first bounds each row's k-th
 //              best score from below, the second lists every key that may still reach it.
@@ -28,10 +28,14 @@ constexpr int PF_KEYS = 64;          // keys per scan step
 constexpr int PF_MAX_K = 96;         // largest k the MFMA scan ranks
 constexpr uint32_t PF_OVERFLOW = 0xFFFFFFFFu;
 
-// Error bound of the MFMA float32 scores: products of bf16 values are exact in float32; allowing
-// every one of the d terms several roundings of the running sum (whatever the matrix unit's
-// internal order and alignment) gives |s_fast - s| <= 2^-14 |q| |k| for d <= 128 with a wide margin.
+// Error bound of the MFMA float32 scores: products of bf16 values are exact in float32, and a
+// float32 sum of d <= 128 terms in any order and grouping is off by less than d 2^-24
+// sum_t |q_t k_t| <= 2^-17 |q| |k| (Cauchy-Schwarz), so |s_fast - s| <= 2^-14 |q| |k| holds with
+// a factor 8 to spare, whatever the matrix unit's internal order and alignment. The spare also
+// covers forming a bound s_fast -+ 2^-14 |q| |k| in float32 (half an ulp of the score, at most
+// 2^-24 |q| |k|). The tests measure the largest |s_fast - s| / (|q| |k|) on the scan's lists.
 constexpr float PF_EPS_COEF = 0x1p-14f;
+float prefill_eps_coef() { return PF_EPS_COEF; }
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 // LDS of the scan for the top-2 values of each row's lanes (phase 1), then for the waves' score
@@ -42,52 +46,64 @@ constexpr int PF_LCAP_MAX = 128;
 static int64_t pf_slot(int32_t k) { return k + 48 < PF_LCAP_MAX ? k + 48 : PF_LCAP_MAX; }
 
 struct PfWs {
-  float* qn;        // [B*Hq*n_q]
-  uint32_t* knmax;  // [B*Hkv] float bits
+  float* qn;        // [B*Hq*n_q]: |q| of every query row (rounded up)
+  float* kn;        // [B*Hkv][n]: |k| of every key (rounded up)
   uint32_t* cnt;    // [B*Hq*n_q]: entries of the row's list (or PF_OVERFLOW)
+  int32_t* path;    // [B*Hq*n_q]: how the finish chose the row's top-k part (PATH_*)
   uint2* surv;      // [B*Hq*n_q][list]: (float bits of the matrix-core score, key position)
   float* win_o;     // [B*Hq*n_q][d]: sum over the row's window of exp(z - m_w) v (bf16 inputs)
   float2* win_mz;   // [B*Hq*n_q]: (m_w, sum over the window of exp(z - m_w))
 };
 
-size_t prefill_workspace_bytes(int32_t B, int32_t Hq, int64_t n_q, int64_t, int32_t d, int32_t, int32_t k) {
-  const size_t rows = (size_t)B * Hq * (size_t)n_q;
-  return align256(rows * 4) + align256((size_t)B * Hq * 4) + align256(rows * 4) +
-         align256(rows * (size_t)pf_slot(k) * sizeof(uint2)) + align256(rows * (size_t)d * 4) + rows * 8;
-}
-
-static PfWs pf_carve(void* ws, int32_t B, int32_t Hq, int64_t n_q, int32_t d, int32_t k) {
+static PfWs pf_carve(void* ws, int32_t B, int32_t Hq, int32_t Hkv, int64_t n_q, int64_t n, int32_t d, int32_t k,
+                     size_t* total = nullptr) {
   const size_t rows = (size_t)B * Hq * (size_t)n_q;
   PfWs w;
   char* p = (char*)ws;
   w.qn = (float*)p;
   p += align256(rows * 4);
-  w.knmax = (uint32_t*)p;
-  p += align256((size_t)B * Hq * 4);
+  w.kn = (float*)p;
+  p += align256((size_t)B * Hkv * (size_t)n * 4);
   w.cnt = (uint32_t*)p;
+  p += align256(rows * 4);
+  w.path = (int32_t*)p;
   p += align256(rows * 4);
   w.surv = (uint2*)p;
   p += align256(rows * (size_t)pf_slot(k) * sizeof(uint2));
   w.win_o = (float*)p;
   p += align256(rows * (size_t)d * 4);
   w.win_mz = (float2*)p;
+  p += rows * 8;
+  if (total) *total = (size_t)(p - (char*)ws);
   return w;
+}
+
+size_t prefill_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int64_t n_q, int64_t n, int32_t d, int32_t, int32_t k) {
+  size_t total = 0;
+  (void)pf_carve(nullptr, B, Hq, Hkv, n_q, n, d, k, &total);
+  return total;
+}
+
+PrefillView prefill_view(int32_t B, int32_t Hq, int32_t Hkv, int64_t n_q, int64_t n, int32_t d, int32_t k) {
+  const PfWs w = pf_carve(nullptr, B, Hq, Hkv, n_q, n, d, k);
+  PrefillView v;
+  v.count = (size_t)(uintptr_t)w.cnt;
+  v.entry = (size_t)(uintptr_t)w.surv;
+  v.path = (size_t)(uintptr_t)w.path;
+  v.slot = pf_slot(k);
+  return v;
 }
 
 // ---------------------------------------------------------------------------------------------
 // Norms of bf16 rows for the error bounds of the matrix-core scores: |q| of every query row and
-// the largest |k| of every kv head. A row is LPR lanes x 16 bytes (coalesced, RPW rows per load
-// instruction). The squares of bf16 values are exact in float32; their float32 sum (8 terms per
-// lane, then a tree over the LPR lanes) and sqrtf carry a relative error far below the factor
-// (1 + 2^-15) that rounds the norm up. Grid (blocks over the rows of a head, heads); with
-// `norm` every row's norm is written, with `head_max` one atomicMax per block into its head
-// (U rows per lane, large for this use: the atomics of all blocks meet on one cache line). Block
-// (0, 0) also clears the `nzero` words at `zero` (the head maxima of the launch that follows).
+// |k| of every key, each score's bound taking its own two norms. A row is LPR lanes x 16 bytes
+// (coalesced, RPW rows per load instruction). The squares of bf16 values are exact in float32;
+// their float32 sum (8 terms per lane, then a tree over the LPR lanes) and sqrtf carry a relative
+// error far below the factor (1 + 2^-15) that rounds the norm up. Grid (blocks over the rows of
+// a head, heads); U rows per lane.
 template <int D, int U>
-__global__ __launch_bounds__(256) void pf_norm_kernel(const unsigned char* x, int64_t rows_per_head, float* norm,
-                                                      uint32_t* head_max, uint32_t* zero, int nzero) {
+__global__ __launch_bounds__(256) void pf_norm_kernel(const unsigned char* x, int64_t rows_per_head, float* norm) {
   constexpr int RB = D * 2, LPR = RB / 16, RPW = 64 / LPR;
-  __shared__ float wm[4];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, gq = lane / LPR, cc = lane % LPR;
   const unsigned char* base = x + (size_t)blockIdx.y * (size_t)rows_per_head * RB;
   const int64_t r0 = (int64_t)blockIdx.x * (4 * U * RPW) + (int64_t)wave * U * RPW + gq;
@@ -97,9 +113,6 @@ __global__ __launch_bounds__(256) void pf_norm_kernel(const unsigned char* x, in
     const int64_t row = r0 + u * RPW;
     v[u] = row < rows_per_head ? *(const uint4*)(base + (size_t)row * RB + cc * 16) : make_uint4(0u, 0u, 0u, 0u);
   }
-  if (zero && blockIdx.x == 0 && blockIdx.y == 0)
-    for (int t = threadIdx.x; t < nzero; t += 256) zero[t] = 0u;
-  float mx = 0.f;
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     const uint32_t w4[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
@@ -113,14 +126,7 @@ __global__ __launch_bounds__(256) void pf_norm_kernel(const unsigned char* x, in
     s2 = group_sum_f32<LPR>(s2);
     const float nrm = sqrtf(s2) * (1.0f + 0x1p-15f);
     const int64_t row = r0 + u * RPW;
-    if (norm && cc == 0 && row < rows_per_head) norm[(size_t)blockIdx.y * rows_per_head + row] = nrm;
-    mx = fmaxf(mx, nrm);
-  }
-  if (head_max) {
-    for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
-    if (lane == 0) wm[wave] = mx;
-    __syncthreads();
-    if (threadIdx.x == 0) atomicMax(&head_max[blockIdx.y], __float_as_uint(fmaxf(fmaxf(wm[0], wm[1]), fmaxf(wm[2], wm[3]))));
+    if (cc == 0 && row < rows_per_head) norm[(size_t)blockIdx.y * rows_per_head + row] = nrm;
   }
 }
 
@@ -172,11 +178,12 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 // 32x32 quadrant (rows 32*(w/2).., keys 32*(w%2)..) with v_mfma_f32_32x32x16_bf16: lane l
 // supplies row / key (l % 32) and elements 8*(l/32) .. +8 of each 16-deep slice, and holds output
 // (row 8*(r/4) + 4*(l/32) + r%4, key l % 32) in register r.
-// Phase 1 keeps, per lane and row, the two largest fast scores it has seen. Those 128 values per
-// row belong to distinct candidate keys, so their k-th largest x_k gives the bound T = x_k - eps
-// below the row's k-th largest exact score. Phase 2 scores the keys again and appends the
-// position of every key whose upper bound reaches T (fast score >= x_k - 2 eps) to the row's list
-// in LDS; the lists are copied out at the end, and the finish ranks them.
+// Every score has its own error bound eps = cq_row |k_j|, cq_row = 2^-14 |q_row| (the key norms
+// travel with the key tiles). Phase 1 keeps, per lane and row, the two largest lower bounds
+// (score - eps) it has seen. Those 128 values per row belong to distinct candidate keys, so any T
+// that k of them reach is a lower bound of the row's k-th largest exact score. Phase 2 scores the
+// keys again and appends every key whose upper bound (score + eps) reaches T to the row's list
+// in global memory; the finish ranks the lists.
 
 template <int D>
 __global__ __launch_bounds__(512) void pf_scan_kernel(PfArgs a) {
@@ -189,6 +196,7 @@ __global__ __launch_bounds__(512) void pf_scan_kernel(PfArgs a) {
   constexpr int TILE_BYTES = PF_KEYS * STRIDE;
   static_assert(PASSES >= 1 && PASSES <= 2, "staging passes");
   __shared__ __align__(16) unsigned char ktiles[2 * TILE_BYTES];
+  __shared__ float knt[2][PF_KEYS];   // norms of the keys of the two tiles in LDS
   __shared__ __align__(16) unsigned char lists[PF_LIST_BYTES];
   __shared__ uint32_t lcnt[PF_ROWS];  // keys appended to each row's list
   __shared__ float lthf[PF_ROWS];
@@ -202,7 +210,7 @@ __global__ __launch_bounds__(512) void pf_scan_kernel(PfArgs a) {
   const int b = bh / a.Hq, h = bh - b * a.Hq, g = h / a.G;
   const int64_t i0 = (nrb - 1 - (job - (int64_t)bh * nrb)) * PF_ROWS;
   const unsigned char* kb = a.k + ((size_t)b * a.Hkv + g) * (size_t)a.n * RB;
-  const float knmax = __uint_as_float(a.w.knmax[(size_t)b * a.Hkv + g]);
+  const float* knb = a.w.kn + ((size_t)b * a.Hkv + g) * (size_t)a.n;
   const uint32_t LCAP = (uint32_t)a.slot;
   // phase 2 stages each wave's 16 scores per lane here (where the top-2 values were): chunk q
   // (registers 4q..4q+3) of lane l at float4 index q * 64 + l of the wave's 4 KB
@@ -223,6 +231,13 @@ __global__ __launch_bounds__(512) void pf_scan_kernel(PfArgs a) {
     }
   }
   const int row_base = rq * 32 + 4 * half;  // block row of register r: row_base + 8*(r/4) + r%4
+  // the error-bound factor of the row of each register: 2^-14 |q_row| (0 for rows past the end)
+  float cq[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int64_t i = i0 + row_base + 8 * (r / 4) + (r % 4);
+    cq[r] = i < a.n_q ? PF_EPS_COEF * a.w.qn[(size_t)bh * a.n_q + i] : 0.f;
+  }
 
   const int64_t i_last = min(i0 + PF_ROWS, a.n_q) - 1;
   const int64_t p_first = a.q_pos0 + i0, p_last = a.q_pos0 + i_last;
@@ -238,35 +253,46 @@ __global__ __launch_bounds__(512) void pf_scan_kernel(PfArgs a) {
 #define PF_INTERIOR(t) ((t) >= 1 && ((t) <= t_a || ((t) >= t_b && (t) <= t_c)))
 
   // Staging of key tiles: thread tid copies 16-byte chunk (tid % NCH) of key rows
-  // u * PF_KEYS + tid / NCH (+ RPP). Raw buffer loads whose range ends at the cache's last key:
-  // rows past the end read as zero, so every load is issued unconditionally and no address is
-  // clamped. Register set (u & 1) holds tile u from its load until its store two steps later.
+  // u * PF_KEYS + tid / NCH (+ RPP), and the norms of those rows. Raw buffer loads whose range
+  // ends at the cache's last key: rows past the end read as zero, so every load is issued
+  // unconditionally and no address is clamped (the norm index is clamped; rows past the end are
+  // never candidates). Register set (u & 1) holds tile u from its load until its store two steps
+  // later.
   const int srow = tid / NCH, schunk = tid % NCH;
   const int voff0 = srow * RB + schunk * 16, voff1 = voff0 + RPP * RB;
   uint4 r00 = make_uint4(0u, 0u, 0u, 0u), r01 = r00, r10 = r00, r11 = r00;
-#define PF_LOAD(DST0, DST1, U)                                                                     \
+  float n00 = 0.f, n01 = 0.f, n10 = 0.f, n11 = 0.f;
+#define PF_LOAD(DST0, DST1, N0, N1, U)                                                             \
   {                                                                                                \
     const int kt_ = min((U) * PF_KEYS, n);                                                         \
     const __amdgpu_buffer_rsrc_t rs_ =                                                             \
         __builtin_amdgcn_make_buffer_rsrc((void*)(kb + (size_t)kt_ * RB), (short)0, (n - kt_) * RB, 0x00020000); \
     DST0 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs_, voff0, 0, 0));    \
-    if (PASSES > 1) DST1 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs_, voff1, 0, 0)); \
+    N0 = knb[min((U) * PF_KEYS + srow, n - 1)];                                                    \
+    if (PASSES > 1) {                                                                              \
+      DST1 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs_, voff1, 0, 0));  \
+      N1 = knb[min((U) * PF_KEYS + srow + RPP, n - 1)];                                            \
+    }                                                                                              \
   }
-#define PF_STORE(SRC0, SRC1, U)                                                                    \
+#define PF_STORE(SRC0, SRC1, N0, N1, U)                                                            \
   {                                                                                                \
     unsigned char* dst = &ktiles[((U) & 1) * TILE_BYTES + srow * STRIDE + schunk * 16];            \
     *(uint4*)dst = SRC0;                                                                           \
     if (PASSES > 1) *(uint4*)(dst + RPP * STRIDE) = SRC1;                                          \
+    if (schunk == 0) {                                                                             \
+      knt[(U) & 1][srow] = N0;                                                                     \
+      if (PASSES > 1) knt[(U) & 1][srow + RPP] = N1;                                               \
+    }                                                                                              \
   }
 // Prologue of a pass over the tiles: tiles 0 and 1 to LDS, tiles 2 and 3 in flight, scores of
 // tile 0 into ACC.
 #define PF_PROLOGUE(ACC)                                                                           \
-  PF_LOAD(r00, r01, 0)                                                                             \
-  PF_LOAD(r10, r11, 1)                                                                             \
-  PF_STORE(r00, r01, 0)                                                                            \
-  PF_STORE(r10, r11, 1)                                                                            \
-  PF_LOAD(r00, r01, 2)                                                                             \
-  PF_LOAD(r10, r11, 3)                                                                             \
+  PF_LOAD(r00, r01, n00, n01, 0)                                                                   \
+  PF_LOAD(r10, r11, n10, n11, 1)                                                                   \
+  PF_STORE(r00, r01, n00, n01, 0)                                                                  \
+  PF_STORE(r10, r11, n10, n11, 1)                                                                  \
+  PF_LOAD(r00, r01, n00, n01, 2)                                                                   \
+  PF_LOAD(r10, r11, n10, n11, 3)                                                                   \
   __syncthreads();                                                                                 \
   PF_MMA(ACC, 0)
 // Scores of the tile in LDS buffer BUF into ACC: v_mfma_f32_32x32x16_bf16 over the D / 16 slices.
@@ -307,7 +333,9 @@ __global__ __launch_bounds__(512) void pf_scan_kernel(PfArgs a) {
 // Scheduling fences keep that order: left to itself the compiler puts the vector work before the
 // matrix instructions, and as the waves of a block meet at every barrier, the two waves of a
 // SIMD would then take turns on the matrix core instead of overlapping.
-#define PF_STEP(PART, POST, t, ACC_CUR, ACC_NEXT, SET0, SET1)                                      \
+#define PF_STEP(PART, POST, t, ACC_CUR, ACC_NEXT, SET0, SET1, NS0, NS1)                            \
+  {                                                                                                \
+  const float knc_ = knt[(t) & 1][kq * 32 + m]; /* norm of the lane's key of tile t */             \
   PF_MASK(ACC_CUR, t)                                                                              \
   {                                                                                                \
     const unsigned char* krow = &ktiles[(((t) + 1) & 1) * TILE_BYTES + (kq * 32 + m) * STRIDE + half * 16]; \
@@ -323,14 +351,15 @@ __global__ __launch_bounds__(512) void pf_scan_kernel(PfArgs a) {
     }                                                                                              \
   }                                                                                                \
   POST(ACC_CUR, t)                                                                                 \
-  PF_STORE(SET0, SET1, (t) + 2)                                                                    \
-  PF_LOAD(SET0, SET1, (t) + 4)                                                                     \
-  __syncthreads();
+  PF_STORE(SET0, SET1, NS0, NS1, (t) + 2)                                                          \
+  PF_LOAD(SET0, SET1, NS0, NS1, (t) + 4)                                                           \
+  __syncthreads();                                                                                 \
+  }
 
   f32x16_t accA, accB;
-  // ---- phase 1: per lane and row, the two largest fast scores of candidate keys. With m1 >= m2,
-  // the new second best is the median of m1, m2 and the score, and the new best is the median of
-  // m1, the score and +inf (a run-time operand, so that no NaN-quieting is added around a max).
+  // ---- phase 1: per lane and row, the two largest lower bounds of candidate keys. With m1 >= m2,
+  // the new second best is the median of m1, m2 and the bound, and the new best is the median of
+  // m1, the bound and +inf (a run-time operand, so that no NaN-quieting is added around a max).
   const float pinf = a.pinf;
   float m1[16], m2[16];
 #pragma unroll
@@ -339,22 +368,23 @@ __global__ __launch_bounds__(512) void pf_scan_kernel(PfArgs a) {
 // without them the compiler sinks the work of a step past the next step's boundary-tile branch.)
 #define PF_PART1(ACC, r)                                                                           \
   {                                                                                                \
-    m2[r] = __builtin_amdgcn_fmed3f(m1[r], m2[r], ACC[r]);                                         \
-    m1[r] = __builtin_amdgcn_fmed3f(m1[r], ACC[r], pinf);                                          \
+    const float lb_ = fmaf(-cq[r], knc_, ACC[r]);                                                  \
+    m2[r] = __builtin_amdgcn_fmed3f(m1[r], m2[r], lb_);                                            \
+    m1[r] = __builtin_amdgcn_fmed3f(m1[r], lb_, pinf);                                             \
     asm volatile("" : "+v"(m1[r]), "+v"(m2[r]));                                                   \
   }
 #define PF_POST1(ACC, t)
   if (ntiles > 0) {
     PF_PROLOGUE(accA)
     for (int t = 0; t < ntiles; t += 2) {
-      PF_STEP(PF_PART1, PF_POST1, t, accA, accB, r00, r01)
-      PF_STEP(PF_PART1, PF_POST1, t + 1, accB, accA, r10, r11)
+      PF_STEP(PF_PART1, PF_POST1, t, accA, accB, r00, r01, n00, n01)
+      PF_STEP(PF_PART1, PF_POST1, t + 1, accB, accA, r10, r11, n10, n11)
     }
   }
 
-  // ---- thresholds: row R's 128 values sit at tops[R][64 * kq + 2 * m + {0, 1}] (even entries:
-  // the lanes' best values, 64 distinct keys; odd entries: their second best). Each row needs a
-  // lower bound T of the k-th largest of its 128 values such that few values lie between: the
+  // ---- thresholds: row R's 128 lower bounds sit at tops[R][64 * kq + 2 * m + {0, 1}] (even
+  // entries: the lanes' best values, 64 distinct keys; odd entries: their second best). Each row
+  // needs a lower bound T of the k-th largest of its 128 values such that few values lie between: the
   // largest T = lo + c (hi - lo) / 1024, c = 0..1023, that at least k values reach (a bitwise
   // search over c, monotone in c), where hi is the largest value and lo a known lower bound of the
   // k-th largest: for k <= 64 and 64 finite best values the smallest of them, else the smallest
@@ -369,12 +399,6 @@ __global__ __launch_bounds__(512) void pf_scan_kernel(PfArgs a) {
     *(float2*)&tops[row * 128 + 64 * kq + 2 * m] = make_float2(m1[r], m2[r]);
   }
   const int sub = lane & 15;
-  float qn_g[4];
-#pragma unroll
-  for (int g = 0; g < 4; ++g) {
-    const int64_t i = i0 + wave * 16 + 4 * g + (lane >> 4);
-    qn_g[g] = i < a.n_q ? a.w.qn[(size_t)bh * a.n_q + i] : 0.f;
-  }
   __syncthreads();
   {
     float v[4][8], lo[4], step[4];
@@ -427,10 +451,9 @@ __global__ __launch_bounds__(512) void pf_scan_kernel(PfArgs a) {
     for (int g = 0; g < 4; ++g) {
       const int row = wave * 16 + 4 * g + (lane >> 4);
       if (sub == 0) {
-        const float eps = i0 + row < a.n_q ? PF_EPS_COEF * qn_g[g] * knmax + 1e-30f : 0.f;
         const float x = ok[g] ? fmaf((float)c[g], step[g], lo[g]) : -INFINITY;
         // kept finite (at least the lowest float), so that the -inf of a masked score never passes
-        lthf[row] = fmaxf(x - 2.0f * eps, -0x1.fffffep+127f);
+        lthf[row] = fmaxf(x, -0x1.fffffep+127f);
       }
     }
   }
@@ -442,8 +465,9 @@ __global__ __launch_bounds__(512) void pf_scan_kernel(PfArgs a) {
 
   // ---- phase 2: every candidate key whose upper bound reaches the row's bound goes to the row's
   // list in global memory, with its score. A lane first gathers the test results of its 16
-  // registers into bit r of `fail`'s complement: the test x >= T is the sign of x - T (T finite,
-  // x finite or -inf), shifted in by v_alignbit from register 15 down to 0; its 16 scores go to
+  // registers into bit r of `fail`'s complement: the test x + eps >= T is the sign of
+  // (x + eps) - T (T finite, x finite or -inf), shifted in by v_alignbit from register 15 down
+  // to 0; its 16 scores go to
   // the wave's LDS stage. Then the lane takes its set bits one at a time: a slot from the row's LDS counter, (score read back from the stage, key
   // position) into the slot. The lanes of a wave pass through that loop together as often as the
   // busiest lane needs (a step has about one passing register per four lanes). Slots past the end
@@ -451,7 +475,8 @@ __global__ __launch_bounds__(512) void pf_scan_kernel(PfArgs a) {
   uint32_t fail = 0u;
 #define PF_PART2(ACC, i)                                                                           \
   {                                                                                                \
-    fail = __builtin_amdgcn_alignbit((i) == 0 ? 0u : fail, __float_as_uint(ACC[15 - (i)] - thf[15 - (i)]), 31); \
+    fail = __builtin_amdgcn_alignbit((i) == 0 ? 0u : fail,                                         \
+                                     __float_as_uint(fmaf(cq[15 - (i)], knc_, ACC[15 - (i)]) - thf[15 - (i)]), 31); \
     asm volatile("" : "+v"(fail));                                                                 \
   }
 #define PF_POST2(ACC, t)                                                                           \
@@ -472,8 +497,8 @@ __global__ __launch_bounds__(512) void pf_scan_kernel(PfArgs a) {
   if (ntiles > 0) {
     PF_PROLOGUE(accA)
     for (int t = 0; t < ntiles; t += 2) {
-      PF_STEP(PF_PART2, PF_POST2, t, accA, accB, r00, r01)
-      PF_STEP(PF_PART2, PF_POST2, t + 1, accB, accA, r10, r11)
+      PF_STEP(PF_PART2, PF_POST2, t, accA, accB, r00, r01, n00, n01)
+      PF_STEP(PF_PART2, PF_POST2, t + 1, accB, accA, r10, r11, n10, n11)
     }
   }
 
@@ -852,9 +877,9 @@ __device__ void pf_row(const PfArgs& a, PfRowSmem* sm, size_t grow) {
   const int64_t p = a.q_pos0 + i;
   const unsigned char* qrow = a.q + grow * RB;
   const int gq = lane / LPR, cc = lane % LPR;
-  // error-bound inputs, requested early: |q| of the row and the largest |k| of the kv head
+  // error-bound inputs: |q| of the row (requested early) and |k| of each listed key
   const float qn_row = a.w.qn[grow];
-  const float kn_max = __uint_as_float(a.w.knmax[(size_t)b * a.Hkv + g]);
+  const float* knh = a.w.kn + ((size_t)b * a.Hkv + g) * (size_t)a.n;
   // the float64 query (canonical scores) is filled where a path needs it: float32 inputs and
   // the exact path always, the bf16 fast path only for a band to re-score
   auto fill_qd = [&]() {
@@ -878,6 +903,7 @@ __device__ void pf_row(const PfArgs& a, PfRowSmem* sm, size_t grow) {
   // ---- the row's list of possible top-k keys (fast path) or the exact path
   int c = 0;
   bool exact = false;
+  int32_t path = PATH_NONE;
   if (a.topk > 0) {
     // The count and the row's whole slot area (at most 128 entries, two per lane) are read
     // together, so that the list costs one memory round trip; slots at or past the count hold
@@ -891,6 +917,7 @@ __device__ void pf_row(const PfArgs& a, PfRowSmem* sm, size_t grow) {
       if (lane + 64 < a.slot) e1 = sv[lane + 64];
     }
     exact = cr == PF_OVERFLOW;
+    if (exact) path = a.exact_all ? PATH_EXACT_ASKED : PATH_EXACT_OVERFLOW;
     if (!exact) {
       c = (int)cr;
       // positions come from the scan and are always keys of the cache; clamping only guards
@@ -921,25 +948,30 @@ __device__ void pf_row(const PfArgs& a, PfRowSmem* sm, size_t grow) {
       if (lane == 0) sm->rs[c] = (double)part;
     }
     __builtin_amdgcn_wave_barrier();
-    const float eps = PF_EPS_COEF * qn_row * kn_max + 1e-30f;
     if (exact) {
       fill_qd();
       nt = pf_exact_row<D, BF16>(sm, a, kb, p);
     } else if (c > a.topk) {
-      // x_k = k-th largest score of the list; A = entries with s_mc >= x_k - 2 eps. Every
-      // entry outside A scores below all k entries with s_mc >= x_k, so the top-k lies in A, and
-      // if |A| = k it is A. Otherwise an entry with s_mc > x_k + 2 eps is surely in the top-k
-      // (only entries with s_mc > x_k, at most k - 1 of them, can score above it), and the rest of
-      // A, the band around x_k, is ranked by float64 canonical scores, then by position; its best
+      // Each entry's bounds L = s_mc - eps_j <= s <= U = s_mc + eps_j, eps_j = 2^-14 |q| |k_j|.
+      // T_L = k-th largest L; A = entries with U >= T_L. Every entry outside A scores below k
+      // entries, so the top-k lies in A, and if |A| = k it is A. Otherwise, with T_U the k-th
+      // largest U over A, an entry with L > T_U is surely in the top-k (only entries with
+      // U > T_U, at most k - 1 of them counting itself, can score above it), and the rest of A,
+      // the band, is ranked by float64 canonical scores, then by position; its best
       // k - (sure entries) complete the top-k.
+      const float cqr = PF_EPS_COEF * qn_row;
       const float s0 = lane < c ? (float)sm->rs[lane] : 0.f;
       const float s1 = lane + 64 < c ? (float)sm->rs[lane + 64] : 0.f;
-      const uint32_t key[2] = {lane < c ? ord_f32(s0) : 0u, lane + 64 < c ? ord_f32(s1) : 0u};
-      const float xk = unord_f32(wave_kth_largest<2>(key, a.topk));
-      const float thr = (xk - 2.0f * eps) - fabsf(xk) * 0x1p-20f;
-      const bool in0 = lane < c && s0 >= thr, in1 = lane + 64 < c && s1 >= thr;
+      const float e0 = lane < c ? cqr * knh[sm->ridx[lane]] : 0.f;
+      const float e1 = lane + 64 < c ? cqr * knh[sm->ridx[lane + 64]] : 0.f;
+      const uint32_t lk0 = ord_f32(s0 - e0), lk1 = ord_f32(s1 - e1);
+      const uint32_t uk0 = ord_f32(s0 + e0), uk1 = ord_f32(s1 + e1);
+      const uint32_t key[2] = {lane < c ? lk0 : 0u, lane + 64 < c ? lk1 : 0u};
+      const uint32_t TL = wave_kth_largest<2>(key, a.topk);
+      const bool in0 = lane < c && uk0 >= TL, in1 = lane + 64 < c && uk1 >= TL;
       const uint64_t m0 = __ballot(in0), m1 = __ballot(in1);
       const int na = __popcll(m0) + __popcll(m1);
+      path = na == a.topk ? PATH_FAST : PATH_BAND;
       if (na == a.topk) {
         if (in0) {
           const int pos = lanes_below(m0);
@@ -954,8 +986,9 @@ __device__ void pf_row(const PfArgs& a, PfRowSmem* sm, size_t grow) {
         nt = a.topk;
         __builtin_amdgcn_wave_barrier();
       } else {
-        const float hi = (xk + 2.0f * eps) + fabsf(xk) * 0x1p-20f;
-        const bool su0 = in0 && s0 > hi, su1 = in1 && s1 > hi;
+        const uint32_t ukey[2] = {in0 ? uk0 : 0u, in1 ? uk1 : 0u};
+        const uint32_t TU = wave_kth_largest<2>(ukey, a.topk);
+        const bool su0 = in0 && lk0 > TU, su1 = in1 && lk1 > TU;
         const bool bd0 = in0 && !su0, bd1 = in1 && !su1;
         const uint64_t ms0 = __ballot(su0), ms1 = __ballot(su1), mb0 = __ballot(bd0), mb1 = __ballot(bd1);
         const int ns = __popcll(ms0) + __popcll(ms1), nb = __popcll(mb0) + __popcll(mb1);
@@ -982,11 +1015,12 @@ __device__ void pf_row(const PfArgs& a, PfRowSmem* sm, size_t grow) {
         const int need = a.topk - ns;
         for (int t = lane; t < nb; t += 64) {
           const double si = sm->rs[t];
+          const uint64_t ki = ord_f64(si);
           const int32_t ji = sm->ridx[t];
           int rank = 0;
           for (int r = 0; r < nb; ++r) {
-            const double sr = sm->rs[r];
-            rank += (sr > si) || (sr == si && sm->ridx[r] < ji);
+            const uint64_t kr = ord_f64(sm->rs[r]);
+            rank += (kr > ki) || (kr == ki && sm->ridx[r] < ji);
           }
           if (rank < need) {
             sm->tidx[ns + rank] = ji;
@@ -1002,6 +1036,7 @@ __device__ void pf_row(const PfArgs& a, PfRowSmem* sm, size_t grow) {
         sm->ts[t] = sm->rs[t];
       }
       nt = c;
+      path = PATH_ALL;
       __builtin_amdgcn_wave_barrier();
     }
   } else {
@@ -1016,11 +1051,12 @@ __device__ void pf_row(const PfArgs& a, PfRowSmem* sm, size_t grow) {
     } else if (c > a.topk) {
       for (int t = lane; t < c; t += 64) {
         const double si = sm->rs[t];
+        const uint64_t ki = ord_f64(si);
         const int32_t ji = sm->ridx[t];
         int rank = 0;
         for (int r = 0; r < c; ++r) {
-          const double sr = sm->rs[r];
-          rank += (sr > si) || (sr == si && sm->ridx[r] < ji);
+          const uint64_t kr = ord_f64(sm->rs[r]);
+          rank += (kr > ki) || (kr == ki && sm->ridx[r] < ji);
         }
         if (rank < a.topk) {
           sm->tidx[rank] = ji;
@@ -1028,6 +1064,7 @@ __device__ void pf_row(const PfArgs& a, PfRowSmem* sm, size_t grow) {
         }
       }
       nt = a.topk;
+      path = PATH_FAST;
       __builtin_amdgcn_wave_barrier();
     } else if (c > 0) {
       for (int t = lane; t < c; t += 64) {
@@ -1035,9 +1072,12 @@ __device__ void pf_row(const PfArgs& a, PfRowSmem* sm, size_t grow) {
         sm->ts[t] = sm->rs[t];
       }
       nt = c;
+      path = PATH_ALL;
       __builtin_amdgcn_wave_barrier();
     }
   }
+
+  if (lane == 0) a.w.path[grow] = path;
 
   // ---- set: {0} u window u T, ascending
   const int count = anchor + nwin + nt;
@@ -1240,12 +1280,11 @@ static hipError_t launch_pf_t(const PrefillLaunch& L, const PfArgs& pa, hipStrea
   if constexpr (BF16) {
     if (!pa.exact_all && L.topk > 0) {
       // norms for the error bounds of the matrix-core scores (only the fast selection uses them)
-      constexpr int RPW = 64 / (D * 2 / 16), QU = 4, KU = 16;  // rows per wave load; loads per lane
+      constexpr int RPW = 64 / (D * 2 / 16), QU = 4;  // rows per wave load; loads per lane
       hipLaunchKernelGGL((pf_norm_kernel<D, QU>), dim3((unsigned)((rows + 4 * QU * RPW - 1) / (4 * QU * RPW)), 1), dim3(256),
-                         0, s, (const unsigned char*)L.q, (int64_t)rows, pa.w.qn, (uint32_t*)nullptr, pa.w.knmax,
-                         L.B * L.Hkv);
-      hipLaunchKernelGGL((pf_norm_kernel<D, KU>), dim3((unsigned)((L.n + 4 * KU * RPW - 1) / (4 * KU * RPW)), (unsigned)(L.B * L.Hkv)),
-                         dim3(256), 0, s, (const unsigned char*)L.k, L.n, (float*)nullptr, pa.w.knmax, (uint32_t*)nullptr, 0);
+                         0, s, (const unsigned char*)L.q, (int64_t)rows, pa.w.qn);
+      hipLaunchKernelGGL((pf_norm_kernel<D, QU>), dim3((unsigned)((L.n + 4 * QU * RPW - 1) / (4 * QU * RPW)), (unsigned)(L.B * L.Hkv)),
+                         dim3(256), 0, s, (const unsigned char*)L.k, L.n, pa.w.kn);
       e = hipGetLastError();
       if (e != hipSuccess) return e;
     }
@@ -1276,6 +1315,15 @@ static hipError_t launch_pf_t(const PrefillLaunch& L, const PfArgs& pa, hipStrea
   return hipGetLastError();
 }
 
+// The finish gives each of its 4 waves (rows) its own LDS region; all four must fit the 160 KB of a
+// compute unit.
+bool prefill_fits(int32_t W, int32_t k) {
+  const int set_cap = 1 + W + k;
+  if (set_cap > PF_FIN_SET) return false;
+  const size_t wave_smem = (PfRowSmem::bytes(pf_slot(k), k, set_cap) + 255) & ~(size_t)255;
+  return 4 * wave_smem <= 160 * 1024;
+}
+
 hipError_t launch_prefill(const PrefillLaunch& L, hipStream_t stream) {
   if (1 + L.W + L.topk > PF_FIN_SET) return hipErrorNotSupported;
   PfArgs pa;
@@ -1285,7 +1333,7 @@ hipError_t launch_prefill(const PrefillLaunch& L, hipStream_t stream) {
   pa.out = L.out;
   pa.sel_idx = L.sel_idx;
   pa.sel_count = L.sel_count;
-  pa.w = pf_carve(L.ws, L.B, L.Hq, L.n_q, L.d, L.topk);
+  pa.w = pf_carve(L.ws, L.B, L.Hq, L.Hkv, L.n_q, L.n, L.d, L.topk);
   pa.n = L.n;
   pa.n_q = L.n_q;
   pa.q_pos0 = L.q_pos0;
@@ -1305,7 +1353,7 @@ hipError_t launch_prefill(const PrefillLaunch& L, hipStream_t stream) {
   pa.pinf = INFINITY;
   pa.rows = (int64_t)L.B * L.Hq * L.n_q;
   pa.wave_smem = (PfRowSmem::bytes(pa.slot, L.topk, pa.set_cap) + 255) & ~(size_t)255;
-  if (4 * pa.wave_smem > 160 * 1024) return hipErrorNotSupported;
+  if (!prefill_fits(L.W, L.topk)) return hipErrorNotSupported;
   if (L.bf16) return L.d == 128 ? launch_pf_t<128, true>(L, pa, stream) : launch_pf_t<64, true>(L, pa, stream);
   return L.d == 128 ? launch_pf_t<128, false>(L, pa, stream) : launch_pf_t<64, false>(L, pa, stream);
 }

@@ -45,6 +45,14 @@
  * nothing has been written. The workspace must hold topo_workspace_bytes() bytes for the same
  * parameters and operation; its contents on entry do not matter and are scratch afterwards.
  * Two calls that run concurrently must not share a workspace.
+ *
+ * Finite inputs. q, k and v must hold finite values (no NaN, no infinity); topo_check_finite
+ * tests a buffer on the device. What a non-finite value does: the kernels rank scores by integer
+ * order keys of their bit patterns (a total order: NaN above +infinity, -0 equal to +0) and
+ * gather only positions of visible keys taken from their own lists, so the set output keeps its
+ * form (strictly ascending positions with the anchor and the window, padded with -1), but which
+ * keys fill the top-k part and sel_count are then not defined by the score rule above, and out
+ * (and rho) may hold NaN or infinity.
  */
 #ifndef TOPO_ATTN_H
 #define TOPO_ATTN_H
@@ -77,7 +85,10 @@ extern "C" {
                                        scratch when TOPO_FLAG_DENSE_FALLBACK is set)            */
 #define TOPO_OP_DECODE_RAGGED 5     /* topo_attn_decode_ragged (sized for the longest position) */
 
-/* Largest condensate set (1 + W + k) a call may ask for. */
+/* Largest condensate set (1 + W + k) a call may ask for. The prefill also needs the LDS of its
+ * per-row finish to hold four rows: 4 * roundup256(2116 + 20 * (1 + W + k) + 12 * (k + 1)
+ * + 12 * min(k + 48, 128)) <= 163840 bytes (1 + W + k <= 1836 at k = 64); larger sets return
+ * TOPO_EUNSUPPORTED from the prefill calls (and 0 from topo_workspace_bytes). */
 #define TOPO_MAX_SET 4096
 
 /* Flag bits of topo_params_t.flags. */
@@ -233,10 +244,69 @@ size_t topo_layers_workspace_bytes(const topo_params_t* p, const topo_layer_t* l
 
 /* A decode step through n_layers attention layers (n_layers >= 1): layer i runs topo_attn_decode
  * with p's shapes, position, scale, dtype and flags and the layer's W and k, or topo_attn_dense
- * when it is a pillar layer, in order on `stream`. Every layer is validated before anything is
- * launched (errors as those calls; TOPO_EINVAL if layers is NULL, n_layers < 1 or reserved != 0). */
+ * when it is a pillar layer, in order on `stream`. TOPO_FLAG_GROUP_SELECT in p->flags applies to
+ * the condensate-set layers (pillar layers are dense and ignore it). Every layer is validated
+ * before anything is launched (errors as those calls, e.g. TOPO_EUNSUPPORTED for the group flag
+ * with G > 4; TOPO_EINVAL if layers is NULL, n_layers < 1 or reserved != 0). */
 int topo_attn_decode_layers(const topo_params_t* p, const topo_layer_t* layers, int32_t n_layers,
                             void* workspace, size_t ws_bytes, hipStream_t stream);
+
+/* The per-layer plan of a stack of n_layers attention layers (host only, no GPU work): the zh page
+ * keeps about one layer in sixteen fully dense, the "pillar" layers, and sizes the condensate set
+ * per layer, with wider windows early and leaner sets late (technical summary §3), without a
+ * formula. This library's reading: max(1, round(n_layers / 16)) pillar layers (halves rounded to
+ * even), layer i * n_layers / n_pillar for i = 0 .. n_pillar - 1; every layer gets
+ * W = round(W_first + (W_last - W_first) * t) and k likewise, t = layer / (n_layers - 1) (0 for
+ * one layer), halves rounded to even. Fills pillar, W and k of layers[0 .. n_layers - 1] (the
+ * other fields are left as they are). TOPO_EINVAL if layers is NULL, n_layers < 1 or a W or k is
+ * negative. */
+int topo_pillar_plan(int32_t n_layers, int32_t W_first, int32_t k_first, int32_t W_last, int32_t k_last,
+                     topo_layer_t* layers);
+
+/* Finite-input check (the calls above require finite q, k and v): sets bit 0 of *flag (one uint32
+ * in device memory, not cleared by this call) if any of the `count` elements of `buf` (dtype
+ * TOPO_F32 or TOPO_BF16) is a NaN or an infinity. Asynchronous on `stream`; read *flag after
+ * synchronising. TOPO_EINVAL on a NULL or misaligned pointer (buf 16-byte, flag 4-byte aligned),
+ * TOPO_EUNSUPPORTED on another dtype. */
+int topo_check_finite(const void* buf, size_t count, int32_t dtype, uint32_t* flag, hipStream_t stream);
+
+/* Diagnostics. How a query's top-k part was chosen (TOPO_PATH_*), and where a call leaves the key
+ * scan's candidate lists in its workspace, so that the fast scores can be checked against exact
+ * ones and the paths counted. The layout describes the workspace of the given parameters and
+ * operation; the contents are those of the last call that used the workspace, once it has
+ * completed. */
+#define TOPO_PATH_NONE 0            /* no top-k part (k = 0 or no candidate)                       */
+#define TOPO_PATH_ALL 1             /* at most k candidates, all taken                             */
+#define TOPO_PATH_FAST 2            /* from the scan's lists: decode re-scores the short list in
+                                       float64; prefill: the fast scores' bounds decided it        */
+#define TOPO_PATH_BAND 3            /* prefill: from the lists, entries in the band re-scored      */
+#define TOPO_PATH_EXACT_ASKED 4     /* exact float64 radix selection over every candidate: flag,
+                                       float32 prefill, or a size above the scan's limits          */
+#define TOPO_PATH_EXACT_OVERFLOW 5  /* the same, after a scan list overflowed (tie-heavy keys)     */
+#define TOPO_PATH_EXACT_CROWDED 6   /* the same, after the decode short list was crowded (ties)    */
+
+typedef struct {
+    int64_t queries;       /* query rows described: B*Hq (decode ops) or B*Hq*n_q (prefill)      */
+    int64_t lists;         /* candidate lists per query row                                      */
+    int64_t slots;         /* entries per list                                                   */
+    size_t  count_offset;  /* uint32 [queries][lists]: entries of each list; 0xFFFFFFFF if the
+                              list overflowed                                                    */
+    size_t  entry_offset;  /* [queries][lists][slots] pairs {float fast score, int32 position}   */
+    size_t  eps_offset;    /* float [queries][lists][slots]: the bound the kernels used for each
+                              entry (decode); 0 when not stored (prefill: eps_coef |q| |k|)      */
+    size_t  path_offset;   /* int32 TOPO_PATH_* of query i at path_offset + i * path_stride       */
+    size_t  path_stride;
+    float   eps_coef;      /* every fast score obeys |s_fast - s| <= eps_coef * |q|_2 * |k|_2    */
+    int32_t reserved;
+} topo_ws_view_t;
+
+/* Fills *view for op TOPO_OP_DECODE, TOPO_OP_SELECT, TOPO_OP_DECODE_CERTIFIED,
+ * TOPO_OP_DECODE_RAGGED or TOPO_OP_PREFILL (decode: the key scan's own lists, before any merge;
+ * prefill: one list per query row). The decode layout depends on the current device's compute
+ * unit count, like the calls. lists = 0 when the call runs no key scan (k = 0, at most k
+ * candidates, the exact flag, or k or the shape above the scan's limits). TOPO_EINVAL for another
+ * op, invalid parameters or a NULL view; TOPO_EUNSUPPORTED as the call itself. */
+int topo_workspace_view(const topo_params_t* p, int op, topo_ws_view_t* view);
 
 /* Measurement helper, not part of the method: streams `bytes` (a multiple of 16) from `buf`
  * once with the same load path as the decode key scan and reduces them into `sink`

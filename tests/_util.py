@@ -86,3 +86,68 @@ def check_set_structure(sel: np.ndarray, cnt: np.ndarray, p: int, W: int, k: int
     w_lo = max(0, p - W + 1)
     assert np.all(body[:, c - (p - w_lo + 1):] == np.arange(w_lo, p + 1))
     assert np.all(body <= p)
+
+
+LIST_OVERFLOW = 0xFFFFFFFF
+
+
+class ListsView:
+    """Host copy of what a call left in its workspace, laid out by topo_workspace_view: the key
+    scan's candidate lists (count per list, (fast score, position) per entry, the bound the kernels
+    used per entry when stored) and every query's selection path."""
+
+    def __init__(self, ws, view):
+        raw = ws.cpu().numpy().view(np.uint8)
+        Q, L, S = int(view.queries), int(view.lists), int(view.slots)
+        self.Q, self.L, self.S = Q, L, S
+        self.eps_coef = float(view.eps_coef)
+
+        def take(off, count, dt):
+            return np.frombuffer(raw, dtype=dt, count=count, offset=int(off)).copy()
+
+        if L > 0:
+            self.count = take(view.count_offset, Q * L, np.uint32).reshape(Q, L)
+            ent = take(view.entry_offset, Q * L * S * 2, np.uint32).reshape(Q, L, S, 2)
+            self.score = ent[..., 0].view(np.float32)
+            self.pos = ent[..., 1].view(np.int32)
+            self.eps = take(view.eps_offset, Q * L * S, np.float32).reshape(Q, L, S) if view.eps_offset else None
+        stride = int(view.path_stride)
+        block = raw[int(view.path_offset): int(view.path_offset) + Q * stride].reshape(Q, stride)
+        self.path = block[:, :4].copy().view(np.int32)[:, 0]
+
+    def entries(self, qi: int):
+        """(positions, fast scores, bounds or None) of every listed entry of query qi; None if one of
+        its lists overflowed."""
+        if self.L == 0:
+            return np.zeros(0, np.int64), np.zeros(0, np.float32), None
+        c = self.count[qi]
+        if np.any(c == LIST_OVERFLOW):
+            return None
+        sel = np.arange(self.S)[None, :] < c[:, None]
+        eps = self.eps[qi][sel] if self.eps is not None else None
+        return self.pos[qi][sel].astype(np.int64), self.score[qi][sel], eps
+
+
+def path_counts(paths) -> dict:
+    import dynamic_sparse_transformer_amd as topo
+    vals, cnts = np.unique(np.asarray(paths), return_counts=True)
+    return {topo.PATH_NAMES.get(int(v), str(int(v))): int(c) for v, c in zip(vals, cnts)}
+
+
+def oracle_decode_heads(q, k, v, W, K, scale, heads, causal=True, q_pos=None):
+    """oracle.topo_attn_decode over the given (b, h) heads, one head per thread (the oracle's own
+    function per head; the heads are independent)."""
+    import oracle
+    from tests._pool import tmap
+    B, Hq = q.shape[0], q.shape[1]
+    d = q.shape[-1]
+    out = np.full((B, Hq, d), np.nan, dtype=np.float32)
+    sel = np.full((B, Hq, 1 + W + K), -1, dtype=np.int32)
+    cnt = np.full((B, Hq), -1, dtype=np.int32)
+
+    def one(bh):
+        return bh, oracle.topo_attn_decode(q, k, v, W, K, scale, causal=causal, q_pos=q_pos, heads=[bh])
+
+    for (b, h), (o, s, c) in tmap(one, heads):
+        out[b, h], sel[b, h], cnt[b, h] = o[b, h], s[b, h], c[b, h]
+    return out, sel, cnt

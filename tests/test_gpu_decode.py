@@ -229,14 +229,6 @@ def test_multi_run_scan_blocks(ties):
     compare_case(vals, store, "bf16", 64, 64, 0.088, heads=heads, what=f"multi-run ties={ties}")
 
 
-def test_config4_full_size():
-    _full_config(4, [(0, 0), (1, 5), (2, 18), (3, 31)])
-
-
-def test_config5_full_size():
-    _full_config(5, [(0, 0), (0, 13), (0, 31)])
-
-
 @pytest.mark.parametrize("cfg,n_ctx", [(2, None), (5, 65536)])
 def test_dense_pillar_matches_oracle(cfg, n_ctx):
     torch_cuda()
