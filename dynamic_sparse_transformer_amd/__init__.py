@@ -20,7 +20,8 @@ __all__ = [
     "topo_attn_prefill", "topo_select", "topo_attn_dense", "topo_bw_probe", "topo_strerror",
     "topo_attn_decode_timed", "topo_attn_prefill_timed", "topo_attn_decode_certified",
     "topo_attn_decode_ragged", "topo_kv_append", "topo_attn_decode_layers", "pillar_schedule",
-    "topo_check_finite", "topo_workspace_view", "WorkspaceView",
+    "topo_check_finite", "topo_workspace_view", "WorkspaceView", "topo_attn_decode_noalloc",
+    "TOPO_NOALLOC_MAX_BYTES",
     "TOPO_FLAG_EXACT_SELECT", "TOPO_FLAG_DENSE_FALLBACK", "TOPO_FLAG_GROUP_SELECT", "TOPO_CERT_RHO", "TOPO_MAX_SET", "EXPORTS",
     "TOPO_PATH_NONE", "TOPO_PATH_ALL", "TOPO_PATH_FAST", "TOPO_PATH_BAND", "TOPO_PATH_EXACT_ASKED",
     "TOPO_PATH_EXACT_OVERFLOW", "TOPO_PATH_EXACT_CROWDED", "PATH_NAMES",
@@ -37,10 +38,12 @@ TOPO_FLAG_DENSE_FALLBACK = 2
 TOPO_FLAG_GROUP_SELECT = 4
 TOPO_CERT_RHO = 2.0 ** -24
 TOPO_MAX_SET = 4096
+TOPO_NOALLOC_MAX_BYTES = 32 << 20
 TOPO_PATH_NONE, TOPO_PATH_ALL, TOPO_PATH_FAST, TOPO_PATH_BAND = 0, 1, 2, 3
 TOPO_PATH_EXACT_ASKED, TOPO_PATH_EXACT_OVERFLOW, TOPO_PATH_EXACT_CROWDED = 4, 5, 6
 PATH_NAMES = {0: "none", 1: "all", 2: "fast", 3: "band", 4: "exact_asked", 5: "exact_overflow", 6: "exact_crowded"}
-EXPORTS = ("topo_workspace_bytes", "topo_attn_decode", "topo_attn_decode_timed", "topo_attn_decode_certified",
+EXPORTS = ("topo_workspace_bytes", "topo_attn_decode", "topo_attn_decode_noalloc", "topo_attn_decode_timed",
+           "topo_attn_decode_certified",
            "topo_attn_decode_ragged", "topo_kv_append", "topo_attn_decode_layers", "topo_layers_workspace_bytes",
            "topo_pillar_plan", "topo_attn_prefill", "topo_attn_prefill_timed", "topo_select", "topo_attn_dense",
            "topo_check_finite", "topo_workspace_view", "topo_bw_probe", "topo_strerror")
@@ -94,6 +97,8 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
         f = getattr(lib, name)
         f.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         f.restype = i32
+    lib.topo_attn_decode_noalloc.argtypes = [P, vp, vp, vp, vp, vp, vp, vp]
+    lib.topo_attn_decode_noalloc.restype = i32
     lib.topo_attn_decode_timed.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, sz, vp, vp, vp]
     lib.topo_attn_decode_timed.restype = i32
     lib.topo_attn_prefill_timed.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, sz, vp, vp, vp]
@@ -227,6 +232,34 @@ def topo_attn_decode(q, k, v, W: int, topk: int, softmax_scale: float, causal: b
     q_pos0 defaults to n-1 (the newest token). Returns (out f32 (B,Hq,1,d), sel_idx, sel_count)."""
     return _attn("topo_attn_decode", q, k, v, W, topk, softmax_scale, causal, q_pos0, flags, out, sel_idx,
                  sel_count, workspace, stream, want_sets)
+
+
+def topo_attn_decode_noalloc(q, k, v, W: int, topk: int, softmax_scale: float, causal: bool = True,
+                             q_pos0: int | None = None, flags: int = 0, out=None, sel_idx=None, sel_count=None,
+                             stream=None):
+    """topo_attn_decode with no workspace argument: the library uses its own static per-GPU buffer
+    (topo_attn_decode_noalloc; calls that overlap on one GPU race). Output and set tensors are
+    created here when not given; pass them to allocate nothing at all."""
+    torch = _torch()
+    lib = load_library()
+    q4 = q if q.dim() == 4 else q.unsqueeze(2)
+    if q_pos0 is None:
+        q_pos0 = k.shape[2] - q4.shape[2]
+    p = _params(q4, k, W, topk, softmax_scale, causal, q_pos0, flags)
+    _check_tensors(q4, k, v)
+    B, Hq, n_q, d = q4.shape
+    if out is None:
+        out = torch.empty((B, Hq, n_q, d), dtype=torch.float32, device=q4.device)
+    if sel_idx is None:
+        sel_idx = torch.empty((B, Hq, n_q, 1 + int(W) + int(topk)), dtype=torch.int32, device=q4.device)
+    if sel_count is None:
+        sel_count = torch.empty((B, Hq, n_q), dtype=torch.int32, device=q4.device)
+    _check_tensors(out, sel_idx, sel_count)
+    rc = lib.topo_attn_decode_noalloc(ctypes.byref(p), _ptr(q4), _ptr(k), _ptr(v), _ptr(out), _ptr(sel_idx),
+                                      _ptr(sel_count), _stream(stream))
+    if rc != 0:
+        raise TopoError(rc, "topo_attn_decode_noalloc")
+    return out, sel_idx, sel_count
 
 
 def _attn_timed(name, op, q, k, v, W, topk, softmax_scale, scan_begin, scan_end, causal, q_pos0, flags, out,

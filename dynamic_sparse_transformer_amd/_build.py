@@ -16,7 +16,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libtopo_attn.so")
 OBJDIR = os.path.join(ROOT, "_build")
-SOURCES = ["topo_api.hip", "topo_decode.hip", "topo_dense.hip", "topo_prefill.hip"]
+SOURCES = ["topo_api.hip", "topo_decode.hip", "topo_dense.hip", "topo_prefill.hip", "topo_noalloc.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

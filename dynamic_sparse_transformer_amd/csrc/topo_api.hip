@@ -433,6 +433,7 @@ const char* topo_strerror(int status) {
     case TOPO_EUNSUPPORTED: return "unsupported dtype or head dimension";
     case TOPO_EWORKSPACE: return "workspace missing or smaller than topo_workspace_bytes()";
     case TOPO_EHIP: return "HIP kernel launch failed";
+    case TOPO_ESCRATCH: return "the call needs more scratch than the allocation-free entry point's static buffer holds";
     default: return "unknown status";
   }
 }

@@ -71,6 +71,8 @@ extern "C" {
 #define TOPO_EUNSUPPORTED -2   /* dtype or head dimension this build has no kernels for       */
 #define TOPO_EWORKSPACE   -3   /* workspace NULL or smaller than topo_workspace_bytes()       */
 #define TOPO_EHIP         -4   /* a kernel launch failed (hipGetLastError after the launch)   */
+#define TOPO_ESCRATCH     -5   /* topo_attn_decode_noalloc: the call needs more scratch than
+                                  TOPO_NOALLOC_MAX_BYTES                                        */
 
 /* Element type of q, k and v. The output is always float32. */
 #define TOPO_F32  0
@@ -140,6 +142,22 @@ size_t topo_workspace_bytes(const topo_params_t* p, int op);
 int topo_attn_decode(const topo_params_t* p, const void* q, const void* k, const void* v,
                      float* out, int32_t* sel_idx, int32_t* sel_count,
                      void* workspace, size_t ws_bytes, hipStream_t stream);
+
+/* Allocation-free variant of topo_attn_decode, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * kernels and results, with the workspace in a buffer of TOPO_NOALLOC_MAX_BYTES that the library
+ * holds per GPU (a static device array, allocated when the library's code is loaded on that GPU
+ * and kept until the process ends) instead of a caller's. It calls no hipMalloc, hipFree or
+ * allocating routine. Unlike the other calls this one has global state: every call on a GPU uses
+ * that GPU's one buffer, so two calls that overlap on one GPU (other streams, other host
+ * threads) race and must be serialised by the caller; calls in stream order are fine (each call
+ * initialises what it reads). Returns TOPO_ESCRATCH, launching nothing, when
+ * topo_workspace_bytes(p, TOPO_OP_DECODE) exceeds TOPO_NOALLOC_MAX_BYTES (e.g. 20.6 MiB for
+ * B = 1, Hq = 32, Hkv = 8, d = 128, n_ctx = 2^20, W = 512, k = 64 bf16 fits); TOPO_EHIP if the
+ * buffer's device address cannot be found; otherwise errors as topo_attn_decode. */
+#define TOPO_NOALLOC_MAX_BYTES (32u << 20)
+int topo_attn_decode_noalloc(const topo_params_t* p, const void* q, const void* k, const void* v,
+                             float* out, int32_t* sel_idx, int32_t* sel_count, hipStream_t stream);
 
 /* Measurement variant of topo_attn_decode: identical results, and additionally records the
  * caller's events scan_begin / scan_end on `stream` immediately before and after the key-scan

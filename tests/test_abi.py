@@ -139,3 +139,16 @@ def test_ragged_decode_and_kv_append_reject_bad_arguments_on_host():
     assert lib.topo_kv_append(ctypes.byref(p), a, None, a, a, a, None) == -1
     assert lib.topo_kv_append(ctypes.byref(p), a, a, a, ctypes.c_void_p((1 << 40) + 8), a, None) == -1
     assert lib.topo_kv_append(ctypes.byref(_p(d=96)), a, a, a, a, a, None) == -2
+
+
+def test_noalloc_checks_on_host():
+    """The allocation-free decode validates like topo_attn_decode and refuses, before any device
+    call, a call whose workspace exceeds its static buffer."""
+    lib = topo.load_library()
+    a = ctypes.c_void_p(1 << 40)  # never dereferenced: validation fails first
+    big = _p(B=8, n_ctx=1 << 22, q_pos0=(1 << 22) - 1)
+    assert lib.topo_workspace_bytes(ctypes.byref(big), 0) > topo.TOPO_NOALLOC_MAX_BYTES
+    assert lib.topo_attn_decode_noalloc(ctypes.byref(big), a, a, a, a, a, a, None) == -5
+    assert topo.topo_strerror(-5)
+    for bad, code in ((dict(d=96), -2), (dict(W=-1), -1), (dict(n_q=2), -1), (dict(flags=8), -1)):
+        assert lib.topo_attn_decode_noalloc(ctypes.byref(_p(**bad)), a, a, a, a, a, a, None) == code
