@@ -10,8 +10,15 @@ bandwidth-bound core of the hot path.
 Workload (default): the 1M-token GQA decode: batch 1, 32 query heads sharing 8 kv heads, d=128,
 n = 2^20 bf16 keys, W=512, k=64, seeded synthetic inputs with a heavy anchor key and planted
 high-score keys (workloads/synth.py). A step is one topo_attn_decode call over all 32 heads,
-inputs resident in HBM. The 128K-context batch-4 decode and the causal 8K-token prefill (matrix-core
-key scan, reported against the bf16 MFMA peak) are reported alongside.
+inputs resident in HBM; `value` is timed on plain calls. The key scan's duration comes from a
+second pass of the same steps through topo_attn_decode_timed, whose HIP events bracket the scan
+launch on the call's stream. Reported alongside: the dense pillar layer on the same 1M inputs, the
+128K-context batch-4 decode (with the cost of the exact fallback selection), the causal 8K-token
+prefill (matrix-core key scan, against the bf16 MFMA peak) and a 32-layer decode stack.
+
+The CPU baseline (the oracle as it stands, on all 32 query heads of the 1M workload, spread over
+worker processes on the host's usable cores) runs before the GPU is touched, so that the workers
+are forked from a process with no GPU state; its sets are then compared with the GPU's.
 
 One JSON line on stdout; progress on stderr.
 """
@@ -65,14 +72,28 @@ def measured_traffic(kernel: str, workload: str):
     return entry.get("hbm_bytes_per_launch")
 
 
-def run_decode_bench(cfg: int, steps: int, warmup: int):
+def path_counts(topo, q, k, s, scale, ws):
+    """Selection path of every query of the last call that used the workspace ws (from the
+    library's workspace view)."""
+    import numpy as np
+    v = topo.topo_workspace_view(q, k, s.W, s.k, scale)
+    raw = ws.cpu().numpy()
+    stride = int(v.path_stride)
+    block = raw[int(v.path_offset): int(v.path_offset) + int(v.queries) * stride].reshape(int(v.queries), stride)
+    paths = block[:, :4].copy().view(np.int32)[:, 0]
+    vals, cnts = np.unique(paths, return_counts=True)
+    return {topo.PATH_NAMES.get(int(a), str(int(a))): int(c) for a, c in zip(vals, cnts)}
+
+
+def run_decode_bench(cfg: int, steps: int, warmup: int, w=None, extras: bool = True):
     import torch
 
     import dynamic_sparse_transformer_amd as topo
     from workloads import make_workload
 
     t0 = time.time()
-    w = make_workload(cfg)
+    if w is None:
+        w = make_workload(cfg)
     s = w.spec
     log(f"[bench] {s.name}: generated in {time.time() - t0:.1f}s")
 
@@ -93,25 +114,40 @@ def run_decode_bench(cfg: int, steps: int, warmup: int):
     def step():
         topo.topo_attn_decode(q, k, v, s.W, s.k, scale, out=out, sel_idx=sel, sel_count=cnt, workspace=ws)
 
-    for _ in range(warmup):
+    # Warm-up: at least `warmup` steps and half a second of them, so that the clocks have left any
+    # idle state before the timed steps.
+    tw = time.perf_counter()
+    nw = 0
+    while nw < warmup or time.perf_counter() - tw < 0.5:
         step()
+        nw += 1
+        if nw % 16 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
 
-    # Timed region: K steps, synchronised on both sides (wall clock), plus HIP events that the
-    # library records around every key-scan launch on this stream.
+    # The key scan's duration: K steps through topo_attn_decode_timed, whose HIP events are
+    # recorded by the library on this stream right before and after the scan launch.
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     for a, b in evs:  # create the underlying HIP events
         a.record(stream)
         b.record(stream)
     torch.cuda.synchronize()
-    t_start = time.perf_counter()
+    t_t0 = time.perf_counter()
     for a, b in evs:
         topo.topo_attn_decode_timed(q, k, v, s.W, s.k, scale, a, b, out=out, sel_idx=sel, sel_count=cnt,
                                     workspace=ws)
     torch.cuda.synchronize()
+    timed_ms = (time.perf_counter() - t_t0) * 1e3 / steps
+    scan_ms = sum(a.elapsed_time(b) for a, b in evs) / steps
+
+    # Timed region: K plain steps, synchronised on both sides (wall clock).
+    t_start = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
     t_end = time.perf_counter()
     ms_per_step = (t_end - t_start) * 1e3 / steps
-    scan_ms = sum(a.elapsed_time(b) for a, b in evs) / steps
+    paths = path_counts(topo, q, k, s, scale, ws)
 
     # The same step captured once into a HIP graph and replayed (a decode loop's per-token call):
     # the three kernels then run without host launches between them.
@@ -174,9 +210,61 @@ def run_decode_bench(cfg: int, steps: int, warmup: int):
     n_cand = s.n_ctx - 1 - s.W                     # keys the scan must rank per (batch, kv head)
     row_bytes = s.d * (2 if s.dtype == "bf16" else 4)
     alg_bytes = s.B * s.Hkv * n_cand * row_bytes   # each candidate key row read once per step
+
+    # The dense pillar layer on the same inputs (the comparison the 1M configuration asks for):
+    # topo_attn_dense reads every K and V row once per (batch, kv head).
+    dws = torch.empty(topo.topo_workspace_bytes(q, k, 0, 0, scale, op=topo.TOPO_OP_DENSE), dtype=torch.uint8,
+                      device="cuda")
+    od = torch.empty_like(out)
+    for _ in range(3):
+        topo.topo_attn_dense(q, k, v, scale, out=od, workspace=dws)
+    torch.cuda.synchronize()
+    td0 = time.perf_counter()
+    for _ in range(steps):
+        topo.topo_attn_dense(q, k, v, scale, out=od, workspace=dws)
+    torch.cuda.synchronize()
+    dense_ms = (time.perf_counter() - td0) * 1e3 / steps
+    dense_bytes = 2 * s.B * s.Hkv * s.n_ctx * row_bytes
+    dense = {"ms_per_step": dense_ms, "value": s.B * s.Hq / (dense_ms / 1e3), "unit": "queries/s",
+             "kv_bytes": dense_bytes, "achieved_gbs": dense_bytes / (dense_ms / 1e3) / 1e9,
+             "frac": dense_bytes / (dense_ms / 1e3) / 1e9 / HBM_PEAK_GBS,
+             "note": "whole call (dense_stream_kernel + dense_combine_kernel), wall clock"}
+    del dws, od
+
+    exact = None
+    if extras:
+        # The exact fallback selection (float64 radix select over every candidate, one block per
+        # query head), forced for every head with TOPO_FLAG_EXACT_SELECT, and reached on its own by
+        # tie-heavy keys (every key the same row: every score ties, the scan's lists overflow).
+        xstep = lambda kk: topo.topo_attn_decode(q, kk, v, s.W, s.k, scale, flags=topo.TOPO_FLAG_EXACT_SELECT,
+                                                 out=out, sel_idx=sel, sel_count=cnt, workspace=ws)
+        xstep(k)
+        torch.cuda.synchronize()
+        tx0 = time.perf_counter()
+        for _ in range(3):
+            xstep(k)
+        torch.cuda.synchronize()
+        x_ms = (time.perf_counter() - tx0) * 1e3 / 3
+        kt = torch.ones_like(k)
+        tstep = lambda: topo.topo_attn_decode(q, kt, v, s.W, s.k, scale, out=out, sel_idx=sel, sel_count=cnt,
+                                              workspace=ws)
+        tstep()
+        torch.cuda.synchronize()
+        tt0 = time.perf_counter()
+        for _ in range(3):
+            tstep()
+        torch.cuda.synchronize()
+        t_ms = (time.perf_counter() - tt0) * 1e3 / 3
+        exact = {"forced_ms_per_step": x_ms, "tie_heavy_ms_per_step": t_ms,
+                 "tie_heavy_paths": path_counts(topo, q, kt, s, scale, ws)}
+        del kt
+        step()  # the lists and outputs of the real inputs again
+        torch.cuda.synchronize()
+
     queries = s.B * s.Hq
     res = {
         "spec": s, "workload": w, "ms_per_step": ms_per_step, "scan_ms": scan_ms, "alg_bytes": alg_bytes,
+        "timed_ms_per_step": timed_ms, "paths": paths, "dense": dense, "exact": exact,
         "queries": queries, "certificate": certificate, "graph_ms_per_step": graph_ms, "group_select": group,
         "out": out.cpu().numpy()[:, :, 0], "sel": sel.cpu().numpy()[:, :, 0],
         "cnt": cnt.cpu().numpy()[:, :, 0],
@@ -293,28 +381,78 @@ def run_layers_bench(n_layers: int, steps: int, warmup: int):
                        "W_first": 512, "k_first": 64, "W_last": 128, "k_last": 32}}
 
 
-def cpu_baseline(res, heads: int):
-    """The CPU oracle, as it stands, on a bounded sample of the same workload: the first `heads`
-    query heads of batch 0. Also checks the GPU sets of those heads against it."""
+_CPU_JOB = None
+
+
+def _cpu_oracle_head(h):
+    import oracle
+    q, k, v, s = _CPU_JOB
+    ro, rs, rc = oracle.topo_attn_decode(q, k, v, s.W, s.k, float(s.softmax_scale), heads=[(0, h)])
+    return ro[0, h], rs[0, h], rc[0, h]
+
+
+def host_description():
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except AttributeError:
+        usable = os.cpu_count() or 1
+    return {"nproc": os.cpu_count(), "usable_cpus": usable, "model": model}
+
+
+def cpu_baseline_run(w, heads: int, single: int = 4):
+    """The CPU oracle, as it stands, on a bounded sample of the workload: the first `heads` query
+    heads of batch 0, one head per worker process on the host's usable cores (at most 16), then
+    `single` heads in this process alone for the one-core rate. Runs before the GPU is touched."""
+    import multiprocessing as mp
+
     import numpy as np
 
-    import oracle
-
-    w, s = res["workload"], res["spec"]
-    sample = [(0, h) for h in range(min(heads, s.Hq))]
+    global _CPU_JOB
+    s = w.spec
+    sample = list(range(min(heads, s.Hq)))
     q, k, v = w.f32("q"), w.f32("k"), w.f32("v")
+    host = host_description()
+    workers = max(1, min(16, host["usable_cpus"], len(sample)))
+    _CPU_JOB = (q, k, v, s)
     t0 = time.perf_counter()
-    ro, rs, rc = oracle.topo_attn_decode(q, k, v, s.W, s.k, float(s.softmax_scale), heads=sample)
+    with mp.get_context("fork").Pool(workers) as pool:
+        parts = pool.map(_cpu_oracle_head, sample, chunksize=1)
     dt = time.perf_counter() - t0
-    idx = tuple(np.array(sample).T)
-    sets_equal = bool(np.array_equal(res["sel"][idx], rs[idx]) and np.array_equal(res["cnt"][idx], rc[idx]))
-    err = float(np.max(np.abs(res["out"][idx].astype(np.float64) - ro[idx])))
-    rel = float(np.max(np.abs(res["out"][idx].astype(np.float64) - ro[idx]) / (np.abs(ro[idx]) + 1e-30)))
-    return {
-        "value": len(sample) / dt, "unit": "queries/s", "cores": 1, "kind": "oracle",
-        "sample": f"{len(sample)} of {s.B * s.Hq} query heads of {s.name} (batch 0), {dt:.1f} s, "
-                  "numpy float64, one thread",
-    }, {"heads_checked": len(sample), "sets_bit_exact": sets_equal, "max_abs_err": err, "max_rel_err": rel}
+    t1 = time.perf_counter()
+    for h in sample[:single]:
+        _cpu_oracle_head(h)
+    dt1 = time.perf_counter() - t1
+    _CPU_JOB = None
+    ref = {"heads": sample, "out": np.stack([p[0] for p in parts]), "sel": np.stack([p[1] for p in parts]),
+           "cnt": np.array([p[2] for p in parts])}
+    cpu = {
+        "value": len(sample) / dt, "unit": "queries/s", "cores": workers, "kind": "oracle",
+        "sample": f"{len(sample)} of {s.B * s.Hq} query heads of {s.name} (batch 0), one head per worker "
+                  f"process, {dt:.1f} s wall on {workers} cores; numpy float64",
+        "host": host,
+        "single_core": {"value": min(single, len(sample)) / dt1, "unit": "queries/s", "heads": min(single, len(sample)),
+                        "seconds": dt1},
+    }
+    return cpu, ref
+
+
+def cpu_parity(res, ref):
+    """The GPU sets and outputs of the baseline's heads against the oracle's."""
+    import numpy as np
+    idx = (np.zeros(len(ref["heads"]), dtype=int), np.array(ref["heads"]))
+    sets_equal = bool(np.array_equal(res["sel"][idx], ref["sel"]) and np.array_equal(res["cnt"][idx], ref["cnt"]))
+    d = np.abs(res["out"][idx].astype(np.float64) - ref["out"].astype(np.float64))
+    return {"heads_checked": len(ref["heads"]), "sets_bit_exact": sets_equal, "max_abs_err": float(d.max()),
+            "max_rel_err": float(np.max(d / (np.abs(ref["out"]) + 1e-30)))}
 
 
 def main():
@@ -340,14 +478,28 @@ def main():
               "(batch, kv head) is described in the design notes, not implemented).", file=sys.stderr)
         sys.exit(2)
 
+    import dynamic_sparse_transformer_amd as topo
+    if not os.path.exists(topo.library_path):  # fail loudly if the HIP library is missing
+        raise FileNotFoundError(f"{topo.library_path} is missing: build it first")
+    from workloads import make_workload
+
+    # The CPU baseline first: its worker processes are forked before anything touches the GPU
+    # (the library itself is loaded only afterwards).
+    t0 = time.time()
+    w_main = make_workload(args.config)
+    log(f"[bench] {w_main.spec.name}: generated in {time.time() - t0:.1f}s")
+    cpu, ref = (None, None)
+    if not args.no_cpu_baseline:
+        log(f"[bench] CPU oracle on {args.cpu_heads} heads")
+        cpu, ref = cpu_baseline_run(w_main, args.cpu_heads)
+
     import torch
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
-    import dynamic_sparse_transformer_amd as topo
-    topo.load_library()  # fail loudly if the HIP library is missing
+    topo.load_library()
 
-    main_res = run_decode_bench(args.config, args.steps, args.warmup)
+    main_res = run_decode_bench(args.config, args.steps, args.warmup, w=w_main, extras=False)
     s = main_res["spec"]
     also = []
     for c in args.also or []:
@@ -359,10 +511,11 @@ def main():
             "ms_per_step": r["ms_per_step"], "kscan_us": r["scan_ms"] * 1e3,
             "kscan_gbs": r["alg_bytes"] / (r["scan_ms"] / 1e3) / 1e9,
             "kscan_frac": r["alg_bytes"] / (r["scan_ms"] / 1e3) / 1e9 / HBM_PEAK_GBS,
+            "timed_ms_per_step": r["timed_ms_per_step"], "paths": r["paths"],
             "certificate": r["certificate"],
             "graph_replay": {"ms_per_step": r["graph_ms_per_step"],
                              "value": r["queries"] / (r["graph_ms_per_step"] / 1e3)},
-            "group_select": r["group_select"],
+            "group_select": r["group_select"], "dense_pillar": r["dense"], "exact_fallback": r["exact"],
         })
 
     if args.prefill:
@@ -391,12 +544,10 @@ def main():
     roofline = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                 "kernel": "kscan_kernel<256,4,bf16>", "kernel_us": main_res["scan_ms"] * 1e3,
-                "alg_bytes_per_launch": main_res["alg_bytes"]}
-
-    cpu, parity = (None, None)
-    if not args.no_cpu_baseline:
-        log(f"[bench] CPU oracle on {args.cpu_heads} heads")
-        cpu, parity = cpu_baseline(main_res, args.cpu_heads)
+                "alg_bytes_per_launch": main_res["alg_bytes"],
+                "timing": "HIP events around the scan launch, in a second pass of the same steps "
+                          f"(topo_attn_decode_timed, {main_res['timed_ms_per_step']:.4f} ms per step)"}
+    parity = cpu_parity(main_res, ref) if ref is not None else None
 
     value = main_res["queries"] / (main_res["ms_per_step"] / 1e3)
     line = {
@@ -408,6 +559,7 @@ def main():
                    "context": s.n_ctx, "window": s.W, "topk": s.k, "set_size": 1 + s.W + s.k,
                    "precision": "bf16 inputs, float64 set re-score and softmax, float32 output"},
         "roofline": roofline, "cpu_baseline": cpu, "parity_sample": parity,
+        "paths": main_res["paths"], "dense_pillar": main_res["dense"],
         "certificate": main_res["certificate"],
         "graph_replay": {"ms_per_step": main_res["graph_ms_per_step"],
                          "value": main_res["queries"] / (main_res["graph_ms_per_step"] / 1e3),

@@ -1,10 +1,12 @@
 // Dense softmax attention over every visible key on gfx950: the full-attention "pillar" layers
 // that the zh page of "The Condensate Theorem: Transformers are O(n), Not O(n^2)" keeps in a few
 // layers (technical summary §3), and the comparator of the exactness claim (technical summary
-// §2). Split over the keys (flash-decoding): each block folds a run of 2048 keys into a partial
+// §2). Split over the keys (flash-decoding): each block folds a range of keys into a partial
 // (max, sum of weights, weighted V sum) per query head with an online softmax; a second kernel
 // merges the partials. K and V are each read once per (batch, kv head) for all G query heads.
-// bf16 inputs use float32 scores and accumulation; float32 inputs use float64 for both.
+// bf16 inputs use float32 scores and accumulation (dense_stream_kernel, which streams K and V
+// like the decode key scan streams K); float32 inputs use float64 for both (dense_partial_kernel,
+// tiles staged through LDS).
 #include "topo_device.h"
 #include "topo_internal.h"
 
@@ -32,7 +34,9 @@ struct DenseArgs {
   const unsigned char* v;
   void* part;
   int64_t n, n_q, q_pos0, chunks;
+  int64_t kpb;        // keys per block (the partial of block x covers keys [x * kpb, (x + 1) * kpb))
   int32_t Hq, Hkv, G, causal, nslices;
+  int32_t runs;       // dense_stream_kernel: runs of DS_KEYS_PER_RUN keys per block
   double scale;
   const float* gate;  // may be null; else rows with gate[row] < gate_min are skipped
   float gate_min;
@@ -249,9 +253,211 @@ __global__ __launch_bounds__(256) void dense_partial_kernel(DenseArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------------------------
+// dense_stream (bf16 inputs): grid (blocks over the keys, B*Hkv, n_q*nslices), 256 threads. Block x
+// folds keys [x * kpb, (x + 1) * kpb) in `runs` runs of 4 waves x 512 keys, as the decode key scan
+// lays out its loads: a 64-key tile is 8 groups of 8 lanes, group r holds keys 8i + r (i < 8) and
+// lane s of a group the 16-byte chunks c*8 + s (c < CPL) of each, so every load instruction reads
+// eight full 128-byte half rows. K and V of a tile have register sets of their own, and each key
+// group's registers are reloaded with the next tile as soon as they are used (K after the partial
+// dot products, V after the weighted sum), so every wave keeps about a tile of K and V (32 KB at
+// d = 128) in flight; with the accumulators of four heads that takes one wave per SIMD (up to 512
+// registers). A reduce-scatter over the 8 lanes of a group leaves every lane the score of key 8s + r; the
+// online softmax keeps a wave-wide running maximum per head (the partial output and sums are
+// rescaled when it rises); the weight of key 8i + r reaches the lanes of group r by a swizzle.
+// At the end the 8 key groups and the 4 waves are folded into one partial per head.
+constexpr int DS_KEYS_PER_RUN = 2048;
+constexpr int DS_MAX_RUNS = 16;
+
+// Value of lane 8 (lane / 8) + i in every lane (i < 8): within each 32-lane half, the swizzle keeps
+// lane bits 3-4 (and_mask 0x18) and sets bits 0-2 to i (or_mask). i is a constant once unrolled.
+__device__ __forceinline__ float group_bcast(float x, int i) {
+  const int v = __float_as_int(x);
+  switch (i) {
+    case 0: return __int_as_float(__builtin_amdgcn_ds_swizzle(v, 0x18 | (0 << 5)));
+    case 1: return __int_as_float(__builtin_amdgcn_ds_swizzle(v, 0x18 | (1 << 5)));
+    case 2: return __int_as_float(__builtin_amdgcn_ds_swizzle(v, 0x18 | (2 << 5)));
+    case 3: return __int_as_float(__builtin_amdgcn_ds_swizzle(v, 0x18 | (3 << 5)));
+    case 4: return __int_as_float(__builtin_amdgcn_ds_swizzle(v, 0x18 | (4 << 5)));
+    case 5: return __int_as_float(__builtin_amdgcn_ds_swizzle(v, 0x18 | (5 << 5)));
+    case 6: return __int_as_float(__builtin_amdgcn_ds_swizzle(v, 0x18 | (6 << 5)));
+    default: return __int_as_float(__builtin_amdgcn_ds_swizzle(v, 0x18 | (7 << 5)));
+  }
+}
+
+template <int RB, int GT>
+__global__ __launch_bounds__(256, 1) void dense_stream_kernel(DenseArgs a) {
+  constexpr int D = RB / 2;       // bf16 elements per row
+  constexpr int CPL = RB / 128;   // 16-byte chunks of a row per lane
+  constexpr int EL = CPL * 8;     // elements of a row per lane
+  __shared__ float wn[4][GT][D];
+  __shared__ float wm[4][GT], wz[4][GT];
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, s = lane & 7, r = lane >> 3;
+  const int grp = blockIdx.y;
+  const int b = grp / a.Hkv, g = grp - b * a.Hkv;
+  const int qi = blockIdx.z / a.nslices, slice = blockIdx.z - qi * a.nslices;
+  const int h0 = g * a.G + slice * GT;
+  const int nh = min(GT, a.G - slice * GT);
+  const int64_t p = a.q_pos0 + qi;
+  const int64_t vis_hi = a.causal ? p : a.n - 1;
+  const int64_t blk_key0 = (int64_t)blockIdx.x * a.kpb;
+  if (blk_key0 > vis_hi) return;  // no visible key: the combine reads no partial of this block
+  if (a.gate) {  // skip the block if none of its query rows is gated in
+    bool any = false;
+    for (int h = 0; h < nh; ++h) any |= a.gate[((size_t)b * a.Hq + h0 + h) * a.n_q + qi] >= a.gate_min;
+    if (!any) return;
+  }
+
+  uint4 qv[GT][CPL];
+#pragma unroll
+  for (int h = 0; h < GT; ++h)
+#pragma unroll
+    for (int c = 0; c < CPL; ++c)
+      qv[h][c] = h < nh ? *(const uint4*)(a.q + (((size_t)b * a.Hq + h0 + h) * a.n_q + qi) * RB + c * 128 + s * 16)
+                        : make_uint4(0u, 0u, 0u, 0u);
+  const float sc = (float)a.scale;
+  const unsigned char* kb = a.k + (size_t)grp * (size_t)a.n * RB;
+  const unsigned char* vb = a.v + (size_t)grp * (size_t)a.n * RB;
+  auto tile_key0 = [&](int t) -> int64_t {  // tile t of this wave: run t / 8, tile t % 8 of the wave's 512 keys
+    return blk_key0 + (int64_t)((t >> 3) * 4 + wave) * 512 + (int64_t)(t & 7) * 64;
+  };
+  // loads of key group i of the tile at row0 (rows past the last visible key clamped onto it; their
+  // weights are zero)
+  auto load_group = [&](uint4 (&dst)[CPL], const unsigned char* base, int64_t row0, int i) {
+    const int64_t row = row0 + 8 * i + r;
+    const unsigned char* src = base + (row <= vis_hi ? row : vis_hi) * RB + s * 16;
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) dst[c] = ntload16(src + c * 128);
+  };
+
+  float acc[GT][EL], m_run[GT], z_run[GT];
+#pragma unroll
+  for (int h = 0; h < GT; ++h) {
+    m_run[h] = -INFINITY;
+    z_run[h] = 0.f;
+#pragma unroll
+    for (int e = 0; e < EL; ++e) acc[h][e] = 0.f;
+  }
+  uint4 kk[8][CPL], vv[8][CPL];
+  const int ntiles = a.runs * 8;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) load_group(kk[i], kb, tile_key0(0), i);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) load_group(vv[i], vb, tile_key0(0), i);
+#pragma unroll 1
+  for (int t = 0; t < ntiles; ++t) {
+    const int64_t row0 = tile_key0(t);
+    const bool more = t + 1 < ntiles;
+    const int64_t nrow0 = more ? tile_key0(t + 1) : row0;
+    // K of tile t: partial dot products, then the registers take K of tile t+1
+    float P[GT][8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+#pragma unroll
+      for (int h = 0; h < GT; ++h) {
+        float d = 0.f;
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) d = dot_chunk_bf16(kk[i][c], qv[h][c], d);
+        P[h][i] = d;
+      }
+      if (more) load_group(kk[i], kb, nrow0, i);
+    }
+    const bool valid = row0 + 8 * s + r <= vis_hi;
+    float w[GT];
+#pragma unroll
+    for (int h = 0; h < GT; ++h) {
+      float Q1[1][8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) Q1[0][i] = P[h][i];
+      reduce_scatter<8, 1>(Q1, s);
+      const float z = valid ? sc * Q1[0][0] : -INFINITY;
+      float tm = z;
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) tm = fmaxf(tm, __shfl_xor(tm, o));
+      if (tm > m_run[h]) {  // wave-uniform: the running maximum rises, rescale what was summed
+        const float f = __expf(m_run[h] - tm);
+        z_run[h] *= f;
+#pragma unroll
+        for (int e = 0; e < EL; ++e) acc[h][e] *= f;
+        m_run[h] = tm;
+      }
+      w[h] = valid ? __expf(z - m_run[h]) : 0.f;
+      z_run[h] += w[h];
+    }
+    // V of tile t: the weighted sum, then the registers take V of tile t+1
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      float wi[GT];
+#pragma unroll
+      for (int h = 0; h < GT; ++h)  // weight of key 8i + r, held by lane 8r + i of the group
+        wi[h] = group_bcast(w[h], i);
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) {
+        const uint32_t ws[4] = {vv[i][c].x, vv[i][c].y, vv[i][c].z, vv[i][c].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float lo = bf16_lo(ws[e]), hi = bf16_hi(ws[e]);
+#pragma unroll
+          for (int h = 0; h < GT; ++h) {
+            acc[h][c * 8 + 2 * e] = fmaf(wi[h], lo, acc[h][c * 8 + 2 * e]);
+            acc[h][c * 8 + 2 * e + 1] = fmaf(wi[h], hi, acc[h][c * 8 + 2 * e + 1]);
+          }
+        }
+      }
+      if (more) load_group(vv[i], vb, nrow0, i);
+    }
+  }
+
+  // fold the key groups (lanes with equal s hold the same elements) and the lanes' weight sums
+#pragma unroll
+  for (int h = 0; h < GT; ++h) {
+#pragma unroll
+    for (int e = 0; e < EL; ++e)
+      for (int o = 8; o < 64; o <<= 1) acc[h][e] += __shfl_xor(acc[h][e], o);
+    z_run[h] = wave_sum_f32(z_run[h]);
+  }
+  if (r == 0) {
+#pragma unroll
+    for (int h = 0; h < GT; ++h)
+#pragma unroll
+      for (int c = 0; c < CPL; ++c)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) wn[wave][h][(c * 8 + s) * 8 + e] = acc[h][c * 8 + e];
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int h = 0; h < GT; ++h) {
+      wm[wave][h] = m_run[h];
+      wz[wave][h] = z_run[h];
+    }
+  }
+  __syncthreads();
+  for (int i = tid; i < nh * D; i += 256) {
+    const int h = i / D, c = i - h * D;
+    float m = wm[0][h];
+    for (int w2 = 1; w2 < 4; ++w2) m = fmaxf(m, wm[w2][h]);
+    double nv = 0.0, zz = 0.0;
+    if (m != -INFINITY) {
+      for (int w2 = 0; w2 < 4; ++w2) {
+        const double f = exp((double)wm[w2][h] - (double)m);
+        nv += f * (double)wn[w2][h][c];
+        zz += f * (double)wz[w2][h];
+      }
+    }
+    DensePartial<D>* part = (DensePartial<D>*)a.part +
+                            ((((size_t)b * a.Hq + h0 + h) * a.n_q + qi) * a.chunks + blockIdx.x);
+    part->nv[c] = nv;
+    if (c == 0) {
+      part->m = (double)m;
+      part->z = zz;
+    }
+  }
+}
+
 // One wave per (batch, query head, query): merge the chunk partials.
 template <int D>
-__global__ __launch_bounds__(64) void dense_combine_kernel(const void* partv, float* out, int64_t chunks,
+__global__ __launch_bounds__(64) void dense_combine_kernel(const void* partv, float* out, int64_t chunks, int64_t kpb,
                                                            int64_t n_q, int64_t q_pos0, int64_t n, int causal,
                                                            const float* gate, float gate_min) {
   const size_t row = blockIdx.x;  // (b*Hq + h)*n_q + qi
@@ -259,7 +465,7 @@ __global__ __launch_bounds__(64) void dense_combine_kernel(const void* partv, fl
   const int64_t qi = (int64_t)(row % (size_t)n_q);
   const int64_t p = q_pos0 + qi;
   const int64_t vis_hi = causal ? p : n - 1;
-  const int64_t used = vis_hi / DN_KEYS + 1;
+  const int64_t used = vis_hi / kpb + 1;
   const DensePartial<D>* part = (const DensePartial<D>*)partv + row * (size_t)chunks;
   const int lane = threadIdx.x;
   double m = -INFINITY;
@@ -293,6 +499,25 @@ static hipError_t launch_dense_g(const DenseArgs& da, int GT, dim3 grid, hipStre
   }
 }
 
+template <int RB>
+static hipError_t launch_stream_g(const DenseArgs& da, int GT, dim3 grid, hipStream_t s) {
+  switch (GT) {
+    case 1: hipLaunchKernelGGL((dense_stream_kernel<RB, 1>), grid, dim3(256), 0, s, da); break;
+    case 2: hipLaunchKernelGGL((dense_stream_kernel<RB, 2>), grid, dim3(256), 0, s, da); break;
+    default: hipLaunchKernelGGL((dense_stream_kernel<RB, 4>), grid, dim3(256), 0, s, da); break;
+  }
+  return hipGetLastError();
+}
+
+static int device_cus() {
+  int dev = 0, cus = 256;
+  if (hipGetDevice(&dev) == hipSuccess) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0) cus = v;
+  }
+  return cus;
+}
+
 hipError_t launch_dense(const DenseLaunch& L, hipStream_t stream) {
   DenseArgs da;
   da.q = (const unsigned char*)L.q;
@@ -314,23 +539,37 @@ hipError_t launch_dense(const DenseLaunch& L, hipStream_t stream) {
   int GT = L.G >= 4 ? 4 : L.G;
   if (!L.bf16) GT = L.d == 128 ? 1 : (L.G >= 2 ? 2 : 1);
   da.nslices = (L.G + GT - 1) / GT;
-  // Only the chunks that hold visible keys of the last query are launched.
+  // Only the blocks that hold visible keys of the last query are launched.
   const int64_t vis_hi_max = L.causal ? L.q_pos0 + L.n_q - 1 : L.n - 1;
-  dim3 grid((unsigned)(vis_hi_max / DN_KEYS + 1), (unsigned)(L.B * L.Hkv), (unsigned)(L.n_q * da.nslices));
   hipError_t e;
   if (L.bf16) {
-    e = L.d == 128 ? launch_dense_g<128, true>(da, GT, grid, stream) : launch_dense_g<64, true>(da, GT, grid, stream);
+    // runs per block: the largest count that still leaves two blocks per compute unit (the
+    // partials fit the workspace sized for one run per block)
+    const int64_t others = (int64_t)L.B * L.Hkv * L.n_q * da.nslices;
+    int runs = 1;
+    for (int rr = DS_MAX_RUNS; rr > 1; rr >>= 1)
+      if ((vis_hi_max / (DS_KEYS_PER_RUN * (int64_t)rr) + 1) * others >= 2 * (int64_t)device_cus()) {
+        runs = rr;
+        break;
+      }
+    da.runs = runs;
+    da.kpb = (int64_t)DS_KEYS_PER_RUN * runs;
+    da.chunks = vis_hi_max / da.kpb + 1;
+    const dim3 grid((unsigned)da.chunks, (unsigned)(L.B * L.Hkv), (unsigned)(L.n_q * da.nslices));
+    e = L.d == 128 ? launch_stream_g<256>(da, GT, grid, stream) : launch_stream_g<128>(da, GT, grid, stream);
   } else {
+    da.kpb = DN_KEYS;
+    const dim3 grid((unsigned)(vis_hi_max / DN_KEYS + 1), (unsigned)(L.B * L.Hkv), (unsigned)(L.n_q * da.nslices));
     e = L.d == 128 ? launch_dense_g<128, false>(da, GT, grid, stream) : launch_dense_g<64, false>(da, GT, grid, stream);
   }
   if (e != hipSuccess) return e;
   const unsigned rows = (unsigned)((size_t)L.B * L.Hq * L.n_q);
   if (L.d == 128) {
-    hipLaunchKernelGGL(dense_combine_kernel<128>, dim3(rows), dim3(64), 0, stream, L.ws, L.out, da.chunks, L.n_q,
-                       L.q_pos0, L.n, L.causal, L.gate, L.gate_min);
+    hipLaunchKernelGGL(dense_combine_kernel<128>, dim3(rows), dim3(64), 0, stream, L.ws, L.out, da.chunks, da.kpb,
+                       L.n_q, L.q_pos0, L.n, L.causal, L.gate, L.gate_min);
   } else {
-    hipLaunchKernelGGL(dense_combine_kernel<64>, dim3(rows), dim3(64), 0, stream, L.ws, L.out, da.chunks, L.n_q,
-                       L.q_pos0, L.n, L.causal, L.gate, L.gate_min);
+    hipLaunchKernelGGL(dense_combine_kernel<64>, dim3(rows), dim3(64), 0, stream, L.ws, L.out, da.chunks, da.kpb,
+                       L.n_q, L.q_pos0, L.n, L.causal, L.gate, L.gate_min);
   }
   return hipGetLastError();
 }

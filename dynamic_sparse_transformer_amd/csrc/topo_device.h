@@ -244,6 +244,32 @@ __device__ __forceinline__ float group_sum_f32(float x) {
   return x;
 }
 
+// One halving step of a reduce-scatter: the lanes of each half of a 2*HALF group keep their half
+// of the remaining keys, summed with the partner's copy.
+template <int HALF, int V, int L>
+__device__ __forceinline__ void rs_step(float (&A)[V][L], bool hi) {
+#pragma unroll
+  for (int v = 0; v < V; ++v) {
+#pragma unroll
+    for (int t = 0; t < HALF; ++t) {
+      const float x0 = A[v][t] + partner<HALF>(A[v][t]);
+      const float x1 = A[v][t + HALF] + partner<HALF>(A[v][t + HALF]);
+      A[v][t] = hi ? x1 : x0;
+    }
+  }
+}
+
+// A[v][m] holds this lane's partial sum of value v for key m of its L-lane group. Afterwards
+// A[v][0] holds the full sum of value v for key m = (lane % L).
+template <int L, int V>
+__device__ __forceinline__ void reduce_scatter(float (&A)[V][L], int s) {
+  if constexpr (L >= 32) rs_step<16, V, L>(A, (s & 16) != 0);
+  if constexpr (L >= 16) rs_step<8, V, L>(A, (s & 8) != 0);
+  rs_step<4, V, L>(A, (s & 4) != 0);
+  rs_step<2, V, L>(A, (s & 2) != 0);
+  rs_step<1, V, L>(A, (s & 1) != 0);
+}
+
 // Job of block `blk` among `njobs`: consecutive block indices go to different XCDs (round robin),
 // so the jobs are dealt out in eight contiguous ranges, one per XCD, and neighbouring jobs (the
 // rows of one head, the heads of one kv group) share one XCD's L2.
