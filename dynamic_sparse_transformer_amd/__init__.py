@@ -60,7 +60,7 @@ class WorkspaceView(ctypes.Structure):
     _fields_ = [("queries", ctypes.c_int64), ("lists", ctypes.c_int64), ("slots", ctypes.c_int64),
                 ("count_offset", ctypes.c_size_t), ("entry_offset", ctypes.c_size_t),
                 ("eps_offset", ctypes.c_size_t), ("path_offset", ctypes.c_size_t),
-                ("path_stride", ctypes.c_size_t), ("eps_coef", ctypes.c_float), ("reserved", ctypes.c_int32)]
+                ("path_stride", ctypes.c_size_t), ("eps_coef", ctypes.c_float), ("count_split", ctypes.c_int32)]
 
 
 class TopoError(RuntimeError):

@@ -397,6 +397,7 @@ int topo_workspace_view(const topo_params_t* p, int op, topo_ws_view_t* view) {
     v.path_offset = pv.path;
     v.path_stride = sizeof(int32_t);
     v.eps_coef = topo::prefill_eps_coef();
+    v.count_split = 1;
   } else if (op == TOPO_OP_DECODE || op == TOPO_OP_SELECT || op == TOPO_OP_DECODE_CERTIFIED ||
              op == TOPO_OP_DECODE_RAGGED) {
     if (p->n_q != 1) return TOPO_EINVAL;

@@ -26,7 +26,6 @@ namespace topo {
 constexpr int PF_ROWS = 128;         // query rows per scan block (8 waves: 4 row groups x 2 key halves)
 constexpr int PF_KEYS = 64;          // keys per scan step
 constexpr int PF_MAX_K = 96;         // largest k the MFMA scan ranks
-constexpr uint32_t PF_OVERFLOW = 0xFFFFFFFFu;
 
 // Error bound of the MFMA float32 scores: products of bf16 values are exact in float32, and a
 // float32 sum of d <= 128 terms in any order and grouping is off by less than d 2^-24
@@ -48,7 +47,8 @@ static int64_t pf_slot(int32_t k) { return k + 48 < PF_LCAP_MAX ? k + 48 : PF_LC
 struct PfWs {
   float* qn;        // [B*Hq*n_q]: |q| of every query row (rounded up)
   float* kn;        // [B*Hkv][n]: |k| of every key (rounded up)
-  uint32_t* cnt;    // [B*Hq*n_q]: entries of the row's list (or PF_OVERFLOW)
+  uint32_t* cnt;    // [B*Hq*n_q]: entries of the row's list, from the front of its slots (low 16 bits)
+                    // and from the back (high 16 bits); more than the slots hold = overflow
   int32_t* path;    // [B*Hq*n_q]: how the finish chose the row's top-k part (PATH_*)
   uint2* surv;      // [B*Hq*n_q][list]: (float bits of the matrix-core score, key position)
   float* win_o;     // [B*Hq*n_q][d]: sum over the row's window of exp(z - m_w) v (bf16 inputs)
@@ -179,11 +179,12 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 // supplies row / key (l % 32) and elements 8*(l/32) .. +8 of each 16-deep slice, and holds output
 // (row 8*(r/4) + 4*(l/32) + r%4, key l % 32) in register r.
 // Every score has its own error bound eps = cq_row |k_j|, cq_row = 2^-14 |q_row| (the key norms
-// travel with the key tiles). Phase 1 keeps, per lane and row, the two largest lower bounds
-// (score - eps) it has seen. Those 128 values per row belong to distinct candidate keys, so any T
-// that k of them reach is a lower bound of the row's k-th largest exact score. Phase 2 scores the
-// keys again and appends every key whose upper bound (score + eps) reaches T to the row's list
-// in global memory; the finish ranks the lists.
+// travel with the key tiles). Phase 1 keeps, per lane and row, the two largest fast scores it has
+// seen, and the block's largest key norm. Those 128 values per row belong to distinct candidate
+// keys, so if k of them reach x, k keys score at least x - cq_row max|k| exactly: T = x -
+// cq_row max|k| is a lower bound of the row's k-th largest exact score. Phase 2 scores the keys
+// again and appends every key whose upper bound (score + its own eps) reaches T to the row's
+// list in global memory; the finish ranks the lists.
 
 template <int D>
 __global__ __launch_bounds__(512) void pf_scan_kernel(PfArgs a) {
@@ -198,8 +199,8 @@ __global__ __launch_bounds__(512) void pf_scan_kernel(PfArgs a) {
   __shared__ __align__(16) unsigned char ktiles[2 * TILE_BYTES];
   __shared__ float knt[2][PF_KEYS];   // norms of the keys of the two tiles in LDS
   __shared__ __align__(16) unsigned char lists[PF_LIST_BYTES];
-  __shared__ uint32_t lcnt[PF_ROWS];  // keys appended to each row's list
   __shared__ float lthf[PF_ROWS];
+  __shared__ uint32_t kmax_blk;  // float bits of the largest key norm the block has scored
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   // Job of this block (the blocks of one head on one XCD). Within a head the row blocks run from
@@ -212,9 +213,6 @@ __global__ __launch_bounds__(512) void pf_scan_kernel(PfArgs a) {
   const unsigned char* kb = a.k + ((size_t)b * a.Hkv + g) * (size_t)a.n * RB;
   const float* knb = a.w.kn + ((size_t)b * a.Hkv + g) * (size_t)a.n;
   const uint32_t LCAP = (uint32_t)a.slot;
-  // phase 2 stages each wave's 16 scores per lane here (where the top-2 values were): chunk q
-  // (registers 4q..4q+3) of lane l at float4 index q * 64 + l of the wave's 4 KB
-  float4* sst = (float4*)lists + wave * 256;
   const size_t grow0 = (size_t)bh * a.n_q + i0;  // global row of block row 0
   const int n = (int)a.n;  // the host runs this scan only when n * RB < 2^31
 
@@ -364,16 +362,17 @@ __global__ __launch_bounds__(512) void pf_scan_kernel(PfArgs a) {
   float m1[16], m2[16];
 #pragma unroll
   for (int r = 0; r < 16; ++r) m1[r] = m2[r] = -INFINITY;
+  float knmx = 0.f;  // the largest norm of the keys this lane has scored
+  if (tid == 0) kmax_blk = 0u;
 // (The empty asm statements pin each result to its place between the matrix instructions;
 // without them the compiler sinks the work of a step past the next step's boundary-tile branch.)
 #define PF_PART1(ACC, r)                                                                           \
   {                                                                                                \
-    const float lb_ = fmaf(-cq[r], knc_, ACC[r]);                                                  \
-    m2[r] = __builtin_amdgcn_fmed3f(m1[r], m2[r], lb_);                                            \
-    m1[r] = __builtin_amdgcn_fmed3f(m1[r], lb_, pinf);                                             \
+    m2[r] = __builtin_amdgcn_fmed3f(m1[r], m2[r], ACC[r]);                                         \
+    m1[r] = __builtin_amdgcn_fmed3f(m1[r], ACC[r], pinf);                                          \
     asm volatile("" : "+v"(m1[r]), "+v"(m2[r]));                                                   \
   }
-#define PF_POST1(ACC, t)
+#define PF_POST1(ACC, t) knmx = fmaxf(knmx, knc_);
   if (ntiles > 0) {
     PF_PROLOGUE(accA)
     for (int t = 0; t < ntiles; t += 2) {
@@ -382,14 +381,18 @@ __global__ __launch_bounds__(512) void pf_scan_kernel(PfArgs a) {
     }
   }
 
-  // ---- thresholds: row R's 128 lower bounds sit at tops[R][64 * kq + 2 * m + {0, 1}] (even
+  // the block's largest key norm (norms are non-negative, so their bits order like the values)
+  knmx = wave_max_f32(knmx);
+  if (lane == 0) atomicMax(&kmax_blk, __float_as_uint(knmx));
+
+  // ---- thresholds: row R's 128 fast scores sit at tops[R][64 * kq + 2 * m + {0, 1}] (even
   // entries: the lanes' best values, 64 distinct keys; odd entries: their second best). Each row
-  // needs a lower bound T of the k-th largest of its 128 values such that few values lie between: the
+  // needs a lower bound x of the k-th largest of its 128 values such that few values lie between: the
   // largest T = lo + c (hi - lo) / 1024, c = 0..1023, that at least k values reach (a bitwise
   // search over c, monotone in c), where hi is the largest value and lo a known lower bound of the
   // k-th largest: for k <= 64 and 64 finite best values the smallest of them, else the smallest
   // finite value (if fewer than k values are finite every candidate stays). The bound is at most
-  // (hi - lo) / 1024 below the k-th largest, and it is never above it. A wave takes 16 rows in
+  // (hi - lo) / 1024 below the k-th largest, and it is never above it; T = x - cq_row max|k|. A wave takes 16 rows in
   // four groups of four; the 16 lanes of a row hold 8 values each, counted lane by lane and
   // summed over the row with DPP moves.
   float* tops = (float*)lists;
@@ -399,7 +402,14 @@ __global__ __launch_bounds__(512) void pf_scan_kernel(PfArgs a) {
     *(float2*)&tops[row * 128 + 64 * kq + 2 * m] = make_float2(m1[r], m2[r]);
   }
   const int sub = lane & 15;
+  float qn_g[4];
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    const int64_t i = i0 + wave * 16 + 4 * g + (lane >> 4);
+    qn_g[g] = i < a.n_q ? a.w.qn[(size_t)bh * a.n_q + i] : 0.f;
+  }
   __syncthreads();
+  const float kmax = __uint_as_float(kmax_blk);
   {
     float v[4][8], lo[4], step[4];
     int c[4];
@@ -451,13 +461,12 @@ __global__ __launch_bounds__(512) void pf_scan_kernel(PfArgs a) {
     for (int g = 0; g < 4; ++g) {
       const int row = wave * 16 + 4 * g + (lane >> 4);
       if (sub == 0) {
-        const float x = ok[g] ? fmaf((float)c[g], step[g], lo[g]) : -INFINITY;
+        const float x = ok[g] ? fmaf((float)c[g], step[g], lo[g]) - PF_EPS_COEF * qn_g[g] * kmax : -INFINITY;
         // kept finite (at least the lowest float), so that the -inf of a masked score never passes
         lthf[row] = fmaxf(x, -0x1.fffffep+127f);
       }
     }
   }
-  if (tid < PF_ROWS) lcnt[tid] = 0u;
   __syncthreads();
   float thf[16];
 #pragma unroll
@@ -467,11 +476,24 @@ __global__ __launch_bounds__(512) void pf_scan_kernel(PfArgs a) {
   // list in global memory, with its score. A lane first gathers the test results of its 16
   // registers into bit r of `fail`'s complement: the test x + eps >= T is the sign of
   // (x + eps) - T (T finite, x finite or -inf), shifted in by v_alignbit from register 15 down
-  // to 0; its 16 scores go to
-  // the wave's LDS stage. Then the lane takes its set bits one at a time: a slot from the row's LDS counter, (score read back from the stage, key
-  // position) into the slot. The lanes of a wave pass through that loop together as often as the
-  // busiest lane needs (a step has about one passing register per four lanes). Slots past the end
-  // are clamped onto the last one; a row whose count ends above LCAP takes the exact path.
+  // to 0. The appends of a step are then batched per wave: a lane with passing registers stores
+  // its 16 scores to the wave's score stage, a prefix sum over the lanes gives it room in the
+  // wave's entry stage for one code (lane, register) per passing key, and the wave takes the
+  // codes 64 at a time, one per lane: the row's slot from the wave's own counter of that row (an
+  // LDS atomic on a counter no other wave touches), the score from the stage, the store. A
+  // row's keys of a step are the 32 lanes of one half of the two waves that share its row tile
+  // (kq = 0, 1): the wave with kq = 0 fills the row's slots from the front, the one with kq = 1
+  // from the back, so no slot is shared; slots are clamped into the row's area, and a row whose
+  // two counts add up to more than LCAP takes the exact path. The stages and counters reuse the
+  // LDS of the thresholds' values (4 KB of scores, 1024 codes and 32 counters per wave).
+  float* const sst_w = (float*)lists + wave * 1024;
+  uint16_t* const stg_w = (uint16_t*)(lists + 32768) + wave * 1024;
+  uint32_t* const cnt_w = (uint32_t*)(lists + 49152) + wave * 32;
+  static_assert(49152 + 8 * 32 * 4 <= PF_LIST_BYTES, "phase 2 stages fit the thresholds' LDS");
+  if (lane < 32) cnt_w[lane] = 0u;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   uint32_t fail = 0u;
 #define PF_PART2(ACC, i)                                                                           \
   {                                                                                                \
@@ -482,16 +504,36 @@ __global__ __launch_bounds__(512) void pf_scan_kernel(PfArgs a) {
 #define PF_POST2(ACC, t)                                                                           \
   {                                                                                                \
     uint32_t bits = ~fail & 0xFFFFu;                                                               \
-    _Pragma("unroll") for (int q4 = 0; q4 < 4; ++q4)                                               \
-      sst[q4 * 64 + lane] = make_float4(ACC[4 * q4], ACC[4 * q4 + 1], ACC[4 * q4 + 2], ACC[4 * q4 + 3]); \
-    const uint32_t jj = (uint32_t)((t) * PF_KEYS + kq * 32 + m);                                   \
-    while (bits) {                                                                                 \
-      const int r = __builtin_ctz(bits);                                                           \
-      bits &= bits - 1u;                                                                           \
-      const int row = row_base + r + (r & 12); /* row_base + 8 * (r / 4) + r % 4 */               \
-      const uint32_t sl = min(atomicAdd(&lcnt[row], 1u), LCAP - 1u);                               \
-      const float x = ((const float*)sst)[((r >> 2) * 64 + lane) * 4 + (r & 3)];                   \
-      a.w.surv[(grow0 + row) * LCAP + sl] = make_uint2(__float_as_uint(x), jj);                    \
+    const int np = __popc(bits);                                                                   \
+    if (__ballot(np != 0)) {                                                                       \
+      _Pragma("unroll") for (int q4 = 0; q4 < 4; ++q4)                                             \
+        ((float4*)sst_w)[q4 * 64 + lane] = make_float4(ACC[4 * q4], ACC[4 * q4 + 1], ACC[4 * q4 + 2], ACC[4 * q4 + 3]); \
+      const int incl_ = wave_incl_scan_i32(np);                                                    \
+      const int total_ = __shfl(incl_, 63);                                                        \
+      int at_ = incl_ - np;                                                                        \
+      while (bits) {                                                                               \
+        const int r_ = __builtin_ctz(bits);                                                        \
+        bits &= bits - 1u;                                                                         \
+        stg_w[at_++] = (uint16_t)((lane << 4) | r_);                                               \
+      }                                                                                            \
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");                                       \
+      __builtin_amdgcn_wave_barrier();                                                             \
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");                                       \
+      for (int e0_ = 0; e0_ < total_; e0_ += 64) {                                                 \
+        if (e0_ + lane < total_) {                                                                 \
+          const uint32_t code_ = stg_w[e0_ + lane];                                                \
+          const int r_ = (int)(code_ & 15u), src_ = (int)(code_ >> 4), hs_ = src_ >> 5;            \
+          const uint32_t sl_ = min(atomicAdd(&cnt_w[16 * hs_ + r_], 1u), LCAP - 1u);              \
+          const int row_ = rq * 32 + 4 * hs_ + 8 * (r_ >> 2) + (r_ & 3);                           \
+          const float x_ = sst_w[((r_ >> 2) * 64 + src_) * 4 + (r_ & 3)];                          \
+          const uint32_t key_ = (uint32_t)((t) * PF_KEYS + kq * 32 + (src_ & 31));                 \
+          a.w.surv[(grow0 + row_) * LCAP + (kq == 0 ? sl_ : LCAP - 1u - sl_)] =                   \
+              make_uint2(__float_as_uint(x_), key_);                                               \
+        }                                                                                          \
+      }                                                                                            \
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");                                       \
+      __builtin_amdgcn_wave_barrier();                                                             \
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");                                       \
     }                                                                                              \
   }
   if (ntiles > 0) {
@@ -502,10 +544,12 @@ __global__ __launch_bounds__(512) void pf_scan_kernel(PfArgs a) {
     }
   }
 
-  // the counts of the lists (or the overflow mark)
-  if (tid < PF_ROWS && i0 + tid < a.n_q) {
-    const uint32_t c = lcnt[tid];
-    a.w.cnt[grow0 + tid] = c > LCAP ? PF_OVERFLOW : c;
+  // the counts of the lists: the wave's counter of (half h, register r), written to the low
+  // (kq = 0, front) or high (kq = 1, back) half of the row's count word
+  if (lane < 32) {
+    const int hs = lane >> 4, r = lane & 15;
+    const int row = rq * 32 + 4 * hs + 8 * (r >> 2) + (r & 3);
+    if (i0 + row < a.n_q) ((uint16_t*)(a.w.cnt + grow0 + row))[kq] = (uint16_t)min(cnt_w[lane], 0xFFFFu);
   }
 #undef PF_INTERIOR
 #undef PF_LOAD
@@ -905,30 +949,39 @@ __device__ void pf_row(const PfArgs& a, PfRowSmem* sm, size_t grow) {
   bool exact = false;
   int32_t path = PATH_NONE;
   if (a.topk > 0) {
-    // The count and the row's whole slot area (at most 128 entries, two per lane) are read
-    // together, so that the list costs one memory round trip; slots at or past the count hold
-    // stale entries and are ignored.
-    uint32_t cr = PF_OVERFLOW;
+    // The count word and the row's whole slot area (at most 128 entries, two per lane) are read
+    // together, so that the list costs one memory round trip. The scan filled c_f slots from the
+    // front and c_b from the back; the slots between hold stale entries and are ignored.
+    uint32_t cf = 0xFFFFu, cb = 0xFFFFu;
     uint2 e0 = make_uint2(0u, 0u), e1 = e0;
+    const int L = (int)a.slot;
     if (!a.exact_all) {
       const uint2* sv = a.w.surv + grow * (size_t)a.slot;
-      cr = a.w.cnt[grow];
-      if (lane < a.slot) e0 = sv[lane];
-      if (lane + 64 < a.slot) e1 = sv[lane + 64];
+      const uint32_t cr = a.w.cnt[grow];
+      cf = cr & 0xFFFFu;
+      cb = cr >> 16;
+      if (lane < L) e0 = sv[lane];
+      if (lane + 64 < L) e1 = sv[lane + 64];
     }
-    exact = cr == PF_OVERFLOW;
+    exact = cf + cb > (uint32_t)L;
     if (exact) path = a.exact_all ? PATH_EXACT_ASKED : PATH_EXACT_OVERFLOW;
     if (!exact) {
-      c = (int)cr;
-      // positions come from the scan and are always keys of the cache; clamping only guards
-      // the reads below. With bf16 inputs the scan's matrix-core scores come along.
-      if (lane < c) {
-        sm->ridx[lane] = (int32_t)min(e0.y, (uint32_t)(a.n - 1));
-        if constexpr (BF16) sm->rs[lane] = (double)__uint_as_float(e0.x);
+      // the entries, packed: positions come from the scan and are always keys of the cache
+      // (clamping only guards the reads below); with bf16 inputs the scan's matrix-core scores
+      // come along
+      const bool v0 = lane < L && (lane < (int)cf || lane >= L - (int)cb);
+      const bool v1 = lane + 64 < L && (lane + 64 < (int)cf || lane + 64 >= L - (int)cb);
+      const uint64_t b0 = __ballot(v0), b1 = __ballot(v1);
+      c = (int)(cf + cb);
+      if (v0) {
+        const int at = lanes_below(b0);
+        sm->ridx[at] = (int32_t)min(e0.y, (uint32_t)(a.n - 1));
+        if constexpr (BF16) sm->rs[at] = (double)__uint_as_float(e0.x);
       }
-      if (lane + 64 < c) {
-        sm->ridx[lane + 64] = (int32_t)min(e1.y, (uint32_t)(a.n - 1));
-        if constexpr (BF16) sm->rs[lane + 64] = (double)__uint_as_float(e1.x);
+      if (v1) {
+        const int at = __popcll(b0) + lanes_below(b1);
+        sm->ridx[at] = (int32_t)min(e1.y, (uint32_t)(a.n - 1));
+        if constexpr (BF16) sm->rs[at] = (double)__uint_as_float(e1.x);
       }
     }
   }

@@ -307,15 +307,17 @@ typedef struct {
     int64_t queries;       /* query rows described: B*Hq (decode ops) or B*Hq*n_q (prefill)      */
     int64_t lists;         /* candidate lists per query row                                      */
     int64_t slots;         /* entries per list                                                   */
-    size_t  count_offset;  /* uint32 [queries][lists]: entries of each list; 0xFFFFFFFF if the
-                              list overflowed                                                    */
+    size_t  count_offset;  /* uint32 [queries][lists]: entries of each list (count_split = 0:
+                              the count, 0xFFFFFFFF if the list overflowed; count_split = 1: the
+                              low 16 bits count entries from the front of the slots, the high 16
+                              bits entries from the back, overflowed if their sum exceeds slots)  */
     size_t  entry_offset;  /* [queries][lists][slots] pairs {float fast score, int32 position}   */
     size_t  eps_offset;    /* float [queries][lists][slots]: the bound the kernels used for each
                               entry (decode); 0 when not stored (prefill: eps_coef |q| |k|)      */
     size_t  path_offset;   /* int32 TOPO_PATH_* of query i at path_offset + i * path_stride       */
     size_t  path_stride;
     float   eps_coef;      /* every fast score obeys |s_fast - s| <= eps_coef * |q|_2 * |k|_2    */
-    int32_t reserved;
+    int32_t count_split;   /* 0: decode lists; 1: prefill lists (see count_offset)              */
 } topo_ws_view_t;
 
 /* Fills *view for op TOPO_OP_DECODE, TOPO_OP_SELECT, TOPO_OP_DECODE_CERTIFIED,

@@ -105,6 +105,7 @@ class ListsView:
         def take(off, count, dt):
             return np.frombuffer(raw, dtype=dt, count=count, offset=int(off)).copy()
 
+        self.split = int(view.count_split)
         if L > 0:
             self.count = take(view.count_offset, Q * L, np.uint32).reshape(Q, L)
             ent = take(view.entry_offset, Q * L * S * 2, np.uint32).reshape(Q, L, S, 2)
@@ -121,9 +122,16 @@ class ListsView:
         if self.L == 0:
             return np.zeros(0, np.int64), np.zeros(0, np.float32), None
         c = self.count[qi]
-        if np.any(c == LIST_OVERFLOW):
-            return None
-        sel = np.arange(self.S)[None, :] < c[:, None]
+        slot = np.arange(self.S)[None, :]
+        if self.split:
+            front, back = (c & 0xFFFF).astype(np.int64), (c >> 16).astype(np.int64)
+            if np.any(front + back > self.S):
+                return None
+            sel = (slot < front[:, None]) | (slot >= self.S - back[:, None])
+        else:
+            if np.any(c == LIST_OVERFLOW):
+                return None
+            sel = slot < c[:, None]
         eps = self.eps[qi][sel] if self.eps is not None else None
         return self.pos[qi][sel].astype(np.int64), self.score[qi][sel], eps
 
