@@ -47,6 +47,7 @@ def log(*a):
 KERNEL_SOURCES = {
     "kscan": ("topo_decode.hip", "topo_device.h", "topo_internal.h"),
     "pf_scan": ("topo_prefill.hip", "topo_device.h", "topo_internal.h"),
+    "dense_stream": ("topo_dense.hip", "topo_device.h", "topo_internal.h"),
 }
 
 
@@ -228,6 +229,7 @@ def run_decode_bench(cfg: int, steps: int, warmup: int, w=None, extras: bool = T
     dense = {"ms_per_step": dense_ms, "value": s.B * s.Hq / (dense_ms / 1e3), "unit": "queries/s",
              "kv_bytes": dense_bytes, "achieved_gbs": dense_bytes / (dense_ms / 1e3) / 1e9,
              "frac": dense_bytes / (dense_ms / 1e3) / 1e9 / HBM_PEAK_GBS,
+             "traffic": measured_traffic("dense_stream", s.name),
              "note": "whole call (dense_stream_kernel + dense_combine_kernel), wall clock"}
     del dws, od
 

@@ -455,11 +455,16 @@ __global__ __launch_bounds__(256, 1) void dense_stream_kernel(DenseArgs a) {
   }
 }
 
-// One wave per (batch, query head, query): merge the chunk partials.
+// One wave per (batch, query head, query): merge the chunk partials. Lane c takes the maximum and
+// sum of partials c, c + 64, ...; the wave reduces them and every lane keeps the weight
+// exp(m_c - m) of its partials in LDS; then each lane sums its D / 64 output elements over all
+// partials, eight partials' loads in flight at a time.
 template <int D>
 __global__ __launch_bounds__(64) void dense_combine_kernel(const void* partv, float* out, int64_t chunks, int64_t kpb,
                                                            int64_t n_q, int64_t q_pos0, int64_t n, int causal,
                                                            const float* gate, float gate_min) {
+  constexpr int MAXP = 1024;  // partials merged per pass through the LDS weights
+  __shared__ double fw[MAXP];
   const size_t row = blockIdx.x;  // (b*Hq + h)*n_q + qi
   if (gate && !(gate[row] >= gate_min)) return;
   const int64_t qi = (int64_t)(row % (size_t)n_q);
@@ -469,17 +474,38 @@ __global__ __launch_bounds__(64) void dense_combine_kernel(const void* partv, fl
   const DensePartial<D>* part = (const DensePartial<D>*)partv + row * (size_t)chunks;
   const int lane = threadIdx.x;
   double m = -INFINITY;
-  for (int64_t c = 0; c < used; ++c) m = fmax(m, part[c].m);
+  for (int64_t c = lane; c < used; c += 64) m = fmax(m, part[c].m);
+  m = wave_max_f64(m);
   constexpr int CPL = D / 64;
   double nv[CPL] = {};
   double z = 0.0;
-  for (int64_t c = 0; c < used; ++c) {
-    if (part[c].m == -INFINITY) continue;
-    const double f = exp(part[c].m - m);
-    z += f * part[c].z;
+  for (int64_t c0 = 0; c0 < used; c0 += MAXP) {
+    const int cnt = (int)min((int64_t)MAXP, used - c0);
+    for (int i = lane; i < cnt; i += 64) {
+      const double mc = part[c0 + i].m;
+      const double f = mc == -INFINITY ? 0.0 : exp(mc - m);
+      fw[i] = f;
+      z += f * part[c0 + i].z;
+    }
+    __syncthreads();
+    int i = 0;
+    for (; i + 8 <= cnt; i += 8) {
+      double x[8][CPL];
 #pragma unroll
-    for (int e = 0; e < CPL; ++e) nv[e] += f * part[c].nv[lane * CPL + e];
+      for (int u = 0; u < 8; ++u)
+#pragma unroll
+        for (int e = 0; e < CPL; ++e) x[u][e] = part[c0 + i + u].nv[lane * CPL + e];
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+#pragma unroll
+        for (int e = 0; e < CPL; ++e) nv[e] += fw[i + u] * x[u][e];
+    }
+    for (; i < cnt; ++i)
+#pragma unroll
+      for (int e = 0; e < CPL; ++e) nv[e] += fw[i] * part[c0 + i].nv[lane * CPL + e];
+    __syncthreads();
   }
+  z = wave_sum_f64(z);
 #pragma unroll
   for (int e = 0; e < CPL; ++e) out[row * D + lane * CPL + e] = (float)(nv[e] / z);
 }
