@@ -9,7 +9,7 @@
 //
 // Launches:
 //   pf_norms   |q| of every query row and |k| of every key (each score's own error bound).
-//   pf_scan    bf16 MFMA tiles, 128 query rows x 64 keys per step (8 waves, one 32x32x16 tile
+//   pf_scan    bf16 MFMA tiles, 128 query rows x 64 keys per step (8 waves, four 16x16x32 tiles
 //              each), float32 scores, two passes over the keys: the first bounds each row's k-th
 //              best score from below, the second lists every key that may still reach it.
 //   pf_window  matrix-core softmax share of every row's window (max, sum, weighted V).
@@ -23,7 +23,7 @@
 
 namespace topo {
 
-constexpr int PF_ROWS = 128;         // query rows per scan block (8 waves: 4 row groups x 2 key halves)
+constexpr int PF_ROWS = 128;         // query rows per scan block (8 waves: 2 row groups x 4 key quarters)
 constexpr int PF_KEYS = 64;          // keys per scan step
 constexpr int PF_MAX_K = 96;         // largest k the MFMA scan ranks
 
@@ -37,9 +37,8 @@ constexpr float PF_EPS_COEF = 0x1p-14f;
 float prefill_eps_coef() { return PF_EPS_COEF; }
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
-// LDS of the scan for the top-2 values of each row's lanes (phase 1), then for the waves' score
-// stages (phase 2). A row's list of possible top-k keys holds k + 48 entries, at most 128 (the
-// finish ranks two per lane).
+// LDS of the scan for the top-2 values of each row's lanes between the two phases. A row's list
+// of possible top-k keys holds k + 48 entries, at most 128 (the finish ranks two per lane).
 constexpr int PF_LIST_BYTES = PF_ROWS * 128 * 4;
 constexpr int PF_LCAP_MAX = 128;
 static int64_t pf_slot(int32_t k) { return k + 48 < PF_LCAP_MAX ? k + 48 : PF_LCAP_MAX; }
@@ -48,7 +47,8 @@ struct PfWs {
   float* qn;        // [B*Hq*n_q]: |q| of every query row (rounded up)
   float* kn;        // [B*Hkv][n]: |k| of every key (rounded up)
   uint32_t* cnt;    // [B*Hq*n_q]: entries of the row's list, from the front of its slots (low 16 bits)
-                    // and from the back (high 16 bits); more than the slots hold = overflow
+                    // and from the back (high 16 bits, 0 from this scan); more than the slots
+                    // hold = overflow
   int32_t* path;    // [B*Hq*n_q]: how the finish chose the row's top-k part (PATH_*)
   uint2* surv;      // [B*Hq*n_q][list]: (float bits of the matrix-core score, key position)
   float* win_o;     // [B*Hq*n_q][d]: sum over the row's window of exp(z - m_w) v (bf16 inputs)
@@ -171,38 +171,53 @@ __device__ __forceinline__ bool pf_is_cand(int64_t j, int64_t p, int64_t n, int3
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 // pf_scan: one block of 512 threads per (b, h, 128 consecutive query rows). Each step scores 64
-// keys held in LDS (padded rows, two buffers) while the loads of the key tile two steps ahead are
-// in flight and the tile one step ahead is written to the other buffer. Wave w computes the
-// 32x32 quadrant (rows 32*(w/2).., keys 32*(w%2)..) with v_mfma_f32_32x32x16_bf16: lane l
-// supplies row / key (l % 32) and elements 8*(l/32) .. +8 of each 16-deep slice, and holds output
-// (row 8*(r/4) + 4*(l/32) + r%4, key l % 32) in register r.
-// Every score has its own error bound eps = cq_row |k_j|, cq_row = 2^-14 |q_row| (the key norms
-// travel with the key tiles). Phase 1 keeps, per lane and row, the two largest fast scores it has
-// seen, and the block's largest key norm. Those 128 values per row belong to distinct candidate
-// keys, so if k of them reach x, k keys score at least x - cq_row max|k| exactly: T = x -
-// cq_row max|k| is a lower bound of the row's k-th largest exact score. Phase 2 scores the keys
-// again and appends every key whose upper bound (score + its own eps) reaches T to the row's
-// list in global memory; the finish ranks the lists.
+// keys held in LDS. Wave w = 4 rg + kg holds the 64 query rows 64 rg .. +64 as the A operands of
+// four 16-row tiles and scores them against keys 16 kg .. +16 of the tile with
+// v_mfma_f32_16x16x32_bf16 (one B operand read from LDS feeds four products). Lane l supplies row
+// / key l % 16 and elements 8 (l / 16) .. +8 of each 32-deep slice; a slice takes, for both
+// operands, the 8 consecutive dimensions starting at 32 (l / 16) + 8 s of each row, so that a
+// lane's operands are one contiguous run of each row (the pairing of dimensions is the same for
+// Q and K, so the sum over them is the dot product). Register e of row tile u holds the score of
+// row 16 u + 4 (l / 16) + e and key l % 16.
+// The key tiles rotate through 2 PF_H LDS buffers: tile t is written PF_H + 1 steps before the
+// step that reads it, so that the waves meet at a barrier only every PF_H steps. The loads of the
+// tile written at step t + 2 are in flight while step t runs.
+// Every score has its own error bound eps = 2^-14 |q| |k| (see PF_EPS_COEF). Phase 1 keeps, per
+// lane and row, the two largest fast scores it has seen, and the largest norm of the keys the
+// block stages. Those 128 values per row belong to distinct candidate keys, so if k of them reach
+// x, k keys score at least x - 2^-14 |q| max|k| exactly, and each of them has a fast score of at
+// least x - 2^-13 |q| max|k|: phase 2 scores the keys again and lists every key whose fast score
+// reaches T = x - 2^-13 |q| max|k| (computed with a spare far above float32 rounding) in its
+// row's list in global memory, with a slot from the row's LDS counter. The finish ranks the
+// lists.
+constexpr int PF_H = 2;              // steps between block barriers
+constexpr int PF_NBUF = 2 * PF_H;    // LDS key tile buffers
 
 template <int D>
 __global__ __launch_bounds__(512) void pf_scan_kernel(PfArgs a) {
   constexpr int RB = D * 2;
-  constexpr int STEPS = D / 16;
+  constexpr int SL = D / 32;              // 32-deep slices of a row
+  constexpr int GB = RB / 4;              // bytes of a row supplied by one lane (SL chunks of 16)
   constexpr int NCH = RB / 16;            // 16-byte chunks per key row
   constexpr int STRIDE = RB + 16;         // padded LDS row
   constexpr int RPP = 512 / NCH;          // key rows staged per load pass
   constexpr int PASSES = PF_KEYS / RPP;
   constexpr int TILE_BYTES = PF_KEYS * STRIDE;
+  constexpr int SMEM = PF_NBUF * TILE_BYTES > PF_LIST_BYTES ? PF_NBUF * TILE_BYTES : PF_LIST_BYTES;
+  constexpr int PER = 16 / (4 * SL);      // score registers handled after each matrix instruction
   static_assert(PASSES >= 1 && PASSES <= 2, "staging passes");
-  __shared__ __align__(16) unsigned char ktiles[2 * TILE_BYTES];
-  __shared__ float knt[2][PF_KEYS];   // norms of the keys of the two tiles in LDS
-  __shared__ __align__(16) unsigned char lists[PF_LIST_BYTES];
-  __shared__ float lthf[PF_ROWS];
-  __shared__ uint32_t kmax_blk;  // float bits of the largest key norm the block has scored
+  __shared__ __align__(16) unsigned char ktiles[SMEM];  // key tiles; the thresholds' values between the phases
+  __shared__ __align__(16) float sstage[8 * 64 * 16];    // phase 2: each lane's 16 scores of a step
+  __shared__ float lthk[PF_ROWS];
+  __shared__ uint32_t rowcnt[PF_ROWS];
+  __shared__ uint32_t kmax_blk;  // float bits of the largest key norm the block has staged
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  // (the wave index through readfirstlane, so that the compiler keeps what derives from it in
+  // scalar registers)
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   // Job of this block (the blocks of one head on one XCD). Within a head the row blocks run from
   // the last (most keys under a causal mask) to the first, so the long jobs start first.
   const int64_t nrb = (a.n_q + PF_ROWS - 1) / PF_ROWS;
@@ -216,25 +231,28 @@ __global__ __launch_bounds__(512) void pf_scan_kernel(PfArgs a) {
   const size_t grow0 = (size_t)bh * a.n_q + i0;  // global row of block row 0
   const int n = (int)a.n;  // the host runs this scan only when n * RB < 2^31
 
-  const int rq = wave >> 1, kq = wave & 1;
-  const int m = lane & 31, half = lane >> 5;
-  bf16x8_t qa[STEPS];
-  {
-    const int64_t i = i0 + rq * 32 + m;
-    const unsigned char* qrow = a.q + ((size_t)bh * a.n_q + (i < a.n_q ? i : 0)) * RB;
+  const int rg = wave >> 2, kg = wave & 3;
+  const int m = lane & 15, grp = lane >> 4;
+  bf16x8_t qa[4][SL];
 #pragma unroll
-    for (int st = 0; st < STEPS; ++st) {
-      const uint4 w = i < a.n_q ? *(const uint4*)(qrow + st * 32 + half * 16) : make_uint4(0u, 0u, 0u, 0u);
-      qa[st] = __builtin_bit_cast(bf16x8_t, w);
+  for (int u = 0; u < 4; ++u) {
+    const int64_t i = i0 + rg * 64 + u * 16 + m;
+    const unsigned char* qrow = a.q + ((size_t)bh * a.n_q + (i < a.n_q ? i : 0)) * RB + grp * GB;
+#pragma unroll
+    for (int s = 0; s < SL; ++s) {
+      const uint4 w = i < a.n_q ? *(const uint4*)(qrow + s * 16) : make_uint4(0u, 0u, 0u, 0u);
+      qa[u][s] = __builtin_bit_cast(bf16x8_t, w);
     }
   }
-  const int row_base = rq * 32 + 4 * half;  // block row of register r: row_base + 8*(r/4) + r%4
-  // the error-bound factor of the row of each register: 2^-14 |q_row| (0 for rows past the end)
-  float cq[16];
+  const int row_base = rg * 64 + 4 * grp;  // block row of register (u, e): row_base + 16 u + e
+  if (tid < PF_ROWS) rowcnt[tid] = 0u;
+  if (tid == 0) kmax_blk = 0u;
+  // |q| of the rows whose threshold this lane helps to find (wave w takes rows 16 w .. +16)
+  float qn_g[4];
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int64_t i = i0 + row_base + 8 * (r / 4) + (r % 4);
-    cq[r] = i < a.n_q ? PF_EPS_COEF * a.w.qn[(size_t)bh * a.n_q + i] : 0.f;
+  for (int gq = 0; gq < 4; ++gq) {
+    const int64_t i = i0 + wave * 16 + 4 * gq + (lane >> 4);
+    qn_g[gq] = i < a.n_q ? a.w.qn[(size_t)bh * a.n_q + i] : 0.f;
   }
 
   const int64_t i_last = min(i0 + PF_ROWS, a.n_q) - 1;
@@ -251,163 +269,164 @@ __global__ __launch_bounds__(512) void pf_scan_kernel(PfArgs a) {
 #define PF_INTERIOR(t) ((t) >= 1 && ((t) <= t_a || ((t) >= t_b && (t) <= t_c)))
 
   // Staging of key tiles: thread tid copies 16-byte chunk (tid % NCH) of key rows
-  // u * PF_KEYS + tid / NCH (+ RPP), and the norms of those rows. Raw buffer loads whose range
-  // ends at the cache's last key: rows past the end read as zero, so every load is issued
-  // unconditionally and no address is clamped (the norm index is clamped; rows past the end are
-  // never candidates). Register set (u & 1) holds tile u from its load until its store two steps
-  // later.
+  // u * PF_KEYS + tid / NCH (+ RPP). Raw buffer loads whose range ends at the cache's last key:
+  // rows past the end read as zero, so every load is issued unconditionally and no address is
+  // clamped. In phase 1 the thread with chunk 0 of a row also loads that key's norm (index
+  // clamped; keys past the range the block scores only make the largest norm larger). Register
+  // set (t & 1) holds the tile that step t writes to LDS.
   const int srow = tid / NCH, schunk = tid % NCH;
   const int voff0 = srow * RB + schunk * 16, voff1 = voff0 + RPP * RB;
   uint4 r00 = make_uint4(0u, 0u, 0u, 0u), r01 = r00, r10 = r00, r11 = r00;
   float n00 = 0.f, n01 = 0.f, n10 = 0.f, n11 = 0.f;
-#define PF_LOAD(DST0, DST1, N0, N1, U)                                                             \
+  float knmx = 0.f;  // the largest key norm this thread has staged
+#define PF_LOAD(DST0, DST1, N0, N1, U, NORM)                                                       \
   {                                                                                                \
     const int kt_ = min((U) * PF_KEYS, n);                                                         \
     const __amdgpu_buffer_rsrc_t rs_ =                                                             \
         __builtin_amdgcn_make_buffer_rsrc((void*)(kb + (size_t)kt_ * RB), (short)0, (n - kt_) * RB, 0x00020000); \
     DST0 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs_, voff0, 0, 0));    \
-    N0 = knb[min((U) * PF_KEYS + srow, n - 1)];                                                    \
+    if (NORM) N0 = knb[min((U) * PF_KEYS + srow, n - 1)];                                          \
     if (PASSES > 1) {                                                                              \
       DST1 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs_, voff1, 0, 0));  \
-      N1 = knb[min((U) * PF_KEYS + srow + RPP, n - 1)];                                            \
+      if (NORM) N1 = knb[min((U) * PF_KEYS + srow + RPP, n - 1)];                                  \
     }                                                                                              \
   }
-#define PF_STORE(SRC0, SRC1, N0, N1, U)                                                            \
+#define PF_STORE(SRC0, SRC1, N0, N1, U, NORM)                                                      \
   {                                                                                                \
-    unsigned char* dst = &ktiles[((U) & 1) * TILE_BYTES + srow * STRIDE + schunk * 16];            \
+    unsigned char* dst = &ktiles[((U) % PF_NBUF) * TILE_BYTES + srow * STRIDE + schunk * 16];      \
     *(uint4*)dst = SRC0;                                                                           \
     if (PASSES > 1) *(uint4*)(dst + RPP * STRIDE) = SRC1;                                          \
-    if (schunk == 0) {                                                                             \
-      knt[(U) & 1][srow] = N0;                                                                     \
-      if (PASSES > 1) knt[(U) & 1][srow + RPP] = N1;                                               \
-    }                                                                                              \
+    if (NORM) knmx = fmaxf(knmx, PASSES > 1 ? fmaxf(N0, N1) : N0);                                 \
   }
-// Prologue of a pass over the tiles: tiles 0 and 1 to LDS, tiles 2 and 3 in flight, scores of
-// tile 0 into ACC.
-#define PF_PROLOGUE(ACC)                                                                           \
-  PF_LOAD(r00, r01, n00, n01, 0)                                                                   \
-  PF_LOAD(r10, r11, n10, n11, 1)                                                                   \
-  PF_STORE(r00, r01, n00, n01, 0)                                                                  \
-  PF_STORE(r10, r11, n10, n11, 1)                                                                  \
-  PF_LOAD(r00, r01, n00, n01, 2)                                                                   \
-  PF_LOAD(r10, r11, n10, n11, 3)                                                                   \
-  __syncthreads();                                                                                 \
-  PF_MMA(ACC, 0)
-// Scores of the tile in LDS buffer BUF into ACC: v_mfma_f32_32x32x16_bf16 over the D / 16 slices.
+// Scores of the tile in LDS buffer BUF into ACC (four 16x16 tiles).
 #define PF_MMA(ACC, BUF)                                                                           \
   {                                                                                                \
-    const unsigned char* krow = &ktiles[(BUF) * TILE_BYTES + (kq * 32 + m) * STRIDE + half * 16]; \
-    uint4 kf[STEPS];                                                                               \
-    _Pragma("unroll") for (int st = 0; st < STEPS; ++st) kf[st] = *(const uint4*)(krow + st * 32); \
-    ACC = f32x16_t{};                                                                              \
-    _Pragma("unroll") for (int st = 0; st < STEPS; ++st)                                           \
-      ACC = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[st], __builtin_bit_cast(bf16x8_t, kf[st]), ACC, 0, 0, 0); \
+    const unsigned char* krow = &ktiles[(BUF) * TILE_BYTES + (kg * 16 + m) * STRIDE + grp * GB];  \
+    uint4 kf[SL];                                                                                  \
+    _Pragma("unroll") for (int s = 0; s < SL; ++s) kf[s] = *(const uint4*)(krow + s * 16);        \
+    _Pragma("unroll") for (int u = 0; u < 4; ++u) ACC[u] = f32x4_t{};                              \
+    _Pragma("unroll") for (int s = 0; s < SL; ++s)                                                 \
+      _Pragma("unroll") for (int u = 0; u < 4; ++u)                                                \
+        ACC[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[u][s], __builtin_bit_cast(bf16x8_t, kf[s]), ACC[u], 0, 0, 0); \
+  }
+// Prologue of a pass over the tiles: tiles 0 .. PF_H to LDS (three loads in flight), the tiles
+// that steps 0 and 1 write in flight, scores of tile 0 into ACC, and a barrier so that no wave
+// overwrites tile 0's buffer before every wave has read it.
+#define PF_PROLOGUE(ACC, NORM)                                                                     \
+  {                                                                                                \
+    static_assert(PF_H == 2, "prologue stages tiles 0 .. 2");                                      \
+    uint4 x0_ = r00, x1_ = r01;                                                                    \
+    float y0_ = 0.f, y1_ = 0.f;                                                                    \
+    PF_LOAD(r00, r01, n00, n01, 0, NORM)                                                           \
+    PF_LOAD(r10, r11, n10, n11, 1, NORM)                                                           \
+    PF_LOAD(x0_, x1_, y0_, y1_, 2, NORM)                                                           \
+    PF_STORE(r00, r01, n00, n01, 0, NORM)                                                          \
+    PF_STORE(r10, r11, n10, n11, 1, NORM)                                                          \
+    PF_STORE(x0_, x1_, y0_, y1_, 2, NORM)                                                          \
+    PF_LOAD(r10, r11, n10, n11, PF_H + 2, NORM)                                                    \
+    PF_LOAD(r00, r01, n00, n01, PF_H + 1, NORM)                                                    \
+    __syncthreads();                                                                               \
+    PF_MMA(ACC, 0)                                                                                 \
+    __syncthreads();                                                                               \
   }
 // On a boundary tile, scores of keys that are not candidates of the register's row become -inf.
 // With dr = (position of the register's row) - j, key j is a candidate of the row iff
-// 1 <= j < n, the row exists, and dr >= W (j before the window) or, without the causal mask,
-// dr < 0 (j after p).
+// 1 <= j < n and dr >= W (j before the window) or, without the causal mask, dr < 0 (j after p).
+// (Rows past the end of the queries score 0 and get the bound +inf in phase 2, so that none of
+// their keys is listed.)
   const int rows_valid = (int)min((int64_t)PF_ROWS, a.n_q - i0);
 // (Positions fit in 32 bits here: the scan runs only when n * RB < 2^31. The tests combine with
 // & and |, so that the 16 selects need no branches.)
-  const int p_first32 = (int)p_first, rv_ = rows_valid - row_base;
+  const int p_first32 = (int)p_first;
   const bool ncausal_ = !a.causal;
 #define PF_MASK(ACC, t)                                                                            \
   if (!PF_INTERIOR(t)) {                                                                           \
-    const int j_ = (t) * PF_KEYS + kq * 32 + m;                                                    \
+    const int j_ = (t) * PF_KEYS + kg * 16 + m;                                                    \
     const int dl = p_first32 + row_base - j_;                                                      \
     const bool jok = (j_ >= 1) & (j_ < n);                                                         \
     const int wl = a.W - dl;                                                                       \
-    _Pragma("unroll") for (int r = 0; r < 16; ++r) {                                               \
-      const int o = 8 * (r / 4) + (r % 4);                                                         \
-      const bool cand = jok & (o < rv_) & ((o >= wl) | (ncausal_ & (o < -dl)));                    \
-      ACC[r] = cand ? ACC[r] : -INFINITY;                                                          \
-    }                                                                                              \
+    _Pragma("unroll") for (int u = 0; u < 4; ++u)                                                  \
+      _Pragma("unroll") for (int e = 0; e < 4; ++e) {                                              \
+        const int o = 16 * u + e;                                                                  \
+        const bool cand = jok & ((o >= wl) | (ncausal_ & (o < -dl)));                              \
+        ACC[u][e] = cand ? ACC[u][e] : -INFINITY;                                                  \
+      }                                                                                            \
   }
 // One step t of a pass: the scores of tile t are in ACC_CUR (issued a step earlier); the matrix
-// cores score tile t+1 into ACC_NEXT while the vector units run the per-score work on tile t: PART
-// for each register of ACC_CUR, 16 / STEPS of them after each matrix instruction, then POST. Tile
-// t+2 then goes from its registers to the LDS buffer that tile t used and tile t+4 is requested.
-// Scheduling fences keep that order: left to itself the compiler puts the vector work before the
-// matrix instructions, and as the waves of a block meet at every barrier, the two waves of a
-// SIMD would then take turns on the matrix core instead of overlapping.
-#define PF_STEP(PART, POST, t, ACC_CUR, ACC_NEXT, SET0, SET1, NS0, NS1)                            \
+// cores score tile t+1 into ACC_NEXT while the vector units run the per-score work on tile t:
+// PART for each register of ACC_CUR, PER of them after each matrix instruction. Tile
+// t + PF_H + 1 then goes from its registers to its LDS buffer and tile t + PF_H + 3 is
+// requested. Scheduling fences keep that order: left to itself the compiler puts the vector work
+// before the matrix instructions.
+#define PF_STEP(PART, t, ACC_CUR, ACC_NEXT, SET0, SET1, NS0, NS1, NORM)                            \
   {                                                                                                \
-  const float knc_ = knt[(t) & 1][kq * 32 + m]; /* norm of the lane's key of tile t */             \
   PF_MASK(ACC_CUR, t)                                                                              \
   {                                                                                                \
-    const unsigned char* krow = &ktiles[(((t) + 1) & 1) * TILE_BYTES + (kq * 32 + m) * STRIDE + half * 16]; \
-    uint4 kf[STEPS];                                                                               \
-    _Pragma("unroll") for (int st = 0; st < STEPS; ++st) kf[st] = *(const uint4*)(krow + st * 32); \
+    const unsigned char* krow = &ktiles[(((t) + 1) % PF_NBUF) * TILE_BYTES + (kg * 16 + m) * STRIDE + grp * GB]; \
+    uint4 kf[SL];                                                                                  \
+    _Pragma("unroll") for (int s = 0; s < SL; ++s) kf[s] = *(const uint4*)(krow + s * 16);        \
     __builtin_amdgcn_sched_barrier(0);                                                             \
-    ACC_NEXT = f32x16_t{};                                                                         \
-    _Pragma("unroll") for (int st = 0; st < STEPS; ++st) {                                         \
-      ACC_NEXT = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[st], __builtin_bit_cast(bf16x8_t, kf[st]), ACC_NEXT, 0, 0, 0); \
-      __builtin_amdgcn_sched_barrier(0);                                                           \
-      _Pragma("unroll") for (int e = 0; e < 16 / STEPS; ++e) PART(ACC_CUR, st * (16 / STEPS) + e)  \
-      __builtin_amdgcn_sched_barrier(0);                                                           \
-    }                                                                                              \
+    _Pragma("unroll") for (int u = 0; u < 4; ++u) ACC_NEXT[u] = f32x4_t{};                         \
+    _Pragma("unroll") for (int s = 0; s < SL; ++s)                                                 \
+      _Pragma("unroll") for (int u = 0; u < 4; ++u) {                                              \
+        ACC_NEXT[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[u][s], __builtin_bit_cast(bf16x8_t, kf[s]), ACC_NEXT[u], 0, 0, 0); \
+        __builtin_amdgcn_sched_barrier(0);                                                         \
+        _Pragma("unroll") for (int e = 0; e < PER; ++e) PART(ACC_CUR, t, (s * 4 + u) * PER + e)   \
+        __builtin_amdgcn_sched_barrier(0);                                                         \
+      }                                                                                            \
   }                                                                                                \
-  POST(ACC_CUR, t)                                                                                 \
-  PF_STORE(SET0, SET1, NS0, NS1, (t) + 2)                                                          \
-  PF_LOAD(SET0, SET1, NS0, NS1, (t) + 4)                                                           \
-  __syncthreads();                                                                                 \
+  PF_STORE(SET0, SET1, NS0, NS1, (t) + PF_H + 1, NORM)                                             \
+  PF_LOAD(SET0, SET1, NS0, NS1, (t) + PF_H + 3, NORM)                                              \
   }
 
-  f32x16_t accA, accB;
-  // ---- phase 1: per lane and row, the two largest lower bounds of candidate keys. With m1 >= m2,
-  // the new second best is the median of m1, m2 and the bound, and the new best is the median of
-  // m1, the bound and +inf (a run-time operand, so that no NaN-quieting is added around a max).
+  f32x4_t accA[4], accB[4];
+  // ---- phase 1: per lane and row, the two largest fast scores of candidate keys. With m1 >= m2,
+  // the new second best is the median of m1, m2 and the score, and the new best is the median of
+  // m1, the score and +inf (a run-time operand, so that no NaN-quieting is added around a max).
   const float pinf = a.pinf;
   float m1[16], m2[16];
 #pragma unroll
   for (int r = 0; r < 16; ++r) m1[r] = m2[r] = -INFINITY;
-  float knmx = 0.f;  // the largest norm of the keys this lane has scored
-  if (tid == 0) kmax_blk = 0u;
 // (The empty asm statements pin each result to its place between the matrix instructions;
 // without them the compiler sinks the work of a step past the next step's boundary-tile branch.)
-#define PF_PART1(ACC, r)                                                                           \
+#define PF_PART1(ACC, t, r)                                                                        \
   {                                                                                                \
-    m2[r] = __builtin_amdgcn_fmed3f(m1[r], m2[r], ACC[r]);                                         \
-    m1[r] = __builtin_amdgcn_fmed3f(m1[r], ACC[r], pinf);                                          \
+    const float x_ = ACC[(r) >> 2][(r) & 3];                                                       \
+    m2[r] = __builtin_amdgcn_fmed3f(m1[r], m2[r], x_);                                             \
+    m1[r] = __builtin_amdgcn_fmed3f(m1[r], x_, pinf);                                              \
     asm volatile("" : "+v"(m1[r]), "+v"(m2[r]));                                                   \
   }
-#define PF_POST1(ACC, t) knmx = fmaxf(knmx, knc_);
   if (ntiles > 0) {
-    PF_PROLOGUE(accA)
-    for (int t = 0; t < ntiles; t += 2) {
-      PF_STEP(PF_PART1, PF_POST1, t, accA, accB, r00, r01, n00, n01)
-      PF_STEP(PF_PART1, PF_POST1, t + 1, accB, accA, r10, r11, n10, n11)
+    PF_PROLOGUE(accA, 1)
+    for (int t = 0; t < ntiles; t += PF_H) {
+      PF_STEP(PF_PART1, t, accA, accB, r00, r01, n00, n01, 1)
+      PF_STEP(PF_PART1, t + 1, accB, accA, r10, r11, n10, n11, 1)
+      __syncthreads();
     }
   }
 
-  // the block's largest key norm (norms are non-negative, so their bits order like the values)
+  // the block's largest staged key norm (norms are non-negative, so their bits order like the
+  // values)
   knmx = wave_max_f32(knmx);
   if (lane == 0) atomicMax(&kmax_blk, __float_as_uint(knmx));
 
-  // ---- thresholds: row R's 128 fast scores sit at tops[R][64 * kq + 2 * m + {0, 1}] (even
+  // ---- thresholds: row R's 128 fast scores sit at tops[R][32 * kg + 2 * m + {0, 1}] (even
   // entries: the lanes' best values, 64 distinct keys; odd entries: their second best). Each row
-  // needs a lower bound x of the k-th largest of its 128 values such that few values lie between: the
-  // largest T = lo + c (hi - lo) / 1024, c = 0..1023, that at least k values reach (a bitwise
-  // search over c, monotone in c), where hi is the largest value and lo a known lower bound of the
-  // k-th largest: for k <= 64 and 64 finite best values the smallest of them, else the smallest
-  // finite value (if fewer than k values are finite every candidate stays). The bound is at most
-  // (hi - lo) / 1024 below the k-th largest, and it is never above it; T = x - cq_row max|k|. A wave takes 16 rows in
-  // four groups of four; the 16 lanes of a row hold 8 values each, counted lane by lane and
-  // summed over the row with DPP moves.
-  float* tops = (float*)lists;
+  // needs a lower bound x of the k-th largest of its 128 values such that few values lie between:
+  // the largest x = lo + c (hi - lo) / 1024, c = 0..1023, that at least k values reach (a bitwise
+  // search over c, monotone in c), where hi is the largest value and lo a known lower bound of
+  // the k-th largest: for k <= 64 and 64 finite best values the smallest of them, else the
+  // smallest finite value (if fewer than k values are finite every candidate stays). The bound is
+  // at most (hi - lo) / 1024 below the k-th largest, and it is never above it. A wave takes 16
+  // rows in four groups of four; the 16 lanes of a row hold 8 values each, counted lane by lane
+  // and summed over the row with DPP moves.
+  float* tops = (float*)ktiles;
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
-    const int row = row_base + 8 * (r / 4) + (r % 4);
-    *(float2*)&tops[row * 128 + 64 * kq + 2 * m] = make_float2(m1[r], m2[r]);
+    const int row = row_base + 16 * (r >> 2) + (r & 3);
+    *(float2*)&tops[row * 128 + 32 * kg + 2 * m] = make_float2(m1[r], m2[r]);
   }
   const int sub = lane & 15;
-  float qn_g[4];
-#pragma unroll
-  for (int g = 0; g < 4; ++g) {
-    const int64_t i = i0 + wave * 16 + 4 * g + (lane >> 4);
-    qn_g[g] = i < a.n_q ? a.w.qn[(size_t)bh * a.n_q + i] : 0.f;
-  }
   __syncthreads();
   const float kmax = __uint_as_float(kmax_blk);
   {
@@ -415,22 +434,22 @@ __global__ __launch_bounds__(512) void pf_scan_kernel(PfArgs a) {
     int c[4];
     bool ok[4];
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const float* src = &tops[(wave * 16 + 4 * g + (lane >> 4)) * 128 + 8 * sub];
+    for (int gq = 0; gq < 4; ++gq) {
+      const float* src = &tops[(wave * 16 + 4 * gq + (lane >> 4)) * 128 + 8 * sub];
       const float4 x0 = *(const float4*)src, x1 = *(const float4*)(src + 4);
-      v[g][0] = x0.x; v[g][1] = x0.y; v[g][2] = x0.z; v[g][3] = x0.w;
-      v[g][4] = x1.x; v[g][5] = x1.y; v[g][6] = x1.z; v[g][7] = x1.w;
+      v[gq][0] = x0.x; v[gq][1] = x0.y; v[gq][2] = x0.z; v[gq][3] = x0.w;
+      v[gq][4] = x1.x; v[gq][5] = x1.y; v[gq][6] = x1.z; v[gq][7] = x1.w;
       float hi = -INFINITY, lo_best = INFINITY, lo_fin = INFINITY;
       int nfin = 0, nbest = 0;
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const bool fin = v[g][j] > -INFINITY;
-        hi = fmaxf(hi, v[g][j]);
+        const bool fin = v[gq][j] > -INFINITY;
+        hi = fmaxf(hi, v[gq][j]);
         nfin += fin;
-        lo_fin = fin ? fminf(lo_fin, v[g][j]) : lo_fin;
+        lo_fin = fin ? fminf(lo_fin, v[gq][j]) : lo_fin;
         if ((j & 1) == 0) {
           nbest += fin;
-          lo_best = fminf(lo_best, v[g][j]);
+          lo_best = fminf(lo_best, v[gq][j]);
         }
       }
       hi = pf_row16<1>(hi);
@@ -438,119 +457,92 @@ __global__ __launch_bounds__(512) void pf_scan_kernel(PfArgs a) {
       nbest = pf_row16<0>(nbest);
       lo_fin = pf_row16<2>(lo_fin);
       lo_best = pf_row16<2>(lo_best);
-      ok[g] = nfin >= a.topk;
-      lo[g] = a.topk <= 64 && nbest == 64 ? lo_best : lo_fin;
-      step[g] = ok[g] ? (hi - lo[g]) * (1.0f / 1024.0f) : 0.f;
-      lo[g] = ok[g] ? lo[g] : 0.f;
-      c[g] = 0;
+      ok[gq] = nfin >= a.topk;
+      lo[gq] = a.topk <= 64 && nbest == 64 ? lo_best : lo_fin;
+      step[gq] = ok[gq] ? (hi - lo[gq]) * (1.0f / 1024.0f) : 0.f;
+      lo[gq] = ok[gq] ? lo[gq] : 0.f;
+      c[gq] = 0;
     }
 #pragma unroll
     for (int bit = 9; bit >= 0; --bit) {
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int cc = c[g] | (1 << bit);
-        const float cand = fmaf((float)cc, step[g], lo[g]);
-        int n = 0;
+      for (int gq = 0; gq < 4; ++gq) {
+        const int cc = c[gq] | (1 << bit);
+        const float cand = fmaf((float)cc, step[gq], lo[gq]);
+        int cnt = 0;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) n += v[g][j] >= cand;
-        n = pf_row16<0>(n);
-        c[g] = n >= a.topk ? cc : c[g];
+        for (int j = 0; j < 8; ++j) cnt += v[gq][j] >= cand;
+        cnt = pf_row16<0>(cnt);
+        c[gq] = cnt >= a.topk ? cc : c[gq];
       }
     }
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const int row = wave * 16 + 4 * g + (lane >> 4);
+    for (int gq = 0; gq < 4; ++gq) {
+      const int row = wave * 16 + 4 * gq + (lane >> 4);
       if (sub == 0) {
-        const float x = ok[g] ? fmaf((float)c[g], step[g], lo[g]) - PF_EPS_COEF * qn_g[g] * kmax : -INFINITY;
-        // kept finite (at least the lowest float), so that the -inf of a masked score never passes
-        lthf[row] = fmaxf(x, -0x1.fffffep+127f);
+        // T = x - 2^-13 |q| max|k|, one rounding (the product by a power of two is exact)
+        const float x = ok[gq] ? fmaf(-2.0f * PF_EPS_COEF * qn_g[gq], kmax, fmaf((float)c[gq], step[gq], lo[gq]))
+                               : -INFINITY;
+        // kept finite (at least the lowest float), so that the -inf of a masked score never
+        // passes; +inf for rows past the end of the queries
+        lthk[row] = row < rows_valid ? fmaxf(x, -0x1.fffffep+127f) : INFINITY;
       }
     }
   }
   __syncthreads();
-  float thf[16];
+  float tk[16];
 #pragma unroll
-  for (int r = 0; r < 16; ++r) thf[r] = lthf[row_base + 8 * (r / 4) + (r % 4)];
+  for (int r = 0; r < 16; ++r) tk[r] = lthk[row_base + 16 * (r >> 2) + (r & 3)];
 
-  // ---- phase 2: every candidate key whose upper bound reaches the row's bound goes to the row's
+  // ---- phase 2: every candidate key whose fast score reaches its row's bound goes to the row's
   // list in global memory, with its score. A lane first gathers the test results of its 16
-  // registers into bit r of `fail`'s complement: the test x + eps >= T is the sign of
-  // (x + eps) - T (T finite, x finite or -inf), shifted in by v_alignbit from register 15 down
-  // to 0. The appends of a step are then batched per wave: a lane with passing registers stores
-  // its 16 scores to the wave's score stage, a prefix sum over the lanes gives it room in the
-  // wave's entry stage for one code (lane, register) per passing key, and the wave takes the
-  // codes 64 at a time, one per lane: the row's slot from the wave's own counter of that row (an
-  // LDS atomic on a counter no other wave touches), the score from the stage, the store. A
-  // row's keys of a step are the 32 lanes of one half of the two waves that share its row tile
-  // (kq = 0, 1): the wave with kq = 0 fills the row's slots from the front, the one with kq = 1
-  // from the back, so no slot is shared; slots are clamped into the row's area, and a row whose
-  // two counts add up to more than LCAP takes the exact path. The stages and counters reuse the
-  // LDS of the thresholds' values (4 KB of scores, 1024 codes and 32 counters per wave).
-  float* const sst_w = (float*)lists + wave * 1024;
-  uint16_t* const stg_w = (uint16_t*)(lists + 32768) + wave * 1024;
-  uint32_t* const cnt_w = (uint32_t*)(lists + 49152) + wave * 32;
-  static_assert(49152 + 8 * 32 * 4 <= PF_LIST_BYTES, "phase 2 stages fit the thresholds' LDS");
-  if (lane < 32) cnt_w[lane] = 0u;
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  // registers into bit r of `fail`'s complement: the test x >= T is the sign of x - T (T finite or
+  // +inf, x finite or -inf), shifted in by v_alignbit from register 15 down to 0. A lane with
+  // passing registers then writes its 16 scores to its own place in LDS and appends its keys one
+  // per round: the score read back by register index, a slot from the row's LDS counter (shared by
+  // the four waves of the row group), the store. Slots past LCAP are not written; the count then
+  // tells the finish that the row overflowed.
+  float* const sst_w = sstage + wave * 1024;
+  const uint32_t kc0 = (uint32_t)(kg * 16 + m);
+  uint2* const survb = a.w.surv + grow0 * LCAP;
   uint32_t fail = 0u;
-#define PF_PART2(ACC, i)                                                                           \
+#define PF_PART2(ACC, t, r)                                                                        \
   {                                                                                                \
-    fail = __builtin_amdgcn_alignbit((i) == 0 ? 0u : fail,                                         \
-                                     __float_as_uint(fmaf(cq[15 - (i)], knc_, ACC[15 - (i)]) - thf[15 - (i)]), 31); \
+    const int r_ = 15 - (r);                                                                       \
+    fail = __builtin_amdgcn_alignbit((r) == 0 ? 0u : fail, __float_as_uint(ACC[r_ >> 2][r_ & 3] - tk[r_]), 31); \
     asm volatile("" : "+v"(fail));                                                                 \
   }
 #define PF_POST2(ACC, t)                                                                           \
   {                                                                                                \
     uint32_t bits = ~fail & 0xFFFFu;                                                               \
-    const int np = __popc(bits);                                                                   \
-    if (__ballot(np != 0)) {                                                                       \
-      _Pragma("unroll") for (int q4 = 0; q4 < 4; ++q4)                                             \
-        ((float4*)sst_w)[q4 * 64 + lane] = make_float4(ACC[4 * q4], ACC[4 * q4 + 1], ACC[4 * q4 + 2], ACC[4 * q4 + 3]); \
-      const int incl_ = wave_incl_scan_i32(np);                                                    \
-      const int total_ = __shfl(incl_, 63);                                                        \
-      int at_ = incl_ - np;                                                                        \
-      while (bits) {                                                                               \
+    if (bits) {                                                                                    \
+      _Pragma("unroll") for (int u = 0; u < 4; ++u) ((f32x4_t*)sst_w)[u * 64 + lane] = ACC[u];    \
+      const uint32_t key_ = kc0 + (uint32_t)(t) * PF_KEYS;                                         \
+      do {                                                                                         \
         const int r_ = __builtin_ctz(bits);                                                        \
         bits &= bits - 1u;                                                                         \
-        stg_w[at_++] = (uint16_t)((lane << 4) | r_);                                               \
-      }                                                                                            \
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");                                       \
-      __builtin_amdgcn_wave_barrier();                                                             \
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");                                       \
-      for (int e0_ = 0; e0_ < total_; e0_ += 64) {                                                 \
-        if (e0_ + lane < total_) {                                                                 \
-          const uint32_t code_ = stg_w[e0_ + lane];                                                \
-          const int r_ = (int)(code_ & 15u), src_ = (int)(code_ >> 4), hs_ = src_ >> 5;            \
-          const uint32_t sl_ = min(atomicAdd(&cnt_w[16 * hs_ + r_], 1u), LCAP - 1u);              \
-          const int row_ = rq * 32 + 4 * hs_ + 8 * (r_ >> 2) + (r_ & 3);                           \
-          const float x_ = sst_w[((r_ >> 2) * 64 + src_) * 4 + (r_ & 3)];                          \
-          const uint32_t key_ = (uint32_t)((t) * PF_KEYS + kq * 32 + (src_ & 31));                 \
-          a.w.surv[(grow0 + row_) * LCAP + (kq == 0 ? sl_ : LCAP - 1u - sl_)] =                   \
-              make_uint2(__float_as_uint(x_), key_);                                               \
-        }                                                                                          \
-      }                                                                                            \
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");                                       \
-      __builtin_amdgcn_wave_barrier();                                                             \
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");                                       \
+        const float x_ = sst_w[((r_ >> 2) * 64 + lane) * 4 + (r_ & 3)];                            \
+        const int row_ = row_base + 16 * (r_ >> 2) + (r_ & 3);                                     \
+        const uint32_t slot_ = atomicAdd(&rowcnt[row_], 1u);                                       \
+        if (slot_ < LCAP) survb[row_ * LCAP + slot_] = make_uint2(__float_as_uint(x_), key_);     \
+      } while (bits);                                                                              \
     }                                                                                              \
   }
   if (ntiles > 0) {
-    PF_PROLOGUE(accA)
-    for (int t = 0; t < ntiles; t += 2) {
-      PF_STEP(PF_PART2, PF_POST2, t, accA, accB, r00, r01, n00, n01)
-      PF_STEP(PF_PART2, PF_POST2, t + 1, accB, accA, r10, r11, n10, n11)
+    PF_PROLOGUE(accA, 0)
+    for (int t = 0; t < ntiles; t += PF_H) {
+      PF_STEP(PF_PART2, t, accA, accB, r00, r01, n00, n01, 0)
+      PF_POST2(accA, t)
+      PF_STEP(PF_PART2, t + 1, accB, accA, r10, r11, n10, n11, 0)
+      PF_POST2(accB, t + 1)
+      __syncthreads();
     }
   }
 
-  // the counts of the lists: the wave's counter of (half h, register r), written to the low
-  // (kq = 0, front) or high (kq = 1, back) half of the row's count word
-  if (lane < 32) {
-    const int hs = lane >> 4, r = lane & 15;
-    const int row = rq * 32 + 4 * hs + 8 * (r >> 2) + (r & 3);
-    if (i0 + row < a.n_q) ((uint16_t*)(a.w.cnt + grow0 + row))[kq] = (uint16_t)min(cnt_w[lane], 0xFFFFu);
-  }
+  // the count word: entries from the front of the row's slots in its low 16 bits, 0 in the high
+  // 16 bits; a count above LCAP sends the row to the exact path
+  __syncthreads();
+  if (tid < PF_ROWS && i0 + tid < a.n_q) a.w.cnt[grow0 + tid] = min(rowcnt[tid], 0xFFFFu);
 #undef PF_INTERIOR
 #undef PF_LOAD
 #undef PF_STORE
@@ -559,7 +551,6 @@ __global__ __launch_bounds__(512) void pf_scan_kernel(PfArgs a) {
 #undef PF_MASK
 #undef PF_STEP
 #undef PF_PART1
-#undef PF_POST1
 #undef PF_PART2
 #undef PF_POST2
 }
