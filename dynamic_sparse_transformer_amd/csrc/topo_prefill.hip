@@ -46,6 +46,7 @@ static int64_t pf_slot(int32_t k) { return k + 48 < PF_LCAP_MAX ? k + 48 : PF_LC
 struct PfWs {
   float* qn;        // [B*Hq*n_q]: |q| of every query row (rounded up)
   float* kn;        // [B*Hkv][n]: |k| of every key (rounded up)
+  float* ktmax;     // [B*Hkv][ceil(n / 64)]: the largest |k| of each 64-key tile
   uint32_t* cnt;    // [B*Hq*n_q]: entries of the row's list, from the front of its slots (low 16 bits)
                     // and from the back (high 16 bits, 0 from this scan); more than the slots
                     // hold = overflow
@@ -64,6 +65,8 @@ static PfWs pf_carve(void* ws, int32_t B, int32_t Hq, int32_t Hkv, int64_t n_q, 
   p += align256(rows * 4);
   w.kn = (float*)p;
   p += align256((size_t)B * Hkv * (size_t)n * 4);
+  w.ktmax = (float*)p;
+  p += align256((size_t)B * Hkv * (size_t)((n + 63) / 64) * 4);
   w.cnt = (uint32_t*)p;
   p += align256(rows * 4);
   w.path = (int32_t*)p;
@@ -100,11 +103,17 @@ PrefillView prefill_view(int32_t B, int32_t Hq, int32_t Hkv, int64_t n_q, int64_
 // (coalesced, RPW rows per load instruction). The squares of bf16 values are exact in float32;
 // their float32 sum (8 terms per lane, then a tree over the LPR lanes) and sqrtf carry a relative
 // error far below the factor (1 + 2^-15) that rounds the norm up. Grid (blocks over the rows of
-// a head, heads); U rows per lane.
+// a head, heads); U rows per lane. With tmax, also the largest norm of each 64-row tile of a head
+// (a block covers whole tiles: 64 or 128 rows).
 template <int D, int U>
-__global__ __launch_bounds__(256) void pf_norm_kernel(const unsigned char* x, int64_t rows_per_head, float* norm) {
-  constexpr int RB = D * 2, LPR = RB / 16, RPW = 64 / LPR;
+__global__ __launch_bounds__(256) void pf_norm_kernel(const unsigned char* x, int64_t rows_per_head, float* norm,
+                                                      float* tmax) {
+  constexpr int RB = D * 2, LPR = RB / 16, RPW = 64 / LPR, BROWS = 4 * U * RPW;
+  static_assert(BROWS % 64 == 0 && 64 % (U * RPW) == 0, "a wave's rows lie in one tile, a block covers whole tiles");
+  __shared__ uint32_t tm[BROWS / 64];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, gq = lane / LPR, cc = lane % LPR;
+  if (threadIdx.x < BROWS / 64) tm[threadIdx.x] = 0u;
+  float wmax = 0.f;
   const unsigned char* base = x + (size_t)blockIdx.y * (size_t)rows_per_head * RB;
   const int64_t r0 = (int64_t)blockIdx.x * (4 * U * RPW) + (int64_t)wave * U * RPW + gq;
   uint4 v[U];
@@ -127,6 +136,16 @@ __global__ __launch_bounds__(256) void pf_norm_kernel(const unsigned char* x, in
     const float nrm = sqrtf(s2) * (1.0f + 0x1p-15f);
     const int64_t row = r0 + u * RPW;
     if (cc == 0 && row < rows_per_head) norm[(size_t)blockIdx.y * rows_per_head + row] = nrm;
+    wmax = row < rows_per_head ? fmaxf(wmax, nrm) : wmax;
+  }
+  if (tmax) {
+    // norms are non-negative, so their bits order like the values
+    wmax = wave_max_f32(wmax);
+    __syncthreads();
+    if (lane == 0) atomicMax(&tm[wave * U * RPW / 64], __float_as_uint(wmax));
+    __syncthreads();
+    const int64_t tiles = (rows_per_head + 63) / 64, t = (int64_t)blockIdx.x * (BROWS / 64) + threadIdx.x;
+    if (threadIdx.x < BROWS / 64 && t < tiles) tmax[(size_t)blockIdx.y * tiles + t] = __uint_as_float(tm[threadIdx.x]);
   }
 }
 
@@ -156,7 +175,7 @@ struct PfArgs {
   int32_t* sel_count;
   PfWs w;
   int64_t n, n_q, q_pos0, slot, rows;
-  int32_t Hq, Hkv, G, W, topk, causal, set_cap, exact_all;
+  int32_t B, Hq, Hkv, G, W, topk, causal, set_cap, exact_all;
   int32_t win;  // 1: the window kernel has left (m_w, Z_w, O_w) of every row in the workspace
   float pinf;   // +inf (a run-time operand of the scan's medians)
   double scale;
@@ -220,40 +239,21 @@ __global__ __launch_bounds__(512) void pf_scan_kernel(PfArgs a) {
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   // Job of this block (the blocks of one head on one XCD). Within a head the row blocks run from
   // the last (most keys under a causal mask) to the first, so the long jobs start first.
-  const int64_t nrb = (a.n_q + PF_ROWS - 1) / PF_ROWS;
-  const int64_t job = xcd_job(blockIdx.x, nrb * a.Hq * (a.rows / (a.n_q * a.Hq)));
-  const int bh = (int)(job / nrb);
-  const int b = bh / a.Hq, h = bh - b * a.Hq, g = h / a.G;
-  const int64_t i0 = (nrb - 1 - (job - (int64_t)bh * nrb)) * PF_ROWS;
+  // (32-bit index arithmetic: the jobs, heads and row blocks fit)
+  const uint32_t nrb = (uint32_t)((a.n_q + PF_ROWS - 1) / PF_ROWS);
+  const uint32_t job = (uint32_t)xcd_job(blockIdx.x, (int64_t)nrb * a.Hq * a.B);
+  const uint32_t bh = job / nrb;
+  const uint32_t b = bh / (uint32_t)a.Hq, h = bh - b * (uint32_t)a.Hq, g = h / (uint32_t)a.G;
+  const int64_t i0 = (int64_t)(nrb - 1 - (job - bh * nrb)) * PF_ROWS;
   const unsigned char* kb = a.k + ((size_t)b * a.Hkv + g) * (size_t)a.n * RB;
-  const float* knb = a.w.kn + ((size_t)b * a.Hkv + g) * (size_t)a.n;
+  const float* ktm = a.w.ktmax + ((size_t)b * a.Hkv + g) * (size_t)((a.n + PF_KEYS - 1) / PF_KEYS);
   const uint32_t LCAP = (uint32_t)a.slot;
   const size_t grow0 = (size_t)bh * a.n_q + i0;  // global row of block row 0
   const int n = (int)a.n;  // the host runs this scan only when n * RB < 2^31
 
   const int rg = wave >> 2, kg = wave & 3;
   const int m = lane & 15, grp = lane >> 4;
-  bf16x8_t qa[4][SL];
-#pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int64_t i = i0 + rg * 64 + u * 16 + m;
-    const unsigned char* qrow = a.q + ((size_t)bh * a.n_q + (i < a.n_q ? i : 0)) * RB + grp * GB;
-#pragma unroll
-    for (int s = 0; s < SL; ++s) {
-      const uint4 w = i < a.n_q ? *(const uint4*)(qrow + s * 16) : make_uint4(0u, 0u, 0u, 0u);
-      qa[u][s] = __builtin_bit_cast(bf16x8_t, w);
-    }
-  }
   const int row_base = rg * 64 + 4 * grp;  // block row of register (u, e): row_base + 16 u + e
-  if (tid < PF_ROWS) rowcnt[tid] = 0u;
-  if (tid == 0) kmax_blk = 0u;
-  // |q| of the rows whose threshold this lane helps to find (wave w takes rows 16 w .. +16)
-  float qn_g[4];
-#pragma unroll
-  for (int gq = 0; gq < 4; ++gq) {
-    const int64_t i = i0 + wave * 16 + 4 * gq + (lane >> 4);
-    qn_g[gq] = i < a.n_q ? a.w.qn[(size_t)bh * a.n_q + i] : 0.f;
-  }
 
   const int64_t i_last = min(i0 + PF_ROWS, a.n_q) - 1;
   const int64_t p_first = a.q_pos0 + i0, p_last = a.q_pos0 + i_last;
@@ -271,32 +271,23 @@ __global__ __launch_bounds__(512) void pf_scan_kernel(PfArgs a) {
   // Staging of key tiles: thread tid copies 16-byte chunk (tid % NCH) of key rows
   // u * PF_KEYS + tid / NCH (+ RPP). Raw buffer loads whose range ends at the cache's last key:
   // rows past the end read as zero, so every load is issued unconditionally and no address is
-  // clamped. In phase 1 the thread with chunk 0 of a row also loads that key's norm (index
-  // clamped; keys past the range the block scores only make the largest norm larger). Register
-  // set (t & 1) holds the tile that step t writes to LDS.
+  // clamped. Register set (t & 1) holds the tile that step t writes to LDS.
   const int srow = tid / NCH, schunk = tid % NCH;
   const int voff0 = srow * RB + schunk * 16, voff1 = voff0 + RPP * RB;
   uint4 r00 = make_uint4(0u, 0u, 0u, 0u), r01 = r00, r10 = r00, r11 = r00;
-  float n00 = 0.f, n01 = 0.f, n10 = 0.f, n11 = 0.f;
-  float knmx = 0.f;  // the largest key norm this thread has staged
-#define PF_LOAD(DST0, DST1, N0, N1, U, NORM)                                                       \
+#define PF_LOAD(DST0, DST1, U)                                                                     \
   {                                                                                                \
     const int kt_ = min((U) * PF_KEYS, n);                                                         \
     const __amdgpu_buffer_rsrc_t rs_ =                                                             \
         __builtin_amdgcn_make_buffer_rsrc((void*)(kb + (size_t)kt_ * RB), (short)0, (n - kt_) * RB, 0x00020000); \
     DST0 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs_, voff0, 0, 0));    \
-    if (NORM) N0 = knb[min((U) * PF_KEYS + srow, n - 1)];                                          \
-    if (PASSES > 1) {                                                                              \
-      DST1 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs_, voff1, 0, 0));  \
-      if (NORM) N1 = knb[min((U) * PF_KEYS + srow + RPP, n - 1)];                                  \
-    }                                                                                              \
+    if (PASSES > 1) DST1 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs_, voff1, 0, 0)); \
   }
-#define PF_STORE(SRC0, SRC1, N0, N1, U, NORM)                                                      \
+#define PF_STORE(SRC0, SRC1, U)                                                                    \
   {                                                                                                \
     unsigned char* dst = &ktiles[((U) % PF_NBUF) * TILE_BYTES + srow * STRIDE + schunk * 16];      \
     *(uint4*)dst = SRC0;                                                                           \
     if (PASSES > 1) *(uint4*)(dst + RPP * STRIDE) = SRC1;                                          \
-    if (NORM) knmx = fmaxf(knmx, PASSES > 1 ? fmaxf(N0, N1) : N0);                                 \
   }
 // Scores of the tile in LDS buffer BUF into ACC (four 16x16 tiles).
 #define PF_MMA(ACC, BUF)                                                                           \
@@ -309,22 +300,25 @@ __global__ __launch_bounds__(512) void pf_scan_kernel(PfArgs a) {
       _Pragma("unroll") for (int u = 0; u < 4; ++u)                                                \
         ACC[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[u][s], __builtin_bit_cast(bf16x8_t, kf[s]), ACC[u], 0, 0, 0); \
   }
-// Prologue of a pass over the tiles: tiles 0 .. PF_H to LDS (three loads in flight), the tiles
-// that steps 0 and 1 write in flight, scores of tile 0 into ACC, and a barrier so that no wave
-// overwrites tile 0's buffer before every wave has read it.
-#define PF_PROLOGUE(ACC, NORM)                                                                     \
+// Prologue of a pass over the tiles, in two parts: the loads of tiles 0 .. PF_H (for LDS) and of
+// the tiles that steps 0 and 1 write (register sets 0 and 1), all in flight together; then tiles
+// 0 .. PF_H to LDS, scores of tile 0 into ACC, and a barrier so that no wave overwrites tile 0's
+// buffer before every wave has read it.
+  static_assert(PF_H == 2, "the prologue stages tiles 0 .. 2");
+  uint4 p00 = r00, p01 = r00, p10 = r00, p11 = r00, p20 = r00, p21 = r00;
+#define PF_PRO_ISSUE()                                                                             \
   {                                                                                                \
-    static_assert(PF_H == 2, "prologue stages tiles 0 .. 2");                                      \
-    uint4 x0_ = r00, x1_ = r01;                                                                    \
-    float y0_ = 0.f, y1_ = 0.f;                                                                    \
-    PF_LOAD(r00, r01, n00, n01, 0, NORM)                                                           \
-    PF_LOAD(r10, r11, n10, n11, 1, NORM)                                                           \
-    PF_LOAD(x0_, x1_, y0_, y1_, 2, NORM)                                                           \
-    PF_STORE(r00, r01, n00, n01, 0, NORM)                                                          \
-    PF_STORE(r10, r11, n10, n11, 1, NORM)                                                          \
-    PF_STORE(x0_, x1_, y0_, y1_, 2, NORM)                                                          \
-    PF_LOAD(r10, r11, n10, n11, PF_H + 2, NORM)                                                    \
-    PF_LOAD(r00, r01, n00, n01, PF_H + 1, NORM)                                                    \
+    PF_LOAD(p00, p01, 0)                                                                           \
+    PF_LOAD(p10, p11, 1)                                                                           \
+    PF_LOAD(p20, p21, 2)                                                                           \
+    PF_LOAD(r00, r01, PF_H + 1)                                                                    \
+    PF_LOAD(r10, r11, PF_H + 2)                                                                    \
+  }
+#define PF_PRO_FINISH(ACC)                                                                         \
+  {                                                                                                \
+    PF_STORE(p00, p01, 0)                                                                          \
+    PF_STORE(p10, p11, 1)                                                                          \
+    PF_STORE(p20, p21, 2)                                                                          \
     __syncthreads();                                                                               \
     PF_MMA(ACC, 0)                                                                                 \
     __syncthreads();                                                                               \
@@ -358,7 +352,7 @@ __global__ __launch_bounds__(512) void pf_scan_kernel(PfArgs a) {
 // t + PF_H + 1 then goes from its registers to its LDS buffer and tile t + PF_H + 3 is
 // requested. Scheduling fences keep that order: left to itself the compiler puts the vector work
 // before the matrix instructions.
-#define PF_STEP(PART, t, ACC_CUR, ACC_NEXT, SET0, SET1, NS0, NS1, NORM)                            \
+#define PF_STEP(PART, t, ACC_CUR, ACC_NEXT, SET0, SET1)                                            \
   {                                                                                                \
   PF_MASK(ACC_CUR, t)                                                                              \
   {                                                                                                \
@@ -375,9 +369,37 @@ __global__ __launch_bounds__(512) void pf_scan_kernel(PfArgs a) {
         __builtin_amdgcn_sched_barrier(0);                                                         \
       }                                                                                            \
   }                                                                                                \
-  PF_STORE(SET0, SET1, NS0, NS1, (t) + PF_H + 1, NORM)                                             \
-  PF_LOAD(SET0, SET1, NS0, NS1, (t) + PF_H + 3, NORM)                                              \
+  PF_STORE(SET0, SET1, (t) + PF_H + 1)                                                             \
+  PF_LOAD(SET0, SET1, (t) + PF_H + 3)                                                              \
   }
+
+  // phase 1's first tiles are requested before the A operands, the longer wait
+  if (ntiles > 0) PF_PRO_ISSUE()
+  // The A operands: rows past the end of the queries load the last row (their scores are never
+  // used: they get the bound +inf in phase 2)
+  bf16x8_t qa[4][SL];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int64_t i = min(i0 + rg * 64 + u * 16 + m, a.n_q - 1);
+    const unsigned char* qrow = a.q + ((size_t)bh * a.n_q + i) * RB + grp * GB;
+#pragma unroll
+    for (int s = 0; s < SL; ++s) qa[u][s] = __builtin_bit_cast(bf16x8_t, *(const uint4*)(qrow + s * 16));
+  }
+  if (tid < PF_ROWS) rowcnt[tid] = 0u;
+  if (tid == 0) kmax_blk = 0u;
+  // |q| of the rows whose threshold this lane helps to find (wave w takes rows 16 w .. +16);
+  // loaded unconditionally from a clamped index, so that no load waits on another
+  float qn_g[4];
+#pragma unroll
+  for (int gq = 0; gq < 4; ++gq) {
+    const int64_t i = i0 + wave * 16 + 4 * gq + (lane >> 4);
+    const float qv = a.w.qn[(size_t)bh * a.n_q + min(i, a.n_q - 1)];
+    qn_g[gq] = i < a.n_q ? qv : 0.f;
+  }
+  // the largest norm of the keys the block scores, from the tiles' maxima (after the other loads
+  // are in flight: its wait covers them all)
+  float knmx = 0.f;
+  for (int t = tid; t < ntiles; t += 512) knmx = fmaxf(knmx, ktm[t]);
 
   f32x4_t accA[4], accB[4];
   // ---- phase 1: per lane and row, the two largest fast scores of candidate keys. With m1 >= m2,
@@ -397,27 +419,32 @@ __global__ __launch_bounds__(512) void pf_scan_kernel(PfArgs a) {
     asm volatile("" : "+v"(m1[r]), "+v"(m2[r]));                                                   \
   }
   if (ntiles > 0) {
-    PF_PROLOGUE(accA, 1)
+    PF_PRO_FINISH(accA)
+    // (the norms arrived with the first tiles; taking them now keeps a wait for them out of the
+    // threshold search, where the loads of phase 2's first tiles are in flight)
+#pragma unroll
+    for (int gq = 0; gq < 4; ++gq) asm volatile("" : "+v"(qn_g[gq]));
     for (int t = 0; t < ntiles; t += PF_H) {
-      PF_STEP(PF_PART1, t, accA, accB, r00, r01, n00, n01, 1)
-      PF_STEP(PF_PART1, t + 1, accB, accA, r10, r11, n10, n11, 1)
+      PF_STEP(PF_PART1, t, accA, accB, r00, r01)
+      PF_STEP(PF_PART1, t + 1, accB, accA, r10, r11)
       __syncthreads();
     }
   }
 
-  // the block's largest staged key norm (norms are non-negative, so their bits order like the
-  // values)
+  // phase 2's first tiles are requested now, so that they arrive during the threshold search
+  if (ntiles > 0) PF_PRO_ISSUE()
+  // the block's largest key norm (norms are non-negative, so their bits order like the values)
   knmx = wave_max_f32(knmx);
   if (lane == 0) atomicMax(&kmax_blk, __float_as_uint(knmx));
 
   // ---- thresholds: row R's 128 fast scores sit at tops[R][32 * kg + 2 * m + {0, 1}] (even
   // entries: the lanes' best values, 64 distinct keys; odd entries: their second best). Each row
   // needs a lower bound x of the k-th largest of its 128 values such that few values lie between:
-  // the largest x = lo + c (hi - lo) / 1024, c = 0..1023, that at least k values reach (a bitwise
+  // the largest x = lo + c (hi - lo) / 128, c = 0..127, that at least k values reach (a bitwise
   // search over c, monotone in c), where hi is the largest value and lo a known lower bound of
   // the k-th largest: for k <= 64 and 64 finite best values the smallest of them, else the
   // smallest finite value (if fewer than k values are finite every candidate stays). The bound is
-  // at most (hi - lo) / 1024 below the k-th largest, and it is never above it. A wave takes 16
+  // at most (hi - lo) / 128 below the k-th largest, and it is never above it. A wave takes 16
   // rows in four groups of four; the 16 lanes of a row hold 8 values each, counted lane by lane
   // and summed over the row with DPP moves.
   float* tops = (float*)ktiles;
@@ -459,12 +486,12 @@ __global__ __launch_bounds__(512) void pf_scan_kernel(PfArgs a) {
       lo_best = pf_row16<2>(lo_best);
       ok[gq] = nfin >= a.topk;
       lo[gq] = a.topk <= 64 && nbest == 64 ? lo_best : lo_fin;
-      step[gq] = ok[gq] ? (hi - lo[gq]) * (1.0f / 1024.0f) : 0.f;
+      step[gq] = ok[gq] ? (hi - lo[gq]) * (1.0f / 128.0f) : 0.f;
       lo[gq] = ok[gq] ? lo[gq] : 0.f;
       c[gq] = 0;
     }
 #pragma unroll
-    for (int bit = 9; bit >= 0; --bit) {
+    for (int bit = 6; bit >= 0; --bit) {
 #pragma unroll
       for (int gq = 0; gq < 4; ++gq) {
         const int cc = c[gq] | (1 << bit);
@@ -502,7 +529,10 @@ __global__ __launch_bounds__(512) void pf_scan_kernel(PfArgs a) {
   // per round: the score read back by register index, a slot from the row's LDS counter (shared by
   // the four waves of the row group), the store. Slots past LCAP are not written; the count then
   // tells the finish that the row overflowed.
-  float* const sst_w = sstage + wave * 1024;
+  // (the lane's stage holds its 16 scores in register order; the row counters are kept in the
+  // order rg, g, register, so that register r of a lane finds its row's counter at cnt_l[r])
+  float* const sst_l = sstage + (wave * 64 + lane) * 16;
+  uint32_t* const cnt_l = rowcnt + rg * 64 + grp * 16;
   const uint32_t kc0 = (uint32_t)(kg * 16 + m);
   uint2* const survb = a.w.surv + grow0 * LCAP;
   uint32_t fail = 0u;
@@ -516,37 +546,42 @@ __global__ __launch_bounds__(512) void pf_scan_kernel(PfArgs a) {
   {                                                                                                \
     uint32_t bits = ~fail & 0xFFFFu;                                                               \
     if (bits) {                                                                                    \
-      _Pragma("unroll") for (int u = 0; u < 4; ++u) ((f32x4_t*)sst_w)[u * 64 + lane] = ACC[u];    \
+      _Pragma("unroll") for (int u = 0; u < 4; ++u) *(f32x4_t*)(sst_l + 4 * u) = ACC[u];          \
       const uint32_t key_ = kc0 + (uint32_t)(t) * PF_KEYS;                                         \
       do {                                                                                         \
         const int r_ = __builtin_ctz(bits);                                                        \
         bits &= bits - 1u;                                                                         \
-        const float x_ = sst_w[((r_ >> 2) * 64 + lane) * 4 + (r_ & 3)];                            \
-        const int row_ = row_base + 16 * (r_ >> 2) + (r_ & 3);                                     \
-        const uint32_t slot_ = atomicAdd(&rowcnt[row_], 1u);                                       \
-        if (slot_ < LCAP) survb[row_ * LCAP + slot_] = make_uint2(__float_as_uint(x_), key_);     \
+        const float x_ = sst_l[r_];                                                                \
+        const uint32_t slot_ = atomicAdd(&cnt_l[r_], 1u);                                          \
+        asm volatile("" : : "v"(x_)); /* both LDS requests in flight before the first wait */      \
+        const uint32_t row_ = (uint32_t)(row_base + r_ + 3 * (r_ & 12));                           \
+        if (slot_ < LCAP)                                                                          \
+          *(uint2*)((char*)survb + (__umul24(row_, LCAP) + slot_) * 8u) = make_uint2(__float_as_uint(x_), key_); \
       } while (bits);                                                                              \
     }                                                                                              \
   }
   if (ntiles > 0) {
-    PF_PROLOGUE(accA, 0)
+    PF_PRO_FINISH(accA)
     for (int t = 0; t < ntiles; t += PF_H) {
-      PF_STEP(PF_PART2, t, accA, accB, r00, r01, n00, n01, 0)
+      PF_STEP(PF_PART2, t, accA, accB, r00, r01)
       PF_POST2(accA, t)
-      PF_STEP(PF_PART2, t + 1, accB, accA, r10, r11, n10, n11, 0)
+      PF_STEP(PF_PART2, t + 1, accB, accA, r10, r11)
       PF_POST2(accB, t + 1)
       __syncthreads();
     }
   }
 
   // the count word: entries from the front of the row's slots in its low 16 bits, 0 in the high
-  // 16 bits; a count above LCAP sends the row to the exact path
+  // 16 bits; a count above LCAP sends the row to the exact path. Block row R = 64 rg + 16 u + 4 g
+  // + e has its counter at 64 rg + 16 g + 4 u + e.
   __syncthreads();
-  if (tid < PF_ROWS && i0 + tid < a.n_q) a.w.cnt[grow0 + tid] = min(rowcnt[tid], 0xFFFFu);
+  if (tid < PF_ROWS && i0 + tid < a.n_q)
+    a.w.cnt[grow0 + tid] = min(rowcnt[(tid & 0x43) | ((tid & 12) << 2) | ((tid >> 2) & 12)], 0xFFFFu);
 #undef PF_INTERIOR
 #undef PF_LOAD
 #undef PF_STORE
-#undef PF_PROLOGUE
+#undef PF_PRO_ISSUE
+#undef PF_PRO_FINISH
 #undef PF_MMA
 #undef PF_MASK
 #undef PF_STEP
@@ -1326,9 +1361,9 @@ static hipError_t launch_pf_t(const PrefillLaunch& L, const PfArgs& pa, hipStrea
       // norms for the error bounds of the matrix-core scores (only the fast selection uses them)
       constexpr int RPW = 64 / (D * 2 / 16), QU = 4;  // rows per wave load; loads per lane
       hipLaunchKernelGGL((pf_norm_kernel<D, QU>), dim3((unsigned)((rows + 4 * QU * RPW - 1) / (4 * QU * RPW)), 1), dim3(256),
-                         0, s, (const unsigned char*)L.q, (int64_t)rows, pa.w.qn);
+                         0, s, (const unsigned char*)L.q, (int64_t)rows, pa.w.qn, (float*)nullptr);
       hipLaunchKernelGGL((pf_norm_kernel<D, QU>), dim3((unsigned)((L.n + 4 * QU * RPW - 1) / (4 * QU * RPW)), (unsigned)(L.B * L.Hkv)),
-                         dim3(256), 0, s, (const unsigned char*)L.k, L.n, pa.w.kn);
+                         dim3(256), 0, s, (const unsigned char*)L.k, L.n, pa.w.kn, pa.w.ktmax);
       e = hipGetLastError();
       if (e != hipSuccess) return e;
     }
@@ -1382,6 +1417,7 @@ hipError_t launch_prefill(const PrefillLaunch& L, hipStream_t stream) {
   pa.n_q = L.n_q;
   pa.q_pos0 = L.q_pos0;
   pa.slot = pf_slot(L.topk);
+  pa.B = L.B;
   pa.Hq = L.Hq;
   pa.Hkv = L.Hkv;
   pa.G = L.G;
