@@ -27,13 +27,16 @@ constexpr int PF_ROWS = 128;         // query rows per scan block (8 waves: 2 ro
 constexpr int PF_KEYS = 64;          // keys per scan step
 constexpr int PF_MAX_K = 96;         // largest k the MFMA scan ranks
 
-// Error bound of the MFMA float32 scores: products of bf16 values are exact in float32, and a
-// float32 sum of d <= 128 terms in any order and grouping is off by less than d 2^-24
-// sum_t |q_t k_t| <= 2^-17 |q| |k| (Cauchy-Schwarz), so |s_fast - s| <= 2^-14 |q| |k| holds with
-// a factor 8 to spare, whatever the matrix unit's internal order and alignment. The spare also
-// covers forming a bound s_fast -+ 2^-14 |q| |k| in float32 (half an ulp of the score, at most
-// 2^-24 |q| |k|). The tests measure the largest |s_fast - s| / (|q| |k|) on the scan's lists.
-constexpr float PF_EPS_COEF = 0x1p-14f;
+// Error bound of the MFMA float32 scores. Products of bf16 values are exact in float32. A float32
+// sum of d <= 128 of them with round-to-nearest, in any order and grouping, is off by less than
+// d 2^-24 sum_t |q_t k_t| <= 2^-17 |q| |k| (Cauchy-Schwarz). A matrix unit that instead aligns
+// the 32 products of a slice to the largest of them and truncates loses less than
+// 32 2^-23 max|p| <= 2^-18 sum|p| per slice, plus at most 2^-23 sum|p| for each of the d / 32
+// float32 accumulations: again less than 2^-17 |q| |k|. So |s_fast - s| <= 2^-15 |q| |k| holds
+// with a factor 4 to spare in either model; the spare also covers forming a bound
+// s_fast -+ 2^-15 |q| |k| in float32 (half an ulp of the score, at most 2^-24 |q| |k|). The
+// tests measure the largest |s_fast - s| / (|q| |k|) on the scan's lists (near 2^-23).
+constexpr float PF_EPS_COEF = 0x1p-15f;
 float prefill_eps_coef() { return PF_EPS_COEF; }
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -204,12 +207,12 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 // The key tiles rotate through 2 PF_H LDS buffers: tile t is written PF_H + 1 steps before the
 // step that reads it, so that the waves meet at a barrier only every PF_H steps. The loads of the
 // tile written at step t + 2 are in flight while step t runs.
-// Every score has its own error bound eps = 2^-14 |q| |k| (see PF_EPS_COEF). Phase 1 keeps, per
-// lane and row, the two largest fast scores it has seen, and the largest norm of the keys the
-// block stages. Those 128 values per row belong to distinct candidate keys, so if k of them reach
-// x, k keys score at least x - 2^-14 |q| max|k| exactly, and each of them has a fast score of at
-// least x - 2^-13 |q| max|k|: phase 2 scores the keys again and lists every key whose fast score
-// reaches T = x - 2^-13 |q| max|k| (computed with a spare far above float32 rounding) in its
+// Every score has its own error bound eps = C |q| |k| (C = PF_EPS_COEF). Phase 1 keeps, per lane
+// and row, the two largest fast scores it has seen; the largest norm of the keys the block scores
+// comes from the tiles' maxima. Those 128 values per row belong to distinct candidate keys, so if
+// k of them reach x, k keys score at least x - C |q| max|k| exactly, and each of them has a fast
+// score of at least x - 2 C |q| max|k|: phase 2 scores the keys again and lists every key whose
+// fast score reaches T = x - 2 C |q| max|k| (computed with a spare far above float32 rounding) in its
 // row's list in global memory, with a slot from the row's LDS counter. The finish ranks the
 // lists.
 constexpr int PF_H = 2;              // steps between block barriers
@@ -507,7 +510,7 @@ __global__ __launch_bounds__(512) void pf_scan_kernel(PfArgs a) {
     for (int gq = 0; gq < 4; ++gq) {
       const int row = wave * 16 + 4 * gq + (lane >> 4);
       if (sub == 0) {
-        // T = x - 2^-13 |q| max|k|, one rounding (the product by a power of two is exact)
+        // T = x - 2 C |q| max|k|, one rounding (the product by a power of two is exact)
         const float x = ok[gq] ? fmaf(-2.0f * PF_EPS_COEF * qn_g[gq], kmax, fmaf((float)c[gq], step[gq], lo[gq]))
                                : -INFINITY;
         // kept finite (at least the lowest float), so that the -inf of a masked score never
@@ -1031,7 +1034,7 @@ __device__ void pf_row(const PfArgs& a, PfRowSmem* sm, size_t grow) {
       fill_qd();
       nt = pf_exact_row<D, BF16>(sm, a, kb, p);
     } else if (c > a.topk) {
-      // Each entry's bounds L = s_mc - eps_j <= s <= U = s_mc + eps_j, eps_j = 2^-14 |q| |k_j|.
+      // Each entry's bounds L = s_mc - eps_j <= s <= U = s_mc + eps_j, eps_j = C |q| |k_j|.
       // T_L = k-th largest L; A = entries with U >= T_L. Every entry outside A scores below k
       // entries, so the top-k lies in A, and if |A| = k it is A. Otherwise, with T_U the k-th
       // largest U over A, an entry with L > T_U is surely in the top-k (only entries with
