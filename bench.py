@@ -301,9 +301,13 @@ def run_prefill_bench(cfg: int, steps: int, warmup: int):
     out = torch.empty((s.B, s.Hq, n_q, s.d), dtype=torch.float32, device="cuda")
     sel = torch.empty((s.B, s.Hq, n_q, 1 + s.W + s.k), dtype=torch.int32, device="cuda")
     cnt = torch.empty((s.B, s.Hq, n_q), dtype=torch.int32, device="cuda")
-    for _ in range(warmup):
+    # warm-up: the given count, and at least half a second of calls (clocks settle)
+    t_w = time.perf_counter()
+    done = 0
+    while done < warmup or time.perf_counter() - t_w < 0.5:
         topo.topo_attn_prefill(q, k, v, s.W, s.k, scale, q_pos0=0, out=out, sel_idx=sel, sel_count=cnt, workspace=ws)
-    torch.cuda.synchronize()
+        torch.cuda.synchronize()
+        done += 1
     stream = torch.cuda.current_stream()
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     for a, b in evs:

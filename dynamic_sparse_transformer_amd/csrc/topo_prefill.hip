@@ -234,7 +234,7 @@ __global__ __launch_bounds__(512) void pf_scan_kernel(PfArgs a) {
   __shared__ __align__(16) unsigned char ktiles[SMEM];  // key tiles; the thresholds' values between the phases
   __shared__ __align__(16) float sstage[8 * 64 * 16];    // phase 2: each lane's 16 scores of a step
   __shared__ float lthk[PF_ROWS];
-  __shared__ uint32_t rowcnt[PF_ROWS];
+  __shared__ uint32_t rowcnt[2 * 4 * 17];  // the rows' list counters (see phase 2)
   __shared__ uint32_t kmax_blk;  // float bits of the largest key norm the block has staged
 
   // (the wave index through readfirstlane, so that the compiler keeps what derives from it in
@@ -388,7 +388,7 @@ __global__ __launch_bounds__(512) void pf_scan_kernel(PfArgs a) {
 #pragma unroll
     for (int s = 0; s < SL; ++s) qa[u][s] = __builtin_bit_cast(bf16x8_t, *(const uint4*)(qrow + s * 16));
   }
-  if (tid < PF_ROWS) rowcnt[tid] = 0u;
+  if (tid < 2 * 4 * 17) rowcnt[tid] = 0u;
   if (tid == 0) kmax_blk = 0u;
   // |q| of the rows whose threshold this lane helps to find (wave w takes rows 16 w .. +16);
   // loaded unconditionally from a clamped index, so that no load waits on another
@@ -532,10 +532,12 @@ __global__ __launch_bounds__(512) void pf_scan_kernel(PfArgs a) {
   // per round: the score read back by register index, a slot from the row's LDS counter (shared by
   // the four waves of the row group), the store. Slots past LCAP are not written; the count then
   // tells the finish that the row overflowed.
-  // (the lane's stage holds its 16 scores in register order; the row counters are kept in the
-  // order rg, g, register, so that register r of a lane finds its row's counter at cnt_l[r])
-  float* const sst_l = sstage + (wave * 64 + lane) * 16;
-  uint32_t* const cnt_l = rowcnt + rg * 64 + grp * 16;
+  // (a wave's stage holds score register u of its lanes as 16-byte entries in lane order, so
+  // that the writes are conflict-free; the row counters are kept in the order rg, g, register,
+  // padded to 17 per g, so that register r of a lane finds its row's counter at cnt_l[r] and the
+  // four groups' counters fall in different LDS banks)
+  float* const sst_w = sstage + wave * 1024;
+  uint32_t* const cnt_l = rowcnt + rg * 68 + grp * 17;
   const uint32_t kc0 = (uint32_t)(kg * 16 + m);
   uint2* const survb = a.w.surv + grow0 * LCAP;
   uint32_t fail = 0u;
@@ -549,12 +551,12 @@ __global__ __launch_bounds__(512) void pf_scan_kernel(PfArgs a) {
   {                                                                                                \
     uint32_t bits = ~fail & 0xFFFFu;                                                               \
     if (bits) {                                                                                    \
-      _Pragma("unroll") for (int u = 0; u < 4; ++u) *(f32x4_t*)(sst_l + 4 * u) = ACC[u];          \
+      _Pragma("unroll") for (int u = 0; u < 4; ++u) ((f32x4_t*)sst_w)[u * 64 + lane] = ACC[u];     \
       const uint32_t key_ = kc0 + (uint32_t)(t) * PF_KEYS;                                         \
       do {                                                                                         \
         const int r_ = __builtin_ctz(bits);                                                        \
         bits &= bits - 1u;                                                                         \
-        const float x_ = sst_l[r_];                                                                \
+        const float x_ = sst_w[((r_ >> 2) * 64 + lane) * 4 + (r_ & 3)];                            \
         const uint32_t slot_ = atomicAdd(&cnt_l[r_], 1u);                                          \
         asm volatile("" : : "v"(x_)); /* both LDS requests in flight before the first wait */      \
         const uint32_t row_ = (uint32_t)(row_base + r_ + 3 * (r_ & 12));                           \
@@ -576,10 +578,10 @@ __global__ __launch_bounds__(512) void pf_scan_kernel(PfArgs a) {
 
   // the count word: entries from the front of the row's slots in its low 16 bits, 0 in the high
   // 16 bits; a count above LCAP sends the row to the exact path. Block row R = 64 rg + 16 u + 4 g
-  // + e has its counter at 64 rg + 16 g + 4 u + e.
+  // + e has its counter at 68 rg + 17 g + 4 u + e.
   __syncthreads();
   if (tid < PF_ROWS && i0 + tid < a.n_q)
-    a.w.cnt[grow0 + tid] = min(rowcnt[(tid & 0x43) | ((tid & 12) << 2) | ((tid >> 2) & 12)], 0xFFFFu);
+    a.w.cnt[grow0 + tid] = min(rowcnt[(tid >> 6) * 68 + ((tid >> 2) & 3) * 17 + ((tid >> 4) & 3) * 4 + (tid & 3)], 0xFFFFu);
 #undef PF_INTERIOR
 #undef PF_LOAD
 #undef PF_STORE
