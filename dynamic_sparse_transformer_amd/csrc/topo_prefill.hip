@@ -910,6 +910,68 @@ __device__ int pf_exact_row(PfRowSmem* sm, const PfArgs& a, const unsigned char*
 }
 
 // Ascending bitonic sort of the 64 E values of a wave (value i = x[i / 64] of lane i % 64).
+// The value of lane (lane ^ S) for S = 1 .. 32 without an address computation: DPP quad
+// permutes (1, 2), row shifts by 4 chosen by lane bit 2 (4), a row rotation by 8 (8), an LDS
+// swizzle (16), and the gfx950 half-wave swap (32; its two results hold, per lane, the values of
+// lanes l mod 32 and l mod 32 + 32).
+template <int S>
+__device__ __forceinline__ uint32_t lane_xor_u32(uint32_t x) {
+  const int v = (int)x;
+  if constexpr (S == 1) return (uint32_t)__builtin_amdgcn_update_dpp(v, v, 0xB1, 0xF, 0xF, false);
+  else if constexpr (S == 2) return (uint32_t)__builtin_amdgcn_update_dpp(v, v, 0x4E, 0xF, 0xF, false);
+  else if constexpr (S == 4) {
+    const int up = __builtin_amdgcn_update_dpp(v, v, 0x104, 0xF, 0xF, false);  // lane + 4
+    const int dn = __builtin_amdgcn_update_dpp(v, v, 0x114, 0xF, 0xF, false);  // lane - 4
+    return (uint32_t)((threadIdx.x & 4) ? dn : up);
+  } else if constexpr (S == 8) return (uint32_t)__builtin_amdgcn_update_dpp(v, v, 0x128, 0xF, 0xF, false);
+  else if constexpr (S == 16) return (uint32_t)__builtin_amdgcn_ds_swizzle(v, 0x401F);
+  else {
+    static_assert(S == 32, "lane_xor_u32: S in 1, 2, 4, 8, 16, 32");
+    const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+    return (threadIdx.x & 32) ? r[0] : r[1];
+  }
+}
+template <int S>
+__device__ __forceinline__ float lane_xor_f32(float x) {
+  return __uint_as_float(lane_xor_u32<S>(__float_as_uint(x)));
+}
+__device__ __forceinline__ float wave_sum_fast(float x) {
+  x += lane_xor_f32<1>(x);
+  x += lane_xor_f32<2>(x);
+  x += lane_xor_f32<4>(x);
+  x += lane_xor_f32<8>(x);
+  x += lane_xor_f32<16>(x);
+  x += lane_xor_f32<32>(x);
+  return x;
+}
+__device__ __forceinline__ float wave_max_fast(float x) {
+  x = fmaxf(x, lane_xor_f32<1>(x));
+  x = fmaxf(x, lane_xor_f32<2>(x));
+  x = fmaxf(x, lane_xor_f32<4>(x));
+  x = fmaxf(x, lane_xor_f32<8>(x));
+  x = fmaxf(x, lane_xor_f32<16>(x));
+  x = fmaxf(x, lane_xor_f32<32>(x));
+  return x;
+}
+template <int S>
+__device__ __forceinline__ void sort_stage_u32(uint32_t& x, int size) {
+  const int lane = threadIdx.x & 63;
+  const uint32_t y = lane_xor_u32<S>(x);
+  x = (((lane & size) == 0) == ((lane & S) == 0)) ? min(x, y) : max(x, y);
+}
+// Ascending bitonic sort of one value per lane across the wave, every exchange without LDS
+// addresses (see lane_xor_u32).
+__device__ __forceinline__ void wave_sort64_asc_u32(uint32_t& x) {
+  sort_stage_u32<1>(x, 2);
+  sort_stage_u32<2>(x, 4);  sort_stage_u32<1>(x, 4);
+  sort_stage_u32<4>(x, 8);  sort_stage_u32<2>(x, 8);  sort_stage_u32<1>(x, 8);
+  sort_stage_u32<8>(x, 16); sort_stage_u32<4>(x, 16); sort_stage_u32<2>(x, 16); sort_stage_u32<1>(x, 16);
+  sort_stage_u32<16>(x, 32); sort_stage_u32<8>(x, 32); sort_stage_u32<4>(x, 32); sort_stage_u32<2>(x, 32);
+  sort_stage_u32<1>(x, 32);
+  sort_stage_u32<32>(x, 64); sort_stage_u32<16>(x, 64); sort_stage_u32<8>(x, 64); sort_stage_u32<4>(x, 64);
+  sort_stage_u32<2>(x, 64); sort_stage_u32<1>(x, 64);
+}
+
 template <int E>
 __device__ __forceinline__ void wave_sort_asc_u32(uint32_t (&x)[E]) {
   const int lane = threadIdx.x & 63;
@@ -1165,6 +1227,21 @@ __device__ void pf_row(const PfArgs& a, PfRowSmem* sm, size_t grow) {
 
   // ---- set: {0} u window u T, ascending
   const int count = anchor + nwin + nt;
+  if (BF16 && nt <= 64) {
+    // The top-k positions sorted across the wave (distinct keys; empty slots sort last), then
+    // every part of the set stored straight to the output: the t-th smallest position at slot
+    // anchor + t, after the window if it lies past p; the window after the positions below it.
+    uint32_t x = lane < nt ? (uint32_t)sm->tidx[lane] : 0xFFFFFFFFu;
+    wave_sort64_asc_u32(x);
+    const int tlo = __popcll(__ballot(lane < nt && (int64_t)x < w_lo));
+    if (a.sel_idx) {
+      int32_t* dst = a.sel_idx + grow * (size_t)a.set_cap;
+      if (anchor && lane == 0) dst[0] = 0;
+      if (lane < nt) dst[anchor + lane + ((int64_t)x > p ? nwin : 0)] = (int32_t)x;
+      for (int t = lane; t < nwin; t += 64) dst[anchor + tlo + t] = (int32_t)(w_lo + t);
+      for (int t = count + lane; t < a.set_cap; t += 64) dst[t] = -1;
+    }
+  } else {
   int tlo = 0;
   for (int t = lane; t < nt; t += 64) tlo += sm->tidx[t] < w_lo;
   tlo = wave_sum_i32(tlo);
@@ -1175,16 +1252,10 @@ __device__ void pf_row(const PfArgs& a, PfRowSmem* sm, size_t grow) {
   if (BF16 && nt <= 128) {
     // the top-k positions sorted (distinct keys; empty slots sort last): the t-th smallest goes
     // to slot anchor + t, after the window if it lies past p
-    if (nt <= 64) {
-      uint32_t x[1] = {lane < nt ? (uint32_t)sm->tidx[lane] : 0xFFFFFFFFu};
-      wave_sort_asc_u32<1>(x);
-      if (lane < nt) sm->cidx[anchor + lane + ((int64_t)x[0] > p ? nwin : 0)] = (int32_t)x[0];
-    } else {
-      uint32_t x[2] = {(uint32_t)sm->tidx[lane], lane + 64 < nt ? (uint32_t)sm->tidx[lane + 64] : 0xFFFFFFFFu};
-      wave_sort_asc_u32<2>(x);
-      sm->cidx[anchor + lane + ((int64_t)x[0] > p ? nwin : 0)] = (int32_t)x[0];
-      if (lane + 64 < nt) sm->cidx[anchor + lane + 64 + ((int64_t)x[1] > p ? nwin : 0)] = (int32_t)x[1];
-    }
+    uint32_t x[2] = {(uint32_t)sm->tidx[lane], lane + 64 < nt ? (uint32_t)sm->tidx[lane + 64] : 0xFFFFFFFFu};
+    wave_sort_asc_u32<2>(x);
+    sm->cidx[anchor + lane + ((int64_t)x[0] > p ? nwin : 0)] = (int32_t)x[0];
+    if (lane + 64 < nt) sm->cidx[anchor + lane + 64 + ((int64_t)x[1] > p ? nwin : 0)] = (int32_t)x[1];
   } else {
     // rank of each top-k position among the others
     for (int t = lane; t < nt; t += 64) {
@@ -1205,6 +1276,7 @@ __device__ void pf_row(const PfArgs& a, PfRowSmem* sm, size_t grow) {
   if (a.sel_idx) {
     int32_t* dst = a.sel_idx + grow * (size_t)a.set_cap;
     for (int t = lane; t < a.set_cap; t += 64) dst[t] = t < count ? sm->cidx[t] : -1;
+  }
   }
   if (a.sel_count && lane == 0) a.sel_count[grow] = count;
   if (!a.out) return;
@@ -1238,17 +1310,19 @@ __device__ void pf_row(const PfArgs& a, PfRowSmem* sm, size_t grow) {
 #pragma unroll
     for (int e = 0; e < EPC / 4; ++e)
       wo[e] = a.win && gq == 0 ? ((const float4*)(a.w.win_o + grow * D + cc * EPC))[e] : make_float4(0.f, 0.f, 0.f, 0.f);
+    // (the weights go to the float32 array wf, which the bf16 path leaves unused otherwise)
+    float* const wf = (float*)sm->cw;
     float zmax = mz.x;
     for (int t = lane; t < ne; t += 64) zmax = fmaxf(zmax, sc * (float)sm->ts[t]);
-    zmax = wave_max_f32(zmax);
+    zmax = wave_max_fast(zmax);
     float zsum = 0.f;
     for (int t = lane; t < ne; t += 64) {
       const float w = __expf(sc * (float)sm->ts[t] - zmax);
-      sm->ts[t] = (double)w;
+      wf[t] = w;
       zsum += w;
     }
     const float fw = a.win ? __expf(mz.x - zmax) : 0.f;
-    zsum = wave_sum_f32(zsum) + fw * mz.y;
+    zsum = wave_sum_fast(zsum) + fw * mz.y;
     __builtin_amdgcn_wave_barrier();
     float acc[EPC];
 #pragma unroll
@@ -1276,14 +1350,17 @@ __device__ void pf_row(const PfArgs& a, PfRowSmem* sm, size_t grow) {
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int t = t0 + u * RPI + gq;
-        w[u] = t < ne ? (float)sm->ts[t] : 0.f;
+        w[u] = t < ne ? wf[t] : 0.f;
       }
       accumulate(x, w);
     }
+    // the lane groups' sums (groups of LPR lanes hold the same output elements)
 #pragma unroll
-    for (int o = LPR; o < 64; o <<= 1)
-#pragma unroll
-      for (int e = 0; e < EPC; ++e) acc[e] += __shfl_xor(acc[e], o);
+    for (int e = 0; e < EPC; ++e) {
+      if constexpr (LPR <= 8) acc[e] += lane_xor_f32<8>(acc[e]);
+      if constexpr (LPR <= 16) acc[e] += lane_xor_f32<16>(acc[e]);
+      acc[e] += lane_xor_f32<32>(acc[e]);
+    }
     if (gq == 0) {
       if (a.win) {
 #pragma unroll
