@@ -494,16 +494,24 @@ __global__ __launch_bounds__(512) void pf_scan_kernel(PfArgs a) {
       c[gq] = 0;
     }
 #pragma unroll
+    // (per step, the four groups' counts, at most 128 each, travel in the four bytes of one word
+    // through the 16-lane sum; a lane counts the values below the candidate from the sign bits
+    // of the differences)
     for (int bit = 6; bit >= 0; --bit) {
+      uint32_t packed = 0u;
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq) {
+        const float cand = fmaf((float)(c[gq] | (1 << bit)), step[gq], lo[gq]);
+        uint32_t below = 0u;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) below = __builtin_amdgcn_alignbit(below, __float_as_uint(v[gq][j] - cand), 31);
+        packed |= (uint32_t)(8 - __popc(below & 0xFFu)) << (8 * gq);
+      }
+      packed = pf_row16<0>(packed);
 #pragma unroll
       for (int gq = 0; gq < 4; ++gq) {
         const int cc = c[gq] | (1 << bit);
-        const float cand = fmaf((float)cc, step[gq], lo[gq]);
-        int cnt = 0;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) cnt += v[gq][j] >= cand;
-        cnt = pf_row16<0>(cnt);
-        c[gq] = cnt >= a.topk ? cc : c[gq];
+        c[gq] = (int)((packed >> (8 * gq)) & 0xFFu) >= a.topk ? cc : c[gq];
       }
     }
 #pragma unroll
@@ -1006,9 +1014,19 @@ __device__ void pf_row(const PfArgs& a, PfRowSmem* sm, size_t grow) {
   // a key row is LPR lanes x 16 bytes, so one load instruction covers RPI rows
   constexpr int LPR = RB / 16, RPI = 64 / LPR, EPC = BF16 ? 8 : 4;
   const int lane = threadIdx.x & 63;
-  const size_t bh = grow / (size_t)a.n_q;
-  const int64_t i = (int64_t)(grow - bh * (size_t)a.n_q);
-  const int b = (int)(bh / a.Hq), h = (int)(bh - (size_t)b * a.Hq), g = h / a.G;
+  // (32-bit divisions when the rows allow)
+  size_t bh;
+  int64_t i;
+  if (a.rows < ((int64_t)1 << 31)) {
+    const uint32_t g32 = (uint32_t)grow, nq = (uint32_t)a.n_q, bh32 = g32 / nq;
+    bh = bh32;
+    i = (int64_t)(g32 - bh32 * nq);
+  } else {
+    bh = grow / (size_t)a.n_q;
+    i = (int64_t)(grow - bh * (size_t)a.n_q);
+  }
+  const int b = (int)((uint32_t)bh / (uint32_t)a.Hq), h = (int)((uint32_t)bh - (uint32_t)b * (uint32_t)a.Hq),
+            g = (int)((uint32_t)h / (uint32_t)a.G);
   const unsigned char* kb = a.k + ((size_t)b * a.Hkv + g) * (size_t)a.n * RB;
   const unsigned char* vb = a.v ? a.v + ((size_t)b * a.Hkv + g) * (size_t)a.n * RB : nullptr;
   const int64_t p = a.q_pos0 + i;
@@ -1425,7 +1443,8 @@ __device__ void pf_row(const PfArgs& a, PfRowSmem* sm, size_t grow) {
 template <int D, bool BF16>
 __global__ __launch_bounds__(256) void pf_finish_kernel(PfArgs a) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
-  const int wave = threadIdx.x >> 6;
+  // (the wave index through readfirstlane: the row's indices stay in scalar registers)
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   PfRowSmem smv;
   smv.carve(smem_raw + wave * a.wave_smem, a.slot, a.topk, a.set_cap);
   const size_t grow = (size_t)xcd_job(blockIdx.x, gridDim.x) * 4 + wave;  // (b*Hq + h) * n_q + i
