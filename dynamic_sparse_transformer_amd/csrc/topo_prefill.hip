@@ -234,7 +234,8 @@ __global__ __launch_bounds__(512) void pf_scan_kernel(PfArgs a) {
   __shared__ __align__(16) unsigned char ktiles[SMEM];  // key tiles; the thresholds' values between the phases
   __shared__ __align__(16) float sstage[8 * 64 * 16];    // phase 2: each lane's 16 scores of a step
   __shared__ float lthk[PF_ROWS];
-  __shared__ uint32_t rowcnt[2 * 4 * 17];  // the rows' list counters (see phase 2)
+  // the rows' list counters (see phase 2), then at +136 the byte offset of each counter's row list
+  __shared__ uint32_t rowcnt[2 * 2 * 4 * 17];
   __shared__ uint32_t kmax_blk;  // float bits of the largest key norm the block has staged
 
   // (the wave index through readfirstlane, so that the compiler keeps what derives from it in
@@ -351,11 +352,14 @@ __global__ __launch_bounds__(512) void pf_scan_kernel(PfArgs a) {
   }
 // One step t of a pass: the scores of tile t are in ACC_CUR (issued a step earlier); the matrix
 // cores score tile t+1 into ACC_NEXT while the vector units run the per-score work on tile t:
-// PART for each register of ACC_CUR, PER of them after each matrix instruction. Tile
-// t + PF_H + 1 then goes from its registers to its LDS buffer and tile t + PF_H + 3 is
-// requested. Scheduling fences keep that order: left to itself the compiler puts the vector work
-// before the matrix instructions.
-#define PF_STEP(PART, t, ACC_CUR, ACC_NEXT, SET0, SET1)                                            \
+// PART for each register of ACC_CUR, PER of them after each matrix instruction, then HOOK with
+// the instruction's index (phase 2 runs the previous tile's appends there). Tile t + PF_H + 1
+// then goes from its registers to its LDS buffer and tile t + PF_H + 3 is requested. Scheduling
+// fences keep that order: left to itself the compiler puts the vector work before the matrix
+// instructions.
+  constexpr int NMMA = 4 * SL;  // matrix instructions per step
+#define PF_NOHOOK(i)
+#define PF_STEP(PART, HOOK, t, ACC_CUR, ACC_NEXT, SET0, SET1)                                      \
   {                                                                                                \
   PF_MASK(ACC_CUR, t)                                                                              \
   {                                                                                                \
@@ -369,6 +373,7 @@ __global__ __launch_bounds__(512) void pf_scan_kernel(PfArgs a) {
         ACC_NEXT[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[u][s], __builtin_bit_cast(bf16x8_t, kf[s]), ACC_NEXT[u], 0, 0, 0); \
         __builtin_amdgcn_sched_barrier(0);                                                         \
         _Pragma("unroll") for (int e = 0; e < PER; ++e) PART(ACC_CUR, t, (s * 4 + u) * PER + e)   \
+        HOOK(s * 4 + u)                                                                            \
         __builtin_amdgcn_sched_barrier(0);                                                         \
       }                                                                                            \
   }                                                                                                \
@@ -388,7 +393,12 @@ __global__ __launch_bounds__(512) void pf_scan_kernel(PfArgs a) {
 #pragma unroll
     for (int s = 0; s < SL; ++s) qa[u][s] = __builtin_bit_cast(bf16x8_t, *(const uint4*)(qrow + s * 16));
   }
-  if (tid < 2 * 4 * 17) rowcnt[tid] = 0u;
+  if (tid < 2 * 4 * 17) {
+    // counter rg * 68 + g * 17 + r (r < 16) is that of block row 64 rg + 4 g + 16 (r >> 2) + (r & 3)
+    const uint32_t rr = (uint32_t)(tid % 17), row = (uint32_t)(tid / 68) * 64u + (uint32_t)((tid % 68) / 17) * 4u + rr + 3u * (rr & 12u);
+    rowcnt[tid] = 0u;
+    rowcnt[2 * 4 * 17 + tid] = rr < 16u ? row * LCAP * 8u : 0u;
+  }
   if (tid == 0) kmax_blk = 0u;
   // |q| of the rows whose threshold this lane helps to find (wave w takes rows 16 w .. +16);
   // loaded unconditionally from a clamped index, so that no load waits on another
@@ -428,8 +438,8 @@ __global__ __launch_bounds__(512) void pf_scan_kernel(PfArgs a) {
 #pragma unroll
     for (int gq = 0; gq < 4; ++gq) asm volatile("" : "+v"(qn_g[gq]));
     for (int t = 0; t < ntiles; t += PF_H) {
-      PF_STEP(PF_PART1, t, accA, accB, r00, r01)
-      PF_STEP(PF_PART1, t + 1, accB, accA, r10, r11)
+      PF_STEP(PF_PART1, PF_NOHOOK, t, accA, accB, r00, r01)
+      PF_STEP(PF_PART1, PF_NOHOOK, t + 1, accB, accA, r10, r11)
       __syncthreads();
     }
   }
@@ -533,55 +543,90 @@ __global__ __launch_bounds__(512) void pf_scan_kernel(PfArgs a) {
   for (int r = 0; r < 16; ++r) tk[r] = lthk[row_base + 16 * (r >> 2) + (r & 3)];
 
   // ---- phase 2: every candidate key whose fast score reaches its row's bound goes to the row's
-  // list in global memory, with its score. A lane first gathers the test results of its 16
-  // registers into bit r of `fail`'s complement: the test x >= T is the sign of x - T (T finite or
-  // +inf, x finite or -inf), shifted in by v_alignbit from register 15 down to 0. A lane with
-  // passing registers then writes its 16 scores to its own place in LDS and appends its keys one
-  // per round: the score read back by register index, a slot from the row's LDS counter (shared by
-  // the four waves of the row group), the store. Slots past LCAP are not written; the count then
-  // tells the finish that the row overflowed.
-  // (a wave's stage holds score register u of its lanes as 16-byte entries in lane order, so
-  // that the writes are conflict-free; the row counters are kept in the order rg, g, register,
-  // padded to 17 per g, so that register r of a lane finds its row's counter at cnt_l[r] and the
-  // four groups' counters fall in different LDS banks)
+  // list in global memory, with its score. A lane gathers the test results of its 16 registers
+  // into bit r of `fail`'s complement: the test x >= T is the sign of x - T (T finite or +inf, x
+  // finite or -inf), shifted in by v_alignbit from register 15 down to 0. At the end of step t a
+  // lane with passing registers writes its 16 scores to its own place in LDS; its keys are then
+  // appended one per round during step t + 1: the score read back by register index, a slot from
+  // the row's LDS counter (shared by the four waves of the row group), the store. Two rounds run
+  // between the matrix instructions of step t + 1 (their LDS round trips overlap the matrix
+  // work); a lane with more passing registers finishes them in a loop at the end of that step,
+  // before the stage is rewritten. Slots past LCAP are not written; the count then tells the
+  // finish that the row overflowed.
+  // (a wave's stage holds its lanes' score register r at r * 64 + lane, so that a lane finds
+  // register r with one shift-add and neither the writes nor the reads conflict; the row
+  // counters are kept in the order rg, g, register, padded to 17 per g, so that register r of a
+  // lane finds its row's counter at cnt_l[r], its row list's byte offset at cnt_l[r + 136], and
+  // the four groups' counters fall in different LDS banks)
   float* const sst_w = sstage + wave * 1024;
   uint32_t* const cnt_l = rowcnt + rg * 68 + grp * 17;
   const uint32_t kc0 = (uint32_t)(kg * 16 + m);
   uint2* const survb = a.w.surv + grow0 * LCAP;
   uint32_t fail = 0u;
+  uint32_t pend = 0u, pkey = 0u;  // the staged tile's passing registers not yet appended, its key
 #define PF_PART2(ACC, t, r)                                                                        \
   {                                                                                                \
     const int r_ = 15 - (r);                                                                       \
     fail = __builtin_amdgcn_alignbit((r) == 0 ? 0u : fail, __float_as_uint(ACC[r_ >> 2][r_ & 3] - tk[r_]), 31); \
     asm volatile("" : "+v"(fail));                                                                 \
   }
+// one append round of the staged tile: issue (score and slot requested together), then store
+#define PF_ROUND_ISSUE(X)                                                                          \
+  X##_on = pend != 0u;                                                                             \
+  if (X##_on) {                                                                                    \
+    const uint32_t r_ = (uint32_t)__builtin_ctz(pend);                                             \
+    pend &= pend - 1u;                                                                             \
+    X##_x = sst_w[r_ * 64u + lane];                                                                \
+    X##_slot = atomicAdd(&cnt_l[r_], 1u);                                                          \
+    X##_off = cnt_l[r_ + 2 * 4 * 17];                                                              \
+  }
+#define PF_ROUND_STORE(X)                                                                          \
+  if (X##_on && X##_slot < LCAP)                                                                   \
+    *(uint2*)((char*)survb + (X##_off + X##_slot * 8u)) = make_uint2(__float_as_uint(X##_x), pkey);
+  // (round A is issued after matrix instruction 1 and stored after NMMA / 2 + 1; round B after
+  // NMMA / 4 and NMMA - 1 - NMMA / 8: a few matrix instructions cover each LDS round trip)
+  bool ra_on = false, rb_on = false;
+  float ra_x = 0.f, rb_x = 0.f;
+  uint32_t ra_slot = 0u, rb_slot = 0u, ra_off = 0u, rb_off = 0u;
+#define PF_HOOK2(i)                                                                                \
+  if ((i) == 1) { PF_ROUND_ISSUE(ra) }                                                             \
+  if ((i) == NMMA / 4) { PF_ROUND_ISSUE(rb) }                                                      \
+  if ((i) == NMMA / 2 + 1) { PF_ROUND_STORE(ra) }                                                  \
+  if ((i) == NMMA - 1 - NMMA / 8) { PF_ROUND_STORE(rb) }
+// the rest of the staged tile's appends, one per round
+#define PF_DRAIN()                                                                                 \
+  if (pend) {                                                                                      \
+    do {                                                                                           \
+      const uint32_t r_ = (uint32_t)__builtin_ctz(pend);                                           \
+      pend &= pend - 1u;                                                                           \
+      const float x_ = sst_w[r_ * 64u + lane];                                                     \
+      const uint32_t slot_ = atomicAdd(&cnt_l[r_], 1u);                                            \
+      const uint32_t off_ = cnt_l[r_ + 2 * 4 * 17];                                                \
+      if (slot_ < LCAP)                                                                            \
+        *(uint2*)((char*)survb + (off_ + slot_ * 8u)) = make_uint2(__float_as_uint(x_), pkey);       \
+    } while (pend);                                                                                \
+  }
+// end of step t: finish the previous tile's appends, then stage this tile's passing scores
 #define PF_POST2(ACC, t)                                                                           \
   {                                                                                                \
-    uint32_t bits = ~fail & 0xFFFFu;                                                               \
-    if (bits) {                                                                                    \
-      _Pragma("unroll") for (int u = 0; u < 4; ++u) ((f32x4_t*)sst_w)[u * 64 + lane] = ACC[u];     \
-      const uint32_t key_ = kc0 + (uint32_t)(t) * PF_KEYS;                                         \
-      do {                                                                                         \
-        const int r_ = __builtin_ctz(bits);                                                        \
-        bits &= bits - 1u;                                                                         \
-        const float x_ = sst_w[((r_ >> 2) * 64 + lane) * 4 + (r_ & 3)];                            \
-        const uint32_t slot_ = atomicAdd(&cnt_l[r_], 1u);                                          \
-        asm volatile("" : : "v"(x_)); /* both LDS requests in flight before the first wait */      \
-        const uint32_t row_ = (uint32_t)(row_base + r_ + 3 * (r_ & 12));                           \
-        if (slot_ < LCAP)                                                                          \
-          *(uint2*)((char*)survb + (__umul24(row_, LCAP) + slot_) * 8u) = make_uint2(__float_as_uint(x_), key_); \
-      } while (bits);                                                                              \
+    PF_DRAIN()                                                                                     \
+    const uint32_t bits_ = ~fail & 0xFFFFu;                                                        \
+    if (bits_) {                                                                                   \
+      _Pragma("unroll") for (int r = 0; r < 16; ++r) sst_w[r * 64 + lane] = ACC[r >> 2][r & 3];    \
     }                                                                                              \
+    pend = bits_;                                                                                  \
+    pkey = kc0 + (uint32_t)(t) * PF_KEYS;                                                          \
   }
   if (ntiles > 0) {
     PF_PRO_FINISH(accA)
     for (int t = 0; t < ntiles; t += PF_H) {
-      PF_STEP(PF_PART2, t, accA, accB, r00, r01)
+      PF_STEP(PF_PART2, PF_HOOK2, t, accA, accB, r00, r01)
       PF_POST2(accA, t)
-      PF_STEP(PF_PART2, t + 1, accB, accA, r10, r11)
+      PF_STEP(PF_PART2, PF_HOOK2, t + 1, accB, accA, r10, r11)
       PF_POST2(accB, t + 1)
       __syncthreads();
     }
+    PF_DRAIN()
   }
 
   // the count word: entries from the front of the row's slots in its low 16 bits, 0 in the high
@@ -601,6 +646,11 @@ __global__ __launch_bounds__(512) void pf_scan_kernel(PfArgs a) {
 #undef PF_PART1
 #undef PF_PART2
 #undef PF_POST2
+#undef PF_DRAIN
+#undef PF_HOOK2
+#undef PF_ROUND_ISSUE
+#undef PF_ROUND_STORE
+#undef PF_NOHOOK
 }
 
 // ---------------------------------------------------------------------------------------------
