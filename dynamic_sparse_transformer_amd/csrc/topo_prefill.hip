@@ -545,14 +545,14 @@ __global__ __launch_bounds__(512) void pf_scan_kernel(PfArgs a) {
   // ---- phase 2: every candidate key whose fast score reaches its row's bound goes to the row's
   // list in global memory, with its score. A lane gathers the test results of its 16 registers
   // into bit r of `fail`'s complement: the test x >= T is the sign of x - T (T finite or +inf, x
-  // finite or -inf), shifted in by v_alignbit from register 15 down to 0. At the end of step t a
-  // lane with passing registers writes its 16 scores to its own place in LDS; its keys are then
-  // appended one per round during step t + 1: the score read back by register index, a slot from
-  // the row's LDS counter (shared by the four waves of the row group), the store. Two rounds run
-  // between the matrix instructions of step t + 1 (their LDS round trips overlap the matrix
-  // work); a lane with more passing registers finishes them in a loop at the end of that step,
-  // before the stage is rewritten. Slots past LCAP are not written; the count then tells the
-  // finish that the row overflowed.
+  // finite or -inf), shifted in by v_alignbit from register 15 down to 0. At the end of step t
+  // every lane writes its 16 scores to its own place in LDS; the keys of its passing registers
+  // are then appended one per round during step t + 1: the score read back by register index, a
+  // slot from the row's LDS counter (shared by the four waves of the row group), the store. Two
+  // rounds run between the matrix instructions of step t + 1 (their LDS round trips overlap the
+  // matrix work); a lane with more passing registers finishes them in a loop at the end of that
+  // step, before the stage is rewritten. Slots past LCAP are not written; the count then tells
+  // the finish that the row overflowed.
   // (a wave's stage holds its lanes' score register r at r * 64 + lane, so that a lane finds
   // register r with one shift-add and neither the writes nor the reads conflict; the row
   // counters are kept in the order rg, g, register, padded to 17 per g, so that register r of a
@@ -606,15 +606,13 @@ __global__ __launch_bounds__(512) void pf_scan_kernel(PfArgs a) {
         *(uint2*)((char*)survb + (off_ + slot_ * 8u)) = make_uint2(__float_as_uint(x_), pkey);       \
     } while (pend);                                                                                \
   }
-// end of step t: finish the previous tile's appends, then stage this tile's passing scores
+// end of step t: finish the previous tile's appends, then stage this tile's scores (every lane:
+// with no branch around the writes the LDS waits that follow stay exact)
 #define PF_POST2(ACC, t)                                                                           \
   {                                                                                                \
     PF_DRAIN()                                                                                     \
-    const uint32_t bits_ = ~fail & 0xFFFFu;                                                        \
-    if (bits_) {                                                                                   \
-      _Pragma("unroll") for (int r = 0; r < 16; ++r) sst_w[r * 64 + lane] = ACC[r >> 2][r & 3];    \
-    }                                                                                              \
-    pend = bits_;                                                                                  \
+    _Pragma("unroll") for (int r = 0; r < 16; ++r) sst_w[r * 64 + lane] = ACC[r >> 2][r & 3];      \
+    pend = ~fail & 0xFFFFu;                                                                        \
     pkey = kc0 + (uint32_t)(t) * PF_KEYS;                                                          \
   }
   if (ntiles > 0) {
