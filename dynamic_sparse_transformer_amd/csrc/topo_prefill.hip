@@ -42,7 +42,7 @@ float prefill_eps_coef() { return PF_EPS_COEF; }
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 // LDS of the scan for the top-2 values of each row's lanes between the two phases. A row's list
 // of possible top-k keys holds k + 48 entries, at most 128 (the finish ranks two per lane).
-constexpr int PF_LIST_BYTES = PF_ROWS * 128 * 4;
+constexpr int PF_LIST_BYTES = PF_ROWS * 136 * 4;
 constexpr int PF_LCAP_MAX = 128;
 static int64_t pf_slot(int32_t k) { return k + 48 < PF_LCAP_MAX ? k + 48 : PF_LCAP_MAX; }
 
@@ -450,21 +450,24 @@ __global__ __launch_bounds__(512) void pf_scan_kernel(PfArgs a) {
   knmx = wave_max_f32(knmx);
   if (lane == 0) atomicMax(&kmax_blk, __float_as_uint(knmx));
 
-  // ---- thresholds: row R's 128 fast scores sit at tops[R][32 * kg + 2 * m + {0, 1}] (even
-  // entries: the lanes' best values, 64 distinct keys; odd entries: their second best). Each row
+  // ---- thresholds: row R's 128 fast scores sit at tops[136 R + 32 kg + 2 m + {0, 1}] (even
+  // entries: the lanes' best values, 64 distinct keys; odd entries: their second best; rows 136
+  // floats apart, so that the four lane groups' rows fall in different LDS banks). Each row
   // needs a lower bound x of the k-th largest of its 128 values such that few values lie between:
   // the largest x = lo + c (hi - lo) / 128, c = 0..127, that at least k values reach (a bitwise
   // search over c, monotone in c), where hi is the largest value and lo a known lower bound of
   // the k-th largest: for k <= 64 and 64 finite best values the smallest of them, else the
   // smallest finite value (if fewer than k values are finite every candidate stays). The bound is
   // at most (hi - lo) / 128 below the k-th largest, and it is never above it. A wave takes 16
-  // rows in four groups of four; the 16 lanes of a row hold 8 values each, counted lane by lane
-  // and summed over the row with DPP moves.
+  // rows in four groups of four; the 16 lanes of a row hold 8 values each (lane s: entries
+  // 4 s .. +4 and 64 + 4 s .. +4, so that each read is conflict-free), counted lane by lane and
+  // summed over the row with DPP moves.
+  static_assert(PF_ROWS * 136 * 4 <= SMEM, "the thresholds' values fit in the tile buffers");
   float* tops = (float*)ktiles;
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     const int row = row_base + 16 * (r >> 2) + (r & 3);
-    *(float2*)&tops[row * 128 + 32 * kg + 2 * m] = make_float2(m1[r], m2[r]);
+    *(float2*)&tops[row * 136 + 32 * kg + 2 * m] = make_float2(m1[r], m2[r]);
   }
   const int sub = lane & 15;
   __syncthreads();
@@ -475,8 +478,8 @@ __global__ __launch_bounds__(512) void pf_scan_kernel(PfArgs a) {
     bool ok[4];
 #pragma unroll
     for (int gq = 0; gq < 4; ++gq) {
-      const float* src = &tops[(wave * 16 + 4 * gq + (lane >> 4)) * 128 + 8 * sub];
-      const float4 x0 = *(const float4*)src, x1 = *(const float4*)(src + 4);
+      const float* src = &tops[(wave * 16 + 4 * gq + (lane >> 4)) * 136 + 4 * sub];
+      const float4 x0 = *(const float4*)src, x1 = *(const float4*)(src + 64);
       v[gq][0] = x0.x; v[gq][1] = x0.y; v[gq][2] = x0.z; v[gq][3] = x0.w;
       v[gq][4] = x1.x; v[gq][5] = x1.y; v[gq][6] = x1.z; v[gq][7] = x1.w;
       float hi = -INFINITY, lo_best = INFINITY, lo_fin = INFINITY;
@@ -853,18 +856,27 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void p
 // pf_finish: one wave per query row (4 rows per 256-thread block), each wave with its own LDS
 // region laid out by PfRowSmem::carve for the call's k and 1 + W + k.
 constexpr int PF_FIN_SET = 4096;   // largest 1 + W + k served by the per-row finish
+// (tidx and cw have room for the V gather's padding: the entries rounded up to a multiple of
+// PF_GATHER, as positions and as float32 weights)
+constexpr int PF_GATHER = 136;
 struct PfRowSmem {
   double* qd;      // [128]
   double* rs;      // [slot + set_cap]: float64 scores of the row's list, window and anchor keys
   double* ts;      // [k + 1]
-  double* cw;      // [set_cap]
+  double* cw;      // [max(set_cap, PF_GATHER / 2)], or float32 weights [round_up(k + 1, PF_GATHER)]
   int32_t* ridx;   // [slot + 1]: the list, then the anchor
-  int32_t* tidx;   // [k + 1]
+  int32_t* tidx;   // [round_up(k + 1, PF_GATHER)]
   int32_t* cidx;   // [set_cap]
   uint32_t* hist;  // [256]
+  static __host__ __device__ size_t tcap(int k) { return ((size_t)k + PF_GATHER) / PF_GATHER * PF_GATHER; }
+  static __host__ __device__ size_t wcap(int k, int set_cap) {
+    const size_t w = (tcap(k) + 1) / 2;
+    return (size_t)set_cap > w ? (size_t)set_cap : w;
+  }
   static __host__ __device__ size_t bytes(int64_t slot, int k, int set_cap) {
     const size_t kk = (size_t)k + 1;
-    return 128 * 8 + ((size_t)slot + set_cap) * 8 + kk * 12 + (size_t)set_cap * 12 + ((size_t)slot + 1) * 4 + 256 * 4 + 64;
+    return 128 * 8 + ((size_t)slot + set_cap) * 8 + kk * 8 + wcap(k, set_cap) * 8 + tcap(k) * 4 +
+           (size_t)set_cap * 4 + ((size_t)slot + 1) * 4 + 256 * 4 + 64;
   }
   __device__ void carve(unsigned char* p, int64_t slot, int k, int set_cap) {
     const size_t kk = (size_t)k + 1;
@@ -875,11 +887,11 @@ struct PfRowSmem {
     ts = (double*)p;
     p += kk * 8;
     cw = (double*)p;
-    p += (size_t)set_cap * 8;
+    p += wcap(k, set_cap) * 8;
     ridx = (int32_t*)p;
     p += ((size_t)slot + 1) * 4;
     tidx = (int32_t*)p;
-    p += kk * 4;
+    p += tcap(k) * 4;
     cidx = (int32_t*)p;
     p += (size_t)set_cap * 4;
     hist = (uint32_t*)(((uintptr_t)p + 15) & ~(uintptr_t)15);
@@ -972,14 +984,16 @@ __device__ int pf_exact_row(PfRowSmem* sm, const PfArgs& a, const unsigned char*
 // lanes l mod 32 and l mod 32 + 32).
 template <int S>
 __device__ __forceinline__ uint32_t lane_xor_u32(uint32_t x) {
+  // (every lane reads a lane that exists for 1, 2 and 8; for 4 each lane keeps the shift whose
+  // source exists, so the zero that bound_ctrl gives a missing source is never used)
   const int v = (int)x;
-  if constexpr (S == 1) return (uint32_t)__builtin_amdgcn_update_dpp(v, v, 0xB1, 0xF, 0xF, false);
-  else if constexpr (S == 2) return (uint32_t)__builtin_amdgcn_update_dpp(v, v, 0x4E, 0xF, 0xF, false);
+  if constexpr (S == 1) return (uint32_t)__builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, true);
+  else if constexpr (S == 2) return (uint32_t)__builtin_amdgcn_mov_dpp(v, 0x4E, 0xF, 0xF, true);
   else if constexpr (S == 4) {
-    const int up = __builtin_amdgcn_update_dpp(v, v, 0x104, 0xF, 0xF, false);  // lane + 4
-    const int dn = __builtin_amdgcn_update_dpp(v, v, 0x114, 0xF, 0xF, false);  // lane - 4
+    const int up = __builtin_amdgcn_mov_dpp(v, 0x104, 0xF, 0xF, true);  // lane + 4
+    const int dn = __builtin_amdgcn_mov_dpp(v, 0x114, 0xF, 0xF, true);  // lane - 4
     return (uint32_t)((threadIdx.x & 4) ? dn : up);
-  } else if constexpr (S == 8) return (uint32_t)__builtin_amdgcn_update_dpp(v, v, 0x128, 0xF, 0xF, false);
+  } else if constexpr (S == 8) return (uint32_t)__builtin_amdgcn_mov_dpp(v, 0x128, 0xF, 0xF, true);
   else if constexpr (S == 16) return (uint32_t)__builtin_amdgcn_ds_swizzle(v, 0x401F);
   else {
     static_assert(S == 32, "lane_xor_u32: S in 1, 2, 4, 8, 16, 32");
@@ -1056,7 +1070,9 @@ __device__ __forceinline__ void wave_sort_asc_u32(uint32_t (&x)[E]) {
 // inside the band), the set in ascending order, then softmax and V sum over the anchor and the
 // top-k in float32, merged with the window's share from pf_window. float32 inputs: float64 canonical scores of the list, anchor and window, exact
 // rank of the list, float64 softmax and V sum over the whole set.
-template <int D, bool BF16>
+// OFF32: every byte offset into a kv head's rows fits in 32 bits (n * row bytes <= 2^32), so the
+// gathers take a 32-bit offset from the head's base address.
+template <int D, bool BF16, bool OFF32>
 __device__ void pf_row(const PfArgs& a, PfRowSmem* sm, size_t grow) {
   constexpr int RB = D * (BF16 ? 2 : 4);
   // a key row is LPR lanes x 16 bytes, so one load instruction covers RPI rows
@@ -1366,11 +1382,22 @@ __device__ void pf_row(const PfArgs& a, PfRowSmem* sm, size_t grow) {
     // are requested before the weights are computed, so that their memory latency overlaps the
     // softmax
     const float2 mz = a.win ? a.w.win_mz[grow] : make_float2(-INFINITY, 0.f);
+    // V row chunk of entry t. The entries are padded to a multiple of U * RPI with the first
+    // entry's position (and a zero weight below), so that no load waits behind a branch and
+    // every LDS index is a constant offset.
+    static_assert(PF_GATHER % (U * RPI) == 0, "gather padding");
+    const int npad = ne > 0 ? (ne + U * RPI - 1) / (U * RPI) * (U * RPI) : 0;
+    for (int t = ne + lane; t < npad; t += 64) sm->tidx[t] = sm->tidx[0];
+    __builtin_amdgcn_wave_barrier();
+    auto vrow = [&](int t) -> uint4 {
+      const uint32_t j = (uint32_t)sm->tidx[t];
+      if constexpr (OFF32) return *(const uint4*)(vb + (j * (uint32_t)RB + (uint32_t)(cc * 16)));
+      else return *(const uint4*)(vb + (size_t)j * RB + cc * 16);
+    };
     uint4 x[U];
+    if (ne > 0) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int t = u * RPI + gq;
-      x[u] = t < ne ? *(const uint4*)(vb + (size_t)sm->tidx[t] * RB + cc * 16) : make_uint4(0u, 0u, 0u, 0u);
+      for (int u = 0; u < U; ++u) x[u] = vrow(u * RPI + gq);
     }
     float4 wo[EPC / 4];
 #pragma unroll
@@ -1387,6 +1414,7 @@ __device__ void pf_row(const PfArgs& a, PfRowSmem* sm, size_t grow) {
       wf[t] = w;
       zsum += w;
     }
+    for (int t = ne + lane; t < npad; t += 64) wf[t] = 0.f;
     const float fw = a.win ? __expf(mz.x - zmax) : 0.f;
     zsum = wave_sum_fast(zsum) + fw * mz.y;
     __builtin_amdgcn_wave_barrier();
@@ -1407,17 +1435,11 @@ __device__ void pf_row(const PfArgs& a, PfRowSmem* sm, size_t grow) {
     for (int t0 = 0; t0 < ne; t0 += U * RPI) {
       if (t0 > 0) {
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-          const int t = t0 + u * RPI + gq;
-          x[u] = t < ne ? *(const uint4*)(vb + (size_t)sm->tidx[t] * RB + cc * 16) : make_uint4(0u, 0u, 0u, 0u);
-        }
+        for (int u = 0; u < U; ++u) x[u] = vrow(t0 + u * RPI + gq);
       }
       float w[U];
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int t = t0 + u * RPI + gq;
-        w[u] = t < ne ? wf[t] : 0.f;
-      }
+      for (int u = 0; u < U; ++u) w[u] = wf[t0 + u * RPI + gq];
       accumulate(x, w);
     }
     // the lane groups' sums (groups of LPR lanes hold the same output elements)
@@ -1487,8 +1509,9 @@ __device__ void pf_row(const PfArgs& a, PfRowSmem* sm, size_t grow) {
   }
 }
 
-// pf_finish: one wave per query row, 4 rows per block (consecutive rows of one head).
-template <int D, bool BF16>
+// pf_finish: one wave per query row, 4 rows per block (consecutive rows of one head). OFF32 as in
+// pf_row (chosen at launch: one row variant per kernel keeps the register count down).
+template <int D, bool BF16, bool OFF32>
 __global__ __launch_bounds__(256) void pf_finish_kernel(PfArgs a) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
   // (the wave index through readfirstlane: the row's indices stay in scalar registers)
@@ -1497,7 +1520,7 @@ __global__ __launch_bounds__(256) void pf_finish_kernel(PfArgs a) {
   smv.carve(smem_raw + wave * a.wave_smem, a.slot, a.topk, a.set_cap);
   const size_t grow = (size_t)xcd_job(blockIdx.x, gridDim.x) * 4 + wave;  // (b*Hq + h) * n_q + i
   if (grow >= (size_t)a.rows) return;
-  pf_row<D, BF16>(a, &smv, grow);
+  pf_row<D, BF16, OFF32>(a, &smv, grow);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -1536,10 +1559,13 @@ static hipError_t launch_pf_t(const PrefillLaunch& L, const PfArgs& pa, hipStrea
     }
   }
   const size_t smem = 4 * pa.wave_smem;
-  if (smem > 48 * 1024)
-    (void)hipFuncSetAttribute((const void*)pf_finish_kernel<D, BF16>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                              (int)smem);
-  hipLaunchKernelGGL((pf_finish_kernel<D, BF16>), dim3((unsigned)((rows + 3) / 4), 1), dim3(256), smem, s, pa);
+  const bool off32 = (uint64_t)L.n * (uint64_t)(D * (BF16 ? 2 : 4)) <= 0xFFFFFFFFull;
+  const void* fk = off32 ? (const void*)pf_finish_kernel<D, BF16, true> : (const void*)pf_finish_kernel<D, BF16, false>;
+  if (smem > 48 * 1024) (void)hipFuncSetAttribute(fk, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+  if (off32)
+    hipLaunchKernelGGL((pf_finish_kernel<D, BF16, true>), dim3((unsigned)((rows + 3) / 4), 1), dim3(256), smem, s, pa);
+  else
+    hipLaunchKernelGGL((pf_finish_kernel<D, BF16, false>), dim3((unsigned)((rows + 3) / 4), 1), dim3(256), smem, s, pa);
   return hipGetLastError();
 }
 
