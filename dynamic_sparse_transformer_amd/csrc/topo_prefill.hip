@@ -105,20 +105,21 @@ PrefillView prefill_view(int32_t B, int32_t Hq, int32_t Hkv, int64_t n_q, int64_
 // |k| of every key, each score's bound taking its own two norms. A row is LPR lanes x 16 bytes
 // (coalesced, RPW rows per load instruction). The squares of bf16 values are exact in float32;
 // their float32 sum (8 terms per lane, then a tree over the LPR lanes) and sqrtf carry a relative
-// error far below the factor (1 + 2^-15) that rounds the norm up. Grid (blocks over the rows of
-// a head, heads); U rows per lane. With tmax, also the largest norm of each 64-row tile of a head
-// (a block covers whole tiles: 64 or 128 rows).
+// error far below the factor (1 + 2^-15) that rounds the norm up. One launch for both: blocks
+// [0, qblocks) take the query rows (one run of rows), the rest the keys, kblocks per kv head;
+// U rows per lane. For the keys, also the largest norm of each 64-row tile of a head (a block
+// covers whole tiles: 64 or 128 rows).
 template <int D, int U>
-__global__ __launch_bounds__(256) void pf_norm_kernel(const unsigned char* x, int64_t rows_per_head, float* norm,
-                                                      float* tmax) {
+__device__ __forceinline__ void pf_norm_rows(const unsigned char* x, int64_t rows_per_head, float* norm, float* tmax,
+                                             uint32_t bx, uint32_t by) {
   constexpr int RB = D * 2, LPR = RB / 16, RPW = 64 / LPR, BROWS = 4 * U * RPW;
   static_assert(BROWS % 64 == 0 && 64 % (U * RPW) == 0, "a wave's rows lie in one tile, a block covers whole tiles");
   __shared__ uint32_t tm[BROWS / 64];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, gq = lane / LPR, cc = lane % LPR;
   if (threadIdx.x < BROWS / 64) tm[threadIdx.x] = 0u;
   float wmax = 0.f;
-  const unsigned char* base = x + (size_t)blockIdx.y * (size_t)rows_per_head * RB;
-  const int64_t r0 = (int64_t)blockIdx.x * (4 * U * RPW) + (int64_t)wave * U * RPW + gq;
+  const unsigned char* base = x + (size_t)by * (size_t)rows_per_head * RB;
+  const int64_t r0 = (int64_t)bx * (4 * U * RPW) + (int64_t)wave * U * RPW + gq;
   uint4 v[U];
 #pragma unroll
   for (int u = 0; u < U; ++u) {
@@ -138,7 +139,7 @@ __global__ __launch_bounds__(256) void pf_norm_kernel(const unsigned char* x, in
     s2 = group_sum_f32<LPR>(s2);
     const float nrm = sqrtf(s2) * (1.0f + 0x1p-15f);
     const int64_t row = r0 + u * RPW;
-    if (cc == 0 && row < rows_per_head) norm[(size_t)blockIdx.y * rows_per_head + row] = nrm;
+    if (cc == 0 && row < rows_per_head) norm[(size_t)by * rows_per_head + row] = nrm;
     wmax = row < rows_per_head ? fmaxf(wmax, nrm) : wmax;
   }
   if (tmax) {
@@ -147,8 +148,19 @@ __global__ __launch_bounds__(256) void pf_norm_kernel(const unsigned char* x, in
     __syncthreads();
     if (lane == 0) atomicMax(&tm[wave * U * RPW / 64], __float_as_uint(wmax));
     __syncthreads();
-    const int64_t tiles = (rows_per_head + 63) / 64, t = (int64_t)blockIdx.x * (BROWS / 64) + threadIdx.x;
-    if (threadIdx.x < BROWS / 64 && t < tiles) tmax[(size_t)blockIdx.y * tiles + t] = __uint_as_float(tm[threadIdx.x]);
+    const int64_t tiles = (rows_per_head + 63) / 64, t = (int64_t)bx * (BROWS / 64) + threadIdx.x;
+    if (threadIdx.x < BROWS / 64 && t < tiles) tmax[(size_t)by * tiles + t] = __uint_as_float(tm[threadIdx.x]);
+  }
+}
+template <int D, int U>
+__global__ __launch_bounds__(256) void pf_norm_kernel(const unsigned char* q, int64_t q_rows, float* qn,
+                                                      const unsigned char* k, int64_t n, float* kn, float* ktmax,
+                                                      uint32_t qblocks, uint32_t kblocks) {
+  if (blockIdx.x < qblocks) {
+    pf_norm_rows<D, U>(q, q_rows, qn, nullptr, blockIdx.x, 0u);
+  } else {
+    const uint32_t j = blockIdx.x - qblocks;
+    pf_norm_rows<D, U>(k, n, kn, ktmax, j % kblocks, j / kblocks);
   }
 }
 
@@ -1532,10 +1544,13 @@ static hipError_t launch_pf_t(const PrefillLaunch& L, const PfArgs& pa, hipStrea
     if (!pa.exact_all && L.topk > 0) {
       // norms for the error bounds of the matrix-core scores (only the fast selection uses them)
       constexpr int RPW = 64 / (D * 2 / 16), QU = 4;  // rows per wave load; loads per lane
-      hipLaunchKernelGGL((pf_norm_kernel<D, QU>), dim3((unsigned)((rows + 4 * QU * RPW - 1) / (4 * QU * RPW)), 1), dim3(256),
-                         0, s, (const unsigned char*)L.q, (int64_t)rows, pa.w.qn, (float*)nullptr);
-      hipLaunchKernelGGL((pf_norm_kernel<D, QU>), dim3((unsigned)((L.n + 4 * QU * RPW - 1) / (4 * QU * RPW)), (unsigned)(L.B * L.Hkv)),
-                         dim3(256), 0, s, (const unsigned char*)L.k, L.n, pa.w.kn, pa.w.ktmax);
+      const uint64_t qblocks = (rows + 4 * QU * RPW - 1) / (4 * QU * RPW);
+      const uint64_t kblocks = ((uint64_t)L.n + 4 * QU * RPW - 1) / (4 * QU * RPW);
+      const uint64_t nblocks = qblocks + kblocks * (uint64_t)(L.B * L.Hkv);
+      if (nblocks > 0x7FFFFFFFull) return hipErrorInvalidValue;
+      hipLaunchKernelGGL((pf_norm_kernel<D, QU>), dim3((unsigned)nblocks), dim3(256), 0, s, (const unsigned char*)L.q,
+                         (int64_t)rows, pa.w.qn, (const unsigned char*)L.k, L.n, pa.w.kn, pa.w.ktmax, (uint32_t)qblocks,
+                         (uint32_t)kblocks);
       e = hipGetLastError();
       if (e != hipSuccess) return e;
     }
