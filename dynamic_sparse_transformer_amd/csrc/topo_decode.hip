@@ -866,6 +866,7 @@ struct FinishSmem {
   int32_t ridx[REFINE_CAP];
   double rs[REFINE_CAP];
   double rg[REFINE_CAP];  // shared selection: group scores of the short list
+  uint64_t rkey[REFINE_CAP];  // order keys of the short list's ranking scores
   double red[FIN_WAVES * 128];
   double scratch[FIN_WAVES];
   double2 wmz[8];  // (maximum logit, sum) of the first window records
@@ -1305,20 +1306,37 @@ __global__ __launch_bounds__(FIN_THREADS) void decode_finish_kernel(FinishArgs a
     // exact rank of each short-list entry (higher score first, then lower position; group scores
     // for a shared selection): the comparisons of entry i are split into `parts` slices over all
     // threads, summed in LDS
+    // (the order keys are computed once; each slice reads them four at a time, so that four LDS
+    // round trips overlap)
     const double* rk_s = group ? sm->rg : sm->rs;
     int* rank = (int*)sm->hist;
-    for (int i = tid; i < nr; i += FIN_THREADS) rank[i] = 0;
+    for (int i = tid; i < nr; i += FIN_THREADS) {
+      rank[i] = 0;
+      sm->rkey[i] = ord_f64(rk_s[i]);
+    }
     __syncthreads();
     const int parts = nr < FIN_THREADS ? FIN_THREADS / nr : 1;
     const int chunk = (nr + parts - 1) / parts;
     for (int idx = tid; idx < nr * parts; idx += FIN_THREADS) {
       const int i = idx % nr, part = idx / nr;
-      const uint64_t ki = ord_f64(rk_s[i]);
+      const uint64_t ki = sm->rkey[i];
       const int32_t ji = sm->ridx[i];
       const int r1 = min(nr, (part + 1) * chunk);
       int cnt = 0;
-      for (int r = part * chunk; r < r1; ++r) {
-        const uint64_t kr = ord_f64(rk_s[r]);
+      int r = part * chunk;
+      for (; r + 4 <= r1; r += 4) {
+        uint64_t kr[4];
+        int32_t jr[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          kr[u] = sm->rkey[r + u];
+          jr[u] = sm->ridx[r + u];
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) cnt += (kr[u] > ki) || (kr[u] == ki && jr[u] < ji);
+      }
+      for (; r < r1; ++r) {
+        const uint64_t kr = sm->rkey[r];
         cnt += (kr > ki) || (kr == ki && sm->ridx[r] < ji);
       }
       if (cnt) atomicAdd(&rank[i], cnt);
@@ -1344,6 +1362,25 @@ __global__ __launch_bounds__(FIN_THREADS) void decode_finish_kernel(FinishArgs a
 
   // ---- set assembly: C = {0} u window u T, ascending
   const int count = anchor + nwin + nt;
+  if (nt <= 64) {
+    // one wave sorts the top-k positions in registers (distinct keys; empty lanes sort last):
+    // the t-th smallest goes to slot anchor + t, after the window if it lies past p; the window
+    // follows the positions below it
+    if (tid < 64) {
+      uint32_t x = tid < nt ? (uint32_t)sm->u.c.tidx[tid] : 0xFFFFFFFFu;
+      wave_sort64_asc_u32(x);
+      const int tlo_w = __popcll(__ballot(tid < nt && (int64_t)x < w_lo));
+      if (tid < nt) sm->u.c.cidx[anchor + tid + ((int64_t)x > p ? nwin : 0)] = (int32_t)x;
+      if (tid == 0) {
+        sm->ival[7] = tlo_w;
+        if (anchor) sm->u.c.cidx[0] = 0;
+      }
+    }
+    __syncthreads();
+    const int tlo = sm->ival[7];
+    for (int i = tid; i < nwin; i += FIN_THREADS) sm->u.c.cidx[anchor + tlo + i] = (int32_t)(w_lo + i);
+    __syncthreads();
+  } else {
   int tlo_local = 0;
   for (int i = tid; i < nt; i += FIN_THREADS) tlo_local += sm->u.c.tidx[i] < w_lo;
   tlo_local = wave_sum_i32(tlo_local);
@@ -1360,6 +1397,7 @@ __global__ __launch_bounds__(FIN_THREADS) void decode_finish_kernel(FinishArgs a
   }
   for (int i = tid; i < nwin; i += FIN_THREADS) sm->u.c.cidx[anchor + tlo + i] = (int32_t)(w_lo + i);
   __syncthreads();
+  }
 
   if (a.sel_idx) {
     int32_t* dst = a.sel_idx + (size_t)bh * a.set_cap;

@@ -304,4 +304,69 @@ __device__ __forceinline__ double block_sum_f64(double x, double* scratch) {
   return r;
 }
 
+// The value of lane (lane ^ S) for S = 1 .. 32 without an address computation: DPP quad
+// permutes (1, 2), row shifts by 4 chosen by lane bit 2 (4), a row rotation by 8 (8), an LDS
+// swizzle (16), and the gfx950 half-wave swap (32; its two results hold, per lane, the values of
+// lanes l mod 32 and l mod 32 + 32).
+template <int S>
+__device__ __forceinline__ uint32_t lane_xor_u32(uint32_t x) {
+  // (every lane reads a lane that exists for 1, 2 and 8; for 4 each lane keeps the shift whose
+  // source exists, so the zero that bound_ctrl gives a missing source is never used)
+  const int v = (int)x;
+  if constexpr (S == 1) return (uint32_t)__builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, true);
+  else if constexpr (S == 2) return (uint32_t)__builtin_amdgcn_mov_dpp(v, 0x4E, 0xF, 0xF, true);
+  else if constexpr (S == 4) {
+    const int up = __builtin_amdgcn_mov_dpp(v, 0x104, 0xF, 0xF, true);  // lane + 4
+    const int dn = __builtin_amdgcn_mov_dpp(v, 0x114, 0xF, 0xF, true);  // lane - 4
+    return (uint32_t)((threadIdx.x & 4) ? dn : up);
+  } else if constexpr (S == 8) return (uint32_t)__builtin_amdgcn_mov_dpp(v, 0x128, 0xF, 0xF, true);
+  else if constexpr (S == 16) return (uint32_t)__builtin_amdgcn_ds_swizzle(v, 0x401F);
+  else {
+    static_assert(S == 32, "lane_xor_u32: S in 1, 2, 4, 8, 16, 32");
+    const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+    return (threadIdx.x & 32) ? r[0] : r[1];
+  }
+}
+template <int S>
+__device__ __forceinline__ float lane_xor_f32(float x) {
+  return __uint_as_float(lane_xor_u32<S>(__float_as_uint(x)));
+}
+__device__ __forceinline__ float wave_sum_fast(float x) {
+  x += lane_xor_f32<1>(x);
+  x += lane_xor_f32<2>(x);
+  x += lane_xor_f32<4>(x);
+  x += lane_xor_f32<8>(x);
+  x += lane_xor_f32<16>(x);
+  x += lane_xor_f32<32>(x);
+  return x;
+}
+__device__ __forceinline__ float wave_max_fast(float x) {
+  x = fmaxf(x, lane_xor_f32<1>(x));
+  x = fmaxf(x, lane_xor_f32<2>(x));
+  x = fmaxf(x, lane_xor_f32<4>(x));
+  x = fmaxf(x, lane_xor_f32<8>(x));
+  x = fmaxf(x, lane_xor_f32<16>(x));
+  x = fmaxf(x, lane_xor_f32<32>(x));
+  return x;
+}
+template <int S>
+__device__ __forceinline__ void sort_stage_u32(uint32_t& x, int size) {
+  const int lane = threadIdx.x & 63;
+  const uint32_t y = lane_xor_u32<S>(x);
+  x = (((lane & size) == 0) == ((lane & S) == 0)) ? min(x, y) : max(x, y);
+}
+// Ascending bitonic sort of one value per lane across the wave, every exchange without LDS
+// addresses (see lane_xor_u32).
+__device__ __forceinline__ void wave_sort64_asc_u32(uint32_t& x) {
+  sort_stage_u32<1>(x, 2);
+  sort_stage_u32<2>(x, 4);  sort_stage_u32<1>(x, 4);
+  sort_stage_u32<4>(x, 8);  sort_stage_u32<2>(x, 8);  sort_stage_u32<1>(x, 8);
+  sort_stage_u32<8>(x, 16); sort_stage_u32<4>(x, 16); sort_stage_u32<2>(x, 16); sort_stage_u32<1>(x, 16);
+  sort_stage_u32<16>(x, 32); sort_stage_u32<8>(x, 32); sort_stage_u32<4>(x, 32); sort_stage_u32<2>(x, 32);
+  sort_stage_u32<1>(x, 32);
+  sort_stage_u32<32>(x, 64); sort_stage_u32<16>(x, 64); sort_stage_u32<8>(x, 64); sort_stage_u32<4>(x, 64);
+  sort_stage_u32<2>(x, 64); sort_stage_u32<1>(x, 64);
+}
+
+
 }  // namespace topo
