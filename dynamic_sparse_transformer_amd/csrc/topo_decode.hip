@@ -1360,6 +1360,29 @@ __global__ __launch_bounds__(FIN_THREADS) void decode_finish_kernel(FinishArgs a
   }
   __syncthreads();
 
+  // The first batch of V row chunks (see the weighted sum below) is requested now, so that its
+  // memory latency overlaps the set assembly and the softmax; entry nt is the anchor, row 0.
+  constexpr int CPR = RB / 16;             // chunks per row
+  constexpr int EPC = BF16 ? 8 : 4;        // elements per chunk
+  constexpr int RPP = FIN_THREADS / CPR;   // rows per pass
+  constexpr int BATCH = 8;
+  const int ne = nt + anchor;
+  // (all the batch's indices are read first, clamped to the last entry, and the loads run under
+  // a bound that is the same in every thread: no load waits behind a per-thread branch; the
+  // clamped slots get weight zero below)
+  const int vc = tid % CPR, vr0 = tid / CPR;
+  const int nbu = a.out ? min(BATCH, (ne + RPP - 1) / RPP) : 0;
+  int32_t jv[BATCH];
+#pragma unroll
+  for (int u = 0; u < BATCH; ++u) {
+    const int ic = min(vr0 + u * RPP, ne > 0 ? ne - 1 : 0);
+    jv[u] = ic < nt ? sm->u.c.tidx[ic] : 0;
+  }
+  uint4 chv[BATCH];
+#pragma unroll
+  for (int u = 0; u < BATCH; ++u)
+    chv[u] = u < nbu ? *(const uint4*)(vb + (size_t)jv[u] * RB + vc * 16) : make_uint4(0u, 0u, 0u, 0u);
+
   // ---- set assembly: C = {0} u window u T, ascending
   const int count = anchor + nwin + nt;
   if (nt <= 64) {
@@ -1412,7 +1435,6 @@ __global__ __launch_bounds__(FIN_THREADS) void decode_finish_kernel(FinishArgs a
   // Z_w = sum_j Z_j exp(m_j - M_w) and O_w = sum_j O_j exp(m_j - M_w); then with zmax the largest
   // logit of the set, out = (sum_e w_e v_e + f O_w) / (sum_e w_e + f Z_w), w_e = exp(z_e - zmax),
   // f = exp(M_w - zmax).
-  const int ne = nt + anchor;
   if (anchor && tid == 0) {
     sm->u.c.tidx[nt] = 0;
     sm->u.c.ts[nt] = sm->ascore;
@@ -1447,17 +1469,48 @@ __global__ __launch_bounds__(FIN_THREADS) void decode_finish_kernel(FinishArgs a
     }
   }
   __syncthreads();
-  double zmax = Mw;
-  for (int i = tid; i < ne; i += FIN_THREADS) zmax = fmax(zmax, a.scale * sm->u.c.ts[i]);
-  zmax = block_max_f64<FIN_WAVES>(zmax, sm->scratch);
-  double zsum = 0.0;
-  for (int i = tid; i < ne; i += FIN_THREADS) {
-    const double w = exp(a.scale * sm->u.c.ts[i] - zmax);
-    sm->u.c.cw[i] = w;
-    zsum += w;
+  double zmax, zsum;
+  if (ne <= 128) {
+    // one wave takes the largest logit, the weights and their sum (two entries per lane); the
+    // other waves wait at a single barrier
+    if (tid < 64) {
+      const double z0 = tid < ne ? a.scale * sm->u.c.ts[tid] : -INFINITY;
+      const double z1 = tid + 64 < ne ? a.scale * sm->u.c.ts[tid + 64] : -INFINITY;
+      const double m = wave_max_f64(fmax(Mw, fmax(z0, z1)));
+      double ws = 0.0;
+      if (tid < ne) {
+        const double w = exp(z0 - m);
+        sm->u.c.cw[tid] = w;
+        ws += w;
+      }
+      if (tid + 64 < ne) {
+        const double w = exp(z1 - m);
+        sm->u.c.cw[tid + 64] = w;
+        ws += w;
+      }
+      ws = wave_sum_f64(ws);
+      if (tid == 0) {
+        sm->scratch[0] = m;
+        sm->scratch[1] = ws;
+      }
+    }
+    __syncthreads();  // (the weights are visible after it)
+    zmax = sm->scratch[0];
+    zsum = sm->scratch[1];
+  } else {
+    zmax = Mw;
+    for (int i = tid; i < ne; i += FIN_THREADS) zmax = fmax(zmax, a.scale * sm->u.c.ts[i]);
+    zmax = block_max_f64<FIN_WAVES>(zmax, sm->scratch);
+    zsum = 0.0;
+    for (int i = tid; i < ne; i += FIN_THREADS) {
+      const double w = exp(a.scale * sm->u.c.ts[i] - zmax);
+      sm->u.c.cw[i] = w;
+      zsum += w;
+    }
+    zsum = block_sum_f64<FIN_WAVES>(zsum, sm->scratch);  // (contains a barrier: weights visible)
   }
   const double fw = Mw > -INFINITY ? exp(Mw - zmax) : 0.0;
-  zsum = block_sum_f64<FIN_WAVES>(zsum, sm->scratch) + fw * Zw;  // (contains a barrier: weights visible)
+  zsum += fw * Zw;
   if (a.rho) {
     // Exactness certificate: every candidate left out scores at most s_k, the lowest score of
     // the top-k part, so the left-out mass relative to the dense total is at most
@@ -1476,22 +1529,24 @@ __global__ __launch_bounds__(FIN_THREADS) void decode_finish_kernel(FinishArgs a
   }
 
   // Thread t reads 16-byte chunk (t % CPR) of entries t / CPR, + RPP, ...; a batch of BATCH rows
-  // per thread is in flight together (one batch covers up to RPP * BATCH entries).
-  constexpr int CPR = RB / 16;             // chunks per row
-  constexpr int EPC = BF16 ? 8 : 4;        // elements per chunk
-  constexpr int RPP = FIN_THREADS / CPR;   // rows per pass
-  constexpr int BATCH = 8;
+  // per thread is in flight together (one batch covers up to RPP * BATCH entries; the first was
+  // requested before the set assembly).
   const int wave = tid >> 6, lane = tid & 63;
-  const int c = tid % CPR, r0 = tid / CPR;
+  const int c = vc, r0 = vr0;
   double acc[EPC];
 #pragma unroll
   for (int e = 0; e < EPC; ++e) acc[e] = 0.0;
   for (int i0 = r0; i0 < ne; i0 += RPP * BATCH) {
     uint4 ch[BATCH];
+    if (i0 == r0) {
 #pragma unroll
-    for (int u = 0; u < BATCH; ++u) {
-      const int i = i0 + u * RPP;
-      ch[u] = i < ne ? *(const uint4*)(vb + (size_t)sm->u.c.tidx[i] * RB + c * 16) : make_uint4(0u, 0u, 0u, 0u);
+      for (int u = 0; u < BATCH; ++u) ch[u] = chv[u];
+    } else {
+#pragma unroll
+      for (int u = 0; u < BATCH; ++u) {
+        const int i = i0 + u * RPP;
+        ch[u] = i < ne ? *(const uint4*)(vb + (size_t)sm->u.c.tidx[i] * RB + c * 16) : make_uint4(0u, 0u, 0u, 0u);
+      }
     }
 #pragma unroll
     for (int u = 0; u < BATCH; ++u) {
