@@ -218,7 +218,7 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 // row 16 u + 4 (l / 16) + e and key l % 16.
 // The key tiles rotate through 2 PF_H LDS buffers: tile t is written PF_H + 1 steps before the
 // step that reads it, so that the waves meet at a barrier only every PF_H steps. The loads of the
-// tile written at step t + 2 are in flight while step t runs.
+// tiles written at steps t + 1 .. t + 4 are in flight while step t runs.
 // Every score has its own error bound eps = C |q| |k| (C = PF_EPS_COEF). Phase 1 keeps, per lane
 // and row, the two largest fast scores it has seen; the largest norm of the keys the block scores
 // comes from the tiles' maxima. Those 128 values per row belong to distinct candidate keys, so if
@@ -287,10 +287,12 @@ __global__ __launch_bounds__(512) void pf_scan_kernel(PfArgs a) {
   // Staging of key tiles: thread tid copies 16-byte chunk (tid % NCH) of key rows
   // u * PF_KEYS + tid / NCH (+ RPP). Raw buffer loads whose range ends at the cache's last key:
   // rows past the end read as zero, so every load is issued unconditionally and no address is
-  // clamped. Register set (t & 1) holds the tile that step t writes to LDS.
+  // clamped. Register set (t & 3) holds the tile that step t writes to LDS (loaded four steps
+  // earlier, so that the memory latency stays hidden).
   const int srow = tid / NCH, schunk = tid % NCH;
   const int voff0 = srow * RB + schunk * 16, voff1 = voff0 + RPP * RB;
-  uint4 r00 = make_uint4(0u, 0u, 0u, 0u), r01 = r00, r10 = r00, r11 = r00;
+  uint4 r00 = make_uint4(0u, 0u, 0u, 0u), r01 = r00, r10 = r00, r11 = r00, r20 = r00, r21 = r00, r30 = r00,
+        r31 = r00;
 #define PF_LOAD(DST0, DST1, U)                                                                     \
   {                                                                                                \
     const int kt_ = min((U) * PF_KEYS, n);                                                         \
@@ -317,7 +319,7 @@ __global__ __launch_bounds__(512) void pf_scan_kernel(PfArgs a) {
         ACC[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[u][s], __builtin_bit_cast(bf16x8_t, kf[s]), ACC[u], 0, 0, 0); \
   }
 // Prologue of a pass over the tiles, in two parts: the loads of tiles 0 .. PF_H (for LDS) and of
-// the tiles that steps 0 and 1 write (register sets 0 and 1), all in flight together; then tiles
+// the tiles that steps 0 .. 3 write (register sets 0 .. 3), all in flight together; then tiles
 // 0 .. PF_H to LDS, scores of tile 0 into ACC, and a barrier so that no wave overwrites tile 0's
 // buffer before every wave has read it.
   static_assert(PF_H == 2, "the prologue stages tiles 0 .. 2");
@@ -329,6 +331,8 @@ __global__ __launch_bounds__(512) void pf_scan_kernel(PfArgs a) {
     PF_LOAD(p20, p21, 2)                                                                           \
     PF_LOAD(r00, r01, PF_H + 1)                                                                    \
     PF_LOAD(r10, r11, PF_H + 2)                                                                    \
+    PF_LOAD(r20, r21, PF_H + 3)                                                                    \
+    PF_LOAD(r30, r31, PF_H + 4)                                                                    \
   }
 #define PF_PRO_FINISH(ACC)                                                                         \
   {                                                                                                \
@@ -366,7 +370,7 @@ __global__ __launch_bounds__(512) void pf_scan_kernel(PfArgs a) {
 // cores score tile t+1 into ACC_NEXT while the vector units run the per-score work on tile t:
 // PART for each register of ACC_CUR, PER of them after each matrix instruction, then HOOK with
 // the instruction's index (phase 2 runs the previous tile's appends there). Tile t + PF_H + 1
-// then goes from its registers to its LDS buffer and tile t + PF_H + 3 is requested. Scheduling
+// then goes from its registers to its LDS buffer and tile t + PF_H + 5 is requested. Scheduling
 // fences keep that order: left to itself the compiler puts the vector work before the matrix
 // instructions.
   constexpr int NMMA = 4 * SL;  // matrix instructions per step
@@ -390,7 +394,7 @@ __global__ __launch_bounds__(512) void pf_scan_kernel(PfArgs a) {
       }                                                                                            \
   }                                                                                                \
   PF_STORE(SET0, SET1, (t) + PF_H + 1)                                                             \
-  PF_LOAD(SET0, SET1, (t) + PF_H + 3)                                                              \
+  PF_LOAD(SET0, SET1, (t) + PF_H + 5)                                                              \
   }
 
   // phase 1's first tiles are requested before the A operands, the longer wait
@@ -449,9 +453,14 @@ __global__ __launch_bounds__(512) void pf_scan_kernel(PfArgs a) {
     // threshold search, where the loads of phase 2's first tiles are in flight)
 #pragma unroll
     for (int gq = 0; gq < 4; ++gq) asm volatile("" : "+v"(qn_g[gq]));
-    for (int t = 0; t < ntiles; t += PF_H) {
+    // (four steps per turn, one register set each; the turn may end after its second step)
+    for (int t = 0; t < ntiles; t += 2 * PF_H) {
       PF_STEP(PF_PART1, PF_NOHOOK, t, accA, accB, r00, r01)
       PF_STEP(PF_PART1, PF_NOHOOK, t + 1, accB, accA, r10, r11)
+      __syncthreads();
+      if (t + 2 >= ntiles) break;
+      PF_STEP(PF_PART1, PF_NOHOOK, t + 2, accA, accB, r20, r21)
+      PF_STEP(PF_PART1, PF_NOHOOK, t + 3, accB, accA, r30, r31)
       __syncthreads();
     }
   }
@@ -632,11 +641,17 @@ __global__ __launch_bounds__(512) void pf_scan_kernel(PfArgs a) {
   }
   if (ntiles > 0) {
     PF_PRO_FINISH(accA)
-    for (int t = 0; t < ntiles; t += PF_H) {
+    for (int t = 0; t < ntiles; t += 2 * PF_H) {
       PF_STEP(PF_PART2, PF_HOOK2, t, accA, accB, r00, r01)
       PF_POST2(accA, t)
       PF_STEP(PF_PART2, PF_HOOK2, t + 1, accB, accA, r10, r11)
       PF_POST2(accB, t + 1)
+      __syncthreads();
+      if (t + 2 >= ntiles) break;
+      PF_STEP(PF_PART2, PF_HOOK2, t + 2, accA, accB, r20, r21)
+      PF_POST2(accA, t + 2)
+      PF_STEP(PF_PART2, PF_HOOK2, t + 3, accB, accA, r30, r31)
+      PF_POST2(accB, t + 3)
       __syncthreads();
     }
     PF_DRAIN()
