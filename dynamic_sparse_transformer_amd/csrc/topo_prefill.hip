@@ -399,15 +399,19 @@ __global__ __launch_bounds__(512) void pf_scan_kernel(PfArgs a) {
 
   // phase 1's first tiles are requested before the A operands, the longer wait
   if (ntiles > 0) PF_PRO_ISSUE()
-  // The A operands: rows past the end of the queries load the last row (their scores are never
-  // used: they get the bound +inf in phase 2)
-  bf16x8_t qa[4][SL];
+  // The A operands: the block's query rows are loaded once (16-byte chunks spread over the
+  // block's threads; the four waves of a row group share their rows), staged in the tile buffers,
+  // which are not in use yet (rows STRIDE bytes apart, as the key tiles), and each wave reads its
+  // rows' operands from there. Rows past the end of the queries load the last row (their scores
+  // are never used: they get the bound +inf in phase 2).
+  constexpr int QPT = PF_ROWS * NCH / 512;  // chunks per thread
+  static_assert(PF_ROWS * NCH % 512 == 0 && PF_ROWS * STRIDE <= SMEM, "query staging");
+  uint4 qv[QPT];
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int64_t i = min(i0 + rg * 64 + u * 16 + m, a.n_q - 1);
-    const unsigned char* qrow = a.q + ((size_t)bh * a.n_q + i) * RB + grp * GB;
-#pragma unroll
-    for (int s = 0; s < SL; ++s) qa[u][s] = __builtin_bit_cast(bf16x8_t, *(const uint4*)(qrow + s * 16));
+  for (int j = 0; j < QPT; ++j) {
+    const int c = tid + 512 * j;
+    const int64_t i = min(i0 + c / NCH, a.n_q - 1);
+    qv[j] = *(const uint4*)(a.q + ((size_t)bh * a.n_q + i) * RB + (c % NCH) * 16);
   }
   if (tid < 2 * 4 * 17) {
     // counter rg * 68 + g * 17 + r (r < 16) is that of block row 64 rg + 4 g + 16 (r >> 2) + (r & 3)
@@ -429,6 +433,19 @@ __global__ __launch_bounds__(512) void pf_scan_kernel(PfArgs a) {
   // are in flight: its wait covers them all)
   float knmx = 0.f;
   for (int t = tid; t < ntiles; t += 512) knmx = fmaxf(knmx, ktm[t]);
+#pragma unroll
+  for (int j = 0; j < QPT; ++j) {
+    const int c = tid + 512 * j;
+    *(uint4*)&ktiles[(c / NCH) * STRIDE + (c % NCH) * 16] = qv[j];
+  }
+  __syncthreads();
+  bf16x8_t qa[4][SL];
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+#pragma unroll
+    for (int s = 0; s < SL; ++s)
+      qa[u][s] = *(const bf16x8_t*)&ktiles[(rg * 64 + u * 16 + m) * STRIDE + grp * GB + s * 16];
+  __syncthreads();  // (before the prologue writes key tiles over the staged rows)
 
   f32x4_t accA[4], accB[4];
   // ---- phase 1: per lane and row, the two largest fast scores of candidate keys. With m1 >= m2,
