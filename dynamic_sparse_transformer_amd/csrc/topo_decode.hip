@@ -403,11 +403,13 @@ __global__ __launch_bounds__(256, TOPO_KS_MIN_BLOCKS) void kscan_kernel(KscanArg
 #pragma unroll
   for (int h = 0; h < GT; ++h) cq[h] = a.eps_coef * qn[h];
 
-  // The block ranks a.runs runs of KS_WAVES x KS_KEYS_PER_WAVE keys; in run r, wave w takes the
-  // KS_KEYS_PER_WAVE keys starting at run_key0(r).
+  // The block ranks a.runs runs of KS_WAVES x KS_KEYS_PER_WAVE keys; tile it of run r (KS_ROWS
+  // keys) of wave w is tile (r KS_IT + it) KS_WAVES + w of the block, so that the four waves take
+  // consecutive tiles and the block streams one contiguous range (a read-only probe streams
+  // faster that way than with each wave on a range of its own).
   const int64_t blk_key0 = (int64_t)blockIdx.x * KS_KEYS_PER_RUN * a.runs;
-  auto run_key0 = [&](int r) -> int64_t {
-    return blk_key0 + (int64_t)(r * KS_WAVES + wave) * KS_KEYS_PER_WAVE;
+  auto tile_key0 = [&](int r, int it) -> int64_t {
+    return blk_key0 + ((int64_t)(r * KS_IT + it) * KS_WAVES + wave) * KS_ROWS;
   };
   const unsigned char* kb = a.k + (size_t)grp * (size_t)a.n * RB;
   const int64_t last_row = q_scan;
@@ -428,7 +430,7 @@ __global__ __launch_bounds__(256, TOPO_KS_MIN_BLOCKS) void kscan_kernel(KscanArg
   // bf16 values are exact in float32 and the float32 sum of the d squares carries a relative
   // error below 2^-19 (float32 data: below 2^-18), covered by the factor that rounds the norm up.
   uint4 kv[8][CPL];
-  kscan_load<RB>(kv, kb, run_key0(0), last_row, lane);
+  kscan_load<RB>(kv, kb, tile_key0(0, 0), last_row, lane);
   const int kr = lane >> 3;
   auto tile = [&](int64_t row0, int64_t nrow0, bool more) {
     const bool nfull = nrow0 + 63 <= last_row;
@@ -483,7 +485,6 @@ __global__ __launch_bounds__(256, TOPO_KS_MIN_BLOCKS) void kscan_kernel(KscanArg
   }
 #pragma unroll 1
   for (int r = 0; r < a.runs; ++r) {
-    const int64_t key0 = run_key0(r);
     // The shared thresholds are read now, so the load overlaps the run (a stale value is still a
     // valid bound: the shared threshold only ever rises). Unconditional loads keep the wait
     // counts of the tile stream exact.
@@ -493,8 +494,8 @@ __global__ __launch_bounds__(256, TOPO_KS_MIN_BLOCKS) void kscan_kernel(KscanArg
       thp[h] = __hip_atomic_load(&a.st[(size_t)b * a.Hq + h0 + (h < nh ? h : nh - 1)].theta, __ATOMIC_RELAXED,
                                  __HIP_MEMORY_SCOPE_AGENT);
 #pragma unroll 1
-    for (int it = 0; it + 1 < KS_IT; ++it) tile(key0 + (int64_t)it * KS_ROWS, key0 + (int64_t)(it + 1) * KS_ROWS, true);
-    tile(key0 + (int64_t)(KS_IT - 1) * KS_ROWS, run_key0(r + 1), r + 1 < a.runs);
+    for (int it = 0; it + 1 < KS_IT; ++it) tile(tile_key0(r, it), tile_key0(r, it + 1), true);
+    tile(tile_key0(r, KS_IT - 1), tile_key0(r + 1, 0), r + 1 < a.runs);
     if constexpr (GROUP) {
 #pragma unroll
       for (int it = 0; it < KS_IT; ++it)
@@ -574,7 +575,7 @@ __global__ __launch_bounds__(256, TOPO_KS_MIN_BLOCKS) void kscan_kernel(KscanArg
         if (ok) {
           const int pos = wtotal[h] + lanes_below(m);
           if (pos < KS_WAVE_CAP) {
-            wbuf[wave][h][pos] = make_uint2(__float_as_uint(sc[h][it]), (uint32_t)(key0 + (int64_t)it * KS_ROWS + my_off));
+            wbuf[wave][h][pos] = make_uint2(__float_as_uint(sc[h][it]), (uint32_t)(tile_key0(r, it) + my_off));
             wbe[wave][h][pos] = e;
           }
         }
