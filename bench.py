@@ -14,7 +14,9 @@ inputs resident in HBM; `value` is timed on plain calls. The key scan's duration
 second pass of the same steps through topo_attn_decode_timed, whose HIP events bracket the scan
 launch on the call's stream. Reported alongside: the dense pillar layer on the same 1M inputs, the
 128K-context batch-4 decode (with the cost of the exact fallback selection), the causal 8K-token
-prefill (matrix-core key scan, against the bf16 MFMA peak) and a 32-layer decode stack.
+prefill (matrix-core key scan, against the bf16 MFMA peak) and a 32-layer decode stack. The
+roofline object also carries the rate of the library's read-only probe over 2 GiB (`probe_gbs`),
+the read bandwidth this chip reaches in practice, and the scan's share of it.
 
 The CPU baseline (the oracle as it stands, on all 32 query heads of the 1M workload, spread over
 worker processes on the host's usable cores) runs before the GPU is touched, so that the workers
@@ -537,6 +539,25 @@ def main():
         log(f"[bench] {args.layers}-layer stack")
         also.append(run_layers_bench(args.layers, max(3, args.steps // 5), min(args.warmup, 2)))
 
+    # Achievable read bandwidth: the library's read-only probe over 2 GiB (the size of the 1M scan's
+    # K), launched back to back as the decode steps are, timed with events on the stream it runs on
+    # (torch's current stream); next to it the scan's own rate.
+    buf = torch.empty(1 << 31, dtype=torch.uint8, device="cuda").fill_(1)
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    for _ in range(3):
+        topo.topo_bw_probe(buf, sink)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 20
+    e0.record()
+    for _ in range(reps):
+        topo.topo_bw_probe(buf, sink)
+    e1.record()
+    e1.synchronize()
+    del buf
+    probe_us = e0.elapsed_time(e1) * 1e3 / reps
+    probe = {"kernel": "bw_probe_kernel", "bytes": 1 << 31, "mean_us": probe_us, "launches": reps,
+             "gbs": (1 << 31) / (probe_us / 1e6) / 1e9}
+
     if args.calibrate:
         # Known traffic: the probe reads every byte of a 2 GiB buffer once; the copy reads and
         # writes 256 MiB. Counter readings of these kernels give the bytes-per-count factors.
@@ -554,6 +575,7 @@ def main():
     traffic = measured_traffic("kscan", s.name)
     roofline = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                "probe_gbs": probe["gbs"], "frac_of_probe": achieved / probe["gbs"],
                 "kernel": "kscan_kernel<256,4,bf16>", "kernel_us": main_res["scan_ms"] * 1e3,
                 "alg_bytes_per_launch": main_res["alg_bytes"],
                 "timing": "HIP events around the scan launch, in a second pass of the same steps "

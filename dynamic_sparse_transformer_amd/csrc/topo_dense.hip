@@ -601,10 +601,12 @@ hipError_t launch_dense(const DenseLaunch& L, hipStream_t stream) {
 }
 
 // ---------------------------------------------------------------------------------------------
-// Read-bandwidth probe: every block streams 64 KiB runs with the key scan's load instruction
-// (16-byte non-temporal loads, one per lane, fully coalesced) and folds them into one word.
+// Read-bandwidth probe: every block streams 128 KiB runs with the key scan's load instruction
+// (16-byte non-temporal loads, one per lane, fully coalesced) and folds them into one word. Of the
+// shapes measured (8 to 32 loads per lane in flight, 1024 to 8192 blocks, grid-stride or one
+// contiguous range per block), 32 loads per lane over 8192 blocks read fastest.
 __global__ __launch_bounds__(256) void bw_probe_kernel(const uint4* buf, size_t n16, uint32_t* sink) {
-  constexpr int U = 16;
+  constexpr int U = 32;
   uint32_t x = 0;
   const size_t run = (size_t)256 * U;
   for (size_t base = (size_t)blockIdx.x * run; base < n16; base += (size_t)gridDim.x * run) {
@@ -623,8 +625,8 @@ __global__ __launch_bounds__(256) void bw_probe_kernel(const uint4* buf, size_t 
 
 hipError_t launch_bw_probe(const void* buf, size_t bytes, uint32_t* sink, hipStream_t stream) {
   const size_t n16 = bytes / 16;
-  const size_t runs = (n16 + 4095) / 4096;
-  const unsigned blocks = (unsigned)(runs < 2048 ? runs : 2048);
+  const size_t runs = (n16 + 8191) / 8192;
+  const unsigned blocks = (unsigned)(runs < 8192 ? runs : 8192);
   hipLaunchKernelGGL(bw_probe_kernel, dim3(blocks), dim3(256), 0, stream, (const uint4*)buf, n16, sink);
   return hipGetLastError();
 }
