@@ -207,8 +207,8 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
-// pf_scan: one block of 512 threads per (b, h, 128 consecutive query rows). Each step scores 64
-// keys held in LDS. Wave w = 4 rg + kg holds the 64 query rows 64 rg .. +64 as the A operands of
+// pf_scan: blocks of 512 threads, each scoring one or more jobs (b, h, 128 consecutive query
+// rows) in turn. Each step scores 64 keys held in LDS. Wave w = 4 rg + kg holds the 64 query rows 64 rg .. +64 as the A operands of
 // four 16-row tiles and scores them against keys 16 kg .. +16 of the tile with
 // v_mfma_f32_16x16x32_bf16 (one B operand read from LDS feeds four products). Lane l supplies row
 // / key l % 16 and elements 8 (l / 16) .. +8 of each 32-deep slice; a slice takes, for both
@@ -253,14 +253,29 @@ __global__ __launch_bounds__(512) void pf_scan_kernel(PfArgs a) {
   // (the wave index through readfirstlane, so that the compiler keeps what derives from it in
   // scalar registers)
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
-  // Job of this block (the blocks of one head on one XCD). Within a head the row blocks run from
-  // the last (most keys under a causal mask) to the first, so the long jobs start first.
+  // Jobs of this block. The host launches at most as many blocks as fit on the GPU at once, so
+  // the block count fixes which jobs share a compute unit instead of the dispatcher's order.
+  // When the blocks and the heads both divide by eight, the jobs form eight lists, one per XCD
+  // (blocks are dealt to the XCDs in turn, so block x + 8 i runs on XCD x; list x holds heads
+  // x H8 .. +H8, whose keys then stay in that XCD's L2), else one list. A list runs from the
+  // longest jobs to the shortest (row blocks from the last, which has the most keys under a
+  // causal mask; heads interleaved), and its blocks take them in snake order: in round r, block
+  // i of P takes job r P + i when r is even and r P + P - 1 - i when r is odd, so the long jobs of
+  // one round pair with the short ones of the next (under a causal mask every block of a list of
+  // two rounds gets the same number of key tiles).
   // (32-bit index arithmetic: the jobs, heads and row blocks fit)
   const uint32_t nrb = (uint32_t)((a.n_q + PF_ROWS - 1) / PF_ROWS);
-  const uint32_t job = (uint32_t)xcd_job(blockIdx.x, (int64_t)nrb * a.Hq * a.B);
-  const uint32_t bh = job / nrb;
+  const uint32_t nbh = (uint32_t)(a.B * a.Hq);
+  const bool xlists = gridDim.x % 8u == 0u && nbh % 8u == 0u;
+  const uint32_t nlist = xlists ? 8u : 1u;
+  const uint32_t lst = blockIdx.x % nlist, lb = blockIdx.x / nlist, lP = gridDim.x / nlist;
+  const uint32_t lh = nbh / nlist, ljobs = lh * nrb;
+  for (uint32_t round = 0;; ++round) {
+  const uint32_t q_ = (round & 1u) ? (round + 1u) * lP - 1u - lb : round * lP + lb;
+  if (q_ >= ljobs) break;
+  const uint32_t bh = lst * lh + q_ % lh;
   const uint32_t b = bh / (uint32_t)a.Hq, h = bh - b * (uint32_t)a.Hq, g = h / (uint32_t)a.G;
-  const int64_t i0 = (int64_t)(nrb - 1 - (job - bh * nrb)) * PF_ROWS;
+  const int64_t i0 = (int64_t)(nrb - 1 - q_ / lh) * PF_ROWS;
   const unsigned char* kb = a.k + ((size_t)b * a.Hkv + g) * (size_t)a.n * RB;
   const float* ktm = a.w.ktmax + ((size_t)b * a.Hkv + g) * (size_t)((a.n + PF_KEYS - 1) / PF_KEYS);
   const uint32_t LCAP = (uint32_t)a.slot;
@@ -680,6 +695,8 @@ __global__ __launch_bounds__(512) void pf_scan_kernel(PfArgs a) {
   __syncthreads();
   if (tid < PF_ROWS && i0 + tid < a.n_q)
     a.w.cnt[grow0 + tid] = min(rowcnt[(tid >> 6) * 68 + ((tid >> 2) & 3) * 17 + ((tid >> 4) & 3) * 4 + (tid & 3)], 0xFFFFu);
+  __syncthreads();  // (the next job resets the counters and overwrites the tile buffers)
+  }
 #undef PF_INTERIOR
 #undef PF_LOAD
 #undef PF_STORE
@@ -1504,6 +1521,19 @@ __global__ __launch_bounds__(256) void pf_finish_kernel(PfArgs a) {
 }
 
 // ---------------------------------------------------------------------------------------------
+// Blocks of pf_scan the current device holds at once (compute units times blocks per unit).
+template <int D>
+static int64_t pf_scan_slots() {
+  int dev = 0, cus = 256, per = 1;
+  if (hipGetDevice(&dev) == hipSuccess) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0) cus = v;
+  }
+  int nb = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, pf_scan_kernel<D>, 512, 0) == hipSuccess && nb > 0) per = nb;
+  return (int64_t)cus * per;
+}
+
 template <int D, bool BF16>
 static hipError_t launch_pf_t(const PrefillLaunch& L, const PfArgs& pa, hipStream_t s) {
   const size_t rows = (size_t)L.B * L.Hq * (size_t)L.n_q;
@@ -1526,8 +1556,9 @@ static hipError_t launch_pf_t(const PrefillLaunch& L, const PfArgs& pa, hipStrea
   if (L.ev_scan_begin) (void)hipEventRecord(L.ev_scan_begin, s);
   if (!pa.exact_all && L.topk > 0) {
     if constexpr (BF16) {
-      hipLaunchKernelGGL((pf_scan_kernel<D>), dim3((unsigned)((L.n_q + PF_ROWS - 1) / PF_ROWS * L.B * L.Hq)),
-                         dim3(512), 0, s, pa);
+      const int64_t jobs = (L.n_q + PF_ROWS - 1) / PF_ROWS * L.B * L.Hq;
+      const int64_t slots = pf_scan_slots<D>();
+      hipLaunchKernelGGL((pf_scan_kernel<D>), dim3((unsigned)(jobs < slots ? jobs : slots)), dim3(512), 0, s, pa);
       e = hipGetLastError();
       if (e != hipSuccess) return e;
     }
