@@ -918,36 +918,36 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void p
 // region laid out by PfRowSmem::carve for the call's k and 1 + W + k.
 constexpr int PF_FIN_SET = 4096;   // largest 1 + W + k served by the per-row finish
 // (tidx and cw have room for the V gather's padding: the entries rounded up to a multiple of
-// PF_GATHER, as positions and as float32 weights)
-constexpr int PF_GATHER = 136;
+// PF_GATHER, as positions and as float32 weights). The float64 query shares its space with cw:
+// every path has read qd for the last time before it writes cw.
+constexpr int PF_GATHER = 144;
 struct PfRowSmem {
-  double* qd;      // [128]
+  double* qd;      // [128], in the space of cw
   double* rs;      // [slot + set_cap]: float64 scores of the row's list, window and anchor keys
   double* ts;      // [k + 1]
-  double* cw;      // [max(set_cap, PF_GATHER / 2)], or float32 weights [round_up(k + 1, PF_GATHER)]
+  double* cw;      // [max(set_cap, PF_GATHER / 2, 128)], or float32 weights [round_up(k + 1, PF_GATHER)]
   int32_t* ridx;   // [slot + 1]: the list, then the anchor
   int32_t* tidx;   // [round_up(k + 1, PF_GATHER)]
   int32_t* cidx;   // [set_cap]
   uint32_t* hist;  // [256]
   static __host__ __device__ size_t tcap(int k) { return ((size_t)k + PF_GATHER) / PF_GATHER * PF_GATHER; }
   static __host__ __device__ size_t wcap(int k, int set_cap) {
-    const size_t w = (tcap(k) + 1) / 2;
-    return (size_t)set_cap > w ? (size_t)set_cap : w;
+    const size_t w = (tcap(k) + 1) / 2, s = (size_t)set_cap > 128 ? (size_t)set_cap : 128;
+    return s > w ? s : w;
   }
   static __host__ __device__ size_t bytes(int64_t slot, int k, int set_cap) {
     const size_t kk = (size_t)k + 1;
-    return 128 * 8 + ((size_t)slot + set_cap) * 8 + kk * 8 + wcap(k, set_cap) * 8 + tcap(k) * 4 +
+    return ((size_t)slot + set_cap) * 8 + kk * 8 + wcap(k, set_cap) * 8 + tcap(k) * 4 +
            (size_t)set_cap * 4 + ((size_t)slot + 1) * 4 + 256 * 4 + 64;
   }
   __device__ void carve(unsigned char* p, int64_t slot, int k, int set_cap) {
     const size_t kk = (size_t)k + 1;
-    qd = (double*)p;
-    p += 128 * 8;
     rs = (double*)p;
     p += ((size_t)slot + set_cap) * 8;
     ts = (double*)p;
     p += kk * 8;
     cw = (double*)p;
+    qd = cw;
     p += wcap(k, set_cap) * 8;
     ridx = (int32_t*)p;
     p += ((size_t)slot + 1) * 4;
@@ -1362,7 +1362,7 @@ __device__ void pf_row(const PfArgs& a, PfRowSmem* sm, size_t grow) {
 
   // ---- softmax over the set and the weighted V rows: lane group gq takes the entries
   // t = gq (mod RPI), each lane a 16-byte chunk of the row; then the groups are summed.
-  constexpr int U = BF16 ? 17 : 4;  // V rows per lane group in flight together (bf16: the whole set for k <= 67)
+  constexpr int U = BF16 ? 9 : 4;  // V rows per lane group in flight together (bf16: 36 rows per batch at d = 128)
   if constexpr (BF16) {
     // The window's part (m_w, Z_w, O_w) comes from pf_window; here the anchor and the top-k
     // (tidx / ts [0, nt), the anchor appended at nt), then the merge of the two parts:
@@ -1509,7 +1509,7 @@ __device__ void pf_row(const PfArgs& a, PfRowSmem* sm, size_t grow) {
 // pf_finish: one wave per query row, 4 rows per block (consecutive rows of one head). OFF32 as in
 // pf_row (chosen at launch: one row variant per kernel keeps the register count down).
 template <int D, bool BF16, bool OFF32>
-__global__ __launch_bounds__(256) void pf_finish_kernel(PfArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5))) void pf_finish_kernel(PfArgs a) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
   // (the wave index through readfirstlane: the row's indices stay in scalar registers)
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);

@@ -88,10 +88,10 @@ extern "C" {
 #define TOPO_OP_DECODE_RAGGED 5     /* topo_attn_decode_ragged (sized for the longest position) */
 
 /* Largest condensate set (1 + W + k) a call may ask for. The prefill also needs the LDS of its
- * per-row finish to hold four rows: with S = 1 + W + k, P = roundup(k + 1, 136) and
- * L = min(k + 48, 128), 4 * roundup256(2116 + 12 * S + 8 * max(S, P / 2) + 8 * (k + 1) + 4 * P
- * + 12 * L) <= 163840 bytes (S <= 1821 at k = 64); larger sets return TOPO_EUNSUPPORTED from the
- * prefill calls (and 0 from topo_workspace_bytes). */
+ * per-row finish to hold four rows: with S = 1 + W + k, P = roundup(k + 1, 144) and
+ * L = min(k + 48, 128), 4 * roundup256(1092 + 12 * S + 8 * max(S, P / 2, 128) + 8 * (k + 1)
+ * + 4 * P + 12 * L) <= 163840 bytes (S <= 1871 at k = 64); larger sets return TOPO_EUNSUPPORTED
+ * from the prefill calls (and 0 from topo_workspace_bytes). */
 #define TOPO_MAX_SET 4096
 
 /* Flag bits of topo_params_t.flags. */

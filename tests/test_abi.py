@@ -161,17 +161,17 @@ def _prefill_params(W, k):
 
 def test_prefill_set_size_limit_on_host():
     """The prefill's per-row finish keeps four rows in one block's LDS, which bounds the set
-    1 + W + k (1821 at k = 64, the header's formula); larger sets are refused on the host, with
+    1 + W + k (1871 at k = 64, the header's formula); larger sets are refused on the host, with
     a zero workspace size and TOPO_EUNSUPPORTED, before anything is launched."""
     lib = topo.load_library()
-    assert lib.topo_workspace_bytes(ctypes.byref(_prefill_params(1821 - 65, 64)), 1) > 0
-    assert lib.topo_workspace_bytes(ctypes.byref(_prefill_params(1822 - 65, 64)), 1) == 0
+    assert lib.topo_workspace_bytes(ctypes.byref(_prefill_params(1871 - 65, 64)), 1) > 0
+    assert lib.topo_workspace_bytes(ctypes.byref(_prefill_params(1872 - 65, 64)), 1) == 0
     assert lib.topo_workspace_bytes(ctypes.byref(_prefill_params(2047, 64)), 1) == 0
     # aligned host addresses stand in for device buffers: the size check refuses the call first
     buf = (ctypes.c_uint8 * 256)()
     a = (ctypes.addressof(buf) + 15) & ~15
     ptr = ctypes.c_void_p(a)
-    for W in (1822 - 65, 2047):
+    for W in (1872 - 65, 2047):
         rc = lib.topo_attn_prefill(ctypes.byref(_prefill_params(W, 64)), ptr, ptr, ptr, ptr, ptr, ptr, ptr,
                                    ctypes.c_size_t(1 << 40), None)
         assert rc == -2, rc
