@@ -18,6 +18,8 @@
 //              and V reduction over anchor and top-k, merged with the window's share. Rows
 //              whose list overflowed (ties), float32 inputs and k above the scan's limit take
 //              an exact float64 radix selection over all of the row's candidates instead.
+#include <atomic>
+
 #include "topo_device.h"
 #include "topo_internal.h"
 
@@ -1521,17 +1523,24 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5))) void p
 }
 
 // ---------------------------------------------------------------------------------------------
-// Blocks of pf_scan the current device holds at once (compute units times blocks per unit).
+// Blocks of pf_scan the current device holds at once (compute units times blocks per unit),
+// queried once per device and kept (racing first calls store the same value).
 template <int D>
 static int64_t pf_scan_slots() {
-  int dev = 0, cus = 256, per = 1;
-  if (hipGetDevice(&dev) == hipSuccess) {
-    int v = 0;
-    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0) cus = v;
+  constexpr int MAX_DEV = 64;
+  static std::atomic<int64_t> cache[MAX_DEV];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) dev = -1;
+  if (dev >= 0 && dev < MAX_DEV) {
+    const int64_t c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
   }
-  int nb = 0;
+  int cus = 256, per = 1, v = 0, nb = 0;
+  if (dev >= 0 && hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0) cus = v;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, pf_scan_kernel<D>, 512, 0) == hipSuccess && nb > 0) per = nb;
-  return (int64_t)cus * per;
+  const int64_t slots = (int64_t)cus * per;
+  if (dev >= 0 && dev < MAX_DEV) cache[dev].store(slots, std::memory_order_relaxed);
+  return slots;
 }
 
 template <int D, bool BF16>
