@@ -63,7 +63,7 @@ size_t certified_workspace_bytes(const topo_params_t* p) {
 }
 
 size_t prefill_ws(const topo_params_t* p) {
-  if (!topo::prefill_fits(p->W, p->k)) return 0;
+  if (!topo::prefill_fits(p->W, p->k, p->dtype == TOPO_BF16)) return 0;
   return topo::prefill_workspace_bytes(p->B, p->Hq, p->Hkv, p->n_q, p->n_ctx, p->d, p->W, p->k);
 }
 
@@ -151,7 +151,7 @@ int prefill_like(const topo_params_t* p, const void* q, const void* k, const voi
   if (softmax && (!v || !out || !aligned16(v) || !aligned16(out))) return TOPO_EINVAL;
   if (!softmax && (!sel_idx || !sel_count)) return TOPO_EINVAL;
   if ((sel_idx && !aligned16(sel_idx)) || (sel_count && !aligned16(sel_count))) return TOPO_EINVAL;
-  if (!topo::prefill_fits(p->W, p->k)) return TOPO_EUNSUPPORTED;
+  if (!topo::prefill_fits(p->W, p->k, p->dtype == TOPO_BF16)) return TOPO_EUNSUPPORTED;
   const size_t need = prefill_ws(p);
   if (!ws || ws_bytes < need || !aligned16(ws)) return TOPO_EWORKSPACE;
   topo::PrefillLaunch L{};
@@ -386,7 +386,7 @@ int topo_workspace_view(const topo_params_t* p, int op, topo_ws_view_t* view) {
   if (rc) return rc;
   topo_ws_view_t v{};
   if (op == TOPO_OP_PREFILL || (op == TOPO_OP_SELECT && p->n_q != 1)) {
-    if (!topo::prefill_fits(p->W, p->k)) return TOPO_EUNSUPPORTED;
+    if (!topo::prefill_fits(p->W, p->k, p->dtype == TOPO_BF16)) return TOPO_EUNSUPPORTED;
     const topo::PrefillView pv = topo::prefill_view(p->B, p->Hq, p->Hkv, p->n_q, p->n_ctx, p->d, p->k);
     v.queries = (int64_t)p->B * p->Hq * p->n_q;
     v.lists = 1;

@@ -156,7 +156,7 @@ struct PrefillLaunch {
 };
 size_t prefill_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int64_t n_q, int64_t n, int32_t d, int32_t W, int32_t k);
 // Whether the per-row finish's LDS holds a set of 1 + W + k (false: the prefill is unsupported).
-bool prefill_fits(int32_t W, int32_t k);
+bool prefill_fits(int32_t W, int32_t k, bool bf16);
 // Byte offsets, within a prefill workspace, of the scan's per-row lists and the rows' paths.
 struct PrefillView {
   size_t count, entry, path;

@@ -923,27 +923,58 @@ constexpr int PF_FIN_SET = 4096;   // largest 1 + W + k served by the per-row fi
 // PF_GATHER, as positions and as float32 weights). The float64 query shares its space with cw:
 // every path has read qd for the last time before it writes cw.
 constexpr int PF_GATHER = 144;
+// Two layouts. The general one (float32 inputs, or k > 64) keeps float64 scores and positions of
+// the whole set. The compact one (bf16 inputs, k <= 64) keeps only what that path touches: the
+// list and its scores, the top-k, the weights and the float64 query, none of it sized by the
+// window, so its LDS does not grow with W. Its radix histogram (exact path only, where the list
+// is never loaded) lies over rs[1 ..] and ridx; rs[0] keeps the anchor's score on that path.
 struct PfRowSmem {
   double* qd;      // [128], in the space of cw
-  double* rs;      // [slot + set_cap]: float64 scores of the row's list, window and anchor keys
+  double* rs;      // general: [slot + set_cap] float64 scores of the list, window and anchor keys;
+                   // compact: [slot + 1] the list's scores, the anchor's, the band's float64 scores
   double* ts;      // [k + 1]
-  double* cw;      // [max(set_cap, PF_GATHER / 2, 128)], or float32 weights [round_up(k + 1, PF_GATHER)]
+  double* cw;      // general: [max(set_cap, PF_GATHER / 2, 128)]; compact: [128]; or float32
+                   // weights [round_up(k + 1, PF_GATHER)]
   int32_t* ridx;   // [slot + 1]: the list, then the anchor
   int32_t* tidx;   // [round_up(k + 1, PF_GATHER)]
-  int32_t* cidx;   // [set_cap]
+  int32_t* cidx;   // general: [set_cap]; compact: none (the set goes from registers to the output)
   uint32_t* hist;  // [256]
+  static __host__ __device__ bool compact(bool bf16, int k) { return bf16 && k <= 64; }
   static __host__ __device__ size_t tcap(int k) { return ((size_t)k + PF_GATHER) / PF_GATHER * PF_GATHER; }
   static __host__ __device__ size_t wcap(int k, int set_cap) {
     const size_t w = (tcap(k) + 1) / 2, s = (size_t)set_cap > 128 ? (size_t)set_cap : 128;
     return s > w ? s : w;
   }
-  static __host__ __device__ size_t bytes(int64_t slot, int k, int set_cap) {
+  // compact: rs and ridx (the histogram over them), rounded to 16 bytes
+  static __host__ __device__ size_t lcap(int64_t slot) {
+    const size_t l = ((size_t)slot + 1) * 12, h = 8 + 256 * 4, m = l > h ? l : h;
+    return (m + 15) & ~(size_t)15;
+  }
+  static __host__ __device__ size_t bytes(int64_t slot, int k, int set_cap, bool cmp) {
     const size_t kk = (size_t)k + 1;
+    if (cmp) {
+      const size_t wc = tcap(k) * 4 > 128 * 8 ? tcap(k) * 4 : 128 * 8;
+      return lcap(slot) + ((kk * 8 + 15) & ~(size_t)15) + wc + tcap(k) * 4;
+    }
     return ((size_t)slot + set_cap) * 8 + kk * 8 + wcap(k, set_cap) * 8 + tcap(k) * 4 +
            (size_t)set_cap * 4 + ((size_t)slot + 1) * 4 + 256 * 4 + 64;
   }
-  __device__ void carve(unsigned char* p, int64_t slot, int k, int set_cap) {
+  __device__ void carve(unsigned char* p, int64_t slot, int k, int set_cap, bool cmp) {
     const size_t kk = (size_t)k + 1;
+    if (cmp) {
+      rs = (double*)p;
+      ridx = (int32_t*)(p + ((size_t)slot + 1) * 8);
+      hist = (uint32_t*)(p + 8);
+      p += lcap(slot);
+      ts = (double*)p;
+      p += (kk * 8 + 15) & ~(size_t)15;
+      cw = (double*)p;
+      qd = cw;
+      p += tcap(k) * 4 > 128 * 8 ? tcap(k) * 4 : 128 * 8;
+      tidx = (int32_t*)p;
+      cidx = nullptr;
+      return;
+    }
     rs = (double*)p;
     p += ((size_t)slot + set_cap) * 8;
     ts = (double*)p;
@@ -1511,12 +1542,12 @@ __device__ void pf_row(const PfArgs& a, PfRowSmem* sm, size_t grow) {
 // pf_finish: one wave per query row, 4 rows per block (consecutive rows of one head). OFF32 as in
 // pf_row (chosen at launch: one row variant per kernel keeps the register count down).
 template <int D, bool BF16, bool OFF32>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5))) void pf_finish_kernel(PfArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(7))) void pf_finish_kernel(PfArgs a) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
   // (the wave index through readfirstlane: the row's indices stay in scalar registers)
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   PfRowSmem smv;
-  smv.carve(smem_raw + wave * a.wave_smem, a.slot, a.topk, a.set_cap);
+  smv.carve(smem_raw + wave * a.wave_smem, a.slot, a.topk, a.set_cap, PfRowSmem::compact(BF16, a.topk));
   const size_t grow = (size_t)xcd_job(blockIdx.x, gridDim.x) * 4 + wave;  // (b*Hq + h) * n_q + i
   if (grow >= (size_t)a.rows) return;
   pf_row<D, BF16, OFF32>(a, &smv, grow);
@@ -1594,10 +1625,11 @@ static hipError_t launch_pf_t(const PrefillLaunch& L, const PfArgs& pa, hipStrea
 
 // The finish gives each of its 4 waves (rows) its own LDS region; all four must fit the 160 KB of a
 // compute unit.
-bool prefill_fits(int32_t W, int32_t k) {
+bool prefill_fits(int32_t W, int32_t k, bool bf16) {
   const int set_cap = 1 + W + k;
   if (set_cap > PF_FIN_SET) return false;
-  const size_t wave_smem = (PfRowSmem::bytes(pf_slot(k), k, set_cap) + 255) & ~(size_t)255;
+  const size_t wave_smem =
+      (PfRowSmem::bytes(pf_slot(k), k, set_cap, PfRowSmem::compact(bf16, k)) + 255) & ~(size_t)255;
   return 4 * wave_smem <= 160 * 1024;
 }
 
@@ -1630,8 +1662,8 @@ hipError_t launch_prefill(const PrefillLaunch& L, hipStream_t stream) {
   pa.scale = L.scale;
   pa.pinf = INFINITY;
   pa.rows = (int64_t)L.B * L.Hq * L.n_q;
-  pa.wave_smem = (PfRowSmem::bytes(pa.slot, L.topk, pa.set_cap) + 255) & ~(size_t)255;
-  if (!prefill_fits(L.W, L.topk)) return hipErrorNotSupported;
+  pa.wave_smem = (PfRowSmem::bytes(pa.slot, L.topk, pa.set_cap, PfRowSmem::compact(L.bf16, L.topk)) + 255) & ~(size_t)255;
+  if (!prefill_fits(L.W, L.topk, L.bf16)) return hipErrorNotSupported;
   if (L.bf16) return L.d == 128 ? launch_pf_t<128, true>(L, pa, stream) : launch_pf_t<64, true>(L, pa, stream);
   return L.d == 128 ? launch_pf_t<128, false>(L, pa, stream) : launch_pf_t<64, false>(L, pa, stream);
 }

@@ -88,10 +88,12 @@ extern "C" {
 #define TOPO_OP_DECODE_RAGGED 5     /* topo_attn_decode_ragged (sized for the longest position) */
 
 /* Largest condensate set (1 + W + k) a call may ask for. The prefill also needs the LDS of its
- * per-row finish to hold four rows: with S = 1 + W + k, P = roundup(k + 1, 144) and
- * L = min(k + 48, 128), 4 * roundup256(1092 + 12 * S + 8 * max(S, P / 2, 128) + 8 * (k + 1)
- * + 4 * P + 12 * L) <= 163840 bytes (S <= 1871 at k = 64); larger sets return TOPO_EUNSUPPORTED
- * from the prefill calls (and 0 from topo_workspace_bytes). */
+ * per-row finish to hold four rows. With bfloat16 inputs and k <= 64 that LDS does not grow with
+ * the set (at most 14 KB per block), so TOPO_MAX_SET is the only limit. Otherwise (float32
+ * inputs, or k > 64), with S = 1 + W + k, P = roundup(k + 1, 144) and L = min(k + 48, 128),
+ * 4 * roundup256(1092 + 12 * S + 8 * max(S, P / 2, 128) + 8 * (k + 1) + 4 * P + 12 * L)
+ * <= 163840 bytes (S <= 1871 at k = 64, S <= 1849 at k = 96); larger sets return
+ * TOPO_EUNSUPPORTED from the prefill calls (and 0 from topo_workspace_bytes). */
 #define TOPO_MAX_SET 4096
 
 /* Flag bits of topo_params_t.flags. */

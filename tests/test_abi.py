@@ -154,26 +154,29 @@ def test_noalloc_checks_on_host():
         assert lib.topo_attn_decode_noalloc(ctypes.byref(_p(**bad)), a, a, a, a, a, a, None) == code
 
 
-def _prefill_params(W, k):
+def _prefill_params(W, k, dtype=1):
     return topo.TopoParams(B=1, Hq=8, Hkv=8, d=128, n_ctx=8192, n_q=8192, q_pos0=0, W=W, k=k, causal=1,
-                           softmax_scale=1.0, dtype=1, flags=0)
+                           softmax_scale=1.0, dtype=dtype, flags=0)
 
 
 def test_prefill_set_size_limit_on_host():
-    """The prefill's per-row finish keeps four rows in one block's LDS, which bounds the set
-    1 + W + k (1871 at k = 64, the header's formula); larger sets are refused on the host, with
-    a zero workspace size and TOPO_EUNSUPPORTED, before anything is launched."""
+    """The prefill's per-row finish keeps four rows in one block's LDS. With bf16 inputs and
+    k <= 64 its compact layout does not grow with the set, so only TOPO_MAX_SET bounds 1 + W + k;
+    otherwise the header's formula does (1871 at k = 64 for float32 inputs, 1849 at k = 96 for
+    bf16). Larger sets are refused on the host, with a zero workspace size and TOPO_EUNSUPPORTED,
+    before anything is launched."""
     lib = topo.load_library()
-    assert lib.topo_workspace_bytes(ctypes.byref(_prefill_params(1871 - 65, 64)), 1) > 0
-    assert lib.topo_workspace_bytes(ctypes.byref(_prefill_params(1872 - 65, 64)), 1) == 0
-    assert lib.topo_workspace_bytes(ctypes.byref(_prefill_params(2047, 64)), 1) == 0
+    ws = lambda W, k, dt=1: lib.topo_workspace_bytes(ctypes.byref(_prefill_params(W, k, dt)), 1)
+    assert ws(4096 - 65, 64) > 0 and ws(2047, 64) > 0 and ws(2047, 8) > 0
+    assert ws(1871 - 65, 64, 0) > 0 and ws(1872 - 65, 64, 0) == 0 and ws(2047, 64, 0) == 0
+    assert ws(1849 - 97, 96) > 0 and ws(1850 - 97, 96) == 0
     # aligned host addresses stand in for device buffers: the size check refuses the call first
     buf = (ctypes.c_uint8 * 256)()
     a = (ctypes.addressof(buf) + 15) & ~15
     ptr = ctypes.c_void_p(a)
-    for W in (1872 - 65, 2047):
-        rc = lib.topo_attn_prefill(ctypes.byref(_prefill_params(W, 64)), ptr, ptr, ptr, ptr, ptr, ptr, ptr,
-                                   ctypes.c_size_t(1 << 40), None)
+    for W, k, dt in ((1872 - 65, 64, 0), (2047, 64, 0), (1850 - 97, 96, 1)):
+        prm = _prefill_params(W, k, dt)
+        rc = lib.topo_attn_prefill(ctypes.byref(prm), ptr, ptr, ptr, ptr, ptr, ptr, ptr, ctypes.c_size_t(1 << 40), None)
         assert rc == -2, rc
-        rc = lib.topo_select(ctypes.byref(_prefill_params(W, 64)), ptr, ptr, ptr, ptr, ptr, ctypes.c_size_t(1 << 40), None)
+        rc = lib.topo_select(ctypes.byref(prm), ptr, ptr, ptr, ptr, ptr, ctypes.c_size_t(1 << 40), None)
         assert rc == -2, rc

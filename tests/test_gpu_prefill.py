@@ -85,7 +85,9 @@ CASES = [
     (900, 300, 200, 128, "bf16", 1, 2, 1, 32, 16, False),     # non-causal
     (700, 700, 0, 64, "f32", 1, 2, 1, 32, 16, True),          # float32: exact selection path
     (1200, 1200, 0, 128, "bf16", 1, 2, 1, 40, 150, True),     # k above the MFMA scan's limit
-    (2500, 2500, 0, 128, "bf16", 1, 1, 1, 1806, 64, True),    # the largest set at k = 64 (1 + W + k = 1871)
+    (2500, 2500, 0, 128, "bf16", 1, 1, 1, 2047, 64, True),    # bf16, k <= 64: a set past the general layout's limit
+    (2500, 2500, 0, 128, "bf16", 1, 1, 1, 1752, 96, True),    # bf16, k = 96: the largest set (1 + W + k = 1849)
+    (2000, 2000, 0, 64, "f32", 1, 1, 1, 1806, 64, True),      # float32: the largest set at k = 64 (1871)
     # more scan jobs than the GPU holds at once: each block takes several in snake order
     (16384, 16384, 0, 128, "bf16", 1, 12, 4, 128, 64, True),  # 1536 jobs, one list (12 heads)
     (8192, 8192, 0, 64, "bf16", 2, 20, 4, 64, 32, True),      # 2560 jobs, eight lists of 5 heads
