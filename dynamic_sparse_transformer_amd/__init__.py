@@ -88,6 +88,14 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     p = path or library_path
     if not os.path.exists(p):
         raise FileNotFoundError(f"{p} is missing: build it first (python -c 'import __graft_entry__ as g; g.build()')")
+    # torch first: it ships its own HIP runtime, whose soname the library's dependency matches, so
+    # both then share one runtime (and one HSA runtime). Loaded the other way round, the process
+    # would hold two runtimes, and torch's streams and allocations passed to the library would
+    # belong to the other one.
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     lib = ctypes.CDLL(p)
     vp, sz, i32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
     P = ctypes.POINTER(TopoParams)

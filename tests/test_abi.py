@@ -5,6 +5,7 @@ import ctypes
 import os
 import re
 import subprocess
+import sys
 
 import pytest
 
@@ -180,3 +181,18 @@ def test_prefill_set_size_limit_on_host():
         assert rc == -2, rc
         rc = lib.topo_select(ctypes.byref(prm), ptr, ptr, ptr, ptr, ptr, ctypes.c_size_t(1 << 40), None)
         assert rc == -2, rc
+
+
+def test_library_shares_torchs_hip_runtime():
+    """Loading the library before anything else imports torch still leaves one HIP runtime and
+    one HSA runtime in the process (the binding imports torch first, whose runtime the library's
+    dependency then resolves to); two runtimes would make torch's streams and allocations foreign
+    to the library."""
+    code = ("import os, dynamic_sparse_transformer_amd as t; t.load_library(); import torch; "
+            "m = open(f'/proc/{os.getpid()}/maps').read().splitlines(); "
+            "print(len({l.split()[-1] for l in m if 'libamdhip64' in l}), "
+            "len({l.split()[-1] for l in m if 'libhsa-runtime64' in l}))")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    out = subprocess.run([sys.executable, "-c", code], cwd=root, capture_output=True, text=True, timeout=600)
+    assert out.returncode == 0, out.stderr
+    assert out.stdout.split()[-2:] == ["1", "1"], out.stdout
