@@ -154,16 +154,28 @@ __device__ __forceinline__ void pf_norm_rows(const unsigned char* x, int64_t row
     if (threadIdx.x < BROWS / 64 && t < tiles) tmax[(size_t)by * tiles + t] = __uint_as_float(tm[threadIdx.x]);
   }
 }
+struct PfNormArgs {
+  const unsigned char* q;
+  int64_t q_rows;
+  float* qn;
+  const unsigned char* k;
+  int64_t n;
+  float* kn;
+  float* ktmax;
+  uint32_t qblocks, kblocks;  // blocks [0, qblocks) take the query rows, the rest kblocks per kv head
+};
 template <int D, int U>
-__global__ __launch_bounds__(256) void pf_norm_kernel(const unsigned char* q, int64_t q_rows, float* qn,
-                                                      const unsigned char* k, int64_t n, float* kn, float* ktmax,
-                                                      uint32_t qblocks, uint32_t kblocks) {
-  if (blockIdx.x < qblocks) {
-    pf_norm_rows<D, U>(q, q_rows, qn, nullptr, blockIdx.x, 0u);
+__device__ __forceinline__ void pf_norm_block(const PfNormArgs& na, uint32_t blk) {
+  if (blk < na.qblocks) {
+    pf_norm_rows<D, U>(na.q, na.q_rows, na.qn, nullptr, blk, 0u);
   } else {
-    const uint32_t j = blockIdx.x - qblocks;
-    pf_norm_rows<D, U>(k, n, kn, ktmax, j % kblocks, j / kblocks);
+    const uint32_t j = blk - na.qblocks;
+    pf_norm_rows<D, U>(na.k, na.n, na.kn, na.ktmax, j % na.kblocks, j / na.kblocks);
   }
+}
+template <int D, int U>
+__global__ __launch_bounds__(256) void pf_norm_kernel(PfNormArgs na) {
+  pf_norm_block<D, U>(na, blockIdx.x);
 }
 
 // Sum, maximum or minimum over each row of 16 lanes, in every lane of the row (DPP: quad swaps,
@@ -737,7 +749,7 @@ __global__ __launch_bounds__(512) void pf_scan_kernel(PfArgs a) {
 // 8(r/4) + 4h + r%4), in the same order in the weight (A) and V (B) operands. The output tiles'
 // rows are 8*(r/4) + 4*(l/32) + r%4, so their factors are read back from LDS.
 template <int D>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void pf_window_kernel(PfArgs a) {
+__device__ __forceinline__ void pf_window_block(const PfArgs& a) {
   constexpr int RB = D * 2, STEPS = D / 16, NW = D / 32, NWD = NW / 2;  // dim tiles per wave
   constexpr int STR = RB + 16;         // padded LDS row (K and V)
   constexpr int CPR = RB / 16;         // 16-byte chunks per key row
@@ -913,6 +925,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void p
     }
   }
   if (dh == 0 && half == 0 && iw < a.n_q) a.w.win_mz[(size_t)bh * a.n_q + iw] = make_float2(mrun, zs);
+}
+
+// One launch for the window's share and the norms: blocks [0, nwin) are window blocks, the rest
+// norm blocks. Both read only the inputs, so neither waits for the other; the norm blocks fill
+// the compute units that the window's last round of blocks leaves idle, and the launch and the
+// separate norm pass's ramp are saved.
+template <int D>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void pf_window_kernel(PfArgs a, PfNormArgs na,
+                                                                                               uint32_t nwin) {
+  if (blockIdx.x < nwin) pf_window_block<D>(a);
+  else pf_norm_block<D, 4>(na, blockIdx.x - nwin);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -1579,16 +1602,27 @@ static hipError_t launch_pf_t(const PrefillLaunch& L, const PfArgs& pa, hipStrea
   const size_t rows = (size_t)L.B * L.Hq * (size_t)L.n_q;
   hipError_t e = hipSuccess;
   if constexpr (BF16) {
-    if (!pa.exact_all && L.topk > 0) {
-      // norms for the error bounds of the matrix-core scores (only the fast selection uses them)
-      constexpr int RPW = 64 / (D * 2 / 16), QU = 4;  // rows per wave load; loads per lane
+    // norms for the error bounds of the matrix-core scores (only the fast selection uses them)
+    // and the window's share of the softmax, in one launch when both are needed; both before the
+    // scan
+    constexpr int RPW = 64 / (D * 2 / 16), QU = 4;  // rows per wave load; loads per lane
+    const bool norms = !pa.exact_all && L.topk > 0;
+    PfNormArgs na{};
+    uint64_t nnorm = 0;
+    if (norms) {
       const uint64_t qblocks = (rows + 4 * QU * RPW - 1) / (4 * QU * RPW);
       const uint64_t kblocks = ((uint64_t)L.n + 4 * QU * RPW - 1) / (4 * QU * RPW);
-      const uint64_t nblocks = qblocks + kblocks * (uint64_t)(L.B * L.Hkv);
-      if (nblocks > 0x7FFFFFFFull) return hipErrorInvalidValue;
-      hipLaunchKernelGGL((pf_norm_kernel<D, QU>), dim3((unsigned)nblocks), dim3(256), 0, s, (const unsigned char*)L.q,
-                         (int64_t)rows, pa.w.qn, (const unsigned char*)L.k, L.n, pa.w.kn, pa.w.ktmax, (uint32_t)qblocks,
-                         (uint32_t)kblocks);
+      nnorm = qblocks + kblocks * (uint64_t)(L.B * L.Hkv);
+      na = PfNormArgs{(const unsigned char*)L.q, (int64_t)rows, pa.w.qn, (const unsigned char*)L.k, L.n, pa.w.kn,
+                      pa.w.ktmax, (uint32_t)qblocks, (uint32_t)kblocks};
+    }
+    const uint64_t nwin = pa.win ? (uint64_t)((L.n_q + 63) / 64) * (uint64_t)(L.B * L.Hq) : 0;
+    if (nwin + nnorm > 0x7FFFFFFFull) return hipErrorInvalidValue;
+    if (nwin + nnorm > 0) {
+      if (nwin > 0)
+        hipLaunchKernelGGL((pf_window_kernel<D>), dim3((unsigned)(nwin + nnorm)), dim3(256), 0, s, pa, na, (uint32_t)nwin);
+      else
+        hipLaunchKernelGGL((pf_norm_kernel<D, QU>), dim3((unsigned)nnorm), dim3(256), 0, s, na);
       e = hipGetLastError();
       if (e != hipSuccess) return e;
     }
@@ -1604,14 +1638,6 @@ static hipError_t launch_pf_t(const PrefillLaunch& L, const PfArgs& pa, hipStrea
     }
   }
   if (L.ev_scan_end) (void)hipEventRecord(L.ev_scan_end, s);
-  if constexpr (BF16) {
-    if (pa.win) {
-      hipLaunchKernelGGL((pf_window_kernel<D>), dim3((unsigned)((L.n_q + 63) / 64 * L.B * L.Hq)), dim3(256), 0, s,
-                         pa);
-      e = hipGetLastError();
-      if (e != hipSuccess) return e;
-    }
-  }
   const size_t smem = 4 * pa.wave_smem;
   const bool off32 = (uint64_t)L.n * (uint64_t)(D * (BF16 ? 2 : 4)) <= 0xFFFFFFFFull;
   const void* fk = off32 ? (const void*)pf_finish_kernel<D, BF16, true> : (const void*)pf_finish_kernel<D, BF16, false>;
