@@ -1418,7 +1418,7 @@ __device__ void pf_row(const PfArgs& a, PfRowSmem* sm, size_t grow) {
 
   // ---- softmax over the set and the weighted V rows: lane group gq takes the entries
   // t = gq (mod RPI), each lane a 16-byte chunk of the row; then the groups are summed.
-  constexpr int U = BF16 ? 9 : 4;  // V rows per lane group in flight together (bf16: 36 rows per batch at d = 128)
+  constexpr int U = BF16 ? 6 : 4;  // V rows per lane group in flight together (bf16: 24 rows per batch at d = 128)
   if constexpr (BF16) {
     // The window's part (m_w, Z_w, O_w) comes from pf_window; here the anchor and the top-k
     // (tidx / ts [0, nt), the anchor appended at nt), then the merge of the two parts:
@@ -1565,7 +1565,7 @@ __device__ void pf_row(const PfArgs& a, PfRowSmem* sm, size_t grow) {
 // pf_finish: one wave per query row, 4 rows per block (consecutive rows of one head). OFF32 as in
 // pf_row (chosen at launch: one row variant per kernel keeps the register count down).
 template <int D, bool BF16, bool OFF32>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(7))) void pf_finish_kernel(PfArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8))) void pf_finish_kernel(PfArgs a) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
   // (the wave index through readfirstlane: the row's indices stay in scalar registers)
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
